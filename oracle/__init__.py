@@ -1,0 +1,207 @@
+"""fp64 CPU oracle for the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import this package.  The HIP library never imports, links or calls it, and the two
+share no code: the only module both sides use is ``workloads`` (seeded random inputs,
+which holds none of the method's arithmetic).
+
+Contents
+  * ``gdn_oracle.c`` (compiled to ``_build/liboracle.so`` with gcc -O2, no fast-math):
+    the plain token-by-token recurrence, the packed-varlen tables and driver, the BiGDN
+    front end (full-channel RMSNorm, ReLU, k-scale, interleaved-pair RoPE) and the
+    frame-level BiGDN scan in both directions.  This is the reference every GPU result is
+    compared with.
+  * ``forms.py``: independent numpy cross-check forms (global O(T^2) solve, chunked WY
+    form, BiGDN product form with flip-and-shift reverse) used only to pin the oracle.
+
+Every function takes and returns float64 numpy arrays; inputs stored as bf16 or fp32 are
+converted to float64 exactly before the call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+_lib = None
+
+CHUNK = 64
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (-O2, OpenMP, no fast-math).  Returns the .so path."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+               "-Wno-unknown-pragmas", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        Dd = ctypes.c_double
+        lib.oracle_gdn.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, Dd, P, P, P, P, P]
+        lib.oracle_gdn_varlen.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, Dd, P, P, P, P, P]
+        lib.oracle_varlen_tables.argtypes = [P, I, I, P, P]
+        lib.oracle_prep.argtypes = [I, I, I, I, P, P, P, P, P, Dd, Dd, P, P, P, P, P, P, P]
+        lib.oracle_bigdn_dir.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.oracle_bigdn.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, Dd, Dd, P, P]
+        lib.oracle_set_threads.argtypes = [I]
+        for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
+                     "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads"):
+            getattr(lib, name).restype = I
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor -> exact float64 copy on the host
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def gdn(q, k, v, beta, g=None, gk=None, scale=1.0, h0=None, chunk=CHUNK,
+        want_h=False, want_vnew=False):
+    """Token recurrence over a dense batch.
+
+    q, k [B,T,H,K]; v [B,T,H,V]; beta, g [B,T,H]; gk [B,T,H,K]; h0 [B,H,K,V].
+    Returns dict with o [B,T,H,V], ht [B,H,K,V], and optionally h [B,H,NT,K,V] (state
+    entering each chunk of ``chunk`` tokens) and v_new [B,T,H,V].
+    """
+    q, k, v, beta, g, gk, h0 = map(_f64, (q, k, v, beta, g, gk, h0))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    NT = (T + chunk - 1) // chunk
+    o = np.empty((B, T, H, V))
+    ht = np.empty((B, H, K, V))
+    hch = np.empty((B, H, NT, K, V)) if want_h else None
+    vn = np.empty((B, T, H, V)) if want_vnew else None
+    rc = _load().oracle_gdn(B, T, H, K, V, chunk, _p(q), _p(k), _p(v), _p(g), _p(gk),
+                            _p(beta), float(scale), _p(h0), _p(o), _p(ht), _p(hch), _p(vn))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn failed")
+    out = {"o": o, "ht": ht}
+    if want_h:
+        out["h"] = hch
+    if want_vnew:
+        out["v_new"] = vn
+    return out
+
+
+def varlen_tables(cu_seqlens, chunk=CHUNK):
+    """(chunk_offsets [N+1] int32, chunk_indices [NT_total,2] int32) for a cu_seqlens array."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+    N = cu.shape[0] - 1
+    lib = _load()
+    nt = lib.oracle_varlen_tables(_p(cu), N, chunk, None, None)
+    if nt < 0:
+        raise ValueError("malformed cu_seqlens")
+    offs = np.empty(N + 1, np.int32)
+    idx = np.empty((nt, 2), np.int32)
+    lib.oracle_varlen_tables(_p(cu), N, chunk, _p(offs), _p(idx))
+    return offs, idx
+
+
+def gdn_varlen(cu_seqlens, q, k, v, beta, g=None, gk=None, scale=1.0, h0=None, chunk=CHUNK,
+               want_h=False, want_vnew=False):
+    """Packed batch of 1: q, k [1,T,H,K] ... ; h0/ht [N,H,K,V]; h [1,H,NT_total,K,V]."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+    q, k, v, beta, g, gk, h0 = map(_f64, (q, k, v, beta, g, gk, h0))
+    _, T, H, K = q.shape
+    V = v.shape[-1]
+    N = cu.shape[0] - 1
+    offs, _ = varlen_tables(cu, chunk)
+    NT = int(offs[-1])
+    o = np.empty((1, T, H, V))
+    ht = np.empty((N, H, K, V))
+    hch = np.empty((1, H, NT, K, V)) if want_h else None
+    vn = np.empty((1, T, H, V)) if want_vnew else None
+    rc = _load().oracle_gdn_varlen(_p(cu), N, H, K, V, chunk, _p(q), _p(k), _p(v), _p(g),
+                                   _p(gk), _p(beta), float(scale), _p(h0), _p(o), _p(ht),
+                                   _p(hch), _p(vn))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_varlen failed")
+    out = {"o": o, "ht": ht}
+    if want_h:
+        out["h"] = hch
+    if want_vnew:
+        out["v_new"] = vn
+    return out
+
+
+def prep(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, eps=1e-5):
+    """BiGDN front end.  qkv [B,N,3,H,D] -> dict of q_inv_rms, k_inv_rms [B,N] and
+    q_rot, k_rot, q_pos, k_pos, v [B,H,N,D]."""
+    qkv, qw, kw, cs, sn = map(_f64, (qkv, q_norm_w, k_norm_w, rope_cos, rope_sin))
+    B, N, _, H, D = qkv.shape
+    out = {name: np.empty((B, H, N, D)) for name in ("q_rot", "k_rot", "q_pos", "k_pos", "v")}
+    out["q_inv_rms"] = np.empty((B, N))
+    out["k_inv_rms"] = np.empty((B, N))
+    rc = _load().oracle_prep(B, N, H, D, _p(qkv), _p(qw), _p(kw), _p(cs), _p(sn),
+                             float(k_scale), float(eps), _p(out["q_inv_rms"]),
+                             _p(out["k_inv_rms"]), _p(out["q_rot"]), _p(out["k_rot"]),
+                             _p(out["q_pos"]), _p(out["k_pos"]), _p(out["v"]))
+    if rc != 0:
+        raise RuntimeError("oracle_prep failed")
+    return out
+
+
+def bigdn_dir(q_rot, k_rot, q_pos, k_pos, v, beta, decay, reverse):
+    """One BiGDN direction on prepped [B,H,N,D] tensors; beta [B,H,F,S], decay [B,H,F].
+    Returns (num [B,N,H,D], den [B,H,N])."""
+    q_rot, k_rot, q_pos, k_pos, v, beta, decay = map(
+        _f64, (q_rot, k_rot, q_pos, k_pos, v, beta, decay))
+    B, H, N, D = q_rot.shape
+    F, S = beta.shape[2], beta.shape[3]
+    num = np.zeros((B, N, H, D))
+    den = np.zeros((B, H, N))
+    rc = _load().oracle_bigdn_dir(B, F, S, H, D, int(bool(reverse)), _p(q_rot), _p(k_rot),
+                                  _p(q_pos), _p(k_pos), _p(v), _p(beta), _p(decay), _p(num),
+                                  _p(den))
+    if rc != 0:
+        raise RuntimeError("oracle_bigdn_dir failed")
+    return num, den
+
+
+def bigdn(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, eps=1e-5):
+    """Whole BiGDN block forward: (num [B,N,H,D], den [B,H,N]) summed over both directions."""
+    qkv, beta, decay, qw, kw, cs, sn = map(
+        _f64, (qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin))
+    B, N, _, H, D = qkv.shape
+    F, S = beta.shape[2], beta.shape[3]
+    num = np.empty((B, N, H, D))
+    den = np.empty((B, H, N))
+    rc = _load().oracle_bigdn(B, F, S, H, D, _p(qkv), _p(beta), _p(decay), _p(qw), _p(kw),
+                              _p(cs), _p(sn), float(k_scale), float(eps), _p(num), _p(den))
+    if rc != 0:
+        raise RuntimeError("oracle_bigdn failed")
+    return num, den

@@ -1,0 +1,406 @@
+/*
+ * gdn_oracle.c -- plain fp64 CPU oracle for the gated delta rule (TEST INFRASTRUCTURE ONLY).
+ *
+ * This file is the correctness reference for the HIP library.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it.  It shares no code,
+ * header, table or helper with the GPU path, and nothing in the GPU path calls it.
+ *
+ * Everything here is the plain definition of the method, written token by token in double
+ * precision, with no blocking, fusion or reordering beyond what the definition states.  The
+ * only parallelism is an OpenMP loop over chains that are independent by definition
+ * (distinct (batch, head) pairs, distinct packed sequences, the two BiGDN directions).
+ *
+ * Sources (pages, as named by their addresses):
+ *  - chunk_gated_delta_rule_fwd_h fragments on the hyper-parallel "Diff Coverage" page
+ *    (MindSpore): the per-chunk state pass (decay by the last gate, optional per-key gate
+ *    row-scaling of the state, v_new = u - w h), the varlen offsets (bos, chunk tables),
+ *    and the [B, H, K, V] fp32 state layout.
+ *  - SANA fused_gdn.py page, section "Unified forward Triton Mega-Kernel"
+ *    (_fused_gdn_kernel): full-channel RMSNorm, ReLU, k-scale, interleaved-pair RoPE,
+ *    the frame-level update (all tokens of a frame read the decayed pre-update state),
+ *    the z normaliser, inclusive outputs, and the reverse direction's frame indexing.
+ *  - SANA fused_gdn.py page, prepare_rope_tables / _precompute_inv_rms: the expanded
+ *    (N, D) cos/sin table format and the full-channel inverse RMS with eps.
+ *  - SANA fused_cam_gdn.py page, "Torch reference implementations" section
+ *    (_flip_and_shift, _torch_cam_scan_reference): reverse = flip-and-shift.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - gates are natural-log: the decay factor of token t on key row d is
+ *    exp(g_t + gk_{t,d}) (a missing g or gk contributes 0);
+ *  - h_chunks[n] is the state entering chunk n, i.e. before token n*C's decay;
+ *  - v_new_t = beta_t (v_t - S'^T k_t) with S' the decayed state (the delta itself);
+ *  - the initial state h0 is the state at the end of a prefix, before any further decay.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_abi_version(void) { return 1; }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/*
+ * One chain of the token recurrence (the definition given with the method):
+ *     S_t = diag(a_t) S_{t-1} + k_t d_t^T,   d_t = beta_t (v_t - (diag(a_t) S_{t-1})^T k_t),
+ *     o_t = scale * S_t^T q_t,               a_{t,d} = exp(g_t + gk_{t,d}).
+ * S is K x V with the key dimension as rows.  Pointers address token 0 of this chain; the
+ * token strides say how far apart consecutive tokens are (in elements).
+ *   q, k  : K values per token, stride sqk     g    : 1 value per token, stride sg
+ *   v     : V values per token, stride sv      gk   : K values per token, stride sqk
+ *   beta  : 1 value per token, stride sg       o,vnew: V values per token, stride sv
+ *   h0/ht : K*V (row-major), may be NULL       hch  : NT*K*V states entering each chunk
+ * S is a caller-provided K*V work array.
+ */
+static void gdn_chain(int T, int K, int V, int C,
+                      const double* q, const double* k, const double* v, long sqk, long sv,
+                      const double* g, const double* gk, const double* beta, long sg,
+                      double scale, const double* h0, double* o, double* ht, double* hch,
+                      double* vnew, double* S, double* a, double* d) {
+  if (h0) memcpy(S, h0, sizeof(double) * (size_t)K * V);
+  else memset(S, 0, sizeof(double) * (size_t)K * V);
+  for (int t = 0; t < T; ++t) {
+    const double* qt = q + (long)t * sqk;
+    const double* kt = k + (long)t * sqk;
+    const double* vt = v + (long)t * sv;
+    const double bt = beta[(long)t * sg];
+    if (hch && (t % C) == 0)  /* state entering chunk t/C, before this token's decay */
+      memcpy(hch + (size_t)(t / C) * K * V, S, sizeof(double) * (size_t)K * V);
+    /* decay: S <- diag(a_t) S */
+    for (int r = 0; r < K; ++r) {
+      double lam = 0.0;
+      if (g) lam += g[(long)t * sg];
+      if (gk) lam += gk[(long)t * sqk + r];
+      a[r] = exp(lam);
+    }
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < V; ++c) S[(size_t)r * V + c] *= a[r];
+    /* delta: d = beta (v - S^T k) */
+    for (int c = 0; c < V; ++c) d[c] = 0.0;
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < V; ++c) d[c] += S[(size_t)r * V + c] * kt[r];
+    for (int c = 0; c < V; ++c) d[c] = bt * (vt[c] - d[c]);
+    /* rank-one write: S <- S + k d^T */
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < V; ++c) S[(size_t)r * V + c] += kt[r] * d[c];
+    /* inclusive output o_t = scale S_t^T q_t */
+    double* ot = o + (long)t * sv;
+    for (int c = 0; c < V; ++c) ot[c] = 0.0;
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < V; ++c) ot[c] += S[(size_t)r * V + c] * qt[r];
+    for (int c = 0; c < V; ++c) ot[c] *= scale;
+    if (vnew)
+      for (int c = 0; c < V; ++c) vnew[(long)t * sv + c] = d[c];
+  }
+  if (ht) memcpy(ht, S, sizeof(double) * (size_t)K * V);
+}
+
+/*
+ * Dense batch: q,k [B,T,H,K], v [B,T,H,V], g,beta [B,T,H], gk [B,T,H,K], h0/ht [B,H,K,V],
+ * o/vnew [B,T,H,V], hch [B,H,NT,K,V] with NT = ceil(T/C).  g, gk, h0, ht, hch, vnew may be
+ * NULL.  Returns 0, or -1 on bad sizes.
+ */
+int oracle_gdn(int B, int T, int H, int K, int V, int C,
+               const double* q, const double* k, const double* v, const double* g,
+               const double* gk, const double* beta, double scale, const double* h0,
+               double* o, double* ht, double* hch, double* vnew) {
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || C <= 0) return -1;
+  const int NT = (T + C - 1) / C;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
+    double* a = (double*)malloc(sizeof(double) * (size_t)K);
+    double* d = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!S || !a || !d) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        const long tok0 = (long)b * T * H + h;
+        gdn_chain(T, K, V, C, q + tok0 * K, k + tok0 * K, v + tok0 * V, (long)H * K,
+                  (long)H * V, g ? g + tok0 : NULL, gk ? gk + tok0 * K : NULL, beta + tok0,
+                  (long)H, scale, h0 ? h0 + (size_t)bh * K * V : NULL, o + tok0 * V,
+                  ht ? ht + (size_t)bh * K * V : NULL,
+                  hch ? hch + (size_t)bh * NT * K * V : NULL, vnew ? vnew + tok0 * V : NULL,
+                  S, a, d);
+      }
+    }
+    free(S);
+    free(a);
+    free(d);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
+ * Varlen chunk tables (the chunk_indices / chunk_offsets the state-pass fragments index
+ * with): chunk_offsets[i] = number of chunks in sequences before i, so it has N+1 entries;
+ * chunk_indices holds one (sequence, chunk-within-sequence) pair per chunk, in order.
+ * Returns the total number of chunks, or -1 if cu is malformed (cu[0] != 0 or a sequence
+ * is empty).  Either output may be NULL.
+ */
+int oracle_varlen_tables(const int* cu, int N, int C, int* chunk_offsets, int* chunk_indices) {
+  if (N <= 0 || C <= 0 || cu[0] != 0) return -1;
+  int total = 0;
+  for (int i = 0; i < N; ++i) {
+    const int len = cu[i + 1] - cu[i];
+    if (len <= 0) return -1;
+    if (chunk_offsets) chunk_offsets[i] = total;
+    const int nc = (len + C - 1) / C;
+    for (int c = 0; c < nc; ++c) {
+      if (chunk_indices) {
+        chunk_indices[2 * (total + c)] = i;
+        chunk_indices[2 * (total + c) + 1] = c;
+      }
+    }
+    total += nc;
+  }
+  if (chunk_offsets) chunk_offsets[N] = total;
+  return total;
+}
+
+/*
+ * Packed variable-length batch (batch 1): tensors are [1, T_total, H, .]; sequence i covers
+ * tokens [cu[i], cu[i+1]) and restarts both the state (from h0[i] or zero) and the chunk
+ * grid.  h0/ht are [N,H,K,V]; hch is [1,H,NT_total,K,V] indexed by chunk_offsets.
+ */
+int oracle_gdn_varlen(const int* cu, int N, int H, int K, int V, int C,
+                      const double* q, const double* k, const double* v, const double* g,
+                      const double* gk, const double* beta, double scale, const double* h0,
+                      double* o, double* ht, double* hch, double* vnew) {
+  const int NT = oracle_varlen_tables(cu, N, C, NULL, NULL);
+  if (NT < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+  int* offs = (int*)malloc(sizeof(int) * (size_t)(N + 1));
+  if (!offs) return -1;
+  oracle_varlen_tables(cu, N, C, offs, NULL);
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
+    double* a = (double*)malloc(sizeof(double) * (size_t)K);
+    double* d = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!S || !a || !d) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int ih = 0; ih < N * H; ++ih) {
+        const int i = ih / H, h = ih % H;
+        const long tok0 = (long)cu[i] * H + h;
+        gdn_chain(cu[i + 1] - cu[i], K, V, C, q + tok0 * K, k + tok0 * K, v + tok0 * V,
+                  (long)H * K, (long)H * V, g ? g + tok0 : NULL, gk ? gk + tok0 * K : NULL,
+                  beta + tok0, (long)H, scale, h0 ? h0 + (size_t)ih * K * V : NULL,
+                  o + tok0 * V, ht ? ht + (size_t)ih * K * V : NULL,
+                  hch ? hch + ((size_t)h * NT + offs[i]) * K * V : NULL,
+                  vnew ? vnew + tok0 * V : NULL, S, a, d);
+      }
+    }
+    free(S);
+    free(a);
+    free(d);
+  }
+  free(offs);
+  return fail ? -1 : 0;
+}
+
+/*
+ * BiGDN front end (SANA fused_gdn.py page: _precompute_inv_rms, prepare_rope_tables and the
+ * load path of _fused_gdn_kernel).  qkv is [B,N,3,H,D]; weights are [H*D]; cos/sin are the
+ * expanded [N,D] tables with y[d] = x[d] cos[n,d] + x[d^1] sin[n,d].
+ *   inv_rms = 1 / sqrt(sum over all H*D channels of x^2 / (H*D) + eps), per (b, n)
+ *   x_hat   = x * inv_rms * w[h*D + d]
+ *   q_pos   = relu(q_hat),  k_pos = relu(k_hat) * k_scale
+ *   x_rot   = x_pos[d] cos[n,d] + x_pos[d^1] sin[n,d]
+ * Outputs (each may be NULL): q_inv_rms/k_inv_rms [B,N]; q_rot, k_rot, q_pos, k_pos, v_hm
+ * [B,H,N,D] (head-major).  D must be even.
+ */
+int oracle_prep(int B, int N, int H, int D, const double* qkv, const double* qw,
+                const double* kw, const double* cosv, const double* sinv, double k_scale,
+                double eps, double* q_inv_rms, double* k_inv_rms, double* q_rot, double* k_rot,
+                double* q_pos, double* k_pos, double* v_hm) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0 || (D % 2) != 0) return -1;
+  const long C = (long)H * D;
+#pragma omp parallel for schedule(static)
+  for (long bn = 0; bn < (long)B * N; ++bn) {
+    const long b = bn / N, n = bn % N;
+    const double* row = qkv + bn * 3 * C;
+    double inv[2];
+    for (int which = 0; which < 2; ++which) {
+      double ss = 0.0;
+      for (long c = 0; c < C; ++c) ss += row[which * C + c] * row[which * C + c];
+      inv[which] = 1.0 / sqrt(ss / (double)C + eps);
+    }
+    if (q_inv_rms) q_inv_rms[bn] = inv[0];
+    if (k_inv_rms) k_inv_rms[bn] = inv[1];
+    for (int h = 0; h < H; ++h) {
+      const long o0 = (((long)b * H + h) * N + n) * D;
+      for (int dd = 0; dd < D; ++dd) {
+        const int pd = dd ^ 1;
+        const long c = (long)h * D + dd, pc = (long)h * D + pd;
+        const double cs = cosv[n * D + dd], sn = sinv[n * D + dd];
+        double qx = row[c] * inv[0] * qw[c], qp = row[pc] * inv[0] * qw[pc];
+        double kx = row[C + c] * inv[1] * kw[c], kp = row[C + pc] * inv[1] * kw[pc];
+        qx = qx > 0.0 ? qx : 0.0;
+        qp = qp > 0.0 ? qp : 0.0;
+        kx = (kx > 0.0 ? kx : 0.0) * k_scale;
+        kp = (kp > 0.0 ? kp : 0.0) * k_scale;
+        if (q_pos) q_pos[o0 + dd] = qx;
+        if (k_pos) k_pos[o0 + dd] = kx;
+        if (q_rot) q_rot[o0 + dd] = qx * cs + qp * sn;
+        if (k_rot) k_rot[o0 + dd] = kx * cs + kp * sn;
+        if (v_hm) v_hm[o0 + dd] = row[2 * C + c];
+      }
+    }
+  }
+  return 0;
+}
+
+/*
+ * Absorb one frame into (S, z) in place, following the frame-level update of
+ * _fused_gdn_kernel: every token of the frame predicts from the same (already decayed)
+ * state snapshot Sp / zp, and the frame's corrections are summed:
+ *     S += sum_s k_rot_s (beta_s (v_s - Sp^T k_rot_s))^T
+ *     z += sum_s k_pos_s  beta_s (1 - k_pos_s . zp)
+ * Pointers address the frame's first token of one (b, h) in [.., N, D] head-major tensors.
+ */
+static void absorb_frame(int S_, int D, const double* kr, const double* kp, const double* vv,
+                         const double* bt, double* S, double* z, double* Sp, double* zp,
+                         double* dv) {
+  memcpy(Sp, S, sizeof(double) * (size_t)D * D);
+  memcpy(zp, z, sizeof(double) * (size_t)D);
+  for (int s = 0; s < S_; ++s) {
+    const double* k = kr + (long)s * D;
+    const double* kq = kp + (long)s * D;
+    const double* v = vv + (long)s * D;
+    for (int c = 0; c < D; ++c) dv[c] = 0.0;
+    for (int r = 0; r < D; ++r)
+      for (int c = 0; c < D; ++c) dv[c] += Sp[(size_t)r * D + c] * k[r];
+    for (int c = 0; c < D; ++c) dv[c] = bt[s] * (v[c] - dv[c]);
+    for (int r = 0; r < D; ++r)
+      for (int c = 0; c < D; ++c) S[(size_t)r * D + c] += k[r] * dv[c];
+    double zh = 0.0;
+    for (int r = 0; r < D; ++r) zh += kq[r] * zp[r];
+    const double dz = bt[s] * (1.0 - zh);
+    for (int r = 0; r < D; ++r) z[r] += kq[r] * dz;
+  }
+}
+
+/* Inclusive outputs of one frame: num_s = S^T q_rot_s, den_s = q_pos_s . z (accumulated). */
+static void emit_frame(int S_, int D, const double* qr, const double* qp, const double* S,
+                       const double* z, double* num, long num_stride, double* den) {
+  for (int s = 0; s < S_; ++s) {
+    const double* q = qr + (long)s * D;
+    const double* qq = qp + (long)s * D;
+    double* o = num + (long)s * num_stride;
+    for (int r = 0; r < D; ++r)
+      for (int c = 0; c < D; ++c) o[c] += S[(size_t)r * D + c] * q[r];
+    double dn = 0.0;
+    for (int r = 0; r < D; ++r) dn += qq[r] * z[r];
+    den[s] += dn;
+  }
+}
+
+/*
+ * One BiGDN direction on prepped head-major tensors q_rot, k_rot, q_pos, k_pos, v
+ * [B,H,N,D] (N = F*S), beta [B,H,F,S], decay [B,H,F] (multiplicative, in (0,1]).
+ * Results are ADDED into num [B,N,H,D] and den [B,H,N] (callers zero them first).
+ *   forward : for f = 0..F-1: S,z *= decay[f]; absorb frame f; emit frame f.
+ *   reverse : frame f is emitted from the state built from frames > f, where absorbing
+ *             frame f+1 first multiplies the state by decay[f+1]; the last frame emits
+ *             from the zero state.
+ */
+int oracle_bigdn_dir(int B, int F, int S_, int H, int D, int reverse, const double* q_rot,
+                     const double* k_rot, const double* q_pos, const double* k_pos,
+                     const double* v, const double* beta, const double* decay, double* num,
+                     double* den) {
+  if (B <= 0 || F <= 0 || S_ <= 0 || H <= 0 || D <= 0) return -1;
+  const long N = (long)F * S_;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* St = (double*)malloc(sizeof(double) * (size_t)D * D);
+    double* Sp = (double*)malloc(sizeof(double) * (size_t)D * D);
+    double* z = (double*)malloc(sizeof(double) * (size_t)D);
+    double* zp = (double*)malloc(sizeof(double) * (size_t)D);
+    double* dv = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!St || !Sp || !z || !zp || !dv) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        const long base = (long)bh * N * D;
+        memset(St, 0, sizeof(double) * (size_t)D * D);
+        memset(z, 0, sizeof(double) * (size_t)D);
+        for (int it = 0; it < F; ++it) {
+          const int f = reverse ? F - 1 - it : it;
+          if (!reverse || it > 0) {
+            const int fa = reverse ? f + 1 : f; /* frame absorbed at this step */
+            const double dcy = decay[(long)bh * F + fa];
+            for (long e = 0; e < (long)D * D; ++e) St[e] *= dcy;
+            for (int r = 0; r < D; ++r) z[r] *= dcy;
+            const long t0 = (long)fa * S_;
+            absorb_frame(S_, D, k_rot + base + t0 * D, k_pos + base + t0 * D,
+                         v + base + t0 * D, beta + (long)bh * N + t0, St, z, Sp, zp, dv);
+          }
+          const long t0 = (long)f * S_;
+          emit_frame(S_, D, q_rot + base + t0 * D, q_pos + base + t0 * D, St, z,
+                     num + (((long)b * N + t0) * H + h) * D, (long)H * D,
+                     den + (long)bh * N + t0);
+        }
+      }
+    }
+    free(St);
+    free(Sp);
+    free(z);
+    free(zp);
+    free(dv);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
+ * Whole BiGDN block forward: prep, then both directions, summed (the sums that
+ * fused_bigdn_func divides; the divide itself is not part of this call).
+ * qkv [B,N,3,H,D]; beta [B,H,F,S]; decay [B,H,F]; outputs num [B,N,H,D], den [B,H,N].
+ */
+int oracle_bigdn(int B, int F, int S_, int H, int D, const double* qkv, const double* beta,
+                 const double* decay, const double* qw, const double* kw, const double* cosv,
+                 const double* sinv, double k_scale, double eps, double* num, double* den) {
+  const long N = (long)F * S_;
+  const size_t n = (size_t)B * H * N * D;
+  double* buf = (double*)malloc(sizeof(double) * n * 5);
+  if (!buf) return -1;
+  double *qr = buf, *kr = buf + n, *qp = buf + 2 * n, *kp = buf + 3 * n, *vv = buf + 4 * n;
+  int rc = oracle_prep(B, (int)N, H, D, qkv, qw, kw, cosv, sinv, k_scale, eps, NULL, NULL,
+                       qr, kr, qp, kp, vv);
+  if (rc == 0) {
+    memset(num, 0, sizeof(double) * n);
+    memset(den, 0, sizeof(double) * (size_t)B * H * N);
+    rc = oracle_bigdn_dir(B, F, S_, H, D, 0, qr, kr, qp, kp, vv, beta, decay, num, den);
+    if (rc == 0)
+      rc = oracle_bigdn_dir(B, F, S_, H, D, 1, qr, kr, qp, kp, vv, beta, decay, num, den);
+  }
+  free(buf);
+  return rc;
+}

@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the gated delta-rule workloads.
+
+This module is shared by the tests, the benchmark and the smoke check.  It draws random
+inputs and nothing else: it holds none of the method's arithmetic, and both the HIP path
+and the CPU oracle consume its tensors unchanged.
+
+Recipe (all draws on the CPU from ``torch.Generator().manual_seed(seed)``, in this order):
+  lengths (packed batches only) -> q -> k -> v -> beta logits -> g logits -> gk logits.
+  q and k are drawn N(0,1) in fp32 and L2-normalised per (token, head) in fp32, then cast
+  (round-to-nearest-even) to the storage dtype; v ~ N(0,1) then cast; beta = sigmoid(N(0,1))
+  and g = logsigmoid(N(0,1) + shift) stay fp32; gk (per-key log decay) likewise.
+The BiGDN block draws qkv ~ N(0,1) (bf16), norm weights 1 + 0.1 N(0,1), beta = sigmoid(N),
+decay = sigmoid(N + 3), and uses rotary angles theta[n, i] = n * 10000^(-2i/D) expanded into
+the (N, D) cos / sin table format of the SANA fused_gdn.py page (prepare_rope_tables):
+cos[n, 2i] = cos[n, 2i+1] = cos(theta), sin[n, 2i] = -sin(theta), sin[n, 2i+1] = +sin(theta).
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _gen(seed):
+    g = torch.Generator()
+    g.manual_seed(int(seed))
+    return g
+
+
+def _l2n(x):
+    return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+
+def gdn_inputs(B, T, H, K, V, dtype="bf16", seed=0, g_shift=3.0, per_key=False,
+               gk_shift=3.0, lengths=None):
+    """Inputs of a dense (or packed, when ``lengths`` is given, B must be 1) GDN forward.
+
+    Returns a dict of CPU tensors: q, k [B,T,H,K] and v [B,T,H,V] in ``dtype``; beta, g
+    [B,T,H] fp32; gk [B,T,H,K] fp32 or None.
+    """
+    gen = _gen(seed)
+    td = DTYPES[dtype]
+    q = _l2n(torch.randn(B, T, H, K, generator=gen)).to(td)
+    k = _l2n(torch.randn(B, T, H, K, generator=gen)).to(td)
+    v = torch.randn(B, T, H, V, generator=gen).to(td)
+    beta = torch.sigmoid(torch.randn(B, T, H, generator=gen))
+    g = torch.nn.functional.logsigmoid(torch.randn(B, T, H, generator=gen) + g_shift)
+    gk = None
+    if per_key:
+        gk = torch.nn.functional.logsigmoid(torch.randn(B, T, H, K, generator=gen) + gk_shift)
+    return {"q": q, "k": k, "v": v, "beta": beta, "g": g, "gk": gk}
+
+
+def varlen_lengths(n_seqs, lo, hi, seed):
+    """Sequence lengths uniform in [lo, hi] (inclusive), drawn first from the seed."""
+    gen = _gen(seed)
+    return torch.randint(lo, hi + 1, (n_seqs,), generator=gen)
+
+
+def varlen_inputs(n_seqs, lo, hi, H, K, V, dtype="bf16", seed=0, g_shift=3.0):
+    """Packed batch: lengths drawn first, then the tensors of gdn_inputs(B=1, T=sum)."""
+    gen = _gen(seed)
+    lengths = torch.randint(lo, hi + 1, (n_seqs,), generator=gen)
+    cu = torch.zeros(n_seqs + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lengths, 0).to(torch.int32)
+    T = int(cu[-1])
+    td = DTYPES[dtype]
+    q = _l2n(torch.randn(1, T, H, K, generator=gen)).to(td)
+    k = _l2n(torch.randn(1, T, H, K, generator=gen)).to(td)
+    v = torch.randn(1, T, H, V, generator=gen).to(td)
+    beta = torch.sigmoid(torch.randn(1, T, H, generator=gen))
+    g = torch.nn.functional.logsigmoid(torch.randn(1, T, H, generator=gen) + g_shift)
+    return {"q": q, "k": k, "v": v, "beta": beta, "g": g, "gk": None, "cu_seqlens": cu}
+
+
+def rope_tables(N, D):
+    """Expanded (N, D) fp32 cos / sin tables for theta[n, i] = n * 10000^(-2i/D)."""
+    n = torch.arange(N, dtype=torch.float64)[:, None]
+    i = torch.arange(D // 2, dtype=torch.float64)[None, :]
+    theta = n * torch.pow(10000.0, -2.0 * i / D)
+    c, s = torch.cos(theta), torch.sin(theta)
+    cos_t = c.repeat_interleave(2, dim=-1)
+    sin_t = torch.stack([-s, s], dim=-1).reshape(N, D)
+    return cos_t.float().contiguous(), sin_t.float().contiguous()
+
+
+def bigdn_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
+    """BiGDN block inputs: qkv [B,N,3,H,D] bf16, beta [B,H,F,S], decay [B,H,F], norm weights
+    [H*D] x2, RoPE tables [N,D] x2, k_scale = D^-1/2 * S^-1/2, eps = 1e-5."""
+    gen = _gen(seed)
+    N = F * S
+    qkv = torch.randn(B, N, 3, H, D, generator=gen).to(torch.bfloat16)
+    q_norm_w = 1.0 + 0.1 * torch.randn(H * D, generator=gen)
+    k_norm_w = 1.0 + 0.1 * torch.randn(H * D, generator=gen)
+    beta = torch.sigmoid(torch.randn(B, H, F, S, generator=gen))
+    decay = torch.sigmoid(torch.randn(B, H, F, generator=gen) + decay_shift)
+    rope_cos, rope_sin = rope_tables(N, D)
+    return {"qkv": qkv, "beta": beta, "decay": decay, "q_norm_w": q_norm_w,
+            "k_norm_w": k_norm_w, "rope_cos": rope_cos, "rope_sin": rope_sin,
+            "k_scale": 1.0 / math.sqrt(D) / math.sqrt(S), "eps": 1e-5}
+
+
+# The five workloads, named by what they are.
+WORKLOADS = {
+    "tiny_f32": dict(kind="gdn", B=1, T=256, H=2, K=64, V=64, dtype="f32", seed=0, g_shift=2.0),
+    "gdn_bf16_b4h16t4096": dict(kind="gdn", B=4, T=4096, H=16, K=128, V=128, dtype="bf16",
+                                seed=0, g_shift=3.0),
+    "varlen_bf16_8seq": dict(kind="varlen", n_seqs=8, lo=512, hi=8192, H=16, K=128, V=128,
+                             dtype="bf16", seed=0, g_shift=3.0),
+    "bigdn_video_f16x1024": dict(kind="bigdn", B=1, F=16, S=1024, H=16, D=128, seed=0),
+    "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
+                                    dtype="bf16", seed=0, g_shift=3.0, per_key=True,
+                                    save=True),
+}
+
+
+def make(name):
+    """Materialise a named workload's inputs (CPU tensors)."""
+    w = dict(WORKLOADS[name])
+    kind = w.pop("kind")
+    w.pop("save", None)
+    if kind == "gdn":
+        return gdn_inputs(**w)
+    if kind == "varlen":
+        return varlen_inputs(**w)
+    if kind == "bigdn":
+        return bigdn_inputs(**w)
+    raise KeyError(name)
