@@ -1,0 +1,210 @@
+"""MI355X (gfx950) chunkwise gated delta-rule forward.
+
+The compute path is libgdn.so: hand-written HIP kernels behind the C ABI of include/gdn.h.
+This module is its Python binding, with the same entry-point names.  It only marshals
+arguments: PyTorch supplies device memory (outputs are allocated with ``torch.empty`` on the
+inputs' device) and the current stream; every step of the method runs in the library.
+
+Shapes are checked here before a pointer reaches the library, since raw pointers carry no
+shape; the library itself validates sizes, dtypes and tables.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
+           "gdn_abi_version", "gdn_last_error", "CHUNK"]
+
+CHUNK = 64
+_DT = {torch.float32: _lib.DTYPE_F32, torch.bfloat16: _lib.DTYPE_BF16}
+
+
+def gdn_abi_version() -> int:
+    return _lib.load().gdn_abi_version()
+
+
+def gdn_last_error() -> str:
+    return _lib.last_error()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def gdn_fwd(q, k, v, beta, g=None, gk=None, scale=1.0, h0=None, *, want_ht=True,
+            want_h=False, want_v_new=False):
+    """Dense forward.  q, k [B,T,H,K], v [B,T,H,V] (fp32 or bf16, same dtype), beta / g
+    [B,T,H] fp32, gk [B,T,H,K] fp32, h0 [B,H,K,V] fp32.  Returns a dict with o [B,T,H,V]
+    (input dtype), and ht [B,H,K,V] fp32, h [B,H,NT,K,V] (input dtype), v_new [B,T,H,V]
+    when requested."""
+    if q.dtype not in _DT:
+        raise ValueError("q must be float32 or bfloat16, got %s" % q.dtype)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, T, H, K), dt, dev)
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(gk, "gk", (B, T, H, K), torch.float32, dev)
+    _need(h0, "h0", (B, H, K, V), torch.float32, dev)
+    NT = (T + CHUNK - 1) // CHUNK
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    ht = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if want_ht else None
+    hch = torch.empty(B, H, NT, K, V, dtype=dt, device=dev) if want_h else None
+    vn = torch.empty(B, T, H, V, dtype=dt, device=dev) if want_v_new else None
+    lib = _lib.load()
+    ws_n = lib.gdn_fwd_workspace_bytes(B, T, H, K, V, _DT[dt])
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta), float(scale),
+                     _ptr(h0), _ptr(o), _ptr(ht), _ptr(hch), _ptr(vn), B, T, H, K, V, _DT[dt],
+                     _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "gdn_fwd")
+    out = {"o": o}
+    if want_ht:
+        out["ht"] = ht
+    if want_h:
+        out["h"] = hch
+    if want_v_new:
+        out["v_new"] = vn
+    return out
+
+
+def gdn_varlen_num_chunks(cu_seqlens_host) -> int:
+    cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
+    return _lib.load().gdn_varlen_num_chunks(_ptr(cu), cu.numel() - 1)
+
+
+def gdn_fwd_varlen(q, k, v, beta, cu_seqlens, g=None, gk=None, scale=1.0, h0=None, *,
+                   want_ht=True, want_h=False, want_v_new=False, want_tables=True):
+    """Packed forward (batch 1).  cu_seqlens [N+1] int32 (a device copy is made if it is a
+    host tensor).  Returns o, and ht [N,H,K,V], h [1,H,NT_total,K,V], v_new,
+    chunk_offsets [N+1] and chunk_indices [NT_total,2] (int32) when requested."""
+    if q.dtype not in _DT:
+        raise ValueError("q must be float32 or bfloat16, got %s" % q.dtype)
+    one, T, H, K = q.shape
+    if one != 1:
+        raise ValueError("packed input must have batch 1, got %d" % one)
+    V = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    cu_dev = cu_seqlens.detach().to(dev, torch.int32).contiguous()
+    N = cu_host.numel() - 1
+    _need(q, "q", (1, T, H, K), dt, dev)
+    _need(k, "k", (1, T, H, K), dt, dev)
+    _need(v, "v", (1, T, H, V), dt, dev)
+    _need(beta, "beta", (1, T, H), torch.float32, dev)
+    _need(g, "g", (1, T, H), torch.float32, dev)
+    _need(gk, "gk", (1, T, H, K), torch.float32, dev)
+    _need(h0, "h0", (N, H, K, V), torch.float32, dev)
+    lib = _lib.load()
+    NT = lib.gdn_varlen_num_chunks(_ptr(cu_host), N)
+    if NT < 0:
+        raise ValueError("malformed cu_seqlens: %s" % cu_host.tolist()[:16])
+    o = torch.empty(1, T, H, V, dtype=dt, device=dev)
+    ht = torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if want_ht else None
+    hch = torch.empty(1, H, NT, K, V, dtype=dt, device=dev) if want_h else None
+    vn = torch.empty(1, T, H, V, dtype=dt, device=dev) if want_v_new else None
+    offs = torch.empty(N + 1, dtype=torch.int32, device=dev) if want_tables else None
+    idx = torch.empty(NT, 2, dtype=torch.int32, device=dev) if want_tables else None
+    ws_n = lib.gdn_fwd_varlen_workspace_bytes(T, N, H, K, V, _DT[dt])
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
+                            float(scale), _ptr(cu_dev), _ptr(cu_host), N, _ptr(h0), _ptr(o),
+                            _ptr(ht), _ptr(hch), _ptr(vn), _ptr(offs), _ptr(idx), T, H, K, V,
+                            _DT[dt], _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "gdn_fwd_varlen")
+    out = {"o": o}
+    if want_ht:
+        out["ht"] = ht
+    if want_h:
+        out["h"] = hch
+    if want_v_new:
+        out["v_new"] = vn
+    if want_tables:
+        out["chunk_offsets"] = offs
+        out["chunk_indices"] = idx
+    return out
+
+
+def gdn_prep(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, norm_eps=1e-5, *,
+             outputs=("q_inv_rms", "k_inv_rms", "q_rot", "k_rot", "q_pos", "k_pos", "v")):
+    """BiGDN front end.  qkv [B,N,3,H,D] bf16; weights [H*D] fp32; rope tables [N,D] fp32.
+    Returns the requested outputs: q_inv_rms / k_inv_rms [B,N] fp32 and q_rot, k_rot, q_pos,
+    k_pos, v [B,H,N,D] bf16."""
+    B, N, three, H, D = qkv.shape
+    dev = qkv.device
+    if three != 3:
+        raise ValueError("qkv must be [B,N,3,H,D]")
+    _need(qkv, "qkv", (B, N, 3, H, D), torch.bfloat16, dev)
+    _need(q_norm_w, "q_norm_w", (H * D,), torch.float32, dev)
+    _need(k_norm_w, "k_norm_w", (H * D,), torch.float32, dev)
+    _need(rope_cos, "rope_cos", (N, D), torch.float32, dev)
+    _need(rope_sin, "rope_sin", (N, D), torch.float32, dev)
+    out = {}
+    for name in outputs:
+        if name in ("q_inv_rms", "k_inv_rms"):
+            out[name] = torch.empty(B, N, dtype=torch.float32, device=dev)
+        elif name in ("q_rot", "k_rot", "q_pos", "k_pos", "v"):
+            out[name] = torch.empty(B, H, N, D, dtype=torch.bfloat16, device=dev)
+        else:
+            raise ValueError("unknown prep output %r" % name)
+    rc = _lib.load().gdn_prep(
+        _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(rope_cos), _ptr(rope_sin),
+        float(k_scale), float(norm_eps), _ptr(out.get("q_inv_rms")), _ptr(out.get("k_inv_rms")),
+        _ptr(out.get("q_rot")), _ptr(out.get("k_rot")), _ptr(out.get("q_pos")),
+        _ptr(out.get("k_pos")), _ptr(out.get("v")), B, N, H, D, _stream(dev))
+    _lib.check(rc, "gdn_prep")
+    return out
+
+
+def bigdn_fwd(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale,
+              norm_eps=1e-5):
+    """BiGDN block forward.  qkv [B,N,3,H,D] bf16, beta [B,H,F,S] fp32, decay [B,H,F] fp32.
+    Returns (num [B,N,H,D] bf16, den [B,H,N] bf16), the sums over both directions."""
+    B, N, three, H, D = qkv.shape
+    dev = qkv.device
+    F, S = beta.shape[2], beta.shape[3]
+    if three != 3 or F * S != N:
+        raise ValueError("qkv must be [B,N,3,H,D] with N = F*S")
+    _need(qkv, "qkv", (B, N, 3, H, D), torch.bfloat16, dev)
+    _need(beta, "beta", (B, H, F, S), torch.float32, dev)
+    _need(decay, "decay", (B, H, F), torch.float32, dev)
+    _need(q_norm_w, "q_norm_w", (H * D,), torch.float32, dev)
+    _need(k_norm_w, "k_norm_w", (H * D,), torch.float32, dev)
+    _need(rope_cos, "rope_cos", (N, D), torch.float32, dev)
+    _need(rope_sin, "rope_sin", (N, D), torch.float32, dev)
+    num = torch.empty(B, N, H, D, dtype=torch.bfloat16, device=dev)
+    den = torch.empty(B, H, N, dtype=torch.bfloat16, device=dev)
+    lib = _lib.load()
+    ws_n = lib.bigdn_fwd_workspace_bytes(B, F, S, H, D)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.bigdn_fwd(_ptr(qkv), _ptr(beta), _ptr(decay), _ptr(q_norm_w), _ptr(k_norm_w),
+                       _ptr(rope_cos), _ptr(rope_sin), float(k_scale), float(norm_eps),
+                       _ptr(num), _ptr(den), B, F, S, H, D, _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "bigdn_fwd")
+    return num, den

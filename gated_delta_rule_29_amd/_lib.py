@@ -1,0 +1,70 @@
+"""ctypes loader for libgdn.so (the C ABI declared in include/gdn.h).
+
+The library is built in-tree by ``gated_delta_rule_29_amd.build``.  Loading fails loudly if
+it is missing: there is no fallback implementation of any entry point.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+F = ctypes.c_float
+SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes), mirroring include/gdn.h
+SIGNATURES = {
+    "gdn_abi_version": (I, []),
+    "gdn_last_error": (ctypes.c_char_p, []),
+    "gdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I, I]),
+    "gdn_fwd": (I, [P, P, P, P, P, P, F, P, P, P, P, P, I, I, I, I, I, I, P, SZ, P]),
+    "gdn_varlen_num_chunks": (I, [P, I]),
+    "gdn_fwd_varlen_workspace_bytes": (SZ, [I, I, I, I, I, I]),
+    "gdn_fwd_varlen": (I, [P, P, P, P, P, P, F, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, P,
+                           SZ, P]),
+    "gdn_prep": (I, [P, P, P, P, P, F, F, P, P, P, P, P, P, P, I, I, I, I, P]),
+    "bigdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I]),
+    "bigdn_fwd": (I, [P, P, P, P, P, P, P, F, F, P, P, I, I, I, I, I, P, SZ, P]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libgdn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libgdn.so is not built; run `python -m gated_delta_rule_29_amd.build` "
+                "(there is no non-HIP fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load().gdn_last_error().decode("utf-8", "replace")
+
+
+def check(rc: int, what: str) -> None:
+    """Map a status code to the exception class the pages' wrappers use for it."""
+    if rc == OK:
+        return
+    msg = "%s: %s" % (what, last_error())
+    if rc == ERR_INVALID or rc == ERR_WORKSPACE:
+        raise ValueError(msg)
+    if rc == ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)

@@ -1,0 +1,158 @@
+// gdn_abi.hip -- the extern "C" boundary of libgdn: argument validation, dispatch and error
+// reporting.  Declarations and the contract of every entry point are in include/gdn.h.
+//
+// Argument classes follow the wrappers on the pages (SANA fused_gdn.py page, fused_gdn_func
+// and fused_bigdn_func checks; hyper-parallel "Diff Coverage" page, KDA state validation):
+// malformed input is GDN_ERR_INVALID (their ValueError), valid-but-unimplemented
+// combinations are GDN_ERR_UNSUPPORTED (their NotImplementedError), runtime failures are
+// GDN_ERR_HIP (their RuntimeError).  Validation always completes before any launch.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return GDN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool kv_supported(int dtype, int K, int V, bool per_key) {
+  if (V != 64 && V != 128) return false;
+  if (dtype == GDN_DTYPE_BF16) return (K == 64 || K == 128) && !per_key;
+  return K == 64 && !per_key;
+}
+
+// Checks shared by the dense and packed forward passes.
+int check_fwd_common(const void* q, const void* k, const void* v, const float* beta, const void* o,
+                     const float* gk, int H, int K, int V, int dtype) {
+  if (!q || !k || !v || !beta || !o)
+    return fail(GDN_ERR_INVALID, "q, k, v, beta and o must be non-null device pointers");
+  if (H <= 0 || K <= 0 || V <= 0) return fail(GDN_ERR_INVALID, "H, K, V must be positive (got %d, %d, %d)", H, K, V);
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID, "dtype must be GDN_DTYPE_F32 (0) or GDN_DTYPE_BF16 (1), got %d", dtype);
+  if (!kv_supported(dtype, K, V, gk != nullptr))
+    return fail(GDN_ERR_UNSUPPORTED,
+                "unsupported combination: dtype=%s K=%d V=%d%s (bf16: K,V in {64,128}; fp32: K=64, "
+                "V in {64,128}; per-key gates not available in this build)",
+                dtype == GDN_DTYPE_BF16 ? "bf16" : "f32", K, V, gk ? " with gk" : "");
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_last_error(void) { return g_err; }
+
+size_t gdn_fwd_workspace_bytes(int, int, int, int, int, int) { return 0; }
+
+int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* gk,
+            const float* beta, float scale, const float* h0, void* o, float* ht, void* h_chunks,
+            void* v_new, int B, int T, int H, int K, int V, int dtype, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_fwd_common(q, k, v, beta, o, gk, H, K, V, dtype);
+  if (rc) return rc;
+  if (B <= 0 || T <= 0) return fail(GDN_ERR_INVALID, "B and T must be positive (got %d, %d)", B, T);
+  const int64_t wgs = (int64_t)B * H * (V / 64);
+  if (wgs > INT32_MAX) return fail(GDN_ERR_INVALID, "B*H*(V/64) = %lld exceeds the grid limit", (long long)wgs);
+  gdn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.g = g; p.gk = gk; p.beta = beta; p.h0 = h0;
+  p.o = o; p.ht = ht; p.h_chunks = h_chunks; p.v_new = v_new; p.cu = nullptr;
+  p.scale = scale; p.B = B; p.T = T; p.H = H; p.V = V; p.nvb = V / 64;
+  p.nseq = 0; p.nt_total = 0;
+  hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_fwd launch");
+  return ok();
+}
+
+int gdn_varlen_num_chunks(const int* cu, int N) {
+  if (!cu || N < 1 || cu[0] != 0) return -1;
+  int64_t total = 0;
+  for (int i = 0; i < N; ++i) {
+    const int64_t len = (int64_t)cu[i + 1] - cu[i];
+    if (len <= 0) return -1;
+    total += (len + GDN_CHUNK - 1) / GDN_CHUNK;
+  }
+  return total > INT32_MAX ? -1 : (int)total;
+}
+
+size_t gdn_fwd_varlen_workspace_bytes(int, int, int, int, int, int) { return 0; }
+
+int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                   const float* gk, const float* beta, float scale, const int* cu_seqlens,
+                   const int* cu_seqlens_host, int N, const float* h0, void* o, float* ht,
+                   void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
+                   int T_total, int H, int K, int V, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_fwd_common(q, k, v, beta, o, gk, H, K, V, dtype);
+  if (rc) return rc;
+  if (!cu_seqlens || !cu_seqlens_host)
+    return fail(GDN_ERR_INVALID, "cu_seqlens (device) and cu_seqlens_host must be non-null");
+  if (N < 1 || T_total < 1) return fail(GDN_ERR_INVALID, "N and T_total must be positive (got %d, %d)", N, T_total);
+  if (cu_seqlens_host[0] != 0) return fail(GDN_ERR_INVALID, "cu_seqlens[0] must be 0 (got %d)", cu_seqlens_host[0]);
+  for (int i = 0; i < N; ++i)
+    if (cu_seqlens_host[i + 1] <= cu_seqlens_host[i])
+      return fail(GDN_ERR_INVALID, "cu_seqlens must be strictly increasing (sequence %d is empty or negative)", i);
+  if (cu_seqlens_host[N] != T_total)
+    return fail(GDN_ERR_INVALID, "cu_seqlens[N] = %d differs from T_total = %d", cu_seqlens_host[N], T_total);
+  const int nt = gdn_varlen_num_chunks(cu_seqlens_host, N);
+  if (nt < 0) return fail(GDN_ERR_INVALID, "too many chunks");
+  const int64_t wgs = (int64_t)N * H * (V / 64);
+  if (wgs > INT32_MAX) return fail(GDN_ERR_INVALID, "N*H*(V/64) exceeds the grid limit");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (chunk_offsets || chunk_indices) {
+    hipError_t e = gdn::launch_varlen_tables(cu_seqlens, N, chunk_offsets, chunk_indices, s);
+    if (e != hipSuccess) return hip_fail(e, "varlen table launch");
+  }
+  gdn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.g = g; p.gk = gk; p.beta = beta; p.h0 = h0;
+  p.o = o; p.ht = ht; p.h_chunks = h_chunks; p.v_new = v_new; p.cu = cu_seqlens;
+  p.scale = scale; p.B = 1; p.T = T_total; p.H = H; p.V = V; p.nvb = V / 64;
+  p.nseq = N; p.nt_total = nt;
+  hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, true, s);
+  if (e != hipSuccess) return hip_fail(e, "gdn_fwd_varlen launch");
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int gdn_prep(const void*, const float*, const float*, const float*, const float*, float, float,
+             float*, float*, void*, void*, void*, void*, void*, int, int, int, int, void*) {
+  return fail(GDN_ERR_UNSUPPORTED, "gdn_prep is not available in this build yet");
+}
+
+size_t bigdn_fwd_workspace_bytes(int, int, int, int, int) { return 0; }
+
+int bigdn_fwd(const void*, const float*, const float*, const float*, const float*, const float*,
+              const float*, float, float, void*, void*, int, int, int, int, int, void*, size_t,
+              void*) {
+  return fail(GDN_ERR_UNSUPPORTED, "bigdn_fwd is not available in this build yet");
+}
+
+}  // extern "C"

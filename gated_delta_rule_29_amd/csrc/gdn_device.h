@@ -1,0 +1,110 @@
+// gdn_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Matrix-core conventions (CDNA4, wave64).  Every product here is issued as 16x16 output
+// tiles with a 32-long contraction slice:
+//   - bf16: one v_mfma_f32_16x16x32_bf16;  fp16: one v_mfma_f32_16x16x32_f16;
+//   - fp32: eight v_mfma_f32_16x16x4_f32, instruction j taking element j of each lane.
+// In both cases lane l = 16*lq + li supplies, for the A operand, row li and contraction
+// indices 8*lq .. 8*lq+7 of the slice; for the B operand, column li and the same contraction
+// indices.  The 16x16 fp32 accumulator holds, in lane l, column li and rows 4*lq .. 4*lq+3.
+// (Verified by an in-bounds layout check on gfx950.)  Because the contraction index a lane
+// supplies is the same for A and B, any fixed assignment of real indices to (lq, j) gives
+// the same sum; the kernels use "8*lq + j" throughout so each lane's operand is one
+// contiguous 16- or 32-byte LDS read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  typedef bf16x8 type;
+};
+template <>
+struct Vec8<f16> {
+  typedef f16x8 type;
+};
+template <>
+struct Vec8<float> {
+  typedef f32x8 type;
+};
+
+__device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma16(const f16x8& a, const f16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma16(const f32x8& a, const f32x8& b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  return c;
+}
+
+// One fp32 16x16x4 step (contraction 4), used by the small fp32 products of the solve.
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 8 contiguous elements from LDS (16-byte aligned address).
+__device__ __forceinline__ bf16x8 lds8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f16x8 lds8(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
+__device__ __forceinline__ f32x8 lds8(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T to_t(float x);
+template <>
+__device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }
+template <>
+__device__ __forceinline__ f16 to_t<f16>(float x) { return (f16)x; }
+template <>
+__device__ __forceinline__ float to_t<float>(float x) { return x; }
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(f16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+// Pack a lane's 8 rows of a tile pair (rows 0..3 from accumulator a, 4..7 from b) as an MFMA
+// operand.
+template <typename T>
+__device__ __forceinline__ typename Vec8<T>::type pack8(const f32x4& a, const f32x4& b) {
+  typename Vec8<T>::type r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = to_t<T>(a[j]);
+    r[4 + j] = to_t<T>(b[j]);
+  }
+  return r;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,175 @@
+/*
+ * gdn.h -- C ABI of libgdn, a gfx950 (MI355X) implementation of the chunkwise gated
+ * delta-rule forward pass.
+ *
+ * Method.  Per (batch, head) a K x V state S evolves token by token as
+ *     S_t = diag(a_t) S_{t-1} + k_t d_t^T,  d_t = beta_t (v_t - (diag(a_t) S_{t-1})^T k_t),
+ *     o_t = scale * S_t^T q_t,              a_{t,d} = exp(g_t + gk_{t,d}),
+ * i.e. S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T for a scalar gate.  The
+ * library computes it chunk by chunk (64 tokens): a WY form of each chunk from a unit-lower-
+ * triangular solve, the sequential inter-chunk state pass v_new = u - w h,
+ * h <- diag(e^{g_last}) h + (k * e^{g_last - g})^T v_new (the state-pass fragments of
+ * chunk_gated_delta_rule_fwd_h on the hyper-parallel "Diff Coverage" page), and the masked
+ * intra-chunk output.  The result equals the token recurrence up to rounding.
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers unless the name ends in _host.  The caller owns
+ *    all memory, including any workspace; the library keeps no device allocation between
+ *    calls and has no other global mutable state.
+ *  - Tensors are dense and row-major in the shapes given (no strides).
+ *  - dtype: GDN_DTYPE_F32 (fp32 inputs, fp32 MFMA, fp32 state) or GDN_DTYPE_BF16 (bf16 q/k/v
+ *    and bf16 outputs, bf16 MFMA operands, fp32 accumulation and fp32 state).  Gates (g, gk,
+ *    beta), initial and final states are always fp32.  Gates are natural-log decays: a base-2
+ *    gate x is passed as x * ln 2.
+ *  - stream is a hipStream_t (0 = the null stream).  Calls are asynchronous on that stream
+ *    and never synchronise the device.
+ *  - Every argument is validated on the host before anything is launched; on an error
+ *    nothing is written.  The return value is a status code below, and gdn_last_error()
+ *    returns a message for the calling thread's most recent failure.
+ *  - Results are deterministic: the forward path uses no atomics, so two identical calls
+ *    give bitwise-identical outputs.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define GDN_API __attribute__((visibility("default")))
+#else
+#define GDN_API
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_CHUNK 64
+
+/* Status codes (the pages' wrappers raise ValueError / NotImplementedError / RuntimeError
+ * for these classes, SANA fused_gdn.py page, fused_gdn_func argument checks). */
+#define GDN_OK 0
+#define GDN_ERR_INVALID 1     /* bad pointer, size, shape or table (ValueError)            */
+#define GDN_ERR_UNSUPPORTED 2 /* valid but not implemented combination (NotImplementedError) */
+#define GDN_ERR_WORKSPACE 3   /* workspace missing or smaller than the size query returns   */
+#define GDN_ERR_HIP 4         /* a HIP launch or runtime call failed (RuntimeError)          */
+
+#define GDN_DTYPE_F32 0
+#define GDN_DTYPE_BF16 1
+
+/* ABI version (GDN_ABI_VERSION) of the loaded library. */
+GDN_API int gdn_abi_version(void);
+
+/* Message for the calling thread's most recent failed call ("" if none).  The pointer stays
+ * valid until the thread's next library call. */
+GDN_API const char* gdn_last_error(void);
+
+/*
+ * gdn_fwd -- dense batch forward.
+ *
+ *   q, k      [B, T, H, K]  dtype      queries and keys (the method assumes unit-norm keys for
+ *                                      stability; nothing here enforces it)
+ *   v         [B, T, H, V]  dtype
+ *   g         [B, T, H]     fp32       scalar log decay per token and head; NULL = 0
+ *   gk        [B, T, H, K]  fp32       per-key log decay, added to g in log space (the per-key
+ *                                      gate row-scaling of the state in the Diff Coverage page's
+ *                                      state pass); NULL = none.  bf16 only.
+ *   beta      [B, T, H]     fp32       write strength
+ *   scale                              output scale (o = scale * S^T q)
+ *   h0        [B, H, K, V]  fp32       state at the end of a prefix, before any further decay
+ *                                      (SANA fused_cam_gdn.py page, LOAD_INIT_STATE); NULL = 0
+ *   o         [B, T, H, V]  dtype      output (required)
+ *   ht        [B, H, K, V]  fp32       final state; NULL = not written
+ *   h_chunks  [B, H, NT, K, V] dtype   state entering each chunk, NT = ceil(T / 64),
+ *                                      h_chunks[.., 0, ..] = h0; NULL = not written
+ *   v_new     [B, T, H, V]  dtype      per-token delta d_t = beta_t (v_t - S'^T k_t), the
+ *                                      v_new = u - w h of the state pass; NULL = not written
+ *   workspace, workspace_bytes          at least gdn_fwd_workspace_bytes(...) bytes (0 today;
+ *                                      a NULL workspace is accepted when the size is 0)
+ * Supported: K in {64, 128}, V in {64, 128} for bf16; K = 64 and V in {64, 128} for fp32
+ * (gk is bf16 only).  B, T, H >= 1 and B*H*(V/64) <= 2^31 - 1 (else GDN_ERR_INVALID).
+ */
+GDN_API size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype);
+GDN_API int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* gk,
+            const float* beta, float scale, const float* h0, void* o, float* ht, void* h_chunks,
+            void* v_new, int B, int T, int H, int K, int V, int dtype, void* workspace,
+            size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length batch (batch 1), the IS_VARLEN layout of the state-pass fragments:
+ * sequence i covers tokens [cu[i], cu[i+1]) of [1, T_total, H, .] tensors; the state
+ * (from h0[i] or zero) and the 64-token chunk grid restart at every sequence.
+ *
+ * gdn_varlen_num_chunks: host-only helper, returns sum_i ceil((cu[i+1]-cu[i]) / 64) for a
+ * HOST array of N+1 offsets, or -1 if cu is malformed (cu[0] != 0, a sequence is empty, or
+ * N < 1).
+ */
+GDN_API int gdn_varlen_num_chunks(const int* cu_seqlens_host, int N);
+
+GDN_API size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype);
+
+/*
+ *   cu_seqlens       [N+1] int32 device   offsets, cu[0] = 0, strictly increasing,
+ *                                          cu[N] = T_total (copied from cu_seqlens_host)
+ *   cu_seqlens_host  [N+1] int32 host     the same offsets; validated and used for sizing
+ *   h0, ht           [N, H, K, V] fp32    per-sequence initial / final state (nullable)
+ *   h_chunks         [1, H, NT_total, K, V] dtype; chunk c of sequence i at index
+ *                                          chunk_offsets[i] + c (nullable)
+ *   chunk_offsets    [N+1] int32 device   OUT: chunks before sequence i (nullable)
+ *   chunk_indices    [NT_total, 2] int32  OUT: (sequence, chunk within sequence) per chunk
+ *                                          in order (nullable)
+ * Other arguments as in gdn_fwd with B = 1 and T = T_total.
+ */
+GDN_API int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                   const float* gk, const float* beta, float scale, const int* cu_seqlens,
+                   const int* cu_seqlens_host, int N, const float* h0, void* o, float* ht,
+                   void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
+                   int T_total, int H, int K, int V, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_prep -- BiGDN front end (SANA fused_gdn.py page: _fused_qk_inv_rms_kernel,
+ * prepare_rope_tables and the load path of _fused_gdn_kernel):
+ *   inv_rms[b,n] = 1 / sqrt(sum_{c < H*D} x[b,n,c]^2 / (H*D) + norm_eps)   for q and for k
+ *   x_hat = x * inv_rms * w[h*D + d];  q_pos = relu(q_hat);  k_pos = relu(k_hat) * k_scale
+ *   x_rot[d] = x_pos[d] * cos[n,d] + x_pos[d^1] * sin[n,d]
+ *
+ *   qkv                [B, N, 3, H, D] bf16
+ *   q_norm_w, k_norm_w [H*D] fp32
+ *   rope_cos, rope_sin [N, D] fp32     expanded tables (sin[2i] = -sin, sin[2i+1] = +sin)
+ *   q_inv_rms, k_inv_rms [B, N] fp32   OUT (nullable)
+ *   q_rot, k_rot, q_pos, k_pos, v_hm   [B, H, N, D] bf16 OUT, head-major (each nullable)
+ * Supported: D in {64, 128}, H*D <= 4096.
+ */
+GDN_API int gdn_prep(const void* qkv, const float* q_norm_w, const float* k_norm_w,
+             const float* rope_cos, const float* rope_sin, float k_scale, float norm_eps,
+             float* q_inv_rms, float* k_inv_rms, void* q_rot, void* k_rot, void* q_pos,
+             void* k_pos, void* v_hm, int B, int N, int H, int D, void* stream);
+
+/*
+ * bigdn_fwd -- frame-level bidirectional GDN block forward (SANA fused_gdn.py page,
+ * _fused_gdn_kernel run forward and REVERSE, summed as in fused_bigdn_func).  N = F * S
+ * tokens form F frames of S tokens; every token of a frame reads the same decayed state.
+ * Forward, per frame f: S,z *= decay[f]; S += K_rot^T (beta (V - K_rot S)),
+ * z += K_pos^T (beta (1 - K_pos z)) (both from the decayed pre-update state);
+ * num = Q_rot S, den = Q_pos . z.  Reverse: frame f reads the state built from frames > f
+ * (flip-and-shift, SANA fused_cam_gdn.py page).  Returned: the sums of both directions.
+ *
+ *   qkv     [B, N, 3, H, D] bf16;  beta [B, H, F, S] fp32;  decay [B, H, F] fp32 in (0, 1]
+ *   q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, norm_eps   as in gdn_prep
+ *   num     [B, N, H, D] bf16 OUT;  den [B, H, N] bf16 OUT
+ *   workspace  at least bigdn_fwd_workspace_bytes(B, F, S, H, D) bytes, 256-byte aligned
+ * Supported: D in {64, 128}, S a multiple of 64, H*D <= 4096.
+ */
+GDN_API size_t bigdn_fwd_workspace_bytes(int B, int F, int S, int H, int D);
+GDN_API int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const float* q_norm_w,
+              const float* k_norm_w, const float* rope_cos, const float* rope_sin,
+              float k_scale, float norm_eps, void* num, void* den, int B, int F, int S, int H,
+              int D, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,95 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments before launching anything (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from gated_delta_rule_29_amd import _lib as L
+
+    return L, L.load()
+
+
+def _declared():
+    names = []
+    for path in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if path.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", path)).read()
+            names += re.findall(r"GDN_API\s+[\w\s\*]+?\b((?:gdn|bigdn)_\w+)\s*\(", src)
+    return names
+
+
+def test_exports_every_declared_symbol():
+    L, lib = _lib()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, "binding lacks %s" % n
+    assert lib.gdn_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=None, gk=None, beta=FAKE, scale=1.0, h0=None, o=FAKE,
+             ht=None, hch=None, vn=None, B=1, T=64, H=2, K=128, V=128, dtype=1)
+    a.update(kw)
+    return lib.gdn_fwd(a["q"], a["k"], a["v"], a["g"], a["gk"], a["beta"], a["scale"], a["h0"],
+                       a["o"], a["ht"], a["hch"], a["vn"], a["B"], a["T"], a["H"], a["K"], a["V"],
+                       a["dtype"], None, 0, None)
+
+
+def test_fwd_validation_codes():
+    L, lib = _lib()
+    assert _fwd(lib, q=None) == L.ERR_INVALID
+    assert "non-null" in L.last_error()
+    assert _fwd(lib, T=0) == L.ERR_INVALID
+    assert _fwd(lib, B=-1) == L.ERR_INVALID
+    assert _fwd(lib, dtype=7) == L.ERR_INVALID
+    assert _fwd(lib, K=32) == L.ERR_UNSUPPORTED
+    assert _fwd(lib, V=96) == L.ERR_UNSUPPORTED
+    assert _fwd(lib, dtype=0, K=128) == L.ERR_UNSUPPORTED
+    assert _fwd(lib, B=1 << 20, H=1 << 12) == L.ERR_INVALID  # grid too large
+
+
+def test_varlen_num_chunks():
+    L, lib = _lib()
+    cu = np.array([0, 1, 64, 65, 300], np.int32)
+    p = cu.ctypes.data_as(ctypes.c_void_p)
+    assert lib.gdn_varlen_num_chunks(p, 4) == 1 + 1 + 1 + 4
+    bad = np.array([0, 5, 5], np.int32)
+    assert lib.gdn_varlen_num_chunks(bad.ctypes.data_as(ctypes.c_void_p), 2) == -1
+    bad = np.array([2, 5], np.int32)
+    assert lib.gdn_varlen_num_chunks(bad.ctypes.data_as(ctypes.c_void_p), 1) == -1
+
+
+def test_varlen_validation_codes():
+    L, lib = _lib()
+
+    def call(cu, N, T_total):
+        cu = np.asarray(cu, np.int32)
+        return lib.gdn_fwd_varlen(FAKE, FAKE, FAKE, None, None, FAKE, 1.0, FAKE,
+                                  cu.ctypes.data_as(ctypes.c_void_p), N, None, FAKE, None, None,
+                                  None, None, None, T_total, 2, 128, 128, 1, None, 0, None)
+
+    assert call([0, 10, 10, 20], 3, 20) == L.ERR_INVALID  # empty sequence
+    assert call([1, 10, 20], 2, 20) == L.ERR_INVALID  # does not start at 0
+    assert call([0, 10, 20], 2, 21) == L.ERR_INVALID  # last offset != T_total
+    assert call([0, 10, 20], 0, 20) == L.ERR_INVALID  # no sequences
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from gated_delta_rule_29_amd import _lib as L
+
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        L.load()

@@ -1,0 +1,122 @@
+"""GPU parity of gdn_fwd (dense) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, assert_close, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _gpu():
+    import gated_delta_rule_29_amd as g
+    return g
+
+
+def _to(d, dev=DEV):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def _run_and_check(inp, scale=1.0, h0=None, want_h=False, want_vnew=False, label=""):
+    g = _gpu()
+    dt = inp["q"].dtype
+    say("case %s: q %s %s" % (label, tuple(inp["q"].shape), dt))
+    d = _to(inp)
+    h0d = None if h0 is None else h0.to(DEV)
+    out = g.gdn_fwd(d["q"], d["k"], d["v"], d["beta"], g=d["g"], gk=d["gk"], scale=scale,
+                    h0=h0d, want_h=want_h, want_v_new=want_vnew)
+    torch.cuda.synchronize()
+    ref = oracle.gdn(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"], gk=inp["gk"],
+                     scale=scale, h0=h0, want_h=want_h, want_vnew=want_vnew)
+    tol = TOL[dt]
+    assert_close("o", out["o"], ref["o"], tol)
+    assert_close("ht", out["ht"], ref["ht"], tol)
+    if want_h:
+        assert_close("h", out["h"], ref["h"], tol)
+    if want_vnew:
+        assert_close("v_new", out["v_new"], ref["v_new"], tol)
+    return out
+
+
+def test_tiny_f32_workload():
+    """B=1 H=2 T=256 K=V=64 fp32, seed 0 (the small fp32 workload), every element."""
+    inp = workloads.make("tiny_f32")
+    _run_and_check(inp, want_h=True, want_vnew=True, label="tiny_f32")
+
+
+@pytest.mark.parametrize("dtype,K,V,T", [("bf16", 128, 128, 200), ("bf16", 64, 128, 131),
+                                         ("bf16", 128, 64, 64), ("bf16", 64, 64, 1),
+                                         ("f32", 64, 128, 190), ("f32", 64, 64, 63)])
+def test_shapes_ragged(dtype, K, V, T):
+    inp = workloads.gdn_inputs(2, T, 3, K, V, dtype=dtype, seed=T + K, g_shift=2.0)
+    h0 = torch.randn(2, 3, K, V, generator=torch.Generator().manual_seed(1)) * 0.3
+    _run_and_check(inp, scale=0.5, h0=h0, want_h=True, want_vnew=True,
+                   label="%s K%d V%d T%d" % (dtype, K, V, T))
+
+
+def test_beta_zero_exact():
+    """beta = 0 from a zero state: the GPU path must return exact zeros."""
+    g = _gpu()
+    inp = _to(workloads.gdn_inputs(1, 150, 2, 128, 128, dtype="bf16", seed=3))
+    out = g.gdn_fwd(inp["q"], inp["k"], inp["v"], torch.zeros_like(inp["beta"]), g=inp["g"],
+                    want_h=True, want_v_new=True)
+    torch.cuda.synchronize()
+    for name in ("o", "ht", "h", "v_new"):
+        assert torch.count_nonzero(out[name]).item() == 0, name
+
+
+def test_no_gate_and_strong_decay():
+    """g = None (no decay) and a strongly decaying gate both stay within tolerance."""
+    inp = workloads.gdn_inputs(1, 257, 2, 128, 128, dtype="bf16", seed=4, g_shift=3.0)
+    inp["g"] = None
+    _run_and_check(inp, label="no gate")
+    inp = workloads.gdn_inputs(1, 257, 2, 128, 128, dtype="bf16", seed=5, g_shift=-2.0)
+    _run_and_check(inp, label="strong decay")
+
+
+def test_deterministic():
+    g = _gpu()
+    inp = _to(workloads.gdn_inputs(2, 300, 4, 128, 128, dtype="bf16", seed=6))
+    a = g.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"])
+    b = g.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"])
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["ht"], b["ht"])
+
+
+def test_split_resume_on_gpu():
+    """Feeding ht of [0, T1) as h0 of [T1, T) matches the one-shot oracle run."""
+    g = _gpu()
+    inp = workloads.gdn_inputs(1, 320, 2, 128, 128, dtype="bf16", seed=7)
+    d = _to(inp)
+    T1 = 128
+    a = g.gdn_fwd(d["q"][:, :T1].contiguous(), d["k"][:, :T1].contiguous(),
+                  d["v"][:, :T1].contiguous(), d["beta"][:, :T1].contiguous(),
+                  g=d["g"][:, :T1].contiguous())
+    b = g.gdn_fwd(d["q"][:, T1:].contiguous(), d["k"][:, T1:].contiguous(),
+                  d["v"][:, T1:].contiguous(), d["beta"][:, T1:].contiguous(),
+                  g=d["g"][:, T1:].contiguous(), h0=a["ht"])
+    torch.cuda.synchronize()
+    ref = oracle.gdn(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"])
+    assert_close("o", torch.cat([a["o"], b["o"]], 1), ref["o"], TOL[torch.bfloat16])
+    assert_close("ht", b["ht"], ref["ht"], TOL[torch.bfloat16])
+
+
+def test_full_bf16_workload():
+    """B=4 H=16 T=4096 K=V=128 bf16 (the benchmarked workload): every element of o and ht
+    against the oracle, in the launch configuration the benchmark times."""
+    inp = workloads.make("gdn_bf16_b4h16t4096")
+    _run_and_check(inp, label="gdn_bf16_b4h16t4096")
+
+
+def test_invalid_arguments_raise():
+    g = _gpu()
+    inp = _to(workloads.gdn_inputs(1, 64, 2, 128, 128, dtype="bf16", seed=8))
+    with pytest.raises(ValueError):
+        g.gdn_fwd(inp["q"], inp["k"], inp["v"][..., :64].contiguous(), inp["beta"][:, :32])
+    with pytest.raises(NotImplementedError):
+        q = inp["q"][..., :32].contiguous()
+        g.gdn_fwd(q, q, inp["v"], inp["beta"])
