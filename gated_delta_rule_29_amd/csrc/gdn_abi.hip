@@ -140,19 +140,105 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
 
 }  // extern "C"
 
-extern "C" {
+namespace {
 
-int gdn_prep(const void*, const float*, const float*, const float*, const float*, float, float,
-             float*, float*, void*, void*, void*, void*, void*, int, int, int, int, void*) {
-  return fail(GDN_ERR_UNSUPPORTED, "gdn_prep is not available in this build yet");
+// bigdn_fwd workspace: every view 256-byte aligned, in the order of BigdnParams.
+struct BigdnWs {
+  size_t q_rms, k_rms, G, Gz, U, uz, Sf, SsumT, zsum, total;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BigdnWs bigdn_ws(int B, int F, int S, int H, int D) {
+  BigdnWs w{};
+  const size_t N = (size_t)F * S, mats = (size_t)B * H * F * D * D, vecs = (size_t)B * H * F * D;
+  size_t off = 0;
+  w.q_rms = off; off = al256(off + (size_t)B * N * 4);
+  w.k_rms = off; off = al256(off + (size_t)B * N * 4);
+  w.G = off; off = al256(off + mats * 2);
+  w.Gz = off; off = al256(off + mats * 2);
+  w.U = off; off = al256(off + mats * 4);
+  w.uz = off; off = al256(off + vecs * 4);
+  w.Sf = off; off = al256(off + mats * 4);
+  w.SsumT = off; off = al256(off + mats * 2);
+  w.zsum = off; off = al256(off + vecs * 4);
+  w.total = off;
+  return w;
 }
 
-size_t bigdn_fwd_workspace_bytes(int, int, int, int, int) { return 0; }
+int check_bigdn_dims(int B, int N, int H, int D) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0)
+    return fail(GDN_ERR_INVALID, "B, N, H, D must be positive (got %d, %d, %d, %d)", B, N, H, D);
+  if (D % 2) return fail(GDN_ERR_INVALID, "D must be even (RoPE pairs), got %d", D);
+  if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
+  if ((int64_t)H * D > 4096) return fail(GDN_ERR_UNSUPPORTED, "H*D must be <= 4096, got %d", H * D);
+  if ((int64_t)B * N > INT32_MAX) return fail(GDN_ERR_INVALID, "B*N exceeds the grid limit");
+  return GDN_OK;
+}
 
-int bigdn_fwd(const void*, const float*, const float*, const float*, const float*, const float*,
-              const float*, float, float, void*, void*, int, int, int, int, int, void*, size_t,
-              void*) {
-  return fail(GDN_ERR_UNSUPPORTED, "bigdn_fwd is not available in this build yet");
+}  // namespace
+
+extern "C" {
+
+int gdn_prep(const void* qkv, const float* q_norm_w, const float* k_norm_w,
+             const float* rope_cos, const float* rope_sin, float k_scale, float norm_eps,
+             float* q_inv_rms, float* k_inv_rms, void* q_rot, void* k_rot, void* q_pos,
+             void* k_pos, void* v_hm, int B, int N, int H, int D, void* stream) {
+  if (!qkv || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin)
+    return fail(GDN_ERR_INVALID, "qkv, norm weights and RoPE tables must be non-null");
+  int rc = check_bigdn_dims(B, N, H, D);
+  if (rc) return rc;
+  if (!(norm_eps > 0.f)) return fail(GDN_ERR_INVALID, "norm_eps must be positive");
+  gdn::PrepParams p{};
+  p.qkv = qkv; p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w; p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin; p.k_scale = k_scale; p.eps = norm_eps; p.q_inv_rms = q_inv_rms;
+  p.k_inv_rms = k_inv_rms; p.q_rot = q_rot; p.k_rot = k_rot; p.q_pos = q_pos; p.k_pos = k_pos;
+  p.v_hm = v_hm; p.B = B; p.N = N; p.H = H; p.D = D;
+  hipError_t e = gdn::launch_prep(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_prep launch");
+  return ok();
+}
+
+size_t bigdn_fwd_workspace_bytes(int B, int F, int S, int H, int D) {
+  if (B <= 0 || F <= 0 || S <= 0 || H <= 0 || D <= 0) return 0;
+  return bigdn_ws(B, F, S, H, D).total;
+}
+
+int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const float* q_norm_w,
+              const float* k_norm_w, const float* rope_cos, const float* rope_sin,
+              float k_scale, float norm_eps, void* num, void* den, int B, int F, int S, int H,
+              int D, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!qkv || !beta || !decay || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin || !num || !den)
+    return fail(GDN_ERR_INVALID, "qkv, beta, decay, norm weights, RoPE tables, num and den must be non-null");
+  if (F <= 0 || S <= 0) return fail(GDN_ERR_INVALID, "F and S must be positive (got %d, %d)", F, S);
+  if ((int64_t)F * S > INT32_MAX) return fail(GDN_ERR_INVALID, "F*S too large");
+  const int N = F * S;
+  int rc = check_bigdn_dims(B, N, H, D);
+  if (rc) return rc;
+  if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
+  if (!(norm_eps > 0.f)) return fail(GDN_ERR_INVALID, "norm_eps must be positive");
+  const BigdnWs w = bigdn_ws(B, F, S, H, D);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", w.total, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  gdn::BigdnParams p{};
+  p.qkv = qkv; p.beta = beta; p.decay = decay; p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w;
+  p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.k_scale = k_scale; p.eps = norm_eps;
+  p.num = num; p.den = den; p.B = B; p.F = F; p.S = S; p.H = H; p.D = D; p.N = N;
+  p.q_inv_rms = reinterpret_cast<float*>(ws + w.q_rms);
+  p.k_inv_rms = reinterpret_cast<float*>(ws + w.k_rms);
+  p.G = reinterpret_cast<_Float16*>(ws + w.G);
+  p.Gz = reinterpret_cast<_Float16*>(ws + w.Gz);
+  p.U = reinterpret_cast<float*>(ws + w.U);
+  p.uz = reinterpret_cast<float*>(ws + w.uz);
+  p.Sf = reinterpret_cast<float*>(ws + w.Sf);
+  p.SsumT = reinterpret_cast<_Float16*>(ws + w.SsumT);
+  p.zsum = reinterpret_cast<float*>(ws + w.zsum);
+  hipError_t e = gdn::launch_bigdn(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bigdn_fwd launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -29,3 +29,51 @@ hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hip
 hipError_t launch_varlen_tables(const int* cu, int N, int* offs, int* idx, hipStream_t stream);
 
 }  // namespace gdn
+
+namespace gdn {
+
+struct PrepParams {
+  const void* qkv;  // [B, N, 3, H, D] bf16
+  const float* q_norm_w;
+  const float* k_norm_w;
+  const float* rope_cos;
+  const float* rope_sin;
+  float k_scale, eps;
+  float* q_inv_rms;  // [B, N] or nullptr
+  float* k_inv_rms;
+  void* q_rot;  // [B, H, N, D] bf16 outputs, each nullable
+  void* k_rot;
+  void* q_pos;
+  void* k_pos;
+  void* v_hm;
+  int B, N, H, D;
+};
+
+struct BigdnParams {
+  const void* qkv;
+  const float* beta;   // [B, H, F, S]
+  const float* decay;  // [B, H, F]
+  const float* q_norm_w;
+  const float* k_norm_w;
+  const float* rope_cos;
+  const float* rope_sin;
+  float k_scale, eps;
+  void* num;  // [B, N, H, D] bf16
+  void* den;  // [B, H, N] bf16
+  int B, F, S, H, D, N;
+  // workspace views
+  float* q_inv_rms;  // [B, N]
+  float* k_inv_rms;  // [B, N]
+  _Float16* G;       // [B, H, F, D, D]
+  _Float16* Gz;      // [B, H, F, D, D]
+  float* U;          // [B, H, F, D, D]
+  float* uz;         // [B, H, F, D]
+  float* Sf;         // [B, H, F, D, D]  forward states
+  _Float16* SsumT;   // [B, H, F, D, D]  (S_f + R_f)^T
+  float* zsum;       // [B, H, F, D]
+};
+
+hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
+hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream);
+
+}  // namespace gdn
