@@ -36,7 +36,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool kv_supported(int dtype, int K, int V, bool per_key) {
   if (V != 64 && V != 128) return false;
-  if (dtype == GDN_DTYPE_BF16) return (K == 64 || K == 128) && !per_key;
+  if (dtype == GDN_DTYPE_BF16) return K == 64 || K == 128;
   return K == 64 && !per_key;
 }
 
@@ -51,7 +51,7 @@ int check_fwd_common(const void* q, const void* k, const void* v, const float* b
   if (!kv_supported(dtype, K, V, gk != nullptr))
     return fail(GDN_ERR_UNSUPPORTED,
                 "unsupported combination: dtype=%s K=%d V=%d%s (bf16: K,V in {64,128}; fp32: K=64, "
-                "V in {64,128}; per-key gates not available in this build)",
+                "V in {64,128}, no per-key gate)",
                 dtype == GDN_DTYPE_BF16 ? "bf16" : "f32", K, V, gk ? " with gk" : "");
   return GDN_OK;
 }

@@ -26,6 +26,8 @@
 // 32G + 8(i/4) + 4t + i%4), which makes the state directly usable as the B operand of the
 // next chunk's K h / Q h products with no data movement.  Token-indexed results (X_K, v_new,
 // o) use the same mapping over tokens, so v_new feeds P v_new and K^T v_new directly too.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -62,16 +64,25 @@ __device__ __forceinline__ int pair_row(int G, int t, int li) {
   return 32 * G + 8 * (li >> 2) + 4 * t + (li & 3);
 }
 
-template <typename TI, int K>
+// Type of the q / k tiles: the inputs as given for a scalar gate; for a per-key gate they
+// hold the decay-scaled operands, so they take the intra-chunk operand type.
+template <typename TI, bool PK>
+struct QKT {
+  typedef typename std::conditional<PK, typename OpT<TI>::type, TI>::type type;
+};
+
+template <typename TI, int K, bool PK>
 struct __attribute__((aligned(16))) Smem {
   typedef typename OpT<TI>::type TO;
+  typedef typename QKT<TI, PK>::type TQ;
   static constexpr int kE = Pad<TI>::kE;
   static constexpr int kKP = K + kE;    // row stride of [token][key] tiles
   static constexpr int kTP = kC + kE;   // row stride of [.][token] tiles
   static constexpr int kAP = kC + 4;    // row stride of the fp32 solve buffer
-  TI q[kC][kKP];
-  TI k[kC][kKP];
-  TO kt[K][kTP];
+  TQ q[kC][kKP];    // Q, or per-key gate: Q * e^{gamma - gamma_mid}
+  TQ k[kC][kKP];    // K, or per-key gate: K * e^{gamma - gamma_mid}
+  TQ kb[PK ? kC : 1][kKP];  // per-key gate: K * e^{gamma_mid - gamma}
+  TO kt[K][kTP];    // K^T, or per-key gate: (K * e^{gamma_last - gamma})^T
   TI vt[kBV][kTP];
   TO tm[kC][kTP];   // (I + A)^-1 as MFMA operand (bf16 path)
   TO p[kC][kTP];    // masked decayed Q K^T
@@ -79,31 +90,39 @@ struct __attribute__((aligned(16))) Smem {
   float x[32][36];  // fp32 scratch of the solve's last merge
   float gam[kC], eg[kC], el[kC], beta[kC];
   float egl;
+  // per-key gate: e^{gamma_mid}, e^{gamma_last} per key, and the cumsum exchange
+  float emid[PK ? K : 1], eglk[PK ? K : 1], gpart[PK ? kThreads / K : 1][PK ? K : 1];
+  float gmid[PK ? K : 1], glast[PK ? K : 1];
 };
 
 // Global -> register staging of one chunk, 16 bytes per load.
-template <typename TI, int K>
+template <typename TI, int K, bool PK>
 struct Stage {
   static constexpr int kE = Pad<TI>::kE;
   static constexpr int kCPR = K / kE;                  // 16-byte chunks per q/k row
   static constexpr int kNQ = kC * kCPR / kThreads;     // per thread, per tensor
   static constexpr int kVPR = kBV / kE;                // 16-byte chunks per v row block
   static constexpr int kNV = kC * kVPR / kThreads;
+  // per-key gate: thread tid owns key tid % K and kGT consecutive tokens
+  static constexpr int kTPK = kThreads / K;
+  static constexpr int kGT = kC / kTPK;
   uint4 q[kNQ], k[kNQ], v[kNV];
   float g, beta;
+  float gk[PK ? kGT : 1];
 };
 
-template <typename TI, int K>
-__device__ __forceinline__ void load_chunk(Stage<TI, K>& st, const FwdParams& p, long tok0,
+template <typename TI, int K, bool PK>
+__device__ __forceinline__ void load_chunk(Stage<TI, K, PK>& st, const FwdParams& p, long tok0,
                                            int h, int t0, int len, int v0, int tid) {
+  typedef Stage<TI, K, PK> St;
   constexpr int kE = Pad<TI>::kE;
   const TI* q = static_cast<const TI*>(p.q);
   const TI* k = static_cast<const TI*>(p.k);
   const TI* v = static_cast<const TI*>(p.v);
 #pragma unroll
-  for (int i = 0; i < Stage<TI, K>::kNQ; ++i) {
+  for (int i = 0; i < St::kNQ; ++i) {
     const int c = tid + kThreads * i;
-    const int row = c / Stage<TI, K>::kCPR, cc = c % Stage<TI, K>::kCPR;
+    const int row = c / St::kCPR, cc = c % St::kCPR;
     const int t = t0 + row;
     uint4 zq = make_uint4(0, 0, 0, 0), zk = zq;
     if (t < len) {
@@ -115,9 +134,9 @@ __device__ __forceinline__ void load_chunk(Stage<TI, K>& st, const FwdParams& p,
     st.k[i] = zk;
   }
 #pragma unroll
-  for (int i = 0; i < Stage<TI, K>::kNV; ++i) {
+  for (int i = 0; i < St::kNV; ++i) {
     const int c = tid + kThreads * i;
-    const int row = c / Stage<TI, K>::kVPR, cc = c % Stage<TI, K>::kVPR;
+    const int row = c / St::kVPR, cc = c % St::kVPR;
     const int t = t0 + row;
     uint4 z = make_uint4(0, 0, 0, 0);
     if (t < len) z = *reinterpret_cast<const uint4*>(v + ((tok0 + t) * p.H + h) * (long)p.V + v0 + cc * kE);
@@ -133,26 +152,46 @@ __device__ __forceinline__ void load_chunk(Stage<TI, K>& st, const FwdParams& p,
       st.beta = p.beta[gi];
     }
   }
+  if constexpr (PK) {
+    const int d = tid % K, t1 = (tid / K) * St::kGT;
+#pragma unroll
+    for (int i = 0; i < St::kGT; ++i) {
+      const int t = t0 + t1 + i;
+      st.gk[i] = t < len ? p.gk[((tok0 + t) * p.H + h) * (long)K + d] : 0.f;
+    }
+  }
 }
 
-template <typename TI, int K>
-__device__ __forceinline__ void store_chunk(const Stage<TI, K>& st, Smem<TI, K>& s, int tid) {
+template <typename TI, int K, bool PK>
+__device__ __forceinline__ void store_chunk(const Stage<TI, K, PK>& st, Smem<TI, K, PK>& s, int tid) {
   typedef typename OpT<TI>::type TO;
+  typedef Stage<TI, K, PK> St;
   constexpr int kE = Pad<TI>::kE;
 #pragma unroll
-  for (int i = 0; i < Stage<TI, K>::kNQ; ++i) {
+  for (int i = 0; i < St::kNQ; ++i) {
     const int c = tid + kThreads * i;
-    const int row = c / Stage<TI, K>::kCPR, cc = c % Stage<TI, K>::kCPR;
-    *reinterpret_cast<uint4*>(&s.q[row][cc * kE]) = st.q[i];
-    *reinterpret_cast<uint4*>(&s.k[row][cc * kE]) = st.k[i];
-    const TI* e = reinterpret_cast<const TI*>(&st.k[i]);
+    const int row = c / St::kCPR, cc = c % St::kCPR;
+    if constexpr (PK) {
+      // raw q / k converted to the operand type; the scaling pass rescales them in place
+      const TI* eq = reinterpret_cast<const TI*>(&st.q[i]);
+      const TI* ek = reinterpret_cast<const TI*>(&st.k[i]);
 #pragma unroll
-    for (int j = 0; j < kE; ++j) s.kt[cc * kE + j][row] = to_t<TO>(to_f(e[j]));
+      for (int j = 0; j < kE; ++j) {
+        s.q[row][cc * kE + j] = to_t<TO>(to_f(eq[j]));
+        s.k[row][cc * kE + j] = to_t<TO>(to_f(ek[j]));
+      }
+    } else {
+      *reinterpret_cast<uint4*>(&s.q[row][cc * kE]) = st.q[i];
+      *reinterpret_cast<uint4*>(&s.k[row][cc * kE]) = st.k[i];
+      const TI* e = reinterpret_cast<const TI*>(&st.k[i]);
+#pragma unroll
+      for (int j = 0; j < kE; ++j) s.kt[cc * kE + j][row] = to_t<TO>(to_f(e[j]));
+    }
   }
 #pragma unroll
-  for (int i = 0; i < Stage<TI, K>::kNV; ++i) {
+  for (int i = 0; i < St::kNV; ++i) {
     const int c = tid + kThreads * i;
-    const int row = c / Stage<TI, K>::kVPR, cc = c % Stage<TI, K>::kVPR;
+    const int row = c / St::kVPR, cc = c % St::kVPR;
     const TI* e = reinterpret_cast<const TI*>(&st.v[i]);
 #pragma unroll
     for (int j = 0; j < kE; ++j) s.vt[cc * kE + j][row] = e[j];
@@ -172,8 +211,8 @@ __device__ __forceinline__ void tri_tile(int idx, int& I, int& J) {
 // (I + A)^-1 for the strictly lower 64x64 A held in s.a, in place, fp32.  Diagonal 16x16
 // blocks by forward substitution, then blocks merged with
 //   T_hi,lo = -T_hi,hi A_hi,lo T_lo,lo       (first for 16-blocks, then for 32-blocks).
-template <typename TI, int K>
-__device__ __forceinline__ void solve_unit_lower(Smem<TI, K>& s, int wave, int lane) {
+template <typename SM>
+__device__ __forceinline__ void solve_unit_lower(SM& s, int wave, int lane) {
   const int li = lane & 15, lq = lane >> 4;
   if (wave == 0) {
     // lane -> (block b = lq, column c = li): forward substitution down column c.
@@ -236,13 +275,17 @@ __device__ __forceinline__ void solve_unit_lower(Smem<TI, K>& s, int wave, int l
   __syncthreads();
 }
 
-template <typename TI, int K, bool VARLEN>
+template <typename TI, int K, bool VARLEN, bool PK>
 __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
   typedef typename OpT<TI>::type TO;
+  typedef typename QKT<TI, PK>::type TQ;
   typedef typename Vec8<TI>::type V8;
   typedef typename Vec8<TO>::type W8;
+  typedef typename Vec8<TQ>::type Q8;
+  typedef Smem<TI, K, PK> SM;
+  typedef Stage<TI, K, PK> St;
   constexpr int kG = K / 32;  // key groups of 32
-  __shared__ Smem<TI, K> s;
+  __shared__ SM s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
@@ -295,8 +338,8 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
       for (int e = 0; e < 4; ++e)
         hs[G][t][e] = p.h0 ? p.h0[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] : 0.f;
 
-  Stage<TI, K> st;
-  load_chunk<TI, K>(st, p, tok0, h, 0, len, v0, tid);
+  St st;
+  load_chunk<TI, K, PK>(st, p, tok0, h, 0, len, v0, tid);
 
   TI* o = static_cast<TI*>(p.o);
   TI* vnew_out = static_cast<TI*>(p.v_new);
@@ -304,12 +347,54 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
 
   for (int n = 0; n < nchunks; ++n) {
     const int t0 = n * kC;
-    store_chunk<TI, K>(st, s, tid);
+    store_chunk<TI, K, PK>(st, s, tid);
+    float gkl[PK ? St::kGT : 1];  // this chunk's per-key log decays (before the prefetch reuses st)
+    if constexpr (PK) {
+#pragma unroll
+      for (int i = 0; i < St::kGT; ++i) gkl[i] = st.gk[i];
+    }
     __syncthreads();
-    if (n + 1 < nchunks) load_chunk<TI, K>(st, p, tok0, h, t0 + kC, len, v0, tid);
+    if (n + 1 < nchunks) load_chunk<TI, K, PK>(st, p, tok0, h, t0 + kC, len, v0, tid);
 
-    // ---- chunk-local cumulative gate and its exponentials
-    if (wave == 0) {
+    if constexpr (PK) {
+      // ---- per-key cumulative gate gamma[t][d] = sum_{i<=t} (g_i + gk_{i,d}) and the
+      // decay-scaled operands.  Thread tid owns key d = tid % K and tokens t1..t1+kGT-1.
+      const int d = tid % K, part = tid / K, t1 = part * St::kGT;
+      float gam[St::kGT];
+      float run = 0.f;
+#pragma unroll
+      for (int i = 0; i < St::kGT; ++i) {
+        run += s.gam[t1 + i] + gkl[i];
+        gam[i] = run;
+      }
+      s.gpart[part][d] = run;
+      __syncthreads();
+      float off = 0.f;
+      for (int pp = 0; pp < part; ++pp) off += s.gpart[pp][d];
+#pragma unroll
+      for (int i = 0; i < St::kGT; ++i) {
+        gam[i] += off;
+        if (t1 + i == kC / 2 - 1) s.gmid[d] = gam[i];
+        if (t1 + i == kC - 1) s.glast[d] = gam[i];  // padded rows add 0: last valid row's value
+      }
+      __syncthreads();
+      const float gm = s.gmid[d], gL = s.glast[d];
+      const float el_mid = __expf(gL - gm);
+      if (part == 0) {
+        s.emid[d] = __expf(gm);
+        s.eglk[d] = __expf(gL);
+      }
+#pragma unroll
+      for (int i = 0; i < St::kGT; ++i) {
+        const int t = t1 + i;
+        const float up = __expf(gam[i] - gm), dn = __expf(gm - gam[i]);
+        const float kk = to_f(s.k[t][d]), qq = to_f(s.q[t][d]);
+        s.k[t][d] = to_t<TQ>(kk * up);
+        s.q[t][d] = to_t<TQ>(qq * up);
+        s.kb[t][d] = to_t<TQ>(kk * dn);
+        s.kt[d][t] = to_t<TO>(kk * dn * el_mid);
+      }
+    } else if (wave == 0) {
       const float gam = wave_incl_scan(s.gam[lane], lane);
       const float gl = __shfl(gam, 63, 64);  // padded rows carry g = 0, so this is the last valid row
       s.gam[lane] = gam;
@@ -319,14 +404,16 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
     }
     __syncthreads();
 
-    // ---- Gram (-> A) and Q K^T (-> P), lower 16x16 tiles, scaled in the epilogue
+    // ---- Gram (-> A) and Q K^T (-> P), lower 16x16 tiles.  Scalar gate: the decay
+    // e^{gamma_r - gamma_s} is applied in the epilogue.  Per-key gate: it is inside the
+    // operands (rows e^{gamma - gamma_mid} against columns e^{gamma_mid - gamma}).
     for (int job = wave; job < 20; job += 4) {
       const bool is_qk = job >= 10;
       int I, J;
       tri_tile(job % 10, I, J);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const TI* arow = is_qk ? &s.q[16 * I + li][0] : &s.k[16 * I + li][0];
-      const TI* brow = &s.k[16 * J + li][0];
+      const TQ* arow = is_qk ? &s.q[16 * I + li][0] : &s.k[16 * I + li][0];
+      const TQ* brow = PK ? &s.kb[(16 * J + li) % (PK ? kC : 1)][0] : &s.k[16 * J + li][0];
 #pragma unroll
       for (int kk = 0; kk < kG; ++kk) acc = mma16(lds8(arow + 32 * kk + 8 * lq), lds8(brow + 32 * kk + 8 * lq), acc);
       const int sc = 16 * J + li;
@@ -334,14 +421,14 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * I + 4 * lq + e;
-        const float d = __expf(s.gam[r] - gs);
+        const float d = PK ? 1.f : __expf(s.gam[r] - gs);
         if (is_qk) s.p[r][sc] = to_t<TO>(sc <= r ? d * acc[e] : 0.f);
         else s.a[r][sc] = sc < r ? s.beta[r] * d * acc[e] : 0.f;
       }
     }
     __syncthreads();
 
-    solve_unit_lower<TI, K>(s, wave, lane);
+    solve_unit_lower(s, wave, lane);
     // (bf16) operand copy of the inverse; fp32 reads it from s.a directly.
     if (sizeof(TI) == 2) {
       for (int e = tid; e < 10 * 256; e += kThreads) {
@@ -354,9 +441,22 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
     }
 
     // ---- per-wave: outputs and the state update for columns 16w..16w+15
-    V8 bh[kG];
+    // B operand of the K h / Q h products (per-key gate: rows scaled by e^{gamma_mid})
+    Q8 bh[kG];
 #pragma unroll
-    for (int G = 0; G < kG; ++G) bh[G] = pack8<TI>(hs[G][0], hs[G][1]);
+    for (int G = 0; G < kG; ++G) {
+      if constexpr (PK) {
+        f32x4 a = hs[G][0], b = hs[G][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] *= s.emid[32 * G + 8 * lq + e];
+          b[e] *= s.emid[32 * G + 8 * lq + 4 + e];
+        }
+        bh[G] = pack8<TQ>(a, b);
+      } else {
+        bh[G] = pack8<TQ>(hs[G][0], hs[G][1]);
+      }
+    }
     if (hch) {
 #pragma unroll
       for (int G = 0; G < kG; ++G)
@@ -392,12 +492,13 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float xkj = j < 4 ? xk[P][0][j] : xk[P][1][j - 4];
-        by[P][j] = to_t<TO>(s.beta[r0 + j] * (to_f(vv[j]) - s.eg[r0 + j] * xkj));
+        const float eg = PK ? 1.f : s.eg[r0 + j];
+        by[P][j] = to_t<TO>(s.beta[r0 + j] * (to_f(vv[j]) - eg * xkj));
       }
     }
 
     const TO* tmb = (sizeof(TI) == 2) ? &s.tm[0][0] : reinterpret_cast<const TO*>(&s.a[0][0]);
-    const int tstride = (sizeof(TI) == 2) ? Smem<TI, K>::kTP : Smem<TI, K>::kAP;
+    const int tstride = (sizeof(TI) == 2) ? SM::kTP : SM::kAP;
 
     // v_new = Tm Y (Tm lower triangular: token group P contributes to groups G >= P).
     f32x4 vn[2][2];
@@ -420,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float vj = j < 4 ? vn[P][0][j] : vn[P][1][j - 4];
-        bvs[P][j] = to_t<TO>(vj * s.el[r0 + j]);
+        bvs[P][j] = to_t<TO>(PK ? vj : vj * s.el[r0 + j]);
       }
     }
 
@@ -438,7 +539,8 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
           const int tl = 32 * G + 8 * lq + 4 * t + e;
           if (t0 + tl < len) {
             const long oi = ((tok0 + t0 + tl) * p.H + h) * (long)p.V + col;
-            o[oi] = to_t<TI>(p.scale * (s.eg[tl] * xq[G][t][e] + acc[e]));
+            const float eg = PK ? 1.f : s.eg[tl];
+            o[oi] = to_t<TI>(p.scale * (eg * xq[G][t][e] + acc[e]));
             if (vnew_out) vnew_out[oi] = to_t<TI>(vn[G][t][e]);
           }
         }
@@ -452,6 +554,10 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
       for (int t = 0; t < 2; ++t) {
         const int kr = pair_row(G, t, li);
         f32x4 acc = hs[G][t] * egl;
+        if constexpr (PK) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = hs[G][t][e] * s.eglk[32 * G + 8 * lq + 4 * t + e];
+        }
 #pragma unroll
         for (int P = 0; P < 2; ++P) acc = mma16(lds8(&s.kt[kr][32 * P + 8 * lq]), bvs[P], acc);
         hs[G][t] = acc;
@@ -504,15 +610,25 @@ __global__ __launch_bounds__(256) void varlen_tables_kernel(const int* cu, int N
 hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream) {
   const int nchains = varlen ? p.nseq * p.H : p.B * p.H;
   const dim3 grid(nchains * p.nvb), block(kThreads);
-#define GDN_LAUNCH(TI, KK, VL) hipLaunchKernelGGL((gdn_fwd_kernel<TI, KK, VL>), grid, block, 0, stream, p)
+#define GDN_LAUNCH(TI, KK, VL, PK) \
+  hipLaunchKernelGGL((gdn_fwd_kernel<TI, KK, VL, PK>), grid, block, 0, stream, p)
+  const bool pk = p.gk != nullptr;
   if (dtype == 1) {
     if (K == 128) {
-      if (varlen) GDN_LAUNCH(bf16, 128, true); else GDN_LAUNCH(bf16, 128, false);
+      if (pk) {
+        if (varlen) GDN_LAUNCH(bf16, 128, true, true); else GDN_LAUNCH(bf16, 128, false, true);
+      } else {
+        if (varlen) GDN_LAUNCH(bf16, 128, true, false); else GDN_LAUNCH(bf16, 128, false, false);
+      }
     } else {
-      if (varlen) GDN_LAUNCH(bf16, 64, true); else GDN_LAUNCH(bf16, 64, false);
+      if (pk) {
+        if (varlen) GDN_LAUNCH(bf16, 64, true, true); else GDN_LAUNCH(bf16, 64, false, true);
+      } else {
+        if (varlen) GDN_LAUNCH(bf16, 64, true, false); else GDN_LAUNCH(bf16, 64, false, false);
+      }
     }
   } else {
-    if (varlen) GDN_LAUNCH(float, 64, true); else GDN_LAUNCH(float, 64, false);
+    if (varlen) GDN_LAUNCH(float, 64, true, false); else GDN_LAUNCH(float, 64, false, false);
   }
 #undef GDN_LAUNCH
   return hipGetLastError();

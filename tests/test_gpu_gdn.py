@@ -120,3 +120,50 @@ def test_invalid_arguments_raise():
     with pytest.raises(NotImplementedError):
         q = inp["q"][..., :32].contiguous()
         g.gdn_fwd(q, q, inp["v"], inp["beta"])
+
+
+@pytest.mark.parametrize("K,V,T", [(128, 128, 200), (64, 128, 131), (128, 64, 70)])
+def test_per_key_gate_ragged(K, V, T):
+    """Per-key log decay gk (added to g in log space), with h0, scale, saved h and v_new."""
+    inp = workloads.gdn_inputs(2, T, 3, K, V, dtype="bf16", seed=T + 1, g_shift=3.0,
+                               per_key=True)
+    h0 = torch.randn(2, 3, K, V, generator=torch.Generator().manual_seed(2)) * 0.3
+    _run_and_check(inp, scale=0.7, h0=h0, want_h=True, want_vnew=True,
+                   label="per-key K%d V%d T%d" % (K, V, T))
+
+
+def test_per_key_gate_only():
+    """gk without a scalar g (g = None) equals folding it into gk."""
+    inp = workloads.gdn_inputs(1, 150, 2, 128, 128, dtype="bf16", seed=11, per_key=True)
+    inp["gk"] = inp["gk"] + inp["g"][..., None]
+    inp["g"] = None
+    _run_and_check(inp, label="gk only")
+
+
+def test_long_perkey_workload_sampled():
+    """B=2 H=32 T=32768 K=V=128 bf16 with per-key gate, saving h [B,H,T/64,K,V] and v_new
+    (the long-context workload), run whole on the GPU; four (b, h) chains are compared with
+    the oracle element by element (o, ht, every saved h and v_new of those chains)."""
+    g = _gpu()
+    inp = workloads.make("long_perkey_b2h32t32768")
+    say("long per-key workload generated")
+    d = _to(inp)
+    out = g.gdn_fwd(d["q"], d["k"], d["v"], d["beta"], g=d["g"], gk=d["gk"], want_h=True,
+                    want_v_new=True)
+    torch.cuda.synchronize()
+    picks = [(0, 0), (0, 17), (1, 5), (1, 31)]
+    sub = {}
+    for name in ("q", "k", "v", "beta", "g", "gk"):
+        sub[name] = torch.stack([inp[name][b, :, h] for b, h in picks], dim=1).unsqueeze(0)
+    say("oracle on %d sampled chains" % len(picks))
+    ref = oracle.gdn(sub["q"], sub["k"], sub["v"], sub["beta"], g=sub["g"], gk=sub["gk"],
+                     want_h=True, want_vnew=True)
+    tol = TOL[torch.bfloat16]
+    o = torch.stack([out["o"][b, :, h] for b, h in picks], dim=1).unsqueeze(0)
+    ht = torch.stack([out["ht"][b, h] for b, h in picks], dim=0).unsqueeze(0)
+    hh = torch.stack([out["h"][b, h] for b, h in picks], dim=0).unsqueeze(0)
+    vn = torch.stack([out["v_new"][b, :, h] for b, h in picks], dim=1).unsqueeze(0)
+    assert_close("o", o, ref["o"], tol)
+    assert_close("ht", ht, ref["ht"], tol)
+    assert_close("h", hh, ref["h"], tol)
+    assert_close("v_new", vn, ref["v_new"], tol)
