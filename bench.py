@@ -31,12 +31,30 @@ KERNEL_SOURCES = ["gated_delta_rule_29_amd/csrc/gdn_fwd.hip", "gated_delta_rule_
 COUNTER_FILE = "profiles/gdn_fwd_kernel_b4h16t4096_hbm_counters.md"
 
 
-def alg_bytes_per_launch(B, T, H, K, V, elt=2):
-    """Minimum HBM bytes of one dense forward: read q, k, v (elt bytes), beta and g (fp32),
-    write o (elt bytes) and the final fp32 state."""
+def alg_bytes_per_launch(B, T, H, K, V, elt=2, per_key=False, save=False, n_states=None,
+                         n_chunks=None):
+    """Minimum HBM bytes of one forward: read q, k, v (elt bytes), beta and g (fp32) and gk
+    (fp32, per-key gate); write o (elt bytes), the final fp32 states and, when saved, v_new
+    (elt bytes) and the state entering every 64-token chunk (elt bytes)."""
     tokens_heads = B * T * H
     per_th = (2 * K + V) * elt + 4 + 4 + V * elt
-    return tokens_heads * per_th + B * H * K * V * 4
+    if per_key:
+        per_th += 4 * K
+    total = tokens_heads * per_th
+    if save:
+        n_chunks = B * H * ((T + 63) // 64) if n_chunks is None else n_chunks
+        total += tokens_heads * V * elt + n_chunks * K * V * elt
+    n_states = B * H if n_states is None else n_states
+    total += n_states * K * V * 4
+    return total
+
+
+def alg_bytes_bigdn(B, F, S, H, D):
+    """Minimum HBM bytes of one BiGDN block forward: read qkv once (bf16), beta, decay, the
+    two RoPE tables and norm weights; write num (bf16) and den (bf16)."""
+    N = F * S
+    return (B * N * 3 * H * D * 2 + B * H * N * 4 + B * H * F * 4 + 2 * N * D * 4
+            + 2 * H * D * 4 + B * N * H * D * 2 + B * H * N * 2)
 
 
 def kernel_source_hash():
@@ -61,29 +79,48 @@ def measured_traffic(launch_bytes):
     return float(m_b.group(1))
 
 
-def cpu_baseline(inp, n_chains_max=64):
-    """The fp64 oracle on a bounded sample of the same workload (the first chains of batch 0
-    onwards), timed on this host's cores."""
-    import numpy as np
-
+def _cpu_time(fn, sample, th):
     import oracle
 
-    B, T, H, K = inp["q"].shape
-    nb = max(1, min(B, n_chains_max // H))
-    sub = {k: (v[:nb] if v is not None else None) for k, v in inp.items()}
-    args = [sub["q"], sub["k"], sub["v"], sub["beta"]]
-    conv = [oracle._f64(a) for a in args]
-    g = oracle._f64(sub["g"])
-    oracle.gdn(conv[0][:, :64], conv[1][:, :64], conv[2][:, :64], conv[3][:, :64],
-               g=g[:, :64])  # warm-up (library load, page-in)
     t0 = time.perf_counter()
-    oracle.gdn(*conv, g=g)
+    fn()
     dt = time.perf_counter() - t0
-    th = nb * T * H
     return {"value": th / dt, "unit": "tokens·heads/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": "fp64 token recurrence on %d of %d batch rows (%d chains x %d tokens = "
-                      "%d token*heads), one run, %.2f s wall" % (nb, B, nb * H, T, th, dt)}
+            "kind": "oracle", "sample": "%s; one run, %.2f s wall" % (sample, dt)}
+
+
+def cpu_baseline(kind, inp, max_chains=64):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload (whole
+    independent chains, so the sample does the same per-token work), timed on this host."""
+    import oracle
+
+    oracle.build()
+    if kind == "bigdn":
+        B, N, _, H, D = inp["qkv"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        args = [oracle._f64(inp[n]) for n in ("qkv", "beta", "decay", "q_norm_w", "k_norm_w",
+                                               "rope_cos", "rope_sin")]
+        return _cpu_time(lambda: oracle.bigdn(*args, inp["k_scale"], inp["eps"]),
+                         "whole block: prep + both directions, %d heads x %d tokens" % (H, N),
+                         B * N * H)
+    if kind == "varlen":
+        cu = inp["cu_seqlens"].numpy()
+        n = 1
+        H = inp["q"].shape[2]
+        T1 = int(cu[n])
+        sub = {k: (oracle._f64(v[:, :T1]) if v is not None and k != "cu_seqlens" else None)
+               for k, v in inp.items()}
+        return _cpu_time(lambda: oracle.gdn_varlen(cu[:n + 1], sub["q"], sub["k"], sub["v"],
+                                                   sub["beta"], g=sub["g"]),
+                         "first packed sequence (%d tokens) x %d heads" % (T1, H), T1 * H)
+    B, T, H, K = inp["q"].shape
+    nb = max(1, min(B, max_chains // H))
+    hh = min(H, max_chains)
+    sub = {k: (oracle._f64(v[:nb, :, :hh]) if v is not None else None) for k, v in inp.items()}
+    return _cpu_time(lambda: oracle.gdn(sub["q"], sub["k"], sub["v"], sub["beta"], g=sub["g"],
+                                        gk=sub["gk"]),
+                     "%d of %d batch rows x %d of %d heads (%d chains x %d tokens)"
+                     % (nb, B, hh, H, nb * hh, T), nb * hh * T)
 
 
 def main():
@@ -92,7 +129,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gdn_bf16_b4h16t4096")
-    ap.add_argument("--rotate", type=int, default=4, help="input copies cycled through")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies cycled through (default: enough to exceed 1 GB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device-to-device copies of MIB "
@@ -119,22 +157,67 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
         return
 
-    spec = workloads.WORKLOADS[args.workload]
-    if spec["kind"] != "gdn":
-        raise SystemExit("bench.py times the dense gdn_fwd workloads")
+    spec = dict(workloads.WORKLOADS[args.workload])
+    kind = spec["kind"]
     dev = torch.device("cuda:0")
     inp = workloads.make(args.workload)
-    B, T, H, K = inp["q"].shape
-    V = inp["v"].shape[-1]
-    dt = inp["q"].dtype
+    in_bytes = sum(v.numel() * v.element_size() for v in inp.values() if isinstance(v, torch.Tensor))
+    rotate = args.rotate or max(2, min(8, -(-(1 << 30) // max(in_bytes, 1))))
     sets = []
-    for r in range(max(1, args.rotate)):
-        sets.append({k: (v.to(dev) if v is not None else None) for k, v in inp.items()})
+    for r in range(rotate):
+        sets.append({k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()})
     torch.cuda.synchronize()
+    save = bool(spec.get("save", False))
 
-    def step(i):
-        s = sets[i % len(sets)]
-        return gdn.gdn_fwd(s["q"], s["k"], s["v"], s["beta"], g=s["g"], gk=s["gk"])
+    if kind == "gdn":
+        B, T, H, K = inp["q"].shape
+        V = inp["v"].shape[-1]
+        dt = inp["q"].dtype
+        th = B * T * H
+        elt = 2 if dt == torch.bfloat16 else 4
+        alg = alg_bytes_per_launch(B, T, H, K, V, elt, inp["gk"] is not None, save)
+        kernel = "gdn_fwd_kernel"
+        config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
+                  "chunk": 64, "state": "fp32", "per_key_gate": inp["gk"] is not None,
+                  "saves_h_and_v_new": save}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.gdn_fwd(s["q"], s["k"], s["v"], s["beta"], g=s["g"], gk=s["gk"],
+                               want_h=save, want_v_new=save)
+    elif kind == "varlen":
+        _, T, H, K = inp["q"].shape
+        V = inp["v"].shape[-1]
+        dt = inp["q"].dtype
+        cu = inp["cu_seqlens"]
+        N = cu.numel() - 1
+        th = T * H
+        elt = 2 if dt == torch.bfloat16 else 4
+        alg = alg_bytes_per_launch(1, T, H, K, V, elt, False, False, n_states=N * H)
+        kernel = "gdn_fwd_kernel (varlen)"
+        config = {"workload": args.workload, "T_total": T, "N": N, "H": H, "K": K, "V": V,
+                  "lengths": (cu[1:] - cu[:-1]).tolist(), "chunk": 64, "state": "fp32"}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.gdn_fwd_varlen(s["q"], s["k"], s["v"], s["beta"], s["cu_seqlens"],
+                                      g=s["g"], want_tables=False)
+    elif kind == "bigdn":
+        B, N, _, H, D = inp["qkv"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        dt = torch.bfloat16
+        th = B * N * H
+        alg = alg_bytes_bigdn(B, F, S, H, D)
+        kernel = "bigdn_fwd (4 kernels, whole call)"
+        config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
+                  "state": "fp32"}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.bigdn_fwd(s["qkv"], s["beta"], s["decay"], s["q_norm_w"], s["k_norm_w"],
+                                 s["rope_cos"], s["rope_sin"], s["k_scale"], s["eps"])
+    else:
+        raise SystemExit("unknown workload kind %s" % kind)
 
     for i in range(args.warmup):
         step(i)
@@ -155,13 +238,10 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = total_ms / args.steps
-    th = B * T * H
     value = th / (ms_per_step / 1e3)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
-    elt = 2 if dt == torch.bfloat16 else 4
-    alg = alg_bytes_per_launch(B, T, H, K, V, elt)
     achieved = alg / avg_launch_s / 1e9
-    traffic = measured_traffic(alg)
+    traffic = measured_traffic(alg) if args.workload == "gdn_bf16_b4h16t4096" else None
     out = {
         "metric": METRIC,
         "value": value,
@@ -174,18 +254,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
-        "data": "synthetic (seeded; q,k L2-normalised, beta=sigmoid(N), g=logsigmoid(N+%g))"
-                % spec.get("g_shift", 3.0),
-        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
-                   "chunk": 64, "state": "fp32", "input_copies_rotated": len(sets)},
+        "data": "synthetic (seeded workloads.py recipe: %s)" % args.workload,
+        "config": dict(config, input_copies_rotated=len(sets)),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn_fwd_kernel", "alg_bytes_per_launch": alg,
-                     "avg_launch_ms": avg_launch_s * 1e3},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel,
+                     "alg_bytes_per_launch": alg, "avg_launch_ms": avg_launch_s * 1e3},
         "cpu_baseline": None,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inp)
+        out["cpu_baseline"] = cpu_baseline(kind, inp)
     print(json.dumps(out), flush=True)
 
 
