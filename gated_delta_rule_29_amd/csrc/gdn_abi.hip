@@ -64,24 +64,33 @@ int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 const char* gdn_last_error(void) { return g_err; }
 
-size_t gdn_fwd_workspace_bytes(int, int, int, int, int, int) { return 0; }
+size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype) {
+  (void)K; (void)V;
+  if (B <= 0 || T <= 0 || H <= 0 || (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)) return 0;
+  return gdn::fwd_workspace_bytes((long)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK), 0, dtype);
+}
 
 int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* gk,
             const float* beta, float scale, const float* h0, void* o, float* ht, void* h_chunks,
             void* v_new, int B, int T, int H, int K, int V, int dtype, void* workspace,
             size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int rc = check_fwd_common(q, k, v, beta, o, gk, H, K, V, dtype);
   if (rc) return rc;
   if (B <= 0 || T <= 0) return fail(GDN_ERR_INVALID, "B and T must be positive (got %d, %d)", B, T);
-  const int64_t wgs = (int64_t)B * H * (V / 64);
-  if (wgs > INT32_MAX) return fail(GDN_ERR_INVALID, "B*H*(V/64) = %lld exceeds the grid limit", (long long)wgs);
+  const int64_t wgs = (int64_t)B * H * (V / 64), nslots = (int64_t)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK);
+  if (wgs > INT32_MAX || nslots > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "B*H*(V/64) = %lld or B*H*chunks = %lld exceeds the grid limit",
+                (long long)wgs, (long long)nslots);
+  const size_t need = gdn_fwd_workspace_bytes(B, T, H, K, V, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
   gdn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.g = g; p.gk = gk; p.beta = beta; p.h0 = h0;
   p.o = o; p.ht = ht; p.h_chunks = h_chunks; p.v_new = v_new; p.cu = nullptr;
   p.scale = scale; p.B = B; p.T = T; p.H = H; p.V = V; p.nvb = V / 64;
-  p.nseq = 0; p.nt_total = 0;
+  p.nseq = 0; p.nt_total = 0; p.ws = workspace; p.coffs = nullptr;
   hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_fwd launch");
   return ok();
@@ -98,7 +107,13 @@ int gdn_varlen_num_chunks(const int* cu, int N) {
   return total > INT32_MAX ? -1 : (int)total;
 }
 
-size_t gdn_fwd_varlen_workspace_bytes(int, int, int, int, int, int) { return 0; }
+size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype) {
+  (void)K; (void)V;
+  if (T_total <= 0 || N <= 0 || H <= 0 || (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)) return 0;
+  // chunks <= T_total / 64 + N (each sequence adds at most one partial chunk)
+  const long nt_max = (long)T_total / GDN_CHUNK + N;
+  return gdn::fwd_workspace_bytes((long)H * nt_max, N, dtype);
+}
 
 int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
                    const float* gk, const float* beta, float scale, const int* cu_seqlens,
@@ -106,8 +121,6 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
                    void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
                    int T_total, int H, int K, int V, int dtype, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int rc = check_fwd_common(q, k, v, beta, o, gk, H, K, V, dtype);
   if (rc) return rc;
   if (!cu_seqlens || !cu_seqlens_host)
@@ -122,7 +135,13 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
   const int nt = gdn_varlen_num_chunks(cu_seqlens_host, N);
   if (nt < 0) return fail(GDN_ERR_INVALID, "too many chunks");
   const int64_t wgs = (int64_t)N * H * (V / 64);
-  if (wgs > INT32_MAX) return fail(GDN_ERR_INVALID, "N*H*(V/64) exceeds the grid limit");
+  if (wgs > INT32_MAX || (int64_t)H * nt > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "N*H*(V/64) or H*chunks exceeds the grid limit");
+  const size_t need = gdn::fwd_workspace_bytes((long)H * nt, N, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (chunk_offsets || chunk_indices) {
     hipError_t e = gdn::launch_varlen_tables(cu_seqlens, N, chunk_offsets, chunk_indices, s);
@@ -132,7 +151,8 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
   p.q = q; p.k = k; p.v = v; p.g = g; p.gk = gk; p.beta = beta; p.h0 = h0;
   p.o = o; p.ht = ht; p.h_chunks = h_chunks; p.v_new = v_new; p.cu = cu_seqlens;
   p.scale = scale; p.B = 1; p.T = T_total; p.H = H; p.V = V; p.nvb = V / 64;
-  p.nseq = N; p.nt_total = nt;
+  p.nseq = N; p.nt_total = nt; p.ws = workspace;
+  p.coffs = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)H * nt * gdn::fwd_slot_bytes(dtype));
   hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, true, s);
   if (e != hipSuccess) return hip_fail(e, "gdn_fwd_varlen launch");
   return ok();

@@ -1,42 +1,53 @@
-// gdn_fwd.hip -- fused chunkwise gated delta-rule forward for gfx950.
+// gdn_fwd.hip -- chunkwise gated delta-rule forward for gfx950: a chunk-parallel prep kernel
+// and a sequential state-pass kernel.
 //
-// One workgroup owns one chain (a (batch, head) pair, or a (sequence, head) pair of a packed
-// batch) and one 64-wide block of the value dimension, and walks the chain's 64-token chunks
-// in order.  Per chunk it does all of the method in LDS and registers:
-//
+// For chunk n of a chain (64 tokens, h = state entering the chunk):
 //   gamma_r = sum_{i<=r} g_i (chunk-local inclusive cumsum),  gl = gamma of the last row
 //   A   = strict_lower( diag(beta) (K K^T o D) ),  D[r,s] = exp(gamma_r - gamma_s)
-//   Tm  = (I + A)^-1                                   (unit lower triangular, fp32)
+//   Tm  = (I + A)^-1                                   (unit lower triangular, fp32 solve)
 //   P   = lower( Q K^T o D )
-//   X_K = diag(e^gamma) K h,    X_Q = diag(e^gamma) Q h           (h = state entering chunk)
+//   X_K = diag(e^gamma) K h,    X_Q = diag(e^gamma) Q h
 //   v_new = Tm ( diag(beta) (V - X_K) )        ( = u - w h of the WY form )
 //   o   = scale (X_Q + P v_new)
 //   h  <- e^gl h + K^T diag(e^{gl - gamma}) v_new
-//
 // This is the WY/chunkwise form of the recurrence: the state-pass lines are the ones in the
 // chunk_gated_delta_rule_fwd_h fragments on the hyper-parallel "Diff Coverage" page (v_new =
 // u - w h, decay by the last gate, state += K^T (v_new * e^{g_last - g})); the intra-chunk
-// solve and the masked output follow from unrolling the recurrence over one chunk.  Here w h
-// is evaluated as Tm (diag(beta e^gamma) K h), so w is never formed.
+// solve and the masked output follow from unrolling the recurrence over one chunk.  w h is
+// evaluated as Tm (diag(beta e^gamma) K h), so w and u are never formed.
 //
-// Layout of the state in registers.  Wave w owns value columns 16w..16w+15 of the block and
-// every key row.  Keys are grouped by 32; for group G a lane holds keys 32G+8lq+j, j=0..7, of
-// its column li, split over two 16x16 accumulators (j<4 and j>=4).  The MFMA tiles that
-// produce the state pick A-operand rows so that this holds (row i of tile t is key
-// 32G + 8(i/4) + 4t + i%4), which makes the state directly usable as the B operand of the
-// next chunk's K h / Q h products with no data movement.  Token-indexed results (X_K, v_new,
-// o) use the same mapping over tokens, so v_new feeds P v_new and K^T v_new directly too.
+// Everything that does not depend on the state (gamma, A, the solve, P) is computed by
+// chunk_prep_kernel, one workgroup per chunk across the whole GPU, into a workspace slot per
+// chunk (Tm and P in the operand type, e^gamma, e^{gl-gamma}, e^gl).  scan_kernel then walks
+// each chain's chunks in order doing only the state-dependent products, with the next chunk's
+// operands staged into the other half of a double-buffered LDS while the current one is used.
+//
+// Per-key gates (gk, added to g in log space) put the decay inside the key sum; the Gram /
+// Q K^T operands are then scaled per key around the chunk's middle token (rows
+// e^{gamma - gamma_mid}, columns e^{gamma_mid - gamma}); K h / Q h use the state rows scaled
+// by e^{gamma_mid}; the state decays row by row with e^{gamma_last}; K^T in the update carries
+// e^{gamma_last - gamma}.  The per-key gamma is a column cumsum done by 2 (K = 128) or 4
+// (K = 64) adjacent lanes per key, combined with shuffles.
+//
+// State layout in scan_kernel's registers.  Wave w owns value columns 16w..16w+15 of the
+// block and every key row.  Keys are grouped by 32; for group G a lane holds keys 32G+8lq+j,
+// j=0..7, of its column li, split over two 16x16 accumulators (j<4 and j>=4).  The MFMA tiles
+// that produce the state pick A-operand rows so that this holds (row i of tile t is key
+// 32G + 8(i/4) + 4t + i%4: "pair rows"), which makes the state directly the B operand of the
+// next chunk's K h / Q h products.  Token-indexed results (X_K, v_new, o) use the same mapping
+// over tokens, so v_new feeds P v_new and K^T v_new directly too.
 #include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_tiles.h"
 
 namespace gdn {
 
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kBV = 64;        // value columns per workgroup
+constexpr int kBV = 64;        // value columns per scan workgroup
 constexpr int kC = 64;         // chunk length
 
 template <typename TI>
@@ -59,11 +70,6 @@ struct OpT<float> {
   typedef float type;
 };
 
-// Row of the 16-row A-operand tile t (0/1) of 32-group G that lane row li supplies.
-__device__ __forceinline__ int pair_row(int G, int t, int li) {
-  return 32 * G + 8 * (li >> 2) + 4 * t + (li & 3);
-}
-
 // Type of the q / k tiles: the inputs as given for a scalar gate; for a per-key gate they
 // hold the decay-scaled operands, so they take the intra-chunk operand type.
 template <typename TI, bool PK>
@@ -71,136 +77,74 @@ struct QKT {
   typedef typename std::conditional<PK, typename OpT<TI>::type, TI>::type type;
 };
 
-template <typename TI, int K, bool PK>
-struct __attribute__((aligned(16))) Smem {
-  typedef typename OpT<TI>::type TO;
-  typedef typename QKT<TI, PK>::type TQ;
-  static constexpr int kE = Pad<TI>::kE;
-  static constexpr int kKP = K + kE;    // row stride of [token][key] tiles
-  static constexpr int kTP = kC + kE;   // row stride of [.][token] tiles
-  static constexpr int kAP = kC + 4;    // row stride of the fp32 solve buffer
-  TQ q[kC][kKP];    // Q, or per-key gate: Q * e^{gamma - gamma_mid}
-  TQ k[kC][kKP];    // K, or per-key gate: K * e^{gamma - gamma_mid}
-  TQ kb[PK ? kC : 1][kKP];  // per-key gate: K * e^{gamma_mid - gamma}
-  TO kt[K][kTP];    // K^T, or per-key gate: (K * e^{gamma_last - gamma})^T
-  TI vt[kBV][kTP];
-  TO tm[kC][kTP];   // (I + A)^-1 as MFMA operand (bf16 path)
-  TO p[kC][kTP];    // masked decayed Q K^T
-  float a[kC][kAP]; // fp32: A, then overwritten in place by (I + A)^-1
-  float x[32][36];  // fp32 scratch of the solve's last merge
-  float gam[kC], eg[kC], el[kC], beta[kC];
-  float egl;
-  // per-key gate: e^{gamma_mid}, e^{gamma_last} per key, and the cumsum exchange
-  float emid[PK ? K : 1], eglk[PK ? K : 1], gpart[PK ? kThreads / K : 1][PK ? K : 1];
-  float gmid[PK ? K : 1], glast[PK ? K : 1];
-};
-
-// Global -> register staging of one chunk, 16 bytes per load.
-template <typename TI, int K, bool PK>
-struct Stage {
-  static constexpr int kE = Pad<TI>::kE;
-  static constexpr int kCPR = K / kE;                  // 16-byte chunks per q/k row
-  static constexpr int kNQ = kC * kCPR / kThreads;     // per thread, per tensor
-  static constexpr int kVPR = kBV / kE;                // 16-byte chunks per v row block
-  static constexpr int kNV = kC * kVPR / kThreads;
-  // per-key gate: thread tid owns key tid % K and kGT consecutive tokens
-  static constexpr int kTPK = kThreads / K;
-  static constexpr int kGT = kC / kTPK;
-  uint4 q[kNQ], k[kNQ], v[kNV];
-  float g, beta;
-  float gk[PK ? kGT : 1];
-};
-
-template <typename TI, int K, bool PK>
-__device__ __forceinline__ void load_chunk(Stage<TI, K, PK>& st, const FwdParams& p, long tok0,
-                                           int h, int t0, int len, int v0, int tid) {
-  typedef Stage<TI, K, PK> St;
-  constexpr int kE = Pad<TI>::kE;
-  const TI* q = static_cast<const TI*>(p.q);
-  const TI* k = static_cast<const TI*>(p.k);
-  const TI* v = static_cast<const TI*>(p.v);
-#pragma unroll
-  for (int i = 0; i < St::kNQ; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c / St::kCPR, cc = c % St::kCPR;
-    const int t = t0 + row;
-    uint4 zq = make_uint4(0, 0, 0, 0), zk = zq;
-    if (t < len) {
-      const long off = ((tok0 + t) * p.H + h) * (long)K + cc * kE;
-      zq = *reinterpret_cast<const uint4*>(q + off);
-      zk = *reinterpret_cast<const uint4*>(k + off);
-    }
-    st.q[i] = zq;
-    st.k[i] = zk;
-  }
-#pragma unroll
-  for (int i = 0; i < St::kNV; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c / St::kVPR, cc = c % St::kVPR;
-    const int t = t0 + row;
-    uint4 z = make_uint4(0, 0, 0, 0);
-    if (t < len) z = *reinterpret_cast<const uint4*>(v + ((tok0 + t) * p.H + h) * (long)p.V + v0 + cc * kE);
-    st.v[i] = z;
-  }
-  st.g = 0.f;
-  st.beta = 0.f;
-  if (tid < kC) {
-    const int t = t0 + tid;
-    if (t < len) {
-      const long gi = (tok0 + t) * p.H + h;
-      st.g = p.g ? p.g[gi] : 0.f;
-      st.beta = p.beta[gi];
-    }
-  }
-  if constexpr (PK) {
-    const int d = tid % K, t1 = (tid / K) * St::kGT;
-#pragma unroll
-    for (int i = 0; i < St::kGT; ++i) {
-      const int t = t0 + t1 + i;
-      st.gk[i] = t < len ? p.gk[((tok0 + t) * p.H + h) * (long)K + d] : 0.f;
-    }
-  }
+// Row of the 16-row A-operand tile t (0/1) of 32-group G that lane row li supplies.
+__device__ __forceinline__ int pair_row(int G, int t, int li) {
+  return 32 * G + 8 * (li >> 2) + 4 * t + (li & 3);
 }
 
-template <typename TI, int K, bool PK>
-__device__ __forceinline__ void store_chunk(const Stage<TI, K, PK>& st, Smem<TI, K, PK>& s, int tid) {
-  typedef typename OpT<TI>::type TO;
-  typedef Stage<TI, K, PK> St;
-  constexpr int kE = Pad<TI>::kE;
-#pragma unroll
-  for (int i = 0; i < St::kNQ; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c / St::kCPR, cc = c % St::kCPR;
-    if constexpr (PK) {
-      // raw q / k converted to the operand type; the scaling pass rescales them in place
-      const TI* eq = reinterpret_cast<const TI*>(&st.q[i]);
-      const TI* ek = reinterpret_cast<const TI*>(&st.k[i]);
-#pragma unroll
-      for (int j = 0; j < kE; ++j) {
-        s.q[row][cc * kE + j] = to_t<TO>(to_f(eq[j]));
-        s.k[row][cc * kE + j] = to_t<TO>(to_f(ek[j]));
-      }
+// Makes one wave's LDS writes visible to its other lanes before they read.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Tile layouts: 16-bit tiles are unpadded and XOR-swizzled (gdn_tiles.h); fp32 tiles are
+// padded by 16 bytes per row.
+template <typename T, int COLS>
+struct Lay {
+  static constexpr bool kSwz = sizeof(T) == 2;
+  static constexpr int kStride = kSwz ? COLS : COLS + 16 / (int)sizeof(T);
+  static constexpr int kElems(int rows) { return rows * kStride; }
+  __device__ static int pair(int r, int c) {
+    if constexpr (kSwz) return tix_pair<COLS>(r, c);
+    else return r * kStride + c;
+  }
+  __device__ static int seq(int r, int c) {
+    if constexpr (kSwz) {
+      static_assert(!kSwz || COLS == 64, "sequential-row swizzle is defined for 64 columns");
+      return tix_seq64(r, c);
     } else {
-      *reinterpret_cast<uint4*>(&s.q[row][cc * kE]) = st.q[i];
-      *reinterpret_cast<uint4*>(&s.k[row][cc * kE]) = st.k[i];
-      const TI* e = reinterpret_cast<const TI*>(&st.k[i]);
-#pragma unroll
-      for (int j = 0; j < kE; ++j) s.kt[cc * kE + j][row] = to_t<TO>(to_f(e[j]));
+      return r * kStride + c;
     }
   }
-#pragma unroll
-  for (int i = 0; i < St::kNV; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c / St::kVPR, cc = c % St::kVPR;
-    const TI* e = reinterpret_cast<const TI*>(&st.v[i]);
-#pragma unroll
-    for (int j = 0; j < kE; ++j) s.vt[cc * kE + j][row] = e[j];
+};
+
+// Workspace slot of one chunk: Tm, P (64x64 operand type), e^gamma, e^{gl - gamma}, e^gl.
+template <typename TO>
+struct Slot {
+  static constexpr size_t kTm = 0;
+  static constexpr size_t kP = (size_t)kC * kC * sizeof(TO);
+  static constexpr size_t kEg = 2 * kP;
+  static constexpr size_t kEl = kEg + kC * 4;
+  static constexpr size_t kEgl = kEl + kC * 4;
+  static constexpr size_t kBytes = (kEgl + 16 + 255) & ~(size_t)255;
+};
+
+// Where a chunk lives: chain index (b*H + h or seq*H + h), first token, its chunk number in
+// the chain, and the chain's token count.
+struct ChunkPos {
+  long tok0;  // first token of the chain
+  int len;    // tokens in the chain
+  long slot0; // workspace / h_chunks index of the chain's chunk 0
+};
+
+__device__ __forceinline__ ChunkPos chain_pos(const FwdParams& p, int chain, bool varlen) {
+  ChunkPos c;
+  const int h = chain % p.H, bs = chain / p.H;
+  if (varlen) {
+    c.tok0 = p.cu[bs];
+    c.len = p.cu[bs + 1] - p.cu[bs];
+    c.slot0 = (long)h * p.nt_total + p.coffs[bs];
+  } else {
+    c.tok0 = (long)bs * p.T;
+    c.len = p.T;
+    c.slot0 = (long)chain * ((p.T + kC - 1) / kC);
   }
-  if (tid < kC) {
-    s.gam[tid] = st.g;
-    s.beta[tid] = st.beta;
-  }
+  return c;
 }
+
+hipError_t launch_varlen_tables_impl(const int* cu, int N, int* offs, int* idx, hipStream_t stream);
 
 // Lower-triangular 16x16 tile enumeration: (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
 __device__ __forceinline__ void tri_tile(int idx, int& I, int& J) {
@@ -208,11 +152,70 @@ __device__ __forceinline__ void tri_tile(int idx, int& I, int& J) {
   J = idx - I * (I + 1) / 2;
 }
 
-// (I + A)^-1 for the strictly lower 64x64 A held in s.a, in place, fp32.  Diagonal 16x16
-// blocks by forward substitution, then blocks merged with
+// Per-key gate, column pass.  Thread tid owns key d = tid / TPK and tokens part*GT..+GT-1
+// (TPK adjacent lanes per key).  gk holds this thread's log decays; g_at(t) gives g_t.  On
+// return gam[] holds gamma[t][d] for its tokens, and gm / gL the key's gamma at tokens 31
+// and 63 (padded rows carry zero decays, so gL is the last valid row's value).
+template <int K, int GT, typename GF>
+__device__ __forceinline__ void key_cumsum(const float* gk, GF g_at, int part, float* gam,
+                                           float& gm, float& gL) {
+  constexpr int kTPK = kThreads / K;
+  float run = 0.f;
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+    run += g_at(part * GT + i) + gk[i];
+    gam[i] = run;
+  }
+  // exclusive prefix over the TPK parts of this key (adjacent lanes of one wave)
+  const int lane0 = (threadIdx.x & 63) & ~(kTPK - 1);
+  float tot[kTPK];
+#pragma unroll
+  for (int q = 0; q < kTPK; ++q) tot[q] = __shfl(run, lane0 + q, 64);
+  float off = 0.f;
+#pragma unroll
+  for (int q = 0; q < kTPK; ++q) off += q < part ? tot[q] : 0.f;
+#pragma unroll
+  for (int i = 0; i < GT; ++i) gam[i] += off;
+  float cum[kTPK];
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < kTPK; ++q) {
+    acc += tot[q];
+    cum[q] = acc;
+  }
+  static_assert((kC / 2) % GT == 0, "the middle token must end a part");
+  gm = cum[kC / 2 / GT - 1];  // gamma at token 31 (the parts up to it sum exactly to it)
+  gL = cum[kTPK - 1];
+}
+
+// ======================================================================================
+// chunk_prep_kernel: one workgroup per chunk.
+// ======================================================================================
+template <typename TI, int K, bool PK>
+struct __attribute__((aligned(16))) PrepSmem {
+  typedef typename OpT<TI>::type TO;
+  typedef typename QKT<TI, PK>::type TQ;
+  static constexpr int kKP = K + Pad<TQ>::kE;
+  static constexpr int kTP = kC + Pad<TO>::kE;
+  static constexpr int kAP = kC + 4;
+  TQ q[kC][kKP];
+  TQ k[kC][kKP];
+  TQ kb[PK ? kC : 1][kKP];
+  TO tm[kC][kTP];
+  TO p[kC][kTP];
+  float a[kC][kAP];
+  float x[32][36];
+  float gam[kC], beta[kC], g[kC];
+};
+
+// (I + A)^-1 for the strictly lower 64x64 A held in s.a, fp32.  Diagonal 16x16 blocks by
+// forward substitution, then blocks merged with
 //   T_hi,lo = -T_hi,hi A_hi,lo T_lo,lo       (first for 16-blocks, then for 32-blocks).
+// Every final block is written to s.tm (operand type) as it is produced; s.a keeps the fp32
+// blocks the later merges read.
 template <typename SM>
 __device__ __forceinline__ void solve_unit_lower(SM& s, int wave, int lane) {
+  typedef typename SM::TO TO;
   const int li = lane & 15, lq = lane >> 4;
   if (wave == 0) {
     // lane -> (block b = lq, column c = li): forward substitution down column c.
@@ -226,7 +229,10 @@ __device__ __forceinline__ void solve_unit_lower(SM& s, int wave, int lane) {
       x[i] = acc;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s.a[b0 + i][b0 + li] = x[i];
+    for (int i = 0; i < 16; ++i) {
+      s.a[b0 + i][b0 + li] = x[i];
+      s.tm[b0 + i][b0 + li] = to_t<TO>(x[i]);
+    }
   }
   __syncthreads();
   if (wave < 2) {
@@ -240,7 +246,10 @@ __device__ __forceinline__ void solve_unit_lower(SM& s, int wave, int lane) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) t = mma4(s.a[hi + li][hi + 4 * lq + kk], m[kk], t);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s.a[hi + 4 * lq + e][lo + li] = -t[e];
+    for (int e = 0; e < 4; ++e) {
+      s.a[hi + 4 * lq + e][lo + li] = -t[e];
+      s.tm[hi + 4 * lq + e][lo + li] = to_t<TO>(-t[e]);
+    }
   }
   __syncthreads();
   {
@@ -270,55 +279,51 @@ __device__ __forceinline__ void solve_unit_lower(SM& s, int wave, int lane) {
         y = mma4(s.a[32 + 16 * ti + li][32 + 16 * m + 4 * kk + lq], s.x[16 * m + 4 * kk + lq][16 * tj + li], y);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s.a[32 + 16 * ti + 4 * lq + e][16 * tj + li] = -y[e];
+    for (int e = 0; e < 4; ++e) s.tm[32 + 16 * ti + 4 * lq + e][16 * tj + li] = to_t<TO>(-y[e]);
   }
   __syncthreads();
 }
 
 template <typename TI, int K, bool VARLEN, bool PK>
-__global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p) {
   typedef typename OpT<TI>::type TO;
   typedef typename QKT<TI, PK>::type TQ;
-  typedef typename Vec8<TI>::type V8;
-  typedef typename Vec8<TO>::type W8;
   typedef typename Vec8<TQ>::type Q8;
-  typedef Smem<TI, K, PK> SM;
-  typedef Stage<TI, K, PK> St;
-  constexpr int kG = K / 32;  // key groups of 32
+  typedef PrepSmem<TI, K, PK> SM;
+  typedef Slot<TO> SL;
+  constexpr int kG = K / 32;
+  constexpr int kE = Pad<TI>::kE;
+  constexpr int kCPR = K / kE;
   __shared__ SM s;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
 
-  // Workgroup -> (chain, value block).  Consecutive workgroup ids are dealt round-robin to
-  // the 8 XCDs; remap so that the value blocks of one chain sit on one XCD and share its L2
-  // for the chain's q/k/g/beta reads.
-  const int nwg = gridDim.x;
-  int logical = blockIdx.x;
-  if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  const int chain = logical / p.nvb;
-  const int v0 = (logical % p.nvb) * kBV;
-  const int h = chain % p.H;
-  const int bs = chain / p.H;
-
-  long tok0;
-  int len;
-  long hbase;  // index of this chain's first chunk state in h_chunks
+  // chunk -> (chain, n)
+  int chain, n;
   if (VARLEN) {
-    tok0 = p.cu[bs];
-    len = p.cu[bs + 1] - p.cu[bs];
-    long before = 0;
-    for (int j = 0; j < bs; ++j) before += (p.cu[j + 1] - p.cu[j] + kC - 1) / kC;
-    hbase = (long)h * p.nt_total + before;
+    const int h = blockIdx.x / p.nt_total, cg = blockIdx.x % p.nt_total;
+    int lo = 0, hi = p.nseq;  // largest i with coffs[i] <= cg
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.coffs[mid] <= cg) lo = mid;
+      else hi = mid;
+    }
+    chain = lo * p.H + h;
+    n = cg - p.coffs[lo];
   } else {
-    tok0 = (long)bs * p.T;
-    len = p.T;
-    hbase = (long)chain * ((p.T + kC - 1) / kC);
+    const int nt = (p.T + kC - 1) / kC;
+    chain = blockIdx.x / nt;
+    n = blockIdx.x % nt;
   }
-  const int nchunks = (len + kC - 1) / kC;
-  const int col = v0 + 16 * wave + li;  // this lane's value column
+  const ChunkPos cp = chain_pos(p, chain, VARLEN);
+  const int h = chain % p.H;
+  const int t0 = n * kC, rows = min(kC, cp.len - t0);
+  const long HK = (long)p.H * K;
+  const TI* q = static_cast<const TI*>(p.q);
+  const TI* k = static_cast<const TI*>(p.k);
 
-  // Strict upper 16x16 tiles of A / Tm / P are never written by the chunk loop: zero once.
+  // strict upper 16x16 tiles of A / Tm / P stay zero
   for (int e = tid; e < 6 * 256; e += kThreads) {
     const int t = e >> 8, r = (e >> 4) & 15, c = e & 15;
     const int I = (t >= 3) + (t >= 5);
@@ -327,8 +332,354 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
     s.tm[16 * I + r][16 * J + c] = to_t<TO>(0.f);
     s.p[16 * I + r][16 * J + c] = to_t<TO>(0.f);
   }
+  // q, k rows (16-byte loads, 16 lanes per row); rows past the end are zero
+#pragma unroll
+  for (int i = 0; i < kC * kCPR / kThreads; ++i) {
+    const int c = tid + kThreads * i;
+    const int row = c / kCPR, cc = c % kCPR;
+    uint4 zq = make_uint4(0, 0, 0, 0), zk = zq;
+    if (row < rows) {
+      const long off = (cp.tok0 + t0 + row) * HK + (long)h * K + cc * kE;
+      zq = *reinterpret_cast<const uint4*>(q + off);
+      zk = *reinterpret_cast<const uint4*>(k + off);
+    }
+    if constexpr (PK) {
+      const TI* eq = reinterpret_cast<const TI*>(&zq);
+      const TI* ek = reinterpret_cast<const TI*>(&zk);
+#pragma unroll
+      for (int j = 0; j < kE; ++j) {
+        s.q[row][cc * kE + j] = to_t<TQ>(to_f(eq[j]));
+        s.k[row][cc * kE + j] = to_t<TQ>(to_f(ek[j]));
+      }
+    } else {
+      *reinterpret_cast<uint4*>(&s.q[row][cc * kE]) = zq;
+      *reinterpret_cast<uint4*>(&s.k[row][cc * kE]) = zk;
+    }
+  }
+  if (tid < kC) {
+    const bool ok = tid < rows;
+    const long gi = (cp.tok0 + t0 + tid) * p.H + h;
+    s.g[tid] = ok && p.g ? p.g[gi] : 0.f;
+    s.beta[tid] = ok ? p.beta[gi] : 0.f;
+  }
+  constexpr int kTPK = kThreads / K, kGT = kC / kTPK;
+  float gkr[PK ? kGT : 1];
+  if constexpr (PK) {
+    const int d = tid / kTPK, part = tid % kTPK;
+#pragma unroll
+    for (int i = 0; i < kGT; ++i) {
+      const int t = part * kGT + i;
+      gkr[i] = t < rows ? p.gk[((cp.tok0 + t0 + t) * p.H + h) * (long)K + d] : 0.f;
+    }
+  }
+  __syncthreads();
 
-  // State: h[G][t] holds keys 32G + 8lq + 4t + e (e = 0..3) of column col.
+  TO* slot = reinterpret_cast<TO*>(static_cast<char*>(p.ws) + (cp.slot0 + n) * SL::kBytes);
+  if constexpr (PK) {
+    // per-key gamma and the scaled Gram / Q K^T operands, in place
+    const int d = tid / kTPK, part = tid % kTPK;
+    float gam[kGT], gm, gL;
+    key_cumsum<K, kGT>(gkr, [&](int t) { return s.g[t]; }, part, gam, gm, gL);
+#pragma unroll
+    for (int i = 0; i < kGT; ++i) {
+      const int t = part * kGT + i;
+      const float up = __expf(gam[i] - gm), dn = __expf(gm - gam[i]);
+      const float kk = to_f(s.k[t][d]), qq = to_f(s.q[t][d]);
+      s.k[t][d] = to_t<TQ>(kk * up);
+      s.q[t][d] = to_t<TQ>(qq * up);
+      s.kb[t][d] = to_t<TQ>(kk * dn);
+    }
+  } else if (wave == 0) {
+    const float gam = wave_incl_scan(s.g[lane], lane);
+    const float gl = __shfl(gam, 63, 64);
+    s.gam[lane] = gam;
+    float* fs = reinterpret_cast<float*>(reinterpret_cast<char*>(slot) + SL::kEg);
+    fs[lane] = __expf(gam);
+    fs[kC + lane] = __expf(gl - gam);
+    if (lane == 0) fs[2 * kC] = __expf(gl);
+  }
+  __syncthreads();
+
+  // Gram (-> A) and Q K^T (-> P), lower 16x16 tiles
+#pragma unroll
+  for (int ji = 0; ji < 5; ++ji) {
+    const int job = wave + 4 * ji;
+    const bool is_qk = job >= 10;
+    int I, J;
+    tri_tile(is_qk ? job - 10 : job, I, J);
+    const TQ* arow = is_qk ? &s.q[16 * I + li][0] : &s.k[16 * I + li][0];
+    const TQ* brow = PK ? &s.kb[(16 * J + li) % (PK ? kC : 1)][0] : &s.k[16 * J + li][0];
+    Q8 av[kG], bv[kG];
+#pragma unroll
+    for (int kk = 0; kk < kG; ++kk) {
+      av[kk] = lds8(arow + 32 * kk + 8 * lq);
+      bv[kk] = lds8(brow + 32 * kk + 8 * lq);
+    }
+    const int sc = 16 * J + li;
+    float gr[4], br[4];
+    const float gs = PK ? 0.f : s.gam[sc];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gr[e] = PK ? 0.f : s.gam[16 * I + 4 * lq + e];
+      br[e] = s.beta[16 * I + 4 * lq + e];
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kG; ++kk) acc = mma16(av[kk], bv[kk], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + 4 * lq + e;
+      const float dd = PK ? 1.f : __expf(gr[e] - gs);
+      if (is_qk) s.p[r][sc] = to_t<TO>(sc <= r ? dd * acc[e] : 0.f);
+      else s.a[r][sc] = sc < r ? br[e] * dd * acc[e] : 0.f;
+    }
+  }
+  __syncthreads();
+  solve_unit_lower(s, wave, lane);
+
+  // Tm, P -> slot (row-major 64x64, 16-byte stores)
+  constexpr int kOE = Pad<TO>::kE;
+  for (int c = tid; c < 2 * kC * kC / kOE; c += kThreads) {
+    const int which = c / (kC * kC / kOE), cc = c % (kC * kC / kOE);
+    const int r = cc / (kC / kOE), c0 = (cc % (kC / kOE)) * kOE;
+    const TO* src = which ? &s.p[r][c0] : &s.tm[r][c0];
+    *reinterpret_cast<uint4*>(slot + (which ? SL::kP / sizeof(TO) : 0) + r * kC + c0) =
+        *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+// ======================================================================================
+// scan_kernel: one workgroup per (chain, 64-wide value block), chunks in order.
+// ======================================================================================
+template <typename TI, int K, bool PK>
+struct __attribute__((aligned(16))) ScanBuf {
+  typedef typename OpT<TI>::type TO;
+  typedef typename QKT<TI, PK>::type TQ;
+  TQ q[Lay<TQ, K>::kElems(kC)];   // Q rows (per-key: Q e^{gamma - gamma_mid})
+  TQ k[Lay<TQ, K>::kElems(kC)];   // K rows (per-key: K e^{gamma - gamma_mid})
+  TO kt[Lay<TO, kC>::kElems(K)];  // K^T (per-key: (K e^{gl - gamma})^T)
+  TI vt[Lay<TI, kC>::kElems(kBV)];
+  TO tm[Lay<TO, kC>::kElems(kC)];
+  TO p[Lay<TO, kC>::kElems(kC)];
+  float eg[kC], el[kC], beta[kC], g[kC];
+  float egl;
+  float emid[PK ? K : 1], eglk[PK ? K : 1];
+};
+
+template <typename TI, int K, bool PK>
+struct __attribute__((aligned(16))) ScanSmem {
+  static constexpr bool kDB = sizeof(TI) == 2;  // double-buffered (16-bit operands)
+  ScanBuf<TI, K, PK> buf[kDB ? 2 : 1];
+  TI stg[4][kC * 16];  // per-wave output staging
+};
+
+// register staging of one chunk for scan_kernel
+template <typename TI, int K, bool PK>
+struct ScanStage {
+  typedef typename OpT<TI>::type TO;
+  static constexpr int kE = Pad<TI>::kE;
+  static constexpr int kCPR = K / kE;
+  static constexpr int kNQ = kC * kCPR / kThreads;
+  static constexpr int kNV = (kBV / kE) / 4;
+  static constexpr int kOE = Pad<TO>::kE;
+  static constexpr int kNT = kC * kC / kOE / kThreads;  // Tm / P 16-byte loads per thread
+  static constexpr int kTPK = kThreads / K, kGT = kC / kTPK;
+  uint4 q[kNQ], k[kNQ], v[kNV], tm[kNT], p[kNT];
+  float vec;  // thread t < 64: e^gamma[t]; < 128: e^{gl-gamma}; < 192: beta; < 256: g
+  float egl;
+  float gk[PK ? kGT : 1];
+};
+
+template <typename TI, int K, bool PK>
+__device__ __forceinline__ void scan_load(ScanStage<TI, K, PK>& st, const FwdParams& p,
+                                          const ChunkPos& cp, int h, int n, int v0, int tid,
+                                          int wave, int lane) {
+  typedef ScanStage<TI, K, PK> St;
+  typedef typename OpT<TI>::type TO;
+  typedef Slot<TO> SL;
+  constexpr int kE = St::kE;
+  const TI* q = static_cast<const TI*>(p.q);
+  const TI* k = static_cast<const TI*>(p.k);
+  const TI* v = static_cast<const TI*>(p.v);
+  const long HK = (long)p.H * K, HV = (long)p.H * p.V;
+  const int t0 = n * kC, rows = cp.len - t0;
+#pragma unroll
+  for (int i = 0; i < St::kNQ; ++i) {
+    const int c = tid + kThreads * i;
+    const int row = c / St::kCPR, cc = c % St::kCPR;
+    st.q[i] = row < rows ? *reinterpret_cast<const uint4*>(q + (cp.tok0 + t0 + row) * HK + (long)h * K + cc * kE)
+                         : make_uint4(0, 0, 0, 0);
+  }
+  const bool ok = lane < rows;
+  const TI* krow = k + (cp.tok0 + t0 + lane) * HK + (long)h * K;
+  const TI* vrow = v + (cp.tok0 + t0 + lane) * HV + (long)h * p.V + v0;
+#pragma unroll
+  for (int i = 0; i < St::kNQ; ++i)
+    st.k[i] = ok ? *reinterpret_cast<const uint4*>(krow + (wave + 4 * i) * kE) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < St::kNV; ++i)
+    st.v[i] = ok ? *reinterpret_cast<const uint4*>(vrow + (wave + 4 * i) * kE) : make_uint4(0, 0, 0, 0);
+  const char* slot = static_cast<const char*>(p.ws) + (cp.slot0 + n) * SL::kBytes;
+#pragma unroll
+  for (int i = 0; i < St::kNT; ++i) {
+    const int c = tid + kThreads * i;
+    st.tm[i] = *reinterpret_cast<const uint4*>(slot + SL::kTm + c * 16);
+    st.p[i] = *reinterpret_cast<const uint4*>(slot + SL::kP + c * 16);
+  }
+  const int t = tid & 63;
+  const long gi = (cp.tok0 + t0 + t) * p.H + h;
+  const float* fs = reinterpret_cast<const float*>(slot + SL::kEg);
+  if (tid < 128) st.vec = PK ? 0.f : fs[tid];  // e^gamma, then e^{gl - gamma}
+  else if (tid < 192) st.vec = t < rows ? p.beta[gi] : 0.f;
+  else st.vec = (t < rows && p.g) ? p.g[gi] : 0.f;
+  st.egl = PK ? 0.f : fs[2 * kC];
+  if constexpr (PK) {
+    const int d = tid / St::kTPK, part = tid % St::kTPK;
+#pragma unroll
+    for (int i = 0; i < St::kGT; ++i) {
+      const int tt = part * St::kGT + i;
+      st.gk[i] = tt < rows ? p.gk[((cp.tok0 + t0 + tt) * p.H + h) * (long)K + d] : 0.f;
+    }
+  }
+}
+
+// Registers -> LDS buffer.  Per-key gate: stores raw q / k; scan_scale_pk then rescales.
+template <typename TI, int K, bool PK>
+__device__ __forceinline__ void scan_store(const ScanStage<TI, K, PK>& st, ScanBuf<TI, K, PK>& b,
+                                           int tid, int wave, int lane) {
+  typedef ScanStage<TI, K, PK> St;
+  typedef typename OpT<TI>::type TO;
+  typedef typename QKT<TI, PK>::type TQ;
+  typedef Lay<TQ, K> LQ;
+  typedef Lay<TO, kC> LO;
+  typedef Lay<TI, kC> LV;
+  constexpr int kE = St::kE, kOE = St::kOE;
+#pragma unroll
+  for (int i = 0; i < St::kNQ; ++i) {
+    const int c = tid + kThreads * i;
+    const int row = c / St::kCPR, cc = c % St::kCPR;
+    if constexpr (PK) {
+      const TI* e = reinterpret_cast<const TI*>(&st.q[i]);
+#pragma unroll
+      for (int j = 0; j < kE; ++j) b.q[LQ::pair(row, cc * kE + j)] = to_t<TQ>(to_f(e[j]));
+    } else {
+      *reinterpret_cast<uint4*>(&b.q[LQ::pair(row, cc * kE)]) = st.q[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < St::kNQ; ++i) {
+    const int cc = wave + 4 * i;
+    const TI* e = reinterpret_cast<const TI*>(&st.k[i]);
+    if constexpr (PK) {
+#pragma unroll
+      for (int j = 0; j < kE; ++j) b.k[LQ::pair(lane, cc * kE + j)] = to_t<TQ>(to_f(e[j]));
+    } else {
+      *reinterpret_cast<uint4*>(&b.k[LQ::pair(lane, cc * kE)]) = st.k[i];
+#pragma unroll
+      for (int j = 0; j < kE; ++j) b.kt[LO::pair(cc * kE + j, lane)] = to_t<TO>(to_f(e[j]));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < St::kNV; ++i) {
+    const int cc = wave + 4 * i;
+    const TI* e = reinterpret_cast<const TI*>(&st.v[i]);
+#pragma unroll
+    for (int j = 0; j < kE; ++j) b.vt[LV::seq(cc * kE + j, lane)] = e[j];
+  }
+#pragma unroll
+  for (int i = 0; i < St::kNT; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c / (kC / kOE), c0 = (c % (kC / kOE)) * kOE;
+    *reinterpret_cast<uint4*>(&b.tm[LO::pair(r, c0)]) = st.tm[i];
+    *reinterpret_cast<uint4*>(&b.p[LO::pair(r, c0)]) = st.p[i];
+  }
+  const int t = tid & 63;
+  if (tid < 64) b.eg[t] = st.vec;
+  else if (tid < 128) b.el[t] = st.vec;
+  else if (tid < 192) b.beta[t] = st.vec;
+  else b.g[t] = st.vec;
+  if (tid == 0) b.egl = st.egl;
+}
+
+// Per-key gate: gamma per key from b.g and the thread's gk, then K, Q rescaled in place, the
+// state-update operand (K e^{gl - gamma})^T, e^{gamma_mid} and e^{gl} per key.
+template <typename TI, int K, bool PK>
+__device__ __forceinline__ void scan_scale_pk(const ScanStage<TI, K, PK>& st,
+                                              ScanBuf<TI, K, PK>& b, int tid) {
+  typedef ScanStage<TI, K, PK> St;
+  typedef typename OpT<TI>::type TO;
+  typedef typename QKT<TI, PK>::type TQ;
+  typedef Lay<TQ, K> LQ;
+  typedef Lay<TO, kC> LO;
+  const int d = tid / St::kTPK, part = tid % St::kTPK;
+  float gam[St::kGT], gm, gL;
+  key_cumsum<K, St::kGT>(st.gk, [&](int t) { return b.g[t]; }, part, gam, gm, gL);
+  const float el_mid = __expf(gL - gm);
+  if (part == 0) {
+    b.emid[d] = __expf(gm);
+    b.eglk[d] = __expf(gL);
+  }
+#pragma unroll
+  for (int i = 0; i < St::kGT; ++i) {
+    const int t = part * St::kGT + i;
+    const float up = __expf(gam[i] - gm), dn = __expf(gm - gam[i]);
+    const float kk = to_f(b.k[LQ::pair(t, d)]), qq = to_f(b.q[LQ::pair(t, d)]);
+    b.k[LQ::pair(t, d)] = to_t<TQ>(kk * up);
+    b.q[LQ::pair(t, d)] = to_t<TQ>(qq * up);
+    b.kt[LO::pair(d, t)] = to_t<TO>(kk * dn * el_mid);
+  }
+}
+
+// Writes a wave's [rows x 16] staging tile (row-major, TI) to global memory with 16-byte
+// stores: row r goes to dst + r * row_stride; rows r >= valid_rows are skipped.
+template <typename TI>
+__device__ __forceinline__ void flush_tile(const TI* stg, int rows, TI* dst, long row_stride,
+                                           int lane, int valid_rows) {
+  constexpr int kE = Pad<TI>::kE;
+  constexpr int kCPR = 16 / kE;  // 16-byte chunks per 16-column row
+  for (int c = lane; c < rows * kCPR; c += 64) {
+    const int r = c / kCPR, part = c % kCPR;
+    if (r < valid_rows)
+      *reinterpret_cast<uint4*>(dst + r * row_stride + part * kE) =
+          *reinterpret_cast<const uint4*>(stg + r * 16 + part * kE);
+  }
+}
+
+template <typename TI, int K, bool VARLEN, bool PK>
+__global__ __launch_bounds__(kThreads) void scan_kernel(const FwdParams p) {
+  typedef typename OpT<TI>::type TO;
+  typedef typename QKT<TI, PK>::type TQ;
+  typedef typename Vec8<TI>::type V8;
+  typedef typename Vec8<TO>::type W8;
+  typedef typename Vec8<TQ>::type Q8;
+  typedef ScanSmem<TI, K, PK> SM;
+  typedef ScanBuf<TI, K, PK> BUF;
+  typedef ScanStage<TI, K, PK> St;
+  typedef Lay<TQ, K> LQ;
+  typedef Lay<TO, kC> LO;
+  typedef Lay<TI, kC> LV;
+  constexpr int kG = K / 32;  // key groups of 32
+  constexpr bool kDB = SM::kDB;
+  __shared__ SM s;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+
+  // Workgroup -> (chain, value block).  Consecutive workgroup ids are dealt round-robin to
+  // the 8 XCDs; remap so that the value blocks of one chain sit on one XCD and share its L2.
+  const int nwg = gridDim.x;
+  int logical = blockIdx.x;
+  if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int chain = logical / p.nvb;
+  const int v0 = (logical % p.nvb) * kBV;
+  const int h = chain % p.H;
+  const ChunkPos cp = chain_pos(p, chain, VARLEN);
+  const int nchunks = (cp.len + kC - 1) / kC;
+  const int col = v0 + 16 * wave + li;  // this lane's value column
+  const long HV = (long)p.H * p.V;
+
+  // State: hs[G][t] holds keys 32G + 8lq + 4t + e (e = 0..3) of column col.
   f32x4 hs[kG][2];
 #pragma unroll
   for (int G = 0; G < kG; ++G)
@@ -338,133 +689,74 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
       for (int e = 0; e < 4; ++e)
         hs[G][t][e] = p.h0 ? p.h0[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] : 0.f;
 
-  St st;
-  load_chunk<TI, K, PK>(st, p, tok0, h, 0, len, v0, tid);
-
   TI* o = static_cast<TI*>(p.o);
   TI* vnew_out = static_cast<TI*>(p.v_new);
   TI* hch = static_cast<TI*>(p.h_chunks);
+  TI* stg = s.stg[wave];
+
+  // Pipeline (16-bit operands, double-buffered LDS): chunk n+1's global loads are issued at
+  // the top of iteration n and written to the other LDS buffer halfway through it, before
+  // this chunk's output stores.  Global loads and stores share one completion counter on this
+  // architecture, so consuming the loads before issuing the stores keeps the wait for them
+  // from also waiting on the previous chunk's output writes.
+  St st;
+  scan_load<TI, K, PK>(st, p, cp, h, 0, v0, tid, wave, lane);
+  if constexpr (kDB) {
+    scan_store<TI, K, PK>(st, s.buf[0], tid, wave, lane);
+    __syncthreads();
+    if constexpr (PK) {
+      scan_scale_pk<TI, K, PK>(st, s.buf[0], tid);
+      __syncthreads();
+    }
+  }
 
   for (int n = 0; n < nchunks; ++n) {
     const int t0 = n * kC;
-    store_chunk<TI, K, PK>(st, s, tid);
-    float gkl[PK ? St::kGT : 1];  // this chunk's per-key log decays (before the prefetch reuses st)
-    if constexpr (PK) {
-#pragma unroll
-      for (int i = 0; i < St::kGT; ++i) gkl[i] = st.gk[i];
-    }
-    __syncthreads();
-    if (n + 1 < nchunks) load_chunk<TI, K, PK>(st, p, tok0, h, t0 + kC, len, v0, tid);
-
-    if constexpr (PK) {
-      // ---- per-key cumulative gate gamma[t][d] = sum_{i<=t} (g_i + gk_{i,d}) and the
-      // decay-scaled operands.  Thread tid owns key d = tid % K and tokens t1..t1+kGT-1.
-      const int d = tid % K, part = tid / K, t1 = part * St::kGT;
-      float gam[St::kGT];
-      float run = 0.f;
-#pragma unroll
-      for (int i = 0; i < St::kGT; ++i) {
-        run += s.gam[t1 + i] + gkl[i];
-        gam[i] = run;
-      }
-      s.gpart[part][d] = run;
+    BUF& b = s.buf[kDB ? (n & 1) : 0];
+    if constexpr (kDB) {
+      if (n + 1 < nchunks) scan_load<TI, K, PK>(st, p, cp, h, n + 1, v0, tid, wave, lane);
+    } else {
+      scan_store<TI, K, PK>(st, b, tid, wave, lane);
       __syncthreads();
-      float off = 0.f;
-      for (int pp = 0; pp < part; ++pp) off += s.gpart[pp][d];
-#pragma unroll
-      for (int i = 0; i < St::kGT; ++i) {
-        gam[i] += off;
-        if (t1 + i == kC / 2 - 1) s.gmid[d] = gam[i];
-        if (t1 + i == kC - 1) s.glast[d] = gam[i];  // padded rows add 0: last valid row's value
+      if constexpr (PK) {
+        scan_scale_pk<TI, K, PK>(st, b, tid);
+        __syncthreads();
       }
-      __syncthreads();
-      const float gm = s.gmid[d], gL = s.glast[d];
-      const float el_mid = __expf(gL - gm);
-      if (part == 0) {
-        s.emid[d] = __expf(gm);
-        s.eglk[d] = __expf(gL);
-      }
-#pragma unroll
-      for (int i = 0; i < St::kGT; ++i) {
-        const int t = t1 + i;
-        const float up = __expf(gam[i] - gm), dn = __expf(gm - gam[i]);
-        const float kk = to_f(s.k[t][d]), qq = to_f(s.q[t][d]);
-        s.k[t][d] = to_t<TQ>(kk * up);
-        s.q[t][d] = to_t<TQ>(qq * up);
-        s.kb[t][d] = to_t<TQ>(kk * dn);
-        s.kt[d][t] = to_t<TO>(kk * dn * el_mid);
-      }
-    } else if (wave == 0) {
-      const float gam = wave_incl_scan(s.gam[lane], lane);
-      const float gl = __shfl(gam, 63, 64);  // padded rows carry g = 0, so this is the last valid row
-      s.gam[lane] = gam;
-      s.eg[lane] = __expf(gam);
-      s.el[lane] = __expf(gl - gam);
-      if (lane == 0) s.egl = __expf(gl);
-    }
-    __syncthreads();
-
-    // ---- Gram (-> A) and Q K^T (-> P), lower 16x16 tiles.  Scalar gate: the decay
-    // e^{gamma_r - gamma_s} is applied in the epilogue.  Per-key gate: it is inside the
-    // operands (rows e^{gamma - gamma_mid} against columns e^{gamma_mid - gamma}).
-    for (int job = wave; job < 20; job += 4) {
-      const bool is_qk = job >= 10;
-      int I, J;
-      tri_tile(job % 10, I, J);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const TQ* arow = is_qk ? &s.q[16 * I + li][0] : &s.k[16 * I + li][0];
-      const TQ* brow = PK ? &s.kb[(16 * J + li) % (PK ? kC : 1)][0] : &s.k[16 * J + li][0];
-#pragma unroll
-      for (int kk = 0; kk < kG; ++kk) acc = mma16(lds8(arow + 32 * kk + 8 * lq), lds8(brow + 32 * kk + 8 * lq), acc);
-      const int sc = 16 * J + li;
-      const float gs = s.gam[sc];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * I + 4 * lq + e;
-        const float d = PK ? 1.f : __expf(s.gam[r] - gs);
-        if (is_qk) s.p[r][sc] = to_t<TO>(sc <= r ? d * acc[e] : 0.f);
-        else s.a[r][sc] = sc < r ? s.beta[r] * d * acc[e] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    solve_unit_lower(s, wave, lane);
-    // (bf16) operand copy of the inverse; fp32 reads it from s.a directly.
-    if (sizeof(TI) == 2) {
-      for (int e = tid; e < 10 * 256; e += kThreads) {
-        int I, J;
-        tri_tile(e >> 8, I, J);
-        const int r = 16 * I + ((e >> 4) & 15), c = 16 * J + (e & 15);
-        s.tm[r][c] = to_t<TO>(s.a[r][c]);
-      }
-      __syncthreads();
+      if (n + 1 < nchunks) scan_load<TI, K, PK>(st, p, cp, h, n + 1, v0, tid, wave, lane);
     }
 
-    // ---- per-wave: outputs and the state update for columns 16w..16w+15
     // B operand of the K h / Q h products (per-key gate: rows scaled by e^{gamma_mid})
     Q8 bh[kG];
 #pragma unroll
     for (int G = 0; G < kG; ++G) {
       if constexpr (PK) {
-        f32x4 a = hs[G][0], b = hs[G][1];
+        f32x4 a = hs[G][0], c = hs[G][1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] *= s.emid[32 * G + 8 * lq + e];
-          b[e] *= s.emid[32 * G + 8 * lq + 4 + e];
+          a[e] *= b.emid[32 * G + 8 * lq + e];
+          c[e] *= b.emid[32 * G + 8 * lq + 4 + e];
         }
-        bh[G] = pack8<TQ>(a, b);
+        bh[G] = pack8<TQ>(a, c);
       } else {
         bh[G] = pack8<TQ>(hs[G][0], hs[G][1]);
       }
     }
     if (hch) {
+      // state entering this chunk -> h_chunks[.., n, :, cols], 64 key rows per pass
 #pragma unroll
-      for (int G = 0; G < kG; ++G)
+      for (int half = 0; half < K / 64; ++half) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int G = 2 * half; G < 2 * half + 2; ++G)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            hch[((hbase + n) * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] = to_t<TI>(hs[G][t][e]);
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              stg[(32 * (G - 2 * half) + 8 * lq + 4 * t + e) * 16 + li] = to_t<TI>(hs[G][t][e]);
+        wave_lds_sync();
+        flush_tile<TI>(stg, kC, hch + ((cp.slot0 + n) * K + 64 * half) * (long)p.V + v0 + 16 * wave,
+                       p.V, lane, kC);
+        wave_lds_sync();
+      }
     }
 
     f32x4 xk[2][2], xq[2][2];
@@ -476,8 +768,8 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
         f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int G = 0; G < kG; ++G) {
-          ak = mma16(lds8(&s.k[r][32 * G + 8 * lq]), bh[G], ak);
-          aq = mma16(lds8(&s.q[r][32 * G + 8 * lq]), bh[G], aq);
+          ak = mma16(lds8(&b.k[LQ::pair(r, 32 * G + 8 * lq)]), bh[G], ak);
+          aq = mma16(lds8(&b.q[LQ::pair(r, 32 * G + 8 * lq)]), bh[G], aq);
         }
         xk[P][t] = ak;
         xq[P][t] = aq;
@@ -488,17 +780,14 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int P = 0; P < 2; ++P) {
       const int r0 = 32 * P + 8 * lq;
-      const V8 vv = lds8(&s.vt[16 * wave + li][r0]);
+      const V8 vv = lds8(&b.vt[LV::seq(16 * wave + li, r0)]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float xkj = j < 4 ? xk[P][0][j] : xk[P][1][j - 4];
-        const float eg = PK ? 1.f : s.eg[r0 + j];
-        by[P][j] = to_t<TO>(s.beta[r0 + j] * (to_f(vv[j]) - eg * xkj));
+        const float eg = PK ? 1.f : b.eg[r0 + j];
+        by[P][j] = to_t<TO>(b.beta[r0 + j] * (to_f(vv[j]) - eg * xkj));
       }
     }
-
-    const TO* tmb = (sizeof(TI) == 2) ? &s.tm[0][0] : reinterpret_cast<const TO*>(&s.a[0][0]);
-    const int tstride = (sizeof(TI) == 2) ? SM::kTP : SM::kAP;
 
     // v_new = Tm Y (Tm lower triangular: token group P contributes to groups G >= P).
     f32x4 vn[2][2];
@@ -509,7 +798,7 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
         const int r = pair_row(G, t, li);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int P = 0; P <= G; ++P) acc = mma16(lds8(tmb + r * tstride + 32 * P + 8 * lq), by[P], acc);
+        for (int P = 0; P <= G; ++P) acc = mma16(lds8(&b.tm[LO::pair(r, 32 * P + 8 * lq)]), by[P], acc);
         vn[G][t] = acc;
       }
 
@@ -521,11 +810,24 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float vj = j < 4 ? vn[P][0][j] : vn[P][1][j - 4];
-        bvs[P][j] = to_t<TO>(PK ? vj : vj * s.el[r0 + j]);
+        bvs[P][j] = to_t<TO>(PK ? vj : vj * b.el[r0 + j]);
       }
     }
 
-    // o = scale (diag(e^gamma) X_Q + P v_new)
+    if constexpr (kDB) {
+      // stage chunk n+1 into the other buffer (last read in iteration n-1)
+      if (n + 1 < nchunks) {
+        BUF& nb = s.buf[(n + 1) & 1];
+        scan_store<TI, K, PK>(st, nb, tid, wave, lane);
+        if constexpr (PK) {
+          __syncthreads();
+          scan_scale_pk<TI, K, PK>(st, nb, tid);
+        }
+      }
+    }
+
+    // o = scale (diag(e^gamma) X_Q + P v_new) -> staging tile -> 16-byte stores
+    const int rows_left = cp.len - t0;
 #pragma unroll
     for (int G = 0; G < 2; ++G)
 #pragma unroll
@@ -533,21 +835,33 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
         const int r = pair_row(G, t, li);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int P = 0; P <= G; ++P) acc = mma16(lds8(&s.p[r][32 * P + 8 * lq]), bv[P], acc);
+        for (int P = 0; P <= G; ++P) acc = mma16(lds8(&b.p[LO::pair(r, 32 * P + 8 * lq)]), bv[P], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int tl = 32 * G + 8 * lq + 4 * t + e;
-          if (t0 + tl < len) {
-            const long oi = ((tok0 + t0 + tl) * p.H + h) * (long)p.V + col;
-            const float eg = PK ? 1.f : s.eg[tl];
-            o[oi] = to_t<TI>(p.scale * (eg * xq[G][t][e] + acc[e]));
-            if (vnew_out) vnew_out[oi] = to_t<TI>(vn[G][t][e]);
-          }
+          const float eg = PK ? 1.f : b.eg[tl];
+          stg[tl * 16 + li] = to_t<TI>(p.scale * (eg * xq[G][t][e] + acc[e]));
         }
       }
+    wave_lds_sync();
+    flush_tile<TI>(stg, kC, o + (cp.tok0 + t0) * HV + (long)h * p.V + v0 + 16 * wave, HV, lane,
+                   rows_left);
+    if (vnew_out) {
+      wave_lds_sync();
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) stg[(32 * G + 8 * lq + 4 * t + e) * 16 + li] = to_t<TI>(vn[G][t][e]);
+      wave_lds_sync();
+      flush_tile<TI>(stg, kC, vnew_out + (cp.tok0 + t0) * HV + (long)h * p.V + v0 + 16 * wave, HV,
+                     lane, rows_left);
+    }
+    wave_lds_sync();
 
     // h <- e^gl h + K^T diag(e^{gl - gamma}) v_new
-    const float egl = s.egl;
+    const float egl = b.egl;
 #pragma unroll
     for (int G = 0; G < kG; ++G)
 #pragma unroll
@@ -556,10 +870,10 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_kernel(const FwdParams p) {
         f32x4 acc = hs[G][t] * egl;
         if constexpr (PK) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = hs[G][t][e] * s.eglk[32 * G + 8 * lq + 4 * t + e];
+          for (int e = 0; e < 4; ++e) acc[e] = hs[G][t][e] * b.eglk[32 * G + 8 * lq + 4 * t + e];
         }
 #pragma unroll
-        for (int P = 0; P < 2; ++P) acc = mma16(lds8(&s.kt[kr][32 * P + 8 * lq]), bvs[P], acc);
+        for (int P = 0; P < 2; ++P) acc = mma16(lds8(&b.kt[LO::pair(kr, 32 * P + 8 * lq)]), bvs[P], acc);
         hs[G][t] = acc;
       }
     __syncthreads();
@@ -605,38 +919,56 @@ __global__ __launch_bounds__(256) void varlen_tables_kernel(const int* cu, int N
   if (tid == 255 && offs) offs[N] = part[256];
 }
 
-}  // namespace
-
-hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream) {
-  const int nchains = varlen ? p.nseq * p.H : p.B * p.H;
-  const dim3 grid(nchains * p.nvb), block(kThreads);
-#define GDN_LAUNCH(TI, KK, VL, PK) \
-  hipLaunchKernelGGL((gdn_fwd_kernel<TI, KK, VL, PK>), grid, block, 0, stream, p)
-  const bool pk = p.gk != nullptr;
-  if (dtype == 1) {
-    if (K == 128) {
-      if (pk) {
-        if (varlen) GDN_LAUNCH(bf16, 128, true, true); else GDN_LAUNCH(bf16, 128, false, true);
-      } else {
-        if (varlen) GDN_LAUNCH(bf16, 128, true, false); else GDN_LAUNCH(bf16, 128, false, false);
-      }
-    } else {
-      if (pk) {
-        if (varlen) GDN_LAUNCH(bf16, 64, true, true); else GDN_LAUNCH(bf16, 64, false, true);
-      } else {
-        if (varlen) GDN_LAUNCH(bf16, 64, true, false); else GDN_LAUNCH(bf16, 64, false, false);
-      }
-    }
-  } else {
-    if (varlen) GDN_LAUNCH(float, 64, true, false); else GDN_LAUNCH(float, 64, false, false);
-  }
-#undef GDN_LAUNCH
+hipError_t launch_varlen_tables_impl(const int* cu, int N, int* offs, int* idx, hipStream_t stream) {
+  hipLaunchKernelGGL(varlen_tables_kernel, dim3(1), dim3(256), 0, stream, cu, N, offs, idx);
   return hipGetLastError();
 }
 
-hipError_t launch_varlen_tables(const int* cu, int N, int* offs, int* idx, hipStream_t stream) {
-  hipLaunchKernelGGL(varlen_tables_kernel, dim3(1), dim3(256), 0, stream, cu, N, offs, idx);
+template <typename TI, int K, bool VL, bool PK>
+hipError_t launch_pair(const FwdParams& p, long nslots, int nchains, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_prep_kernel<TI, K, VL, PK>), dim3(nslots), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((scan_kernel<TI, K, VL, PK>), dim3(nchains * p.nvb), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+size_t fwd_slot_bytes(int dtype) {
+  return dtype == 1 ? Slot<f16>::kBytes : Slot<float>::kBytes;
+}
+
+size_t fwd_workspace_bytes(long nslots, int nseq, int dtype) {
+  size_t b = (size_t)nslots * fwd_slot_bytes(dtype);
+  if (nseq > 0) b += ((size_t)(nseq + 1) * sizeof(int) + 255) & ~(size_t)255;
+  return b;
+}
+
+hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream) {
+  const int nchains = varlen ? p.nseq * p.H : p.B * p.H;
+  const long nslots = varlen ? (long)p.H * p.nt_total : (long)p.B * p.H * ((p.T + kC - 1) / kC);
+  if (varlen) {
+    hipError_t e = launch_varlen_tables_impl(p.cu, p.nseq, p.coffs, nullptr, stream);
+    if (e != hipSuccess) return e;
+  }
+  const bool pk = p.gk != nullptr;
+  if (dtype == 1) {
+    if (K == 128) {
+      if (pk) return varlen ? launch_pair<bf16, 128, true, true>(p, nslots, nchains, stream)
+                            : launch_pair<bf16, 128, false, true>(p, nslots, nchains, stream);
+      return varlen ? launch_pair<bf16, 128, true, false>(p, nslots, nchains, stream)
+                    : launch_pair<bf16, 128, false, false>(p, nslots, nchains, stream);
+    }
+    if (pk) return varlen ? launch_pair<bf16, 64, true, true>(p, nslots, nchains, stream)
+                          : launch_pair<bf16, 64, false, true>(p, nslots, nchains, stream);
+    return varlen ? launch_pair<bf16, 64, true, false>(p, nslots, nchains, stream)
+                  : launch_pair<bf16, 64, false, false>(p, nslots, nchains, stream);
+  }
+  return varlen ? launch_pair<float, 64, true, false>(p, nslots, nchains, stream)
+                : launch_pair<float, 64, false, false>(p, nslots, nchains, stream);
+}
+
+hipError_t launch_varlen_tables(const int* cu, int N, int* offs, int* idx, hipStream_t stream) {
+  return launch_varlen_tables_impl(cu, N, offs, idx, stream);
 }
 
 }  // namespace gdn

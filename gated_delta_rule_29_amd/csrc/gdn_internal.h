@@ -23,7 +23,14 @@ struct FwdParams {
   int nvb;            // V / 64 value blocks
   int nseq;           // packed batches: number of sequences
   int nt_total;       // packed batches: total chunks (h_chunks indexing)
+  void* ws;           // workspace: per-chunk slots, then (packed batches) chunk offsets
+  int* coffs;         // packed batches: chunk offsets table inside the workspace
 };
+
+// Workspace of a forward call with `nslots` chunk slots (B*H*NT dense, H*NT_total packed)
+// and, for packed batches, nseq + 1 chunk offsets.
+size_t fwd_workspace_bytes(long nslots, int nseq, int dtype);
+size_t fwd_slot_bytes(int dtype);
 
 hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream);
 hipError_t launch_varlen_tables(const int* cu, int N, int* offs, int* idx, hipStream_t stream);

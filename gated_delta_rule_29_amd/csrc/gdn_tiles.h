@@ -1,0 +1,37 @@
+// gdn_tiles.h -- LDS tile layouts for 16-bit operand tiles without padding.
+//
+// A tile is rows x COLS elements of 2 bytes, row-major, with the 16-byte "octets" of each row
+// permuted by an XOR so that the accesses the kernels make touch distinct LDS banks:
+//
+//  * Matrix-core operand reads take, in one instruction, one octet from each of 16 rows.
+//    With the pair-row mapping (rows 32G + 8(i/4) + 4t + i%4 for lane row i) the swizzles
+//    below give those 16 rows 16 distinct bank groups (256-byte rows: distinct octets;
+//    128-byte rows: distinct (row parity, octet) pairs, since two such rows share one pass
+//    over the banks).
+//  * Transposed stores (one token per lane, the same tile row for the whole wave) write one
+//    full row per instruction, which is conflict-free under any permutation of its octets.
+//  * Row-wise 16-byte stores (16 lanes per row) write a permutation of one row.
+#pragma once
+
+namespace gdn {
+
+// octet permutation for tiles whose rows are read 16 at a time in pair-row order
+template <int COLS>
+__device__ __forceinline__ int swz_pair(int r) {
+  if constexpr (COLS == 128) return (r & 3) | (((r >> 3) & 3) << 2);   // 16 octets per row
+  else return ((r >> 1) & 1) | (((r >> 3) & 3) << 1);                  // 8 octets per row
+}
+
+// octet permutation for 128-byte-row tiles whose rows are read 16 consecutive at a time
+__device__ __forceinline__ int swz_seq(int r) { return (r >> 1) & 7; }
+
+template <int COLS>
+__device__ __forceinline__ int tix_pair(int r, int c) {
+  return r * COLS + ((((c >> 3) ^ swz_pair<COLS>(r))) << 3) + (c & 7);
+}
+
+__device__ __forceinline__ int tix_seq64(int r, int c) {
+  return r * 64 + (((c >> 3) ^ swz_seq(r)) << 3) + (c & 7);
+}
+
+}  // namespace gdn
