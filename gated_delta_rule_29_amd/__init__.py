@@ -78,7 +78,7 @@ def gdn_fwd(q, k, v, beta, g=None, gk=None, scale=1.0, h0=None, *, want_ht=True,
     hch = torch.empty(B, H, NT, K, V, dtype=dt, device=dev) if want_h else None
     vn = torch.empty(B, T, H, V, dtype=dt, device=dev) if want_v_new else None
     lib = _lib.load()
-    ws_n = lib.gdn_fwd_workspace_bytes(B, T, H, K, V, _DT[dt])
+    ws_n = lib.gdn_fwd_workspace_bytes(B, T, H, K, V, _DT[dt], int(gk is not None))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     rc = lib.gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta), float(scale),
                      _ptr(h0), _ptr(o), _ptr(ht), _ptr(hch), _ptr(vn), B, T, H, K, V, _DT[dt],
@@ -131,7 +131,7 @@ def gdn_fwd_varlen(q, k, v, beta, cu_seqlens, g=None, gk=None, scale=1.0, h0=Non
     vn = torch.empty(1, T, H, V, dtype=dt, device=dev) if want_v_new else None
     offs = torch.empty(N + 1, dtype=torch.int32, device=dev) if want_tables else None
     idx = torch.empty(NT, 2, dtype=torch.int32, device=dev) if want_tables else None
-    ws_n = lib.gdn_fwd_varlen_workspace_bytes(T, N, H, K, V, _DT[dt])
+    ws_n = lib.gdn_fwd_varlen_workspace_bytes(T, N, H, K, V, _DT[dt], int(gk is not None))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     rc = lib.gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
                             float(scale), _ptr(cu_dev), _ptr(cu_host), N, _ptr(h0), _ptr(o),

@@ -23,10 +23,10 @@ SZ = ctypes.c_size_t
 SIGNATURES = {
     "gdn_abi_version": (I, []),
     "gdn_last_error": (ctypes.c_char_p, []),
-    "gdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I, I]),
+    "gdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I, I, I]),
     "gdn_fwd": (I, [P, P, P, P, P, P, F, P, P, P, P, P, I, I, I, I, I, I, P, SZ, P]),
     "gdn_varlen_num_chunks": (I, [P, I]),
-    "gdn_fwd_varlen_workspace_bytes": (SZ, [I, I, I, I, I, I]),
+    "gdn_fwd_varlen_workspace_bytes": (SZ, [I, I, I, I, I, I, I]),
     "gdn_fwd_varlen": (I, [P, P, P, P, P, P, F, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, P,
                            SZ, P]),
     "gdn_prep": (I, [P, P, P, P, P, F, F, P, P, P, P, P, P, P, I, I, I, I, P]),

@@ -56,6 +56,15 @@ int check_fwd_common(const void* q, const void* k, const void* v, const float* b
   return GDN_OK;
 }
 
+// 16-bit inputs are addressed with 32-bit buffer offsets over one head's rows.
+int check_row_span(int64_t tokens, int H, int K, int V, int dtype) {
+  const int64_t span = tokens * H * (K > V ? K : V) * 2;
+  if (dtype == GDN_DTYPE_BF16 && span >= ((int64_t)1 << 32))
+    return fail(GDN_ERR_UNSUPPORTED, "tokens*H*max(K,V)*2 = %lld bytes exceeds 32-bit buffer offsets",
+                (long long)span);
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,10 +73,10 @@ int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 const char* gdn_last_error(void) { return g_err; }
 
-size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype) {
-  (void)K; (void)V;
-  if (B <= 0 || T <= 0 || H <= 0 || (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)) return 0;
-  return gdn::fwd_workspace_bytes((long)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK), 0, dtype);
+size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype, int per_key) {
+  if (B <= 0 || T <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key != 0)) return 0;
+  return gdn::fwd_workspace_bytes((long)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK), 0, dtype, K,
+                                  per_key != 0);
 }
 
 int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* gk,
@@ -77,11 +86,13 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   int rc = check_fwd_common(q, k, v, beta, o, gk, H, K, V, dtype);
   if (rc) return rc;
   if (B <= 0 || T <= 0) return fail(GDN_ERR_INVALID, "B and T must be positive (got %d, %d)", B, T);
+  rc = check_row_span(T, H, K, V, dtype);
+  if (rc) return rc;
   const int64_t wgs = (int64_t)B * H * (V / 64), nslots = (int64_t)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK);
   if (wgs > INT32_MAX || nslots > INT32_MAX)
     return fail(GDN_ERR_INVALID, "B*H*(V/64) = %lld or B*H*chunks = %lld exceeds the grid limit",
                 (long long)wgs, (long long)nslots);
-  const size_t need = gdn_fwd_workspace_bytes(B, T, H, K, V, dtype);
+  const size_t need = gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, gk != nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
@@ -107,12 +118,12 @@ int gdn_varlen_num_chunks(const int* cu, int N) {
   return total > INT32_MAX ? -1 : (int)total;
 }
 
-size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype) {
-  (void)K; (void)V;
-  if (T_total <= 0 || N <= 0 || H <= 0 || (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)) return 0;
+size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype,
+                                      int per_key) {
+  if (T_total <= 0 || N <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key != 0)) return 0;
   // chunks <= T_total / 64 + N (each sequence adds at most one partial chunk)
   const long nt_max = (long)T_total / GDN_CHUNK + N;
-  return gdn::fwd_workspace_bytes((long)H * nt_max, N, dtype);
+  return gdn::fwd_workspace_bytes((long)H * nt_max, N, dtype, K, per_key != 0);
 }
 
 int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
@@ -126,6 +137,8 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
   if (!cu_seqlens || !cu_seqlens_host)
     return fail(GDN_ERR_INVALID, "cu_seqlens (device) and cu_seqlens_host must be non-null");
   if (N < 1 || T_total < 1) return fail(GDN_ERR_INVALID, "N and T_total must be positive (got %d, %d)", N, T_total);
+  rc = check_row_span(T_total, H, K, V, dtype);
+  if (rc) return rc;
   if (cu_seqlens_host[0] != 0) return fail(GDN_ERR_INVALID, "cu_seqlens[0] must be 0 (got %d)", cu_seqlens_host[0]);
   for (int i = 0; i < N; ++i)
     if (cu_seqlens_host[i + 1] <= cu_seqlens_host[i])
@@ -137,7 +150,7 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
   const int64_t wgs = (int64_t)N * H * (V / 64);
   if (wgs > INT32_MAX || (int64_t)H * nt > INT32_MAX)
     return fail(GDN_ERR_INVALID, "N*H*(V/64) or H*chunks exceeds the grid limit");
-  const size_t need = gdn::fwd_workspace_bytes((long)H * nt, N, dtype);
+  const size_t need = gdn::fwd_workspace_bytes((long)H * nt, N, dtype, K, gk != nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
@@ -152,7 +165,7 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
   p.o = o; p.ht = ht; p.h_chunks = h_chunks; p.v_new = v_new; p.cu = cu_seqlens;
   p.scale = scale; p.B = 1; p.T = T_total; p.H = H; p.V = V; p.nvb = V / 64;
   p.nseq = N; p.nt_total = nt; p.ws = workspace;
-  p.coffs = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)H * nt * gdn::fwd_slot_bytes(dtype));
+  p.coffs = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)H * nt * gdn::fwd_slot_bytes(dtype, K, gk != nullptr));
   hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, true, s);
   if (e != hipSuccess) return hip_fail(e, "gdn_fwd_varlen launch");
   return ok();

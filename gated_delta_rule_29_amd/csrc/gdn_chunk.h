@@ -1,0 +1,141 @@
+// gdn_chunk.h -- definitions shared by the chunkwise forward kernels (prep, state scans):
+// chunk geometry, operand types, chain positions, workspace slot layouts and LDS tile layouts.
+#pragma once
+
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdn_tiles.h"
+
+namespace gdn {
+namespace chunk {
+
+constexpr int kC = 64;  // chunk length (tokens)
+
+template <typename TI>
+struct Pad {
+  static constexpr int kE = 16 / sizeof(TI);  // elements per 16 bytes
+};
+
+// Operand type of the intra-chunk products (Tm Y, P v_new, K^T v_new).  For bf16 inputs these
+// use fp16 operands: the factors are bounded (unit-norm keys give |P|, |A| <= 1, and Y, v_new
+// stay O(|v|)), and fp16's 11 significant bits keep the stored bf16 output within tolerance
+// where 8-bit operands would not.  The fp32 path stays fp32 throughout.
+template <typename TI>
+struct OpT;
+template <>
+struct OpT<bf16> {
+  typedef f16 type;
+};
+template <>
+struct OpT<float> {
+  typedef float type;
+};
+
+// Type of the q / k tiles: the inputs as given for a scalar gate; for a per-key gate they
+// hold the decay-scaled operands, so they take the intra-chunk operand type.
+template <typename TI, bool PK>
+struct QKT {
+  typedef typename std::conditional<PK, typename OpT<TI>::type, TI>::type type;
+};
+
+// Row of the 16-row A-operand tile t (0/1) of 32-group G that lane row li supplies.
+__device__ __forceinline__ int pair_row(int G, int t, int li) {
+  return 32 * G + 8 * (li >> 2) + 4 * t + (li & 3);
+}
+
+// Makes one wave's LDS writes visible to its other lanes before they read.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Tile layouts: 16-bit tiles are unpadded and XOR-swizzled (gdn_tiles.h); fp32 tiles are
+// padded by 16 bytes per row.
+template <typename T, int COLS>
+struct Lay {
+  static constexpr bool kSwz = sizeof(T) == 2;
+  static constexpr int kStride = kSwz ? COLS : COLS + 16 / (int)sizeof(T);
+  static constexpr int kElems(int rows) { return rows * kStride; }
+  __device__ static int pair(int r, int c) {
+    if constexpr (kSwz) return tix_pair<COLS>(r, c);
+    else return r * kStride + c;
+  }
+  __device__ static int seq(int r, int c) {
+    if constexpr (kSwz) {
+      static_assert(!kSwz || COLS == 64, "sequential-row swizzle is defined for 64 columns");
+      return tix_seq64(r, c);
+    } else {
+      return r * kStride + c;
+    }
+  }
+};
+
+// Workspace slot of one chunk, fp32 inputs: Tm, P (64x64 fp32, row-major), e^gamma,
+// e^{gl - gamma}, e^gl.
+struct SlotF {
+  static constexpr size_t kTm = 0;
+  static constexpr size_t kP = (size_t)kC * kC * sizeof(float);
+  static constexpr size_t kEg = 2 * kP;
+  static constexpr size_t kEl = kEg + kC * 4;
+  static constexpr size_t kEgl = kEl + kC * 4;
+  static constexpr size_t kBytes = (kEgl + 16 + 255) & ~(size_t)255;
+};
+
+// Workspace slot of one chunk, 16-bit inputs.  Every region is the exact image of the LDS
+// tile the scan keeps it in, so the scan copies it with linear 16-byte transfers:
+//   Tm, P     [64][64] fp16 in the pair-row layout (tix_pair<64>)
+//   vec       scalar gate: e^gamma[64], e^{gl-gamma}[64], beta[64], e^gl, padding
+//             per-key gate: beta[64], e^{gamma_mid}[K], e^{gamma_last}[K], padding
+//   per-key gate only: Q e^{gamma-gamma_mid}, K e^{gamma-gamma_mid} ([64][K] fp16,
+//             tix_pair<K>) and K e^{gamma_last-gamma} ([64][K] fp16, tix_pair<K>).
+template <int K, bool PK>
+struct Slot16 {
+  static constexpr size_t kTile = (size_t)kC * K * 2;
+  static constexpr size_t kTm = 0;
+  static constexpr size_t kP = kC * kC * 2;
+  static constexpr size_t kVec = 2 * kP;
+  static constexpr size_t kVecBytes = PK ? (((kC + 2 * K) * 4 + 1023) & ~(size_t)1023) : 1024;
+  static constexpr size_t kQ = kVec + kVecBytes;
+  static constexpr size_t kK = kQ + (PK ? kTile : 0);
+  static constexpr size_t kKh = kK + (PK ? kTile : 0);
+  static constexpr size_t kBytes = kKh + (PK ? kTile : 0);
+  // float offsets inside vec
+  static constexpr int kEg = 0, kEl = kC, kBeta = PK ? 0 : 2 * kC, kEgl = 3 * kC;
+  static constexpr int kEmid = kC, kEglk = kC + K;
+  static_assert(kBytes % 1024 == 0, "slot regions are whole 1 KiB blocks");
+};
+
+// Where a chain lives: first token, token count, workspace / h_chunks index of chunk 0.
+struct ChunkPos {
+  long tok0;
+  int len;
+  long slot0;
+};
+
+__device__ __forceinline__ ChunkPos chain_pos(const FwdParams& p, int chain, bool varlen) {
+  ChunkPos c;
+  const int h = chain % p.H, bs = chain / p.H;
+  if (varlen) {
+    c.tok0 = p.cu[bs];
+    c.len = p.cu[bs + 1] - p.cu[bs];
+    c.slot0 = (long)h * p.nt_total + p.coffs[bs];
+  } else {
+    c.tok0 = (long)bs * p.T;
+    c.len = p.T;
+    c.slot0 = (long)chain * ((p.T + kC - 1) / kC);
+  }
+  return c;
+}
+
+}  // namespace chunk
+
+// Scan of 16-bit inputs (gdn_scan16.hip): one workgroup per (chain, 64-column value block).
+hipError_t launch_scan16(const FwdParams& p, int K, bool varlen, bool pk, int nchains,
+                         hipStream_t stream);
+
+}  // namespace gdn

@@ -36,113 +36,16 @@
 // 32G + 8(i/4) + 4t + i%4: "pair rows"), which makes the state directly the B operand of the
 // next chunk's K h / Q h products.  Token-indexed results (X_K, v_new, o) use the same mapping
 // over tokens, so v_new feeds P v_new and K^T v_new directly too.
-#include <type_traits>
-
-#include "gdn_device.h"
-#include "gdn_internal.h"
-#include "gdn_tiles.h"
+#include "gdn_chunk.h"
 
 namespace gdn {
 
 namespace {
 
+using namespace chunk;
+
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kBV = 64;        // value columns per scan workgroup
-constexpr int kC = 64;         // chunk length
-
-template <typename TI>
-struct Pad {
-  static constexpr int kE = 16 / sizeof(TI);  // elements per 16 bytes
-};
-
-// Operand type of the intra-chunk products (Tm Y, P v_new, K^T v_new).  For bf16 inputs these
-// use fp16 operands: the factors are bounded (unit-norm keys give |P|, |A| <= 1, and Y, v_new
-// stay O(|v|)), and fp16's 11 significant bits keep the stored bf16 output within tolerance
-// where 8-bit operands would not.  The fp32 path stays fp32 throughout.
-template <typename TI>
-struct OpT;
-template <>
-struct OpT<bf16> {
-  typedef f16 type;
-};
-template <>
-struct OpT<float> {
-  typedef float type;
-};
-
-// Type of the q / k tiles: the inputs as given for a scalar gate; for a per-key gate they
-// hold the decay-scaled operands, so they take the intra-chunk operand type.
-template <typename TI, bool PK>
-struct QKT {
-  typedef typename std::conditional<PK, typename OpT<TI>::type, TI>::type type;
-};
-
-// Row of the 16-row A-operand tile t (0/1) of 32-group G that lane row li supplies.
-__device__ __forceinline__ int pair_row(int G, int t, int li) {
-  return 32 * G + 8 * (li >> 2) + 4 * t + (li & 3);
-}
-
-// Makes one wave's LDS writes visible to its other lanes before they read.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Tile layouts: 16-bit tiles are unpadded and XOR-swizzled (gdn_tiles.h); fp32 tiles are
-// padded by 16 bytes per row.
-template <typename T, int COLS>
-struct Lay {
-  static constexpr bool kSwz = sizeof(T) == 2;
-  static constexpr int kStride = kSwz ? COLS : COLS + 16 / (int)sizeof(T);
-  static constexpr int kElems(int rows) { return rows * kStride; }
-  __device__ static int pair(int r, int c) {
-    if constexpr (kSwz) return tix_pair<COLS>(r, c);
-    else return r * kStride + c;
-  }
-  __device__ static int seq(int r, int c) {
-    if constexpr (kSwz) {
-      static_assert(!kSwz || COLS == 64, "sequential-row swizzle is defined for 64 columns");
-      return tix_seq64(r, c);
-    } else {
-      return r * kStride + c;
-    }
-  }
-};
-
-// Workspace slot of one chunk: Tm, P (64x64 operand type), e^gamma, e^{gl - gamma}, e^gl.
-template <typename TO>
-struct Slot {
-  static constexpr size_t kTm = 0;
-  static constexpr size_t kP = (size_t)kC * kC * sizeof(TO);
-  static constexpr size_t kEg = 2 * kP;
-  static constexpr size_t kEl = kEg + kC * 4;
-  static constexpr size_t kEgl = kEl + kC * 4;
-  static constexpr size_t kBytes = (kEgl + 16 + 255) & ~(size_t)255;
-};
-
-// Where a chunk lives: chain index (b*H + h or seq*H + h), first token, its chunk number in
-// the chain, and the chain's token count.
-struct ChunkPos {
-  long tok0;  // first token of the chain
-  int len;    // tokens in the chain
-  long slot0; // workspace / h_chunks index of the chain's chunk 0
-};
-
-__device__ __forceinline__ ChunkPos chain_pos(const FwdParams& p, int chain, bool varlen) {
-  ChunkPos c;
-  const int h = chain % p.H, bs = chain / p.H;
-  if (varlen) {
-    c.tok0 = p.cu[bs];
-    c.len = p.cu[bs + 1] - p.cu[bs];
-    c.slot0 = (long)h * p.nt_total + p.coffs[bs];
-  } else {
-    c.tok0 = (long)bs * p.T;
-    c.len = p.T;
-    c.slot0 = (long)chain * ((p.T + kC - 1) / kC);
-  }
-  return c;
-}
+constexpr int kBV = 64;        // value columns per fp32 scan workgroup
 
 hipError_t launch_varlen_tables_impl(const int* cu, int N, int* offs, int* idx, hipStream_t stream);
 
@@ -201,6 +104,7 @@ struct __attribute__((aligned(16))) PrepSmem {
   TQ q[kC][kKP];
   TQ k[kC][kKP];
   TQ kb[PK ? kC : 1][kKP];
+  TQ kh[PK ? kC : 1][kKP];  // per-key gate: K e^{gamma_last - gamma}
   TO tm[kC][kTP];
   TO p[kC][kTP];
   float a[kC][kAP];
@@ -290,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p)
   typedef typename QKT<TI, PK>::type TQ;
   typedef typename Vec8<TQ>::type Q8;
   typedef PrepSmem<TI, K, PK> SM;
-  typedef Slot<TO> SL;
+  typedef SlotF SL;
   constexpr int kG = K / 32;
   constexpr int kE = Pad<TI>::kE;
   constexpr int kCPR = K / kE;
@@ -374,9 +278,15 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p)
   }
   __syncthreads();
 
-  TO* slot = reinterpret_cast<TO*>(static_cast<char*>(p.ws) + (cp.slot0 + n) * SL::kBytes);
+  // 16-bit inputs: the slot holds LDS images for the 16-bit scan (Slot16); fp32: SlotF
+  constexpr bool k16 = sizeof(TI) == 2;
+  typedef Slot16<K, PK> S16;
+  constexpr size_t kSlotBytes = k16 ? S16::kBytes : SL::kBytes;
+  char* slot = static_cast<char*>(p.ws) + (cp.slot0 + n) * kSlotBytes;
+  float* vec = reinterpret_cast<float*>(slot + (k16 ? S16::kVec : SL::kEg));
   if constexpr (PK) {
-    // per-key gamma and the scaled Gram / Q K^T operands, in place
+    // per-key gamma and the scaled Gram / Q K^T operands, in place; the state-update
+    // operand K e^{gamma_last - gamma}; beta, e^{gamma_mid}, e^{gamma_last} to the slot
     const int d = tid / kTPK, part = tid % kTPK;
     float gam[kGT], gm, gL;
     key_cumsum<K, kGT>(gkr, [&](int t) { return s.g[t]; }, part, gam, gm, gL);
@@ -388,15 +298,27 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p)
       s.k[t][d] = to_t<TQ>(kk * up);
       s.q[t][d] = to_t<TQ>(qq * up);
       s.kb[t][d] = to_t<TQ>(kk * dn);
+      s.kh[t][d] = to_t<TQ>(kk * __expf(gL - gam[i]));
     }
+    if (part == 0) {
+      vec[S16::kEmid + d] = __expf(gm);
+      vec[S16::kEglk + d] = __expf(gL);
+    }
+    if (tid < kC) vec[S16::kBeta + tid] = s.beta[tid];
   } else if (wave == 0) {
     const float gam = wave_incl_scan(s.g[lane], lane);
     const float gl = __shfl(gam, 63, 64);
     s.gam[lane] = gam;
-    float* fs = reinterpret_cast<float*>(reinterpret_cast<char*>(slot) + SL::kEg);
-    fs[lane] = __expf(gam);
-    fs[kC + lane] = __expf(gl - gam);
-    if (lane == 0) fs[2 * kC] = __expf(gl);
+    if constexpr (k16) {
+      vec[S16::kEg + lane] = __expf(gam);
+      vec[S16::kEl + lane] = __expf(gl - gam);
+      vec[S16::kBeta + lane] = s.beta[lane];
+      if (lane == 0) vec[S16::kEgl] = __expf(gl);
+    } else {
+      vec[lane] = __expf(gam);
+      vec[kC + lane] = __expf(gl - gam);
+      if (lane == 0) vec[2 * kC] = __expf(gl);
+    }
   }
   __syncthreads();
 
@@ -437,14 +359,28 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p)
   __syncthreads();
   solve_unit_lower(s, wave, lane);
 
-  // Tm, P -> slot (row-major 64x64, 16-byte stores)
+  // Tm, P -> slot, 16-byte pieces (16-bit: in the scan's pair-row tile layout)
   constexpr int kOE = Pad<TO>::kE;
+  TO* tslot = reinterpret_cast<TO*>(slot);
   for (int c = tid; c < 2 * kC * kC / kOE; c += kThreads) {
     const int which = c / (kC * kC / kOE), cc = c % (kC * kC / kOE);
     const int r = cc / (kC / kOE), c0 = (cc % (kC / kOE)) * kOE;
     const TO* src = which ? &s.p[r][c0] : &s.tm[r][c0];
-    *reinterpret_cast<uint4*>(slot + (which ? SL::kP / sizeof(TO) : 0) + r * kC + c0) =
-        *reinterpret_cast<const uint4*>(src);
+    int dst = r * kC + c0;
+    if constexpr (k16) dst = tix_pair<kC>(r, c0);
+    *reinterpret_cast<uint4*>(tslot + (which ? kC * kC : 0) + dst) = *reinterpret_cast<const uint4*>(src);
+  }
+  if constexpr (PK) {
+    // scaled Q, K and the update operand, in the scan's tix_pair<K> tile layout
+    constexpr int kPieces = kC * K / 8;
+    for (int c = tid; c < 3 * kPieces; c += kThreads) {
+      const int which = c / kPieces, cc = c % kPieces;
+      const int r = cc / (K / 8), c0 = (cc % (K / 8)) * 8;
+      const TQ* src = which == 0 ? &s.q[r][c0] : (which == 1 ? &s.k[r][c0] : &s.kh[r][c0]);
+      const size_t base = which == 0 ? S16::kQ : (which == 1 ? S16::kK : S16::kKh);
+      *reinterpret_cast<uint4*>(slot + base + 2 * tix_pair<K>(r, c0)) =
+          *reinterpret_cast<const uint4*>(src);
+    }
   }
 }
 
@@ -496,7 +432,7 @@ __device__ __forceinline__ void scan_load(ScanStage<TI, K, PK>& st, const FwdPar
                                           int wave, int lane) {
   typedef ScanStage<TI, K, PK> St;
   typedef typename OpT<TI>::type TO;
-  typedef Slot<TO> SL;
+  typedef SlotF SL;
   constexpr int kE = St::kE;
   const TI* q = static_cast<const TI*>(p.q);
   const TI* k = static_cast<const TI*>(p.k);
@@ -927,18 +863,26 @@ hipError_t launch_varlen_tables_impl(const int* cu, int N, int* offs, int* idx, 
 template <typename TI, int K, bool VL, bool PK>
 hipError_t launch_pair(const FwdParams& p, long nslots, int nchains, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_prep_kernel<TI, K, VL, PK>), dim3(nslots), dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL((scan_kernel<TI, K, VL, PK>), dim3(nchains * p.nvb), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (sizeof(TI) == 2) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_scan16(p, K, VL, PK, nchains, stream);
+  } else {
+    hipLaunchKernelGGL((scan_kernel<TI, K, VL, PK>), dim3(nchains * p.nvb), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
 }
 
 }  // namespace
 
-size_t fwd_slot_bytes(int dtype) {
-  return dtype == 1 ? Slot<f16>::kBytes : Slot<float>::kBytes;
+size_t fwd_slot_bytes(int dtype, int K, bool pk) {
+  if (dtype != 1) return chunk::SlotF::kBytes;
+  if (K == 128) return pk ? chunk::Slot16<128, true>::kBytes : chunk::Slot16<128, false>::kBytes;
+  return pk ? chunk::Slot16<64, true>::kBytes : chunk::Slot16<64, false>::kBytes;
 }
 
-size_t fwd_workspace_bytes(long nslots, int nseq, int dtype) {
-  size_t b = (size_t)nslots * fwd_slot_bytes(dtype);
+size_t fwd_workspace_bytes(long nslots, int nseq, int dtype, int K, bool pk) {
+  size_t b = (size_t)nslots * fwd_slot_bytes(dtype, K, pk);
   if (nseq > 0) b += ((size_t)(nseq + 1) * sizeof(int) + 255) & ~(size_t)255;
   return b;
 }

@@ -29,8 +29,8 @@ struct FwdParams {
 
 // Workspace of a forward call with `nslots` chunk slots (B*H*NT dense, H*NT_total packed)
 // and, for packed batches, nseq + 1 chunk offsets.
-size_t fwd_workspace_bytes(long nslots, int nseq, int dtype);
-size_t fwd_slot_bytes(int dtype);
+size_t fwd_workspace_bytes(long nslots, int nseq, int dtype, int K, bool per_key);
+size_t fwd_slot_bytes(int dtype, int K, bool per_key);
 
 hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream);
 hipError_t launch_varlen_tables(const int* cu, int N, int* offs, int* idx, hipStream_t stream);

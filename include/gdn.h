@@ -44,7 +44,7 @@ extern "C" {
 #define GDN_API
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 #define GDN_CHUNK 64
 
 /* Status codes (the pages' wrappers raise ValueError / NotImplementedError / RuntimeError
@@ -85,12 +85,20 @@ GDN_API const char* gdn_last_error(void);
  *                                      h_chunks[.., 0, ..] = h0; NULL = not written
  *   v_new     [B, T, H, V]  dtype      per-token delta d_t = beta_t (v_t - S'^T k_t), the
  *                                      v_new = u - w h of the state pass; NULL = not written
- *   workspace, workspace_bytes          at least gdn_fwd_workspace_bytes(...) bytes (0 today;
- *                                      a NULL workspace is accepted when the size is 0)
+ *   workspace, workspace_bytes          caller-owned device scratch, 256-byte aligned, of at
+ *                                      least gdn_fwd_workspace_bytes(B, T, H, K, V, dtype,
+ *                                      gk != NULL) bytes.  The call fills it with per-chunk
+ *                                      terms (WY inverse, masked Q K^T, decays) and reads them
+ *                                      back; it is free again once the call's work on
+ *                                      `stream` has completed.  Too small or NULL:
+ *                                      GDN_ERR_WORKSPACE.
  * Supported: K in {64, 128}, V in {64, 128} for bf16; K = 64 and V in {64, 128} for fp32
- * (gk is bf16 only).  B, T, H >= 1 and B*H*(V/64) <= 2^31 - 1 (else GDN_ERR_INVALID).
+ * (gk is bf16 only).  B, T, H >= 1 and B*H*(V/64) <= 2^31 - 1 (else GDN_ERR_INVALID); bf16
+ * also needs T*H*max(K, V)*2 < 2^32, the byte span of one head's rows (else
+ * GDN_ERR_UNSUPPORTED).  The size query returns 0 for arguments it cannot size.
  */
-GDN_API size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype);
+GDN_API size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype,
+                                       int per_key);
 GDN_API int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* gk,
             const float* beta, float scale, const float* h0, void* o, float* ht, void* h_chunks,
             void* v_new, int B, int T, int H, int K, int V, int dtype, void* workspace,
@@ -107,7 +115,9 @@ GDN_API int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
  */
 GDN_API int gdn_varlen_num_chunks(const int* cu_seqlens_host, int N);
 
-GDN_API size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype);
+/* Workspace bound for any packing of T_total tokens into N sequences (per_key: gk given). */
+GDN_API size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype,
+                                              int per_key);
 
 /*
  *   cu_seqlens       [N+1] int32 device   offsets, cu[0] = 0, strictly increasing,
