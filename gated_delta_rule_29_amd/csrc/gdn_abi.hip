@@ -88,9 +88,9 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   if (B <= 0 || T <= 0) return fail(GDN_ERR_INVALID, "B and T must be positive (got %d, %d)", B, T);
   rc = check_row_span(T, H, K, V, dtype);
   if (rc) return rc;
-  const int64_t wgs = (int64_t)B * H * (V / 64), nslots = (int64_t)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK);
+  const int64_t wgs = (int64_t)B * H * (V / 32), nslots = (int64_t)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK);
   if (wgs > INT32_MAX || nslots > INT32_MAX)
-    return fail(GDN_ERR_INVALID, "B*H*(V/64) = %lld or B*H*chunks = %lld exceeds the grid limit",
+    return fail(GDN_ERR_INVALID, "B*H*(V/32) = %lld or B*H*chunks = %lld exceeds the grid limit",
                 (long long)wgs, (long long)nslots);
   const size_t need = gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, gk != nullptr);
   if (!workspace || workspace_bytes < need)
@@ -147,9 +147,9 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
     return fail(GDN_ERR_INVALID, "cu_seqlens[N] = %d differs from T_total = %d", cu_seqlens_host[N], T_total);
   const int nt = gdn_varlen_num_chunks(cu_seqlens_host, N);
   if (nt < 0) return fail(GDN_ERR_INVALID, "too many chunks");
-  const int64_t wgs = (int64_t)N * H * (V / 64);
+  const int64_t wgs = (int64_t)N * H * (V / 32);
   if (wgs > INT32_MAX || (int64_t)H * nt > INT32_MAX)
-    return fail(GDN_ERR_INVALID, "N*H*(V/64) or H*chunks exceeds the grid limit");
+    return fail(GDN_ERR_INVALID, "N*H*(V/32) or H*chunks exceeds the grid limit");
   const size_t need = gdn::fwd_workspace_bytes((long)H * nt, N, dtype, K, gk != nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);

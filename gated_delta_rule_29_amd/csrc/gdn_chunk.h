@@ -87,12 +87,13 @@ struct SlotF {
 };
 
 // Workspace slot of one chunk, 16-bit inputs.  Every region is the exact image of the LDS
-// tile the scan keeps it in, so the scan copies it with linear 16-byte transfers:
-//   Tm, P     [64][64] fp16 in the pair-row layout (tix_pair<64>)
+// tile the scan keeps it in (column-split layout tix_s32<64>), so the scan copies it with
+// linear 16-byte transfers:
+//   Tm, P     [64][64] fp16
 //   vec       scalar gate: e^gamma[64], e^{gl-gamma}[64], beta[64], e^gl, padding
 //             per-key gate: beta[64], e^{gamma_mid}[K], e^{gamma_last}[K], padding
-//   per-key gate only: Q e^{gamma-gamma_mid}, K e^{gamma-gamma_mid} ([64][K] fp16,
-//             tix_pair<K>) and K e^{gamma_last-gamma} ([64][K] fp16, tix_pair<K>).
+//   K         [64][K] fp16: K itself (scalar gate) or K e^{gamma-gamma_mid} (per-key gate)
+//   per-key gate only: Q e^{gamma-gamma_mid} and K e^{gamma_last-gamma}, [64][K] fp16
 template <int K, bool PK>
 struct Slot16 {
   static constexpr size_t kTile = (size_t)kC * K * 2;
@@ -100,9 +101,9 @@ struct Slot16 {
   static constexpr size_t kP = kC * kC * 2;
   static constexpr size_t kVec = 2 * kP;
   static constexpr size_t kVecBytes = PK ? (((kC + 2 * K) * 4 + 1023) & ~(size_t)1023) : 1024;
-  static constexpr size_t kQ = kVec + kVecBytes;
-  static constexpr size_t kK = kQ + (PK ? kTile : 0);
-  static constexpr size_t kKh = kK + (PK ? kTile : 0);
+  static constexpr size_t kK = kVec + kVecBytes;
+  static constexpr size_t kQ = kK + kTile;
+  static constexpr size_t kKh = kQ + (PK ? kTile : 0);
   static constexpr size_t kBytes = kKh + (PK ? kTile : 0);
   // float offsets inside vec
   static constexpr int kEg = 0, kEl = kC, kBeta = PK ? 0 : 2 * kC, kEgl = 3 * kC;

@@ -367,19 +367,28 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p)
     const int r = cc / (kC / kOE), c0 = (cc % (kC / kOE)) * kOE;
     const TO* src = which ? &s.p[r][c0] : &s.tm[r][c0];
     int dst = r * kC + c0;
-    if constexpr (k16) dst = tix_pair<kC>(r, c0);
+    if constexpr (k16) dst = tix_s32<kC>(r, c0);
     *reinterpret_cast<uint4*>(tslot + (which ? kC * kC : 0) + dst) = *reinterpret_cast<const uint4*>(src);
   }
   if constexpr (PK) {
-    // scaled Q, K and the update operand, in the scan's tix_pair<K> tile layout
+    // scaled Q, K and the update operand, in the scan's column-split tile layout
     constexpr int kPieces = kC * K / 8;
     for (int c = tid; c < 3 * kPieces; c += kThreads) {
       const int which = c / kPieces, cc = c % kPieces;
       const int r = cc / (K / 8), c0 = (cc % (K / 8)) * 8;
       const TQ* src = which == 0 ? &s.q[r][c0] : (which == 1 ? &s.k[r][c0] : &s.kh[r][c0]);
       const size_t base = which == 0 ? S16::kQ : (which == 1 ? S16::kK : S16::kKh);
-      *reinterpret_cast<uint4*>(slot + base + 2 * tix_pair<K>(r, c0)) =
+      *reinterpret_cast<uint4*>(slot + base + 2 * tix_s32<kC>(r, c0)) =
           *reinterpret_cast<const uint4*>(src);
+    }
+  } else if constexpr (k16) {
+    // K as fp16 (exact for bf16 values in fp16's normal range), column-split layout
+    for (int c = tid; c < kC * K / 8; c += kThreads) {
+      const int r = c / (K / 8), c0 = (c % (K / 8)) * 8;
+      typename Vec8<f16>::type h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = (f16)to_f(s.k[r][c0 + j]);
+      *reinterpret_cast<typename Vec8<f16>::type*>(slot + S16::kK + 2 * tix_s32<kC>(r, c0)) = h;
     }
   }
 }

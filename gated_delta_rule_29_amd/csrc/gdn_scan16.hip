@@ -41,9 +41,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kNW = 4;         // waves per workgroup
-constexpr int kBV = 16 * kNW;  // value columns per workgroup
-constexpr int kThr = 64 * kNW;
+constexpr int kNW = 2;   // compute waves per workgroup
+constexpr int kNCT = 1;  // 16-column tiles per compute wave (each LDS operand read feeds kNCT products)
+constexpr int kTW = 2;   // transfer waves per workgroup
+constexpr int kWC = 16 * kNCT;  // value columns per compute wave
+constexpr int kBV = kWC * kNW;  // value columns per workgroup
+constexpr int kThr = 64 * (kNW + kTW);
 
 // ---------------------------------------------------------------------------------------
 // LDS / buffer primitives
@@ -71,8 +74,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, uint32_
 }
 
 // 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 * lane.  Issued as
-// inline assembly so the compiler does not serialise LDS reads of the other buffer behind
-// it; completion is waited for explicitly (wait_vm).
+// inline assembly: the compiler would otherwise make every later LDS read wait for it.
 __device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t soff,
                                       uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -81,10 +83,7 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t so
                : "memory");
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
 // Transpose read (8 bytes per lane).  The result is consumed only as a whole vector (bit
 // casts of the full vector, shuffles): element-wise casts of it have been miscompiled.
@@ -114,36 +113,30 @@ __device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d)
   return r;
 }
 
-// ---------------------------------------------------------------------------------------
-// LDS tile layouts (element index of logical (row, col))
-// ---------------------------------------------------------------------------------------
-
-// v tile [64 tokens][kBV columns] bf16: octets XOR-permuted so that one transpose read (four
-// rows x two octets per 16-lane group) spreads over distinct banks.
-__device__ __forceinline__ int swz_v(int r) {
-  return ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2)) & (kBV / 8 - 1);
-}
-__device__ __forceinline__ int vix(int r, int c) {
-  return r * kBV + ((((c >> 3) ^ swz_v(r))) << 3) + (c & 7);
-}
+// All operand tiles use the column-split layout tix_s32<64> (gdn_tiles.h).
+__device__ __forceinline__ int tix(int r, int c) { return tix_s32<kC>(r, c); }
 
 template <int K, bool PK>
 struct __attribute__((aligned(16))) S16Buf {
-  u16 q[kC * K];  // tix_pair<K>: bf16 Q (per-key gate: fp16 Q e^{gamma - gamma_mid})
-  u16 k[kC * K];  // tix_pair<K>: bf16 K (per-key gate: fp16 K e^{gamma - gamma_mid})
+  u16 q[kC * K];  // bf16 Q (per-key gate: fp16 Q e^{gamma - gamma_mid})
+  u16 k[kC * K];  // fp16 K (per-key gate: K e^{gamma - gamma_mid})
+  u16 kh[PK ? kC * K : 8];  // per-key gate: fp16 K e^{gamma_last - gamma}
   u16 tm[kC * kC];
   u16 p[kC * kC];
-  u16 v[kC * kBV];
-  u16 kh[PK ? kC * K : 8];  // per-key gate: fp16 K e^{gamma_last - gamma}, tix_pair<K>
+  u16 v[kC * kBV];  // bf16 V columns of this workgroup
   float vec[Slot16<K, PK>::kVecBytes / 4];
 };
 
 template <int K, bool PK>
 struct __attribute__((aligned(16))) S16Smem {
   S16Buf<K, PK> buf[2];
-  u16 kh[PK ? 8 : kC * K];  // scalar gate: fp16 copy of K, tix_pair<K>
-  u16 stg[kNW][16 * kC];    // per-wave output staging, [16 columns][64 rows]
+  u16 stg[kNW][16 * kC];  // per-wave output staging, [16 columns][64 rows]
 };
+
+// Keeps the compiler from moving LDS accesses across this point.  Within one wave the LDS
+// executes accesses in issue order, so this is all a wave's write -> read (or read -> write)
+// of its own staging tile needs; unlike a fence it leaves arithmetic free to move across.
+__device__ __forceinline__ void lds_order() { asm volatile("" : : : "memory"); }
 
 // Per-wave output of a 64-row x 16-column fp32 block held in accumulator layout (rows
 // 32G + 8lq + 4t + e of column li in acc[G][t][e]) as bf16 rows: staging tile, transpose
@@ -159,7 +152,7 @@ __device__ __forceinline__ void store_rows(u16* stg, F val, __amdgpu_buffer_rsrc
       const u32x2 w = pack_bf16x4(val(G, t, 0), val(G, t, 1), val(G, t, 2), val(G, t, 3));
       *reinterpret_cast<u32x2*>(&stg[li * kC + 32 * G + 8 * lq + 4 * t]) = w;
     }
-  wave_lds_sync();
+  lds_order();
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const u32x4 d = __builtin_shufflevector(tr16(&stg[(8 * s + trj) * kC + 16 * lq + 4 * trc]),
@@ -168,7 +161,7 @@ __device__ __forceinline__ void store_rows(u16* stg, F val, __amdgpu_buffer_rsrc
     __builtin_amdgcn_raw_buffer_store_b128(d, r, (16 * lq + li) * row_bytes + col0_bytes + 16 * s,
                                            0, 0);
   }
-  wave_lds_sync();
+  lds_order();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -178,18 +171,12 @@ __device__ __forceinline__ void store_rows(u16* stg, F val, __amdgpu_buffer_rsrc
 template <int K, bool VARLEN, bool PK, bool VN>
 __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
   typedef Slot16<K, PK> SL;
-  typedef typename QKT<bf16, PK>::type TQ;
+  typedef typename QKT<bf16, PK>::type TQ;  // Q tile type
   typedef typename Vec8<TQ>::type Q8;
   typedef S16Buf<K, PK> BUF;
   constexpr int kG = K / 32;
-  constexpr int kOPR = K / 8;         // 16-byte octets per q / k row
-  constexpr int kQB = kC * K * 2 / 1024;   // 1 KiB blocks per q / k tile
-  constexpr int kVB = kC * kBV * 2 / 1024;  // blocks of the v tile
-  constexpr int kVOPR = kBV / 8;
   constexpr int kVecB = SL::kVecBytes / 1024;
-  static_assert(kQB % kNW == 0 && kVB % kNW == 0 && kVecB <= kNW, "block split");
-  // vector-memory operations issued after the next chunk's transfers in one iteration
-  constexpr int kStoresAfter = VN ? 4 : 2;
+  constexpr int kVB = kC * kBV * 2 / 1024;  // 1 KiB blocks of the v tile
   __shared__ S16Smem<K, PK> s;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -207,251 +194,294 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
   const int h = chain % p.H;
   const ChunkPos cp = chain_pos(p, chain, VARLEN);
   const int nchunks = (cp.len + kC - 1) / kC;
-  const int col = v0 + 16 * wave + li;
   const uint32_t qk_row = (uint32_t)p.H * K * 2, v_row = (uint32_t)p.H * p.V * 2;
 
-  // State: hs[G][t] holds keys 32G + 8lq + 4t + e (e = 0..3) of column col.
-  f32x4 hs[kG][2];
+  if (wave >= kNW) {
+    // ---- transfer waves: chunk n+1's tiles into the other LDS buffer while chunk n is used.
+    // One wave sustains only a fraction of a CU's load bandwidth, so the 1 KiB blocks of a
+    // chunk are dealt round-robin to kTW waves.
+    const int tw = wave - kNW;
+    const bf16* qg = static_cast<const bf16*>(p.q);
+    const bf16* vg = static_cast<const bf16*>(p.v);
+    const char* wsg = static_cast<const char*>(p.ws);
+    // Per-lane source offsets of the input tiles.  LDS block b (1 KiB) of a column-split tile
+    // holds sub-tile b / 4, rows 16 (b % 4) .. +15; lane L writes its octet L % 4 of row
+    // 16 (b % 4) + L / 4, which holds the row's logical octet (L % 4) ^ ((row >> 3) & 3).
+    uint32_t voff_q[PK ? 1 : 4 * kG], voff_v[kVB];
 #pragma unroll
-  for (int G = 0; G < kG; ++G)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        hs[G][t][e] = p.h0 ? p.h0[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] : 0.f;
-
-  const bf16* qg = static_cast<const bf16*>(p.q);
-  const bf16* kg = static_cast<const bf16*>(p.k);
-  const bf16* vg = static_cast<const bf16*>(p.v);
-  bf16* og = static_cast<bf16*>(p.o);
-  bf16* vng = static_cast<bf16*>(p.v_new);
-  bf16* hcg = static_cast<bf16*>(p.h_chunks);
-  const char* wsg = static_cast<const char*>(p.ws);
-
-  // loop-invariant per-lane source offsets of this wave's input blocks
-  uint32_t voff_qk[PK ? 1 : kQB / kNW], voff_v[kVB / kNW];
-  if constexpr (!PK) {
-#pragma unroll
-    for (int i = 0; i < kQB / kNW; ++i) {
-      const int flat = 64 * (wave + kNW * i) + lane, r = flat / kOPR, po = flat % kOPR;
-      voff_qk[i] = r * qk_row + ((po ^ swz_pair<K>(r)) << 4);
+    for (int b = 0; b < 4 * kG; ++b) {
+      const int r = 16 * (b & 3) + (lane >> 2), lo = (lane & 3) ^ ((r >> 3) & 3);
+      if constexpr (!PK) voff_q[b] = r * qk_row + (4 * (b >> 2) + lo) * 16;
+      if (b < kVB) voff_v[b] = r * v_row + (4 * (b >> 2) + lo) * 16;
     }
-  }
-#pragma unroll
-  for (int i = 0; i < kVB / kNW; ++i) {
-    const int flat = 64 * (wave + kNW * i) + lane, r = flat / kVOPR, po = flat % kVOPR;
-    voff_v[i] = r * v_row + ((po ^ swz_v(r)) << 4);
-  }
-
-  // Issue chunk n's transfers into buffer B (this wave's share of the 1 KiB blocks).
-  auto issue = [&](int n, BUF& B) {
-    const long tok = cp.tok0 + (long)n * kC;
-    const uint32_t rows = (uint32_t)(cp.len - n * kC);
-    const i32x4 rw = make_rsrc(wsg + (cp.slot0 + n) * (long)SL::kBytes, (uint32_t)SL::kBytes);
     const uint32_t l16 = 16u * lane;
-    if constexpr (!PK) {
-      const i32x4 rq = make_rsrc(qg + (tok * p.H + h) * K, rows * qk_row);
-      const i32x4 rk = make_rsrc(kg + (tok * p.H + h) * K, rows * qk_row);
+    auto issue = [&](int n, BUF& B) {
+      int slot = 0;  // running block number; this wave issues blocks slot % kTW == tw
+      auto dma = [&](const i32x4& r, uint32_t voff, uint32_t soff, uint32_t lds) {
+        if (slot++ % kTW == tw) dma16(r, voff, soff, lds);
+      };
+      const long tok = cp.tok0 + (long)n * kC;
+      const uint32_t rows = (uint32_t)(cp.len - n * kC);
+      const i32x4 rw = make_rsrc(wsg + (cp.slot0 + n) * (long)SL::kBytes, (uint32_t)SL::kBytes);
 #pragma unroll
-      for (int i = 0; i < kQB / kNW; ++i)
-        dma16(rq, voff_qk[i], 0, lds_addr(B.q) + 1024u * (wave + kNW * i));
+      for (int b = 0; b < kVecB; ++b)
+        dma(rw, l16, (uint32_t)SL::kVec + 1024u * b, lds_addr(B.vec) + 1024u * b);
+      if constexpr (!PK) {
+        const i32x4 rq = make_rsrc(qg + (tok * p.H + h) * K, rows * qk_row);
 #pragma unroll
-      for (int i = 0; i < kQB / kNW; ++i)
-        dma16(rk, voff_qk[i], 0, lds_addr(B.k) + 1024u * (wave + kNW * i));
-    } else {
-#pragma unroll
-      for (int i = 0; i < kQB / kNW; ++i) {
-        const uint32_t b = 1024u * (wave + kNW * i);
-        dma16(rw, l16, (uint32_t)SL::kQ + b, lds_addr(B.q) + b);
-        dma16(rw, l16, (uint32_t)SL::kK + b, lds_addr(B.k) + b);
-        dma16(rw, l16, (uint32_t)SL::kKh + b, lds_addr(B.kh) + b);
-      }
-    }
-    const i32x4 rv = make_rsrc(vg + (tok * p.H + h) * p.V + v0, rows * v_row);
-#pragma unroll
-    for (int i = 0; i < kVB / kNW; ++i) dma16(rv, voff_v[i], 0, lds_addr(B.v) + 1024u * (wave + kNW * i));
-#pragma unroll
-    for (int i = 0; i < 8 / kNW; ++i) {
-      const uint32_t b = 1024u * (wave + kNW * i);
-      dma16(rw, l16, (uint32_t)SL::kTm + b, lds_addr(B.tm) + b);
-      dma16(rw, l16, (uint32_t)SL::kP + b, lds_addr(B.p) + b);
-    }
-    if (wave < kVecB) dma16(rw, l16, (uint32_t)SL::kVec + 1024u * wave, lds_addr(B.vec) + 1024u * wave);
-  };
-
-  if (nchunks > 0) issue(0, s.buf[0]);
-
-  for (int n = 0; n < nchunks; ++n) {
-    BUF& B = s.buf[n & 1];
-    const long tok = cp.tok0 + (long)n * kC;
-    const uint32_t rows = (uint32_t)(cp.len - n * kC);
-    if (n == 0) wait_vm<0>();
-    else wait_vm<kStoresAfter>();
-    __syncthreads();
-
-    // state entering this chunk -> h_chunks (issued before the next transfers so the next
-    // wait does not count these stores)
-    if (hcg) {
-      const __amdgpu_buffer_rsrc_t rh =
-          store_rsrc(hcg + (cp.slot0 + n) * (long)K * p.V + v0, (uint32_t)(K * p.V - v0) * 2u);
-#pragma unroll
-      for (int half = 0; half < K / 64; ++half)
-        store_rows(s.stg[wave], [&](int G, int t, int e) { return hs[2 * half + G][t][e]; }, rh,
-                   (uint32_t)p.V * 2u, (uint32_t)(64 * half * p.V + 16 * wave) * 2u, lane);
-    }
-
-    if (n + 1 < nchunks) issue(n + 1, s.buf[(n + 1) & 1]);
-
-    // scalar gate: fp16 copy of K for the state update (bf16 -> fp16 is exact in fp16's
-    // normal range)
-    if constexpr (!PK) {
-#pragma unroll
-      for (int i = 0; i < kC * kOPR / kThr; ++i) {
-        const int oc = tid + kThr * i, r = oc / kOPR, lo = oc % kOPR;
-        const int ix = tix_pair<K>(r, 8 * lo);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(&B.k[ix]);
-        u32x4 y;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          y[w] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(bf_lo(x[w]), bf_hi(x[w])));
-        *reinterpret_cast<u32x4*>(&s.kh[ix]) = y;
-      }
-    }
-
-    // B operand of K h / Q h (per-key gate: rows scaled by e^{gamma_mid})
-    Q8 bh[kG];
-#pragma unroll
-    for (int G = 0; G < kG; ++G) {
-      if constexpr (PK) {
-        const f32x4 m0 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq]);
-        const f32x4 m1 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq + 4]);
-        bh[G] = pack8<TQ>(hs[G][0] * m0, hs[G][1] * m1);
+        for (int b = 0; b < 4 * kG; ++b) dma(rq, voff_q[b], 0, lds_addr(B.q) + 1024u * b);
       } else {
-        bh[G] = pack8<TQ>(hs[G][0], hs[G][1]);
+#pragma unroll
+        for (int b = 0; b < 4 * kG; ++b) dma(rw, l16, (uint32_t)SL::kQ + 1024u * b, lds_addr(B.q) + 1024u * b);
       }
-    }
-
-    const TQ* qt = reinterpret_cast<const TQ*>(B.q);
-    const TQ* kt = reinterpret_cast<const TQ*>(B.k);
-    f32x4 xk[2][2], xq[2][2];
 #pragma unroll
-    for (int P = 0; P < 2; ++P)
+      for (int b = 0; b < 4 * kG; ++b) dma(rw, l16, (uint32_t)SL::kK + 1024u * b, lds_addr(B.k) + 1024u * b);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = pair_row(P, t, li);
-        f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int G = 0; G < kG; ++G) {
-          ak = mma16(lds8(kt + tix_pair<K>(r, 32 * G + 8 * lq)), bh[G], ak);
-          aq = mma16(lds8(qt + tix_pair<K>(r, 32 * G + 8 * lq)), bh[G], aq);
-        }
-        xk[P][t] = ak;
-        xq[P][t] = aq;
+      for (int b = 0; b < 8; ++b) {
+        dma(rw, l16, (uint32_t)SL::kTm + 1024u * b, lds_addr(B.tm) + 1024u * b);
+        dma(rw, l16, (uint32_t)SL::kP + 1024u * b, lds_addr(B.p) + 1024u * b);
       }
-
-    // Y = diag(beta) (V - diag(e^gamma) X_K): tokens 32P + 8lq + 4t + e of column col
-    f16x8 by[2];
+      const i32x4 rv = make_rsrc(vg + (tok * p.H + h) * p.V + v0, rows * v_row);
 #pragma unroll
-    for (int P = 0; P < 2; ++P)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r0 = 32 * P + 8 * lq + 4 * t;
-        const u32x2 vv = tr16(&B.v[vix(r0 + trj, 16 * wave + 4 * trc)]);
-        const f32x4 be = *reinterpret_cast<const f32x4*>(&B.vec[SL::kBeta + r0]);
-        f32x4 eg = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (!PK) eg = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEg + r0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) by[P][4 * t + e] = (f16)(be[e] * (bf_at(vv, e) - eg[e] * xk[P][t][e]));
-      }
-
-    // v_new = Tm Y (Tm lower triangular: token group P feeds groups G >= P)
-    const f16* tmt = reinterpret_cast<const f16*>(B.tm);
-    f32x4 vn[2][2];
-#pragma unroll
-    for (int G = 0; G < 2; ++G)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = pair_row(G, t, li);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int P = 0; P <= G; ++P) acc = mma16(lds8(tmt + tix_pair<kC>(r, 32 * P + 8 * lq)), by[P], acc);
-        vn[G][t] = acc;
-      }
-    f16x8 bv[2], bu[2];
-#pragma unroll
-    for (int P = 0; P < 2; ++P) {
-      bv[P] = pack8<f16>(vn[P][0], vn[P][1]);
+      for (int b = 0; b < kVB; ++b) dma(rv, voff_v[b], 0, lds_addr(B.v) + 1024u * b);
       if constexpr (PK) {
-        bu[P] = bv[P];
-      } else {
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq + 4]);
-        bu[P] = pack8<f16>(vn[P][0] * l0, vn[P][1] * l1);
+#pragma unroll
+        for (int b = 0; b < 4 * kG; ++b) dma(rw, l16, (uint32_t)SL::kKh + 1024u * b, lds_addr(B.kh) + 1024u * b);
       }
+    };
+    if (nchunks > 0) issue(0, s.buf[0]);
+    for (int n = 0; n < nchunks; ++n) {
+      wait_vm0();       // this wave's transfers of chunk n have landed in LDS
+      __syncthreads();  // ... and every compute wave is done with chunk n-1
+      if (n + 1 < nchunks) issue(n + 1, s.buf[(n + 1) & 1]);
     }
-
-    // o = scale (diag(e^gamma) X_Q + P v_new)
-    const f16* pt = reinterpret_cast<const f16*>(B.p);
-    f32x4 ov[2][2];
-#pragma unroll
-    for (int G = 0; G < 2; ++G)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = pair_row(G, t, li);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int P = 0; P <= G; ++P) acc = mma16(lds8(pt + tix_pair<kC>(r, 32 * P + 8 * lq)), bv[P], acc);
-        f32x4 eg = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (!PK) eg = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEg + 32 * G + 8 * lq + 4 * t]);
-        ov[G][t] = p.scale * (eg * xq[G][t] + acc);
-      }
-    const uint32_t out_bytes = rows * v_row;
-    store_rows(s.stg[wave], [&](int G, int t, int e) { return ov[G][t][e]; },
-               store_rsrc(og + (tok * p.H + h) * p.V + v0, out_bytes), v_row, 32u * wave, lane);
-    if constexpr (VN)
-      store_rows(s.stg[wave], [&](int G, int t, int e) { return vn[G][t][e]; },
-                 store_rsrc(vng + (tok * p.H + h) * p.V + v0, out_bytes), v_row, 32u * wave, lane);
-
-    // h <- e^gl h + K^T diag(e^{gl - gamma}) v_new
-    const u16* kht;
-    if constexpr (PK) {
-      kht = B.kh;
-    } else {
-      __syncthreads();  // every wave's part of the fp16 K copy is written
-      kht = s.kh;
-    }
-    const float egl = PK ? 1.f : B.vec[SL::kEgl];
-#pragma unroll
-    for (int G = 0; G < kG; ++G)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x4 acc;
-        if constexpr (PK) acc = hs[G][t] * *reinterpret_cast<const f32x4*>(&B.vec[SL::kEglk + 32 * G + 8 * lq + 4 * t]);
-        else acc = hs[G][t] * egl;
-#pragma unroll
-        for (int P = 0; P < 2; ++P) {
-          const int c0 = 32 * G + 8 * trc + 4 * t;
-          const f16x8 a = tr16_pair(&kht[tix_pair<K>(32 * P + 8 * lq + trj, c0)],
-                                    &kht[tix_pair<K>(32 * P + 8 * lq + 4 + trj, c0)]);
-          acc = mma16(a, bu[P], acc);
-        }
-        hs[G][t] = acc;
-      }
+    return;
   }
 
-  if (p.ht) {
+  // ---- compute waves: wave w owns value columns 32w + 16c + li (tile c < kNCT) of the block
+  // State: hs[c][G][t] holds keys 32G + 8lq + 4t + e (e = 0..3) of column v0 + 32w + 16c + li.
+  f32x4 hs[kNCT][kG][2];
+#pragma unroll
+  for (int c = 0; c < kNCT; ++c)
 #pragma unroll
     for (int G = 0; G < kG; ++G)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          p.ht[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] = hs[G][t][e];
+          hs[c][G][t][e] = p.h0 ? p.h0[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + v0 +
+                                       kWC * wave + 16 * c + li]
+                                : 0.f;
+
+  bf16* og = static_cast<bf16*>(p.o);
+  bf16* vng = static_cast<bf16*>(p.v_new);
+  bf16* hcg = static_cast<bf16*>(p.h_chunks);
+
+  for (int n = 0; n < nchunks; ++n) {
+    __syncthreads();  // chunk n is in buffer n & 1
+    const BUF& B = s.buf[n & 1];
+    const long tok = cp.tok0 + (long)n * kC;
+    const uint32_t rows = (uint32_t)(cp.len - n * kC);
+
+    // state entering this chunk -> h_chunks
+    if (hcg) {
+      const __amdgpu_buffer_rsrc_t rh =
+          store_rsrc(hcg + (cp.slot0 + n) * (long)K * p.V + v0, (uint32_t)(K * p.V - v0) * 2u);
+#pragma unroll
+      for (int c = 0; c < kNCT; ++c)
+#pragma unroll
+        for (int half = 0; half < K / 64; ++half)
+          store_rows(s.stg[wave], [&](int G, int t, int e) { return hs[c][2 * half + G][t][e]; }, rh,
+                     (uint32_t)p.V * 2u, (uint32_t)(64 * half * p.V + kWC * wave + 16 * c) * 2u, lane);
+    }
+
+    // B operands of K h and Q h: the state (per-key gate: rows scaled by e^{gamma_mid})
+    f16x8 bk[kNCT][kG];
+    Q8 bq[kNCT][kG];
+#pragma unroll
+    for (int G = 0; G < kG; ++G) {
+      f32x4 m0 = {1.f, 1.f, 1.f, 1.f}, m1 = m0;
+      if constexpr (PK) {
+        m0 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq]);
+        m1 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq + 4]);
+      }
+#pragma unroll
+      for (int c = 0; c < kNCT; ++c) {
+        if constexpr (PK) {
+          bk[c][G] = pack8<f16>(hs[c][G][0] * m0, hs[c][G][1] * m1);
+          bq[c][G] = bk[c][G];
+        } else {
+          bk[c][G] = pack8<f16>(hs[c][G][0], hs[c][G][1]);
+          bq[c][G] = pack8<TQ>(hs[c][G][0], hs[c][G][1]);
+        }
+      }
+    }
+
+    // X_K = K h (tokens 32P + 8lq + 4t + e of each column)
+    const f16* kt = reinterpret_cast<const f16*>(B.k);
+    f32x4 xk[kNCT][2][2];
+#pragma unroll
+    for (int P = 0; P < 2; ++P)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = pair_row(P, t, li);
+        f32x4 ak[kNCT];
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) ak[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int G = 0; G < kG; ++G) {
+          const f16x8 a = lds8(kt + tix(r, 32 * G + 8 * lq));
+#pragma unroll
+          for (int c = 0; c < kNCT; ++c) ak[c] = mma16(a, bk[c][G], ak[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) xk[c][P][t] = ak[c];
+      }
+
+    // Y = diag(beta) (V - diag(e^gamma) X_K)
+    f16x8 by[kNCT][2];
+#pragma unroll
+    for (int P = 0; P < 2; ++P)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r0 = 32 * P + 8 * lq + 4 * t;
+        const f32x4 be = *reinterpret_cast<const f32x4*>(&B.vec[SL::kBeta + r0]);
+        f32x4 eg = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (!PK) eg = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEg + r0]);
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) {
+          const u32x2 vv = tr16(&B.v[tix(r0 + trj, kWC * wave + 16 * c + 4 * trc)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            by[c][P][4 * t + e] = (f16)(be[e] * (bf_at(vv, e) - eg[e] * xk[c][P][t][e]));
+        }
+      }
+
+    // v_new = Tm Y (Tm lower triangular: token group P feeds groups G >= P)
+    const f16* tmt = reinterpret_cast<const f16*>(B.tm);
+    f32x4 vn[kNCT][2][2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = pair_row(G, t, li);
+        f32x4 acc[kNCT];
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int P = 0; P <= G; ++P) {
+          const f16x8 a = lds8(tmt + tix(r, 32 * P + 8 * lq));
+#pragma unroll
+          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(a, by[c][P], acc[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) vn[c][G][t] = acc[c];
+      }
+    // bv: v_new (for P v_new); bu: the update's B operand (scalar gate: v_new e^{gl-gamma})
+    f16x8 bv[kNCT][2], bu[kNCT][2];
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      f32x4 l0 = {1.f, 1.f, 1.f, 1.f}, l1 = l0;
+      if constexpr (!PK) {
+        l0 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq]);
+        l1 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq + 4]);
+      }
+#pragma unroll
+      for (int c = 0; c < kNCT; ++c) {
+        bv[c][P] = pack8<f16>(vn[c][P][0], vn[c][P][1]);
+        if constexpr (PK) bu[c][P] = bv[c][P];
+        else bu[c][P] = pack8<f16>(vn[c][P][0] * l0, vn[c][P][1] * l1);
+      }
+    }
+
+    // h <- e^gl h + K^T diag(e^{gl - gamma}) v_new   (A operand: K^T by transpose reads)
+    const u16* kht = PK ? B.kh : B.k;
+    const float egl = PK ? 1.f : B.vec[SL::kEgl];
+#pragma unroll
+    for (int G = 0; G < kG; ++G)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4 dec = {egl, egl, egl, egl};
+        if constexpr (PK) dec = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEglk + 32 * G + 8 * lq + 4 * t]);
+        f32x4 acc[kNCT];
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) acc[c] = hs[c][G][t] * dec;
+#pragma unroll
+        for (int P = 0; P < 2; ++P) {
+          const int c0 = 32 * G + 8 * trc + 4 * t;
+          const f16x8 a = tr16_pair(&kht[tix(32 * P + 8 * lq + trj, c0)],
+                                    &kht[tix(32 * P + 8 * lq + 4 + trj, c0)]);
+#pragma unroll
+          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(a, bu[c][P], acc[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) hs[c][G][t] = acc[c];
+      }
+
+    // o^T = scale ((Q h)^T diag(e^gamma) + (P v_new)^T), computed with the state and v_new as
+    // the A operands (the operand layouts are symmetric) and Q, P read as B with the same
+    // addresses as the A reads above: the accumulator then holds value columns 4lq .. 4lq+3
+    // of a 16-column tile for token pair_row(G, t, li), i.e. 8 contiguous bytes of an output row.
+    const TQ* qt = reinterpret_cast<const TQ*>(B.q);
+    const f16* pt = reinterpret_cast<const f16*>(B.p);
+    const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = pair_row(G, t, li);
+        f32x4 acc[kNCT];
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int Gk = 0; Gk < kG; ++Gk) {
+          const Q8 b = lds8(qt + tix(r, 32 * Gk + 8 * lq));
+#pragma unroll
+          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(bq[c][Gk], b, acc[c]);
+        }
+        const float eg = PK ? 1.f : B.vec[SL::kEg + r];
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) acc[c] = acc[c] * eg;
+#pragma unroll
+        for (int P = 0; P <= G; ++P) {
+          const f16x8 b = lds8(pt + tix(r, 32 * P + 8 * lq));
+#pragma unroll
+          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(bv[c][P], b, acc[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < kNCT; ++c) {
+          const f32x4 ov = acc[c] * p.scale;
+          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(ov[0], ov[1], ov[2], ov[3]), ro,
+                                                r * v_row + (kWC * wave + 16 * c + 4 * lq) * 2, 0, 0);
+        }
+      }
+    if constexpr (VN) {
+      const __amdgpu_buffer_rsrc_t rv = store_rsrc(vng + (tok * p.H + h) * p.V + v0, rows * v_row);
+#pragma unroll
+      for (int c = 0; c < kNCT; ++c)
+        store_rows(s.stg[wave], [&](int G, int t, int e) { return vn[c][G][t][e]; }, rv, v_row,
+                   (kWC * wave + 16u * c) * 2u, lane);
+    }
+  }
+
+  if (p.ht) {
+#pragma unroll
+    for (int c = 0; c < kNCT; ++c)
+#pragma unroll
+      for (int G = 0; G < kG; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p.ht[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + v0 + kWC * wave + 16 * c + li] =
+                hs[c][G][t][e];
   }
 }
 
 template <int K, bool VL, bool PK>
-hipError_t launch_k(const FwdParams& p, int nchains, hipStream_t stream) {
+hipError_t launch_k(const FwdParams& p0, int nchains, hipStream_t stream) {
+  FwdParams p = p0;
+  p.nvb = p.V / kBV;
   const dim3 grid(nchains * p.nvb), block(kThr);
   if (p.v_new)
     hipLaunchKernelGGL((scan16_kernel<K, VL, PK, true>), grid, block, 0, stream, p);

@@ -34,4 +34,16 @@ __device__ __forceinline__ int tix_seq64(int r, int c) {
   return r * 64 + (((c >> 3) ^ swz_seq(r)) << 3) + (c & 7);
 }
 
+// Column-split tile: [R rows][W columns] kept as W/32 sub-tiles of [R][32] (64-byte rows),
+// sub-tile s at element s*R*32; octet o (0..3) of row r inside a sub-tile is stored at
+// o ^ ((r >> 3) & 3).  A sub-tile offset is then a constant (an instruction immediate), and
+//  * 16-byte reads of one octet from the pair rows of 16 lanes hit 16 distinct 16-byte bank
+//    groups ((r & 3) and (r >> 3) & 3 both vary over the 16 rows);
+//  * transpose reads of four consecutive rows x four octets (one 16-lane group) touch 16
+//    distinct 8-byte bank slots.
+template <int R>
+__device__ __forceinline__ int tix_s32(int r, int c) {
+  return (c >> 5) * (R * 32) + r * 32 + ((((c >> 3) & 3) ^ ((r >> 3) & 3)) << 3) + (c & 7);
+}
+
 }  // namespace gdn

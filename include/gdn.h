@@ -93,7 +93,7 @@ GDN_API const char* gdn_last_error(void);
  *                                      `stream` has completed.  Too small or NULL:
  *                                      GDN_ERR_WORKSPACE.
  * Supported: K in {64, 128}, V in {64, 128} for bf16; K = 64 and V in {64, 128} for fp32
- * (gk is bf16 only).  B, T, H >= 1 and B*H*(V/64) <= 2^31 - 1 (else GDN_ERR_INVALID); bf16
+ * (gk is bf16 only).  B, T, H >= 1 and B*H*(V/32) <= 2^31 - 1 (else GDN_ERR_INVALID); bf16
  * also needs T*H*max(K, V)*2 < 2^32, the byte span of one head's rows (else
  * GDN_ERR_UNSUPPORTED).  The size query returns 0 for arguments it cannot size.
  */
