@@ -49,48 +49,6 @@ constexpr int kBV = 64;        // value columns per fp32 scan workgroup
 
 hipError_t launch_varlen_tables_impl(const int* cu, int N, int* offs, int* idx, hipStream_t stream);
 
-// Lower-triangular 16x16 tile enumeration: (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
-__device__ __forceinline__ void tri_tile(int idx, int& I, int& J) {
-  I = (idx >= 1) + (idx >= 3) + (idx >= 6);
-  J = idx - I * (I + 1) / 2;
-}
-
-// Per-key gate, column pass.  Thread tid owns key d = tid / TPK and tokens part*GT..+GT-1
-// (TPK adjacent lanes per key).  gk holds this thread's log decays; g_at(t) gives g_t.  On
-// return gam[] holds gamma[t][d] for its tokens, and gm / gL the key's gamma at tokens 31
-// and 63 (padded rows carry zero decays, so gL is the last valid row's value).
-template <int K, int GT, typename GF>
-__device__ __forceinline__ void key_cumsum(const float* gk, GF g_at, int part, float* gam,
-                                           float& gm, float& gL) {
-  constexpr int kTPK = kThreads / K;
-  float run = 0.f;
-#pragma unroll
-  for (int i = 0; i < GT; ++i) {
-    run += g_at(part * GT + i) + gk[i];
-    gam[i] = run;
-  }
-  // exclusive prefix over the TPK parts of this key (adjacent lanes of one wave)
-  const int lane0 = (threadIdx.x & 63) & ~(kTPK - 1);
-  float tot[kTPK];
-#pragma unroll
-  for (int q = 0; q < kTPK; ++q) tot[q] = __shfl(run, lane0 + q, 64);
-  float off = 0.f;
-#pragma unroll
-  for (int q = 0; q < kTPK; ++q) off += q < part ? tot[q] : 0.f;
-#pragma unroll
-  for (int i = 0; i < GT; ++i) gam[i] += off;
-  float cum[kTPK];
-  float acc = 0.f;
-#pragma unroll
-  for (int q = 0; q < kTPK; ++q) {
-    acc += tot[q];
-    cum[q] = acc;
-  }
-  static_assert((kC / 2) % GT == 0, "the middle token must end a part");
-  gm = cum[kC / 2 / GT - 1];  // gamma at token 31 (the parts up to it sum exactly to it)
-  gL = cum[kTPK - 1];
-}
-
 // ======================================================================================
 // chunk_prep_kernel: one workgroup per chunk.
 // ======================================================================================
@@ -111,82 +69,6 @@ struct __attribute__((aligned(16))) PrepSmem {
   float x[32][36];
   float gam[kC], beta[kC], g[kC];
 };
-
-// (I + A)^-1 for the strictly lower 64x64 A held in s.a, fp32.  Diagonal 16x16 blocks by
-// forward substitution, then blocks merged with
-//   T_hi,lo = -T_hi,hi A_hi,lo T_lo,lo       (first for 16-blocks, then for 32-blocks).
-// Every final block is written to s.tm (operand type) as it is produced; s.a keeps the fp32
-// blocks the later merges read.
-template <typename SM>
-__device__ __forceinline__ void solve_unit_lower(SM& s, int wave, int lane) {
-  typedef typename SM::TO TO;
-  const int li = lane & 15, lq = lane >> 4;
-  if (wave == 0) {
-    // lane -> (block b = lq, column c = li): forward substitution down column c.
-    const int b0 = 16 * lq;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == li) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < i; ++j) acc -= s.a[b0 + i][b0 + j] * x[j];
-      x[i] = acc;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s.a[b0 + i][b0 + li] = x[i];
-      s.tm[b0 + i][b0 + li] = to_t<TO>(x[i]);
-    }
-  }
-  __syncthreads();
-  if (wave < 2) {
-    // wave 0: block (1,0); wave 1: block (3,2).
-    const int hi = 16 * (1 + 2 * wave), lo = hi - 16;
-    f32x4 m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      m = mma4(s.a[hi + li][lo + 4 * kk + lq], s.a[lo + 4 * kk + lq][lo + li], m);
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) t = mma4(s.a[hi + li][hi + 4 * lq + kk], m[kk], t);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s.a[hi + 4 * lq + e][lo + li] = -t[e];
-      s.tm[hi + 4 * lq + e][lo + li] = to_t<TO>(-t[e]);
-    }
-  }
-  __syncthreads();
-  {
-    // X = A[32:64, 0:32] T[0:32, 0:32]; wave -> tile (ti, tj) of X.
-    const int ti = wave >> 1, tj = wave & 1;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (m < tj) continue;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        x = mma4(s.a[32 + 16 * ti + li][16 * m + 4 * kk + lq], s.a[16 * m + 4 * kk + lq][16 * tj + li], x);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s.x[16 * ti + 4 * lq + e][16 * tj + li] = x[e];
-  }
-  __syncthreads();
-  {
-    // T[32:64, 0:32] = -T[32:64, 32:64] X.
-    const int ti = wave >> 1, tj = wave & 1;
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (m > ti) continue;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        y = mma4(s.a[32 + 16 * ti + li][32 + 16 * m + 4 * kk + lq], s.x[16 * m + 4 * kk + lq][16 * tj + li], y);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s.tm[32 + 16 * ti + 4 * lq + e][16 * tj + li] = to_t<TO>(-y[e]);
-  }
-  __syncthreads();
-}
 
 template <typename TI, int K, bool VARLEN, bool PK>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p) {
@@ -871,12 +753,12 @@ hipError_t launch_varlen_tables_impl(const int* cu, int N, int* offs, int* idx, 
 
 template <typename TI, int K, bool VL, bool PK>
 hipError_t launch_pair(const FwdParams& p, long nslots, int nchains, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_prep_kernel<TI, K, VL, PK>), dim3(nslots), dim3(kThreads), 0, stream, p);
   if constexpr (sizeof(TI) == 2) {
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_prep16(p, K, VL, PK, nslots, stream);
     if (e != hipSuccess) return e;
     return launch_scan16(p, K, VL, PK, nchains, stream);
   } else {
+    hipLaunchKernelGGL((chunk_prep_kernel<TI, K, VL, PK>), dim3(nslots), dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL((scan_kernel<TI, K, VL, PK>), dim3(nchains * p.nvb), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
   }

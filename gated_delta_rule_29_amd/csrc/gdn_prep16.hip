@@ -1,0 +1,253 @@
+// gdn_prep16.hip -- per-chunk prep of the chunkwise forward for bf16 inputs on gfx950.
+//
+// One workgroup per 64-token chunk computes everything that does not depend on the state
+// (definitions in gdn_fwd.hip): gamma, the decays, A = strict_lower(diag(beta)(K K^T o D)),
+// Tm = (I + A)^-1, P = lower(Q K^T o D), and writes them to the chunk's workspace slot as the
+// exact LDS images the state scan copies (Slot16): Tm, P and K in fp16, plus the per-token /
+// per-key vectors.  For a per-key gate the decay sits inside the key sum, so Q and K are
+// scaled per key around the chunk's middle token (rows e^{gamma - gamma_mid}, Gram columns
+// e^{gamma_mid - gamma}) and the update operand K e^{gamma_last - gamma} is produced too.
+//
+// q and k arrive by direct global-to-LDS transfers (one batch, one wait); rows past the end
+// of the sequence read as zero through the buffer bounds.  Their LDS layout XOR-permutes the
+// 16-byte octets of a row by (row >> 2) & 3, which makes the 16-byte operand reads of 16
+// consecutive rows (one octet each) hit 16 distinct bank groups.
+#include "gdn_chunk.h"
+#include "gdn_dma.h"
+
+namespace gdn {
+namespace {
+
+using namespace chunk;
+using namespace dma;
+
+constexpr int kThreads = 256;
+
+// element index of (row r, column c) in a [64][K] q / k tile (32-column sub-tiles of 64-byte
+// rows, octet o of row r stored at o ^ ((r >> 2) & 3))
+__device__ __forceinline__ int pix(int r, int c) {
+  return (c >> 5) * (kC * 32) + r * 32 + ((((c >> 3) & 3) ^ ((r >> 2) & 3)) << 3) + (c & 7);
+}
+
+template <int K, bool PK>
+struct __attribute__((aligned(16))) Prep16Smem {
+  typedef f16 TO;
+  static constexpr int kTP = kC + 8;
+  u16 q[kC * K];            // bf16 Q (per-key gate: fp16 Q e^{gamma - gamma_mid}, in place)
+  u16 k[kC * K];            // bf16 K (per-key gate: fp16 K e^{gamma - gamma_mid}, in place)
+  u16 kb[PK ? kC * K : 8];  // per-key gate: fp16 K e^{gamma_mid - gamma} (Gram columns)
+  u16 kh[PK ? kC * K : 8];  // per-key gate: fp16 K e^{gamma_last - gamma}
+  TO tm[kC][kTP];
+  TO p[kC][kTP];
+  float a[kC][kC + 4];
+  float x[32][36];
+  float gam[kC], beta[kC], g[kC];
+};
+
+template <int K, bool VARLEN, bool PK>
+__global__ __launch_bounds__(kThreads) void prep16_kernel(const FwdParams p) {
+  typedef Prep16Smem<K, PK> SM;
+  typedef Slot16<K, PK> SL;
+  typedef typename QKT<bf16, PK>::type TQ;  // tile element type for the products
+  typedef typename Vec8<TQ>::type Q8;
+  constexpr int kG = K / 32;
+  constexpr int kQB = kC * K * 2 / 1024;  // 1 KiB transfer blocks per tile
+  __shared__ SM s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+
+  // chunk -> (chain, n)
+  int chain, n;
+  if (VARLEN) {
+    const int h = blockIdx.x / p.nt_total, cg = blockIdx.x % p.nt_total;
+    int lo = 0, hi = p.nseq;  // largest i with coffs[i] <= cg
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.coffs[mid] <= cg) lo = mid;
+      else hi = mid;
+    }
+    chain = lo * p.H + h;
+    n = cg - p.coffs[lo];
+  } else {
+    const int nt = (p.T + kC - 1) / kC;
+    chain = blockIdx.x / nt;
+    n = blockIdx.x % nt;
+  }
+  const ChunkPos cp = chain_pos(p, chain, VARLEN);
+  const int h = chain % p.H;
+  const int t0 = n * kC, rows = min(kC, cp.len - t0);
+  const long tok = cp.tok0 + t0;
+  const uint32_t qk_row = (uint32_t)p.H * K * 2;
+
+  // q, k -> LDS (this wave's blocks), bounded to the sequence's remaining rows
+  {
+    const uint32_t span = (uint32_t)(cp.len - t0) * qk_row;
+    const i32x4 rq = make_rsrc(static_cast<const bf16*>(p.q) + (tok * p.H + h) * K, span);
+    const i32x4 rk = make_rsrc(static_cast<const bf16*>(p.k) + (tok * p.H + h) * K, span);
+#pragma unroll
+    for (int i = 0; i < kQB / 4; ++i) {
+      const int b = wave + 4 * i;
+      const int r = 16 * (b & 3) + (lane >> 2), lo = (lane & 3) ^ ((r >> 2) & 3);
+      const uint32_t voff = r * qk_row + (4 * (b >> 2) + lo) * 16;
+      dma16(rq, voff, 0, lds_addr(s.q) + 1024u * b);
+      dma16(rk, voff, 0, lds_addr(s.k) + 1024u * b);
+    }
+  }
+  if (tid < kC) {
+    const bool ok = tid < rows;
+    const long gi = (tok + tid) * p.H + h;
+    s.g[tid] = ok && p.g ? p.g[gi] : 0.f;
+    s.beta[tid] = ok ? p.beta[gi] : 0.f;
+  }
+  constexpr int kTPK = kThreads / K, kGT = kC / kTPK;
+  float gkr[PK ? kGT : 1];
+  if constexpr (PK) {
+    const int d = tid / kTPK, part = tid % kTPK;
+#pragma unroll
+    for (int i = 0; i < kGT; ++i) {
+      const int t = part * kGT + i;
+      gkr[i] = t < rows ? p.gk[((tok + t) * p.H + h) * (long)K + d] : 0.f;
+    }
+  }
+  // strict upper 16x16 tiles of A / Tm / P stay zero
+  for (int e = tid; e < 6 * 256; e += kThreads) {
+    const int t = e >> 8, r = (e >> 4) & 15, c = e & 15;
+    const int I = (t >= 3) + (t >= 5);
+    const int J = (t < 3) ? t + 1 : (t < 5 ? t - 1 : 3);
+    s.a[16 * I + r][16 * J + c] = 0.f;
+    s.tm[16 * I + r][16 * J + c] = (f16)0.f;
+    s.p[16 * I + r][16 * J + c] = (f16)0.f;
+  }
+  wait_vm0();
+  __syncthreads();
+
+  char* slot = static_cast<char*>(p.ws) + (cp.slot0 + n) * (long)SL::kBytes;
+  float* vec = reinterpret_cast<float*>(slot + SL::kVec);
+  if constexpr (PK) {
+    // per-key gamma; scaled Q, K in place, the Gram column operand and the update operand;
+    // beta, e^{gamma_mid}, e^{gamma_last} to the slot
+    const int d = tid / kTPK, part = tid % kTPK;
+    float gam[kGT], gm, gL;
+    key_cumsum<K, kGT>(gkr, [&](int t) { return s.g[t]; }, part, gam, gm, gL);
+    const bf16* qb = reinterpret_cast<const bf16*>(s.q);
+    const bf16* kbf = reinterpret_cast<const bf16*>(s.k);
+#pragma unroll
+    for (int i = 0; i < kGT; ++i) {
+      const int t = part * kGT + i, ix = pix(t, d);
+      const float up = __expf(gam[i] - gm), dn = __expf(gm - gam[i]);
+      const float kk = (float)kbf[ix], qq = (float)qb[ix];
+      reinterpret_cast<f16*>(s.k)[ix] = (f16)(kk * up);
+      reinterpret_cast<f16*>(s.q)[ix] = (f16)(qq * up);
+      reinterpret_cast<f16*>(s.kb)[ix] = (f16)(kk * dn);
+      reinterpret_cast<f16*>(s.kh)[ix] = (f16)(kk * __expf(gL - gam[i]));
+    }
+    if (part == 0) {
+      vec[SL::kEmid + d] = __expf(gm);
+      vec[SL::kEglk + d] = __expf(gL);
+    }
+    if (tid < kC) vec[SL::kBeta + tid] = s.beta[tid];
+  } else if (wave == 0) {
+    const float gam = wave_incl_scan(s.g[lane], lane);
+    const float gl = __shfl(gam, 63, 64);
+    s.gam[lane] = gam;
+    vec[SL::kEg + lane] = __expf(gam);
+    vec[SL::kEl + lane] = __expf(gl - gam);
+    vec[SL::kBeta + lane] = s.beta[lane];
+    if (lane == 0) vec[SL::kEgl] = __expf(gl);
+  }
+  __syncthreads();
+
+  // Gram (-> A) and Q K^T (-> P), lower 16x16 tiles: 20 jobs, 5 per wave
+  const TQ* qt = reinterpret_cast<const TQ*>(s.q);
+  const TQ* kt = reinterpret_cast<const TQ*>(s.k);
+  const TQ* kbt = reinterpret_cast<const TQ*>(PK ? s.kb : s.k);
+#pragma unroll
+  for (int ji = 0; ji < 5; ++ji) {
+    const int job = wave + 4 * ji;
+    const bool is_qk = job >= 10;
+    int I, J;
+    tri_tile(is_qk ? job - 10 : job, I, J);
+    const TQ* at = is_qk ? qt : kt;
+    Q8 av[kG], bv[kG];
+#pragma unroll
+    for (int kk = 0; kk < kG; ++kk) {
+      av[kk] = lds8(at + pix(16 * I + li, 32 * kk + 8 * lq));
+      bv[kk] = lds8(kbt + pix(16 * J + li, 32 * kk + 8 * lq));
+    }
+    const int sc = 16 * J + li;
+    float gr[4], br[4];
+    const float gs = PK ? 0.f : s.gam[sc];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gr[e] = PK ? 0.f : s.gam[16 * I + 4 * lq + e];
+      br[e] = s.beta[16 * I + 4 * lq + e];
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kG; ++kk) acc = mma16(av[kk], bv[kk], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + 4 * lq + e;
+      const float dd = PK ? 1.f : __expf(gr[e] - gs);
+      if (is_qk) s.p[r][sc] = (f16)(sc <= r ? dd * acc[e] : 0.f);
+      else s.a[r][sc] = sc < r ? br[e] * dd * acc[e] : 0.f;
+    }
+  }
+  __syncthreads();
+  solve_unit_lower(s, wave, lane);
+
+  // Tm, P -> slot, 16-byte pieces in the scan's column-split layout
+  for (int c = tid; c < 2 * kC * kC / 8; c += kThreads) {
+    const int which = c / (kC * kC / 8), cc = c % (kC * kC / 8);
+    const int r = cc / (kC / 8), c0 = (cc % (kC / 8)) * 8;
+    const f16* src = which ? &s.p[r][c0] : &s.tm[r][c0];
+    *reinterpret_cast<u32x4*>(slot + (which ? SL::kP : SL::kTm) + 2 * tix_s32<kC>(r, c0)) =
+        *reinterpret_cast<const u32x4*>(src);
+  }
+  if constexpr (PK) {
+    // scaled Q, K and the update operand (already fp16)
+    constexpr int kPieces = kC * K / 8;
+    for (int c = tid; c < 3 * kPieces; c += kThreads) {
+      const int which = c / kPieces, cc = c % kPieces;
+      const int r = cc / (K / 8), c0 = (cc % (K / 8)) * 8;
+      const u16* src = which == 0 ? s.q : (which == 1 ? s.k : s.kh);
+      const size_t base = which == 0 ? SL::kQ : (which == 1 ? SL::kK : SL::kKh);
+      *reinterpret_cast<u32x4*>(slot + base + 2 * tix_s32<kC>(r, c0)) =
+          *reinterpret_cast<const u32x4*>(&src[pix(r, c0)]);
+    }
+  } else {
+    // K as fp16 (exact for bf16 values in fp16's normal range)
+    for (int c = tid; c < kC * K / 8; c += kThreads) {
+      const int r = c / (K / 8), c0 = (c % (K / 8)) * 8;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&s.k[pix(r, c0)]);
+      u32x4 y;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float lo = __uint_as_float(x[w] << 16), hi = __uint_as_float(x[w] & 0xffff0000u);
+        y[w] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+      }
+      *reinterpret_cast<u32x4*>(slot + SL::kK + 2 * tix_s32<kC>(r, c0)) = y;
+    }
+  }
+}
+
+template <int K, bool VL, bool PK>
+hipError_t launch_k(const FwdParams& p, long nslots, hipStream_t stream) {
+  hipLaunchKernelGGL((prep16_kernel<K, VL, PK>), dim3(nslots), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prep16(const FwdParams& p, int K, bool varlen, bool pk, long nslots,
+                         hipStream_t stream) {
+  if (K == 128) {
+    if (pk) return varlen ? launch_k<128, true, true>(p, nslots, stream) : launch_k<128, false, true>(p, nslots, stream);
+    return varlen ? launch_k<128, true, false>(p, nslots, stream) : launch_k<128, false, false>(p, nslots, stream);
+  }
+  if (pk) return varlen ? launch_k<64, true, true>(p, nslots, stream) : launch_k<64, false, true>(p, nslots, stream);
+  return varlen ? launch_k<64, true, false>(p, nslots, stream) : launch_k<64, false, false>(p, nslots, stream);
+}
+
+}  // namespace gdn

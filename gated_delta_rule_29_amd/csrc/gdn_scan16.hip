@@ -28,17 +28,15 @@
 // per-wave [16 columns][64 rows] staging tile (8-byte writes) -> transpose reads -> 16-byte
 // row stores.
 #include "gdn_chunk.h"
+#include "gdn_dma.h"
 
 namespace gdn {
 namespace {
 
 using namespace chunk;
+using namespace dma;
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kNW = 2;   // compute waves per workgroup
@@ -47,43 +45,6 @@ constexpr int kTW = 2;   // transfer waves per workgroup
 constexpr int kWC = 16 * kNCT;  // value columns per compute wave
 constexpr int kBV = kWC * kNW;  // value columns per workgroup
 constexpr int kThr = 64 * (kNW + kTW);
-
-// ---------------------------------------------------------------------------------------
-// LDS / buffer primitives
-// ---------------------------------------------------------------------------------------
-
-template <typename T>
-__device__ __forceinline__ uint32_t lds_addr(const T* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return zero, stores past
-// it are dropped.  All fields are workgroup-uniform.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = 0x00020000;  // 32-bit data format, no swizzle, no index
-  return r;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
-}
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 * lane.  Issued as
-// inline assembly: the compiler would otherwise make every later LDS read wait for it.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t soff,
-                                      uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
-}
-
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
 // Transpose read (8 bytes per lane).  The result is consumed only as a whole vector (bit
 // casts of the full vector, shuffles): element-wise casts of it have been miscompiled.
