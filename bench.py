@@ -27,7 +27,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "tokens·heads/sec for chunked gated delta-rule fwd; % MFMA (or HBM) peak"
-KERNEL_SOURCES = ["gated_delta_rule_29_amd/csrc/gdn_fwd.hip", "gated_delta_rule_29_amd/csrc/gdn_device.h"]
+KERNEL_SOURCE_DIR = "gated_delta_rule_29_amd/csrc"
+# The kernels one forward call launches; the roofline covers the whole call (every kernel on
+# the path), timed with HIP events around it on the launch stream.
+KERNELS_BF16 = "gdn_fwd call: prep16_kernel + scan16_kernel"
+KERNELS_F32 = "gdn_fwd call: chunk_prep_kernel + scan_kernel"
 COUNTER_FILE = "profiles/gdn_fwd_kernel_b4h16t4096_hbm_counters.md"
 
 
@@ -58,10 +62,14 @@ def alg_bytes_bigdn(B, F, S, H, D):
 
 
 def kernel_source_hash():
+    """Hash of every kernel source: a counter summary is valid only for the code it measured."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    d = os.path.join(ROOT, KERNEL_SOURCE_DIR)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -176,7 +184,7 @@ def main():
         th = B * T * H
         elt = 2 if dt == torch.bfloat16 else 4
         alg = alg_bytes_per_launch(B, T, H, K, V, elt, inp["gk"] is not None, save)
-        kernel = "gdn_fwd_kernel"
+        kernel = KERNELS_BF16 if dt == torch.bfloat16 else KERNELS_F32
         config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
                   "chunk": 64, "state": "fp32", "per_key_gate": inp["gk"] is not None,
                   "saves_h_and_v_new": save}
@@ -194,7 +202,7 @@ def main():
         th = T * H
         elt = 2 if dt == torch.bfloat16 else 4
         alg = alg_bytes_per_launch(1, T, H, K, V, elt, False, False, n_states=N * H)
-        kernel = "gdn_fwd_kernel (varlen)"
+        kernel = (KERNELS_BF16 if dt == torch.bfloat16 else KERNELS_F32) + " (packed)"
         config = {"workload": args.workload, "T_total": T, "N": N, "H": H, "K": K, "V": V,
                   "lengths": (cu[1:] - cu[:-1]).tolist(), "chunk": 64, "state": "fp32"}
 
