@@ -257,6 +257,10 @@ __device__ __forceinline__ void solve_unit_lower(SM& s, int wave, int lane) {
 hipError_t launch_prep16(const FwdParams& p, int K, bool varlen, bool pk, long nslots,
                          hipStream_t stream);
 
+// Single-kernel forward of bf16 inputs with a scalar gate and no saved states
+// (gdn_fused16.hip): one workgroup per (chain, 32-column value block).
+hipError_t launch_fused16(const FwdParams& p, int K, bool varlen, int nchains, hipStream_t stream);
+
 // Scan of 16-bit inputs (gdn_scan16.hip).
 hipError_t launch_scan16(const FwdParams& p, int K, bool varlen, bool pk, int nchains,
                          hipStream_t stream);

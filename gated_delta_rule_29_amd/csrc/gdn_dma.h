@@ -45,7 +45,13 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t so
                : "memory");
 }
 
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+// Waits for every vector-memory load of this wave, the direct-to-LDS ones included.  Issued
+// through the builtin so the compiler's own wait tracking knows all loads have completed
+// (an opaque inline-assembly wait would leave it inserting further waits for them).
+__device__ __forceinline__ void wait_vm0() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left alone
+  asm volatile("" : : : "memory");
+}
 
 }  // namespace dma
 }  // namespace gdn

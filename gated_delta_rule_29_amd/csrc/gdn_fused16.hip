@@ -1,0 +1,730 @@
+// gdn_fused16.hip -- single-kernel chunkwise gated delta-rule forward for bf16 inputs with a
+// scalar gate (gfx950).
+//
+// The state pass over the chunks of a chain is sequential; everything a chunk needs that does
+// not depend on the state (gamma, the decays, A = strict_lower(diag(beta)(K K^T o D)),
+// Tm = (I + A)^-1 and P = lower(Q K^T o D); definitions in gdn_fwd.hip) is not.  This kernel
+// overlaps the two inside one workgroup per (chain, 32-column value block), eight waves (wave
+// w and w + 4 share a SIMD):
+//
+//   waves 0, 1     state scan of chunk n for 16 value columns each (h in registers, fp32):
+//                    X_K = K h, Y = diag(beta)(V - diag(e^gamma) X_K), v_new = Tm Y,
+//                    o = scale (diag(e^gamma) Q h + P v_new),
+//                    h <- e^gl h + K^T diag(e^{gl-gamma}) v_new
+//   waves 2, 3     Gram tiles of the diagonal 16x16 blocks of chunk n+1 and their inverses;
+//                    then the off-diagonal block columns of Tm
+//   wave 6         off-diagonal Gram tiles of chunk n+1 -> A
+//   wave 7         Q K^T tiles of chunk n+1 -> P
+//   waves 4, 5     transfers: q, k of chunk n+2 and v of chunk n+1 straight from HBM into
+//                    LDS (buffer loads with the LDS destination); g, beta of chunk n+3 into
+//                    registers; the gate quantities of chunk n+2 (gamma and its exponentials).
+//
+// One workgroup barrier per chunk hands every stage on.  q / k tiles and the gate quantities
+// sit in rings of three LDS slots (scan reads n, prep reads n+1, transfers fill n+2); v, Tm
+// and P in rings of two.  Waves 2, 3 and 6 meet once more inside a step through a counter in
+// LDS (solve_bar).  Nothing per chunk goes through HBM: q, k, v are read once per workgroup
+// (the value blocks of a chain share them in L2) and o is written once.
+//
+// Decays.  The Gram and Q K^T epilogues need e^{gamma_r - gamma_s} for s <= r.  When the
+// chunk's total decay gamma_0 - gamma_63 is below 80 it is formed as the product of per-token
+// factors around the middle token, e^{gamma_r - gamma_31} e^{gamma_31 - gamma_s}, which cannot
+// overflow; otherwise every element takes its own exponential.
+//
+// The solve.  A diagonal block L (strictly lower, L^16 = 0) is inverted as
+// (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8); the off-diagonal blocks follow block
+// column by block column, T_ij = -T_ii sum_{j<=k<i} A_ik T_kj.  Both use 16x16x16 fp16
+// matrix products with fp32 accumulation; every matrix is kept in the two register layouts
+// the products need (a product's accumulator is the B operand of the next one, and the
+// accumulator of the transposed product is its A operand), so the chains never go through LDS.
+//
+// Operand precision: K h, Q h and the Gram / Q K^T products take bf16 operands (the inputs are
+// bf16; h is rounded to bf16); Tm Y and P v_new take fp16 (bounded factors, 11-bit
+// significands); the state update K^T v_new takes K exactly in bf16 against v_new e^{gl-gamma}
+// split into a bf16 high part and a bf16 remainder (two products).
+//
+// LDS tiles: column-split [64][W] layout (32-column sub-tiles of 64-byte rows) whose 16-byte
+// octets are XOR-permuted by ((r >> 2) ^ (r >> 3)) & 3.  Both row orders the kernel reads 16
+// rows at a time in -- 16 consecutive rows (Gram tiles) and the pair rows 32G + 8i + 4t + j
+// (scan products) -- then hit 16 distinct 16-byte bank groups, and the transposed 8-byte reads
+// (four consecutive rows x four octets) 16 distinct 8-byte slots.
+#include "gdn_chunk.h"
+#include "gdn_dma.h"
+
+namespace gdn {
+namespace {
+
+using namespace chunk;
+using namespace dma;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kBV = 32;    // value columns per workgroup (16 per scan wave)
+constexpr int kThr = 512;  // 8 waves
+
+// element index of (r, c) in a [64][W] tile (W a multiple of 32)
+__device__ __forceinline__ int tix(int r, int c) {
+  return (c >> 5) * (kC * 32) + r * 32 + ((((c >> 3) & 3) ^ (((r >> 2) ^ (r >> 3)) & 3)) << 3) + (c & 7);
+}
+// logical octet a lane must fetch so that a linear 16-byte-per-lane LDS write lands it at
+// physical octet (lane & 3) of row r
+__device__ __forceinline__ int src_octet(int r, int lane) { return (lane & 3) ^ (((r >> 2) ^ (r >> 3)) & 3); }
+
+// Gate slot of one chunk (floats): e^gamma [0, 64), e^{gl - gamma} [64, 128), beta [128, 192),
+// e^gl at 192; factors beta e^{gamma - gamma_31} [256, 320), e^{gamma - gamma_31} [320, 384),
+// e^{gamma_31 - gamma} [384, 448); gamma [448, 512); at 512 a flag: the factors are usable.
+constexpr int kEg = 0, kEl = 64, kBeta = 128, kEgl = 192, kFrk = 256, kFrq = 320, kFc = 384,
+              kGam = 448, kFast = 512, kGateF = 516;
+
+template <int K>
+struct __attribute__((aligned(16))) FusedSmem {
+  struct QK {
+    u16 q[kC * K];
+    u16 k[kC * K];
+  } qk[3];
+  u16 v[2][kC * kBV];
+  struct TP {
+    u16 tm[kC * kC];  // fp16 Tm
+    u16 p[kC * kC];   // fp16 P
+  } tp[2];
+  float gate[3][kGateF];
+  u16 af[kC * kC];      // fp16 rows of the off-diagonal blocks of A (tix layout)
+  unsigned pbar;        // prep-wave pair barrier counter
+};
+
+__device__ __forceinline__ u32x2 tr16(const u16* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lds_addr(p)));
+}
+
+// A operand of 8 16-bit values from two transpose reads (elements 0..3, then 4..7).
+__device__ __forceinline__ bf16x8 tr16_pair(const u16* p0, const u16* p1) {
+  const u32x4 w = __builtin_shufflevector(tr16(p0), tr16(p1), 0, 1, 2, 3);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf_at(const u32x2& v, int e) {
+  return (e & 1) ? bf_hi(v[e >> 1]) : bf_lo(v[e >> 1]);
+}
+
+__device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d) {
+  const bf16 x0 = (bf16)a, x1 = (bf16)b, x2 = (bf16)c, x3 = (bf16)d;
+  u32x2 r;
+  r[0] = (unsigned)__builtin_bit_cast(u16, x0) | ((unsigned)__builtin_bit_cast(u16, x1) << 16);
+  r[1] = (unsigned)__builtin_bit_cast(u16, x2) | ((unsigned)__builtin_bit_cast(u16, x3) << 16);
+  return r;
+}
+
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x4 cvt_f16x4(const f32x4& x) {
+  return f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+}
+
+// 16x16 output, contraction 16: lane (li, lq) supplies A[li][4lq + j] and B[4lq + j][li]
+// (j = 0..3) and holds C[4lq + e][li], so an accumulator can feed the next product as B.
+__device__ __forceinline__ f32x4 mma16x16x16(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// The lane index, opaque to the optimiser: addresses derived from it inside a loop are
+// recomputed each iteration (a few integer operations) instead of being hoisted out and kept
+// in registers for the whole loop.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+// Barrier of the prep waves that build Tm (three of them).  Each wave's earlier LDS accesses
+// complete before its increment (lgkmcnt(0)); LDS is coherent within the workgroup, so after
+// the wait the other waves' writes are visible.  Each of them calls it once per step.
+__device__ __forceinline__ void solve_bar(unsigned* ctr, unsigned& target) {
+  target += 3;
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    __builtin_amdgcn_s_sleep(1);
+  asm volatile("" : : : "memory");
+}
+
+template <int K, bool VARLEN>
+__global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
+  typedef FusedSmem<K> SM;
+  constexpr int kG = K / 32;
+  __shared__ SM s;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+  const int trj = (lane >> 2) & 3, trc = lane & 3;
+
+  // Workgroup -> (chain, value block); the value blocks of a chain stay on one XCD.
+  const int nwg = gridDim.x;
+  int logical = blockIdx.x;
+  if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int chain = logical / p.nvb;
+  const int v0 = (logical % p.nvb) * kBV;
+  const int h = chain % p.H, bs = chain / p.H;
+  long tok0;
+  int len;
+  if (VARLEN) {
+    tok0 = p.cu[bs];
+    len = p.cu[bs + 1] - p.cu[bs];
+  } else {
+    tok0 = (long)bs * p.T;
+    len = p.T;
+  }
+  const int nchunks = (len + kC - 1) / kC;
+  const uint32_t qk_row = (uint32_t)p.H * K * 2, v_row = (uint32_t)p.H * p.V * 2;
+
+  if (wave == 4 || wave == 5) {
+    // =============================== transfer waves ===============================
+    const int tw = wave - 4;  // 0: q, g, beta and the gate slots; 1: k and v
+    // per-lane source offsets of the 1 KiB transfer blocks: block b holds rows 16 (b & 3) ..
+    // +15 of sub-tile b >> 2; lane L writes physical octet L & 3 of row 16 (b & 3) + L / 4
+    uint32_t off_qk[4], off_v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * j + (lane >> 2), o = src_octet(r, lane);
+      off_qk[j] = r * qk_row + o * 16;
+      off_v[j] = r * v_row + o * 16;
+    }
+    const bf16* qg = static_cast<const bf16*>(p.q);
+    const bf16* kg = static_cast<const bf16*>(p.k);
+    const bf16* vg = static_cast<const bf16*>(p.v);
+    auto rows_of = [&](int c) { return (uint32_t)min(kC, len - c * kC); };
+    auto issue_qk = [&](int c) {  // q (wave 4) or k (wave 5) of chunk c into ring slot c % 3
+      if (c >= nchunks) return;
+      const long tok = tok0 + (long)c * kC;
+      const i32x4 r = make_rsrc((tw ? kg : qg) + (tok * p.H + h) * K, rows_of(c) * qk_row);
+      u16* dst = tw ? s.qk[c % 3].k : s.qk[c % 3].q;
+#pragma unroll
+      for (int b = 0; b < 4 * kG; ++b) dma16(r, off_qk[b & 3] + (b >> 2) * 64, 0, lds_addr(dst) + 1024u * b);
+    };
+    auto issue_v = [&](int c) {  // v of chunk c (this workgroup's 32 columns, four blocks)
+      if (c >= nchunks) return;
+      const long tok = tok0 + (long)c * kC;
+      const i32x4 r = make_rsrc(vg + (tok * p.H + h) * p.V + v0, rows_of(c) * v_row);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dma16(r, off_v[b], 0, lds_addr(s.v[c & 1]) + 1024u * b);
+    };
+    auto load_gb = [&](int c, float& gv, float& bv) {  // lane = token of chunk c
+      const int t = c * kC + lane;
+      const bool ok = c < nchunks && t < len;
+      const long gi = (tok0 + t) * p.H + h;
+      gv = ok && p.g ? p.g[gi] : 0.f;
+      bv = ok ? p.beta[gi] : 0.f;
+    };
+    // gate slot of chunk c from its g, beta (rows past the end carry g = 0, beta = 0)
+    auto gates = [&](int c, float gv, float bv) {
+      if (c >= nchunks) return;
+      float* G = s.gate[c % 3];
+      const float gam = wave_incl_scan(gv, lane);
+      const float gl = __shfl(gam, 63, 64), gref = __shfl(gam, 31, 64), g0 = __shfl(gam, 0, 64);
+      G[kEg + lane] = __expf(gam);
+      G[kEl + lane] = __expf(gl - gam);
+      G[kBeta + lane] = bv;
+      const float up = __expf(gam - gref);
+      G[kFrk + lane] = bv * up;
+      G[kFrq + lane] = up;
+      G[kFc + lane] = __expf(gref - gam);
+      G[kGam + lane] = gam;
+      if (lane == 0) {
+        G[kEgl] = __expf(gl);
+        G[kFast] = (g0 - gl < 80.f) ? 1.f : 0.f;
+      }
+    };
+    float g1 = 0.f, b1 = 0.f, g2 = 0.f, b2 = 0.f;
+    issue_qk(0);
+    if (tw == 0) {
+      float g0v, b0v;
+      load_gb(0, g0v, b0v);
+      load_gb(1, g1, b1);
+      wait_vm0();
+      gates(0, g0v, b0v);
+    } else {
+      wait_vm0();
+    }
+    __syncthreads();
+    for (int n = -1; n < nchunks; ++n) {
+      issue_qk(n + 2);
+      if (tw == 1) {
+        issue_v(n + 1);
+      } else {
+        load_gb(n + 3, g2, b2);
+        gates(n + 2, g1, b1);
+      }
+      wait_vm0();
+      g1 = g2;
+      b1 = b2;
+      __syncthreads();
+    }
+    return;
+  }
+
+  if (wave >= 2) {
+    // =============================== prep waves ===============================
+    // Four waves; waves 2 and 6 share a SIMD, as do 3 and 7.
+    //   pq 0 (wave 2), pq 1 (wave 3): Gram tiles (b, b) and the inverses T_bb of the
+    //     diagonal blocks b = 2pq, 2pq + 1; then the off-diagonal block columns of Tm
+    //     (pq 0: column 0; pq 1: columns 1, 2)
+    //   pq 2 (wave 6): off-diagonal Gram tiles -> A (fp16 rows)
+    //   pq 3 (wave 7): Q K^T tiles -> P
+    const int pq = wave == 2 ? 0 : wave == 3 ? 1 : wave == 6 ? 2 : 3;
+    unsigned pbt = 0;
+    if (pq == 0 && lane == 0) s.pbar = 0u;
+    // upper 16x16 tiles (0,1) and (2,3) of Tm and P stay zero in both slots
+    for (int e = 64 * pq + lane; e < 2 * 2 * 2 * 256; e += 256) {
+      const int slot = e >> 10, which = (e >> 9) & 1, t = (e >> 8) & 1, rr = (e >> 4) & 15, cc = e & 15;
+      u16* tile = which ? s.tp[slot].p : s.tp[slot].tm;
+      tile[tix(32 * t + rr, 32 * t + 16 + cc)] = 0;
+    }
+    __syncthreads();
+
+    for (int n = -1; n < nchunks; ++n) {
+      const int m = n + 1;  // chunk prepared in this step
+      if (m < nchunks) {
+        const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+        typename SM::TP& T = s.tp[m & 1];
+        const typename SM::QK& Q = s.qk[m % 3];
+        const float* G = s.gate[m % 3];
+        const bf16* qt = reinterpret_cast<const bf16*>(Q.q);
+        const bf16* kt = reinterpret_cast<const bf16*>(Q.k);
+        f16* tmt = reinterpret_cast<f16*>(T.tm);
+        f16* ptt = reinterpret_cast<f16*>(T.p);
+        f16* aft = reinterpret_cast<f16*>(s.af);
+        const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(G[kFast])) != 0;
+        f16x4 tc0, tc1;  // C-form (accumulator layout) of this wave's diagonal inverses
+
+        // The products below take the rows of their second factor as the A operand, so a
+        // lane's accumulator of tile (I, J) holds columns s = 16J + 4lq + e of row
+        // r = 16I + li ("row form", the A-operand layout of the product); the Gram tile is
+        // symmetric, so the same accumulator also gives the C form r = 16I + 4lq + e,
+        // s = 16I + li of a diagonal block.  decay(r, s) = e^{gamma_r - gamma_s} (times
+        // beta_r unless the Q K^T tile is meant), from per-token factors or, when the chunk
+        // decays too fast for them, from gamma itself.
+        auto body = [&](auto fast_c) {
+          constexpr bool kFastDecay = decltype(fast_c)::value;
+          auto rowv = [&](int r, bool qk) -> float {
+            return kFastDecay ? G[(qk ? kFrq : kFrk) + r] : G[kGam + r];
+          };
+          auto colv = [&](int c) -> float { return kFastDecay ? G[kFc + c] : G[kGam + c]; };
+          auto rows4 = [&](int r0, bool qk) -> f32x4 {
+            return *reinterpret_cast<const f32x4*>(&G[(kFastDecay ? (qk ? kFrq : kFrk) : kGam) + r0]);
+          };
+          auto cols4 = [&](int c0) -> f32x4 {
+            return *reinterpret_cast<const f32x4*>(&G[(kFastDecay ? kFc : kGam) + c0]);
+          };
+          auto dec = [&](float rv, float cv, float beta_r) -> float {
+            if constexpr (kFastDecay) return rv * cv;
+            else return beta_r * __expf(rv - cv);
+          };
+
+          if (pq < 2) {
+            // ---- diagonal blocks b = 2pq, 2pq + 1: Gram tile, then (I + L)^-1 as
+            // (I - L)(I + L^2)(I + L^4)(I + L^8) (L strictly lower, L^16 = 0) on fp16 operands
+            bf16x8 kf[2][kG];
+#pragma unroll
+            for (int kk = 0; kk < kG; ++kk)
+#pragma unroll
+              for (int u = 0; u < 2; ++u) kf[u][kk] = lds8(kt + tix(16 * (2 * pq + u) + li, 32 * kk + 8 * lq));
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 g[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < kG; ++kk)
+#pragma unroll
+              for (int u = 0; u < 2; ++u) g[u] = mma16(kf[u][kk], kf[u][kk], g[u]);
+            f16x4 la[2], lc[2];
+            f32x4 x0a[2], x0c[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int b0 = 16 * (2 * pq + u);
+              const float r_li = rowv(b0 + li, false), c_li = colv(b0 + li);
+              const float be_li = kFastDecay ? 1.f : G[kBeta + b0 + li];
+              const f32x4 r_q = rows4(b0 + 4 * lq, false), c_q = cols4(b0 + 4 * lq);
+              f32x4 be_q = {1.f, 1.f, 1.f, 1.f};
+              if constexpr (!kFastDecay) be_q = *reinterpret_cast<const f32x4*>(&G[kBeta + b0 + 4 * lq]);
+              f32x4 va, vc;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int c = 4 * lq + e;
+                va[e] = (c < li) ? dec(r_li, c_q[e], be_li) * g[u][e] : 0.f;   // L[li][c]
+                vc[e] = (li < c) ? dec(r_q[e], c_li, be_q[e]) * g[u][e] : 0.f;  // L[c][li]
+                x0a[u][e] = (c == li ? 1.f : 0.f) - va[e];
+                x0c[u][e] = (c == li ? 1.f : 0.f) - vc[e];
+              }
+              la[u] = cvt_f16x4(va);
+              lc[u] = cvt_f16x4(vc);
+            }
+            f16x4 p2a[2], p2c[2], p4a[2], p4c[2], p8c[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              p2c[u] = cvt_f16x4(mma16x16x16(la[u], lc[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+              p2a[u] = cvt_f16x4(mma16x16x16(lc[u], la[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              p4c[u] = cvt_f16x4(mma16x16x16(p2a[u], p2c[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+              p4a[u] = cvt_f16x4(mma16x16x16(p2c[u], p2a[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) p8c[u] = cvt_f16x4(mma16x16x16(p4a[u], p4c[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+            // X_{k+1} = X_k + X_k L^(2^k) in both forms (the row form of X is the C form of X^T)
+            f32x4 xa[2], xc[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const f16x4 x0a16 = cvt_f16x4(x0a[u]);
+              xc[u] = mma16x16x16(x0a16, p2c[u], x0c[u]);
+              xa[u] = mma16x16x16(p2c[u], x0a16, x0a[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const f16x4 x1a16 = cvt_f16x4(xa[u]);
+              xc[u] = mma16x16x16(x1a16, p4c[u], xc[u]);
+              xa[u] = mma16x16x16(p4c[u], x1a16, xa[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const f16x4 x2a16 = cvt_f16x4(xa[u]);
+              xc[u] = mma16x16x16(x2a16, p8c[u], xc[u]);
+              xa[u] = mma16x16x16(p8c[u], x2a16, xa[u]);
+              const int b0 = 16 * (2 * pq + u);
+              *reinterpret_cast<f16x4*>(&tmt[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u]);
+            }
+            tc0 = cvt_f16x4(xc[0]);
+            tc1 = cvt_f16x4(xc[1]);
+          } else {
+            // ---- pq 2: off-diagonal Gram tiles -> A rows (fp16); pq 3: Q K^T tiles -> P rows
+            auto tiles = [&](auto isq_c) {
+              constexpr bool isq = decltype(isq_c)::value;
+              // lower tiles (I, J), bit I (I + 1) / 2 + J; the Gram leaves out the diagonal
+              constexpr int mask = isq ? 0x3ff : (0x3ff & ~(0x001 | 0x004 | 0x020 | 0x200));
+              f16* dst = isq ? ptt : aft;
+              bf16x8 af[4][kG], bf[4][kG];
+#pragma unroll
+              for (int kk = 0; kk < kG; ++kk)
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                  bf[I][kk] = lds8(kt + tix(16 * I + li, 32 * kk + 8 * lq));
+                  if constexpr (isq) af[I][kk] = lds8(qt + tix(16 * I + li, 32 * kk + 8 * lq));
+                  else af[I][kk] = bf[I][kk];
+                }
+              __builtin_amdgcn_sched_barrier(0);
+              f32x4 acc[10];
+#pragma unroll
+              for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int kk = 0; kk < kG; ++kk) {
+#pragma unroll
+                for (int I = 0, t = 0; I < 4; ++I)
+#pragma unroll
+                  for (int J = 0; J <= I; ++J, ++t)
+                    if ((mask >> t) & 1) acc[t] = mma16(bf[J][kk], af[I][kk], acc[t]);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              f32x4 cv[4];
+#pragma unroll
+              for (int J = 0; J < 4; ++J) cv[J] = cols4(16 * J + 4 * lq);
+#pragma unroll
+              for (int I = 0, t = 0; I < 4; ++I) {
+                const int r = 16 * I + li;
+                const float rv = rowv(r, isq);
+                const float be_r = (kFastDecay || isq) ? 1.f : G[kBeta + r];
+#pragma unroll
+                for (int J = 0; J <= I; ++J, ++t) {
+                  if (!((mask >> t) & 1)) continue;
+                  f32x4 val;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    val[e] = dec(rv, cv[J][e], be_r) * acc[t][e];
+                    if (J == I) val[e] = (4 * lq + e <= li) ? val[e] : 0.f;
+                  }
+                  *reinterpret_cast<f16x4*>(&dst[tix(r, 16 * J + 4 * lq)]) = cvt_f16x4(val);
+                }
+              }
+            };
+            if (pq == 3) tiles(std::true_type{});
+            else tiles(std::false_type{});
+          }
+        };
+        if (fast) body(std::true_type{});
+        else body(std::false_type{});
+
+        if (pq < 3) solve_bar(&s.pbar, pbt);  // A rows (pq 2) and T_bb (pq 0, 1) are in LDS
+        // Off-diagonal 16x16 blocks, one block column per chain of products (fp16 operands,
+        // fp32 accumulation):  T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, with A_ik and T_ii as
+        // row-form A operands from LDS and T_kj in C form (the B-operand layout) in registers.
+        // pq 0 takes column 0, pq 1 columns 1 and 2.
+        if (pq < 2) {
+          auto chain = [&](int j, f16x4 tjj) {
+            f16x4 bt[4];
+            bt[j] = tjj;
+#pragma unroll
+            for (int i = 1; i < 4; ++i) {
+              if (i <= j) continue;
+              f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int k = 0; k < i; ++k)
+                if (k >= j)
+                  sacc = mma16x16x16(*reinterpret_cast<const f16x4*>(&aft[tix(16 * i + li, 16 * k + 4 * lq)]), bt[k], sacc);
+              const f16x4 tii = *reinterpret_cast<const f16x4*>(&tmt[tix(16 * i + li, 16 * i + 4 * lq)]);
+              const f32x4 t = mma16x16x16(tii, cvt_f16x4(sacc), f32x4{0.f, 0.f, 0.f, 0.f});
+              bt[i] = cvt_f16x4(-t);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) tmt[tix(16 * i + 4 * lq + e, 16 * j + li)] = bt[i][e];
+            }
+          };
+          if (pq == 0) {
+            chain(0, tc0);
+          } else {
+            // T_11 in C form from the stored rows of block 1
+            f16x4 t11;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t11[e] = tmt[tix(16 + 4 * lq + e, 16 + li)];
+            chain(1, t11);
+            chain(2, tc0);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // =============================== scan waves ===============================
+  // hs[G][t] holds keys 32G + 8lq + 4t + e (e = 0..3) of value column v0 + 16 wave + li.
+  const int col = v0 + 16 * wave + li;
+  f32x4 hs[kG][2];
+#pragma unroll
+  for (int G = 0; G < kG; ++G)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hs[G][t][e] = p.h0 ? p.h0[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] : 0.f;
+  bf16* og = static_cast<bf16*>(p.o);
+  __syncthreads();
+
+  for (int n = -1; n < nchunks; ++n) {
+    if (n >= 0) {
+      const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+      const int trj = (lane >> 2) & 3, trc = lane & 3;
+      const typename SM::QK& Q = s.qk[n % 3];
+      const u16* vt = s.v[n & 1];
+      const typename SM::TP& T = s.tp[n & 1];
+      const float* vec = s.gate[n % 3];
+      const bf16* kt = reinterpret_cast<const bf16*>(Q.k);
+      const bf16* qt = reinterpret_cast<const bf16*>(Q.q);
+      const f16* tmt = reinterpret_cast<const f16*>(T.tm);
+      const f16* ptt = reinterpret_cast<const f16*>(T.p);
+      const long tok = tok0 + (long)n * kC;
+      const uint32_t rows = (uint32_t)min(kC, len - n * kC);
+
+      // The step is software-pipelined in stages: each stage issues the LDS reads of a later
+      // stage before its own products, and a scheduling barrier between stages keeps the
+      // compiler from sinking those reads next to their uses, so LDS latency overlaps matrix
+      // work.  Dependent chain: K h -> Y -> Tm Y -> update (-> next chunk); Q h and P v_new
+      // are off it and fill the matrix pipe while the chain waits on vector work.
+
+      // ---- stage 0: K rows (pair-row order) for K h; the state as a bf16 B operand
+      bf16x8 kfr[2][2][kG];
+#pragma unroll
+      for (int G = 0; G < kG; ++G)
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) kfr[P][t][G] = lds8(kt + tix(pair_row(P, t, li), 32 * G + 8 * lq));
+      bf16x8 bh[kG];
+#pragma unroll
+      for (int G = 0; G < kG; ++G) bh[G] = pack8<bf16>(hs[G][0], hs[G][1]);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- stage 1: reads of V, the Y gates and Q rows; X_K = K h (tokens
+      // 32P + 8lq + 4t + e of this lane's column), one contraction round at a time
+      u32x2 vv[2][2];
+      f32x4 be[2][2], eg[2][2];
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r0 = 32 * P + 8 * lq + 4 * t;
+          vv[P][t] = tr16(&vt[tix(r0 + trj, 16 * wave + 4 * trc)]);
+          be[P][t] = *reinterpret_cast<const f32x4*>(&vec[kBeta + r0]);
+          eg[P][t] = *reinterpret_cast<const f32x4*>(&vec[kEg + r0]);
+        }
+      bf16x8 qfr[2][2][kG];
+#pragma unroll
+      for (int Gk = 0; Gk < kG; ++Gk)
+#pragma unroll
+        for (int G = 0; G < 2; ++G)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) qfr[G][t][Gk] = lds8(qt + tix(pair_row(G, t, li), 32 * Gk + 8 * lq));
+      f32x4 xk[2][2];
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) xk[P][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int G = 0; G < kG; ++G) {
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) xk[P][t] = mma16(kfr[P][t][G], bh[G], xk[P][t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- stage 2: reads of Tm rows; Y = diag(beta) (V - diag(e^gamma) X_K) (fp16 B
+      // operand); the Q h part of o (value columns 4lq..4lq+3 of token pair_row(G, t, li),
+      // the state as the A operand), which fills the matrix pipe while Y is formed
+      f16x8 tmf[2][2][2];
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int G = P; G < 2; ++G)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) tmf[G][t][P] = lds8(tmt + tix(pair_row(G, t, li), 32 * P + 8 * lq));
+      f32x4 oacc[2][2];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) oacc[G][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f16x8 by[2];
+#pragma unroll
+      for (int Gk = 0; Gk < kG; ++Gk) {
+#pragma unroll
+        for (int G = 0; G < 2; ++G)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) oacc[G][t] = mma16(bh[Gk], qfr[G][t][Gk], oacc[G][t]);
+        if (Gk == 0) {
+#pragma unroll
+          for (int P = 0; P < 2; ++P)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                by[P][4 * t + e] = (f16)(be[P][t][e] * (bf_at(vv[P][t], e) - eg[P][t][e] * xk[P][t][e]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- stage 3: reads of K^T (the update's A operand, transpose reads) and of the
+      // update gates; v_new = Tm Y (token group P feeds groups G >= P)
+      bf16x8 ktf[kG][2][2];
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int G = 0; G < kG; ++G)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int c0 = 32 * G + 8 * trc + 4 * t;
+            ktf[G][t][P] = tr16_pair(&Q.k[tix(32 * P + 8 * lq + trj, c0)], &Q.k[tix(32 * P + 8 * lq + 4 + trj, c0)]);
+          }
+      f32x4 l0[2], l1[2];
+#pragma unroll
+      for (int P = 0; P < 2; ++P) {
+        l0[P] = *reinterpret_cast<const f32x4*>(&vec[kEl + 32 * P + 8 * lq]);
+        l1[P] = *reinterpret_cast<const f32x4*>(&vec[kEl + 32 * P + 8 * lq + 4]);
+      }
+      const float egl = vec[kEgl];
+      f32x4 vn[2][2];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) vn[G][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int P = 0; P < 2; ++P) {
+#pragma unroll
+        for (int G = P; G < 2; ++G)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) vn[G][t] = mma16(tmf[G][t][P], by[P], vn[G][t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- stage 4: reads of P rows and the o gates; bv = v_new (fp16) for P v_new;
+      // v_new e^{gl - gamma} as two bf16 parts; h <- e^gl h + K^T diag(e^{gl - gamma}) v_new,
+      // one round (token half, part) at a time
+      f16x8 pfr[2][2][2];
+      float ego[2][2];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = pair_row(G, t, li);
+#pragma unroll
+          for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds8(ptt + tix(r, 32 * P + 8 * lq));
+          ego[G][t] = vec[kEg + r];
+        }
+      f16x8 bv[2];
+      bf16x8 buh[2], bul[2];
+#pragma unroll
+      for (int P = 0; P < 2; ++P) {
+        bv[P] = pack8<f16>(vn[P][0], vn[P][1]);
+        const f32x4 u0 = vn[P][0] * l0[P], u1 = vn[P][1] * l1[P];
+        buh[P] = pack8<bf16>(u0, u1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bul[P][j] = (bf16)(u0[j] - (float)buh[P][j]);
+          bul[P][4 + j] = (bf16)(u1[j] - (float)buh[P][4 + j]);
+        }
+      }
+#pragma unroll
+      for (int G = 0; G < kG; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) hs[G][t] = hs[G][t] * egl;
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+#pragma unroll
+          for (int G = 0; G < kG; ++G)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) hs[G][t] = mma16(ktf[G][t][P], part ? bul[P] : buh[P], hs[G][t]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+      // ---- stage 5: o^T = scale ((Q h)^T diag(e^gamma) + (P v_new)^T), 8-byte row stores
+      const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4 acc = oacc[G][t] * ego[G][t];
+#pragma unroll
+          for (int P = 0; P <= G; ++P) acc = mma16(bv[P], pfr[G][t][P], acc);
+          const f32x4 ov = acc * p.scale;
+          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(ov[0], ov[1], ov[2], ov[3]), ro,
+                                                pair_row(G, t, li) * v_row + (16 * wave + 4 * lq) * 2, 0, 0);
+        }
+    }
+    __syncthreads();
+  }
+
+  if (p.ht) {
+#pragma unroll
+    for (int G = 0; G < kG; ++G)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p.ht[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] = hs[G][t][e];
+  }
+}
+
+template <int K, bool VL>
+hipError_t launch_k(const FwdParams& p0, int nchains, hipStream_t stream) {
+  FwdParams p = p0;
+  p.nvb = p.V / kBV;
+  hipLaunchKernelGGL((fused16_kernel<K, VL>), dim3(nchains * p.nvb), dim3(kThr), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fused16(const FwdParams& p, int K, bool varlen, int nchains, hipStream_t stream) {
+  if (K == 128) return varlen ? launch_k<128, true>(p, nchains, stream) : launch_k<128, false>(p, nchains, stream);
+  return varlen ? launch_k<64, true>(p, nchains, stream) : launch_k<64, false>(p, nchains, stream);
+}
+
+}  // namespace gdn

@@ -781,6 +781,8 @@ size_t fwd_workspace_bytes(long nslots, int nseq, int dtype, int K, bool pk) {
 hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream) {
   const int nchains = varlen ? p.nseq * p.H : p.B * p.H;
   const long nslots = varlen ? (long)p.H * p.nt_total : (long)p.B * p.H * ((p.T + kC - 1) / kC);
+  // bf16 with a scalar gate and nothing saved per chunk: one fused kernel, no workspace traffic
+  if (dtype == 1 && !p.gk && !p.v_new && !p.h_chunks) return launch_fused16(p, K, varlen, nchains, stream);
   if (varlen) {
     hipError_t e = launch_varlen_tables_impl(p.cu, p.nseq, p.coffs, nullptr, stream);
     if (e != hipSuccess) return e;

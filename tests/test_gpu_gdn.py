@@ -58,6 +58,26 @@ def test_shapes_ragged(dtype, K, V, T):
                    label="%s K%d V%d T%d" % (dtype, K, V, T))
 
 
+@pytest.mark.parametrize("K,V,T", [(128, 128, 200), (64, 128, 131), (128, 64, 64), (64, 64, 1),
+                                   (128, 128, 129), (128, 128, 383)])
+def test_single_kernel_ragged(K, V, T):
+    """bf16 with a scalar gate and no per-chunk saves, the single-kernel path: ragged T (one
+    token, exact chunks, a tail), h0, scale, K and V of 64 and 128."""
+    inp = workloads.gdn_inputs(2, T, 3, K, V, dtype="bf16", seed=T + K + 100, g_shift=2.0)
+    h0 = torch.randn(2, 3, K, V, generator=torch.Generator().manual_seed(3)) * 0.3
+    _run_and_check(inp, scale=0.5, h0=h0, label="single kernel K%d V%d T%d" % (K, V, T))
+
+
+def test_single_kernel_beta_zero_exact():
+    """beta = 0 from a zero state on the single-kernel path: exact zeros."""
+    g = _gpu()
+    inp = _to(workloads.gdn_inputs(2, 150, 2, 128, 128, dtype="bf16", seed=3))
+    out = g.gdn_fwd(inp["q"], inp["k"], inp["v"], torch.zeros_like(inp["beta"]), g=inp["g"])
+    torch.cuda.synchronize()
+    for name in ("o", "ht"):
+        assert torch.count_nonzero(out[name]).item() == 0, name
+
+
 def test_beta_zero_exact():
     """beta = 0 from a zero state: the GPU path must return exact zeros."""
     g = _gpu()

@@ -35,10 +35,13 @@ def _run(inp, h0=None, want_h=True, label=""):
     return out
 
 
+@pytest.mark.parametrize("want_h", [True, False])
 @pytest.mark.parametrize("lengths,K,dtype", [([1, 64, 65, 200, 7], 128, "bf16"),
                                              ([130, 3, 64], 64, "bf16"),
                                              ([100, 28, 129], 64, "f32")])
-def test_packed_small(lengths, K, dtype):
+def test_packed_small(lengths, K, dtype, want_h):
+    """Packed sequences with h0; with and without saved h / v_new (bf16 without saves runs
+    the single-kernel path)."""
     gen = torch.Generator().manual_seed(sum(lengths))
     cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
     cu[1:] = torch.cumsum(torch.tensor(lengths), 0)
@@ -46,7 +49,7 @@ def test_packed_small(lengths, K, dtype):
     inp = workloads.gdn_inputs(1, T, 3, K, 128, dtype=dtype, seed=len(lengths), g_shift=2.0)
     inp["cu_seqlens"] = cu
     h0 = torch.randn(len(lengths), 3, K, 128, generator=gen) * 0.3
-    _run(inp, h0=h0, label="lengths %s K%d %s" % (lengths, K, dtype))
+    _run(inp, h0=h0, want_h=want_h, label="lengths %s K%d %s saves %s" % (lengths, K, dtype, want_h))
 
 
 def test_packed_equals_separate_runs_bitwise():
