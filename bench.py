@@ -30,9 +30,20 @@ METRIC = "tokens·heads/sec for chunked gated delta-rule fwd; % MFMA (or HBM) pe
 KERNEL_SOURCE_DIR = "gated_delta_rule_29_amd/csrc"
 # The kernels one forward call launches; the roofline covers the whole call (every kernel on
 # the path), timed with HIP events around it on the launch stream.
+KERNELS_FUSED = "gdn_fwd call: fused16_kernel"
 KERNELS_BF16 = "gdn_fwd call: prep16_kernel + scan16_kernel"
 KERNELS_F32 = "gdn_fwd call: chunk_prep_kernel + scan_kernel"
-COUNTER_FILE = "profiles/gdn_fwd_kernel_b4h16t4096_hbm_counters.md"
+
+
+def kernels_of(dt, per_key, save):
+    """Kernels one forward call launches: bf16 with a scalar gate and nothing saved per chunk
+    runs the single fused kernel; per-key gates or saved states take the two-kernel path."""
+    import torch
+
+    if dt != torch.bfloat16:
+        return KERNELS_F32
+    return KERNELS_BF16 if (per_key or save) else KERNELS_FUSED
+COUNTER_FILE = "profiles/fused16_kernel_b4h16t4096_hbm_counters.md"
 
 
 def alg_bytes_per_launch(B, T, H, K, V, elt=2, per_key=False, save=False, n_states=None,
@@ -184,7 +195,7 @@ def main():
         th = B * T * H
         elt = 2 if dt == torch.bfloat16 else 4
         alg = alg_bytes_per_launch(B, T, H, K, V, elt, inp["gk"] is not None, save)
-        kernel = KERNELS_BF16 if dt == torch.bfloat16 else KERNELS_F32
+        kernel = kernels_of(dt, inp["gk"] is not None, save)
         config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
                   "chunk": 64, "state": "fp32", "per_key_gate": inp["gk"] is not None,
                   "saves_h_and_v_new": save}
@@ -202,7 +213,7 @@ def main():
         th = T * H
         elt = 2 if dt == torch.bfloat16 else 4
         alg = alg_bytes_per_launch(1, T, H, K, V, elt, False, False, n_states=N * H)
-        kernel = (KERNELS_BF16 if dt == torch.bfloat16 else KERNELS_F32) + " (packed)"
+        kernel = kernels_of(dt, inp["gk"] is not None, False) + " (packed)"
         config = {"workload": args.workload, "T_total": T, "N": N, "H": H, "K": K, "V": V,
                   "lengths": (cu[1:] - cu[:-1]).tolist(), "chunk": 64, "state": "fp32"}
 

@@ -495,7 +495,6 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 
   // =============================== scan waves ===============================
   // hs[G][t] holds keys 32G + 8lq + 4t + e (e = 0..3) of value column v0 + 16 wave + li.
-  const int col = v0 + 16 * wave + li;
   f32x4 hs[kG][2];
 #pragma unroll
   for (int G = 0; G < kG; ++G)
@@ -503,64 +502,65 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        hs[G][t][e] = p.h0 ? p.h0[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] : 0.f;
+        hs[G][t][e] = p.h0 ? p.h0[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + v0 + 16 * wave + li] : 0.f;
   bf16* og = static_cast<bf16*>(p.o);
+  // K and Q rows of a chunk (pair-row order).  The first contraction half of K is read during
+  // the step before the one that uses it (a chunk's q / k tiles are in LDS from the end of
+  // the step two before its own); the rest is read under the K h products.
+  bf16x8 kfr[2][2][kG], qfr[2][2][kG];
+  auto read_k = [&](int c, int li, int lq, int g0, int g1) {
+    const bf16* kt = reinterpret_cast<const bf16*>(s.qk[c % 3].k);
+#pragma unroll
+    for (int G = 0; G < kG; ++G)
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (G >= g0 && G < g1) kfr[P][t][G] = lds8(kt + tix(pair_row(P, t, li), 32 * G + 8 * lq));
+  };
+  auto read_q = [&](int c, int li, int lq) {
+    const bf16* qt = reinterpret_cast<const bf16*>(s.qk[c % 3].q);
+#pragma unroll
+    for (int Gk = 0; Gk < kG; ++Gk)
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) qfr[G][t][Gk] = lds8(qt + tix(pair_row(G, t, li), 32 * Gk + 8 * lq));
+  };
   __syncthreads();
 
   for (int n = -1; n < nchunks; ++n) {
-    if (n >= 0) {
-      const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
-      const int trj = (lane >> 2) & 3, trc = lane & 3;
+    const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+    const int trj = (lane >> 2) & 3, trc = lane & 3;
+    if (n < 0) {
+      if (nchunks > 0) read_k(0, li, lq, 0, kG / 2);
+    } else {
       const typename SM::QK& Q = s.qk[n % 3];
       const u16* vt = s.v[n & 1];
       const typename SM::TP& T = s.tp[n & 1];
       const float* vec = s.gate[n % 3];
-      const bf16* kt = reinterpret_cast<const bf16*>(Q.k);
-      const bf16* qt = reinterpret_cast<const bf16*>(Q.q);
       const f16* tmt = reinterpret_cast<const f16*>(T.tm);
       const f16* ptt = reinterpret_cast<const f16*>(T.p);
       const long tok = tok0 + (long)n * kC;
       const uint32_t rows = (uint32_t)min(kC, len - n * kC);
+      const bool more = n + 1 < nchunks;
 
       // The step is software-pipelined in stages: each stage issues the LDS reads of a later
-      // stage before its own products, and a scheduling barrier between stages keeps the
-      // compiler from sinking those reads next to their uses, so LDS latency overlaps matrix
-      // work.  Dependent chain: K h -> Y -> Tm Y -> update (-> next chunk); Q h and P v_new
-      // are off it and fill the matrix pipe while the chain waits on vector work.
+      // stage (or of the next chunk) before its own products, and scheduling barriers keep
+      // the compiler from sinking those reads next to their uses, so LDS latency overlaps
+      // matrix work.  Dependent chain: K h -> Y -> Tm Y -> update (-> next chunk); Q h and
+      // P v_new are off it and fill the matrix pipe while the chain waits on vector work.
 
-      // ---- stage 0: K rows (pair-row order) for K h; the state as a bf16 B operand
-      bf16x8 kfr[2][2][kG];
-#pragma unroll
-      for (int G = 0; G < kG; ++G)
-#pragma unroll
-        for (int P = 0; P < 2; ++P)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) kfr[P][t][G] = lds8(kt + tix(pair_row(P, t, li), 32 * G + 8 * lq));
+      // ---- stage 1: X_K = K h (tokens 32P + 8lq + 4t + e of this lane's column), a
+      // contraction round at a time; under it, reads of the rest of K, of V, the Y gates and
+      // the Q rows
+      read_k(n, li, lq, kG / 2, kG);
       bf16x8 bh[kG];
 #pragma unroll
       for (int G = 0; G < kG; ++G) bh[G] = pack8<bf16>(hs[G][0], hs[G][1]);
       __builtin_amdgcn_sched_barrier(0);
-
-      // ---- stage 1: reads of V, the Y gates and Q rows; X_K = K h (tokens
-      // 32P + 8lq + 4t + e of this lane's column), one contraction round at a time
       u32x2 vv[2][2];
       f32x4 be[2][2], eg[2][2];
-#pragma unroll
-      for (int P = 0; P < 2; ++P)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r0 = 32 * P + 8 * lq + 4 * t;
-          vv[P][t] = tr16(&vt[tix(r0 + trj, 16 * wave + 4 * trc)]);
-          be[P][t] = *reinterpret_cast<const f32x4*>(&vec[kBeta + r0]);
-          eg[P][t] = *reinterpret_cast<const f32x4*>(&vec[kEg + r0]);
-        }
-      bf16x8 qfr[2][2][kG];
-#pragma unroll
-      for (int Gk = 0; Gk < kG; ++Gk)
-#pragma unroll
-        for (int G = 0; G < 2; ++G)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) qfr[G][t][Gk] = lds8(qt + tix(pair_row(G, t, li), 32 * Gk + 8 * lq));
       f32x4 xk[2][2];
 #pragma unroll
       for (int P = 0; P < 2; ++P)
@@ -572,12 +572,24 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         for (int P = 0; P < 2; ++P)
 #pragma unroll
           for (int t = 0; t < 2; ++t) xk[P][t] = mma16(kfr[P][t][G], bh[G], xk[P][t]);
+        if (G == kG / 2 - 1) {
+#pragma unroll
+          for (int P = 0; P < 2; ++P)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int r0 = 32 * P + 8 * lq + 4 * t;
+              vv[P][t] = tr16(&vt[tix(r0 + trj, 16 * wave + 4 * trc)]);
+              be[P][t] = *reinterpret_cast<const f32x4*>(&vec[kBeta + r0]);
+              eg[P][t] = *reinterpret_cast<const f32x4*>(&vec[kEg + r0]);
+            }
+        }
+        if (G == kG - 1) read_q(n, li, lq);
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- stage 2: reads of Tm rows; Y = diag(beta) (V - diag(e^gamma) X_K) (fp16 B
-      // operand); the Q h part of o (value columns 4lq..4lq+3 of token pair_row(G, t, li),
-      // the state as the A operand), which fills the matrix pipe while Y is formed
+      // ---- stage 2: reads of Tm rows; Y = diag(beta) (V - diag(e^gamma) X_K) (fp16 B operand); the Q h part
+      // of o (value columns 4lq..4lq+3 of token pair_row(G, t, li), the state as the A
+      // operand), which fills the matrix pipe while Y is formed
       f16x8 tmf[2][2][2];
 #pragma unroll
       for (int P = 0; P < 2; ++P)
@@ -609,8 +621,8 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- stage 3: reads of K^T (the update's A operand, transpose reads) and of the
-      // update gates; v_new = Tm Y (token group P feeds groups G >= P)
+      // ---- stage 3: reads of K^T (the update's A operand, transpose reads), the update
+      // gates, P rows and the o gates; v_new = Tm Y (token group P feeds groups G >= P)
       bf16x8 ktf[kG][2][2];
 #pragma unroll
       for (int P = 0; P < 2; ++P)
@@ -628,6 +640,17 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         l1[P] = *reinterpret_cast<const f32x4*>(&vec[kEl + 32 * P + 8 * lq + 4]);
       }
       const float egl = vec[kEgl];
+      f16x8 pfr[2][2][2];
+      float ego[2][2];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = pair_row(G, t, li);
+#pragma unroll
+          for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds8(ptt + tix(r, 32 * P + 8 * lq));
+          ego[G][t] = vec[kEg + r];
+        }
       f32x4 vn[2][2];
 #pragma unroll
       for (int G = 0; G < 2; ++G)
@@ -642,20 +665,8 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- stage 4: reads of P rows and the o gates; bv = v_new (fp16) for P v_new;
-      // v_new e^{gl - gamma} as two bf16 parts; h <- e^gl h + K^T diag(e^{gl - gamma}) v_new,
-      // one round (token half, part) at a time
-      f16x8 pfr[2][2][2];
-      float ego[2][2];
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = pair_row(G, t, li);
-#pragma unroll
-          for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds8(ptt + tix(r, 32 * P + 8 * lq));
-          ego[G][t] = vec[kEg + r];
-        }
+      // ---- stage 4: bv = v_new (fp16) for P v_new; v_new e^{gl - gamma} as two bf16 parts;
+      // h <- e^gl h + K^T diag(e^{gl - gamma}) v_new, a round (token half, part) at a time
       f16x8 bv[2];
       bf16x8 buh[2], bul[2];
 #pragma unroll
@@ -674,7 +685,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) hs[G][t] = hs[G][t] * egl;
 #pragma unroll
-      for (int P = 0; P < 2; ++P)
+      for (int P = 0; P < 2; ++P) {
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
 #pragma unroll
@@ -683,8 +694,11 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
             for (int t = 0; t < 2; ++t) hs[G][t] = mma16(ktf[G][t][P], part ? bul[P] : buh[P], hs[G][t]);
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
 
-      // ---- stage 5: o^T = scale ((Q h)^T diag(e^gamma) + (P v_new)^T), 8-byte row stores
+      // ---- stage 5: o^T = scale ((Q h)^T diag(e^gamma) + (P v_new)^T), 8-byte row stores;
+      // reads of the first half of the next chunk's K rows
+      if (more) read_k(n + 1, li, lq, 0, kG / 2);
       const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
 #pragma unroll
       for (int G = 0; G < 2; ++G)
@@ -702,13 +716,15 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   }
 
   if (p.ht) {
+    // lane-derived offsets recomputed here rather than kept live across the loop
+    const int ln = opaque_lane();
+    float* ht = p.ht + (long)chain * K * p.V + v0 + 16 * wave + (ln & 15);
 #pragma unroll
     for (int G = 0; G < kG; ++G)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p.ht[((long)chain * K + 32 * G + 8 * lq + 4 * t + e) * p.V + col] = hs[G][t][e];
+        for (int e = 0; e < 4; ++e) ht[(long)(32 * G + 8 * (ln >> 4) + 4 * t + e) * p.V] = hs[G][t][e];
   }
 }
 
