@@ -19,11 +19,13 @@
 //   num = Q_rot (S_f + R_f),   den = Q_pos . (z_f + zR_f).
 //
 // Kernels: rms (inv-RMS per token; with outputs it is gdn_prep), frame_stats (G, U, Gz, uz
-// per (b, h, f) from k, v with the prep applied on the fly), scan (16-column blocks of the
-// state per (b, h), both directions, writes the summed states), out (num, den per 64-token
-// block).  Products use fp16 operands and fp32 accumulation; the state is fp32.
+// per (b, h, f) from k, v with the prep applied on the fly, one workgroup per frame), scan
+// (16-column blocks of the state per (b, h), both directions, writes the summed states), out
+// (num, den per 64-token block).  Products use fp16 operands and fp32 accumulation; the state
+// is fp32.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_tiles.h"
 
 namespace gdn {
 
@@ -126,126 +128,156 @@ __global__ __launch_bounds__(kPrepThreads) void rms_prep_kernel(const PrepParams
 }
 
 // ---- frame statistics -------------------------------------------------------------------
-// Transposed [d][token] tiles of 64 tokens.  Token octets are XOR-swizzled with the row's
-// d-octet so that the per-token stores of one wave spread over the LDS banks, while every
-// 8-token run a matrix-core operand needs stays contiguous.
-__device__ __forceinline__ int tr_idx(int d, int s) {
-  return d * 64 + ((((s >> 3) ^ (d >> 3)) & 7) << 3) + (s & 7);
+// One workgroup of twelve waves per (b, h, frame) computes all three statistics over the
+// frame's tokens, 64 at a time:
+//   G = K_rot^T diag(beta) K_rot,  U = K_rot^T diag(beta) V,  Gz = K_pos^T diag(beta) K_pos,
+//   uz = K_pos^T beta.
+// Prep: every thread takes (token, 8-channel octet) items -- 16 threads per token row, so the
+// qkv loads are whole 256-byte rows -- applies the front end once and writes five fp16 token
+// rows (K_rot, beta K_rot, beta V, K_pos, beta K_pos) into LDS with 16-byte stores.
+// Products: wave w accumulates quadrant (w % 4) of statistic w / 4; both operands contract
+// over tokens, so they come from the row-major tiles by LDS transpose reads
+// (ds_read_b64_tr_b16: within a 16-lane group, lane n receives element j of the 8-byte piece
+// addressed by lane 4j + n / 4, halfword n % 4).  A transpose-read operand pair for
+// (32-block Gb, half t) gives lane (li, lq) channel 32Gb + 8(li >> 2) + 4t + (li & 3) at
+// tokens 8lq + j; the accumulator of such a pair of operands holds row channel
+// 32Gb + 8lq + 4t + e and column channel 32Gb' + 8(li >> 2) + 4t' + (li & 3).
+constexpr int kStatThreads = 768;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x8 tr_pair(const f16* p0, const f16* p1) {
+  auto rd = [](const f16* p) {
+    return __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(uintptr_t)(const __attribute__((address_space(3))) char*)p));
+  };
+  const u32x4v w = __builtin_shufflevector(rd(p0), rd(p1), 0, 1, 2, 3);
+  return __builtin_bit_cast(f16x8, w);
 }
 
-constexpr int kStatThreads = 256;
-
-// part 0: G_f (fp16); part 1: U_f (fp32); part 2: Gz_f (fp16) and uz_f.  One workgroup per
-// (b, h, f, part); wave w accumulates the D/2 x D/2 quadrant (w/2, w%2).
 template <int D>
 __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnParams p) {
-  constexpr int kT = 64;  // tokens per block
-  __shared__ __attribute__((aligned(16))) f16 xa[D * kT];   // A side: x^T  (x = k_rot or k_pos)
-  __shared__ __attribute__((aligned(16))) f16 xb[D * kT];   // B side: (beta x)^T or (beta v)^T
-  const int part = blockIdx.y;  // 0: G, 1: U, 2: Gz
+  constexpr int kT = 64;         // tokens per block
+  constexpr int kOct = D / 8;    // octets per token row
+  constexpr int kNG = D / 64;    // 32-channel blocks per quadrant side
+  // tiles: 0 K_rot, 1 beta K_rot, 2 beta V, 3 K_pos, 4 beta K_pos  ([64][D] fp16, tix_x64)
+  __shared__ __attribute__((aligned(16))) f16 tl[5][kT * D];
   const int bhf = blockIdx.x;
   const int f = bhf % p.F, h = (bhf / p.F) % p.H, b = bhf / (p.F * p.H);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, lq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4, trj = (lane >> 2) & 3, trc = lane & 3;
   const int C = p.H * D;
   const bf16* qkv = static_cast<const bf16*>(p.qkv);
-  const int qi = wave >> 1, qj = wave & 1;  // quadrant of D/2 x D/2
-  constexpr int kQT = D / 32;                // 16x16 tiles per quadrant side
-  f32x4 acc[kQT][kQT];
+  const int m = wave >> 2, qi = (wave & 3) >> 1, qj = wave & 1;
+  const f16* ta = tl[m == 2 ? 3 : 0];
+  const f16* tb = tl[m == 0 ? 1 : (m == 1 ? 2 : 4)];
+  f32x4 acc[kNG][2][kNG][2];
 #pragma unroll
-  for (int i = 0; i < kQT; ++i)
+  for (int a = 0; a < kNG; ++a)
 #pragma unroll
-    for (int j = 0; j < kQT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // part 2: this lane's running sum over its tokens of beta * k_pos for the d-octets its
-  // wave writes (octet wave + 4i); reduced across lanes once at the end.
-  float uzr[D / 32][8];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+      for (int c = 0; c < kNG; ++c)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) uzr[i][j] = 0.f;
+        for (int u = 0; u < 2; ++u) acc[a][t][c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this thread's octet (fixed: kStatThreads is a multiple of kOct) and running beta k_pos
+  const int oct = tid % kOct;
+  float uzr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) uzr[j] = 0.f;
+  float w8[8];
+  load8f(p.k_norm_w + h * D + 8 * oct, w8);
 
   for (int t0 = 0; t0 < p.S; t0 += kT) {
     __syncthreads();
-    // lane -> token s = t0 + lane; wave w handles d-octets w, w+4, ... (D/8 octets)
-    const int s = lane;
-    const long n = (long)f * p.S + t0 + s;
-    const long bn = (long)b * p.N + n;
-    const float inv = p.k_inv_rms[bn];
-    const float bt = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
-    const bf16* krow = qkv + bn * 3L * C + C + (long)h * D;
-    const bf16* vrow = krow + C;
+    for (int it = tid; it < kT * kOct; it += kStatThreads) {
+      const int s = it / kOct;
+      const long n = (long)f * p.S + t0 + s;
+      const long bn = (long)b * p.N + n;
+      const float inv = p.k_inv_rms[bn];
+      const float bt = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
+      const bf16* krow = qkv + bn * 3L * C + C + (long)h * D + 8 * oct;
+      float x[8], v[8], cs[8], sn[8], pos[8], rot[8];
+      load8f(krow, x);
+      load8f(krow + C, v);
+      load8f(p.rope_cos + n * D + 8 * oct, cs);
+      load8f(p.rope_sin + n * D + 8 * oct, sn);
+      prep8(x, inv, w8, cs, sn, p.k_scale, pos, rot);
+      f16x8 r0, r1, r2, r3, r4;
 #pragma unroll
-    for (int oi = 0; oi < D / 32; ++oi) {
-      const int oc = wave + 4 * oi;
-      const int d0 = oc * 8;
-      float x[8], pos[8], rot[8];
-      if (part == 1) {
-        float w[8], cs[8], sn[8], v[8];
-        load8f(krow + d0, x);
-        load8f(p.k_norm_w + h * D + d0, w);
-        load8f(p.rope_cos + n * D + d0, cs);
-        load8f(p.rope_sin + n * D + d0, sn);
-        prep8(x, inv, w, cs, sn, p.k_scale, pos, rot);
-        load8f(vrow + d0, v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xa[tr_idx(d0 + j, s)] = (f16)rot[j];
-          xb[tr_idx(d0 + j, s)] = (f16)(bt * v[j]);
-        }
-      } else {
-        float w[8], cs[8], sn[8];
-        load8f(krow + d0, x);
-        load8f(p.k_norm_w + h * D + d0, w);
-        load8f(p.rope_cos + n * D + d0, cs);
-        load8f(p.rope_sin + n * D + d0, sn);
-        prep8(x, inv, w, cs, sn, p.k_scale, pos, rot);
-        const float* src = part == 0 ? rot : pos;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xa[tr_idx(d0 + j, s)] = (f16)src[j];
-          xb[tr_idx(d0 + j, s)] = (f16)(bt * src[j]);
-          uzr[oi][j] += bt * pos[j];
-        }
+      for (int j = 0; j < 8; ++j) {
+        r0[j] = (f16)rot[j];
+        r1[j] = (f16)(bt * rot[j]);
+        r2[j] = (f16)(bt * v[j]);
+        r3[j] = (f16)pos[j];
+        r4[j] = (f16)(bt * pos[j]);
+        uzr[j] += bt * pos[j];
       }
+      const int ix = tix_x64(s, 8 * oct);
+      *reinterpret_cast<f16x8*>(&tl[0][ix]) = r0;
+      *reinterpret_cast<f16x8*>(&tl[1][ix]) = r1;
+      *reinterpret_cast<f16x8*>(&tl[2][ix]) = r2;
+      *reinterpret_cast<f16x8*>(&tl[3][ix]) = r3;
+      *reinterpret_cast<f16x8*>(&tl[4][ix]) = r4;
     }
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < kT / 32; ++ks) {
-      f16x8 a[kQT], bb[kQT];
+    for (int P = 0; P < kT / 32; ++P) {
+      f16x8 af[kNG][2], bf[kNG][2];
 #pragma unroll
-      for (int i = 0; i < kQT; ++i) a[i] = lds8(&xa[tr_idx((D / 2) * qi + 16 * i + li, 32 * ks + 8 * lq)]);
+      for (int g = 0; g < kNG; ++g)
 #pragma unroll
-      for (int j = 0; j < kQT; ++j) bb[j] = lds8(&xb[tr_idx((D / 2) * qj + 16 * j + li, 32 * ks + 8 * lq)]);
+        for (int t = 0; t < 2; ++t) {
+          const int ca = 32 * (kNG * qi + g) + 8 * trc + 4 * t;
+          const int cb = 32 * (kNG * qj + g) + 8 * trc + 4 * t;
+          af[g][t] = tr_pair(&ta[tix_x64(32 * P + 8 * lq + trj, ca)], &ta[tix_x64(32 * P + 8 * lq + 4 + trj, ca)]);
+          bf[g][t] = tr_pair(&tb[tix_x64(32 * P + 8 * lq + trj, cb)], &tb[tix_x64(32 * P + 8 * lq + 4 + trj, cb)]);
+        }
 #pragma unroll
-      for (int i = 0; i < kQT; ++i)
+      for (int a = 0; a < kNG; ++a)
 #pragma unroll
-        for (int j = 0; j < kQT; ++j) acc[i][j] = mma16(a[i], bb[j], acc[i][j]);
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int c = 0; c < kNG; ++c)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) acc[a][t][c][u] = mma16(af[a][t], bf[c][u], acc[a][t][c][u]);
     }
   }
-  // epilogue: rows d1 = (D/2)qi + 16i + 4lq + e, columns d2 = (D/2)qj + 16j + li
+  // epilogue: row channel 32(kNG qi + a) + 8lq + 4t + e, column 32(kNG qj + c) + 8(li >> 2) + 4u + (li & 3)
   const long mat = (((long)b * p.H + h) * p.F + f) * (long)D * D;
 #pragma unroll
-  for (int i = 0; i < kQT; ++i)
+  for (int a = 0; a < kNG; ++a)
 #pragma unroll
-    for (int j = 0; j < kQT; ++j)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d1 = (D / 2) * qi + 16 * i + 4 * lq + e, d2 = (D / 2) * qj + 16 * j + li;
-        const long idx = mat + (long)d1 * D + d2;
-        if (part == 0) p.G[idx] = (f16)acc[i][j][e];
-        else if (part == 2) p.Gz[idx] = (f16)acc[i][j][e];
-        else p.U[idx] = acc[i][j][e];
-      }
-  if (part == 2) {
+      for (int c = 0; c < kNG; ++c)
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float x = uzr[i][j];
+          for (int e = 0; e < 4; ++e) {
+            const int d1 = 32 * (kNG * qi + a) + 8 * lq + 4 * t + e;
+            const int d2 = 32 * (kNG * qj + c) + 8 * (li >> 2) + 4 * u + (li & 3);
+            const long idx = mat + (long)d1 * D + d2;
+            const float x = acc[a][t][c][u][e];
+            if (m == 0) p.G[idx] = (f16)x;
+            else if (m == 1) p.U[idx] = x;
+            else p.Gz[idx] = (f16)x;
+          }
+  // uz: sum of the per-thread partial sums of each channel (threads of one octet)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&tl[0][0]);  // [kStatThreads][8]
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-        if (lane == 0) p.uz[(((long)b * p.H + h) * p.F + f) * D + 8 * (wave + 4 * i) + j] = x;
-      }
+  for (int j = 0; j < 8; ++j) red[tid * 8 + j] = uzr[j];
+  __syncthreads();
+  if (tid < D) {
+    const int o = tid / 8, j = tid % 8;
+    float x = 0.f;
+    for (int t = o; t < kStatThreads; t += kOct) x += red[t * 8 + j];
+    p.uz[(((long)b * p.H + h) * p.F + f) * D + tid] = x;
   }
 }
 
@@ -452,11 +484,11 @@ hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int nbhf = p.B * p.H * p.F;
   if (p.D == 128) {
-    hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf, 3), dim3(kStatThreads), 0, stream, p);
+    hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
     hipLaunchKernelGGL(scan_kernel<128>, dim3(p.B * p.H * (128 / 16 + 1)), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(out_kernel<128>, dim3(p.B * p.H * (p.N / 64)), dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf, 3), dim3(kStatThreads), 0, stream, p);
+    hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
     hipLaunchKernelGGL(scan_kernel<64>, dim3(p.B * p.H * (64 / 16 + 1)), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(out_kernel<64>, dim3(p.B * p.H * (p.N / 64)), dim3(256), 0, stream, p);
   }

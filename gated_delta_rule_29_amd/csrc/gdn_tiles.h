@@ -46,4 +46,12 @@ __device__ __forceinline__ int tix_s32(int r, int c) {
   return (c >> 5) * (R * 32) + r * 32 + ((((c >> 3) & 3) ^ ((r >> 3) & 3)) << 3) + (c & 7);
 }
 
+// Column-split [64][W] tile (W a multiple of 32) whose octets are permuted by
+// ((r >> 2) ^ (r >> 3)) & 3.  16-byte reads of one octet from 16 consecutive rows or from the
+// pair rows 32G + 8i + 4t + j hit 16 distinct bank groups, and transposed 8-byte reads of four
+// consecutive rows x four octets hit 16 distinct 8-byte slots.
+__device__ __forceinline__ int tix_x64(int r, int c) {
+  return (c >> 5) * (64 * 32) + r * 32 + ((((c >> 3) & 3) ^ (((r >> 2) ^ (r >> 3)) & 3)) << 3) + (c & 7);
+}
+
 }  // namespace gdn
