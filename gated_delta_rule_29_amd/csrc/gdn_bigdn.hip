@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
   const int f = bhf % p.F, h = (bhf / p.F) % p.H, b = bhf / (p.F * p.H);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 15, lq = lane >> 4, trj = (lane >> 2) & 3, trc = lane & 3;
+  const int li = lane & 15, lq = lane >> 4;
   const int C = p.H * D;
   const bf16* qkv = static_cast<const bf16*>(p.qkv);
   const int m = wave >> 2, qi = (wave & 3) >> 1, qj = wave & 1;
@@ -189,24 +189,61 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
   float uzr[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) uzr[j] = 0.f;
-  float w8[8];
-  load8f(p.k_norm_w + h * D + 8 * oct, w8);
+
+  // Items (token, octet) of a block: this thread takes it = tid + kStatThreads i.  The k, v
+  // rows, inverse RMS and beta of its first item are loaded one block ahead (in flight during
+  // the products of the block before); the RoPE tables, shared by every head, and a second
+  // item's rows are loaded when used.
+  constexpr int kItems = (kT * kOct + kStatThreads - 1) / kStatThreads;
+  bf16x8 kx, vx;
+  float ivx = 0.f, btx = 0.f;
+  auto load_items = [&](int t0) {
+    const int it = tid;
+    if (it < kT * kOct && t0 < p.S) {
+      const int s = it / kOct;
+      const long bn = (long)b * p.N + (long)f * p.S + t0 + s;
+      const bf16* krow = qkv + bn * 3L * C + C + (long)h * D + 8 * oct;
+      kx = *reinterpret_cast<const bf16x8*>(krow);
+      vx = *reinterpret_cast<const bf16x8*>(krow + C);
+      ivx = p.k_inv_rms[bn];
+      btx = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
+    }
+  };
+  load_items(0);
 
   for (int t0 = 0; t0 < p.S; t0 += kT) {
     __syncthreads();
-    for (int it = tid; it < kT * kOct; it += kStatThreads) {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = tid + kStatThreads * i;
+      if (it >= kT * kOct) continue;
       const int s = it / kOct;
       const long n = (long)f * p.S + t0 + s;
       const long bn = (long)b * p.N + n;
-      const float inv = p.k_inv_rms[bn];
-      const float bt = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
-      const bf16* krow = qkv + bn * 3L * C + C + (long)h * D + 8 * oct;
-      float x[8], v[8], cs[8], sn[8], pos[8], rot[8];
-      load8f(krow, x);
-      load8f(krow + C, v);
+      bf16x8 ki, vi;
+      float ivi, bt;
+      if (i == 0) {
+        ki = kx;
+        vi = vx;
+        ivi = ivx;
+        bt = btx;
+      } else {
+        const bf16* krow = qkv + bn * 3L * C + C + (long)h * D + 8 * oct;
+        ki = *reinterpret_cast<const bf16x8*>(krow);
+        vi = *reinterpret_cast<const bf16x8*>(krow + C);
+        ivi = p.k_inv_rms[bn];
+        bt = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
+      }
+      float x[8], v[8], cs[8], sn[8], pos[8], rot[8], w8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = (float)ki[j];
+        v[j] = (float)vi[j];
+      }
       load8f(p.rope_cos + n * D + 8 * oct, cs);
       load8f(p.rope_sin + n * D + 8 * oct, sn);
-      prep8(x, inv, w8, cs, sn, p.k_scale, pos, rot);
+      load8f(p.k_norm_w + h * D + 8 * oct, w8);
+      prep8(x, ivi, w8, cs, sn, p.k_scale, pos, rot);
       f16x8 r0, r1, r2, r3, r4;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -225,6 +262,11 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
       *reinterpret_cast<f16x8*>(&tl[4][ix]) = r4;
     }
     __syncthreads();
+    load_items(t0 + kT);
+    // lane-derived LDS addresses recomputed per block instead of held across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int li = ln & 15, lq = ln >> 4, trj = (ln >> 2) & 3, trc = ln & 3;
 #pragma unroll
     for (int P = 0; P < kT / 32; ++P) {
       f16x8 af[kNG][2], bf[kNG][2];
@@ -283,8 +325,10 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
 
 // ---- scan -------------------------------------------------------------------------------
 // One workgroup per (b, h, 16-column block cb) of the state; block cb == D/16 runs z.
-// Wave w owns state rows 32w..32w+31 of the block.  The state lives in registers (fp32) and
-// is exchanged through LDS (fp16 transposed copy) as the B operand of G S each frame.
+// Wave w owns state rows (D/4)w .. (D/4)w + D/4 - 1 of the block.  The state lives in
+// registers (fp32) and is exchanged through LDS (fp16 transposed copy) as the B operand of
+// G S each frame.  The frames' G rows and U entries a lane needs are loaded one frame ahead,
+// so the global-memory latency overlaps the previous frame's products.
 template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   __shared__ __attribute__((aligned(16))) f16 st[16][D];  // state^T as fp16 operand
@@ -298,38 +342,57 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   const float* decay = p.decay + (long)bh * F;
 
   if (cb == D / 16) {
-    // z: z <- d (z - Gz z) + uz, forward then reverse; zsum_f = z_f + zR_f.
-    if (tid < D) zs[tid] = 0.f;
-    __syncthreads();
-    for (int f = 0; f < F; ++f) {
+    // z: z <- d (z - Gz z) + uz, forward then reverse; zsum_f = z_f + zR_f.  Thread tid < D
+    // owns entry tid; its Gz row of the next frame is loaded ahead.
+    typedef f16 f16x8_t __attribute__((ext_vector_type(8)));
+    f16x8_t gr[D / 8], gn[D / 8];
+    float un = 0.f;
+    auto load_row = [&](int fa, f16x8_t* g, float& u) {
+      if (tid < D && fa >= 0 && fa < F) {
+        const f16* src = p.Gz + mat0 + (long)fa * D * D + (long)tid * D;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) g[c] = *reinterpret_cast<const f16x8_t*>(src + 8 * c);
+        u = p.uz[((long)bh * F + fa) * D + tid];
+      }
+    };
+    auto zstep = [&](int fa) {  // gr, un hold frame fa
       float nz = 0.f;
       if (tid < D) {
-        const f16* g = p.Gz + mat0 + (long)f * D * D + (long)tid * D;
         float acc = 0.f;
-        for (int c = 0; c < D; ++c) acc += (float)g[c] * zs[c];
-        nz = decay[f] * (zs[tid] - acc) + p.uz[((long)bh * F + f) * D + tid];
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc += (float)gr[c][j] * zs[8 * c + j];
+        nz = decay[fa] * (zs[tid] - acc) + un;
       }
       __syncthreads();
-      if (tid < D) {
-        zs[tid] = nz;
-        p.zsum[((long)bh * F + f) * D + tid] = nz;  // forward part
-      }
+      if (tid < D) zs[tid] = nz;
       __syncthreads();
+    };
+    if (tid < D) zs[tid] = 0.f;
+    load_row(0, gr, un);
+    __syncthreads();
+    for (int f = 0; f < F; ++f) {
+      float u2 = 0.f;
+      load_row(f + 1, gn, u2);
+      zstep(f);
+      if (tid < D) p.zsum[((long)bh * F + f) * D + tid] = zs[tid];  // forward part
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) gr[c] = gn[c];
+      un = u2;
     }
     if (tid < D) zs[tid] = 0.f;
+    load_row(F - 1, gr, un);
     __syncthreads();
     for (int f = F - 1; f >= 0; --f) {
+      // frame f reads the state built from frames > f: absorb frame f + 1 first
       if (f < F - 1) {
-        float nz = 0.f;
-        if (tid < D) {
-          const f16* g = p.Gz + mat0 + (long)(f + 1) * D * D + (long)tid * D;
-          float acc = 0.f;
-          for (int c = 0; c < D; ++c) acc += (float)g[c] * zs[c];
-          nz = decay[f + 1] * (zs[tid] - acc) + p.uz[((long)bh * F + f + 1) * D + tid];
-        }
-        __syncthreads();
-        if (tid < D) zs[tid] = nz;
-        __syncthreads();
+        float u2 = 0.f;
+        load_row(f, gn, u2);
+        zstep(f + 1);
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) gr[c] = gn[c];
+        un = u2;
       }
       if (tid < D) p.zsum[((long)bh * F + f) * D + tid] += zs[tid];
     }
@@ -342,70 +405,112 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
 #pragma unroll
   for (int t = 0; t < kRT; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto row_of = [&](int t, int e) { return (D / 4) * wave + 16 * t + 4 * lq + e; };
-  // one step: s <- d (s - G s) + U, with G, U of frame fa
+  // operands of one frame: G rows (A operand) and U entries of this lane
+  f16x8 ga[kRT][D / 32], gb[kRT][D / 32];
+  f32x4 ua[kRT], ub[kRT];
+  auto load_frame = [&](int fa, f16x8 (*g)[D / 32], f32x4* u) {
+    if (fa < 0 || fa >= F) return;
+    const f16* G = p.G + mat0 + (long)fa * D * D;
+    const float* U = p.U + mat0 + (long)fa * D * D;
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) {
+      const int r = (D / 4) * wave + 16 * t + li;
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k) g[t][k] = *reinterpret_cast<const f16x8*>(G + (long)r * D + 32 * k + 8 * lq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[t][e] = U[(long)row_of(t, e) * D + col];
+    }
+  };
+  // one step: s <- d (s - G s) + U with the frame-fa operands in ga, ua
   auto step = [&](int fa) {
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[li][row_of(t, e)] = (f16)s[t][e];
     __syncthreads();
-    const f16* G = p.G + mat0 + (long)fa * D * D;
-    const float* U = p.U + mat0 + (long)fa * D * D;
     const float dcy = decay[fa];
     f32x4 gs[kRT];
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
       gs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = (D / 4) * wave + 16 * t + li;
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32)
-        gs[t] = mma16(*reinterpret_cast<const f16x8*>(G + (long)r * D + k0 + 8 * lq),
-                      lds8(&st[li][k0 + 8 * lq]), gs[t]);
+      for (int k = 0; k < D / 32; ++k) gs[t] = mma16(ga[t][k], lds8(&st[li][32 * k + 8 * lq]), gs[t]);
     }
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s[t][e] = dcy * (s[t][e] - gs[t][e]) + U[(long)row_of(t, e) * D + col];
+      for (int e = 0; e < 4; ++e) s[t][e] = dcy * (s[t][e] - gs[t][e]) + ua[t][e];
     __syncthreads();
   };
+  auto advance = [&]() {
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) {
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k) ga[t][k] = gb[t][k];
+      ua[t] = ub[t];
+    }
+  };
   // forward: S_f after absorbing frame f; kept in fp32 in the workspace
+  load_frame(0, ga, ua);
   for (int f = 0; f < F; ++f) {
+    load_frame(f + 1, gb, ub);
     step(f);
+    advance();
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) p.Sf[mat0 + (long)f * D * D + (long)row_of(t, e) * D + col] = s[t][e];
   }
-  // reverse: R_{F-1} = 0, R_f from frame f+1; write (S_f + R_f)^T as fp16
+  // reverse: R_{F-1} = 0, R_f from frame f+1; write (S_f + R_f)^T as fp16, four consecutive
+  // rows of one column per lane (8 bytes)
 #pragma unroll
   for (int t = 0; t < kRT; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int f = F - 1; f >= 0; --f) {
-    if (f < F - 1) step(f + 1);
+  // the forward state of frame f is loaded with the operands of the frame absorbed before it
+  f32x4 sfa[kRT], sfb[kRT];
+  auto load_sf = [&](int fa, f32x4* dst) {
+    if (fa < 0) return;
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = row_of(t, e);
-        const float tot = s[t][e] + p.Sf[mat0 + (long)f * D * D + (long)r * D + col];
-        p.SsumT[mat0 + (long)f * D * D + (long)col * D + r] = (f16)tot;
-      }
+      for (int e = 0; e < 4; ++e) dst[t][e] = p.Sf[mat0 + (long)fa * D * D + (long)row_of(t, e) * D + col];
+  };
+  load_frame(F - 1, ga, ua);
+  load_sf(F - 1, sfa);
+  for (int f = F - 1; f >= 0; --f) {
+    load_sf(f - 1, sfb);
+    if (f < F - 1) {
+      load_frame(f, gb, ub);
+      step(f + 1);
+      advance();
+    }
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) {
+      typedef f16 f16x4_t __attribute__((ext_vector_type(4)));
+      f16x4_t tot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tot[e] = (f16)(s[t][e] + sfa[t][e]);
+      *reinterpret_cast<f16x4_t*>(p.SsumT + mat0 + (long)f * D * D + (long)col * D + row_of(t, 0)) = tot;
+      sfa[t] = sfb[t];
+    }
   }
 }
 
 // ---- output -----------------------------------------------------------------------------
-// One workgroup per (b, h, 64-token block): num = Q_rot (S + R), den = Q_pos . (z + zR).
+// One workgroup per (b, h, group of `grp` consecutive 64-token blocks of one frame):
+// num = Q_rot (S + R), den = Q_pos . (z + zR).  The frame's (S + R)^T is loaded once per group.
+// num is formed transposed (the state rows as the A operand) so a lane's accumulator holds
+// four consecutive value columns of one token: 8-byte stores.
 template <int D>
-__global__ __launch_bounds__(256) void out_kernel(const BigdnParams p) {
+__global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) {
   __shared__ __attribute__((aligned(16))) f16 sT[D][D + 8];  // (S + R)^T, row = value column
   __shared__ __attribute__((aligned(16))) f16 qr[64][D + 8];  // Q_rot rows
   __shared__ float zsum[D];
-  __shared__ float den_part[64][4];
-  const int nblk = p.N / 64;
-  const int blk = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
+  __shared__ float den_part[64];
+  const int nblk = p.N / 64, ngrp = nblk / grp;
+  const int g = blockIdx.x % ngrp;
+  const int bh = blockIdx.x / ngrp;
   const int b = bh / p.H, h = bh % p.H;
-  const int n0 = blk * 64, f = n0 / p.S;
+  const int f = (g * grp * 64) / p.S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const int C = p.H * D;
@@ -415,47 +520,52 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p) {
     *reinterpret_cast<uint4*>(&sT[r][c0]) = *reinterpret_cast<const uint4*>(p.SsumT + mat + (long)r * D + c0);
   }
   if (tid < D) zsum[tid] = p.zsum[((long)bh * p.F + f) * D + tid];
-  __syncthreads();
-  // prep of q: token t = tid / (D/8) ... 64 tokens x D/8 octets, 256 threads
   const bf16* qkv = static_cast<const bf16*>(p.qkv);
-  for (int e = tid; e < 64 * (D / 8); e += 256) {
-    const int t = e / (D / 8), d0 = (e % (D / 8)) * 8;
-    const long n = n0 + t, bn = (long)b * p.N + n;
-    float x[8], w[8], cs[8], sn[8], pos[8], rot[8];
-    load8f(qkv + bn * 3L * C + (long)h * D + d0, x);
-    load8f(p.q_norm_w + h * D + d0, w);
-    load8f(p.rope_cos + n * D + d0, cs);
-    load8f(p.rope_sin + n * D + d0, sn);
-    prep8(x, p.q_inv_rms[bn], w, cs, sn, 1.f, pos, rot);
-    f16x8 v;
-    float dp = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[j] = (f16)rot[j];
-      dp += pos[j] * zsum[d0 + j];
-    }
-    *reinterpret_cast<f16x8*>(&qr[t][d0]) = v;
-    // den partial: reduce over the D/8 octets of token t (consecutive e)
-#pragma unroll
-    for (int off = 1; off < D / 8; off <<= 1) dp += __shfl_xor(dp, off, 64);
-    if ((e % (D / 8)) == 0) den_part[t][0] = dp;
-  }
-  __syncthreads();
-  // num: wave w -> tokens 16w..16w+15, all D columns
   bf16* num = static_cast<bf16*>(p.num);
+  for (int blk = g * grp; blk < (g + 1) * grp; ++blk) {
+    const int n0 = blk * 64;
+    __syncthreads();
+    // prep of q: 64 tokens x D/8 octets over 256 threads
+    for (int e = tid; e < 64 * (D / 8); e += 256) {
+      const int t = e / (D / 8), d0 = (e % (D / 8)) * 8;
+      const long n = n0 + t, bn = (long)b * p.N + n;
+      float x[8], w[8], cs[8], sn[8], pos[8], rot[8];
+      load8f(qkv + bn * 3L * C + (long)h * D + d0, x);
+      load8f(p.q_norm_w + h * D + d0, w);
+      load8f(p.rope_cos + n * D + d0, cs);
+      load8f(p.rope_sin + n * D + d0, sn);
+      prep8(x, p.q_inv_rms[bn], w, cs, sn, 1.f, pos, rot);
+      f16x8 v;
+      float dp = 0.f;
 #pragma unroll
-  for (int ct = 0; ct < D / 16; ++ct) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 8; ++j) {
+        v[j] = (f16)rot[j];
+        dp += pos[j] * zsum[d0 + j];
+      }
+      *reinterpret_cast<f16x8*>(&qr[t][d0]) = v;
+      // den partial: reduce over the D/8 octets of token t (consecutive e)
 #pragma unroll
-    for (int k0 = 0; k0 < D; k0 += 32)
-      acc = mma16(lds8(&qr[16 * wave + li][k0 + 8 * lq]), lds8(&sT[16 * ct + li][k0 + 8 * lq]), acc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const long n = n0 + 16 * wave + 4 * lq + e;
-      num[(((long)b * p.N + n) * p.H + h) * D + 16 * ct + li] = (bf16)acc[e];
+      for (int off = 1; off < D / 8; off <<= 1) dp += __shfl_xor(dp, off, 64);
+      if ((e % (D / 8)) == 0) den_part[t] = dp;
     }
+    __syncthreads();
+    // num^T: wave w -> tokens 16w..16w+15 (column li of the accumulator), all D value columns
+    const long n = n0 + 16 * wave + li;
+    bf16* orow = num + (((long)b * p.N + n) * p.H + h) * D;
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32)
+        acc = mma16(lds8(&sT[16 * ct + li][k0 + 8 * lq]), lds8(&qr[16 * wave + li][k0 + 8 * lq]), acc);
+      typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (bf16)acc[e];
+      *reinterpret_cast<bf16x4_t*>(orow + 16 * ct + 4 * lq) = o4;
+    }
+    if (tid < 64) static_cast<bf16*>(p.den)[(long)bh * p.N + n0 + tid] = (bf16)den_part[tid];
   }
-  if (tid < 64) static_cast<bf16*>(p.den)[(long)bh * p.N + n0 + tid] = (bf16)den_part[tid][0];
 }
 
 }  // namespace
@@ -483,14 +593,16 @@ hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream) {
   hipError_t e = launch_prep(pp, stream);
   if (e != hipSuccess) return e;
   const int nbhf = p.B * p.H * p.F;
+  // 64-token blocks per output workgroup (a divisor of the blocks of a frame)
+  const int grp = 1;
   if (p.D == 128) {
     hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
     hipLaunchKernelGGL(scan_kernel<128>, dim3(p.B * p.H * (128 / 16 + 1)), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(out_kernel<128>, dim3(p.B * p.H * (p.N / 64)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(out_kernel<128>, dim3(p.B * p.H * (p.N / 64 / grp)), dim3(256), 0, stream, p, grp);
   } else {
     hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
     hipLaunchKernelGGL(scan_kernel<64>, dim3(p.B * p.H * (64 / 16 + 1)), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(out_kernel<64>, dim3(p.B * p.H * (p.N / 64)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(out_kernel<64>, dim3(p.B * p.H * (p.N / 64 / grp)), dim3(256), 0, stream, p, grp);
   }
   return hipGetLastError();
 }
