@@ -161,11 +161,31 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   const int trj = (lane >> 2) & 3, trc = lane & 3;
 
   // Workgroup -> (chain, value block); the value blocks of a chain stay on one XCD.
-  const int nwg = gridDim.x;
-  int logical = blockIdx.x;
-  if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  const int chain = logical / p.nvb;
-  const int v0 = (logical % p.nvb) * kBV;
+  // Consecutive workgroup ids go round-robin to the 8 XCDs, and each XCD starts its
+  // workgroups in id order.  Dense batches: XCD x takes a contiguous range of chains.  Packed
+  // batches: chains start longest first (sequences ranked by length, heads of one sequence
+  // consecutive) and are dealt to the XCDs in turn, so that the long chains start at once and
+  // the short ones fill in behind them.
+  const int nwg = gridDim.x, bid = blockIdx.x, nch = nwg / p.nvb;
+  int chain, vb;
+  if (VARLEN && p.order) {
+    int j;
+    if ((nch & 7) == 0) {
+      const int sl = bid >> 3;
+      j = 8 * (sl / p.nvb) + (bid & 7);
+      vb = sl % p.nvb;
+    } else {
+      j = bid / p.nvb;
+      vb = bid % p.nvb;
+    }
+    chain = p.order[j / p.H] * p.H + j % p.H;
+  } else {
+    int logical = bid;
+    if ((nwg & 7) == 0) logical = (bid & 7) * (nwg >> 3) + (bid >> 3);
+    chain = logical / p.nvb;
+    vb = logical % p.nvb;
+  }
+  const int v0 = vb * kBV;
   const int h = chain % p.H, bs = chain / p.H;
   long tok0;
   int len;
@@ -728,10 +748,40 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   }
 }
 
+// Packed batches: order[r] = the sequence of rank r by chunk count, longest first, ties by
+// index (rank of i = number of longer sequences + number of equally long ones before it).
+// One workgroup; up to kMaxRank sequences, beyond that the identity order.
+constexpr int kMaxRank = 4096;
+__global__ __launch_bounds__(1024) void rank_kernel(const int* cu, int N, int* order) {
+  __shared__ int nc[kMaxRank];
+  if (N > kMaxRank) {
+    for (int i = threadIdx.x; i < N; i += 1024) order[i] = i;
+    return;
+  }
+  for (int i = threadIdx.x; i < N; i += 1024) nc[i] = (cu[i + 1] - cu[i] + kC - 1) / kC;
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += 1024) {
+    const int ci = nc[i];
+    int r = 0;
+    for (int j = 0; j < N; ++j) {
+      const int cj = nc[j];
+      r += (cj > ci) || (cj == ci && j < i);
+    }
+    order[r] = i;
+  }
+}
+
 template <int K, bool VL>
 hipError_t launch_k(const FwdParams& p0, int nchains, hipStream_t stream) {
   FwdParams p = p0;
   p.nvb = p.V / kBV;
+  p.order = nullptr;
+  if (VL) {
+    // the order table sits at the start of the workspace (unused by this path otherwise)
+    int* order = static_cast<int*>(p.ws);
+    hipLaunchKernelGGL(rank_kernel, dim3(1), dim3(1024), 0, stream, p.cu, p.nseq, order);
+    p.order = order;
+  }
   hipLaunchKernelGGL((fused16_kernel<K, VL>), dim3(nchains * p.nvb), dim3(kThr), 0, stream, p);
   return hipGetLastError();
 }

@@ -25,6 +25,7 @@ struct FwdParams {
   int nt_total;       // packed batches: total chunks (h_chunks indexing)
   void* ws;           // workspace: per-chunk slots, then (packed batches) chunk offsets
   int* coffs;         // packed batches: chunk offsets table inside the workspace
+  const int* order;   // packed batches, single-kernel path: sequences, longest first
 };
 
 // Workspace of a forward call with `nslots` chunk slots (B*H*NT dense, H*NT_total packed)

@@ -38,6 +38,11 @@ def _run(inp, h0=None, want_h=True, label=""):
 @pytest.mark.parametrize("want_h", [True, False])
 @pytest.mark.parametrize("lengths,K,dtype", [([1, 64, 65, 200, 7], 128, "bf16"),
                                              ([130, 3, 64], 64, "bf16"),
+                                             # 24 sequences x 3 heads: longest-first order dealt
+                                             # round-robin to the XCDs (72 chains)
+                                             ([37, 300, 5, 64, 129, 1, 250, 77, 64, 190, 12, 3,
+                                               280, 65, 99, 140, 2, 31, 222, 128, 45, 160, 9, 300],
+                                              128, "bf16"),
                                              ([100, 28, 129], 64, "f32")])
 def test_packed_small(lengths, K, dtype, want_h):
     """Packed sequences with h0; with and without saved h / v_new (bf16 without saves runs
