@@ -43,10 +43,10 @@
 // split into a bf16 high part and a bf16 remainder (two products).
 //
 // LDS tiles: column-split [64][W] layout (32-column sub-tiles of 64-byte rows) whose 16-byte
-// octets are XOR-permuted by ((r >> 2) ^ (r >> 3)) & 3.  Both row orders the kernel reads 16
-// rows at a time in -- 16 consecutive rows (Gram tiles) and the pair rows 32G + 8i + 4t + j
-// (scan products) -- then hit 16 distinct 16-byte bank groups, and the transposed 8-byte reads
-// (four consecutive rows x four octets) 16 distinct 8-byte slots.
+// octets are XOR-permuted by swz64(r) (gdn_tiles.h): the reads of one octet from 16 rows in
+// both row orders the kernel uses -- 16 consecutive rows (Gram tiles) and the pair rows
+// 32G + 8i + 4t + j (scan products) -- and the transposed reads of the v tile are then free of
+// LDS bank conflicts on gfx950.
 #include "gdn_chunk.h"
 #include "gdn_dma.h"
 
@@ -64,11 +64,11 @@ constexpr int kThr = 512;  // 8 waves
 
 // element index of (r, c) in a [64][W] tile (W a multiple of 32)
 __device__ __forceinline__ int tix(int r, int c) {
-  return (c >> 5) * (kC * 32) + r * 32 + ((((c >> 3) & 3) ^ (((r >> 2) ^ (r >> 3)) & 3)) << 3) + (c & 7);
+  return (c >> 5) * (kC * 32) + r * 32 + ((((c >> 3) & 3) ^ swz64(r)) << 3) + (c & 7);
 }
 // logical octet a lane must fetch so that a linear 16-byte-per-lane LDS write lands it at
 // physical octet (lane & 3) of row r
-__device__ __forceinline__ int src_octet(int r, int lane) { return (lane & 3) ^ (((r >> 2) ^ (r >> 3)) & 3); }
+__device__ __forceinline__ int src_octet(int r, int lane) { return (lane & 3) ^ swz64(r); }
 
 // Gate slot of one chunk (floats): e^gamma [0, 64), e^{gl - gamma} [64, 128), beta [128, 192),
 // e^gl at 192; factors beta e^{gamma - gamma_31} [256, 320), e^{gamma - gamma_31} [320, 384),

@@ -10,7 +10,7 @@
 //
 // q and k arrive by direct global-to-LDS transfers (one batch, one wait); rows past the end
 // of the sequence read as zero through the buffer bounds.  Their LDS layout XOR-permutes the
-// 16-byte octets of a row by (row >> 2) & 3, which makes the 16-byte operand reads of 16
+// 16-byte octets of a row by swz64(row) (gdn_tiles.h), which makes the 16-byte operand reads of 16
 // consecutive rows (one octet each) hit 16 distinct bank groups.
 #include "gdn_chunk.h"
 #include "gdn_dma.h"
@@ -24,9 +24,9 @@ using namespace dma;
 constexpr int kThreads = 256;
 
 // element index of (row r, column c) in a [64][K] q / k tile (32-column sub-tiles of 64-byte
-// rows, octet o of row r stored at o ^ ((r >> 2) & 3))
+// rows, octet o of row r stored at o ^ swz64(r))
 __device__ __forceinline__ int pix(int r, int c) {
-  return (c >> 5) * (kC * 32) + r * 32 + ((((c >> 3) & 3) ^ ((r >> 2) & 3)) << 3) + (c & 7);
+  return (c >> 5) * (kC * 32) + r * 32 + ((((c >> 3) & 3) ^ swz64(r)) << 3) + (c & 7);
 }
 
 template <int K, bool PK>
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void prep16_kernel(const FwdParams p) {
 #pragma unroll
     for (int i = 0; i < kQB / 4; ++i) {
       const int b = wave + 4 * i;
-      const int r = 16 * (b & 3) + (lane >> 2), lo = (lane & 3) ^ ((r >> 2) & 3);
+      const int r = 16 * (b & 3) + (lane >> 2), lo = (lane & 3) ^ swz64(r);
       const uint32_t voff = r * qk_row + (4 * (b >> 2) + lo) * 16;
       dma16(rq, voff, 0, lds_addr(s.q) + 1024u * b);
       dma16(rk, voff, 0, lds_addr(s.k) + 1024u * b);

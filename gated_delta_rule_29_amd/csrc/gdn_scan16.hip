@@ -167,11 +167,11 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
     const char* wsg = static_cast<const char*>(p.ws);
     // Per-lane source offsets of the input tiles.  LDS block b (1 KiB) of a column-split tile
     // holds sub-tile b / 4, rows 16 (b % 4) .. +15; lane L writes its octet L % 4 of row
-    // 16 (b % 4) + L / 4, which holds the row's logical octet (L % 4) ^ ((row >> 3) & 3).
+    // 16 (b % 4) + L / 4, which holds the row's logical octet (L % 4) ^ swz64(row).
     uint32_t voff_q[PK ? 1 : 4 * kG], voff_v[kVB];
 #pragma unroll
     for (int b = 0; b < 4 * kG; ++b) {
-      const int r = 16 * (b & 3) + (lane >> 2), lo = (lane & 3) ^ ((r >> 3) & 3);
+      const int r = 16 * (b & 3) + (lane >> 2), lo = (lane & 3) ^ swz64(r);
       if constexpr (!PK) voff_q[b] = r * qk_row + (4 * (b >> 2) + lo) * 16;
       if (b < kVB) voff_v[b] = r * v_row + (4 * (b >> 2) + lo) * 16;
     }

@@ -34,16 +34,20 @@ __device__ __forceinline__ int tix_seq64(int r, int c) {
   return r * 64 + (((c >> 3) ^ swz_seq(r)) << 3) + (c & 7);
 }
 
+// Octet permutation of row r in the column-split tiles below.  Measured on gfx950 with the
+// LDS bank-conflict counter (a 16-byte read serves 16 lanes per cycle, an 8-byte read 32):
+// 16-byte reads of one octet from 16 consecutive rows, or from the pair rows
+// 32G + 8(i/4) + 4t + i%4, run conflict-free with this permutation.  Transposed 8-byte reads
+// of eight rows x four octets at one 8-byte half take two cycles per pass under any octet
+// permutation (their 32 lanes cover half of the bank slots).
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 // Column-split tile: [R rows][W columns] kept as W/32 sub-tiles of [R][32] (64-byte rows),
 // sub-tile s at element s*R*32; octet o (0..3) of row r inside a sub-tile is stored at
-// o ^ ((r >> 3) & 3).  A sub-tile offset is then a constant (an instruction immediate), and
-//  * 16-byte reads of one octet from the pair rows of 16 lanes hit 16 distinct 16-byte bank
-//    groups ((r & 3) and (r >> 3) & 3 both vary over the 16 rows);
-//  * transpose reads of four consecutive rows x four octets (one 16-lane group) touch 16
-//    distinct 8-byte bank slots.
+// o ^ swz64(r).  A sub-tile offset is then a constant (an instruction immediate).
 template <int R>
 __device__ __forceinline__ int tix_s32(int r, int c) {
-  return (c >> 5) * (R * 32) + r * 32 + ((((c >> 3) & 3) ^ ((r >> 3) & 3)) << 3) + (c & 7);
+  return (c >> 5) * (R * 32) + r * 32 + ((((c >> 3) & 3) ^ swz64(r)) << 3) + (c & 7);
 }
 
 // Column-split [64][W] tile (W a multiple of 32) whose octets are permuted by
