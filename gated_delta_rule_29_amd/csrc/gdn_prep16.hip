@@ -232,9 +232,241 @@ __global__ __launch_bounds__(kThreads) void prep16_kernel(const FwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Per-key gate.  The scaled operands are formed in registers from global loads: thread
+// (octet o, part) holds keys 8o .. 8o+7 for kTP consecutive tokens, so the per-key cumulative
+// decay is a running sum over its tokens plus a prefix over the parts (lanes of one wave),
+// and every scaled operand leaves as 16-byte pieces: to LDS for the Gram and Q K^T products
+// and straight to the slot for the scan.  The operand tiles share LDS with the solve's work
+// arrays, which keeps the kernel at 2 workgroups per CU.
+// ---------------------------------------------------------------------------------------
+template <int K>
+struct __attribute__((aligned(16))) PrepPkSmem {
+  typedef f16 TO;
+  static constexpr int kTP = kC + 8;
+  union {
+    struct {
+      u16 q[kC * K];   // fp16 Q e^{gamma - gamma_mid}        (pix layout)
+      u16 k[kC * K];   // fp16 K e^{gamma - gamma_mid}        (pix layout)
+      u16 kb[kC * K];  // fp16 K e^{gamma_mid - gamma}: Gram columns (pix layout)
+    };
+    struct {           // solve work arrays, used once the products are done
+      float x[32][36];
+      TO tm[kC][kTP];
+    };
+  };
+  float a[kC][kC + 4];
+  TO p[kC][kTP];
+  float beta[kC];
+};
+
+template <int K, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p) {
+  typedef PrepPkSmem<K> SM;
+  typedef Slot16<K, true> SL;
+  constexpr int kG = K / 32;
+  constexpr int kOct = K / 8;              // 16-byte octets per row
+  constexpr int kParts = kThreads / kOct;  // token parts (lanes of one wave per octet)
+  constexpr int kTP = kC / kParts;         // tokens per thread
+  static_assert(kParts <= 64 && kC % kParts == 0 && (kC / 2) % kTP == 0, "thread layout");
+  __shared__ SM s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+
+  // chunk -> (chain, n)
+  int chain, n;
+  if (VARLEN) {
+    const int hh = blockIdx.x / p.nt_total, cg = blockIdx.x % p.nt_total;
+    int lo = 0, hi = p.nseq;  // largest i with coffs[i] <= cg
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.coffs[mid] <= cg) lo = mid;
+      else hi = mid;
+    }
+    chain = lo * p.H + hh;
+    n = cg - p.coffs[lo];
+  } else {
+    const int nt = (p.T + kC - 1) / kC;
+    chain = blockIdx.x / nt;
+    n = blockIdx.x % nt;
+  }
+  const ChunkPos cp = chain_pos(p, chain, VARLEN);
+  const int h = chain % p.H;
+  const int t0 = n * kC;
+  const uint32_t rows = (uint32_t)min(kC, cp.len - t0);
+  const long tok = cp.tok0 + t0;
+  char* slot = static_cast<char*>(p.ws) + (cp.slot0 + n) * (long)SL::kBytes;
+  float* vec = reinterpret_cast<float*>(slot + SL::kVec);
+
+  // ---- loads: q, k (bf16) and gk (fp32) of this thread's keys and tokens, g and beta per
+  // token; rows past the end of the sequence read as zero through the buffer bounds
+  const int o = tid / kParts, part = tid % kParts;
+  const uint32_t qk_row = (uint32_t)p.H * K * 2, gk_row = (uint32_t)p.H * K * 4;
+  const __amdgpu_buffer_rsrc_t rq = store_rsrc(const_cast<bf16*>(static_cast<const bf16*>(p.q)) + (tok * p.H + h) * K, rows * qk_row);
+  const __amdgpu_buffer_rsrc_t rk = store_rsrc(const_cast<bf16*>(static_cast<const bf16*>(p.k)) + (tok * p.H + h) * K, rows * qk_row);
+  const __amdgpu_buffer_rsrc_t rg = store_rsrc(const_cast<float*>(p.gk) + (tok * p.H + h) * (long)K, rows * gk_row);
+  u32x4 qv[kTP], kv[kTP];
+  f32x4 gk0[kTP], gk1[kTP];
+  float gt[kTP];
+#pragma unroll
+  for (int i = 0; i < kTP; ++i) {
+    const int t = part * kTP + i;
+    qv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, t * qk_row + 16 * o, 0, 0));
+    kv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, t * qk_row + 16 * o, 0, 0));
+    gk0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * gk_row + 32 * o, 0, 0));
+    gk1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * gk_row + 32 * o + 16, 0, 0));
+    gt[i] = (p.g && (uint32_t)t < rows) ? p.g[(tok + t) * p.H + h] : 0.f;
+  }
+  if (tid < kC) s.beta[tid] = (uint32_t)tid < rows ? p.beta[(tok + tid) * p.H + h] : 0.f;
+
+  // ---- per-key cumulative decay gamma[t][8o + j]: running sum over this thread's tokens,
+  // then the exclusive prefix over the parts before it (Hillis-Steele over the part lanes)
+  float gam[kTP][8], tot[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < kTP; ++i) {
+      run += gt[i] + (j < 4 ? gk0[i][j] : gk1[i][j - 4]);
+      gam[i][j] = run;
+    }
+    tot[j] = run;
+  }
+  float incl[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) incl[j] = tot[j];
+#pragma unroll
+  for (int sh = 1; sh < kParts; sh <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = __shfl_up(incl[j], sh, kParts);
+      incl[j] += part >= sh ? u : 0.f;
+    }
+  }
+  float gm[8], gl[8];
+  const int row0 = lane & ~(kParts - 1);  // lane of part 0 of this octet
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float ex = incl[j] - tot[j];
+#pragma unroll
+    for (int i = 0; i < kTP; ++i) gam[i][j] += ex;
+    gm[j] = __shfl(incl[j], row0 + (kC / 2) / kTP - 1, 64);  // gamma at token 31
+    gl[j] = __shfl(incl[j], row0 + kParts - 1, 64);          // gamma at token 63
+  }
+  if (part == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      vec[SL::kEmid + 8 * o + j] = __expf(gm[j]);
+      vec[SL::kEglk + 8 * o + j] = __expf(gl[j]);
+    }
+  }
+
+  // ---- scaled operands: Q, K times e^{gamma - gamma_mid} (LDS and slot), K times
+  // e^{gamma_mid - gamma} (LDS: Gram columns), K times e^{gamma_last - gamma} (slot)
+  float lm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lm[j] = __expf(gl[j] - gm[j]);
+#pragma unroll
+  for (int i = 0; i < kTP; ++i) {
+    const int t = part * kTP + i;
+    f32x4 up0, up1, dn0, dn1, kf0, kf1, qf0, qf1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      up0[j] = __expf(gam[i][j] - gm[j]);
+      up1[j] = __expf(gam[i][4 + j] - gm[4 + j]);
+      dn0[j] = __expf(gm[j] - gam[i][j]);
+      dn1[j] = __expf(gm[4 + j] - gam[i][4 + j]);
+      const unsigned kw0 = kv[i][j >> 1], kw1 = kv[i][2 + (j >> 1)];
+      const unsigned qw0 = qv[i][j >> 1], qw1 = qv[i][2 + (j >> 1)];
+      kf0[j] = (j & 1) ? __uint_as_float(kw0 & 0xffff0000u) : __uint_as_float(kw0 << 16);
+      kf1[j] = (j & 1) ? __uint_as_float(kw1 & 0xffff0000u) : __uint_as_float(kw1 << 16);
+      qf0[j] = (j & 1) ? __uint_as_float(qw0 & 0xffff0000u) : __uint_as_float(qw0 << 16);
+      qf1[j] = (j & 1) ? __uint_as_float(qw1 & 0xffff0000u) : __uint_as_float(qw1 << 16);
+    }
+    f32x4 lh0, lh1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lh0[j] = lm[j] * dn0[j];
+      lh1[j] = lm[4 + j] * dn1[j];
+    }
+    const u32x4 qu = __builtin_bit_cast(u32x4, pack8<f16>(qf0 * up0, qf1 * up1));
+    const u32x4 ku = __builtin_bit_cast(u32x4, pack8<f16>(kf0 * up0, kf1 * up1));
+    const u32x4 kb = __builtin_bit_cast(u32x4, pack8<f16>(kf0 * dn0, kf1 * dn1));
+    const u32x4 kh = __builtin_bit_cast(u32x4, pack8<f16>(kf0 * lh0, kf1 * lh1));
+    const int ix = pix(t, 8 * o);
+    *reinterpret_cast<u32x4*>(&s.q[ix]) = qu;
+    *reinterpret_cast<u32x4*>(&s.k[ix]) = ku;
+    *reinterpret_cast<u32x4*>(&s.kb[ix]) = kb;
+    const int sx = 2 * tix_s32<kC>(t, 8 * o);
+    *reinterpret_cast<u32x4*>(slot + SL::kQ + sx) = qu;
+    *reinterpret_cast<u32x4*>(slot + SL::kK + sx) = ku;
+    *reinterpret_cast<u32x4*>(slot + SL::kKh + sx) = kh;
+  }
+  // strict upper 16x16 tiles of A and P stay zero
+  for (int e = tid; e < 6 * 256; e += kThreads) {
+    const int t = e >> 8, r = (e >> 4) & 15, c = e & 15;
+    const int I = (t >= 3) + (t >= 5);
+    const int J = (t < 3) ? t + 1 : (t < 5 ? t - 1 : 3);
+    s.a[16 * I + r][16 * J + c] = 0.f;
+    s.p[16 * I + r][16 * J + c] = (f16)0.f;
+  }
+  __syncthreads();
+  if (tid < kC) vec[SL::kBeta + tid] = s.beta[tid];
+
+  // ---- Gram (-> A, rows scaled by beta) and Q K^T (-> P), lower 16x16 tiles: 20 jobs,
+  // 5 per wave
+  const f16* qt = reinterpret_cast<const f16*>(s.q);
+  const f16* kt = reinterpret_cast<const f16*>(s.k);
+  const f16* kbt = reinterpret_cast<const f16*>(s.kb);
+#pragma unroll
+  for (int ji = 0; ji < 5; ++ji) {
+    const int job = wave + 4 * ji;
+    const bool is_qk = job >= 10;
+    int I, J;
+    tri_tile(is_qk ? job - 10 : job, I, J);
+    const f16* at = is_qk ? qt : kt;
+    f16x8 av[kG], bv[kG];
+#pragma unroll
+    for (int kk = 0; kk < kG; ++kk) {
+      av[kk] = lds8(at + pix(16 * I + li, 32 * kk + 8 * lq));
+      bv[kk] = lds8(kbt + pix(16 * J + li, 32 * kk + 8 * lq));
+    }
+    const int sc = 16 * J + li;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kG; ++kk) acc = mma16(av[kk], bv[kk], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + 4 * lq + e;
+      if (is_qk) s.p[r][sc] = (f16)(sc <= r ? acc[e] : 0.f);
+      else s.a[r][sc] = sc < r ? s.beta[r] * acc[e] : 0.f;
+    }
+  }
+  __syncthreads();  // the operand tiles are dead from here: x and tm reuse their space
+  // strict upper 16x16 tiles of Tm stay zero
+  for (int e = tid; e < 6 * 256; e += kThreads) {
+    const int t = e >> 8, r = (e >> 4) & 15, c = e & 15;
+    const int I = (t >= 3) + (t >= 5);
+    const int J = (t < 3) ? t + 1 : (t < 5 ? t - 1 : 3);
+    s.tm[16 * I + r][16 * J + c] = (f16)0.f;
+  }
+  solve_unit_lower(s, wave, lane);
+
+  // Tm, P -> slot, 16-byte pieces in the scan's column-split layout
+  for (int c = tid; c < 2 * kC * kC / 8; c += kThreads) {
+    const int which = c / (kC * kC / 8), cc = c % (kC * kC / 8);
+    const int r = cc / (kC / 8), c0 = (cc % (kC / 8)) * 8;
+    const f16* src = which ? &s.p[r][c0] : &s.tm[r][c0];
+    *reinterpret_cast<u32x4*>(slot + (which ? SL::kP : SL::kTm) + 2 * tix_s32<kC>(r, c0)) =
+        *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
 template <int K, bool VL, bool PK>
 hipError_t launch_k(const FwdParams& p, long nslots, hipStream_t stream) {
-  hipLaunchKernelGGL((prep16_kernel<K, VL, PK>), dim3(nslots), dim3(kThreads), 0, stream, p);
+  if constexpr (PK) hipLaunchKernelGGL((prep16pk_kernel<K, VL>), dim3(nslots), dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((prep16_kernel<K, VL, PK>), dim3(nslots), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

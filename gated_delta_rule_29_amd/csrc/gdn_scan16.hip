@@ -94,6 +94,15 @@ struct __attribute__((aligned(16))) S16Smem {
   u16 stg[kNW][16 * kC];  // per-wave output staging, [16 columns][64 rows]
 };
 
+// The lane index, opaque to the optimiser: addresses derived from it inside the chunk loop are
+// recomputed each iteration (a few integer operations) instead of being hoisted out of the
+// loop and kept in registers.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // Keeps the compiler from moving LDS accesses across this point.  Within one wave the LDS
 // executes accesses in issue order, so this is all a wave's write -> read (or read -> write)
 // of its own staging tile needs; unlike a fence it leaves arithmetic free to move across.
@@ -238,190 +247,227 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
   bf16* vng = static_cast<bf16*>(p.v_new);
   bf16* hcg = static_cast<bf16*>(p.h_chunks);
 
+  static_assert(kNCT == 1, "one 16-column tile per compute wave");
   for (int n = 0; n < nchunks; ++n) {
     __syncthreads();  // chunk n is in buffer n & 1
+    const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+    const int trj = (lane >> 2) & 3, trc = lane & 3;
     const BUF& B = s.buf[n & 1];
     const long tok = cp.tok0 + (long)n * kC;
     const uint32_t rows = (uint32_t)(cp.len - n * kC);
+    const f16* kt = reinterpret_cast<const f16*>(B.k);
+    const TQ* qt = reinterpret_cast<const TQ*>(B.q);
+    const f16* tmt = reinterpret_cast<const f16*>(B.tm);
+    const f16* pt = reinterpret_cast<const f16*>(B.p);
+    const u16* kht = PK ? B.kh : B.k;
+    const int col = kWC * wave;  // this wave's first value column within the block
 
-    // state entering this chunk -> h_chunks
+    // The step is software-pipelined in stages: each stage issues the LDS reads of a later
+    // stage before its own products, and scheduling barriers keep the compiler from sinking
+    // those reads next to their uses, so LDS latency overlaps matrix and vector work.
+
+    // ---- stage 0: K rows (A operand of K h) in flight; the state entering the chunk ->
+    // h_chunks; the B operands of K h and Q h (per-key gate: rows scaled by e^{gamma_mid})
+    f16x8 kfr[2][2][kG];
+#pragma unroll
+    for (int G = 0; G < kG; ++G)
+#pragma unroll
+      for (int P = 0; P < 2; ++P)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) kfr[P][t][G] = lds8(kt + tix(pair_row(P, t, li), 32 * G + 8 * lq));
     if (hcg) {
       const __amdgpu_buffer_rsrc_t rh =
           store_rsrc(hcg + (cp.slot0 + n) * (long)K * p.V + v0, (uint32_t)(K * p.V - v0) * 2u);
 #pragma unroll
-      for (int c = 0; c < kNCT; ++c)
-#pragma unroll
-        for (int half = 0; half < K / 64; ++half)
-          store_rows(s.stg[wave], [&](int G, int t, int e) { return hs[c][2 * half + G][t][e]; }, rh,
-                     (uint32_t)p.V * 2u, (uint32_t)(64 * half * p.V + kWC * wave + 16 * c) * 2u, lane);
+      for (int half = 0; half < K / 64; ++half)
+        store_rows(s.stg[wave], [&](int G, int t, int e) { return hs[0][2 * half + G][t][e]; }, rh,
+                   (uint32_t)p.V * 2u, (uint32_t)(64 * half * p.V + col) * 2u, lane);
     }
-
-    // B operands of K h and Q h: the state (per-key gate: rows scaled by e^{gamma_mid})
-    f16x8 bk[kNCT][kG];
-    Q8 bq[kNCT][kG];
+    f16x8 bk[kG];
+    Q8 bq[kG];
 #pragma unroll
     for (int G = 0; G < kG; ++G) {
-      f32x4 m0 = {1.f, 1.f, 1.f, 1.f}, m1 = m0;
       if constexpr (PK) {
-        m0 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq]);
-        m1 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq + 4]);
-      }
-#pragma unroll
-      for (int c = 0; c < kNCT; ++c) {
-        if constexpr (PK) {
-          bk[c][G] = pack8<f16>(hs[c][G][0] * m0, hs[c][G][1] * m1);
-          bq[c][G] = bk[c][G];
-        } else {
-          bk[c][G] = pack8<f16>(hs[c][G][0], hs[c][G][1]);
-          bq[c][G] = pack8<TQ>(hs[c][G][0], hs[c][G][1]);
-        }
+        const f32x4 m0 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq]);
+        const f32x4 m1 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEmid + 32 * G + 8 * lq + 4]);
+        bk[G] = pack8<f16>(hs[0][G][0] * m0, hs[0][G][1] * m1);
+        bq[G] = bk[G];
+      } else {
+        bk[G] = pack8<f16>(hs[0][G][0], hs[0][G][1]);
+        bq[G] = pack8<TQ>(hs[0][G][0], hs[0][G][1]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // X_K = K h (tokens 32P + 8lq + 4t + e of each column)
-    const f16* kt = reinterpret_cast<const f16*>(B.k);
-    f32x4 xk[kNCT][2][2];
+    // ---- stage 1: X_K = K h (tokens 32P + 8lq + 4t + e of this lane's column), a contraction
+    // round at a time; under it, reads of the Q rows, V, the Y gates and the Tm rows
+    Q8 qfr[2][2][kG];
+    u32x2 vv[2][2];
+    f32x4 be[2][2], eg[2][2];
+    f16x8 tmf[2][2][2];
+    f32x4 xk[2][2];
 #pragma unroll
     for (int P = 0; P < 2; ++P)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = pair_row(P, t, li);
-        f32x4 ak[kNCT];
+      for (int t = 0; t < 2; ++t) xk[P][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < kNCT; ++c) ak[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int G = 0; G < kG; ++G) {
 #pragma unroll
-        for (int G = 0; G < kG; ++G) {
-          const f16x8 a = lds8(kt + tix(r, 32 * G + 8 * lq));
+      for (int P = 0; P < 2; ++P)
 #pragma unroll
-          for (int c = 0; c < kNCT; ++c) ak[c] = mma16(a, bk[c][G], ak[c]);
-        }
+        for (int t = 0; t < 2; ++t) xk[P][t] = mma16(kfr[P][t][G], bk[G], xk[P][t]);
+      if (G == 0) {
 #pragma unroll
-        for (int c = 0; c < kNCT; ++c) xk[c][P][t] = ak[c];
+        for (int Gk = 0; Gk < kG; ++Gk)
+#pragma unroll
+          for (int Gr = 0; Gr < 2; ++Gr)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) qfr[Gr][t][Gk] = lds8(qt + tix(pair_row(Gr, t, li), 32 * Gk + 8 * lq));
       }
-
-    // Y = diag(beta) (V - diag(e^gamma) X_K)
-    f16x8 by[kNCT][2];
+      if (G == kG - 1) {
 #pragma unroll
-    for (int P = 0; P < 2; ++P)
+        for (int P = 0; P < 2; ++P)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r0 = 32 * P + 8 * lq + 4 * t;
-        const f32x4 be = *reinterpret_cast<const f32x4*>(&B.vec[SL::kBeta + r0]);
-        f32x4 eg = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (!PK) eg = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEg + r0]);
+          for (int t = 0; t < 2; ++t) {
+            const int r0 = 32 * P + 8 * lq + 4 * t;
+            vv[P][t] = tr16(&B.v[tix(r0 + trj, col + 4 * trc)]);
+            be[P][t] = *reinterpret_cast<const f32x4*>(&B.vec[SL::kBeta + r0]);
+            eg[P][t] = PK ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&B.vec[SL::kEg + r0]);
+          }
 #pragma unroll
-        for (int c = 0; c < kNCT; ++c) {
-          const u32x2 vv = tr16(&B.v[tix(r0 + trj, kWC * wave + 16 * c + 4 * trc)]);
+        for (int P = 0; P < 2; ++P)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            by[c][P][4 * t + e] = (f16)(be[e] * (bf_at(vv, e) - eg[e] * xk[c][P][t][e]));
-        }
+          for (int Gr = P; Gr < 2; ++Gr)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) tmf[Gr][t][P] = lds8(tmt + tix(pair_row(Gr, t, li), 32 * P + 8 * lq));
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
+    // ---- stage 2: Y = diag(beta) (V - diag(e^gamma) X_K) (fp16 B operand of Tm Y); the Q h
+    // part of o (value columns 4lq..4lq+3 of token pair_row(G, t, li), the state as the A
+    // operand) fills the matrix pipe meanwhile; reads of the first token half of the update
+    // operand K^T (transpose reads)
+    f16x8 khf[kG][2][2];
+    auto read_kh = [&](int P) {
+#pragma unroll
+      for (int G = 0; G < kG; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int c0 = 32 * G + 8 * trc + 4 * t;
+          khf[G][t][P] = tr16_pair(&kht[tix(32 * P + 8 * lq + trj, c0)], &kht[tix(32 * P + 8 * lq + 4 + trj, c0)]);
+        }
+    };
+    f32x4 oacc[2][2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) oacc[G][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f16x8 by[2];
+#pragma unroll
+    for (int Gk = 0; Gk < kG; ++Gk) {
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) oacc[G][t] = mma16(bq[Gk], qfr[G][t][Gk], oacc[G][t]);
+      if (Gk == 0) {
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              by[P][4 * t + e] = (f16)(be[P][t][e] * (bf_at(vv[P][t], e) - eg[P][t][e] * xk[P][t][e]));
+      }
+      if (Gk == 1) read_kh(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- stage 3: reads of the second half of K^T, the P rows and the update / o gates;
     // v_new = Tm Y (Tm lower triangular: token group P feeds groups G >= P)
-    const f16* tmt = reinterpret_cast<const f16*>(B.tm);
-    f32x4 vn[kNCT][2][2];
+    read_kh(1);
+    f16x8 pfr[2][2][2];
+    float ego[2][2];
 #pragma unroll
     for (int G = 0; G < 2; ++G)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int r = pair_row(G, t, li);
-        f32x4 acc[kNCT];
 #pragma unroll
-        for (int c = 0; c < kNCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int P = 0; P <= G; ++P) {
-          const f16x8 a = lds8(tmt + tix(r, 32 * P + 8 * lq));
-#pragma unroll
-          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(a, by[c][P], acc[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < kNCT; ++c) vn[c][G][t] = acc[c];
+        for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds8(pt + tix(r, 32 * P + 8 * lq));
+        ego[G][t] = PK ? 1.f : B.vec[SL::kEg + r];
       }
-    // bv: v_new (for P v_new); bu: the update's B operand (scalar gate: v_new e^{gl-gamma})
-    f16x8 bv[kNCT][2], bu[kNCT][2];
+    f32x4 l0[2], l1[2], dec[kG][2];
 #pragma unroll
     for (int P = 0; P < 2; ++P) {
-      f32x4 l0 = {1.f, 1.f, 1.f, 1.f}, l1 = l0;
-      if constexpr (!PK) {
-        l0 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq]);
-        l1 = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq + 4]);
-      }
-#pragma unroll
-      for (int c = 0; c < kNCT; ++c) {
-        bv[c][P] = pack8<f16>(vn[c][P][0], vn[c][P][1]);
-        if constexpr (PK) bu[c][P] = bv[c][P];
-        else bu[c][P] = pack8<f16>(vn[c][P][0] * l0, vn[c][P][1] * l1);
-      }
+      l0[P] = PK ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq]);
+      l1[P] = PK ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&B.vec[SL::kEl + 32 * P + 8 * lq + 4]);
     }
-
-    // h <- e^gl h + K^T diag(e^{gl - gamma}) v_new   (A operand: K^T by transpose reads)
-    const u16* kht = PK ? B.kh : B.k;
-    const float egl = PK ? 1.f : B.vec[SL::kEgl];
 #pragma unroll
     for (int G = 0; G < kG; ++G)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        f32x4 dec = {egl, egl, egl, egl};
-        if constexpr (PK) dec = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEglk + 32 * G + 8 * lq + 4 * t]);
-        f32x4 acc[kNCT];
-#pragma unroll
-        for (int c = 0; c < kNCT; ++c) acc[c] = hs[c][G][t] * dec;
-#pragma unroll
-        for (int P = 0; P < 2; ++P) {
-          const int c0 = 32 * G + 8 * trc + 4 * t;
-          const f16x8 a = tr16_pair(&kht[tix(32 * P + 8 * lq + trj, c0)],
-                                    &kht[tix(32 * P + 8 * lq + 4 + trj, c0)]);
-#pragma unroll
-          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(a, bu[c][P], acc[c]);
+        if constexpr (PK) {
+          dec[G][t] = *reinterpret_cast<const f32x4*>(&B.vec[SL::kEglk + 32 * G + 8 * lq + 4 * t]);
+        } else {
+          const float egl = B.vec[SL::kEgl];
+          dec[G][t] = f32x4{egl, egl, egl, egl};
         }
-#pragma unroll
-        for (int c = 0; c < kNCT; ++c) hs[c][G][t] = acc[c];
       }
+    f32x4 vn[2][2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) vn[G][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+#pragma unroll
+      for (int G = P; G < 2; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) vn[G][t] = mma16(tmf[G][t][P], by[P], vn[G][t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // o^T = scale ((Q h)^T diag(e^gamma) + (P v_new)^T), computed with the state and v_new as
-    // the A operands (the operand layouts are symmetric) and Q, P read as B with the same
-    // addresses as the A reads above: the accumulator then holds value columns 4lq .. 4lq+3
-    // of a 16-column tile for token pair_row(G, t, li), i.e. 8 contiguous bytes of an output row.
-    const TQ* qt = reinterpret_cast<const TQ*>(B.q);
-    const f16* pt = reinterpret_cast<const f16*>(B.p);
+    // ---- stage 4: bv = v_new (fp16) for P v_new; bu = the update's B operand (scalar gate:
+    // v_new e^{gl-gamma}); h <- decay h + K^T diag(...) v_new, a token half at a time
+    f16x8 bv[2], bu[2];
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      bv[P] = pack8<f16>(vn[P][0], vn[P][1]);
+      if constexpr (PK) bu[P] = bv[P];
+      else bu[P] = pack8<f16>(vn[P][0] * l0[P], vn[P][1] * l1[P]);
+    }
+#pragma unroll
+    for (int G = 0; G < kG; ++G)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) hs[0][G][t] = hs[0][G][t] * dec[G][t];
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+#pragma unroll
+      for (int G = 0; G < kG; ++G)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) hs[0][G][t] = mma16(khf[G][t][P], bu[P], hs[0][G][t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- stage 5: o^T = scale ((Q h)^T diag(e^gamma) + (P v_new)^T), 8-byte row stores;
+    // v_new -> its output rows
     const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
 #pragma unroll
     for (int G = 0; G < 2; ++G)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int r = pair_row(G, t, li);
-        f32x4 acc[kNCT];
+        f32x4 acc = oacc[G][t] * ego[G][t];
 #pragma unroll
-        for (int c = 0; c < kNCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int Gk = 0; Gk < kG; ++Gk) {
-          const Q8 b = lds8(qt + tix(r, 32 * Gk + 8 * lq));
-#pragma unroll
-          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(bq[c][Gk], b, acc[c]);
-        }
-        const float eg = PK ? 1.f : B.vec[SL::kEg + r];
-#pragma unroll
-        for (int c = 0; c < kNCT; ++c) acc[c] = acc[c] * eg;
-#pragma unroll
-        for (int P = 0; P <= G; ++P) {
-          const f16x8 b = lds8(pt + tix(r, 32 * P + 8 * lq));
-#pragma unroll
-          for (int c = 0; c < kNCT; ++c) acc[c] = mma16(bv[c][P], b, acc[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < kNCT; ++c) {
-          const f32x4 ov = acc[c] * p.scale;
-          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(ov[0], ov[1], ov[2], ov[3]), ro,
-                                                r * v_row + (kWC * wave + 16 * c + 4 * lq) * 2, 0, 0);
-        }
+        for (int P = 0; P <= G; ++P) acc = mma16(bv[P], pfr[G][t][P], acc);
+        const f32x4 ov = acc * p.scale;
+        __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(ov[0], ov[1], ov[2], ov[3]), ro,
+                                              pair_row(G, t, li) * v_row + (col + 4 * lq) * 2, 0, 0);
       }
     if constexpr (VN) {
       const __amdgpu_buffer_rsrc_t rv = store_rsrc(vng + (tok * p.H + h) * p.V + v0, rows * v_row);
-#pragma unroll
-      for (int c = 0; c < kNCT; ++c)
-        store_rows(s.stg[wave], [&](int G, int t, int e) { return vn[c][G][t][e]; }, rv, v_row,
-                   (kWC * wave + 16u * c) * 2u, lane);
+      store_rows(s.stg[wave], [&](int G, int t, int e) { return vn[G][t][e]; }, rv, v_row,
+                 (uint32_t)col * 2u, lane);
     }
   }
 
