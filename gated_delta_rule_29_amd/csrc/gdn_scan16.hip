@@ -88,10 +88,13 @@ struct __attribute__((aligned(16))) S16Buf {
   float vec[Slot16<K, PK>::kVecBytes / 4];
 };
 
+constexpr int kSW = kC + 8;  // staging row length (elements): padded against bank conflicts
+
 template <int K, bool PK>
 struct __attribute__((aligned(16))) S16Smem {
   S16Buf<K, PK> buf[2];
-  u16 stg[kNW][16 * kC];  // per-wave output staging, [16 columns][64 rows]
+  u16 stg[kNW][16 * kSW];           // per-wave staging of v_new, [16 columns][64 rows]
+  u16 stgh[kNW][K / 64][16 * kSW];  // per-wave staging of the state, one tile per 64 keys
 };
 
 // The lane index, opaque to the optimiser: addresses derived from it inside the chunk loop are
@@ -109,24 +112,31 @@ __device__ __forceinline__ int opaque_lane() {
 __device__ __forceinline__ void lds_order() { asm volatile("" : : : "memory"); }
 
 // Per-wave output of a 64-row x 16-column fp32 block held in accumulator layout (rows
-// 32G + 8lq + 4t + e of column li in acc[G][t][e]) as bf16 rows: staging tile, transpose
-// reads, two 16-byte buffer stores per lane at rsrc offset row * row_bytes + col0 * 2.
+// 32G + 8lq + 4t + e of column li in acc[G][t][e]) as bf16 rows, in two halves that can sit
+// apart in the step: stage_rows writes the block to a staging tile [16 columns][kSW] (one
+// 16-byte write per lane and G: rows 32G + 8lq .. +7 of its column), flush_rows reads it back
+// transposed and stores two 16-byte row pieces per lane at rsrc offset
+// row * row_bytes + col0_bytes.  Within one wave the LDS performs accesses in issue order, so
+// the write -> read order needs no wait; lds_order keeps the compiler from reordering them.
 template <typename F>
-__device__ __forceinline__ void store_rows(u16* stg, F val, __amdgpu_buffer_rsrc_t r,
-                                           uint32_t row_bytes, uint32_t col0_bytes, int lane) {
+__device__ __forceinline__ void stage_rows(u16* stg, F val, int lane) {
+  const int li = lane & 15, lq = lane >> 4;
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    const u32x2 w0 = pack_bf16x4(val(G, 0, 0), val(G, 0, 1), val(G, 0, 2), val(G, 0, 3));
+    const u32x2 w1 = pack_bf16x4(val(G, 1, 0), val(G, 1, 1), val(G, 1, 2), val(G, 1, 3));
+    *reinterpret_cast<u32x4*>(&stg[li * kSW + 32 * G + 8 * lq]) = __builtin_shufflevector(w0, w1, 0, 1, 2, 3);
+  }
+  lds_order();
+}
+
+__device__ __forceinline__ void flush_rows(const u16* stg, __amdgpu_buffer_rsrc_t r, uint32_t row_bytes,
+                                           uint32_t col0_bytes, int lane) {
   const int li = lane & 15, lq = lane >> 4, trj = (lane >> 2) & 3, trc = lane & 3;
 #pragma unroll
-  for (int G = 0; G < 2; ++G)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x2 w = pack_bf16x4(val(G, t, 0), val(G, t, 1), val(G, t, 2), val(G, t, 3));
-      *reinterpret_cast<u32x2*>(&stg[li * kC + 32 * G + 8 * lq + 4 * t]) = w;
-    }
-  lds_order();
-#pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const u32x4 d = __builtin_shufflevector(tr16(&stg[(8 * s + trj) * kC + 16 * lq + 4 * trc]),
-                                            tr16(&stg[(8 * s + 4 + trj) * kC + 16 * lq + 4 * trc]),
+    const u32x4 d = __builtin_shufflevector(tr16(&stg[(8 * s + trj) * kSW + 16 * lq + 4 * trc]),
+                                            tr16(&stg[(8 * s + 4 + trj) * kSW + 16 * lq + 4 * trc]),
                                             0, 1, 2, 3);
     __builtin_amdgcn_raw_buffer_store_b128(d, r, (16 * lq + li) * row_bytes + col0_bytes + 16 * s,
                                            0, 0);
@@ -275,13 +285,10 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
       for (int P = 0; P < 2; ++P)
 #pragma unroll
         for (int t = 0; t < 2; ++t) kfr[P][t][G] = lds8(kt + tix(pair_row(P, t, li), 32 * G + 8 * lq));
-    if (hcg) {
-      const __amdgpu_buffer_rsrc_t rh =
-          store_rsrc(hcg + (cp.slot0 + n) * (long)K * p.V + v0, (uint32_t)(K * p.V - v0) * 2u);
+    if (hcg) {  // staged now, stored at the end of the step (stage 5)
 #pragma unroll
       for (int half = 0; half < K / 64; ++half)
-        store_rows(s.stg[wave], [&](int G, int t, int e) { return hs[0][2 * half + G][t][e]; }, rh,
-                   (uint32_t)p.V * 2u, (uint32_t)(64 * half * p.V + col) * 2u, lane);
+        stage_rows(s.stgh[wave][half], [&](int G, int t, int e) { return hs[0][2 * half + G][t][e]; }, lane);
     }
     f16x8 bk[kG];
     Q8 bq[kG];
@@ -466,8 +473,17 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
       }
     if constexpr (VN) {
       const __amdgpu_buffer_rsrc_t rv = store_rsrc(vng + (tok * p.H + h) * p.V + v0, rows * v_row);
-      store_rows(s.stg[wave], [&](int G, int t, int e) { return vn[G][t][e]; }, rv, v_row,
-                 (uint32_t)col * 2u, lane);
+      stage_rows(s.stg[wave], [&](int G, int t, int e) { return vn[G][t][e]; }, lane);
+      flush_rows(s.stg[wave], rv, v_row, (uint32_t)col * 2u, lane);
+    }
+    // the state entering the chunk -> h_chunks (its global stores are kept away from the start
+    // of the step, where they would delay the next chunk's transfers)
+    if (hcg) {
+      const __amdgpu_buffer_rsrc_t rh =
+          store_rsrc(hcg + (cp.slot0 + n) * (long)K * p.V + v0, (uint32_t)(K * p.V - v0) * 2u);
+#pragma unroll
+      for (int half = 0; half < K / 64; ++half)
+        flush_rows(s.stgh[wave][half], rh, (uint32_t)p.V * 2u, (uint32_t)(64 * half * p.V + col) * 2u, lane);
     }
   }
 
