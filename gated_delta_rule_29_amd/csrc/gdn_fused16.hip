@@ -57,6 +57,7 @@ using namespace chunk;
 using namespace dma;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kBV = 32;    // value columns per workgroup (16 per scan wave)
@@ -102,6 +103,23 @@ __device__ __forceinline__ bf16x8 tr16_pair(const u16* p0, const u16* p1) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// LDS base addresses the optimiser cannot relate to one another: each tile read is then
+// issued as its own base plus an instruction immediate (the compiler would otherwise derive
+// many addresses from one register with a separate add each).
+typedef __attribute__((address_space(3))) const u16 lds_u16;
+__device__ __forceinline__ lds_u16* lds_base(const u16* p) {
+  lds_u16* b = (lds_u16*)(uintptr_t)lds_addr(p);
+  asm volatile("" : "+v"(b));
+  return b;
+}
+template <typename V>
+__device__ __forceinline__ V lds_at(lds_u16* b, int off) {
+  return *(const __attribute__((address_space(3))) V*)(b + off);
+}
+__device__ __forceinline__ u32x2 tr16_at(lds_u16* b, int off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + off)));
+}
+
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf_at(const u32x2& v, int e) {
@@ -109,11 +127,13 @@ __device__ __forceinline__ float bf_at(const u32x2& v, int e) {
 }
 
 __device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d) {
-  const bf16 x0 = (bf16)a, x1 = (bf16)b, x2 = (bf16)c, x3 = (bf16)d;
-  u32x2 r;
-  r[0] = (unsigned)__builtin_bit_cast(u16, x0) | ((unsigned)__builtin_bit_cast(u16, x1) << 16);
-  r[1] = (unsigned)__builtin_bit_cast(u16, x2) | ((unsigned)__builtin_bit_cast(u16, x3) << 16);
-  return r;
+  // built as one vector so that the conversions pair up into packed converts
+  bf16x4 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  v[2] = (bf16)c;
+  v[3] = (bf16)d;
+  return __builtin_bit_cast(u32x2, v);
 }
 
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
@@ -450,8 +470,10 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 #pragma unroll
               for (int I = 0, t = 0; I < 4; ++I) {
                 const int r = 16 * I + li;
-                const float rv = rowv(r, isq);
-                const float be_r = (kFastDecay || isq) ? 1.f : G[kBeta + r];
+                // P carries the output scale: one factor per row here instead of one per
+                // output element in the scan
+                const float rv = rowv(r, isq) * ((isq && kFastDecay) ? p.scale : 1.f);
+                const float be_r = isq ? (kFastDecay ? 1.f : p.scale) : (kFastDecay ? 1.f : G[kBeta + r]);
 #pragma unroll
                 for (int J = 0; J <= I; ++J, ++t) {
                   if (!((mask >> t) & 1)) continue;
@@ -528,32 +550,38 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   // the step before the one that uses it (a chunk's q / k tiles are in LDS from the end of
   // the step two before its own); the rest is read under the K h products.
   bf16x8 kfr[2][2][kG], qfr[2][2][kG];
-  auto read_k = [&](int c, int li, int lq, int g0, int g1) {
-    const bf16* kt = reinterpret_cast<const bf16*>(s.qk[c % 3].k);
+  // Tile reads go through a few per-lane element offsets taken once per step: the swizzle
+  // does not see row bit 5 or the column sub-tile, so rows 32P and sub-tiles 32G add the
+  // constants 1024 P and 2048 G (instruction immediates).  ob[t]: the pair rows
+  // pair_row(0, t, li) at octet lq; ot[h]: rows 8lq + 4h + trj at octet trc (transposed reads).
+  auto read_k = [&](int c, const int* ob, int g0, int g1) {
+    lds_u16* kb[2] = {lds_base(s.qk[c % 3].k + ob[0]), lds_base(s.qk[c % 3].k + ob[1])};
 #pragma unroll
     for (int G = 0; G < kG; ++G)
 #pragma unroll
       for (int P = 0; P < 2; ++P)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          if (G >= g0 && G < g1) kfr[P][t][G] = lds8(kt + tix(pair_row(P, t, li), 32 * G + 8 * lq));
+          if (G >= g0 && G < g1) kfr[P][t][G] = lds_at<bf16x8>(kb[t], 1024 * P + 2048 * G);
   };
-  auto read_q = [&](int c, int li, int lq) {
-    const bf16* qt = reinterpret_cast<const bf16*>(s.qk[c % 3].q);
+  auto read_q = [&](int c, const int* ob) {
+    lds_u16* qb[2] = {lds_base(s.qk[c % 3].q + ob[0]), lds_base(s.qk[c % 3].q + ob[1])};
 #pragma unroll
     for (int Gk = 0; Gk < kG; ++Gk)
 #pragma unroll
       for (int G = 0; G < 2; ++G)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) qfr[G][t][Gk] = lds8(qt + tix(pair_row(G, t, li), 32 * Gk + 8 * lq));
+        for (int t = 0; t < 2; ++t) qfr[G][t][Gk] = lds_at<bf16x8>(qb[t], 1024 * G + 2048 * Gk);
   };
   __syncthreads();
 
   for (int n = -1; n < nchunks; ++n) {
     const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
     const int trj = (lane >> 2) & 3, trc = lane & 3;
+    const int ob[2] = {tix(pair_row(0, 0, li), 8 * lq), tix(pair_row(0, 1, li), 8 * lq)};
+    const int ot[2] = {tix(8 * lq + trj, 8 * trc), tix(8 * lq + 4 + trj, 8 * trc)};
     if (n < 0) {
-      if (nchunks > 0) read_k(0, li, lq, 0, kG / 2);
+      if (nchunks > 0) read_k(0, ob, 0, kG / 2);
     } else {
       const typename SM::QK& Q = s.qk[n % 3];
       const u16* vt = s.v[n & 1];
@@ -574,12 +602,14 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       // ---- stage 1: X_K = K h (tokens 32P + 8lq + 4t + e of this lane's column), a
       // contraction round at a time; under it, reads of the rest of K, of V, the Y gates and
       // the Q rows
-      read_k(n, li, lq, kG / 2, kG);
+      read_k(n, ob, kG / 2, kG);
       bf16x8 bh[kG];
 #pragma unroll
       for (int G = 0; G < kG; ++G) bh[G] = pack8<bf16>(hs[G][0], hs[G][1]);
       __builtin_amdgcn_sched_barrier(0);
       u32x2 vv[2][2];
+      lds_u16* vb[2] = {lds_base(vt + tix(8 * lq + trj, 16 * wave + 4 * trc)),
+                        lds_base(vt + tix(8 * lq + 4 + trj, 16 * wave + 4 * trc))};
       f32x4 be[2][2], eg[2][2];
       f32x4 xk[2][2];
 #pragma unroll
@@ -598,12 +628,12 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const int r0 = 32 * P + 8 * lq + 4 * t;
-              vv[P][t] = tr16(&vt[tix(r0 + trj, 16 * wave + 4 * trc)]);
+              vv[P][t] = tr16_at(vb[t], 1024 * P);
               be[P][t] = *reinterpret_cast<const f32x4*>(&vec[kBeta + r0]);
               eg[P][t] = *reinterpret_cast<const f32x4*>(&vec[kEg + r0]);
             }
         }
-        if (G == kG - 1) read_q(n, li, lq);
+        if (G == kG - 1) read_q(n, ob);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -611,12 +641,13 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       // of o (value columns 4lq..4lq+3 of token pair_row(G, t, li), the state as the A
       // operand), which fills the matrix pipe while Y is formed
       f16x8 tmf[2][2][2];
+      lds_u16* tb[2] = {lds_base(T.tm + ob[0]), lds_base(T.tm + ob[1])};
 #pragma unroll
       for (int P = 0; P < 2; ++P)
 #pragma unroll
         for (int G = P; G < 2; ++G)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) tmf[G][t][P] = lds8(tmt + tix(pair_row(G, t, li), 32 * P + 8 * lq));
+          for (int t = 0; t < 2; ++t) tmf[G][t][P] = lds_at<f16x8>(tb[t], 1024 * G + 2048 * P);
       f32x4 oacc[2][2];
 #pragma unroll
       for (int G = 0; G < 2; ++G)
@@ -644,14 +675,15 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       // ---- stage 3: reads of K^T (the update's A operand, transpose reads), the update
       // gates, P rows and the o gates; v_new = Tm Y (token group P feeds groups G >= P)
       bf16x8 ktf[kG][2][2];
+      lds_u16* ktb[2] = {lds_base(Q.k + ot[0]), lds_base(Q.k + ot[1])};
 #pragma unroll
       for (int P = 0; P < 2; ++P)
 #pragma unroll
         for (int G = 0; G < kG; ++G)
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const int c0 = 32 * G + 8 * trc + 4 * t;
-            ktf[G][t][P] = tr16_pair(&Q.k[tix(32 * P + 8 * lq + trj, c0)], &Q.k[tix(32 * P + 8 * lq + 4 + trj, c0)]);
+            ktf[G][t][P] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr16_at(ktb[0], 1024 * P + 2048 * G + 4 * t),
+                                                                              tr16_at(ktb[1], 1024 * P + 2048 * G + 4 * t), 0, 1, 2, 3));
           }
       f32x4 l0[2], l1[2];
 #pragma unroll
@@ -661,6 +693,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       }
       const float egl = vec[kEgl];
       f16x8 pfr[2][2][2];
+      lds_u16* pb[2] = {lds_base(T.p + ob[0]), lds_base(T.p + ob[1])};
       float ego[2][2];
 #pragma unroll
       for (int G = 0; G < 2; ++G)
@@ -668,8 +701,8 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         for (int t = 0; t < 2; ++t) {
           const int r = pair_row(G, t, li);
 #pragma unroll
-          for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds8(ptt + tix(r, 32 * P + 8 * lq));
-          ego[G][t] = vec[kEg + r];
+          for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds_at<f16x8>(pb[t], 1024 * G + 2048 * P);
+          ego[G][t] = vec[kEg + r] * p.scale;
         }
       f32x4 vn[2][2];
 #pragma unroll
@@ -716,9 +749,10 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         }
       }
 
-      // ---- stage 5: o^T = scale ((Q h)^T diag(e^gamma) + (P v_new)^T), 8-byte row stores;
+      // ---- stage 5: o^T = (Q h)^T diag(scale e^gamma) + (scale P v_new)^T (P carries the
+      // scale), 8-byte row stores;
       // reads of the first half of the next chunk's K rows
-      if (more) read_k(n + 1, li, lq, 0, kG / 2);
+      if (more) read_k(n + 1, ob, 0, kG / 2);
       const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
 #pragma unroll
       for (int G = 0; G < 2; ++G)
@@ -727,8 +761,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
           f32x4 acc = oacc[G][t] * ego[G][t];
 #pragma unroll
           for (int P = 0; P <= G; ++P) acc = mma16(bv[P], pfr[G][t][P], acc);
-          const f32x4 ov = acc * p.scale;
-          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(ov[0], ov[1], ov[2], ov[3]), ro,
+          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(acc[0], acc[1], acc[2], acc[3]), ro,
                                                 pair_row(G, t, li) * v_row + (16 * wave + 4 * lq) * 2, 0, 0);
         }
     }

@@ -37,6 +37,7 @@ using namespace chunk;
 using namespace dma;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kNW = 2;   // compute waves per workgroup
@@ -67,11 +68,13 @@ __device__ __forceinline__ float bf_at(const u32x2& v, int e) {
 
 // four fp32 -> four bf16 (round to nearest even), packed for one 8-byte store
 __device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d) {
-  const bf16 x0 = (bf16)a, x1 = (bf16)b, x2 = (bf16)c, x3 = (bf16)d;
-  u32x2 r;
-  r[0] = (unsigned)__builtin_bit_cast(u16, x0) | ((unsigned)__builtin_bit_cast(u16, x1) << 16);
-  r[1] = (unsigned)__builtin_bit_cast(u16, x2) | ((unsigned)__builtin_bit_cast(u16, x3) << 16);
-  return r;
+  // built as one vector so that the conversions pair up into packed converts
+  bf16x4 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  v[2] = (bf16)c;
+  v[3] = (bf16)d;
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // All operand tiles use the column-split layout tix_s32<64> (gdn_tiles.h).
