@@ -31,7 +31,9 @@ KERNEL_SOURCE_DIR = "gated_delta_rule_29_amd/csrc"
 # The kernels one forward call launches; the roofline covers the whole call (every kernel on
 # the path), timed with HIP events around it on the launch stream.
 KERNELS_FUSED = "gdn_fwd call: fused16_kernel"
+KERNELS_FUSED_PACKED = "gdn_fwd_varlen call: rank_kernel + fused16_kernel"
 KERNELS_BF16 = "gdn_fwd call: prep16_kernel + scan16_kernel"
+KERNELS_BF16_PK = "gdn_fwd call: prep16pk_kernel + scan16_kernel"
 KERNELS_F32 = "gdn_fwd call: chunk_prep_kernel + scan_kernel"
 
 
@@ -42,7 +44,9 @@ def kernels_of(dt, per_key, save):
 
     if dt != torch.bfloat16:
         return KERNELS_F32
-    return KERNELS_BF16 if (per_key or save) else KERNELS_FUSED
+    if per_key:
+        return KERNELS_BF16_PK
+    return KERNELS_BF16 if save else KERNELS_FUSED
 COUNTER_FILE = "profiles/fused16_kernel_b4h16t4096_hbm_counters.md"
 
 
@@ -213,7 +217,8 @@ def main():
         th = T * H
         elt = 2 if dt == torch.bfloat16 else 4
         alg = alg_bytes_per_launch(1, T, H, K, V, elt, False, False, n_states=N * H)
-        kernel = kernels_of(dt, inp["gk"] is not None, False) + " (packed)"
+        kernel = kernels_of(dt, inp["gk"] is not None, False)
+        kernel = KERNELS_FUSED_PACKED if kernel == KERNELS_FUSED else kernel + " (packed)"
         config = {"workload": args.workload, "T_total": T, "N": N, "H": H, "K": K, "V": V,
                   "lengths": (cu[1:] - cu[:-1]).tolist(), "chunk": 64, "state": "fp32"}
 
