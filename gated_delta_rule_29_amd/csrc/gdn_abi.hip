@@ -177,7 +177,7 @@ namespace {
 
 // bigdn_fwd workspace: every view 256-byte aligned, in the order of BigdnParams.
 struct BigdnWs {
-  size_t q_rms, k_rms, G, Gz, U, uz, Sf, SsumT, zsum, total;
+  size_t q_rms, k_rms, G, Gz, U, uz, Sf, Zf, SsumT, zsum, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -193,6 +193,7 @@ BigdnWs bigdn_ws(int B, int F, int S, int H, int D) {
   w.U = off; off = al256(off + mats * 4);
   w.uz = off; off = al256(off + vecs * 4);
   w.Sf = off; off = al256(off + mats * 4);
+  w.Zf = off; off = al256(off + vecs * 16 * 4);
   w.SsumT = off; off = al256(off + mats * 2);
   w.zsum = off; off = al256(off + vecs * 4);
   w.total = off;
@@ -245,6 +246,8 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
     return fail(GDN_ERR_INVALID, "qkv, beta, decay, norm weights, RoPE tables, num and den must be non-null");
   if (F <= 0 || S <= 0) return fail(GDN_ERR_INVALID, "F and S must be positive (got %d, %d)", F, S);
   if ((int64_t)F * S > INT32_MAX) return fail(GDN_ERR_INVALID, "F*S too large");
+  // the scan addresses one (b, h)'s per-frame statistics with 32-bit byte offsets
+  if (F > 65535) return fail(GDN_ERR_UNSUPPORTED, "F must be <= 65535, got %d", F);
   const int N = F * S;
   int rc = check_bigdn_dims(B, N, H, D);
   if (rc) return rc;
@@ -267,6 +270,7 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
   p.U = reinterpret_cast<float*>(ws + w.U);
   p.uz = reinterpret_cast<float*>(ws + w.uz);
   p.Sf = reinterpret_cast<float*>(ws + w.Sf);
+  p.Zf = reinterpret_cast<float*>(ws + w.Zf);
   p.SsumT = reinterpret_cast<_Float16*>(ws + w.SsumT);
   p.zsum = reinterpret_cast<float*>(ws + w.zsum);
   hipError_t e = gdn::launch_bigdn(p, static_cast<hipStream_t>(stream));

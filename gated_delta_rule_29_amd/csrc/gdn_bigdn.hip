@@ -24,6 +24,7 @@
 // (num, den per 64-token block).  Products use fp16 operands and fp32 accumulation; the state
 // is fp32.
 #include "gdn_device.h"
+#include "gdn_dma.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
 
@@ -127,6 +128,26 @@ __global__ __launch_bounds__(kPrepThreads) void rms_prep_kernel(const PrepParams
   }
 }
 
+// Workspace layouts of G and U (written by frame_stats, read by scan), per (b, h, frame):
+//   G: A-operand order, element (r, c) at ((((r / (D/4)) kRT + (r % (D/4)) / 16) (D/32)
+//      + c / 32) 64 + ((c / 8) % 4) 16 + r % 16) 8 + c % 8 with kRT = D / 64, so a scan
+//      lane's 16-byte operand is one load and a wave's loads are contiguous;
+//   U: accumulator order, element (r, c) at (c / 16) 16D + (((r / (D/4)) kRT
+//      + (r % (D/4)) / 16) 64 + ((r % 16) / 4) 16 + c % 16) 4 + r % 4.
+template <int D>
+__device__ __forceinline__ long g_lane_index(int r, int c) {
+  constexpr int kRT = D / 64;
+  return ((((long)(r / (D / 4)) * kRT + (r % (D / 4)) / 16) * (D / 32) + c / 32) * 64 +
+          ((c / 8) & 3) * 16 + (r & 15)) * 8 + (c & 7);
+}
+template <int D>
+__device__ __forceinline__ long u_lane_index(int r, int c) {
+  constexpr int kRT = D / 64;
+  return (long)(c >> 4) * (16 * D) +
+         (((long)(r / (D / 4)) * kRT + (r % (D / 4)) / 16) * 64 + ((r & 15) >> 2) * 16 + (c & 15)) * 4 +
+         (r & 3);
+}
+
 // ---- frame statistics -------------------------------------------------------------------
 // One workgroup of twelve waves per (b, h, frame) computes all three statistics over the
 // frame's tokens, 64 at a time:
@@ -145,6 +166,7 @@ __global__ __launch_bounds__(kPrepThreads) void rms_prep_kernel(const PrepParams
 constexpr int kStatThreads = 768;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
@@ -289,7 +311,10 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
             for (int u = 0; u < 2; ++u) acc[a][t][c][u] = mma16(af[a][t], bf[c][u], acc[a][t][c][u]);
     }
   }
-  // epilogue: row channel 32(kNG qi + a) + 8lq + 4t + e, column 32(kNG qj + c) + 8(li >> 2) + 4u + (li & 3)
+  // epilogue: row channel 32(kNG qi + a) + 8lq + 4t + e, column 32(kNG qj + c) + 8(li >> 2) + 4u + (li & 3).
+  // G, Gz and U go out in the scan's operand layouts (g_lane_index, u_lane_index): U's four
+  // rows e are one 16-byte store; G and Gz, being symmetric, are stored transposed, so their
+  // four e become four consecutive columns of one row (8 bytes).
   const long mat = (((long)b * p.H + h) * p.F + f) * (long)D * D;
 #pragma unroll
   for (int a = 0; a < kNG; ++a)
@@ -298,17 +323,19 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
 #pragma unroll
       for (int c = 0; c < kNG; ++c)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u) {
+          const int d1 = 32 * (kNG * qi + a) + 8 * lq + 4 * t;
+          const int d2 = 32 * (kNG * qj + c) + 8 * (li >> 2) + 4 * u + (li & 3);
+          const f32x4 x = acc[a][t][c][u];
+          if (m == 1) {
+            *reinterpret_cast<f32x4*>(p.U + mat + u_lane_index<D>(d1, d2)) = x;
+          } else {
+            f16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int d1 = 32 * (kNG * qi + a) + 8 * lq + 4 * t + e;
-            const int d2 = 32 * (kNG * qj + c) + 8 * (li >> 2) + 4 * u + (li & 3);
-            const long idx = mat + (long)d1 * D + d2;
-            const float x = acc[a][t][c][u][e];
-            if (m == 0) p.G[idx] = (f16)x;
-            else if (m == 1) p.U[idx] = x;
-            else p.Gz[idx] = (f16)x;
+            for (int e = 0; e < 4; ++e) v[e] = (f16)x[e];
+            *reinterpret_cast<f16x4*>((m == 0 ? p.G : p.Gz) + mat + g_lane_index<D>(d2, d1)) = v;
           }
+        }
   // uz: sum of the per-thread partial sums of each channel (threads of one octet)
   __syncthreads();
   float* red = reinterpret_cast<float*>(&tl[0][0]);  // [kStatThreads][8]
@@ -324,175 +351,164 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
 }
 
 // ---- scan -------------------------------------------------------------------------------
-// One workgroup per (b, h, 16-column block cb) of the state; block cb == D/16 runs z.
-// Wave w owns state rows (D/4)w .. (D/4)w + D/4 - 1 of the block.  The state lives in
-// registers (fp32) and is exchanged through LDS (fp16 transposed copy) as the B operand of
-// G S each frame.  The frames' G rows and U entries a lane needs are loaded one frame ahead,
-// so the global-memory latency overlaps the previous frame's products.
+// One workgroup per (b, h, 16-column block cb) of the state, plus one (cb == D/16) for z: z
+// runs as a 16-column block whose columns all hold z (A operand Gz, U the uz entries of each
+// row), so both share this code.  Wave w owns state rows (D/4)w .. (D/4)w + D/4 - 1 of the
+// block.  The state lives in registers (fp32) and is exchanged through LDS (fp16 transposed
+// copy, double-buffered so one barrier per frame suffices) as the B operand of G S.
+//
+// Operands are staged per wave in a three-frame LDS ring by direct-to-LDS transfers issued
+// two frames ahead; each wave reads back only what it transferred (at its own lane slots, so
+// without bank conflicts), so a counted wait on its own loads is the only synchronisation.
+// A ring stage holds, per wave: the lane-ordered G (or Gz) operands (kNG KB), the U tile
+// (kRT KB), in the reverse pass the forward state of the frame being written (kRT KB), and
+// the frame's decay (256 B).
 template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
-  __shared__ __attribute__((aligned(16))) f16 st[16][D];  // state^T as fp16 operand
-  __shared__ float zs[D];
+  using namespace dma;
+  constexpr int kRT = D / 64;                            // 16-row tiles per wave
+  constexpr int kNG = kRT * (D / 32);                    // 1 KB G transfers per wave and frame
+  constexpr int kStage = (kNG + 2 * kRT) * 1024 + 256;   // bytes per wave and ring stage
+  constexpr int kLd = kNG + kRT + 1;                     // forward loads per frame
+  constexpr int kLdR = kLd + kRT;                        // reverse loads per frame (+ S_f)
+  constexpr int kSP = D + 8;  // padded st row: the 16 rows of a B-operand read hit distinct banks
+  __shared__ __attribute__((aligned(1024))) char ring[4 * 3 * kStage];
+  __shared__ __attribute__((aligned(16))) f16 st[2][16 * kSP];  // state^T as fp16 operand
   const int cb = blockIdx.x % (D / 16 + 1);
   const int bh = blockIdx.x / (D / 16 + 1);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool zb = cb == D / 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
   const int F = p.F;
   const long mat0 = (long)bh * F * D * D;
-  const float* decay = p.decay + (long)bh * F;
+  auto clampf = [&](int fa) { return fa < 0 ? 0 : (fa >= F ? F - 1 : fa); };
+  auto row_of = [&](int t, int e) { return (D / 4) * wave + 16 * t + 4 * lq + e; };
 
-  if (cb == D / 16) {
-    // z: z <- d (z - Gz z) + uz, forward then reverse; zsum_f = z_f + zR_f.  Thread tid < D
-    // owns entry tid; its Gz row of the next frame is loaded ahead.
-    typedef f16 f16x8_t __attribute__((ext_vector_type(8)));
-    f16x8_t gr[D / 8], gn[D / 8];
-    float un = 0.f;
-    auto load_row = [&](int fa, f16x8_t* g, float& u) {
-      if (tid < D && fa >= 0 && fa < F) {
-        const f16* src = p.Gz + mat0 + (long)fa * D * D + (long)tid * D;
+  // sources (every byte count below fits 32 bits: F <= 65535 and D <= 128)
+  const i32x4 rG = make_rsrc(zb ? p.Gz + mat0 : p.G + mat0, (uint32_t)F * D * D * 2);
+  const i32x4 rU = zb ? make_rsrc(p.uz + (long)bh * F * D, (uint32_t)F * D * 4)
+                      : make_rsrc(p.U + mat0, (uint32_t)F * D * D * 4);
+  const long fst = zb ? 16 * D : (long)D * D;  // floats between frames of the forward states
+  float* sfw = zb ? p.Zf + (long)bh * F * 16 * D : p.Sf + mat0 + cb * 16 * D;
+  const i32x4 rS = make_rsrc(sfw, (uint32_t)((F - 1) * fst + 16 * D) * 4);
+  const i32x4 rD = make_rsrc(p.decay + (long)bh * F, (uint32_t)F * 4);
+  const uint32_t vU = zb ? 16 * lq : 16 * lane;
+  const uint32_t ringw = lds_addr(ring) + wave * 3 * kStage;
+  // transfers of frame fa (and, in the reverse pass, forward state fs) into ring stage stg
+  auto issue = [&](int fa, int stg, bool with_sf, int fs) {
+    fa = clampf(fa);
+    const uint32_t sb = ringw + stg * kStage;
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) g[c] = *reinterpret_cast<const f16x8_t*>(src + 8 * c);
-        u = p.uz[((long)bh * F + fa) * D + tid];
-      }
-    };
-    auto zstep = [&](int fa) {  // gr, un hold frame fa
-      float nz = 0.f;
-      if (tid < D) {
-        float acc = 0.f;
+    for (int n = 0; n < kNG; ++n) dma16(rG, 16 * lane, (uint32_t)fa * (D * D * 2) + (wave * kNG + n) * 1024, sb + n * 1024);
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc += (float)gr[c][j] * zs[8 * c + j];
-        nz = decay[fa] * (zs[tid] - acc) + un;
-      }
-      __syncthreads();
-      if (tid < D) zs[tid] = nz;
-      __syncthreads();
-    };
-    if (tid < D) zs[tid] = 0.f;
-    load_row(0, gr, un);
-    __syncthreads();
-    for (int f = 0; f < F; ++f) {
-      float u2 = 0.f;
-      load_row(f + 1, gn, u2);
-      zstep(f);
-      if (tid < D) p.zsum[((long)bh * F + f) * D + tid] = zs[tid];  // forward part
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) gr[c] = gn[c];
-      un = u2;
+    for (int t = 0; t < kRT; ++t) {
+      const uint32_t so = zb ? ((uint32_t)fa * D + (D / 4) * wave + 16 * t) * 4
+                             : (uint32_t)fa * (D * D * 4) + cb * 64 * D + (wave * kRT + t) * 1024;
+      dma16(rU, vU, so, sb + (kNG + t) * 1024);
     }
-    if (tid < D) zs[tid] = 0.f;
-    load_row(F - 1, gr, un);
-    __syncthreads();
-    for (int f = F - 1; f >= 0; --f) {
-      // frame f reads the state built from frames > f: absorb frame f + 1 first
-      if (f < F - 1) {
-        float u2 = 0.f;
-        load_row(f, gn, u2);
-        zstep(f + 1);
+    dma4(rD, 0, (uint32_t)fa * 4, sb + (kNG + 2 * kRT) * 1024);
+    if (with_sf) {
+      fs = clampf(fs);
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) gr[c] = gn[c];
-        un = u2;
-      }
-      if (tid < D) p.zsum[((long)bh * F + f) * D + tid] += zs[tid];
+      for (int t = 0; t < kRT; ++t)
+        dma16(rS, 16 * lane, (uint32_t)(fs * fst * 4) + (wave * kRT + t) * 1024, sb + (kNG + kRT + t) * 1024);
     }
-    return;
-  }
+  };
+  auto stage_ptr = [&](int stg) { return ring + (wave * 3 + stg) * kStage; };
 
-  constexpr int kRT = D / 64;  // 16-row tiles per wave (wave covers D/4 rows)
-  const int col = cb * 16 + li;
   f32x4 s[kRT];
 #pragma unroll
   for (int t = 0; t < kRT; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto row_of = [&](int t, int e) { return (D / 4) * wave + 16 * t + 4 * lq + e; };
-  // operands of one frame: G rows (A operand) and U entries of this lane
-  f16x8 ga[kRT][D / 32], gb[kRT][D / 32];
-  f32x4 ua[kRT], ub[kRT];
-  auto load_frame = [&](int fa, f16x8 (*g)[D / 32], f32x4* u) {
-    if (fa < 0 || fa >= F) return;
-    const f16* G = p.G + mat0 + (long)fa * D * D;
-    const float* U = p.U + mat0 + (long)fa * D * D;
+  // s <- d (s - G s) + U with the operands of ring stage stg; writes and reads st[ph]
+  auto step = [&](int stg, int ph) {
+    const char* sb = stage_ptr(stg);
+    f16x8 ga[kRT][D / 32];
+    f32x4 uu[kRT];
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
-      const int r = (D / 4) * wave + 16 * t + li;
 #pragma unroll
-      for (int k = 0; k < D / 32; ++k) g[t][k] = *reinterpret_cast<const f16x8*>(G + (long)r * D + 32 * k + 8 * lq);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[t][e] = U[(long)row_of(t, e) * D + col];
+      for (int k = 0; k < D / 32; ++k)
+        ga[t][k] = *reinterpret_cast<const f16x8*>(sb + (t * (D / 32) + k) * 1024 + 16 * lane);
+      uu[t] = *reinterpret_cast<const f32x4*>(sb + (kNG + t) * 1024 + 16 * lane);
     }
-  };
-  // one step: s <- d (s - G s) + U with the frame-fa operands in ga, ua
-  auto step = [&](int fa) {
+    const float dcy = *reinterpret_cast<const float*>(sb + (kNG + 2 * kRT) * 1024 + 4 * lane);
+    f16* sp = st[ph];
 #pragma unroll
-    for (int t = 0; t < kRT; ++t)
+    for (int t = 0; t < kRT; ++t) {
+      f16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st[li][row_of(t, e)] = (f16)s[t][e];
+      for (int e = 0; e < 4; ++e) v[e] = (f16)s[t][e];
+      *reinterpret_cast<f16x4*>(sp + li * kSP + row_of(t, 0)) = v;
+    }
     __syncthreads();
-    const float dcy = decay[fa];
     f32x4 gs[kRT];
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
       gs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < D / 32; ++k) gs[t] = mma16(ga[t][k], lds8(&st[li][32 * k + 8 * lq]), gs[t]);
+      for (int k = 0; k < D / 32; ++k) gs[t] = mma16(ga[t][k], lds8(sp + li * kSP + 32 * k + 8 * lq), gs[t]);
     }
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[t][e] = dcy * (s[t][e] - gs[t][e]) + ua[t][e];
-    __syncthreads();
+      for (int e = 0; e < 4; ++e) s[t][e] = dcy * (s[t][e] - gs[t][e]) + uu[t][e];
   };
-  auto advance = [&]() {
+  // output of frame fa: s + add (the forward state), as fp16 (S + R)^T -- four consecutive
+  // rows of one column per lane, 8 bytes -- or, for z, fp32 entries of column 0
+  auto store_sum = [&](int fa, const f32x4* add) {
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
+      f32x4 tot;
 #pragma unroll
-      for (int k = 0; k < D / 32; ++k) ga[t][k] = gb[t][k];
-      ua[t] = ub[t];
+      for (int e = 0; e < 4; ++e) tot[e] = s[t][e] + (add ? add[t][e] : 0.f);
+      if (zb) {
+        if (li == 0) *reinterpret_cast<f32x4*>(p.zsum + ((long)bh * F + fa) * D + row_of(t, 0)) = tot;
+      } else {
+        f16x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (f16)tot[e];
+        *reinterpret_cast<f16x4*>(p.SsumT + mat0 + (long)fa * D * D + (long)(cb * 16 + li) * D + row_of(t, 0)) = h;
+      }
     }
   };
-  // forward: S_f after absorbing frame f; kept in fp32 in the workspace
-  load_frame(0, ga, ua);
+
+  // forward: S_f after absorbing frame f (ring stage f % 3), kept in fp32 in the workspace in
+  // the per-lane tile order
+  issue(0, 0, false, 0);
+  issue(1, 1, false, 0);
   for (int f = 0; f < F; ++f) {
-    load_frame(f + 1, gb, ub);
-    step(f);
-    advance();
+    issue(f + 2, (f + 2) % 3, false, 0);
+    wait_vm<2 * kLd>();  // frame f's loads are done once only frames f+1, f+2 may be pending
+    step(f % 3, f & 1);
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p.Sf[mat0 + (long)f * D * D + (long)row_of(t, e) * D + col] = s[t][e];
+      *reinterpret_cast<f32x4*>(sfw + (long)f * fst + (wave * kRT + t) * 256 + 4 * lane) = s[t];
   }
-  // reverse: R_{F-1} = 0, R_f from frame f+1; write (S_f + R_f)^T as fp16, four consecutive
-  // rows of one column per lane (8 bytes)
+  // frame F-1 reads R_{F-1} = 0: its sum is the forward state itself
+  store_sum(F - 1, nullptr);
+  // the reverse pass reads the forward states back and restarts the st phases: every store
+  // of this wave has landed and every wave is past its last forward read
+  wait_vm0();
+  __syncthreads();
+  // reverse: step i absorbs frame F-1-i and gives R of frame F-2-i, whose forward state comes
+  // in the same ring stage (i % 3)
 #pragma unroll
   for (int t = 0; t < kRT; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the forward state of frame f is loaded with the operands of the frame absorbed before it
-  f32x4 sfa[kRT], sfb[kRT];
-  auto load_sf = [&](int fa, f32x4* dst) {
-    if (fa < 0) return;
+  issue(F - 1, 0, true, F - 2);
+  issue(F - 2, 1, true, F - 3);
+  for (int i = 0; i < F - 1; ++i) {
+    issue(F - 3 - i, (i + 2) % 3, true, F - 4 - i);
+    wait_vm<2 * kLdR>();
+    step(i % 3, i & 1);
+    f32x4 sf[kRT];
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[t][e] = p.Sf[mat0 + (long)fa * D * D + (long)row_of(t, e) * D + col];
-  };
-  load_frame(F - 1, ga, ua);
-  load_sf(F - 1, sfa);
-  for (int f = F - 1; f >= 0; --f) {
-    load_sf(f - 1, sfb);
-    if (f < F - 1) {
-      load_frame(f, gb, ub);
-      step(f + 1);
-      advance();
-    }
-#pragma unroll
-    for (int t = 0; t < kRT; ++t) {
-      typedef f16 f16x4_t __attribute__((ext_vector_type(4)));
-      f16x4_t tot;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tot[e] = (f16)(s[t][e] + sfa[t][e]);
-      *reinterpret_cast<f16x4_t*>(p.SsumT + mat0 + (long)f * D * D + (long)col * D + row_of(t, 0)) = tot;
-      sfa[t] = sfb[t];
-    }
+      sf[t] = *reinterpret_cast<const f32x4*>(stage_ptr(i % 3) + (kNG + kRT + t) * 1024 + 16 * lane);
+    store_sum(F - 2 - i, sf);
   }
+  // no transfer may still be writing the ring when the workgroup ends
+  wait_vm0();
 }
 
 // ---- output -----------------------------------------------------------------------------
@@ -525,16 +541,25 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
   for (int blk = g * grp; blk < (g + 1) * grp; ++blk) {
     const int n0 = blk * 64;
     __syncthreads();
-    // prep of q: 64 tokens x D/8 octets over 256 threads
-    for (int e = tid; e < 64 * (D / 8); e += 256) {
-      const int t = e / (D / 8), d0 = (e % (D / 8)) * 8;
+    // prep of q: 64 tokens x D/8 octets over 256 threads; every load of this thread's items
+    // is issued before any of them is used
+    constexpr int kItems = 64 * (D / 8) / 256;
+    float x[kItems][8], w[kItems][8], cs[kItems][8], sn[kItems][8], inv[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int e = tid + 256 * i, t = e / (D / 8), d0 = (e % (D / 8)) * 8;
       const long n = n0 + t, bn = (long)b * p.N + n;
-      float x[8], w[8], cs[8], sn[8], pos[8], rot[8];
-      load8f(qkv + bn * 3L * C + (long)h * D + d0, x);
-      load8f(p.q_norm_w + h * D + d0, w);
-      load8f(p.rope_cos + n * D + d0, cs);
-      load8f(p.rope_sin + n * D + d0, sn);
-      prep8(x, p.q_inv_rms[bn], w, cs, sn, 1.f, pos, rot);
+      load8f(qkv + bn * 3L * C + (long)h * D + d0, x[i]);
+      load8f(p.q_norm_w + h * D + d0, w[i]);
+      load8f(p.rope_cos + n * D + d0, cs[i]);
+      load8f(p.rope_sin + n * D + d0, sn[i]);
+      inv[i] = p.q_inv_rms[bn];
+    }
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int e = tid + 256 * i, t = e / (D / 8), d0 = (e % (D / 8)) * 8;
+      float pos[8], rot[8];
+      prep8(x[i], inv[i], w[i], cs[i], sn[i], 1.f, pos, rot);
       f16x8 v;
       float dp = 0.f;
 #pragma unroll

@@ -45,6 +45,25 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t so
                : "memory");
 }
 
+// 4 bytes per lane from buffer offset voff + soff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
+
+// Waits until at most N vector-memory instructions of this wave are outstanding.  Loads
+// (direct-to-LDS ones included) complete in issue order among themselves, but stores count
+// too and may complete out of that order, so a load is known complete once N is at most the
+// number of loads issued after it; stores still pending only make the wait longer.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" : : : "memory");
+}
+
 // Waits for every vector-memory load of this wave, the direct-to-LDS ones included.  Issued
 // through the builtin so the compiler's own wait tracking knows all loads have completed
 // (an opaque inline-assembly wait would leave it inserting further waits for them).

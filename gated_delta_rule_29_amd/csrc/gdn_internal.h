@@ -77,6 +77,7 @@ struct BigdnParams {
   float* U;          // [B, H, F, D, D]
   float* uz;         // [B, H, F, D]
   float* Sf;         // [B, H, F, D, D]  forward states
+  float* Zf;         // [B, H, F, 16 D]  forward z (16 identical columns)
   _Float16* SsumT;   // [B, H, F, D, D]  (S_f + R_f)^T
   float* zsum;       // [B, H, F, D]
 };

@@ -170,7 +170,8 @@ GDN_API int gdn_prep(const void* qkv, const float* q_norm_w, const float* k_norm
  *   q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, norm_eps   as in gdn_prep
  *   num     [B, N, H, D] bf16 OUT;  den [B, H, N] bf16 OUT
  *   workspace  at least bigdn_fwd_workspace_bytes(B, F, S, H, D) bytes, 256-byte aligned
- * Supported: D in {64, 128}, S a multiple of 64, H*D <= 4096.
+ * Supported: D in {64, 128}, S a multiple of 64, H*D <= 4096, F <= 65535 (GDN_ERR_UNSUPPORTED
+ * otherwise).
  */
 GDN_API size_t bigdn_fwd_workspace_bytes(int B, int F, int S, int H, int D);
 GDN_API int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const float* q_norm_w,

@@ -34,7 +34,8 @@ def test_prep(B, N, H, D):
         assert_close(name, out[name], ref[name], 1e-4)
 
 
-@pytest.mark.parametrize("B,F,S,H,D", [(1, 3, 64, 2, 64), (2, 5, 128, 3, 128), (1, 1, 64, 2, 128)])
+@pytest.mark.parametrize("B,F,S,H,D", [(1, 3, 64, 2, 64), (2, 5, 128, 3, 128), (1, 1, 64, 2, 128),
+                                          (1, 2, 64, 1, 64), (1, 7, 64, 2, 128)])
 def test_bigdn_small(B, F, S, H, D):
     import gated_delta_rule_29_amd as g
 
