@@ -177,7 +177,7 @@ namespace {
 
 // bigdn_fwd workspace: every view 256-byte aligned, in the order of BigdnParams.
 struct BigdnWs {
-  size_t q_rms, k_rms, G, Gz, U, uz, Sf, Zf, SsumT, zsum, total;
+  size_t q_rms, k_rms, G, Gz, U, uz, SdT, zd, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -192,10 +192,8 @@ BigdnWs bigdn_ws(int B, int F, int S, int H, int D) {
   w.Gz = off; off = al256(off + mats * 2);
   w.U = off; off = al256(off + mats * 4);
   w.uz = off; off = al256(off + vecs * 4);
-  w.Sf = off; off = al256(off + mats * 4);
-  w.Zf = off; off = al256(off + vecs * 16 * 4);
-  w.SsumT = off; off = al256(off + mats * 2);
-  w.zsum = off; off = al256(off + vecs * 4);
+  w.SdT = off; off = al256(off + 2 * mats * 2);
+  w.zd = off; off = al256(off + 2 * vecs * 4);
   w.total = off;
   return w;
 }
@@ -269,10 +267,8 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
   p.Gz = reinterpret_cast<_Float16*>(ws + w.Gz);
   p.U = reinterpret_cast<float*>(ws + w.U);
   p.uz = reinterpret_cast<float*>(ws + w.uz);
-  p.Sf = reinterpret_cast<float*>(ws + w.Sf);
-  p.Zf = reinterpret_cast<float*>(ws + w.Zf);
-  p.SsumT = reinterpret_cast<_Float16*>(ws + w.SsumT);
-  p.zsum = reinterpret_cast<float*>(ws + w.zsum);
+  p.SdT = reinterpret_cast<_Float16*>(ws + w.SdT);
+  p.zd = reinterpret_cast<float*>(ws + w.zd);
   hipError_t e = gdn::launch_bigdn(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "bigdn_fwd launch");
   return ok();

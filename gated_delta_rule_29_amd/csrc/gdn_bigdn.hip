@@ -20,9 +20,9 @@
 //
 // Kernels: rms (inv-RMS per token; with outputs it is gdn_prep), frame_stats (G, U, Gz, uz
 // per (b, h, f) from k, v with the prep applied on the fly, one workgroup per frame), scan
-// (16-column blocks of the state per (b, h), both directions, writes the summed states), out
-// (num, den per 64-token block).  Products use fp16 operands and fp32 accumulation; the state
-// is fp32.
+// (32-column blocks of the state per (b, h) and direction, the two directions concurrently;
+// writes every frame's state), out (num, den per 64-token blocks, adding the directions).
+// Products use fp16 operands and fp32 accumulation; the scanned state is fp32.
 #include "gdn_device.h"
 #include "gdn_dma.h"
 #include "gdn_internal.h"
@@ -61,16 +61,23 @@ __device__ __forceinline__ void load8f(const float* p, float* out) {
   }
 }
 
-// Front end of 8 channels d0..d0+7 (d0 a multiple of 8, so every RoPE pair is inside).
-__device__ __forceinline__ void prep8(const float* x, float inv, const float* w, const float* cs,
-                                      const float* sn, float scale, float* pos, float* rot) {
+// Front end of W channels d0..d0+W-1 (W even, d0 a multiple of W, so every RoPE pair is
+// inside).
+template <int W>
+__device__ __forceinline__ void prep_w(const float* x, float inv, const float* w, const float* cs,
+                                       const float* sn, float scale, float* pos, float* rot) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < W; ++j) {
     const float y = x[j] * inv * w[j];
     pos[j] = (y > 0.f ? y : 0.f) * scale;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) rot[j] = pos[j] * cs[j] + pos[j ^ 1] * sn[j];
+  for (int j = 0; j < W; ++j) rot[j] = pos[j] * cs[j] + pos[j ^ 1] * sn[j];
+}
+
+__device__ __forceinline__ void prep8(const float* x, float inv, const float* w, const float* cs,
+                                      const float* sn, float scale, float* pos, float* rot) {
+  prep_w<8>(x, inv, w, cs, sn, scale, pos, rot);
 }
 
 __device__ __forceinline__ void store8(bf16* p, const float* x) {
@@ -128,12 +135,13 @@ __global__ __launch_bounds__(kPrepThreads) void rms_prep_kernel(const PrepParams
   }
 }
 
-// Workspace layouts of G and U (written by frame_stats, read by scan), per (b, h, frame):
+// Workspace layouts of G and U (written by frame_stats, read by scan), per (b, h, frame),
+// with kRT = D / 64 row tiles per scan wave and 32-column scan blocks:
 //   G: A-operand order, element (r, c) at ((((r / (D/4)) kRT + (r % (D/4)) / 16) (D/32)
-//      + c / 32) 64 + ((c / 8) % 4) 16 + r % 16) 8 + c % 8 with kRT = D / 64, so a scan
-//      lane's 16-byte operand is one load and a wave's loads are contiguous;
-//   U: accumulator order, element (r, c) at (c / 16) 16D + (((r / (D/4)) kRT
-//      + (r % (D/4)) / 16) 64 + ((r % 16) / 4) 16 + c % 16) 4 + r % 4.
+//      + c / 32) 64 + ((c / 8) % 4) 16 + r % 16) 8 + c % 8, so a scan lane's 16-byte
+//      operand is one load and a wave's loads are contiguous;
+//   U: accumulator order, element (r, c) at (c / 32) 32D + ((((r / (D/4)) kRT
+//      + (r % (D/4)) / 16) 2 + (c % 32) / 16) 64 + ((r % 16) / 4) 16 + c % 16) 4 + r % 4.
 template <int D>
 __device__ __forceinline__ long g_lane_index(int r, int c) {
   constexpr int kRT = D / 64;
@@ -143,8 +151,9 @@ __device__ __forceinline__ long g_lane_index(int r, int c) {
 template <int D>
 __device__ __forceinline__ long u_lane_index(int r, int c) {
   constexpr int kRT = D / 64;
-  return (long)(c >> 4) * (16 * D) +
-         (((long)(r / (D / 4)) * kRT + (r % (D / 4)) / 16) * 64 + ((r & 15) >> 2) * 16 + (c & 15)) * 4 +
+  return (long)(c >> 5) * (32 * D) +
+         ((((long)(r / (D / 4)) * kRT + (r % (D / 4)) / 16) * 2 + ((c >> 4) & 1)) * 64 +
+          ((r & 15) >> 2) * 16 + (c & 15)) * 4 +
          (r & 3);
 }
 
@@ -351,32 +360,55 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
 }
 
 // ---- scan -------------------------------------------------------------------------------
-// One workgroup per (b, h, 16-column block cb) of the state, plus one (cb == D/16) for z: z
-// runs as a 16-column block whose columns all hold z (A operand Gz, U the uz entries of each
-// row), so both share this code.  Wave w owns state rows (D/4)w .. (D/4)w + D/4 - 1 of the
-// block.  The state lives in registers (fp32) and is exchanged through LDS (fp16 transposed
-// copy, double-buffered so one barrier per frame suffices) as the B operand of G S.
+// The forward and reverse scans are independent, so they run in separate workgroups: per
+// (b, h, direction), one workgroup per 32-column block cb of the state plus one (cb == D/32)
+// for z, which runs as a block whose columns all hold z (A operand Gz, U the uz entries of
+// each row).  The forward scan writes S_f^T after absorbing frame f; the reverse scan writes
+// R_f^T, built from frames > f (R_{F-1} = 0), both fp16 (z and zR in fp32); the output
+// kernel adds the two.  Wave w owns state rows (D/4)w .. (D/4)w + D/4 - 1 of the block.
+// The state lives in registers (fp32) and is exchanged through LDS (fp16 transposed copy,
+// double-buffered so one barrier per frame suffices) as the B operand of G S.
 //
 // Operands are staged per wave in a three-frame LDS ring by direct-to-LDS transfers issued
 // two frames ahead; each wave reads back only what it transferred (at its own lane slots, so
 // without bank conflicts), so a counted wait on its own loads is the only synchronisation.
-// A ring stage holds, per wave: the lane-ordered G (or Gz) operands (kNG KB), the U tile
-// (kRT KB), in the reverse pass the forward state of the frame being written (kRT KB), and
-// the frame's decay (256 B).
+// A ring stage holds, per wave, the lane-ordered G (or Gz) operands (kNG KB) and the U tiles
+// (kRT kCT KB).  A lane holds the decays of 64 consecutive steps and reads the current one by
+// lane index.
 template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   using namespace dma;
-  constexpr int kRT = D / 64;                            // 16-row tiles per wave
-  constexpr int kNG = kRT * (D / 32);                    // 1 KB G transfers per wave and frame
-  constexpr int kStage = (kNG + 2 * kRT) * 1024 + 256;   // bytes per wave and ring stage
-  constexpr int kLd = kNG + kRT + 1;                     // forward loads per frame
-  constexpr int kLdR = kLd + kRT;                        // reverse loads per frame (+ S_f)
-  constexpr int kSP = D + 8;  // padded st row: the 16 rows of a B-operand read hit distinct banks
+  constexpr int kRT = D / 64;                  // 16-row tiles per wave
+  constexpr int kCT = 2;                       // 16-column tiles per block
+  constexpr int kNG = kRT * (D / 32);          // 1 KB G transfers per wave and frame
+  constexpr int kStage = (kNG + kRT * kCT) * 1024;  // bytes per wave and ring stage
+  constexpr int kLd = kNG + kRT * kCT;         // loads per frame
+  constexpr int kNB = 2 * (D / 32 + 1);        // workgroups per (b, h)
   __shared__ __attribute__((aligned(1024))) char ring[4 * 3 * kStage];
-  __shared__ __attribute__((aligned(16))) f16 st[2][16 * kSP];  // state^T as fp16 operand
-  const int cb = blockIdx.x % (D / 16 + 1);
-  const int bh = blockIdx.x / (D / 16 + 1);
-  const bool zb = cb == D / 16;
+  // state^T as fp16 operand, [32 columns][D rows].  For D = 128 the 16-byte chunks of a row
+  // are XOR-swizzled by the column, so the 16 columns of a B-operand read hit distinct banks
+  // without padding (the ring and both buffers then fill the 160 KB exactly); for D = 64 rows
+  // are padded instead.
+  constexpr int kSP = D == 128 ? D : D + 8;
+  __shared__ __attribute__((aligned(16))) f16 st[2][32 * kSP];
+  auto st_idx = [](int c, int r) {
+    if constexpr (D == 128) return c * kSP + ((((r >> 3) ^ (c & 15)) << 3) | (r & 7));
+    else return c * kSP + r;
+  };
+  // Workgroups are dealt to the eight XCDs round-robin by index; when B*H is a multiple of
+  // eight, the workgroups of one (b, h) are given indices on one XCD, so a frame's G (read by
+  // all of them) comes from that XCD's L2 after the first read.
+  int slot, bh;
+  if (p.B * p.H % 8 == 0) {
+    const int s8 = blockIdx.x / 8;
+    bh = blockIdx.x % 8 + 8 * (s8 / kNB);
+    slot = s8 % kNB;
+  } else {
+    slot = blockIdx.x % kNB;
+    bh = blockIdx.x / kNB;
+  }
+  const int rev = slot & 1, cb = slot >> 1;
+  const bool zb = cb == D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
@@ -384,212 +416,241 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   const long mat0 = (long)bh * F * D * D;
   auto clampf = [&](int fa) { return fa < 0 ? 0 : (fa >= F ? F - 1 : fa); };
   auto row_of = [&](int t, int e) { return (D / 4) * wave + 16 * t + 4 * lq + e; };
+  // step i absorbs frame fr(i) and gives the state of frame fr(i) (forward) or fr(i) - 1
+  // (reverse)
+  const int nsteps = rev ? F - 1 : F;
+  auto fr = [&](int i) { return clampf(rev ? F - 1 - i : i); };
 
   // sources (every byte count below fits 32 bits: F <= 65535 and D <= 128)
   const i32x4 rG = make_rsrc(zb ? p.Gz + mat0 : p.G + mat0, (uint32_t)F * D * D * 2);
   const i32x4 rU = zb ? make_rsrc(p.uz + (long)bh * F * D, (uint32_t)F * D * 4)
                       : make_rsrc(p.U + mat0, (uint32_t)F * D * D * 4);
-  const long fst = zb ? 16 * D : (long)D * D;  // floats between frames of the forward states
-  float* sfw = zb ? p.Zf + (long)bh * F * 16 * D : p.Sf + mat0 + cb * 16 * D;
-  const i32x4 rS = make_rsrc(sfw, (uint32_t)((F - 1) * fst + 16 * D) * 4);
-  const i32x4 rD = make_rsrc(p.decay + (long)bh * F, (uint32_t)F * 4);
   const uint32_t vU = zb ? 16 * lq : 16 * lane;
   const uint32_t ringw = lds_addr(ring) + wave * 3 * kStage;
-  // transfers of frame fa (and, in the reverse pass, forward state fs) into ring stage stg
-  auto issue = [&](int fa, int stg, bool with_sf, int fs) {
-    fa = clampf(fa);
+  // transfers of frame fa into ring stage stg
+  auto issue = [&](int fa, int stg) {
     const uint32_t sb = ringw + stg * kStage;
 #pragma unroll
-    for (int n = 0; n < kNG; ++n) dma16(rG, 16 * lane, (uint32_t)fa * (D * D * 2) + (wave * kNG + n) * 1024, sb + n * 1024);
+    for (int n = 0; n < kNG; ++n)
+      dma16(rG, 16 * lane, (uint32_t)fa * (D * D * 2) + (wave * kNG + n) * 1024, sb + n * 1024);
 #pragma unroll
-    for (int t = 0; t < kRT; ++t) {
-      const uint32_t so = zb ? ((uint32_t)fa * D + (D / 4) * wave + 16 * t) * 4
-                             : (uint32_t)fa * (D * D * 4) + cb * 64 * D + (wave * kRT + t) * 1024;
-      dma16(rU, vU, so, sb + (kNG + t) * 1024);
-    }
-    dma4(rD, 0, (uint32_t)fa * 4, sb + (kNG + 2 * kRT) * 1024);
-    if (with_sf) {
-      fs = clampf(fs);
+    for (int t = 0; t < kRT; ++t)
 #pragma unroll
-      for (int t = 0; t < kRT; ++t)
-        dma16(rS, 16 * lane, (uint32_t)(fs * fst * 4) + (wave * kRT + t) * 1024, sb + (kNG + kRT + t) * 1024);
-    }
+      for (int ct = 0; ct < kCT; ++ct) {
+        const uint32_t so = zb ? ((uint32_t)fa * D + (D / 4) * wave + 16 * t) * 4
+                               : (uint32_t)fa * (D * D * 4) + cb * 128 * D + ((wave * kRT + t) * kCT + ct) * 1024;
+        dma16(rU, vU, so, sb + (kNG + t * kCT + ct) * 1024);
+      }
   };
-  auto stage_ptr = [&](int stg) { return ring + (wave * 3 + stg) * kStage; };
 
-  f32x4 s[kRT];
+  f32x4 s[kRT][kCT];
 #pragma unroll
-  for (int t = 0; t < kRT; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < kRT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) s[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   // s <- d (s - G s) + U with the operands of ring stage stg; writes and reads st[ph]
-  auto step = [&](int stg, int ph) {
-    const char* sb = stage_ptr(stg);
+  auto step = [&](int stg, int ph, float dcy) {
+    const char* sb = ring + (wave * 3 + stg) * kStage;
     f16x8 ga[kRT][D / 32];
-    f32x4 uu[kRT];
+    f32x4 uu[kRT][kCT];
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
 #pragma unroll
       for (int k = 0; k < D / 32; ++k)
         ga[t][k] = *reinterpret_cast<const f16x8*>(sb + (t * (D / 32) + k) * 1024 + 16 * lane);
-      uu[t] = *reinterpret_cast<const f32x4*>(sb + (kNG + t) * 1024 + 16 * lane);
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+        uu[t][ct] = *reinterpret_cast<const f32x4*>(sb + (kNG + t * kCT + ct) * 1024 + 16 * lane);
     }
-    const float dcy = *reinterpret_cast<const float*>(sb + (kNG + 2 * kRT) * 1024 + 4 * lane);
     f16* sp = st[ph];
-#pragma unroll
-    for (int t = 0; t < kRT; ++t) {
-      f16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (f16)s[t][e];
-      *reinterpret_cast<f16x4*>(sp + li * kSP + row_of(t, 0)) = v;
-    }
-    __syncthreads();
-    f32x4 gs[kRT];
-#pragma unroll
-    for (int t = 0; t < kRT; ++t) {
-      gs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < D / 32; ++k) gs[t] = mma16(ga[t][k], lds8(sp + li * kSP + 32 * k + 8 * lq), gs[t]);
-    }
 #pragma unroll
     for (int t = 0; t < kRT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[t][e] = dcy * (s[t][e] - gs[t][e]) + uu[t][e];
+      for (int ct = 0; ct < kCT; ++ct) {
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (f16)s[t][ct][e];
+        *reinterpret_cast<f16x4*>(sp + st_idx(16 * ct + li, row_of(t, 0))) = v;
+      }
+    __syncthreads();
+    f32x4 gs[kRT][kCT];
+#pragma unroll
+    for (int t = 0; t < kRT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) gs[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k)
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        const f16x8 bq = lds8(sp + st_idx(16 * ct + li, 32 * k + 8 * lq));
+#pragma unroll
+        for (int t = 0; t < kRT; ++t) gs[t][ct] = mma16(ga[t][k], bq, gs[t][ct]);
+      }
+#pragma unroll
+    for (int t = 0; t < kRT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[t][ct][e] = dcy * (s[t][ct][e] - gs[t][ct][e]) + uu[t][ct][e];
   };
-  // output of frame fa: s + add (the forward state), as fp16 (S + R)^T -- four consecutive
-  // rows of one column per lane, 8 bytes -- or, for z, fp32 entries of column 0
-  auto store_sum = [&](int fa, const f32x4* add) {
+  // the state of frame fa: fp16 transposed (four consecutive rows of one column per lane,
+  // 8 bytes) or, for z, fp32 entries of column 0
+  _Float16* sdt = p.SdT + (long)rev * p.B * p.H * F * D * D + mat0;
+  float* zd = p.zd + ((long)rev * p.B * p.H + bh) * F * D;
+  auto store_state = [&](int fa) {
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
-      f32x4 tot;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tot[e] = s[t][e] + (add ? add[t][e] : 0.f);
       if (zb) {
-        if (li == 0) *reinterpret_cast<f32x4*>(p.zsum + ((long)bh * F + fa) * D + row_of(t, 0)) = tot;
+        if (li == 0) *reinterpret_cast<f32x4*>(zd + (long)fa * D + row_of(t, 0)) = s[t][0];
       } else {
-        f16x4 h;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = (f16)tot[e];
-        *reinterpret_cast<f16x4*>(p.SsumT + mat0 + (long)fa * D * D + (long)(cb * 16 + li) * D + row_of(t, 0)) = h;
+        for (int ct = 0; ct < kCT; ++ct) {
+          f16x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (f16)s[t][ct][e];
+          *reinterpret_cast<f16x4*>(sdt + (long)fa * D * D + (long)(cb * 32 + 16 * ct + li) * D + row_of(t, 0)) = h;
+        }
       }
     }
   };
 
-  // forward: S_f after absorbing frame f (ring stage f % 3), kept in fp32 in the workspace in
-  // the per-lane tile order
-  issue(0, 0, false, 0);
-  issue(1, 1, false, 0);
-  for (int f = 0; f < F; ++f) {
-    issue(f + 2, (f + 2) % 3, false, 0);
-    wait_vm<2 * kLd>();  // frame f's loads are done once only frames f+1, f+2 may be pending
-    step(f % 3, f & 1);
-#pragma unroll
-    for (int t = 0; t < kRT; ++t)
-      *reinterpret_cast<f32x4*>(sfw + (long)f * fst + (wave * kRT + t) * 256 + 4 * lane) = s[t];
-  }
-  // frame F-1 reads R_{F-1} = 0: its sum is the forward state itself
-  store_sum(F - 1, nullptr);
-  // the reverse pass reads the forward states back and restarts the st phases: every store
-  // of this wave has landed and every wave is past its last forward read
-  wait_vm0();
-  __syncthreads();
-  // reverse: step i absorbs frame F-1-i and gives R of frame F-2-i, whose forward state comes
-  // in the same ring stage (i % 3)
-#pragma unroll
-  for (int t = 0; t < kRT; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  issue(F - 1, 0, true, F - 2);
-  issue(F - 2, 1, true, F - 3);
-  for (int i = 0; i < F - 1; ++i) {
-    issue(F - 3 - i, (i + 2) % 3, true, F - 4 - i);
-    wait_vm<2 * kLdR>();
-    step(i % 3, i & 1);
-    f32x4 sf[kRT];
-#pragma unroll
-    for (int t = 0; t < kRT; ++t)
-      sf[t] = *reinterpret_cast<const f32x4*>(stage_ptr(i % 3) + (kNG + kRT + t) * 1024 + 16 * lane);
-    store_sum(F - 2 - i, sf);
+  if (rev) store_state(F - 1);  // R_{F-1} = 0
+  issue(fr(0), 0);
+  issue(fr(1), 1);
+  float dv = 0.f;  // lane j: the decay of step (i & ~63) + j
+  for (int i = 0; i < nsteps; ++i) {
+    if ((i & 63) == 0) dv = p.decay[(long)bh * F + fr(i + lane)];
+    issue(fr(i + 2), (i + 2) % 3);
+    wait_vm<2 * kLd>();  // step i's loads are done once only those of steps i+1, i+2 may be pending
+    const float dcy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dv), i & 63));
+    step(i % 3, i & 1, dcy);
+    store_state(rev ? F - 2 - i : i);
   }
   // no transfer may still be writing the ring when the workgroup ends
   wait_vm0();
 }
 
 // ---- output -----------------------------------------------------------------------------
-// One workgroup per (b, h, group of `grp` consecutive 64-token blocks of one frame):
-// num = Q_rot (S + R), den = Q_pos . (z + zR).  The frame's (S + R)^T is loaded once per group.
-// num is formed transposed (the state rows as the A operand) so a lane's accumulator holds
-// four consecutive value columns of one token: 8-byte stores.
-template <int D>
+// One workgroup per (b, group of kHW heads, frame f, group of grp consecutive 64-token blocks
+// of f): num = Q_rot (S + R), den = Q_pos . (z + zR).  Wave w forms value columns
+// (D/4)w .. (D/4)w + D/4 - 1 of every token: its slice of each head's (S + R)^T is the A
+// operand, summed from the two directions' fp16 states into registers once per workgroup; the prepped Q_rot rows are the B operand,
+// from LDS.  The accumulator of lane (li, lq) holds four consecutive value columns of token li
+// (8-byte stores).  A thread's (token, octet) items keep one octet, so its norm weights load
+// once, and the RoPE tables and inverse RMS of an item load once for all kHW heads.
+// (Measured on the 16-frame video block: two heads and four blocks per workgroup beat one
+// head or other block counts; issuing the next block's loads before the products, or using
+// 4-channel items, did not help.)
+template <int D, int kHW>
 __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) {
-  __shared__ __attribute__((aligned(16))) f16 sT[D][D + 8];  // (S + R)^T, row = value column
-  __shared__ __attribute__((aligned(16))) f16 qr[64][D + 8];  // Q_rot rows
-  __shared__ float zsum[D];
-  __shared__ float den_part[64];
-  const int nblk = p.N / 64, ngrp = nblk / grp;
-  const int g = blockIdx.x % ngrp;
-  const int bh = blockIdx.x / ngrp;
-  const int b = bh / p.H, h = bh % p.H;
-  const int f = (g * grp * 64) / p.S;
+  constexpr int kOct = D / 8, kItems = 64 * kOct / 256, kCT = D / 64, kSP = D + 8;
+  __shared__ __attribute__((aligned(16))) f16 qr[kHW][64 * kSP];  // Q_rot rows, padded
+  __shared__ float zsum[kHW][D];
+  __shared__ float den_part[kHW][64];
+  const int ngrp = (p.S / 64) / grp;
+  int x = blockIdx.x;
+  const int g = x % ngrp;
+  x /= ngrp;
+  const int f = x % p.F;
+  x /= p.F;
+  const int h0 = (x % (p.H / kHW)) * kHW, b = x / (p.H / kHW);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
-  const int C = p.H * D;
-  const long mat = ((long)bh * p.F + f) * D * D;
-  for (int e = tid; e < D * D / 8; e += 256) {
-    const int r = e / (D / 8), c0 = (e % (D / 8)) * 8;
-    *reinterpret_cast<uint4*>(&sT[r][c0]) = *reinterpret_cast<const uint4*>(p.SsumT + mat + (long)r * D + c0);
-  }
-  if (tid < D) zsum[tid] = p.zsum[((long)bh * p.F + f) * D + tid];
+  const int C = p.H * D, o = tid % kOct;
   const bf16* qkv = static_cast<const bf16*>(p.qkv);
   bf16* num = static_cast<bf16*>(p.num);
-  for (int blk = g * grp; blk < (g + 1) * grp; ++blk) {
-    const int n0 = blk * 64;
-    __syncthreads();
-    // prep of q: 64 tokens x D/8 octets over 256 threads; every load of this thread's items
-    // is issued before any of them is used
-    constexpr int kItems = 64 * (D / 8) / 256;
-    float x[kItems][8], w[kItems][8], cs[kItems][8], sn[kItems][8], inv[kItems];
+  f16x8 sa[kHW][kCT][D / 32];
+  float w[kHW][8];
+  const long dir_m = (long)p.B * p.H * p.F * D * D, dir_v = (long)p.B * p.H * p.F * D;
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int e = tid + 256 * i, t = e / (D / 8), d0 = (e % (D / 8)) * 8;
-      const long n = n0 + t, bn = (long)b * p.N + n;
-      load8f(qkv + bn * 3L * C + (long)h * D + d0, x[i]);
-      load8f(p.q_norm_w + h * D + d0, w[i]);
-      load8f(p.rope_cos + n * D + d0, cs[i]);
-      load8f(p.rope_sin + n * D + d0, sn[i]);
-      inv[i] = p.q_inv_rms[bn];
-    }
+  for (int hh = 0; hh < kHW; ++hh) {
+    const long bhf = ((long)b * p.H + h0 + hh) * p.F + f;
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int e = tid + 256 * i, t = e / (D / 8), d0 = (e % (D / 8)) * 8;
-      float pos[8], rot[8];
-      prep8(x[i], inv[i], w[i], cs[i], sn[i], 1.f, pos, rot);
-      f16x8 v;
-      float dp = 0.f;
+    for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v[j] = (f16)rot[j];
-        dp += pos[j] * zsum[d0 + j];
+      for (int k = 0; k < D / 32; ++k) {
+        const long e = bhf * D * D + (long)((D / 4) * wave + 16 * ct + li) * D + 32 * k + 8 * lq;
+        const f16x8 sf = *reinterpret_cast<const f16x8*>(p.SdT + e);
+        const f16x8 sr = *reinterpret_cast<const f16x8*>(p.SdT + dir_m + e);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sa[hh][ct][k][j] = (f16)((float)sf[j] + (float)sr[j]);
       }
-      *reinterpret_cast<f16x8*>(&qr[t][d0]) = v;
-      // den partial: reduce over the D/8 octets of token t (consecutive e)
+    if (tid < D) zsum[hh][tid] = p.zd[bhf * D + tid] + p.zd[dir_v + bhf * D + tid];
+    load8f(p.q_norm_w + (h0 + hh) * D + 8 * o, w[hh]);
+  }
+  for (int blk = g * grp; blk < (g + 1) * grp; ++blk) {
+    const int n0 = f * p.S + blk * 64;
+    __syncthreads();  // the previous block's qr and den_part reads are done
+    // every load of this thread's items is issued before any of them is used
+    float cs[kItems][8], sn[kItems][8], inv[kItems];
+    bf16x8 qx[kItems][kHW];
 #pragma unroll
-      for (int off = 1; off < D / 8; off <<= 1) dp += __shfl_xor(dp, off, 64);
-      if ((e % (D / 8)) == 0) den_part[t] = dp;
+    for (int i = 0; i < kItems; ++i) {
+      const int t = tid / kOct + (256 / kOct) * i;
+      const long n = n0 + t, bn = (long)b * p.N + n;
+      load8f(p.rope_cos + n * D + 8 * o, cs[i]);
+      load8f(p.rope_sin + n * D + 8 * o, sn[i]);
+      inv[i] = p.q_inv_rms[bn];
+#pragma unroll
+      for (int hh = 0; hh < kHW; ++hh)
+        qx[i][hh] = *reinterpret_cast<const bf16x8*>(qkv + bn * 3L * C + (long)(h0 + hh) * D + 8 * o);
+    }
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int t = tid / kOct + (256 / kOct) * i;
+#pragma unroll
+      for (int hh = 0; hh < kHW; ++hh) {
+        float xq[8], pos[8], rot[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xq[j] = (float)qx[i][hh][j];
+        prep8(xq, inv[i], w[hh], cs[i], sn[i], 1.f, pos, rot);
+        f16x8 v;
+        float dp = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          v[j] = (f16)rot[j];
+          dp += pos[j] * zsum[hh][8 * o + j];
+        }
+        *reinterpret_cast<f16x8*>(&qr[hh][t * kSP + 8 * o]) = v;
+        // den: reduce over the kOct consecutive threads of token t
+#pragma unroll
+        for (int off = 1; off < kOct; off <<= 1) dp += __shfl_xor(dp, off, 64);
+        if (o == 0) den_part[hh][t] = dp;
+      }
     }
     __syncthreads();
-    // num^T: wave w -> tokens 16w..16w+15 (column li of the accumulator), all D value columns
-    const long n = n0 + 16 * wave + li;
-    bf16* orow = num + (((long)b * p.N + n) * p.H + h) * D;
 #pragma unroll
-    for (int ct = 0; ct < D / 16; ++ct) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < kHW; ++hh) {
+      f32x4 acc[4][kCT];
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32)
-        acc = mma16(lds8(&sT[16 * ct + li][k0 + 8 * lq]), lds8(&qr[16 * wave + li][k0 + 8 * lq]), acc);
-      typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-      bf16x4_t o4;
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (bf16)acc[e];
-      *reinterpret_cast<bf16x4_t*>(orow + 16 * ct + 4 * lq) = o4;
+        for (int ct = 0; ct < kCT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+          const f16x8 bq = lds8(&qr[hh][(16 * tt + li) * kSP + 32 * k + 8 * lq]);
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct) acc[tt][ct] = mma16(sa[hh][ct][k], bq, acc[tt][ct]);
+        }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        bf16* orow = num + (((long)b * p.N + n0 + 16 * tt + li) * p.H + h0 + hh) * D + (D / 4) * wave + 4 * lq;
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) {
+          typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+          bf16x4_t o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (bf16)acc[tt][ct][e];
+          *reinterpret_cast<bf16x4_t*>(orow + 16 * ct) = o4;
+        }
+      }
     }
-    if (tid < 64) static_cast<bf16*>(p.den)[(long)bh * p.N + n0 + tid] = (bf16)den_part[tid];
+    if (tid < 64 * kHW) {
+      const int hh = tid / 64, t = tid % 64;
+      static_cast<bf16*>(p.den)[((long)b * p.H + h0 + hh) * p.N + n0 + t] = (bf16)den_part[hh][t];
+    }
   }
 }
 
@@ -618,16 +679,23 @@ hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream) {
   hipError_t e = launch_prep(pp, stream);
   if (e != hipSuccess) return e;
   const int nbhf = p.B * p.H * p.F;
-  // 64-token blocks per output workgroup (a divisor of the blocks of a frame)
-  const int grp = 1;
+  // 64-token blocks per output workgroup: the largest divisor of a frame's blocks up to 4;
+  // two heads per output workgroup when H is even
+  const int nblk = p.S / 64;
+  int grp = 4;
+  while (nblk % grp) grp >>= 1;
+  const int hw = p.H % 2 ? 1 : 2;
+  const dim3 og(p.B * (p.H / hw) * p.F * (nblk / grp));
   if (p.D == 128) {
     hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
-    hipLaunchKernelGGL(scan_kernel<128>, dim3(p.B * p.H * (128 / 16 + 1)), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(out_kernel<128>, dim3(p.B * p.H * (p.N / 64 / grp)), dim3(256), 0, stream, p, grp);
+    hipLaunchKernelGGL(scan_kernel<128>, dim3(p.B * p.H * 2 * (128 / 32 + 1)), dim3(256), 0, stream, p);
+    if (hw == 2) hipLaunchKernelGGL((out_kernel<128, 2>), og, dim3(256), 0, stream, p, grp);
+    else hipLaunchKernelGGL((out_kernel<128, 1>), og, dim3(256), 0, stream, p, grp);
   } else {
     hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
-    hipLaunchKernelGGL(scan_kernel<64>, dim3(p.B * p.H * (64 / 16 + 1)), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(out_kernel<64>, dim3(p.B * p.H * (p.N / 64 / grp)), dim3(256), 0, stream, p, grp);
+    hipLaunchKernelGGL(scan_kernel<64>, dim3(p.B * p.H * 2 * (64 / 32 + 1)), dim3(256), 0, stream, p);
+    if (hw == 2) hipLaunchKernelGGL((out_kernel<64, 2>), og, dim3(256), 0, stream, p, grp);
+    else hipLaunchKernelGGL((out_kernel<64, 1>), og, dim3(256), 0, stream, p, grp);
   }
   return hipGetLastError();
 }

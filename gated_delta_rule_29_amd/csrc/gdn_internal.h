@@ -76,10 +76,8 @@ struct BigdnParams {
   _Float16* Gz;      // [B, H, F, D, D]
   float* U;          // [B, H, F, D, D]
   float* uz;         // [B, H, F, D]
-  float* Sf;         // [B, H, F, D, D]  forward states
-  float* Zf;         // [B, H, F, 16 D]  forward z (16 identical columns)
-  _Float16* SsumT;   // [B, H, F, D, D]  (S_f + R_f)^T
-  float* zsum;       // [B, H, F, D]
+  _Float16* SdT;     // [2, B, H, F, D, D]  S_f^T (forward) and R_f^T (reverse)
+  float* zd;         // [2, B, H, F, D]     z_f and zR_f
 };
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
