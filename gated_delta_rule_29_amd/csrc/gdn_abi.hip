@@ -177,7 +177,7 @@ namespace {
 
 // bigdn_fwd workspace: every view 256-byte aligned, in the order of BigdnParams.
 struct BigdnWs {
-  size_t q_rms, k_rms, G, Gz, U, uz, SdT, zd, total;
+  size_t q_rms, k_rms, rope_h, G, Gz, U, uz, SdT, zd, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -188,6 +188,7 @@ BigdnWs bigdn_ws(int B, int F, int S, int H, int D) {
   size_t off = 0;
   w.q_rms = off; off = al256(off + (size_t)B * N * 4);
   w.k_rms = off; off = al256(off + (size_t)B * N * 4);
+  w.rope_h = off; off = al256(off + N * D * 4);
   w.G = off; off = al256(off + mats * 2);
   w.Gz = off; off = al256(off + mats * 2);
   w.U = off; off = al256(off + mats * 4);
@@ -263,6 +264,7 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
   p.num = num; p.den = den; p.B = B; p.F = F; p.S = S; p.H = H; p.D = D; p.N = N;
   p.q_inv_rms = reinterpret_cast<float*>(ws + w.q_rms);
   p.k_inv_rms = reinterpret_cast<float*>(ws + w.k_rms);
+  p.rope_h = reinterpret_cast<_Float16*>(ws + w.rope_h);
   p.G = reinterpret_cast<_Float16*>(ws + w.G);
   p.Gz = reinterpret_cast<_Float16*>(ws + w.Gz);
   p.U = reinterpret_cast<float*>(ws + w.U);

@@ -34,14 +34,21 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 
-__device__ __forceinline__ float block_sum_256(float x, float* red) {
+// Sums of x and y over a 256-thread workgroup (every thread gets both).
+__device__ __forceinline__ void block_sum2_256(float& x, float& y, float* red) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  for (int off = 32; off > 0; off >>= 1) {
+    x += __shfl_xor(x, off, 64);
+    y += __shfl_xor(y, off, 64);
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    red[wave] = x;
+    red[4 + wave] = y;
+  }
   __syncthreads();
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+  x = red[0] + red[1] + red[2] + red[3];
+  y = red[4] + red[5] + red[6] + red[7];
 }
 
 // Loads 8 consecutive channels (16 bytes) of bf16 as floats.
@@ -95,6 +102,14 @@ __global__ __launch_bounds__(kPrepThreads) void rms_prep_kernel(const PrepParams
   const int b = bn / p.N, n = bn % p.N;
   const int C = p.H * p.D, groups = C / 8;
   const bf16* row = static_cast<const bf16*>(p.qkv) + bn * 3L * C;
+  // the RoPE tables of token n as (cos, sin) fp16 pairs, 8 channels (32 bytes) per thread;
+  // loaded before the reductions so the loads overlap them
+  const bool tab = p.rope_h && b == 0 && threadIdx.x < p.D / 8;
+  float cs[8], sn[8];
+  if (tab) {
+    load8f(p.rope_cos + (long)n * p.D + 8 * threadIdx.x, cs);
+    load8f(p.rope_sin + (long)n * p.D + 8 * threadIdx.x, sn);
+  }
   float sq = 0.f, sk = 0.f;
   for (int gi = threadIdx.x; gi < groups; gi += kPrepThreads) {
     float xq[8], xk[8];
@@ -106,12 +121,24 @@ __global__ __launch_bounds__(kPrepThreads) void rms_prep_kernel(const PrepParams
       sk += xk[j] * xk[j];
     }
   }
-  sq = block_sum_256(sq, red);
-  sk = block_sum_256(sk, red + 4);
+  block_sum2_256(sq, sk, red);
   const float iq = rsqrtf(sq / (float)C + p.eps), ik = rsqrtf(sk / (float)C + p.eps);
   if (threadIdx.x == 0) {
     if (p.q_inv_rms) p.q_inv_rms[bn] = iq;
     if (p.k_inv_rms) p.k_inv_rms[bn] = ik;
+  }
+  if (tab) {
+    f16x8 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[2 * j] = (f16)cs[j];
+      lo[2 * j + 1] = (f16)sn[j];
+      hi[2 * j] = (f16)cs[4 + j];
+      hi[2 * j + 1] = (f16)sn[4 + j];
+    }
+    f16x8* dst = reinterpret_cast<f16x8*>(p.rope_h + ((long)n * p.D + 8 * threadIdx.x) * 2);
+    dst[0] = lo;
+    dst[1] = hi;
   }
   if (!(p.q_rot || p.k_rot || p.q_pos || p.k_pos || p.v_hm)) return;
   for (int gi = threadIdx.x; gi < groups; gi += kPrepThreads) {
@@ -162,9 +189,14 @@ __device__ __forceinline__ long u_lane_index(int r, int c) {
 // frame's tokens, 64 at a time:
 //   G = K_rot^T diag(beta) K_rot,  U = K_rot^T diag(beta) V,  Gz = K_pos^T diag(beta) K_pos,
 //   uz = K_pos^T beta.
+// beta >= 0 splits as sqrt(beta) on both sides, so three fp16 token tiles serve all of them:
+// sqrt(beta) K_rot, sqrt(beta) V and sqrt(beta) K_pos.
 // Prep: every thread takes (token, 8-channel octet) items -- 16 threads per token row, so the
-// qkv loads are whole 256-byte rows -- applies the front end once and writes five fp16 token
-// rows (K_rot, beta K_rot, beta V, K_pos, beta K_pos) into LDS with 16-byte stores.
+// qkv loads are whole 256-byte rows -- applies the front end once and writes the three rows
+// into LDS with 16-byte stores.  The tiles are double-buffered: a block's prep runs while the
+// previous block's products do (one barrier per block), and an item's inputs are loaded one
+// block ahead of its prep (the RoPE table rows by direct-to-LDS transfers, which hold no
+// registers).
 // Products: wave w accumulates quadrant (w % 4) of statistic w / 4; both operands contract
 // over tokens, so they come from the row-major tiles by LDS transpose reads
 // (ds_read_b64_tr_b16: within a 16-lane group, lane n receives element j of the 8-byte piece
@@ -191,11 +223,21 @@ __device__ __forceinline__ f16x8 tr_pair(const f16* p0, const f16* p1) {
 
 template <int D>
 __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnParams p) {
+  using namespace dma;
   constexpr int kT = 64;         // tokens per block
   constexpr int kOct = D / 8;    // octets per token row
   constexpr int kNG = D / 64;    // 32-channel blocks per quadrant side
-  // tiles: 0 K_rot, 1 beta K_rot, 2 beta V, 3 K_pos, 4 beta K_pos  ([64][D] fp16, tix_x64)
-  __shared__ __attribute__((aligned(16))) f16 tl[5][kT * D];
+  // Items (token, octet) of a block: this thread takes it = tid + kStatThreads i.
+  constexpr int kItems = (kT * kOct + kStatThreads - 1) / kStatThreads;
+  constexpr int kI1 = kT * kOct > kStatThreads ? kT * kOct - kStatThreads : 0;  // threads with a 2nd item
+  // tiles: 0 sqrt(beta) K_rot, 1 sqrt(beta) V, 2 sqrt(beta) K_pos  ([64][D] fp16, tix_x64),
+  // two buffers; then the RoPE table rows of the next block's items ((cos, sin) fp16 pairs,
+  // 16-byte pieces j = channels 4j .. 4j + 3 of the octet) at the transferring lane's own slot
+  constexpr int kTiles = 2 * 3 * kT * D * 2;
+  constexpr int kTab = (2 * kStatThreads + 2 * kI1) * 16;
+  __shared__ __attribute__((aligned(1024))) char smem[kTiles + kTab];
+  typedef f16 tile_t[3][kT * D];
+  tile_t* tl = reinterpret_cast<tile_t*>(smem);
   const int bhf = blockIdx.x;
   const int f = bhf % p.F, h = (bhf / p.F) % p.H, b = bhf / (p.F * p.H);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -204,8 +246,7 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
   const int C = p.H * D;
   const bf16* qkv = static_cast<const bf16*>(p.qkv);
   const int m = wave >> 2, qi = (wave & 3) >> 1, qj = wave & 1;
-  const f16* ta = tl[m == 2 ? 3 : 0];
-  const f16* tb = tl[m == 0 ? 1 : (m == 1 ? 2 : 4)];
+  const int ta = m == 2 ? 2 : 0, tb = m;  // operand tiles of statistic m
   f32x4 acc[kNG][2][kNG][2];
 #pragma unroll
   for (int a = 0; a < kNG; ++a)
@@ -217,87 +258,85 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
         for (int u = 0; u < 2; ++u) acc[a][t][c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   // this thread's octet (fixed: kStatThreads is a multiple of kOct) and running beta k_pos
   const int oct = tid % kOct;
-  float uzr[8];
+  float uzr[8], w8[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) uzr[j] = 0.f;
+  load8f(p.k_norm_w + h * D + 8 * oct, w8);
 
-  // Items (token, octet) of a block: this thread takes it = tid + kStatThreads i.  The k, v
-  // rows, inverse RMS and beta of its first item are loaded one block ahead (in flight during
-  // the products of the block before); the RoPE tables, shared by every head, and a second
-  // item's rows are loaded when used.
-  constexpr int kItems = (kT * kOct + kStatThreads - 1) / kStatThreads;
-  bf16x8 kx, vx;
-  float ivx = 0.f, btx = 0.f;
-  auto load_items = [&](int t0) {
-    const int it = tid;
-    if (it < kT * kOct && t0 < p.S) {
-      const int s = it / kOct;
-      const long bn = (long)b * p.N + (long)f * p.S + t0 + s;
-      const bf16* krow = qkv + bn * 3L * C + C + (long)h * D + 8 * oct;
-      kx = *reinterpret_cast<const bf16x8*>(krow);
-      vx = *reinterpret_cast<const bf16x8*>(krow + C);
-      ivx = p.k_inv_rms[bn];
-      btx = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
-    }
+  // An item's k, v rows, inverse RMS and beta are loaded into registers, and its RoPE table
+  // rows transferred into LDS, one block ahead of its prep.
+  bf16x8 kx[kItems], vx[kItems];
+  float ivx[kItems], btx[kItems];
+  const long frame_tok = (long)f * p.S;
+  const i32x4 rtab = make_rsrc(p.rope_h + frame_tok * D * 2, (uint32_t)p.S * D * 4);
+  const uint32_t tab = lds_addr(smem + kTiles);
+  auto tab_off = [&](int i, int j) {  // byte offset of piece j of item i of this thread's wave
+    return i == 0 ? (j * kStatThreads + 64 * wave) * 16 : (2 * kStatThreads + j * kI1 + 64 * wave) * 16;
   };
-  load_items(0);
-
-  for (int t0 = 0; t0 < p.S; t0 += kT) {
-    __syncthreads();
+  auto load_items = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int it = tid + kStatThreads * i;
-      if (it >= kT * kOct) continue;
-      const int s = it / kOct;
-      const long n = (long)f * p.S + t0 + s;
-      const long bn = (long)b * p.N + n;
-      bf16x8 ki, vi;
-      float ivi, bt;
-      if (i == 0) {
-        ki = kx;
-        vi = vx;
-        ivi = ivx;
-        bt = btx;
-      } else {
+      if (it < kT * kOct) {
+        const int s = it / kOct;
+        const long n = frame_tok + t0 + s, bn = (long)b * p.N + n;
         const bf16* krow = qkv + bn * 3L * C + C + (long)h * D + 8 * oct;
-        ki = *reinterpret_cast<const bf16x8*>(krow);
-        vi = *reinterpret_cast<const bf16x8*>(krow + C);
-        ivi = p.k_inv_rms[bn];
-        bt = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
-      }
-      float x[8], v[8], cs[8], sn[8], pos[8], rot[8], w8[8];
+        kx[i] = *reinterpret_cast<const bf16x8*>(krow);
+        vx[i] = *reinterpret_cast<const bf16x8*>(krow + C);
+        ivx[i] = p.k_inv_rms[bn];
+        btx[i] = p.beta[(((long)b * p.H + h) * p.F + f) * p.S + t0 + s];
+        const uint32_t vo = ((t0 + s) * D + 8 * oct) * 4;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[j] = (float)ki[j];
-        v[j] = (float)vi[j];
+        for (int j = 0; j < 2; ++j) dma16(rtab, vo + 16 * j, 0, tab + tab_off(i, j));
       }
-      load8f(p.rope_cos + n * D + 8 * oct, cs);
-      load8f(p.rope_sin + n * D + 8 * oct, sn);
-      load8f(p.k_norm_w + h * D + 8 * oct, w8);
-      prep8(x, ivi, w8, cs, sn, p.k_scale, pos, rot);
-      f16x8 r0, r1, r2, r3, r4;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        r0[j] = (f16)rot[j];
-        r1[j] = (f16)(bt * rot[j]);
-        r2[j] = (f16)(bt * v[j]);
-        r3[j] = (f16)pos[j];
-        r4[j] = (f16)(bt * pos[j]);
-        uzr[j] += bt * pos[j];
-      }
-      const int ix = tix_x64(s, 8 * oct);
-      *reinterpret_cast<f16x8*>(&tl[0][ix]) = r0;
-      *reinterpret_cast<f16x8*>(&tl[1][ix]) = r1;
-      *reinterpret_cast<f16x8*>(&tl[2][ix]) = r2;
-      *reinterpret_cast<f16x8*>(&tl[3][ix]) = r3;
-      *reinterpret_cast<f16x8*>(&tl[4][ix]) = r4;
     }
-    __syncthreads();
-    load_items(t0 + kT);
+  };
+  auto prep = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = tid + kStatThreads * i;
+      if (it < kT * kOct) {
+        const int s = it / kOct;
+        float x[8], v[8], pos[8], rot[8], cs[8], sn[8];
+        const char* tp = smem + kTiles + 16 * lane;
+        const f16x8 t0 = *reinterpret_cast<const f16x8*>(tp + tab_off(i, 0));
+        const f16x8 t1 = *reinterpret_cast<const f16x8*>(tp + tab_off(i, 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cs[j] = (float)t0[2 * j];
+          sn[j] = (float)t0[2 * j + 1];
+          cs[4 + j] = (float)t1[2 * j];
+          sn[4 + j] = (float)t1[2 * j + 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j] = (float)kx[i][j];
+          v[j] = (float)vx[i][j];
+        }
+        prep8(x, ivx[i], w8, cs, sn, p.k_scale, pos, rot);
+        const float bt = btx[i], sb = sqrtf(bt);
+        f16x8 r0, r1, r2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          r0[j] = (f16)(sb * rot[j]);
+          r1[j] = (f16)(sb * v[j]);
+          r2[j] = (f16)(sb * pos[j]);
+          uzr[j] += bt * pos[j];
+        }
+        const int ix = tix_x64(s, 8 * oct);
+        *reinterpret_cast<f16x8*>(&tl[buf][0][ix]) = r0;
+        *reinterpret_cast<f16x8*>(&tl[buf][1][ix]) = r1;
+        *reinterpret_cast<f16x8*>(&tl[buf][2][ix]) = r2;
+      }
+    }
+  };
+  auto mma_block = [&](int buf) {
+    const f16* pa = tl[buf][ta];
+    const f16* pb = tl[buf][tb];
     // lane-derived LDS addresses recomputed per block instead of held across the loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int li = ln & 15, lq = ln >> 4, trj = (ln >> 2) & 3, trc = ln & 3;
+    const int lq = ln >> 4, trj = (ln >> 2) & 3, trc = ln & 3;
 #pragma unroll
     for (int P = 0; P < kT / 32; ++P) {
       f16x8 af[kNG][2], bf[kNG][2];
@@ -307,8 +346,8 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
         for (int t = 0; t < 2; ++t) {
           const int ca = 32 * (kNG * qi + g) + 8 * trc + 4 * t;
           const int cb = 32 * (kNG * qj + g) + 8 * trc + 4 * t;
-          af[g][t] = tr_pair(&ta[tix_x64(32 * P + 8 * lq + trj, ca)], &ta[tix_x64(32 * P + 8 * lq + 4 + trj, ca)]);
-          bf[g][t] = tr_pair(&tb[tix_x64(32 * P + 8 * lq + trj, cb)], &tb[tix_x64(32 * P + 8 * lq + 4 + trj, cb)]);
+          af[g][t] = tr_pair(&pa[tix_x64(32 * P + 8 * lq + trj, ca)], &pa[tix_x64(32 * P + 8 * lq + 4 + trj, ca)]);
+          bf[g][t] = tr_pair(&pb[tix_x64(32 * P + 8 * lq + trj, cb)], &pb[tix_x64(32 * P + 8 * lq + 4 + trj, cb)]);
         }
 #pragma unroll
       for (int a = 0; a < kNG; ++a)
@@ -319,6 +358,25 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
 #pragma unroll
             for (int u = 0; u < 2; ++u) acc[a][t][c][u] = mma16(af[a][t], bf[c][u], acc[a][t][c][u]);
     }
+  };
+
+  // Block n's products run while block n + 1 is prepped into the other tile buffer and block
+  // n + 2's inputs are in flight; one barrier per block.  Everything a prep reads was issued
+  // a whole block earlier, so it waits for all of this thread's loads.
+  const int nb = p.S / kT;
+  load_items(0);
+  wait_vm0();
+  prep(0);
+  if (nb > 1) load_items(kT);
+  __syncthreads();
+  for (int n = 0; n < nb; ++n) {
+    if (n + 1 < nb) {
+      wait_vm0();
+      prep((n + 1) & 1);
+      if (n + 2 < nb) load_items((n + 2) * kT);
+    }
+    mma_block(n & 1);
+    __syncthreads();
   }
   // epilogue: row channel 32(kNG qi + a) + 8lq + 4t + e, column 32(kNG qj + c) + 8(li >> 2) + 4u + (li & 3).
   // G, Gz and U go out in the scan's operand layouts (g_lane_index, u_lane_index): U's four
@@ -347,7 +405,7 @@ __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnPa
         }
   // uz: sum of the per-thread partial sums of each channel (threads of one octet)
   __syncthreads();
-  float* red = reinterpret_cast<float*>(&tl[0][0]);  // [kStatThreads][8]
+  float* red = reinterpret_cast<float*>(smem);  // [kStatThreads][8]
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[tid * 8 + j] = uzr[j];
   __syncthreads();
@@ -582,14 +640,16 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
     const int n0 = f * p.S + blk * 64;
     __syncthreads();  // the previous block's qr and den_part reads are done
     // every load of this thread's items is issued before any of them is used
-    float cs[kItems][8], sn[kItems][8], inv[kItems];
+    float inv[kItems];
+    f16x8 tab[kItems][2];  // (cos, sin) pairs of the item's 8 channels
     bf16x8 qx[kItems][kHW];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int t = tid / kOct + (256 / kOct) * i;
       const long n = n0 + t, bn = (long)b * p.N + n;
-      load8f(p.rope_cos + n * D + 8 * o, cs[i]);
-      load8f(p.rope_sin + n * D + 8 * o, sn[i]);
+      const f16x8* tp = reinterpret_cast<const f16x8*>(p.rope_h + (n * D + 8 * o) * 2);
+      tab[i][0] = tp[0];
+      tab[i][1] = tp[1];
       inv[i] = p.q_inv_rms[bn];
 #pragma unroll
       for (int hh = 0; hh < kHW; ++hh)
@@ -598,12 +658,18 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int t = tid / kOct + (256 / kOct) * i;
+      float cs[8], sn[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cs[j] = (float)tab[i][j >> 2][2 * (j & 3)];
+        sn[j] = (float)tab[i][j >> 2][2 * (j & 3) + 1];
+      }
 #pragma unroll
       for (int hh = 0; hh < kHW; ++hh) {
         float xq[8], pos[8], rot[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) xq[j] = (float)qx[i][hh][j];
-        prep8(xq, inv[i], w[hh], cs[i], sn[i], 1.f, pos, rot);
+        prep8(xq, inv[i], w[hh], cs, sn, 1.f, pos, rot);
         f16x8 v;
         float dp = 0.f;
 #pragma unroll
@@ -672,6 +738,7 @@ hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream) {
   pp.eps = p.eps;
   pp.q_inv_rms = p.q_inv_rms;
   pp.k_inv_rms = p.k_inv_rms;
+  pp.rope_h = p.rope_h;
   pp.B = p.B;
   pp.N = p.N;
   pp.H = p.H;

@@ -54,6 +54,7 @@ struct PrepParams {
   void* q_pos;
   void* k_pos;
   void* v_hm;
+  _Float16* rope_h;  // [N, D, 2] (cos, sin) fp16 pairs, or nullptr
   int B, N, H, D;
 };
 
@@ -72,6 +73,7 @@ struct BigdnParams {
   // workspace views
   float* q_inv_rms;  // [B, N]
   float* k_inv_rms;  // [B, N]
+  _Float16* rope_h;  // [N, D, 2]  RoPE tables as (cos, sin) fp16 pairs
   _Float16* G;       // [B, H, F, D, D]
   _Float16* Gz;      // [B, H, F, D, D]
   float* U;          // [B, H, F, D, D]
