@@ -8,7 +8,7 @@
 // w and w + 4 share a SIMD):
 //
 //   waves 0, 1     state scan of chunk n for 16 value columns each (h in registers, fp32):
-//                    X_K = K h, Y = diag(beta)(V - diag(e^gamma) X_K), v_new = Tm Y,
+//                    X_K = K h, Y = V - diag(e^gamma) X_K, v_new = (Tm diag(beta)) Y,
 //                    o = scale (diag(e^gamma) Q h + P v_new),
 //                    h <- e^gl h + K^T diag(e^{gl-gamma}) v_new
 //   waves 2, 3     Gram tiles of the diagonal 16x16 blocks of chunk n+1 and their inverses;
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         f16* ptt = reinterpret_cast<f16*>(T.p);
         f16* aft = reinterpret_cast<f16*>(s.af);
         const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(G[kFast])) != 0;
-        f16x4 tc0, tc1;  // C-form (accumulator layout) of this wave's diagonal inverses
+        f16x4 tc0;  // C-form (accumulator layout) of this wave's first diagonal block of Tm
 
         // The products below take the rows of their second factor as the A operand, so a
         // lane's accumulator of tile (I, J) holds columns s = 16J + 4lq + e of row
@@ -411,7 +411,10 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) p8c[u] = cvt_f16x4(mma16x16x16(p4a[u], p4c[u], f32x4{0.f, 0.f, 0.f, 0.f}));
-            // X_{k+1} = X_k + X_k L^(2^k) in both forms (the row form of X is the C form of X^T)
+            // X_{k+1} = X_k + X_k L^(2^k) in both forms (the row form of X is the C form of X^T).
+            // The scan forms v_new = (Tm diag(beta)) (V - diag(e^gamma) K h), so the Tm it reads
+            // carries beta on its columns; the unscaled T_bb, the left factor of the block-column
+            // chains below, goes into the diagonal block of the A tile, which A leaves unused.
             f32x4 xa[2], xc[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -431,10 +434,11 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
               xc[u] = mma16x16x16(x2a16, p8c[u], xc[u]);
               xa[u] = mma16x16x16(p8c[u], x2a16, xa[u]);
               const int b0 = 16 * (2 * pq + u);
-              *reinterpret_cast<f16x4*>(&tmt[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u]);
+              const f32x4 bc = *reinterpret_cast<const f32x4*>(&G[kBeta + b0 + 4 * lq]);
+              *reinterpret_cast<f16x4*>(&aft[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u]);
+              *reinterpret_cast<f16x4*>(&tmt[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u] * bc);
             }
-            tc0 = cvt_f16x4(xc[0]);
-            tc1 = cvt_f16x4(xc[1]);
+            tc0 = cvt_f16x4(xc[0] * G[kBeta + 32 * pq + li]);
           } else {
             // ---- pq 2: off-diagonal Gram tiles -> A rows (fp16); pq 3: Q K^T tiles -> P rows
             auto tiles = [&](auto isq_c) {
@@ -498,6 +502,8 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         // Off-diagonal 16x16 blocks, one block column per chain of products (fp16 operands,
         // fp32 accumulation):  T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, with A_ik and T_ii as
         // row-form A operands from LDS and T_kj in C form (the B-operand layout) in registers.
+        // Scaling column block j by beta commutes with the chain, so seeding it with the
+        // scaled T_jj yields the scaled T_ij.
         // pq 0 takes column 0, pq 1 columns 1 and 2.
         if (pq < 2) {
           auto chain = [&](int j, f16x4 tjj) {
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
               for (int k = 0; k < i; ++k)
                 if (k >= j)
                   sacc = mma16x16x16(*reinterpret_cast<const f16x4*>(&aft[tix(16 * i + li, 16 * k + 4 * lq)]), bt[k], sacc);
-              const f16x4 tii = *reinterpret_cast<const f16x4*>(&tmt[tix(16 * i + li, 16 * i + 4 * lq)]);
+              const f16x4 tii = *reinterpret_cast<const f16x4*>(&aft[tix(16 * i + li, 16 * i + 4 * lq)]);
               const f32x4 t = mma16x16x16(tii, cvt_f16x4(sacc), f32x4{0.f, 0.f, 0.f, 0.f});
               bt[i] = cvt_f16x4(-t);
 #pragma unroll
@@ -591,7 +597,6 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       const f16* ptt = reinterpret_cast<const f16*>(T.p);
       const long tok = tok0 + (long)n * kC;
       const uint32_t rows = (uint32_t)min(kC, len - n * kC);
-      const bool more = n + 1 < nchunks;
 
       // The step is software-pipelined in stages: each stage issues the LDS reads of a later
       // stage (or of the next chunk) before its own products, and scheduling barriers keep
@@ -610,7 +615,11 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       u32x2 vv[2][2];
       lds_u16* vb[2] = {lds_base(vt + tix(8 * lq + trj, 16 * wave + 4 * trc)),
                         lds_base(vt + tix(8 * lq + 4 + trj, 16 * wave + 4 * trc))};
-      f32x4 be[2][2], eg[2][2];
+      // gate vectors through two per-lane bases (the ring sits beyond the 64 KB reach of an
+      // instruction offset from address 0): rows 8lq + c and pair rows pair_row(0, 0, li) + c
+      lds_u16* gq = lds_base(reinterpret_cast<const u16*>(vec + 8 * lq));
+      lds_u16* gp = lds_base(reinterpret_cast<const u16*>(vec + pair_row(0, 0, li)));
+      f32x4 eg[2][2];
       f32x4 xk[2][2];
 #pragma unroll
       for (int P = 0; P < 2; ++P)
@@ -629,15 +638,15 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
             for (int t = 0; t < 2; ++t) {
               const int r0 = 32 * P + 8 * lq + 4 * t;
               vv[P][t] = tr16_at(vb[t], 1024 * P);
-              be[P][t] = *reinterpret_cast<const f32x4*>(&vec[kBeta + r0]);
-              eg[P][t] = *reinterpret_cast<const f32x4*>(&vec[kEg + r0]);
+              eg[P][t] = lds_at<f32x4>(gq, 2 * (kEg + r0 - 8 * lq));
             }
         }
         if (G == kG - 1) read_q(n, ob);
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- stage 2: reads of Tm rows; Y = diag(beta) (V - diag(e^gamma) X_K) (fp16 B operand); the Q h part
+      // ---- stage 2: reads of Tm rows; Y = V - diag(e^gamma) X_K (fp16 B operand; beta is on
+      // the columns of the stored Tm); the Q h part
       // of o (value columns 4lq..4lq+3 of token pair_row(G, t, li), the state as the A
       // operand), which fills the matrix pipe while Y is formed
       f16x8 tmf[2][2][2];
@@ -667,7 +676,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                by[P][4 * t + e] = (f16)(be[P][t][e] * (bf_at(vv[P][t], e) - eg[P][t][e] * xk[P][t][e]));
+                by[P][4 * t + e] = (f16)(bf_at(vv[P][t], e) - eg[P][t][e] * xk[P][t][e]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -688,8 +697,8 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       f32x4 l0[2], l1[2];
 #pragma unroll
       for (int P = 0; P < 2; ++P) {
-        l0[P] = *reinterpret_cast<const f32x4*>(&vec[kEl + 32 * P + 8 * lq]);
-        l1[P] = *reinterpret_cast<const f32x4*>(&vec[kEl + 32 * P + 8 * lq + 4]);
+        l0[P] = lds_at<f32x4>(gq, 2 * (kEl + 32 * P));
+        l1[P] = lds_at<f32x4>(gq, 2 * (kEl + 32 * P + 4));
       }
       const float egl = vec[kEgl];
       f16x8 pfr[2][2][2];
@@ -702,7 +711,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
           const int r = pair_row(G, t, li);
 #pragma unroll
           for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds_at<f16x8>(pb[t], 1024 * G + 2048 * P);
-          ego[G][t] = vec[kEg + r] * p.scale;
+          ego[G][t] = lds_at<float>(gp, 2 * (kEg + r - pair_row(0, 0, li))) * p.scale;
         }
       f32x4 vn[2][2];
 #pragma unroll
@@ -751,8 +760,10 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 
       // ---- stage 5: o^T = (Q h)^T diag(scale e^gamma) + (scale P v_new)^T (P carries the
       // scale), 8-byte row stores;
-      // reads of the first half of the next chunk's K rows
-      if (more) read_k(n + 1, ob, 0, kG / 2);
+      // reads of the first half of the next chunk's K rows (after the last chunk they read a
+      // stale ring slot and go unused: reading unconditionally keeps the registers in place
+      // instead of copying the old values on the path that skips the read)
+      read_k(n + 1, ob, 0, kG / 2);
       const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
 #pragma unroll
       for (int G = 0; G < 2; ++G)
