@@ -7,7 +7,8 @@ which holds none of the method's arithmetic).
 
 Contents
   * ``gdn_oracle.c`` (compiled to ``_build/liboracle.so`` with gcc -O2, no fast-math):
-    the plain token-by-token recurrence, the packed-varlen tables and driver, the BiGDN
+    the plain token-by-token recurrence and its transition matrix (the linear part of the
+    map from initial to final state), the packed-varlen tables and driver, the BiGDN
     front end (full-channel RMSNorm, ReLU, k-scale, interleaved-pair RoPE) and the
     frame-level BiGDN scan in both directions.  This is the reference every GPU result is
     compared with.
@@ -61,9 +62,11 @@ def _load():
         lib.oracle_prep.argtypes = [I, I, I, I, P, P, P, P, P, Dd, Dd, P, P, P, P, P, P, P]
         lib.oracle_bigdn_dir.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         lib.oracle_bigdn.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, Dd, Dd, P, P]
+        lib.oracle_gdn_transition.argtypes = [I, I, I, I, P, P, P, P, P]
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
-                     "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads"):
+                     "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
+                     "oracle_gdn_transition"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -115,6 +118,32 @@ def gdn(q, k, v, beta, g=None, gk=None, scale=1.0, h0=None, chunk=CHUNK,
     if want_vnew:
         out["v_new"] = vn
     return out
+
+
+def transition(k, beta, g=None, gk=None):
+    """Linear part of a fragment's state map: ht(h0) = M h0 + ht(0) per (b, h), with
+    M = A_T ... A_1, A_t = (I - beta_t k_t k_t^T) diag(exp(g_t + gk_t)).
+    k [B,T,H,K]; beta, g [B,T,H]; gk [B,T,H,K].  Returns M [B,H,K,K]."""
+    k, beta, g, gk = map(_f64, (k, beta, g, gk))
+    B, T, H, K = k.shape
+    M = np.empty((B, H, K, K))
+    rc = _load().oracle_gdn_transition(B, T, H, K, _p(k), _p(g), _p(gk), _p(beta), _p(M))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_transition failed")
+    return M
+
+
+def state_summary(k, v, beta, g=None, gk=None):
+    """State summary of a fragment (for composing fragments run separately): state_ext =
+    ht with a zero initial state [B,H,K,V], transition = M [B,H,K,K]."""
+    ht = gdn(k, k, v, beta, g=g, gk=gk)["ht"]
+    return {"state_ext": ht, "transition": transition(k, beta, g=g, gk=gk)}
+
+
+def apply_summary(state_ext, trans, h_in=None):
+    """h_out = transition h_in + state_ext per (b, h); h_in None means zero."""
+    state_ext, trans, h_in = map(_f64, (state_ext, trans, h_in))
+    return state_ext.copy() if h_in is None else np.matmul(trans, h_in) + state_ext
 
 
 def varlen_tables(cu_seqlens, chunk=CHUNK):

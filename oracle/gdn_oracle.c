@@ -152,6 +152,72 @@ int oracle_gdn(int B, int T, int H, int K, int V, int C,
 }
 
 /*
+ * Transition of one chain: the linear part of the map h0 -> ht of the recurrence above.
+ * Each token applies S <- A_t S + beta_t k_t v_t^T with
+ *     A_t = (I - beta_t k_t k_t^T) diag(a_t),
+ * so ht(h0) = M h0 + ht(0) with M = A_T ... A_1 (K x K).  M is formed by running the same
+ * token steps on a K x K state that starts as the identity and has no value term.
+ *   k, gk : K values per token, stride sk     g, beta : 1 value per token, stride sg
+ * M is K*K row-major; a, w are K-element work arrays.
+ */
+static void transition_chain(int T, int K, const double* k, long sk, const double* g,
+                             const double* gk, const double* beta, long sg, double* M,
+                             double* a, double* w) {
+  for (int r = 0; r < K; ++r)
+    for (int c = 0; c < K; ++c) M[(size_t)r * K + c] = (r == c) ? 1.0 : 0.0;
+  for (int t = 0; t < T; ++t) {
+    const double* kt = k + (long)t * sk;
+    const double bt = beta[(long)t * sg];
+    for (int r = 0; r < K; ++r) {
+      double lam = 0.0;
+      if (g) lam += g[(long)t * sg];
+      if (gk) lam += gk[(long)t * sk + r];
+      a[r] = exp(lam);
+    }
+    /* M <- diag(a_t) M */
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < K; ++c) M[(size_t)r * K + c] *= a[r];
+    /* M <- M - beta k (k^T M) */
+    for (int c = 0; c < K; ++c) w[c] = 0.0;
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < K; ++c) w[c] += kt[r] * M[(size_t)r * K + c];
+    for (int r = 0; r < K; ++r)
+      for (int c = 0; c < K; ++c) M[(size_t)r * K + c] -= bt * kt[r] * w[c];
+  }
+}
+
+/*
+ * Dense batch transitions: k [B,T,H,K], g, beta [B,T,H], gk [B,T,H,K] (g, gk may be NULL)
+ * -> M [B,H,K,K].  Returns 0, or -1 on bad sizes.
+ */
+int oracle_gdn_transition(int B, int T, int H, int K, const double* k, const double* g,
+                          const double* gk, const double* beta, double* M) {
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0) return -1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)K);
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!a || !w) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        const long tok0 = (long)b * T * H + h;
+        transition_chain(T, K, k + tok0 * K, (long)H * K, g ? g + tok0 : NULL,
+                         gk ? gk + tok0 * K : NULL, beta + tok0, (long)H,
+                         M + (size_t)bh * K * K, a, w);
+      }
+    }
+    free(a);
+    free(w);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
  * Varlen chunk tables (the chunk_indices / chunk_offsets the state-pass fragments index
  * with): chunk_offsets[i] = number of chunks in sequences before i, so it has N+1 entries;
  * chunk_indices holds one (sequence, chunk-within-sequence) pair per chunk, in order.

@@ -418,3 +418,62 @@ def test_bigdn_block_is_prep_plus_both_directions():
     nr, dr = oracle.bigdn_dir(*ins, reverse=True)
     np.testing.assert_allclose(num, nf + nr, atol=1e-14)
     np.testing.assert_allclose(den, df + dr, atol=1e-14)
+
+
+# ------------------------------------------------- fragment state summaries (transition)
+# The final state of a fragment is affine in its initial state: ht(h0) = M h0 + ht(0).  These
+# pin M against closed forms and against the separately pinned recurrence.
+@pytest.mark.parametrize("per_key", [False, True])
+def test_transition_beta_zero_is_total_decay(per_key):
+    # beta = 0 makes every token map diagonal: M = diag(exp(sum_t (g_t + gk_t)))
+    rng = np.random.default_rng(11)
+    q, k, v, beta, g, gk = _rand_chain(rng, 37, 16, 8, per_key=per_key)
+    beta = np.zeros_like(beta)
+    M = oracle.transition(k, beta, g=g, gk=gk)[0, 0]
+    lam = g[0, :, 0].sum() + (gk[0, :, 0, :].sum(axis=0) if per_key else np.zeros(16))
+    np.testing.assert_allclose(M, np.diag(np.exp(lam)), rtol=1e-12, atol=0.0)
+
+
+def test_transition_orthonormal_keys_is_projection():
+    # no decay, beta = 1, orthonormal keys: the token maps I - k_t k_t^T are commuting
+    # projections, so M = I - sum_t k_t k_t^T, the projection onto the keys' complement
+    rng = np.random.default_rng(12)
+    K, T = 16, 6
+    Q, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    k = Q[:, :T].T.reshape(1, T, 1, K)
+    M = oracle.transition(k, np.ones((1, T, 1)))[0, 0]
+    np.testing.assert_allclose(M, np.eye(K) - Q[:, :T] @ Q[:, :T].T, atol=1e-13)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_transition_is_linear_part_of_the_recurrence(per_key):
+    # ht(h0) from the recurrence equals M h0 + state_ext for a random h0
+    rng = np.random.default_rng(13)
+    q, k, v, beta, g, gk = _rand_chain(rng, 70, 16, 12, per_key=per_key)
+    h0 = rng.standard_normal((1, 1, 16, 12))
+    s = oracle.state_summary(k, v, beta, g=g, gk=gk)
+    full = oracle.gdn(q, k, v, beta, g=g, gk=gk, h0=h0)["ht"]
+    np.testing.assert_allclose(oracle.apply_summary(s["state_ext"], s["transition"], h0), full,
+                               rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(oracle.apply_summary(s["state_ext"], s["transition"]),
+                               oracle.gdn(q, k, v, beta, g=g, gk=gk)["ht"], atol=0.0)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_summaries_compose_over_fragments(per_key):
+    # cut a chain into fragments: composing the fragments' summaries in order gives the whole
+    # chain's final state, and the whole chain's M is the ordered product of the fragments'
+    rng = np.random.default_rng(14)
+    q, k, v, beta, g, gk = _rand_chain(rng, 150, 16, 8, per_key=per_key)
+    cuts = [0, 41, 64, 130, 150]
+    h, m_all = None, np.eye(16)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sl = (slice(None), slice(a, b))
+        s = oracle.state_summary(k[sl], v[sl], beta[sl], g=g[sl],
+                                 gk=None if gk is None else gk[sl])
+        h = oracle.apply_summary(s["state_ext"], s["transition"], h)
+        m_all = s["transition"][0, 0] @ m_all
+    np.testing.assert_allclose(h, oracle.gdn(q, k, v, beta, g=g, gk=gk)["ht"], rtol=1e-11,
+                               atol=1e-12)
+    np.testing.assert_allclose(m_all, oracle.transition(k, beta, g=g, gk=gk)[0, 0], rtol=1e-11,
+                               atol=1e-13)
