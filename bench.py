@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP32_VALU_PEAK_TFLOPS = 157.3  # published fp32 vector peak (packed fp32 FMA, 256 CUs, 2.4 GHz)
 METRIC = "tokens·heads/sec for chunked gated delta-rule fwd; % MFMA (or HBM) peak"
 KERNEL_SOURCE_DIR = "gated_delta_rule_29_amd/csrc"
 # The kernels one forward call launches; the roofline covers the whole call (every kernel on
@@ -126,6 +127,13 @@ def cpu_baseline(kind, inp, max_chains=64):
         return _cpu_time(lambda: oracle.bigdn(*args, inp["k_scale"], inp["eps"]),
                          "whole block: prep + both directions, %d heads x %d tokens" % (H, N),
                          B * N * H)
+    if kind == "summary":
+        B, T, H, K = inp["k"].shape
+        nb, hh = 1, min(H, 8)
+        sub = {k: (oracle._f64(v[:nb, :, :hh]) if v is not None else None) for k, v in inp.items()}
+        return _cpu_time(lambda: oracle.state_summary(sub["k"], sub["v"], sub["beta"], g=sub["g"]),
+                         "1 of %d batch rows x %d of %d heads (%d chains x %d tokens)"
+                         % (B, hh, H, hh, T), hh * T)
     if kind == "varlen":
         cu = inp["cu_seqlens"].numpy()
         n = 1
@@ -226,6 +234,21 @@ def main():
             s = sets[i % len(sets)]
             return gdn.gdn_fwd_varlen(s["q"], s["k"], s["v"], s["beta"], s["cu_seqlens"],
                                       g=s["g"], want_tables=False)
+    elif kind == "summary":
+        B, T, H, K = inp["q"].shape
+        V = inp["v"].shape[-1]
+        dt = inp["q"].dtype
+        th = B * T * H
+        # the transition's token recurrence: decay (K^2), k^T M (2K^2) and the rank-one
+        # update (2K^2) flops per token and chain
+        alg = 5 * K * K * th
+        kernel = "gdn_state_summary call: fused16_kernel (zero-start state) + transition_kernel"
+        config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
+                  "state": "fp32", "outputs": "state_ext [B,H,K,V] + transition [B,H,K,K]"}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.gdn_state_summary(s["k"], s["v"], s["beta"], g=s["g"])
     elif kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -265,6 +288,12 @@ def main():
     value = th / (ms_per_step / 1e3)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     achieved = alg / avg_launch_s / 1e9
+    if kind == "summary":  # flop-bound: alg counts flops, reported in TFLOP/s
+        roof = {"bound": "alu", "achieved": achieved / 1e3, "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / 1e3 / FP32_VALU_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
     traffic = measured_traffic(alg) if args.workload == "gdn_bf16_b4h16t4096" else None
     out = {
         "metric": METRIC,
@@ -280,9 +309,10 @@ def main():
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic (seeded workloads.py recipe: %s)" % args.workload,
         "config": dict(config, input_copies_rotated=len(sets)),
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel,
-                     "alg_bytes_per_launch": alg, "avg_launch_ms": avg_launch_s * 1e3},
+        "roofline": dict(roof, traffic=traffic, kernel=kernel,
+                         **{("alg_flops_per_launch" if kind == "summary" else
+                             "alg_bytes_per_launch"): alg},
+                         avg_launch_ms=avg_launch_s * 1e3),
         "cpu_baseline": None,
     }
     if not args.no_cpu:

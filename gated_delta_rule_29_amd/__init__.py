@@ -17,6 +17,7 @@ import torch
 from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
+           "gdn_state_summary", "gdn_state_apply",
            "gdn_abi_version", "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
@@ -92,6 +93,48 @@ def gdn_fwd(q, k, v, beta, g=None, gk=None, scale=1.0, h0=None, *, want_ht=True,
     if want_v_new:
         out["v_new"] = vn
     return out
+
+
+def gdn_state_summary(k, v, beta, g=None, gk=None, *, want_transition=True):
+    """State summary of a fragment: (state_ext [B,H,K,V] fp32, transition [B,H,K,K] fp32 or
+    None) with ht(h0) = transition @ h0 + state_ext.  k [B,T,H,K], v [B,T,H,V] (fp32 or
+    bf16), beta, g [B,T,H] fp32, gk [B,T,H,K] fp32."""
+    if k.dtype not in _DT:
+        raise ValueError("k must be float32 or bfloat16, got %s" % k.dtype)
+    B, T, H, K = k.shape
+    V = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(gk, "gk", (B, T, H, K), torch.float32, dev)
+    st = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
+    tr = torch.empty(B, H, K, K, dtype=torch.float32, device=dev) if want_transition else None
+    lib = _lib.load()
+    ws_n = lib.gdn_state_summary_workspace_bytes(B, T, H, K, V, _DT[dt], int(gk is not None))
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.gdn_state_summary(_ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta), _ptr(st),
+                               _ptr(tr), B, T, H, K, V, _DT[dt], _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "gdn_state_summary")
+    return st, tr
+
+
+def gdn_state_apply(state_ext, transition, h_in=None):
+    """h_out = transition @ h_in + state_ext per (b, h) (fp32 [.., K, V]); h_in None = zero."""
+    *lead, K, V = state_ext.shape
+    BH = 1
+    for d in lead:
+        BH *= d
+    dev = state_ext.device
+    _need(state_ext, "state_ext", tuple(lead) + (K, V), torch.float32, dev)
+    _need(transition, "transition", tuple(lead) + (K, K), torch.float32, dev)
+    _need(h_in, "h_in", tuple(lead) + (K, V), torch.float32, dev)
+    h_out = torch.empty_like(state_ext)
+    rc = _lib.load().gdn_state_apply(_ptr(state_ext), _ptr(transition), _ptr(h_in), _ptr(h_out),
+                                     BH, K, V, _stream(dev))
+    _lib.check(rc, "gdn_state_apply")
+    return h_out
 
 
 def gdn_varlen_num_chunks(cu_seqlens_host) -> int:

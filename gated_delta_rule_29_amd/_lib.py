@@ -30,6 +30,9 @@ SIGNATURES = {
     "gdn_fwd_varlen": (I, [P, P, P, P, P, P, F, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, P,
                            SZ, P]),
     "gdn_prep": (I, [P, P, P, P, P, F, F, P, P, P, P, P, P, P, I, I, I, I, P]),
+    "gdn_state_summary_workspace_bytes": (SZ, [I, I, I, I, I, I, I]),
+    "gdn_state_summary": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, P, SZ, P]),
+    "gdn_state_apply": (I, [P, P, P, P, I, I, I, P]),
     "bigdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I]),
     "bigdn_fwd": (I, [P, P, P, P, P, P, P, F, F, P, P, I, I, I, I, I, P, SZ, P]),
 }

@@ -107,6 +107,89 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// gdn_state_summary workspace: the forward pass's own workspace and its discarded per-token
+// outputs.  Every view 256-byte aligned.
+struct SummaryWs {
+  size_t fwd, o, total;
+};
+
+size_t al256s(size_t x) { return (x + 255) & ~(size_t)255; }
+
+SummaryWs summary_ws(int B, int T, int H, int K, int V, int dtype, bool per_key) {
+  SummaryWs w{};
+  const size_t es = dtype == GDN_DTYPE_BF16 ? 2 : 4, tok = (size_t)B * T * H;
+  size_t off = 0;
+  w.fwd = off;
+  off = al256s(off + gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, per_key));
+  w.o = off;
+  off = al256s(off + tok * (size_t)V * es);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_state_summary_workspace_bytes(int B, int T, int H, int K, int V, int dtype, int per_key) {
+  if (B <= 0 || T <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key != 0)) return 0;
+  return summary_ws(B, T, H, K, V, dtype, per_key != 0).total;
+}
+
+int gdn_state_summary(const void* k, const void* v, const float* g, const float* gk,
+                      const float* beta, float* state_ext, float* transition, int B, int T, int H,
+                      int K, int V, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int rc = check_fwd_common(k, k, v, beta, state_ext, gk, H, K, V, dtype);
+  if (rc) return rc;
+  if (B <= 0 || T <= 0) return fail(GDN_ERR_INVALID, "B and T must be positive (got %d, %d)", B, T);
+  rc = check_row_span(T, H, K, V, dtype);
+  if (rc) return rc;
+  const int64_t wgs = (int64_t)B * H * ((K > V ? K : V) / 32), nslots = (int64_t)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK);
+  if (wgs > INT32_MAX || nslots > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "B*H*(V/32) = %lld or B*H*chunks = %lld exceeds the grid limit",
+                (long long)wgs, (long long)nslots);
+  const SummaryWs w = summary_ws(B, T, H, K, V, dtype, gk != nullptr);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", w.total, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // state_ext: the fragment from a zero initial state (the per-token outputs are discarded)
+  gdn::FwdParams p{};
+  p.q = k; p.k = k; p.v = v; p.g = g; p.gk = gk; p.beta = beta; p.h0 = nullptr;
+  p.o = ws + w.o; p.ht = state_ext; p.h_chunks = nullptr; p.v_new = nullptr; p.cu = nullptr;
+  p.scale = 1.f; p.B = B; p.T = T; p.H = H; p.V = V; p.nvb = V / 64;
+  p.nseq = 0; p.nt_total = 0; p.ws = ws + w.fwd; p.coffs = nullptr;
+  hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, false, st);
+  if (e != hipSuccess) return hip_fail(e, "gdn_state_summary launch");
+  if (transition) {
+    e = gdn::launch_transition(k, g, gk, beta, transition, B, T, H, K, dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "gdn_state_summary launch");
+  }
+  return ok();
+}
+
+int gdn_state_apply(const float* state_ext, const float* transition, const float* h_in,
+                    float* h_out, int BH, int K, int V, void* stream) {
+  if (!state_ext || !h_out || (h_in && !transition))
+    return fail(GDN_ERR_INVALID, "state_ext and h_out must be non-null, and transition too when h_in is");
+  if (BH <= 0 || K <= 0 || V <= 0) return fail(GDN_ERR_INVALID, "BH, K, V must be positive (got %d, %d, %d)", BH, K, V);
+  if (K > gdn::kApplyMaxK) return fail(GDN_ERR_UNSUPPORTED, "K must be <= %d, got %d", gdn::kApplyMaxK, K);
+  if (BH > 65535) return fail(GDN_ERR_INVALID, "BH must be <= 65535, got %d", BH);
+  const uintptr_t bytes = (uintptr_t)BH * K * V * 4;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(h_out), b0 = reinterpret_cast<uintptr_t>(h_in);
+  if (h_in && a0 < b0 + bytes && b0 < a0 + bytes) return fail(GDN_ERR_INVALID, "h_out must not overlap h_in");
+  hipError_t e = gdn::launch_apply(state_ext, transition, h_in, h_out, BH, K, V, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_state_apply launch");
+  return ok();
+}
+
 int gdn_varlen_num_chunks(const int* cu, int N) {
   if (!cu || N < 1 || cu[0] != 0) return -1;
   int64_t total = 0;

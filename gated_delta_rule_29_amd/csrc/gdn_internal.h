@@ -36,6 +36,16 @@ size_t fwd_slot_bytes(int dtype, int K, bool per_key);
 hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream);
 hipError_t launch_varlen_tables(const int* cu, int N, int* offs, int* idx, hipStream_t stream);
 
+// fragment state summary helpers (gdn_summary.hip)
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);  // bytes a multiple of 16
+hipError_t launch_identity(float* m, long BH, int K, hipStream_t stream);
+hipError_t launch_apply(const float* c, const float* M, const float* h_in, float* h_out, int BH,
+                        int K, int V, hipStream_t stream);
+// M [B,H,K,K] fp32 from k (dtype 0 fp32, 1 bf16), g, gk (each may be null), beta; K in {64, 128}
+hipError_t launch_transition(const void* k, const float* g, const float* gk, const float* beta,
+                             float* M, int B, int T, int H, int K, int dtype, hipStream_t stream);
+constexpr int kApplyMaxK = 256;
+
 }  // namespace gdn
 
 namespace gdn {

@@ -158,6 +158,43 @@ GDN_API int gdn_prep(const void* qkv, const float* q_norm_w, const float* k_norm
              void* k_pos, void* v_hm, int B, int N, int H, int D, void* stream);
 
 /*
+ * gdn_state_summary -- the state summary of one fragment of a sequence, so that the
+ * fragments of a long sequence can run separately and be joined (the context-parallel GDN /
+ * KDA state summary of the MindSpore hyper-parallel "Diff Coverage" page: a per-chunk
+ * transition diag(decay) - K^T W composed over the fragment, plus the state reached from a
+ * zero start).  Over a fragment the final state is affine in the initial state:
+ *     ht(h0) = transition h0 + state_ext,
+ *     state_ext  = ht with h0 = 0                                   [B,H,K,V] fp32 OUT
+ *     transition = A_T ... A_1,  A_t = (I - beta_t k_t k_t^T) diag(exp(g_t + gk_t))
+ *                                                                    [B,H,K,K] fp32 OUT
+ *   k [B,T,H,K], v [B,T,H,V] (dtype), g [B,T,H] or NULL, gk [B,T,H,K] or NULL, beta [B,T,H]
+ *   as in gdn_fwd (q is not needed).  transition may be NULL (not formed).  state_ext comes
+ *   from the forward kernels; the transition from an fp32 kernel that keeps a power-of-two
+ *   exponent per column (it decays like the product of all the fragment's decays, so values
+ *   below fp32 range become zero, as they would in any fp32 result).
+ *   workspace  at least gdn_state_summary_workspace_bytes(B, T, H, K, V, dtype, gk != NULL)
+ *              bytes, 256-byte aligned, caller-owned
+ * Supported and errors: as gdn_fwd.
+ */
+GDN_API size_t gdn_state_summary_workspace_bytes(int B, int T, int H, int K, int V, int dtype,
+                                                 int per_key);
+GDN_API int gdn_state_summary(const void* k, const void* v, const float* g, const float* gk,
+                              const float* beta, float* state_ext, float* transition, int B,
+                              int T, int H, int K, int V, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_state_apply -- joins a fragment to the state before it: per (b, h),
+ *     h_out = transition h_in + state_ext          ([K,K] x [K,V] + [K,V], fp32)
+ * state_ext [BH,K,V], transition [BH,K,K], h_in [BH,K,V] (NULL = zero: h_out = state_ext),
+ * h_out [BH,K,V] OUT, all fp32 device pointers; h_out must not overlap h_in.
+ * Supported: K <= 256, BH <= 65535.  GDN_ERR_INVALID on null/overlapping pointers or
+ * non-positive sizes.
+ */
+GDN_API int gdn_state_apply(const float* state_ext, const float* transition, const float* h_in,
+                            float* h_out, int BH, int K, int V, void* stream);
+
+/*
  * bigdn_fwd -- frame-level bidirectional GDN block forward (SANA fused_gdn.py page,
  * _fused_gdn_kernel run forward and REVERSE, summed as in fused_bigdn_func).  N = F * S
  * tokens form F frames of S tokens; every token of a frame reads the same decayed state.

@@ -93,3 +93,39 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         L.load()
+
+
+def test_state_summary_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, g=None, gk=None, beta=FAKE, st=FAKE, tr=FAKE, B=1, T=64, H=2,
+                 K=128, V=128, dtype=1, ws=None, wsn=0)
+        a.update(kw)
+        return lib.gdn_state_summary(a["k"], a["v"], a["g"], a["gk"], a["beta"], a["st"], a["tr"],
+                                     a["B"], a["T"], a["H"], a["K"], a["V"], a["dtype"], a["ws"],
+                                     a["wsn"], None)
+
+    assert call(k=None) == L.ERR_INVALID
+    assert call(st=None) == L.ERR_INVALID
+    assert call(T=0) == L.ERR_INVALID
+    assert call(dtype=3) == L.ERR_INVALID
+    assert call(K=32) == L.ERR_UNSUPPORTED
+    assert call(dtype=0, K=128) == L.ERR_UNSUPPORTED
+    assert call() == L.ERR_WORKSPACE  # no workspace given
+    n = lib.gdn_state_summary_workspace_bytes(1, 64, 2, 128, 128, 1, 0)
+    assert n >= lib.gdn_fwd_workspace_bytes(1, 64, 2, 128, 128, 1, 0) + 64 * 2 * 128 * 2
+    assert lib.gdn_state_summary_workspace_bytes(1, 64, 2, 32, 128, 1, 0) == 0
+
+
+def test_state_apply_validation_codes():
+    L, lib = _lib()
+    assert lib.gdn_state_apply(None, FAKE, None, FAKE, 4, 128, 128, None) == L.ERR_INVALID
+    assert lib.gdn_state_apply(FAKE, None, FAKE, ctypes.c_void_p(0x900000), 4, 128, 128,
+                               None) == L.ERR_INVALID  # h_in without transition
+    assert lib.gdn_state_apply(FAKE, FAKE, None, FAKE, 0, 128, 128, None) == L.ERR_INVALID
+    assert lib.gdn_state_apply(FAKE, FAKE, None, FAKE, 4, 512, 128, None) == L.ERR_UNSUPPORTED
+    # h_out overlapping h_in
+    assert lib.gdn_state_apply(FAKE, FAKE, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x2100), 1,
+                               16, 16, None) == L.ERR_INVALID
+    assert "overlap" in L.last_error()

@@ -113,6 +113,10 @@ WORKLOADS = {
     "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
                                     dtype="bf16", seed=0, g_shift=3.0, per_key=True,
                                     save=True),
+    # fragment state summary (transition + zero-start state) at the dense bf16 shape; the
+    # gate is milder (g_shift 8) so the 4096-token transition stays inside fp32 range
+    "summary_bf16_b4h16t4096": dict(kind="summary", B=4, T=4096, H=16, K=128, V=128,
+                                    dtype="bf16", seed=0, g_shift=8.0),
 }
 
 
@@ -121,7 +125,7 @@ def make(name):
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
     w.pop("save", None)
-    if kind == "gdn":
+    if kind in ("gdn", "summary"):
         return gdn_inputs(**w)
     if kind == "varlen":
         return varlen_inputs(**w)
