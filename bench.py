@@ -119,6 +119,14 @@ def cpu_baseline(kind, inp, max_chains=64):
     import oracle
 
     oracle.build()
+    if kind == "bigdn_merged":
+        B, N, _, H, D = inp["qkv"].shape
+        return _cpu_time(lambda: oracle.bigdn_merged(
+            inp["qkv"], inp["beta"], inp["decay"], inp["q_norm_w"], inp["k_norm_w"],
+            inp["rope_cos"], inp["rope_sin"], inp["k_scale"], inp["eps"],
+            decay_bwd=inp["decay_bwd"], gate=inp["gate"], merge_eps=1e-6),
+            "whole merged block: prep + both directions + merge, %d heads x %d tokens"
+            % (H, N), B * N * H)
     if kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -249,6 +257,26 @@ def main():
         def step(i):
             s = sets[i % len(sets)]
             return gdn.gdn_state_summary(s["k"], s["v"], s["beta"], g=s["g"])
+    elif kind == "bigdn_merged":
+        B, N, _, H, D = inp["qkv"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        dt = torch.bfloat16
+        th = B * N * H
+        # as the block above, plus the reverse decay and the gate read; out written instead of
+        # num and den
+        alg = (alg_bytes_bigdn(B, F, S, H, D) + B * H * F * 4 + B * N * H * D * 2
+               - B * H * N * 2)
+        kernel = "bigdn_fwd_merged (4 kernels, whole call)"
+        config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
+                  "state": "fp32", "reverse": "decay 0 at every 4th frame",
+                  "merge": "num / (den + 1e-6) * SiLU(gate)"}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.bigdn_fwd_merged(s["qkv"], s["beta"], s["decay"], s["q_norm_w"],
+                                        s["k_norm_w"], s["rope_cos"], s["rope_sin"],
+                                        s["k_scale"], s["eps"], decay_bwd=s["decay_bwd"],
+                                        gate=s["gate"], merge_eps=1e-6)
     elif kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

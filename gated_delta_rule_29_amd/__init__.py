@@ -17,7 +17,7 @@ import torch
 from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
-           "gdn_state_summary", "gdn_state_apply",
+           "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged",
            "gdn_abi_version", "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
@@ -251,3 +251,39 @@ def bigdn_fwd(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale,
                        _ptr(num), _ptr(den), B, F, S, H, D, _ptr(ws), ws_n, _stream(dev))
     _lib.check(rc, "bigdn_fwd")
     return num, den
+
+
+def bigdn_fwd_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale,
+                     norm_eps=1e-5, *, beta_bwd=None, decay_bwd=None, gate=None,
+                     merge_eps=1e-6, want_num_den=False):
+    """BiGDN block with reverse-direction overrides (beta_bwd [B,H,F,S], decay_bwd [B,H,F]
+    fp32) and the merge epilogue out = num / (den + merge_eps) * SiLU(gate) (gate [B,N,H,D]
+    bf16 or None).  Returns out [B,N,H,D] bf16, or (out, num, den) with want_num_den."""
+    B, N, three, H, D = qkv.shape
+    dev = qkv.device
+    F, S = beta.shape[2], beta.shape[3]
+    if three != 3 or F * S != N:
+        raise ValueError("qkv must be [B,N,3,H,D] with N = F*S")
+    _need(qkv, "qkv", (B, N, 3, H, D), torch.bfloat16, dev)
+    _need(beta, "beta", (B, H, F, S), torch.float32, dev)
+    _need(decay, "decay", (B, H, F), torch.float32, dev)
+    _need(beta_bwd, "beta_bwd", (B, H, F, S), torch.float32, dev)
+    _need(decay_bwd, "decay_bwd", (B, H, F), torch.float32, dev)
+    _need(gate, "gate", (B, N, H, D), torch.bfloat16, dev)
+    _need(q_norm_w, "q_norm_w", (H * D,), torch.float32, dev)
+    _need(k_norm_w, "k_norm_w", (H * D,), torch.float32, dev)
+    _need(rope_cos, "rope_cos", (N, D), torch.float32, dev)
+    _need(rope_sin, "rope_sin", (N, D), torch.float32, dev)
+    out = torch.empty(B, N, H, D, dtype=torch.bfloat16, device=dev)
+    num = torch.empty(B, N, H, D, dtype=torch.bfloat16, device=dev) if want_num_den else None
+    den = torch.empty(B, H, N, dtype=torch.bfloat16, device=dev) if want_num_den else None
+    lib = _lib.load()
+    ws_n = lib.bigdn_fwd_merged_workspace_bytes(B, F, S, H, D, int(beta_bwd is not None))
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.bigdn_fwd_merged(_ptr(qkv), _ptr(beta), _ptr(decay), _ptr(beta_bwd),
+                              _ptr(decay_bwd), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(rope_cos),
+                              _ptr(rope_sin), float(k_scale), float(norm_eps), _ptr(gate),
+                              float(merge_eps), _ptr(out), _ptr(num), _ptr(den), B, F, S, H, D,
+                              _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "bigdn_fwd_merged")
+    return (out, num, den) if want_num_den else out

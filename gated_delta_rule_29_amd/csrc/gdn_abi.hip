@@ -260,12 +260,13 @@ namespace {
 
 // bigdn_fwd workspace: every view 256-byte aligned, in the order of BigdnParams.
 struct BigdnWs {
-  size_t q_rms, k_rms, rope_h, G, Gz, U, uz, SdT, zd, total;
+  size_t q_rms, k_rms, rope_h, G, Gz, U, uz, G_b, Gz_b, U_b, uz_b, SdT, zd, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BigdnWs bigdn_ws(int B, int F, int S, int H, int D) {
+// rev_stats: room for the reverse direction's own statistics (its beta overridden)
+BigdnWs bigdn_ws(int B, int F, int S, int H, int D, bool rev_stats = false) {
   BigdnWs w{};
   const size_t N = (size_t)F * S, mats = (size_t)B * H * F * D * D, vecs = (size_t)B * H * F * D;
   size_t off = 0;
@@ -276,6 +277,12 @@ BigdnWs bigdn_ws(int B, int F, int S, int H, int D) {
   w.Gz = off; off = al256(off + mats * 2);
   w.U = off; off = al256(off + mats * 4);
   w.uz = off; off = al256(off + vecs * 4);
+  if (rev_stats) {
+    w.G_b = off; off = al256(off + mats * 2);
+    w.Gz_b = off; off = al256(off + mats * 2);
+    w.U_b = off; off = al256(off + mats * 4);
+    w.uz_b = off; off = al256(off + vecs * 4);
+  }
   w.SdT = off; off = al256(off + 2 * mats * 2);
   w.zd = off; off = al256(off + 2 * vecs * 4);
   w.total = off;
@@ -320,12 +327,17 @@ size_t bigdn_fwd_workspace_bytes(int B, int F, int S, int H, int D) {
   return bigdn_ws(B, F, S, H, D).total;
 }
 
-int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const float* q_norm_w,
-              const float* k_norm_w, const float* rope_cos, const float* rope_sin,
-              float k_scale, float norm_eps, void* num, void* den, int B, int F, int S, int H,
-              int D, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!qkv || !beta || !decay || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin || !num || !den)
-    return fail(GDN_ERR_INVALID, "qkv, beta, decay, norm weights, RoPE tables, num and den must be non-null");
+int bigdn_fwd_merged(const void* qkv, const float* beta, const float* decay,
+                     const float* beta_bwd, const float* decay_bwd, const float* q_norm_w,
+                     const float* k_norm_w, const float* rope_cos, const float* rope_sin,
+                     float k_scale, float norm_eps, const void* gate, float merge_eps, void* out,
+                     void* num, void* den, int B, int F, int S, int H, int D, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!qkv || !beta || !decay || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin)
+    return fail(GDN_ERR_INVALID, "qkv, beta, decay, norm weights and RoPE tables must be non-null");
+  if (!out && !(num && den))
+    return fail(GDN_ERR_INVALID, "out, or both num and den, must be non-null");
+  if (gate && !out) return fail(GDN_ERR_INVALID, "gate needs out");
   if (F <= 0 || S <= 0) return fail(GDN_ERR_INVALID, "F and S must be positive (got %d, %d)", F, S);
   if ((int64_t)F * S > INT32_MAX) return fail(GDN_ERR_INVALID, "F*S too large");
   // the scan addresses one (b, h)'s per-frame statistics with 32-bit byte offsets
@@ -335,16 +347,19 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
   if (rc) return rc;
   if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
   if (!(norm_eps > 0.f)) return fail(GDN_ERR_INVALID, "norm_eps must be positive");
-  const BigdnWs w = bigdn_ws(B, F, S, H, D);
+  if (out && !(merge_eps >= 0.f)) return fail(GDN_ERR_INVALID, "merge_eps must be >= 0");
+  const BigdnWs w = bigdn_ws(B, F, S, H, D, beta_bwd != nullptr);
   if (!workspace || workspace_bytes < w.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", w.total, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
   gdn::BigdnParams p{};
-  p.qkv = qkv; p.beta = beta; p.decay = decay; p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w;
+  p.qkv = qkv; p.beta = beta; p.decay = decay; p.beta_bwd = beta_bwd; p.decay_bwd = decay_bwd;
+  p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w;
   p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.k_scale = k_scale; p.eps = norm_eps;
-  p.num = num; p.den = den; p.B = B; p.F = F; p.S = S; p.H = H; p.D = D; p.N = N;
+  p.num = num; p.den = den; p.gate = gate; p.out = out; p.merge_eps = merge_eps;
+  p.B = B; p.F = F; p.S = S; p.H = H; p.D = D; p.N = N;
   p.q_inv_rms = reinterpret_cast<float*>(ws + w.q_rms);
   p.k_inv_rms = reinterpret_cast<float*>(ws + w.k_rms);
   p.rope_h = reinterpret_cast<_Float16*>(ws + w.rope_h);
@@ -352,11 +367,33 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
   p.Gz = reinterpret_cast<_Float16*>(ws + w.Gz);
   p.U = reinterpret_cast<float*>(ws + w.U);
   p.uz = reinterpret_cast<float*>(ws + w.uz);
+  if (beta_bwd) {
+    p.G_b = reinterpret_cast<_Float16*>(ws + w.G_b);
+    p.Gz_b = reinterpret_cast<_Float16*>(ws + w.Gz_b);
+    p.U_b = reinterpret_cast<float*>(ws + w.U_b);
+    p.uz_b = reinterpret_cast<float*>(ws + w.uz_b);
+  }
   p.SdT = reinterpret_cast<_Float16*>(ws + w.SdT);
   p.zd = reinterpret_cast<float*>(ws + w.zd);
   hipError_t e = gdn::launch_bigdn(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "bigdn_fwd launch");
   return ok();
+}
+
+size_t bigdn_fwd_merged_workspace_bytes(int B, int F, int S, int H, int D, int has_beta_bwd) {
+  if (B <= 0 || F <= 0 || S <= 0 || H <= 0 || D <= 0) return 0;
+  return bigdn_ws(B, F, S, H, D, has_beta_bwd != 0).total;
+}
+
+int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const float* q_norm_w,
+              const float* k_norm_w, const float* rope_cos, const float* rope_sin,
+              float k_scale, float norm_eps, void* num, void* den, int B, int F, int S, int H,
+              int D, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!num || !den)
+    return fail(GDN_ERR_INVALID, "qkv, beta, decay, norm weights, RoPE tables, num and den must be non-null");
+  return bigdn_fwd_merged(qkv, beta, decay, nullptr, nullptr, q_norm_w, k_norm_w, rope_cos,
+                          rope_sin, k_scale, norm_eps, nullptr, 0.f, nullptr, num, den, B, F, S, H,
+                          D, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

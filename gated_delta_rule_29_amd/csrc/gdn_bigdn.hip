@@ -480,9 +480,10 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   auto fr = [&](int i) { return clampf(rev ? F - 1 - i : i); };
 
   // sources (every byte count below fits 32 bits: F <= 65535 and D <= 128)
-  const i32x4 rG = make_rsrc(zb ? p.Gz + mat0 : p.G + mat0, (uint32_t)F * D * D * 2);
-  const i32x4 rU = zb ? make_rsrc(p.uz + (long)bh * F * D, (uint32_t)F * D * 4)
-                      : make_rsrc(p.U + mat0, (uint32_t)F * D * D * 4);
+  const _Float16* Gs = rev ? (zb ? p.Gz_b : p.G_b) : (zb ? p.Gz : p.G);
+  const i32x4 rG = make_rsrc(Gs + mat0, (uint32_t)F * D * D * 2);
+  const i32x4 rU = zb ? make_rsrc((rev ? p.uz_b : p.uz) + (long)bh * F * D, (uint32_t)F * D * 4)
+                      : make_rsrc((rev ? p.U_b : p.U) + mat0, (uint32_t)F * D * D * 4);
   const uint32_t vU = zb ? 16 * lq : 16 * lane;
   const uint32_t ringw = lds_addr(ring) + wave * 3 * kStage;
   // transfers of frame fa into ring stage stg
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   issue(fr(1), 1);
   float dv = 0.f;  // lane j: the decay of step (i & ~63) + j
   for (int i = 0; i < nsteps; ++i) {
-    if ((i & 63) == 0) dv = p.decay[(long)bh * F + fr(i + lane)];
+    if ((i & 63) == 0) dv = (rev ? p.decay_bwd : p.decay)[(long)bh * F + fr(i + lane)];
     issue(fr(i + 2), (i + 2) % 3);
     wait_vm<2 * kLd>();  // step i's loads are done once only those of steps i+1, i+2 may be pending
     const float dcy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dv), i & 63));
@@ -599,8 +600,9 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
 // (Measured on the 16-frame video block: two heads and four blocks per workgroup beat one
 // head or other block counts; issuing the next block's loads before the products, or using
 // 4-channel items, did not help.)
-template <int D, int kHW>
+template <int D, int kHW, bool kMerge>
 __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) {
+  typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   constexpr int kOct = D / 8, kItems = 64 * kOct / 256, kCT = D / 64, kSP = D + 8;
   __shared__ __attribute__((aligned(16))) f16 qr[kHW][64 * kSP];  // Q_rot rows, padded
   __shared__ float zsum[kHW][D];
@@ -687,6 +689,19 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
     __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < kHW; ++hh) {
+      // lane (li, lq): token n0 + 16 tt + li, value columns (D/4) wave + 16 ct + 4 lq + e
+      auto at = [&](int tt) {
+        return (((long)b * p.N + n0 + 16 * tt + li) * p.H + h0 + hh) * D + (D / 4) * wave + 4 * lq;
+      };
+      bf16x4_t gv[4][kCT];
+      if constexpr (kMerge) {
+        if (p.gate)  // issued before the products, which hide their latency
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < kCT; ++ct)
+              gv[tt][ct] = *reinterpret_cast<const bf16x4_t*>(static_cast<const bf16*>(p.gate) + at(tt) + 16 * ct);
+      }
       f32x4 acc[4][kCT];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -702,18 +717,33 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
         }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        bf16* orow = num + (((long)b * p.N + n0 + 16 * tt + li) * p.H + h0 + hh) * D + (D / 4) * wave + 4 * lq;
+        float rden = 0.f;
+        if constexpr (kMerge) rden = 1.f / (den_part[hh][16 * tt + li] + p.merge_eps);
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct) {
-          typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-          bf16x4_t o4;
+          if (num) {
+            bf16x4_t o4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = (bf16)acc[tt][ct][e];
-          *reinterpret_cast<bf16x4_t*>(orow + 16 * ct) = o4;
+            for (int e = 0; e < 4; ++e) o4[e] = (bf16)acc[tt][ct][e];
+            *reinterpret_cast<bf16x4_t*>(num + at(tt) + 16 * ct) = o4;
+          }
+          if constexpr (kMerge) {
+            bf16x4_t o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x = acc[tt][ct][e] * rden;
+              if (p.gate) {
+                const float gt = (float)gv[tt][ct][e];
+                x *= gt / (1.f + __expf(-gt));
+              }
+              o4[e] = (bf16)x;
+            }
+            *reinterpret_cast<bf16x4_t*>(static_cast<bf16*>(p.out) + at(tt) + 16 * ct) = o4;
+          }
         }
       }
     }
-    if (tid < 64 * kHW) {
+    if (p.den && tid < 64 * kHW) {
       const int hh = tid / 64, t = tid % 64;
       static_cast<bf16*>(p.den)[((long)b * p.H + h0 + hh) * p.N + n0 + t] = (bf16)den_part[hh][t];
     }
@@ -727,7 +757,15 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream) {
+hipError_t launch_bigdn(const BigdnParams& p_in, hipStream_t stream) {
+  BigdnParams p = p_in;
+  if (!p.decay_bwd) p.decay_bwd = p.decay;
+  if (!p.beta_bwd) {  // the reverse direction shares the forward statistics
+    p.G_b = p.G;
+    p.Gz_b = p.Gz;
+    p.U_b = p.U;
+    p.uz_b = p.uz;
+  }
   PrepParams pp{};
   pp.qkv = p.qkv;
   pp.q_norm_w = p.q_norm_w;
@@ -746,6 +784,13 @@ hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream) {
   hipError_t e = launch_prep(pp, stream);
   if (e != hipSuccess) return e;
   const int nbhf = p.B * p.H * p.F;
+  // the reverse direction's statistics, when its beta differs
+  BigdnParams pb = p;
+  pb.beta = p.beta_bwd;
+  pb.G = p.G_b;
+  pb.Gz = p.Gz_b;
+  pb.U = p.U_b;
+  pb.uz = p.uz_b;
   // 64-token blocks per output workgroup: the largest divisor of a frame's blocks up to 4;
   // two heads per output workgroup when H is even
   const int nblk = p.S / 64;
@@ -753,17 +798,26 @@ hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream) {
   while (nblk % grp) grp >>= 1;
   const int hw = p.H % 2 ? 1 : 2;
   const dim3 og(p.B * (p.H / hw) * p.F * (nblk / grp));
+  const bool merge = p.out != nullptr;
+#define GDN_OUT(DD)                                                                                     \
+  do {                                                                                                  \
+    if (hw == 2 && merge) hipLaunchKernelGGL((out_kernel<DD, 2, true>), og, dim3(256), 0, stream, p, grp);  \
+    else if (hw == 2) hipLaunchKernelGGL((out_kernel<DD, 2, false>), og, dim3(256), 0, stream, p, grp);     \
+    else if (merge) hipLaunchKernelGGL((out_kernel<DD, 1, true>), og, dim3(256), 0, stream, p, grp);        \
+    else hipLaunchKernelGGL((out_kernel<DD, 1, false>), og, dim3(256), 0, stream, p, grp);                  \
+  } while (0)
   if (p.D == 128) {
     hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
+    if (p.beta_bwd) hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, pb);
     hipLaunchKernelGGL(scan_kernel<128>, dim3(p.B * p.H * 2 * (128 / 32 + 1)), dim3(256), 0, stream, p);
-    if (hw == 2) hipLaunchKernelGGL((out_kernel<128, 2>), og, dim3(256), 0, stream, p, grp);
-    else hipLaunchKernelGGL((out_kernel<128, 1>), og, dim3(256), 0, stream, p, grp);
+    GDN_OUT(128);
   } else {
     hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
+    if (p.beta_bwd) hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, pb);
     hipLaunchKernelGGL(scan_kernel<64>, dim3(p.B * p.H * 2 * (64 / 32 + 1)), dim3(256), 0, stream, p);
-    if (hw == 2) hipLaunchKernelGGL((out_kernel<64, 2>), og, dim3(256), 0, stream, p, grp);
-    else hipLaunchKernelGGL((out_kernel<64, 1>), og, dim3(256), 0, stream, p, grp);
+    GDN_OUT(64);
   }
+#undef GDN_OUT
   return hipGetLastError();
 }
 

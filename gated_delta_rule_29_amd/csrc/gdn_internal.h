@@ -70,15 +70,21 @@ struct PrepParams {
 
 struct BigdnParams {
   const void* qkv;
-  const float* beta;   // [B, H, F, S]
-  const float* decay;  // [B, H, F]
+  const float* beta;       // [B, H, F, S]
+  const float* decay;      // [B, H, F]
+  const float* decay_bwd;  // [B, H, F] decay of the reverse direction, or nullptr (= decay)
+  const float* beta_bwd;   // [B, H, F, S] beta of the reverse direction, or nullptr (= beta)
   const float* q_norm_w;
   const float* k_norm_w;
   const float* rope_cos;
   const float* rope_sin;
   float k_scale, eps;
-  void* num;  // [B, N, H, D] bf16
-  void* den;  // [B, H, N] bf16
+  void* num;  // [B, N, H, D] bf16, or nullptr
+  void* den;  // [B, H, N] bf16, or nullptr
+  // merge epilogue: out = num / (den + merge_eps) * SiLU(gate) (gate nullable), when out is set
+  const void* gate;  // [B, N, H, D] bf16
+  void* out;         // [B, N, H, D] bf16
+  float merge_eps;
   int B, F, S, H, D, N;
   // workspace views
   float* q_inv_rms;  // [B, N]
@@ -88,6 +94,11 @@ struct BigdnParams {
   _Float16* Gz;      // [B, H, F, D, D]
   float* U;          // [B, H, F, D, D]
   float* uz;         // [B, H, F, D]
+  // statistics of the reverse direction (the same buffers unless beta is overridden for it)
+  _Float16* G_b;
+  _Float16* Gz_b;
+  float* U_b;
+  float* uz_b;
   _Float16* SdT;     // [2, B, H, F, D, D]  S_f^T (forward) and R_f^T (reverse)
   float* zd;         // [2, B, H, F, D]     z_f and zR_f
 };

@@ -129,3 +129,25 @@ def test_state_apply_validation_codes():
     assert lib.gdn_state_apply(FAKE, FAKE, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x2100), 1,
                                16, 16, None) == L.ERR_INVALID
     assert "overlap" in L.last_error()
+
+
+def test_bigdn_merged_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(qkv=FAKE, beta=FAKE, decay=FAKE, bb=None, db=None, gate=None, eps_m=1e-6,
+                 out=FAKE, num=None, den=None, F=2, S=64)
+        a.update(kw)
+        return lib.bigdn_fwd_merged(a["qkv"], a["beta"], a["decay"], a["bb"], a["db"], FAKE, FAKE,
+                                    FAKE, FAKE, 0.1, 1e-5, a["gate"], a["eps_m"], a["out"],
+                                    a["num"], a["den"], 1, a["F"], a["S"], 2, 128, None, 0, None)
+
+    assert call(out=None) == L.ERR_INVALID               # nothing to write
+    assert call(out=None, num=FAKE) == L.ERR_INVALID     # den missing
+    assert call(out=None, num=FAKE, den=FAKE, gate=FAKE) == L.ERR_INVALID  # gate needs out
+    assert call(eps_m=-1.0) == L.ERR_INVALID
+    assert call(S=100) == L.ERR_UNSUPPORTED
+    assert call() == L.ERR_WORKSPACE
+    n0 = lib.bigdn_fwd_merged_workspace_bytes(1, 2, 64, 2, 128, 0)
+    n1 = lib.bigdn_fwd_merged_workspace_bytes(1, 2, 64, 2, 128, 1)
+    assert n0 == lib.bigdn_fwd_workspace_bytes(1, 2, 64, 2, 128) and n1 > n0

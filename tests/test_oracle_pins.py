@@ -477,3 +477,71 @@ def test_summaries_compose_over_fragments(per_key):
                                atol=1e-12)
     np.testing.assert_allclose(m_all, oracle.transition(k, beta, g=g, gk=gk)[0, 0], rtol=1e-11,
                                atol=1e-13)
+
+
+# ------------------------------------------------- BiGDN block: overrides and merge epilogue
+def _merged_inputs(F=4, S=8, H=2, D=8, seed=21):
+    import workloads
+
+    return workloads.bigdn_inputs(1, F, S, H, D, seed=seed)
+
+
+def _bm(w, **kw):
+    return oracle.bigdn_merged(w["qkv"], w["beta"], w["decay"], w["q_norm_w"], w["k_norm_w"],
+                               w["rope_cos"], w["rope_sin"], w["k_scale"], w["eps"], **kw)
+
+
+def test_bigdn_merged_without_overrides_is_the_block():
+    w = _merged_inputs()
+    out, num, den = _bm(w)
+    rn, rd = oracle.bigdn(w["qkv"], w["beta"], w["decay"], w["q_norm_w"], w["k_norm_w"],
+                          w["rope_cos"], w["rope_sin"], w["k_scale"], w["eps"])
+    np.testing.assert_allclose(num, rn, atol=1e-14)
+    np.testing.assert_allclose(den, rd, atol=1e-14)
+    out2, _, _ = _bm(w, beta_bwd=w["beta"], decay_bwd=w["decay"])
+    np.testing.assert_array_equal(out, out2)
+
+
+def test_bigdn_zero_reverse_decay_cuts_the_reverse_direction():
+    # decay_bwd = 0 at frame c: absorbing frame c wipes the reverse state, so frames before c
+    # see nothing after c (chunk-causal); the plain reverse direction does see it
+    w = _merged_inputs(F=5)
+    c, S = 2, w["beta"].shape[3]
+    dbwd = w["decay"].clone()
+    dbwd[:, :, c] = 0.0
+    w2 = dict(w)
+    qkv2 = w["qkv"].clone()
+    qkv2[:, (c + 1) * S:] = torch.randn(qkv2[:, (c + 1) * S:].shape, generator=torch.Generator().manual_seed(9)).to(qkv2.dtype)
+    w2["qkv"] = qkv2
+    _, n1, d1 = _bm(w, decay_bwd=dbwd)
+    _, n2, d2 = _bm(w2, decay_bwd=dbwd)
+    np.testing.assert_allclose(n1[:, :c * S], n2[:, :c * S], atol=1e-13)
+    np.testing.assert_allclose(d1[:, :, :c * S], d2[:, :, :c * S], atol=1e-13)
+    _, m1, _ = _bm(w)
+    _, m2, _ = _bm(w2)
+    assert np.abs(m1[:, :c * S] - m2[:, :c * S]).max() > 1e-3
+
+
+def test_bigdn_reverse_beta_override_reaches_only_the_reverse():
+    # beta_bwd = 0: the reverse direction absorbs nothing, leaving the forward direction alone
+    w = _merged_inputs()
+    _, num, den = _bm(w, beta_bwd=torch.zeros_like(w["beta"]))
+    p = oracle.prep(w["qkv"], w["q_norm_w"], w["k_norm_w"], w["rope_cos"], w["rope_sin"],
+                    w["k_scale"], w["eps"])
+    nf, df = oracle.bigdn_dir(p["q_rot"], p["k_rot"], p["q_pos"], p["k_pos"], p["v"], w["beta"],
+                              w["decay"], reverse=False)
+    np.testing.assert_allclose(num, nf, atol=1e-14)
+    np.testing.assert_allclose(den, df, atol=1e-14)
+
+
+def test_bigdn_merge_gate_is_silu():
+    # SiLU(x) - SiLU(-x) = x and SiLU(0) = 0: a sigmoid gate or a sign slip fails these
+    w = _merged_inputs()
+    B, N, _, H, D = w["qkv"].shape
+    g = torch.randn(B, N, H, D, generator=torch.Generator().manual_seed(4))
+    base, _, _ = _bm(w)
+    up, _, _ = _bm(w, gate=g)
+    dn, _, _ = _bm(w, gate=-g)
+    np.testing.assert_allclose(up - dn, base * g.double().numpy(), rtol=1e-12, atol=1e-13)
+    zero, _, _ = _bm(w, gate=torch.zeros_like(g))
+    assert np.abs(zero).max() == 0.0

@@ -110,6 +110,10 @@ WORKLOADS = {
     "varlen_bf16_8seq": dict(kind="varlen", n_seqs=8, lo=512, hi=8192, H=16, K=128, V=128,
                              dtype="bf16", seed=0, g_shift=3.0),
     "bigdn_video_f16x1024": dict(kind="bigdn", B=1, F=16, S=1024, H=16, D=128, seed=0),
+    # the whole block output of the same video block: chunk-causal reverse direction (reverse
+    # decay 0 at every fourth frame) and the merge epilogue with a SiLU gate
+    "bigdn_video_merged_f16x1024": dict(kind="bigdn_merged", B=1, F=16, S=1024, H=16, D=128,
+                                        seed=0),
     "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
                                     dtype="bf16", seed=0, g_shift=3.0, per_key=True,
                                     save=True),
@@ -131,4 +135,12 @@ def make(name):
         return varlen_inputs(**w)
     if kind == "bigdn":
         return bigdn_inputs(**w)
+    if kind == "bigdn_merged":
+        inp = bigdn_inputs(**w)
+        gen = _gen(w["seed"] + 1)
+        B, N, _, H, D = inp["qkv"].shape
+        inp["decay_bwd"] = inp["decay"].clone()
+        inp["decay_bwd"][:, :, ::4] = 0.0
+        inp["gate"] = torch.randn(B, N, H, D, generator=gen).to(torch.bfloat16)
+        return inp
     raise KeyError(name)
