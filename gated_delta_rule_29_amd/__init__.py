@@ -254,10 +254,10 @@ def bigdn_fwd(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale,
 
 
 def bigdn_fwd_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale,
-                     norm_eps=1e-5, *, beta_bwd=None, decay_bwd=None, gate=None,
+                     norm_eps=1e-5, *, qkv_bwd=None, beta_bwd=None, decay_bwd=None, gate=None,
                      merge_eps=1e-6, want_num_den=False):
-    """BiGDN block with reverse-direction overrides (beta_bwd [B,H,F,S], decay_bwd [B,H,F]
-    fp32) and the merge epilogue out = num / (den + merge_eps) * SiLU(gate) (gate [B,N,H,D]
+    """BiGDN block with reverse-direction overrides (qkv_bwd [B,N,3,H,D] bf16, beta_bwd
+    [B,H,F,S], decay_bwd [B,H,F] fp32) and the merge epilogue out = num / (den + merge_eps) * SiLU(gate) (gate [B,N,H,D]
     bf16 or None).  Returns out [B,N,H,D] bf16, or (out, num, den) with want_num_den."""
     B, N, three, H, D = qkv.shape
     dev = qkv.device
@@ -265,6 +265,7 @@ def bigdn_fwd_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k
     if three != 3 or F * S != N:
         raise ValueError("qkv must be [B,N,3,H,D] with N = F*S")
     _need(qkv, "qkv", (B, N, 3, H, D), torch.bfloat16, dev)
+    _need(qkv_bwd, "qkv_bwd", (B, N, 3, H, D), torch.bfloat16, dev)
     _need(beta, "beta", (B, H, F, S), torch.float32, dev)
     _need(decay, "decay", (B, H, F), torch.float32, dev)
     _need(beta_bwd, "beta_bwd", (B, H, F, S), torch.float32, dev)
@@ -278,9 +279,10 @@ def bigdn_fwd_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k
     num = torch.empty(B, N, H, D, dtype=torch.bfloat16, device=dev) if want_num_den else None
     den = torch.empty(B, H, N, dtype=torch.bfloat16, device=dev) if want_num_den else None
     lib = _lib.load()
-    ws_n = lib.bigdn_fwd_merged_workspace_bytes(B, F, S, H, D, int(beta_bwd is not None))
+    rev = qkv_bwd is not None or beta_bwd is not None
+    ws_n = lib.bigdn_fwd_merged_workspace_bytes(B, F, S, H, D, int(rev))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
-    rc = lib.bigdn_fwd_merged(_ptr(qkv), _ptr(beta), _ptr(decay), _ptr(beta_bwd),
+    rc = lib.bigdn_fwd_merged(_ptr(qkv), _ptr(qkv_bwd), _ptr(beta), _ptr(decay), _ptr(beta_bwd),
                               _ptr(decay_bwd), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(rope_cos),
                               _ptr(rope_sin), float(k_scale), float(norm_eps), _ptr(gate),
                               float(merge_eps), _ptr(out), _ptr(num), _ptr(den), B, F, S, H, D,

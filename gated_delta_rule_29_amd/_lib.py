@@ -36,8 +36,8 @@ SIGNATURES = {
     "bigdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I]),
     "bigdn_fwd": (I, [P, P, P, P, P, P, P, F, F, P, P, I, I, I, I, I, P, SZ, P]),
     "bigdn_fwd_merged_workspace_bytes": (SZ, [I, I, I, I, I, I]),
-    "bigdn_fwd_merged": (I, [P, P, P, P, P, P, P, P, P, F, F, P, F, P, P, P, I, I, I, I, I, P, SZ,
-                             P]),
+    "bigdn_fwd_merged": (I, [P, P, P, P, P, P, P, P, P, P, F, F, P, F, P, P, P, I, I, I, I, I, P,
+                             SZ, P]),
 }
 
 _lib = None

@@ -260,18 +260,24 @@ namespace {
 
 // bigdn_fwd workspace: every view 256-byte aligned, in the order of BigdnParams.
 struct BigdnWs {
-  size_t q_rms, k_rms, rope_h, G, Gz, U, uz, G_b, Gz_b, U_b, uz_b, SdT, zd, total;
+  size_t q_rms, k_rms, q_rms_b, k_rms_b, rope_h, G, Gz, U, uz, G_b, Gz_b, U_b, uz_b, SdT, zd,
+      total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// rev_stats: room for the reverse direction's own statistics (its beta overridden)
+// rev_stats: room for the reverse direction's own statistics (its beta or its q, k, v
+// overridden) and its inverse RMS
 BigdnWs bigdn_ws(int B, int F, int S, int H, int D, bool rev_stats = false) {
   BigdnWs w{};
   const size_t N = (size_t)F * S, mats = (size_t)B * H * F * D * D, vecs = (size_t)B * H * F * D;
   size_t off = 0;
   w.q_rms = off; off = al256(off + (size_t)B * N * 4);
   w.k_rms = off; off = al256(off + (size_t)B * N * 4);
+  if (rev_stats) {
+    w.q_rms_b = off; off = al256(off + (size_t)B * N * 4);
+    w.k_rms_b = off; off = al256(off + (size_t)B * N * 4);
+  }
   w.rope_h = off; off = al256(off + N * D * 4);
   w.G = off; off = al256(off + mats * 2);
   w.Gz = off; off = al256(off + mats * 2);
@@ -327,7 +333,7 @@ size_t bigdn_fwd_workspace_bytes(int B, int F, int S, int H, int D) {
   return bigdn_ws(B, F, S, H, D).total;
 }
 
-int bigdn_fwd_merged(const void* qkv, const float* beta, const float* decay,
+int bigdn_fwd_merged(const void* qkv, const void* qkv_bwd, const float* beta, const float* decay,
                      const float* beta_bwd, const float* decay_bwd, const float* q_norm_w,
                      const float* k_norm_w, const float* rope_cos, const float* rope_sin,
                      float k_scale, float norm_eps, const void* gate, float merge_eps, void* out,
@@ -348,14 +354,15 @@ int bigdn_fwd_merged(const void* qkv, const float* beta, const float* decay,
   if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
   if (!(norm_eps > 0.f)) return fail(GDN_ERR_INVALID, "norm_eps must be positive");
   if (out && !(merge_eps >= 0.f)) return fail(GDN_ERR_INVALID, "merge_eps must be >= 0");
-  const BigdnWs w = bigdn_ws(B, F, S, H, D, beta_bwd != nullptr);
+  const bool rev = beta_bwd || qkv_bwd;
+  const BigdnWs w = bigdn_ws(B, F, S, H, D, rev);
   if (!workspace || workspace_bytes < w.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", w.total, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
   gdn::BigdnParams p{};
-  p.qkv = qkv; p.beta = beta; p.decay = decay; p.beta_bwd = beta_bwd; p.decay_bwd = decay_bwd;
+  p.qkv = qkv; p.qkv_bwd = qkv_bwd; p.beta = beta; p.decay = decay; p.beta_bwd = beta_bwd; p.decay_bwd = decay_bwd;
   p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w;
   p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.k_scale = k_scale; p.eps = norm_eps;
   p.num = num; p.den = den; p.gate = gate; p.out = out; p.merge_eps = merge_eps;
@@ -367,7 +374,9 @@ int bigdn_fwd_merged(const void* qkv, const float* beta, const float* decay,
   p.Gz = reinterpret_cast<_Float16*>(ws + w.Gz);
   p.U = reinterpret_cast<float*>(ws + w.U);
   p.uz = reinterpret_cast<float*>(ws + w.uz);
-  if (beta_bwd) {
+  if (rev) {
+    p.q_inv_rms_b = reinterpret_cast<float*>(ws + w.q_rms_b);
+    p.k_inv_rms_b = reinterpret_cast<float*>(ws + w.k_rms_b);
     p.G_b = reinterpret_cast<_Float16*>(ws + w.G_b);
     p.Gz_b = reinterpret_cast<_Float16*>(ws + w.Gz_b);
     p.U_b = reinterpret_cast<float*>(ws + w.U_b);
@@ -380,9 +389,9 @@ int bigdn_fwd_merged(const void* qkv, const float* beta, const float* decay,
   return ok();
 }
 
-size_t bigdn_fwd_merged_workspace_bytes(int B, int F, int S, int H, int D, int has_beta_bwd) {
+size_t bigdn_fwd_merged_workspace_bytes(int B, int F, int S, int H, int D, int has_rev_inputs) {
   if (B <= 0 || F <= 0 || S <= 0 || H <= 0 || D <= 0) return 0;
-  return bigdn_ws(B, F, S, H, D, has_beta_bwd != 0).total;
+  return bigdn_ws(B, F, S, H, D, has_rev_inputs != 0).total;
 }
 
 int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const float* q_norm_w,
@@ -391,7 +400,7 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
               int D, void* workspace, size_t workspace_bytes, void* stream) {
   if (!num || !den)
     return fail(GDN_ERR_INVALID, "qkv, beta, decay, norm weights, RoPE tables, num and den must be non-null");
-  return bigdn_fwd_merged(qkv, beta, decay, nullptr, nullptr, q_norm_w, k_norm_w, rope_cos,
+  return bigdn_fwd_merged(qkv, nullptr, beta, decay, nullptr, nullptr, q_norm_w, k_norm_w, rope_cos,
                           rope_sin, k_scale, norm_eps, nullptr, 0.f, nullptr, num, den, B, F, S, H,
                           D, workspace, workspace_bytes, stream);
 }

@@ -600,8 +600,14 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
 // (Measured on the 16-frame video block: two heads and four blocks per workgroup beat one
 // head or other block counts; issuing the next block's loads before the products, or using
 // 4-channel items, did not help.)
-template <int D, int kHW, bool kMerge>
+//
+// kTwoQ (the reverse direction reads its own q, k, v): the two slots are the forward and the
+// reverse direction of one head, each with its own state and its own prepped Q rows, and their
+// products accumulate into one output, num = Q_f S_f + Q_r R_f, den = q_f z_f + q_r zR_f.
+template <int D, int kHW, bool kMerge, bool kTwoQ>
 __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) {
+  static_assert(!kTwoQ || kHW == 2, "the two-Q form has one slot per direction");
+  constexpr int kHeads = kTwoQ ? 1 : kHW;  // heads per workgroup
   typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   constexpr int kOct = D / 8, kItems = 64 * kOct / 256, kCT = D / 64, kSP = D + 8;
   __shared__ __attribute__((aligned(16))) f16 qr[kHW][64 * kSP];  // Q_rot rows, padded
@@ -613,7 +619,7 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
   x /= ngrp;
   const int f = x % p.F;
   x /= p.F;
-  const int h0 = (x % (p.H / kHW)) * kHW, b = x / (p.H / kHW);
+  const int h0 = (x % (p.H / kHeads)) * kHeads, b = x / (p.H / kHeads);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const int C = p.H * D, o = tid % kOct;
@@ -624,25 +630,32 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
   const long dir_m = (long)p.B * p.H * p.F * D * D, dir_v = (long)p.B * p.H * p.F * D;
 #pragma unroll
   for (int hh = 0; hh < kHW; ++hh) {
-    const long bhf = ((long)b * p.H + h0 + hh) * p.F + f;
+    const int hd = kTwoQ ? h0 : h0 + hh;
+    const long bhf = ((long)b * p.H + hd) * p.F + f;
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
       for (int k = 0; k < D / 32; ++k) {
         const long e = bhf * D * D + (long)((D / 4) * wave + 16 * ct + li) * D + 32 * k + 8 * lq;
-        const f16x8 sf = *reinterpret_cast<const f16x8*>(p.SdT + e);
-        const f16x8 sr = *reinterpret_cast<const f16x8*>(p.SdT + dir_m + e);
+        if constexpr (kTwoQ) {
+          sa[hh][ct][k] = *reinterpret_cast<const f16x8*>(p.SdT + hh * dir_m + e);
+        } else {
+          const f16x8 sf = *reinterpret_cast<const f16x8*>(p.SdT + e);
+          const f16x8 sr = *reinterpret_cast<const f16x8*>(p.SdT + dir_m + e);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sa[hh][ct][k][j] = (f16)((float)sf[j] + (float)sr[j]);
+          for (int j = 0; j < 8; ++j) sa[hh][ct][k][j] = (f16)((float)sf[j] + (float)sr[j]);
+        }
       }
-    if (tid < D) zsum[hh][tid] = p.zd[bhf * D + tid] + p.zd[dir_v + bhf * D + tid];
-    load8f(p.q_norm_w + (h0 + hh) * D + 8 * o, w[hh]);
+    if (tid < D)
+      zsum[hh][tid] = kTwoQ ? p.zd[hh * dir_v + bhf * D + tid]
+                            : p.zd[bhf * D + tid] + p.zd[dir_v + bhf * D + tid];
+    load8f(p.q_norm_w + hd * D + 8 * o, w[hh]);
   }
   for (int blk = g * grp; blk < (g + 1) * grp; ++blk) {
     const int n0 = f * p.S + blk * 64;
     __syncthreads();  // the previous block's qr and den_part reads are done
     // every load of this thread's items is issued before any of them is used
-    float inv[kItems];
+    float inv[kItems][kTwoQ ? 2 : 1];
     f16x8 tab[kItems][2];  // (cos, sin) pairs of the item's 8 channels
     bf16x8 qx[kItems][kHW];
 #pragma unroll
@@ -652,10 +665,14 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
       const f16x8* tp = reinterpret_cast<const f16x8*>(p.rope_h + (n * D + 8 * o) * 2);
       tab[i][0] = tp[0];
       tab[i][1] = tp[1];
-      inv[i] = p.q_inv_rms[bn];
+      inv[i][0] = p.q_inv_rms[bn];
+      if constexpr (kTwoQ) inv[i][1] = p.q_inv_rms_b[bn];
 #pragma unroll
-      for (int hh = 0; hh < kHW; ++hh)
-        qx[i][hh] = *reinterpret_cast<const bf16x8*>(qkv + bn * 3L * C + (long)(h0 + hh) * D + 8 * o);
+      for (int hh = 0; hh < kHW; ++hh) {
+        const bf16* src = kTwoQ && hh ? static_cast<const bf16*>(p.qkv_bwd) : qkv;
+        const int hd = kTwoQ ? h0 : h0 + hh;
+        qx[i][hh] = *reinterpret_cast<const bf16x8*>(src + bn * 3L * C + (long)hd * D + 8 * o);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
@@ -671,7 +688,7 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
         float xq[8], pos[8], rot[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) xq[j] = (float)qx[i][hh][j];
-        prep8(xq, inv[i], w[hh], cs, sn, 1.f, pos, rot);
+        prep8(xq, inv[i][kTwoQ ? hh : 0], w[hh], cs, sn, 1.f, pos, rot);
         f16x8 v;
         float dp = 0.f;
 #pragma unroll
@@ -687,26 +704,29 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
       }
     }
     __syncthreads();
+    bf16x4_t gv[4][kCT];
+    f32x4 acc[4][kCT];
 #pragma unroll
     for (int hh = 0; hh < kHW; ++hh) {
+      const int hs = kTwoQ ? 0 : hh;  // output head slot
       // lane (li, lq): token n0 + 16 tt + li, value columns (D/4) wave + 16 ct + 4 lq + e
       auto at = [&](int tt) {
-        return (((long)b * p.N + n0 + 16 * tt + li) * p.H + h0 + hh) * D + (D / 4) * wave + 4 * lq;
+        return (((long)b * p.N + n0 + 16 * tt + li) * p.H + h0 + hs) * D + (D / 4) * wave + 4 * lq;
       };
-      bf16x4_t gv[4][kCT];
-      if constexpr (kMerge) {
-        if (p.gate)  // issued before the products, which hide their latency
+      if (!kTwoQ || hh == 0) {
+        if constexpr (kMerge) {
+          if (p.gate)  // issued before the products, which hide their latency
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
+            for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int ct = 0; ct < kCT; ++ct)
-              gv[tt][ct] = *reinterpret_cast<const bf16x4_t*>(static_cast<const bf16*>(p.gate) + at(tt) + 16 * ct);
+              for (int ct = 0; ct < kCT; ++ct)
+                gv[tt][ct] = *reinterpret_cast<const bf16x4_t*>(static_cast<const bf16*>(p.gate) + at(tt) + 16 * ct);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      f32x4 acc[4][kCT];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -715,10 +735,15 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
 #pragma unroll
           for (int ct = 0; ct < kCT; ++ct) acc[tt][ct] = mma16(sa[hh][ct][k], bq, acc[tt][ct]);
         }
+      if (kTwoQ && hh == 0) continue;  // the reverse slot adds its products first
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         float rden = 0.f;
-        if constexpr (kMerge) rden = 1.f / (den_part[hh][16 * tt + li] + p.merge_eps);
+        if constexpr (kMerge) {
+          const float dn = kTwoQ ? den_part[0][16 * tt + li] + den_part[1][16 * tt + li]
+                                 : den_part[hh][16 * tt + li];
+          rden = 1.f / (dn + p.merge_eps);
+        }
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct) {
           if (num) {
@@ -743,9 +768,10 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
         }
       }
     }
-    if (p.den && tid < 64 * kHW) {
+    if (p.den && tid < 64 * kHeads) {
       const int hh = tid / 64, t = tid % 64;
-      static_cast<bf16*>(p.den)[((long)b * p.H + h0 + hh) * p.N + n0 + t] = (bf16)den_part[hh][t];
+      const float dn = kTwoQ ? den_part[0][t] + den_part[1][t] : den_part[hh][t];
+      static_cast<bf16*>(p.den)[((long)b * p.H + h0 + hh) * p.N + n0 + t] = (bf16)dn;
     }
   }
 }
@@ -760,7 +786,8 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
 hipError_t launch_bigdn(const BigdnParams& p_in, hipStream_t stream) {
   BigdnParams p = p_in;
   if (!p.decay_bwd) p.decay_bwd = p.decay;
-  if (!p.beta_bwd) {  // the reverse direction shares the forward statistics
+  const bool rev_stats = p.beta_bwd || p.qkv_bwd;
+  if (!rev_stats) {  // the reverse direction shares the forward statistics
     p.G_b = p.G;
     p.Gz_b = p.Gz;
     p.U_b = p.U;
@@ -783,10 +810,22 @@ hipError_t launch_bigdn(const BigdnParams& p_in, hipStream_t stream) {
   pp.D = p.D;
   hipError_t e = launch_prep(pp, stream);
   if (e != hipSuccess) return e;
+  if (p.qkv_bwd) {  // the inverse RMS of the reverse direction's q and k
+    pp.qkv = p.qkv_bwd;
+    pp.q_inv_rms = p.q_inv_rms_b;
+    pp.k_inv_rms = p.k_inv_rms_b;
+    pp.rope_h = nullptr;
+    e = launch_prep(pp, stream);
+    if (e != hipSuccess) return e;
+  }
   const int nbhf = p.B * p.H * p.F;
-  // the reverse direction's statistics, when its beta differs
+  // the reverse direction's statistics, when its beta or its keys and values differ
   BigdnParams pb = p;
-  pb.beta = p.beta_bwd;
+  if (p.qkv_bwd) {
+    pb.qkv = p.qkv_bwd;
+    pb.k_inv_rms = p.k_inv_rms_b;
+  }
+  if (p.beta_bwd) pb.beta = p.beta_bwd;
   pb.G = p.G_b;
   pb.Gz = p.Gz_b;
   pb.U = p.U_b;
@@ -796,24 +835,27 @@ hipError_t launch_bigdn(const BigdnParams& p_in, hipStream_t stream) {
   const int nblk = p.S / 64;
   int grp = 4;
   while (nblk % grp) grp >>= 1;
-  const int hw = p.H % 2 ? 1 : 2;
+  // (one head per workgroup when the directions read different q)
+  const int hw = p.H % 2 || p.qkv_bwd ? 1 : 2;
   const dim3 og(p.B * (p.H / hw) * p.F * (nblk / grp));
   const bool merge = p.out != nullptr;
-#define GDN_OUT(DD)                                                                                     \
-  do {                                                                                                  \
-    if (hw == 2 && merge) hipLaunchKernelGGL((out_kernel<DD, 2, true>), og, dim3(256), 0, stream, p, grp);  \
-    else if (hw == 2) hipLaunchKernelGGL((out_kernel<DD, 2, false>), og, dim3(256), 0, stream, p, grp);     \
-    else if (merge) hipLaunchKernelGGL((out_kernel<DD, 1, true>), og, dim3(256), 0, stream, p, grp);        \
-    else hipLaunchKernelGGL((out_kernel<DD, 1, false>), og, dim3(256), 0, stream, p, grp);                  \
+#define GDN_OUT(DD)                                                                                          \
+  do {                                                                                                       \
+    if (p.qkv_bwd && merge) hipLaunchKernelGGL((out_kernel<DD, 2, true, true>), og, dim3(256), 0, stream, p, grp);  \
+    else if (p.qkv_bwd) hipLaunchKernelGGL((out_kernel<DD, 2, false, true>), og, dim3(256), 0, stream, p, grp);     \
+    else if (hw == 2 && merge) hipLaunchKernelGGL((out_kernel<DD, 2, true, false>), og, dim3(256), 0, stream, p, grp); \
+    else if (hw == 2) hipLaunchKernelGGL((out_kernel<DD, 2, false, false>), og, dim3(256), 0, stream, p, grp);   \
+    else if (merge) hipLaunchKernelGGL((out_kernel<DD, 1, true, false>), og, dim3(256), 0, stream, p, grp);      \
+    else hipLaunchKernelGGL((out_kernel<DD, 1, false, false>), og, dim3(256), 0, stream, p, grp);                \
   } while (0)
   if (p.D == 128) {
     hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
-    if (p.beta_bwd) hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, pb);
+    if (rev_stats) hipLaunchKernelGGL(frame_stats_kernel<128>, dim3(nbhf), dim3(kStatThreads), 0, stream, pb);
     hipLaunchKernelGGL(scan_kernel<128>, dim3(p.B * p.H * 2 * (128 / 32 + 1)), dim3(256), 0, stream, p);
     GDN_OUT(128);
   } else {
     hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, p);
-    if (p.beta_bwd) hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, pb);
+    if (rev_stats) hipLaunchKernelGGL(frame_stats_kernel<64>, dim3(nbhf), dim3(kStatThreads), 0, stream, pb);
     hipLaunchKernelGGL(scan_kernel<64>, dim3(p.B * p.H * 2 * (64 / 32 + 1)), dim3(256), 0, stream, p);
     GDN_OUT(64);
   }

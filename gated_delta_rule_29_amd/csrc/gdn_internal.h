@@ -70,6 +70,7 @@ struct PrepParams {
 
 struct BigdnParams {
   const void* qkv;
+  const void* qkv_bwd;     // [B, N, 3, H, D] q, k, v of the reverse direction, or nullptr (= qkv)
   const float* beta;       // [B, H, F, S]
   const float* decay;      // [B, H, F]
   const float* decay_bwd;  // [B, H, F] decay of the reverse direction, or nullptr (= decay)
@@ -89,12 +90,15 @@ struct BigdnParams {
   // workspace views
   float* q_inv_rms;  // [B, N]
   float* k_inv_rms;  // [B, N]
+  float* q_inv_rms_b;  // [B, N] of qkv_bwd (when set)
+  float* k_inv_rms_b;  // [B, N]
   _Float16* rope_h;  // [N, D, 2]  RoPE tables as (cos, sin) fp16 pairs
   _Float16* G;       // [B, H, F, D, D]
   _Float16* Gz;      // [B, H, F, D, D]
   float* U;          // [B, H, F, D, D]
   float* uz;         // [B, H, F, D]
-  // statistics of the reverse direction (the same buffers unless beta is overridden for it)
+  // statistics of the reverse direction (the same buffers unless beta or qkv is overridden
+  // for it)
   _Float16* G_b;
   _Float16* Gz_b;
   float* U_b;

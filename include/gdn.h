@@ -219,23 +219,26 @@ GDN_API int bigdn_fwd(const void* qkv, const float* beta, const float* decay, co
 /*
  * bigdn_fwd_merged -- bigdn_fwd with the options of the [SANA fused_gdn.py page]
  * block wrapper (fused_bigdn_func and fused_bidi_merge):
- *   - chunk-causal overrides of the REVERSE direction: beta_bwd [B,H,F,S] and decay_bwd
- *     [B,H,F] fp32 replace beta / decay for that direction only (NULL = the forward one).
- *     A zero decay_bwd at frame f resets the reverse state when frame f is absorbed, so
- *     frames before f see no frame after f.  (qkv_bwd, the third override there, is not
- *     supported: both directions read qkv.)
+ *   - chunk-causal overrides of the REVERSE direction, each NULL = the forward one:
+ *     qkv_bwd [B,N,3,H,D] bf16 (its own q, k, v; the inverse RMS of its q and k is computed
+ *     from it), beta_bwd [B,H,F,S] and decay_bwd [B,H,F] fp32.  A zero decay_bwd at frame f
+ *     resets the reverse state when frame f is absorbed, so frames before f see no frame
+ *     after f; zeroed k or v (qkv_bwd) or beta_bwd at a frame keep that frame out of it.
+ *     With qkv_bwd the outputs sum Q_fwd S_f + Q_bwd R_f and q_fwd z_f + q_bwd zR_f.
  *   - the bidirectional merge epilogue, fused into the output kernel:
  *       out = (num_fwd + num_bwd) / (den_fwd + den_bwd + merge_eps) * SiLU(gate)
  *     out [B,N,H,D] bf16 OUT; gate [B,N,H,D] bf16 or NULL (no gate); the division uses the
  *     fp32 sums before they are rounded.
  *   num [B,N,H,D], den [B,H,N] bf16 OUT as in bigdn_fwd; either may be NULL when out is set.
- *   workspace  at least bigdn_fwd_merged_workspace_bytes(B, F, S, H, D, beta_bwd != NULL)
+ *   workspace  at least bigdn_fwd_merged_workspace_bytes(B, F, S, H, D, has_rev_inputs),
+ *              has_rev_inputs = (qkv_bwd != NULL || beta_bwd != NULL)
  * Errors as bigdn_fwd; GDN_ERR_INVALID also when out and num/den are all NULL, when gate is
  * given without out, or merge_eps < 0.
  */
 GDN_API size_t bigdn_fwd_merged_workspace_bytes(int B, int F, int S, int H, int D,
-                                                int has_beta_bwd);
-GDN_API int bigdn_fwd_merged(const void* qkv, const float* beta, const float* decay,
+                                                int has_rev_inputs);
+GDN_API int bigdn_fwd_merged(const void* qkv, const void* qkv_bwd, const float* beta,
+                             const float* decay,
                              const float* beta_bwd, const float* decay_bwd,
                              const float* q_norm_w, const float* k_norm_w,
                              const float* rope_cos, const float* rope_sin, float k_scale,

@@ -237,15 +237,19 @@ def bigdn(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, eps
 
 
 def bigdn_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, eps=1e-5,
-                 beta_bwd=None, decay_bwd=None, gate=None, merge_eps=1e-6):
-    """BiGDN block with the reverse direction's own beta / decay (chunk-causal overrides; None
-    = the forward ones) and the merge (SANA fused_gdn.py page, fused_bigdn_func and
-    fused_bidi_merge): out = (num_f + num_r) / (den_f + den_r + merge_eps) * SiLU(gate).
+                 beta_bwd=None, decay_bwd=None, gate=None, merge_eps=1e-6, qkv_bwd=None):
+    """BiGDN block with the reverse direction's own q, k, v / beta / decay (chunk-causal
+    overrides; None = the forward ones; the reverse direction's inverse RMS is that of its own
+    q and k) and the merge (SANA fused_gdn.py page, fused_bigdn_func and fused_bidi_merge):
+    out = (num_f + num_r) / (den_f + den_r + merge_eps) * SiLU(gate).
     Returns (out [B,N,H,D], num [B,N,H,D], den [B,H,N])."""
-    p = prep(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, eps)
-    t = (p["q_rot"], p["k_rot"], p["q_pos"], p["k_pos"], p["v"])
+    def tensors(x):
+        p = prep(x, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, eps)
+        return (p["q_rot"], p["k_rot"], p["q_pos"], p["k_pos"], p["v"])
+    t = tensors(qkv)
+    tr = t if qkv_bwd is None else tensors(qkv_bwd)
     nf, df = bigdn_dir(*t, beta, decay, reverse=False)
-    nr, dr = bigdn_dir(*t, beta if beta_bwd is None else beta_bwd,
+    nr, dr = bigdn_dir(*tr, beta if beta_bwd is None else beta_bwd,
                        decay if decay_bwd is None else decay_bwd, reverse=True)
     num, den = nf + nr, df + dr
     out = num / (np.transpose(den, (0, 2, 1))[..., None] + merge_eps)

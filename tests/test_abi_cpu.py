@@ -135,12 +135,13 @@ def test_bigdn_merged_validation_codes():
     L, lib = _lib()
 
     def call(**kw):
-        a = dict(qkv=FAKE, beta=FAKE, decay=FAKE, bb=None, db=None, gate=None, eps_m=1e-6,
-                 out=FAKE, num=None, den=None, F=2, S=64)
+        a = dict(qkv=FAKE, qb=None, beta=FAKE, decay=FAKE, bb=None, db=None, gate=None,
+                 eps_m=1e-6, out=FAKE, num=None, den=None, F=2, S=64, ws=None, ws_n=0)
         a.update(kw)
-        return lib.bigdn_fwd_merged(a["qkv"], a["beta"], a["decay"], a["bb"], a["db"], FAKE, FAKE,
-                                    FAKE, FAKE, 0.1, 1e-5, a["gate"], a["eps_m"], a["out"],
-                                    a["num"], a["den"], 1, a["F"], a["S"], 2, 128, None, 0, None)
+        return lib.bigdn_fwd_merged(a["qkv"], a["qb"], a["beta"], a["decay"], a["bb"], a["db"],
+                                    FAKE, FAKE, FAKE, FAKE, 0.1, 1e-5, a["gate"], a["eps_m"],
+                                    a["out"], a["num"], a["den"], 1, a["F"], a["S"], 2, 128,
+                                    a["ws"], a["ws_n"], None)
 
     assert call(out=None) == L.ERR_INVALID               # nothing to write
     assert call(out=None, num=FAKE) == L.ERR_INVALID     # den missing
@@ -151,3 +152,6 @@ def test_bigdn_merged_validation_codes():
     n0 = lib.bigdn_fwd_merged_workspace_bytes(1, 2, 64, 2, 128, 0)
     n1 = lib.bigdn_fwd_merged_workspace_bytes(1, 2, 64, 2, 128, 1)
     assert n0 == lib.bigdn_fwd_workspace_bytes(1, 2, 64, 2, 128) and n1 > n0
+    # reverse-direction inputs need the larger workspace
+    assert call(ws=FAKE, ws_n=n0, qb=FAKE) == L.ERR_WORKSPACE
+    assert call(ws=FAKE, ws_n=n0, bb=FAKE) == L.ERR_WORKSPACE

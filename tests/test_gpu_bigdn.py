@@ -82,42 +82,50 @@ def test_bigdn_video_workload():
     assert_close("den", den, rd, 2e-2)
 
 
-@pytest.mark.parametrize("B,F,S,H,D,gated,override", [(1, 5, 128, 2, 128, True, True),
-                                                        (2, 3, 64, 3, 64, False, True),
-                                                        (1, 4, 64, 2, 128, True, False),
-                                                        (1, 1, 64, 1, 64, True, True)])
+@pytest.mark.parametrize("B,F,S,H,D,gated,override", [(1, 5, 128, 2, 128, True, 1),
+                                                        (2, 3, 64, 3, 64, False, 1),
+                                                        (1, 4, 64, 2, 128, True, 0),
+                                                        (1, 1, 64, 1, 64, True, 1),
+                                                        (1, 3, 128, 2, 128, True, 2),
+                                                        (2, 2, 64, 3, 64, False, 2)])
 def test_bigdn_merged(B, F, S, H, D, gated, override):
-    """bigdn_fwd_merged: reverse-direction beta / decay overrides (a zero reverse decay at one
-    frame, chunk-causal) and the fused merge epilogue, against the oracle's block."""
+    """bigdn_fwd_merged: reverse-direction overrides (override 1: beta / decay with a zero
+    reverse decay at one frame, chunk-causal; 2: also the reverse direction's own q, k, v, its k
+    and v zero at that frame) and the fused merge epilogue, against the oracle's block."""
     import gated_delta_rule_29_amd as g
 
     w = workloads.bigdn_inputs(B, F, S, H, D, seed=F * S + H)
     gen = torch.Generator().manual_seed(F + D)
     N = F * S
     gate = torch.randn(B, N, H, D, generator=gen).to(torch.bfloat16) if gated else None
-    bb = db = None
+    bb = db = qb = None
     if override:
         bb = torch.sigmoid(torch.randn(B, H, F, S, generator=gen))
         db = w["decay"].clone()
         db[:, :, F // 2] = 0.0
+    if override == 2:
+        qb = workloads.bigdn_inputs(B, F, S, H, D, seed=F * S + H + 1)["qkv"].clone()
+        qb[:, (F // 2) * S:(F // 2 + 1) * S, 1:] = 0
     say("bigdn merged B%d F%d S%d H%d D%d gate%d override%d" % (B, F, S, H, D, gated, override))
     d = _dev(w)
     out, num, den = g.bigdn_fwd_merged(
         d["qkv"], d["beta"], d["decay"], d["q_norm_w"], d["k_norm_w"], d["rope_cos"],
-        d["rope_sin"], w["k_scale"], w["eps"], beta_bwd=None if bb is None else bb.to(DEV),
+        d["rope_sin"], w["k_scale"], w["eps"], qkv_bwd=None if qb is None else qb.to(DEV),
+        beta_bwd=None if bb is None else bb.to(DEV),
         decay_bwd=None if db is None else db.to(DEV), gate=None if gate is None else gate.to(DEV),
         merge_eps=1e-6, want_num_den=True)
     torch.cuda.synchronize()
     ro, rn, rd = oracle.bigdn_merged(w["qkv"], w["beta"], w["decay"], w["q_norm_w"],
                                      w["k_norm_w"], w["rope_cos"], w["rope_sin"], w["k_scale"],
                                      w["eps"], beta_bwd=bb, decay_bwd=db, gate=gate,
-                                     merge_eps=1e-6)
+                                     merge_eps=1e-6, qkv_bwd=qb)
     assert_close("num", num, rn, 2e-2)
     assert_close("den", den, rd, 2e-2)
     assert_close("out", out, ro, 2e-2)
     out_only = g.bigdn_fwd_merged(
         d["qkv"], d["beta"], d["decay"], d["q_norm_w"], d["k_norm_w"], d["rope_cos"],
-        d["rope_sin"], w["k_scale"], w["eps"], beta_bwd=None if bb is None else bb.to(DEV),
+        d["rope_sin"], w["k_scale"], w["eps"], qkv_bwd=None if qb is None else qb.to(DEV),
+        beta_bwd=None if bb is None else bb.to(DEV),
         decay_bwd=None if db is None else db.to(DEV), gate=None if gate is None else gate.to(DEV),
         merge_eps=1e-6)
     torch.cuda.synchronize()

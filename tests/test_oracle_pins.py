@@ -545,3 +545,36 @@ def test_bigdn_merge_gate_is_silu():
     np.testing.assert_allclose(up - dn, base * g.double().numpy(), rtol=1e-12, atol=1e-13)
     zero, _, _ = _bm(w, gate=torch.zeros_like(g))
     assert np.abs(zero).max() == 0.0
+
+
+def test_bigdn_reverse_qkv_override():
+    # the reverse direction's q, k, v and their inverse RMS come from qkv_bwd
+    w = _merged_inputs()
+    base, num, den = _bm(w)
+    # the same tensor as override: the same block
+    same, n1, d1 = _bm(w, qkv_bwd=w["qkv"].clone())
+    np.testing.assert_array_equal(same, base)
+    # q and k scaled by 4 (exact in bf16): the RMS norm of qkv_bwd's own channels removes it
+    # (a negligible norm eps, so that the scaling is exactly invisible)
+    wt = dict(w, eps=1e-30)
+    _, nt, dt = _bm(wt)
+    sc = w["qkv"].clone()
+    sc[:, :, :2] *= 4
+    _, n2, d2 = _bm(wt, qkv_bwd=sc)
+    np.testing.assert_allclose(n2, nt, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(d2, dt, rtol=1e-9, atol=1e-12)
+    # q of qkv_bwd zero: the reverse direction adds nothing to num and den, which then match a
+    # reverse direction with beta_bwd = 0 (no state at all)
+    zq = w["qkv"].clone()
+    zq[:, :, 0] = 0
+    _, n3, d3 = _bm(w, qkv_bwd=zq)
+    _, n4, d4 = _bm(w, beta_bwd=torch.zeros_like(w["beta"]))
+    np.testing.assert_allclose(n3, n4, atol=1e-14)
+    np.testing.assert_allclose(d3, d4, atol=1e-14)
+    # k and v of qkv_bwd zero: the reverse state stays zero, the same result again
+    zkv = w["qkv"].clone()
+    zkv[:, :, 1:] = 0
+    _, n5, d5 = _bm(w, qkv_bwd=zkv)
+    np.testing.assert_allclose(n5, n4, atol=1e-14)
+    np.testing.assert_allclose(d5, d4, atol=1e-14)
+    assert np.abs(n4 - num).max() > 1e-3
