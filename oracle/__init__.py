@@ -10,8 +10,9 @@ Contents
     the plain token-by-token recurrence and its transition matrix (the linear part of the
     map from initial to final state), the packed-varlen tables and driver, the BiGDN
     front end (full-channel RMSNorm, ReLU, k-scale, interleaved-pair RoPE) and the
-    frame-level BiGDN scan in both directions.  This is the reference every GPU result is
-    compared with.
+    frame-level BiGDN scan in both directions, the camera-branch prep (UCPE 4x4 blocks and
+    half-width RoPE) and its numerator-only frame scan with state in and out.  This is the
+    reference every GPU result is compared with.
   * ``forms.py``: independent numpy cross-check forms (global O(T^2) solve, chunked WY
     form, BiGDN product form with flip-and-shift reverse) used only to pin the oracle.
 
@@ -63,6 +64,9 @@ def _load():
         lib.oracle_bigdn_dir.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         lib.oracle_bigdn.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, Dd, Dd, P, P]
         lib.oracle_gdn_transition.argtypes = [I, I, I, I, P, P, P, P, P]
+        lib.oracle_cam_prep.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, Dd, Dd, P, P, P,
+                                        P]
+        lib.oracle_cam_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
@@ -257,3 +261,41 @@ def bigdn_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_sca
         g = _f64(gate)
         out = out * (g / (1.0 + np.exp(-g)))
     return out, num, den
+
+
+def cam_prep(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale,
+             eps=1e-5):
+    """Camera-branch prep (SANA fused_cam_gdn.py page, cam_prep_func): q, k, v [B,N,H,D];
+    proj_q, proj_kv [B,N,4,4]; rope_cos, rope_sin [N, D/2].  Returns q_t, k_t, v_t [B,H,D,N]
+    and inflation [B,H,N]."""
+    q, k, v, qw, kw, pq, pkv, cs, sn = map(
+        _f64, (q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin))
+    B, N, H, D = q.shape
+    outs = [np.empty((B, H, D, N)) for _ in range(3)]
+    infl = np.empty((B, H, N))
+    rc = _load().oracle_cam_prep(B, N, H, D, _p(q), _p(k), _p(v), _p(qw), _p(kw), _p(pq),
+                                 _p(pkv), _p(cs), _p(sn), float(k_scale), float(eps),
+                                 _p(outs[0]), _p(outs[1]), _p(outs[2]), _p(infl))
+    if rc != 0:
+        raise RuntimeError("oracle_cam_prep failed")
+    return outs[0], outs[1], outs[2], infl
+
+
+def cam_scan(q, k, v, beta, decay, reverse=False, init_state=None, want_final=False):
+    """Camera-branch numerator-only frame scan (SANA fused_cam_gdn.py page, cam_scan_func):
+    q, k, v [B,H,D,N]; beta [B,H,F,S]; decay [B,H,F]; init_state [B*H,D,D] (forward only).
+    Returns out [B,H,D,N], or (out, final [B*H,D,D]) with want_final (forward only)."""
+    q, k, v, beta, decay = map(_f64, (q, k, v, beta, decay))
+    B, H, D, N = q.shape
+    F, S = beta.shape[2], beta.shape[3]
+    if reverse and (init_state is not None or want_final):
+        raise NotImplementedError("state in / out is defined for the forward scan only")
+    init = None if init_state is None else _f64(init_state)
+    out = np.empty((B, H, D, N))
+    fin = np.empty((B * H, D, D)) if want_final else None
+    rc = _load().oracle_cam_scan(B, H, D, F, S, int(bool(reverse)), _p(q), _p(k), _p(v),
+                                 _p(beta), _p(decay), None if init is None else _p(init),
+                                 _p(out), None if fin is None else _p(fin))
+    if rc != 0:
+        raise RuntimeError("oracle_cam_scan failed")
+    return (out, fin) if want_final else out

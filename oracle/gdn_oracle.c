@@ -470,3 +470,147 @@ int oracle_bigdn(int B, int F, int S_, int H, int D, const double* qkv, const do
   free(buf);
   return rc;
 }
+
+/*
+ * Camera-branch prep (SANA fused_cam_gdn.py page: _cam_prep_kernel, cam_prep_func and the
+ * torch reference of the prep).  Inputs q, k, v [B,N,H,D]; qw, kw [H*D]; pq, pkv [B,N,4,4]
+ * (row i, column j); cosv, sinv [N, D/2] (the expanded interleaved-pair tables, sin already
+ * signed).  Per token n and head h, with inverse RMS over all H*D channels of the token:
+ *   q_n = relu(q * inv_q * qw),  k_n = relu(k * inv_k * kw) * k_scale,  v_n = v
+ *   first D/2 channels, in groups of four:  y[4g + i] = sum_j P[i][j] x[4g + j]
+ *       (P = pq for q, pkv for k and v)
+ *   last D/2 channels:  y[D/2 + r] = x[D/2 + r] cos[n, r] + x[D/2 + (r ^ 1)] sin[n, r]
+ *   inflation = max(|k_out|^2, 1e-12) / max(|k_n|^2, 1e-12)
+ * Outputs q_t, k_t, v_t [B,H,D,N] (channel-major); inflation [B,H,N].  D/2 must be a
+ * multiple of 4.
+ */
+int oracle_cam_prep(int B, int N, int H, int D, const double* q, const double* k,
+                    const double* v, const double* qw, const double* kw, const double* pq,
+                    const double* pkv, const double* cosv, const double* sinv, double k_scale,
+                    double eps, double* q_t, double* k_t, double* v_t, double* inflation) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0 || (D % 8) != 0) return -1;
+  const long C = (long)H * D;
+  const int Dh = D / 2;
+#pragma omp parallel for schedule(static)
+  for (long bn = 0; bn < (long)B * N; ++bn) {
+    const long b = bn / N, n = bn % N;
+    const double* xr[3] = {q + bn * C, k + bn * C, v + bn * C};
+    double inv[2];
+    for (int which = 0; which < 2; ++which) {
+      double ss = 0.0;
+      for (long c = 0; c < C; ++c) ss += xr[which][c] * xr[which][c];
+      inv[which] = 1.0 / sqrt(ss / (double)C + eps);
+    }
+    const double* P[3] = {pq + bn * 16, pkv + bn * 16, pkv + bn * 16};
+    double* outs[3] = {q_t, k_t, v_t};
+    double xn[512], y[512];
+    for (int h = 0; h < H; ++h) {
+      double pre = 0.0, post = 0.0;
+      for (int which = 0; which < 3; ++which) {
+        const double* x = xr[which] + (long)h * D;
+        for (int d = 0; d < D; ++d) {
+          if (which == 2) {
+            xn[d] = x[d];
+          } else {
+            const double w = (which == 0 ? qw : kw)[(long)h * D + d];
+            double t = x[d] * inv[which] * w;
+            t = t > 0.0 ? t : 0.0;
+            xn[d] = which == 1 ? t * k_scale : t;
+          }
+        }
+        for (int g = 0; g < Dh / 4; ++g)
+          for (int i = 0; i < 4; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < 4; ++j) acc += P[which][i * 4 + j] * xn[4 * g + j];
+            y[4 * g + i] = acc;
+          }
+        for (int r = 0; r < Dh; ++r)
+          y[Dh + r] = xn[Dh + r] * cosv[n * Dh + r] + xn[Dh + (r ^ 1)] * sinv[n * Dh + r];
+        if (which == 1)
+          for (int d = 0; d < D; ++d) {
+            pre += xn[d] * xn[d];
+            post += y[d] * y[d];
+          }
+        for (int d = 0; d < D; ++d) outs[which][(((long)b * H + h) * D + d) * N + n] = y[d];
+      }
+      inflation[((long)b * H + h) * N + n] = (post > 1e-12 ? post : 1e-12) / (pre > 1e-12 ? pre : 1e-12);
+    }
+  }
+  return 0;
+}
+
+/*
+ * Camera-branch scan (SANA fused_cam_gdn.py page: _cam_scan_kernel and cam_scan_func), the
+ * numerator-only frame-level delta rule on channel-major tensors q, k, v [B,H,D,N] (N = F*S),
+ * beta [B,H,F,S], decay [B,H,F].  The state St is [D_k rows, D_v columns] per (b, h).
+ *   forward: for f = 0..F-1: St *= decay[f]; Sp = St; for every token s of frame f:
+ *            St += k_s (beta_s (v_s - Sp^T k_s))^T; then out[:, s] = St^T q_s for the tokens
+ *            of frame f (after the frame's update).
+ *   reverse: frame f reads the state built from the frames after it (frame F-1 reads the
+ *            zero state); absorbing frame f+1 first multiplies the state by decay[f+1].
+ *   init   : forward only, may be NULL: [B*H, D, D] state at the end of a prefix, decayed by
+ *            decay[0] at the first frame like any other state.
+ *   final  : forward only, may be NULL: St after the last frame's update.
+ * Returns -1 for a reverse scan with init or final (there is no cross-prefix reverse state).
+ */
+int oracle_cam_scan(int B, int H, int D, int F, int S_, int reverse, const double* q,
+                    const double* k, const double* v, const double* beta, const double* decay,
+                    const double* init, double* out, double* final_state) {
+  if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S_ <= 0) return -1;
+  if (reverse && (init || final_state)) return -1;
+  const long N = (long)F * S_;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* St = (double*)malloc(sizeof(double) * (size_t)D * D);
+    double* Sp = (double*)malloc(sizeof(double) * (size_t)D * D);
+    double* dv = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!St || !Sp || !dv) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int bh = 0; bh < B * H; ++bh) {
+        const long base = (long)bh * D * N;
+        if (init)
+          memcpy(St, init + (long)bh * D * D, sizeof(double) * (size_t)D * D);
+        else
+          memset(St, 0, sizeof(double) * (size_t)D * D);
+        for (int it = 0; it < F; ++it) {
+          const int f = reverse ? F - 1 - it : it;
+          if (!reverse || it > 0) {
+            const int fa = reverse ? f + 1 : f; /* frame absorbed at this step */
+            const double g = decay[(long)bh * F + fa];
+            for (long e = 0; e < (long)D * D; ++e) St[e] *= g;
+            memcpy(Sp, St, sizeof(double) * (size_t)D * D);
+            for (int s = 0; s < S_; ++s) {
+              const long t = (long)fa * S_ + s;
+              for (int c = 0; c < D; ++c) {
+                double pred = 0.0;
+                for (int r = 0; r < D; ++r) pred += k[base + (long)r * N + t] * Sp[(size_t)r * D + c];
+                dv[c] = beta[(long)bh * N + t] * (v[base + (long)c * N + t] - pred);
+              }
+              for (int r = 0; r < D; ++r) {
+                const double kr = k[base + (long)r * N + t];
+                for (int c = 0; c < D; ++c) St[(size_t)r * D + c] += kr * dv[c];
+              }
+            }
+          }
+          for (int s = 0; s < S_; ++s) {
+            const long t = (long)f * S_ + s;
+            for (int c = 0; c < D; ++c) {
+              double o = 0.0;
+              for (int r = 0; r < D; ++r) o += St[(size_t)r * D + c] * q[base + (long)r * N + t];
+              out[base + (long)c * N + t] = o;
+            }
+          }
+        }
+        if (final_state) memcpy(final_state + (long)bh * D * D, St, sizeof(double) * (size_t)D * D);
+      }
+    }
+    free(St);
+    free(Sp);
+    free(dv);
+  }
+  return fail ? -1 : 0;
+}

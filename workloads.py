@@ -102,7 +102,52 @@ def bigdn_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
             "k_scale": 1.0 / math.sqrt(D) / math.sqrt(S), "eps": 1e-5}
 
 
-# The five workloads, named by what they are.
+def cam_inputs(B, F, S, H, D, seed=0, decay_shift=3.0, translate=0.3):
+    """Camera-branch inputs: raw q, k, v [B,N,H,D] fp32; norm weights [H*D] x2; per-token 4x4
+    camera matrices proj_q = M^T and proj_kv = M^-1 [B,N,4,4] for a random rigid motion M
+    (rotation from the QR factor of a Gaussian matrix, translation N(0, translate^2));
+    RoPE tables [N, D/2] x2; beta [B,H,F,S]; decay [B,H,F]; k_scale = D^-1/2 * S^-1/2."""
+    gen = _gen(seed)
+    N = F * S
+    q = torch.randn(B, N, H, D, generator=gen)
+    k = torch.randn(B, N, H, D, generator=gen)
+    v = torch.randn(B, N, H, D, generator=gen)
+    q_norm_w = 1.0 + 0.1 * torch.randn(H * D, generator=gen)
+    k_norm_w = 1.0 + 0.1 * torch.randn(H * D, generator=gen)
+    a = torch.randn(B * N, 3, 3, generator=gen, dtype=torch.float64)
+    rot, r = torch.linalg.qr(a)
+    rot = rot * torch.sign(torch.diagonal(r, dim1=-2, dim2=-1))[:, None, :]
+    m = torch.zeros(B * N, 4, 4, dtype=torch.float64)
+    m[:, :3, :3] = rot
+    m[:, :3, 3] = translate * torch.randn(B * N, 3, generator=gen, dtype=torch.float64)
+    m[:, 3, 3] = 1.0
+    proj_q = m.transpose(1, 2).reshape(B, N, 4, 4).float().contiguous()
+    proj_kv = torch.linalg.inv(m).reshape(B, N, 4, 4).float().contiguous()
+    beta = torch.sigmoid(torch.randn(B, H, F, S, generator=gen))
+    decay = torch.sigmoid(torch.randn(B, H, F, generator=gen) + decay_shift)
+    rope_cos, rope_sin = rope_tables(N, D // 2)
+    return {"q": q, "k": k, "v": v, "q_norm_w": q_norm_w, "k_norm_w": k_norm_w,
+            "proj_q": proj_q, "proj_kv": proj_kv, "rope_cos": rope_cos, "rope_sin": rope_sin,
+            "beta": beta, "decay": decay, "k_scale": 1.0 / math.sqrt(D) / math.sqrt(S),
+            "eps": 1e-5}
+
+
+def cam_scan_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
+    """Camera-scan inputs in the channel-major layout [B,H,D,N] fp32, with the magnitudes of
+    prepped tensors: q, v ~ N(0, 1), k ~ N(0, k_scale^2) (k_scale = D^-1/2 * S^-1/2); beta
+    [B,H,F,S]; decay [B,H,F]."""
+    gen = _gen(seed)
+    N = F * S
+    ks = 1.0 / math.sqrt(D) / math.sqrt(S)
+    q = torch.randn(B, H, D, N, generator=gen)
+    k = ks * torch.randn(B, H, D, N, generator=gen)
+    v = torch.randn(B, H, D, N, generator=gen)
+    beta = torch.sigmoid(torch.randn(B, H, F, S, generator=gen))
+    decay = torch.sigmoid(torch.randn(B, H, F, generator=gen) + decay_shift)
+    return {"q": q, "k": k, "v": v, "beta": beta, "decay": decay}
+
+
+# The workloads, named by what they are.
 WORKLOADS = {
     "tiny_f32": dict(kind="gdn", B=1, T=256, H=2, K=64, V=64, dtype="f32", seed=0, g_shift=2.0),
     "gdn_bf16_b4h16t4096": dict(kind="gdn", B=4, T=4096, H=16, K=128, V=128, dtype="bf16",
