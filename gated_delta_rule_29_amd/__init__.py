@@ -17,7 +17,7 @@ import torch
 from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
-           "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged",
+           "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
            "gdn_abi_version", "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
@@ -289,3 +289,56 @@ def bigdn_fwd_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k
                               _ptr(ws), ws_n, _stream(dev))
     _lib.check(rc, "bigdn_fwd_merged")
     return (out, num, den) if want_num_den else out
+
+
+def cam_prep(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale,
+             norm_eps=1e-5):
+    """Camera-branch prep.  q, k, v [B,N,H,D] fp32; proj_q, proj_kv [B,N,4,4] fp32; rope_cos,
+    rope_sin [N,D/2] fp32.  Returns (q_t, k_t, v_t) [B,H,D,N] fp32 and inflation [B,H,N]."""
+    B, N, H, D = q.shape
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, (B, N, H, D), torch.float32, dev)
+    _need(q_norm_w, "q_norm_w", (H * D,), torch.float32, dev)
+    _need(k_norm_w, "k_norm_w", (H * D,), torch.float32, dev)
+    _need(proj_q, "proj_q", (B, N, 4, 4), torch.float32, dev)
+    _need(proj_kv, "proj_kv", (B, N, 4, 4), torch.float32, dev)
+    _need(rope_cos, "rope_cos", (N, D // 2), torch.float32, dev)
+    _need(rope_sin, "rope_sin", (N, D // 2), torch.float32, dev)
+    outs = [torch.empty(B, H, D, N, dtype=torch.float32, device=dev) for _ in range(3)]
+    infl = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    ws_n = lib.cam_prep_workspace_bytes(B, N)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.cam_prep(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(proj_q),
+                      _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin), float(k_scale),
+                      float(norm_eps), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(infl),
+                      B, N, H, D, _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "cam_prep")
+    return outs[0], outs[1], outs[2], infl
+
+
+def cam_scan(q, k, v, beta, decay, *, reverse=False, init_state=None, save_final_state=False):
+    """Camera-branch numerator-only frame scan.  q, k, v [B,H,D,N] fp32 (channel-major);
+    beta [B,H,F,S]; decay [B,H,F]; init_state [B*H,D,D] fp32 (forward only).  Returns out
+    [B,H,D,N] fp32, or (out, final_state [B*H,D,D]) with save_final_state (forward only)."""
+    B, H, D, N = q.shape
+    dev = q.device
+    F, S = beta.shape[2], beta.shape[3]
+    if F * S != N:
+        raise ValueError("q must be [B,H,D,N] with N = F*S")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, (B, H, D, N), torch.float32, dev)
+    _need(beta, "beta", (B, H, F, S), torch.float32, dev)
+    _need(decay, "decay", (B, H, F), torch.float32, dev)
+    _need(init_state, "init_state", (B * H, D, D), torch.float32, dev)
+    out = torch.empty(B, H, D, N, dtype=torch.float32, device=dev)
+    fin = torch.empty(B * H, D, D, dtype=torch.float32, device=dev) if save_final_state else None
+    lib = _lib.load()
+    ws_n = lib.cam_scan_workspace_bytes(B, H, D, F)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.cam_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), int(bool(reverse)),
+                      _ptr(init_state), _ptr(fin), _ptr(out), B, H, D, F, S, _ptr(ws), ws_n,
+                      _stream(dev))
+    _lib.check(rc, "cam_scan")
+    return (out, fin) if save_final_state else out

@@ -38,6 +38,10 @@ SIGNATURES = {
     "bigdn_fwd_merged_workspace_bytes": (SZ, [I, I, I, I, I, I]),
     "bigdn_fwd_merged": (I, [P, P, P, P, P, P, P, P, P, P, F, F, P, F, P, P, P, I, I, I, I, I, P,
                              SZ, P]),
+    "cam_prep_workspace_bytes": (SZ, [I, I]),
+    "cam_prep": (I, [P, P, P, P, P, P, P, P, P, F, F, P, P, P, P, I, I, I, I, P, SZ, P]),
+    "cam_scan_workspace_bytes": (SZ, [I, I, I, I]),
+    "cam_scan": (I, [P, P, P, P, P, I, P, P, P, I, I, I, I, I, P, SZ, P]),
 }
 
 _lib = None

@@ -405,4 +405,88 @@ int bigdn_fwd(const void* qkv, const float* beta, const float* decay, const floa
                           D, workspace, workspace_bytes, stream);
 }
 
+
+// ---- camera branch ----------------------------------------------------------------------
+
+size_t cam_prep_workspace_bytes(int B, int N) {
+  if (B <= 0 || N <= 0) return 0;
+  return 2 * al256((size_t)B * N * 4);
+}
+
+int cam_prep(const float* q, const float* k, const float* v, const float* q_norm_w,
+             const float* k_norm_w, const float* proj_q, const float* proj_kv,
+             const float* rope_cos, const float* rope_sin, float k_scale, float norm_eps,
+             float* q_out, float* k_out, float* v_out, float* inflation, int B, int N, int H,
+             int D, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !q_norm_w || !k_norm_w || !proj_q || !proj_kv || !rope_cos || !rope_sin ||
+      !q_out || !k_out || !v_out || !inflation)
+    return fail(GDN_ERR_INVALID, "every input and output pointer of cam_prep must be non-null");
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0)
+    return fail(GDN_ERR_INVALID, "B, N, H, D must be positive (got %d, %d, %d, %d)", B, N, H, D);
+  if (D % 8) return fail(GDN_ERR_INVALID, "D must be even with D/2 a multiple of 4, got %d", D);
+  if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
+  if (N % 4) return fail(GDN_ERR_UNSUPPORTED, "N must be a multiple of 4, got %d", N);
+  if ((int64_t)B * N > INT32_MAX || (int64_t)B * H * ((N + 63) / 64) > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "B*N exceeds the grid limit");
+  if (!(norm_eps > 0.f)) return fail(GDN_ERR_INVALID, "norm_eps must be positive");
+  const size_t need = cam_prep_workspace_bytes(B, N);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  gdn::CamPrepParams p{};
+  p.q = q; p.k = k; p.v = v; p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w;
+  p.proj_q = proj_q; p.proj_kv = proj_kv; p.rope_cos = rope_cos; p.rope_sin = rope_sin;
+  p.k_scale = k_scale; p.eps = norm_eps;
+  p.q_out = q_out; p.k_out = k_out; p.v_out = v_out; p.inflation = inflation;
+  p.q_inv_rms = static_cast<float*>(workspace);
+  p.k_inv_rms = reinterpret_cast<float*>(static_cast<char*>(workspace) + al256((size_t)B * N * 4));
+  p.B = B; p.N = N; p.H = H; p.D = D;
+  hipError_t e = gdn::launch_cam_prep(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cam_prep launch");
+  return ok();
+}
+
+size_t cam_scan_workspace_bytes(int B, int H, int D, int F) {
+  if (B <= 0 || H <= 0 || D <= 0 || F <= 0) return 0;
+  const size_t mats = (size_t)B * H * F * D * D;
+  return al256(mats * 2) + al256(mats * 4) + al256(mats * 2);
+}
+
+int cam_scan(const float* q, const float* k, const float* v, const float* beta,
+             const float* decay, int reverse, const float* init_state, float* final_state,
+             float* out, int B, int H, int D, int F, int S, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !beta || !decay || !out)
+    return fail(GDN_ERR_INVALID, "q, k, v, beta, decay and out must be non-null");
+  if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S <= 0)
+    return fail(GDN_ERR_INVALID, "B, H, D, F, S must be positive (got %d, %d, %d, %d, %d)", B, H,
+                D, F, S);
+  if (reverse && (init_state || final_state))
+    return fail(GDN_ERR_UNSUPPORTED,
+                "state in / out is defined for the forward scan only (reverse=1 with a state)");
+  if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
+  if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
+  if (F > 65535) return fail(GDN_ERR_UNSUPPORTED, "F must be <= 65535, got %d", F);
+  if ((int64_t)F * S > INT32_MAX || (int64_t)B * H * F * (S / 64) > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "F*S exceeds the grid limit");
+  const size_t mats = (size_t)B * H * F * D * D;
+  const size_t need = cam_scan_workspace_bytes(B, H, D, F);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  gdn::CamScanParams p{};
+  p.q = q; p.k = k; p.v = v; p.beta = beta; p.decay = decay; p.reverse = reverse ? 1 : 0;
+  p.init_state = init_state; p.final_state = final_state; p.out = out;
+  p.B = B; p.H = H; p.D = D; p.F = F; p.S = S;
+  p.G = reinterpret_cast<_Float16*>(ws);
+  p.U = reinterpret_cast<float*>(ws + al256(mats * 2));
+  p.SdT = reinterpret_cast<_Float16*>(ws + al256(mats * 2) + al256(mats * 4));
+  hipError_t e = gdn::launch_cam_scan(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cam_scan launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -25,6 +25,7 @@
 // Products use fp16 operands and fp32 accumulation; the scanned state is fp32.
 #include "gdn_device.h"
 #include "gdn_dma.h"
+#include "gdn_frame.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
 
@@ -162,28 +163,6 @@ __global__ __launch_bounds__(kPrepThreads) void rms_prep_kernel(const PrepParams
   }
 }
 
-// Workspace layouts of G and U (written by frame_stats, read by scan), per (b, h, frame),
-// with kRT = D / 64 row tiles per scan wave and 32-column scan blocks:
-//   G: A-operand order, element (r, c) at ((((r / (D/4)) kRT + (r % (D/4)) / 16) (D/32)
-//      + c / 32) 64 + ((c / 8) % 4) 16 + r % 16) 8 + c % 8, so a scan lane's 16-byte
-//      operand is one load and a wave's loads are contiguous;
-//   U: accumulator order, element (r, c) at (c / 32) 32D + ((((r / (D/4)) kRT
-//      + (r % (D/4)) / 16) 2 + (c % 32) / 16) 64 + ((r % 16) / 4) 16 + c % 16) 4 + r % 4.
-template <int D>
-__device__ __forceinline__ long g_lane_index(int r, int c) {
-  constexpr int kRT = D / 64;
-  return ((((long)(r / (D / 4)) * kRT + (r % (D / 4)) / 16) * (D / 32) + c / 32) * 64 +
-          ((c / 8) & 3) * 16 + (r & 15)) * 8 + (c & 7);
-}
-template <int D>
-__device__ __forceinline__ long u_lane_index(int r, int c) {
-  constexpr int kRT = D / 64;
-  return (long)(c >> 5) * (32 * D) +
-         ((((long)(r / (D / 4)) * kRT + (r % (D / 4)) / 16) * 2 + ((c >> 4) & 1)) * 64 +
-          ((r & 15) >> 2) * 16 + (c & 15)) * 4 +
-         (r & 3);
-}
-
 // ---- frame statistics -------------------------------------------------------------------
 // One workgroup of twelve waves per (b, h, frame) computes all three statistics over the
 // frame's tokens, 64 at a time:
@@ -205,21 +184,6 @@ __device__ __forceinline__ long u_lane_index(int r, int c) {
 // tokens 8lq + j; the accumulator of such a pair of operands holds row channel
 // 32Gb + 8lq + 4t + e and column channel 32Gb' + 8(li >> 2) + 4t' + (li & 3).
 constexpr int kStatThreads = 768;
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef f16 f16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f16x8 tr_pair(const f16* p0, const f16* p1) {
-  auto rd = [](const f16* p) {
-    return __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(uintptr_t)(const __attribute__((address_space(3))) char*)p));
-  };
-  const u32x4v w = __builtin_shufflevector(rd(p0), rd(p1), 0, 1, 2, 3);
-  return __builtin_bit_cast(f16x8, w);
-}
 
 template <int D>
 __global__ __launch_bounds__(kStatThreads) void frame_stats_kernel(const BigdnParams p) {
@@ -441,7 +405,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   constexpr int kNG = kRT * (D / 32);          // 1 KB G transfers per wave and frame
   constexpr int kStage = (kNG + kRT * kCT) * 1024;  // bytes per wave and ring stage
   constexpr int kLd = kNG + kRT * kCT;         // loads per frame
-  constexpr int kNB = 2 * (D / 32 + 1);        // workgroups per (b, h)
+  // workgroups per (b, h): per direction run, one per 32-column block, plus z if it runs
+  const int nb = (p.scan_dirs == 3 ? 2 : 1) * (D / 32 + p.scan_z);
   __shared__ __attribute__((aligned(1024))) char ring[4 * 3 * kStage];
   // state^T as fp16 operand, [32 columns][D rows].  For D = 128 the 16-byte chunks of a row
   // are XOR-swizzled by the column, so the 16 columns of a B-operand read hit distinct banks
@@ -459,13 +424,14 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   int slot, bh;
   if (p.B * p.H % 8 == 0) {
     const int s8 = blockIdx.x / 8;
-    bh = blockIdx.x % 8 + 8 * (s8 / kNB);
-    slot = s8 % kNB;
+    bh = blockIdx.x % 8 + 8 * (s8 / nb);
+    slot = s8 % nb;
   } else {
-    slot = blockIdx.x % kNB;
-    bh = blockIdx.x / kNB;
+    slot = blockIdx.x % nb;
+    bh = blockIdx.x / nb;
   }
-  const int rev = slot & 1, cb = slot >> 1;
+  const int rev = p.scan_dirs == 3 ? slot & 1 : p.scan_dirs == 2;
+  const int cb = p.scan_dirs == 3 ? slot >> 1 : slot;
   const bool zb = cb == D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -507,6 +473,15 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   for (int t = 0; t < kRT; ++t)
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) s[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the forward state entering frame 0 (not for z)
+  const long st0 = (long)bh * D * D + cb * 32;
+  if (p.s_init && !rev && !zb)
+#pragma unroll
+    for (int t = 0; t < kRT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[t][ct][e] = p.s_init[st0 + (long)row_of(t, e) * D + 16 * ct + li];
   // s <- d (s - G s) + U with the operands of ring stage stg; writes and reads st[ph]
   auto step = [&](int stg, int ph, float dcy) {
     const char* sb = ring + (wave * 3 + stg) * kStage;
@@ -554,7 +529,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
   };
   // the state of frame fa: fp16 transposed (four consecutive rows of one column per lane,
   // 8 bytes) or, for z, fp32 entries of column 0
-  _Float16* sdt = p.SdT + (long)rev * p.B * p.H * F * D * D + mat0;
+  _Float16* sdt = p.SdT + (p.dir_slots == 2 ? (long)rev * p.B * p.H * F * D * D : 0L) + mat0;
   float* zd = p.zd + ((long)rev * p.B * p.H + bh) * F * D;
   auto store_state = [&](int fa) {
 #pragma unroll
@@ -585,6 +560,13 @@ __global__ __launch_bounds__(256) void scan_kernel(const BigdnParams p) {
     step(i % 3, i & 1, dcy);
     store_state(rev ? F - 2 - i : i);
   }
+  if (p.s_final && !rev && !zb)
+#pragma unroll
+    for (int t = 0; t < kRT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.s_final[st0 + (long)row_of(t, e) * D + 16 * ct + li] = s[t][ct][e];
   // no transfer may still be writing the ring when the workgroup ends
   wait_vm0();
 }
@@ -785,6 +767,11 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
 
 hipError_t launch_bigdn(const BigdnParams& p_in, hipStream_t stream) {
   BigdnParams p = p_in;
+  p.scan_dirs = 3;
+  p.scan_z = 1;
+  p.dir_slots = 2;
+  p.s_init = nullptr;
+  p.s_final = nullptr;
   if (!p.decay_bwd) p.decay_bwd = p.decay;
   const bool rev_stats = p.beta_bwd || p.qkv_bwd;
   if (!rev_stats) {  // the reverse direction shares the forward statistics
@@ -860,6 +847,15 @@ hipError_t launch_bigdn(const BigdnParams& p_in, hipStream_t stream) {
     GDN_OUT(64);
   }
 #undef GDN_OUT
+  return hipGetLastError();
+}
+
+hipError_t launch_frame_scan(const BigdnParams& p, hipStream_t stream) {
+  const int nb = (p.scan_dirs == 3 ? 2 : 1) * (p.D / 32 + p.scan_z);
+  if (p.D == 128)
+    hipLaunchKernelGGL(scan_kernel<128>, dim3(p.B * p.H * nb), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(scan_kernel<64>, dim3(p.B * p.H * nb), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

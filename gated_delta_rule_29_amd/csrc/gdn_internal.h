@@ -103,9 +103,56 @@ struct BigdnParams {
   _Float16* Gz_b;
   float* U_b;
   float* uz_b;
-  _Float16* SdT;     // [2, B, H, F, D, D]  S_f^T (forward) and R_f^T (reverse)
+  _Float16* SdT;     // [dir_slots, B, H, F, D, D]  S_f^T (forward) and R_f^T (reverse)
   float* zd;         // [2, B, H, F, D]     z_f and zR_f
+  // scan set-up: directions run (1 forward, 2 reverse, 3 both), whether the z block runs,
+  // SdT direction slots (2: indexed by direction; 1: the one direction run), and the forward
+  // state in / out ([B*H, D, D] fp32, keys as rows; nullable)
+  int scan_dirs, scan_z, dir_slots;
+  const float* s_init;
+  float* s_final;
 };
+
+// camera branch (gdn_cam.hip)
+struct CamPrepParams {
+  const float* q;  // [B, N, H, D] fp32
+  const float* k;
+  const float* v;
+  const float* q_norm_w;  // [H*D]
+  const float* k_norm_w;
+  const float* proj_q;    // [B, N, 4, 4]
+  const float* proj_kv;
+  const float* rope_cos;  // [N, D/2]
+  const float* rope_sin;
+  float k_scale, eps;
+  float* q_out;  // [B, H, D, N] fp32
+  float* k_out;
+  float* v_out;
+  float* inflation;  // [B, H, N]
+  float* q_inv_rms;  // [B, N] workspace
+  float* k_inv_rms;
+  int B, N, H, D;
+};
+struct CamScanParams {
+  const float* q;  // [B, H, D, N] fp32
+  const float* k;
+  const float* v;
+  const float* beta;   // [B, H, F, S]
+  const float* decay;  // [B, H, F]
+  int reverse;
+  const float* init_state;  // [B*H, D, D] or nullptr (forward only)
+  float* final_state;       // [B*H, D, D] or nullptr (forward only)
+  float* out;               // [B, H, D, N] fp32
+  int B, H, D, F, S;
+  // workspace views
+  _Float16* G;    // [B, H, F, D, D]
+  float* U;       // [B, H, F, D, D]
+  _Float16* SdT;  // [B, H, F, D, D]
+};
+hipError_t launch_cam_prep(const CamPrepParams& p, hipStream_t stream);
+hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream);
+// the frame scan of gdn_bigdn.hip, for one direction without z
+hipError_t launch_frame_scan(const BigdnParams& p, hipStream_t stream);
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
 hipError_t launch_bigdn(const BigdnParams& p, hipStream_t stream);

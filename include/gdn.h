@@ -246,6 +246,58 @@ GDN_API int bigdn_fwd_merged(const void* qkv, const void* qkv_bwd, const float* 
                              void* num, void* den, int B, int F, int S, int H, int D,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * cam_prep -- camera-branch prep of the SANA video block ([SANA fused_cam_gdn.py page],
+ * _cam_prep_kernel and cam_prep_func), per token n and head h:
+ *   q_n = relu(q * inv_rms_q * q_norm_w),  k_n = relu(k * inv_rms_k * k_norm_w) * k_scale,
+ *   v_n = v, with inv_rms = 1/sqrt(mean over all H*D channels of the token of x^2 + norm_eps);
+ *   channels [0, D/2): groups of four mixed by the token's camera matrix,
+ *     y[4g+i] = sum_j P[i][j] x[4g+j]  (P = proj_q for q, proj_kv for k and v);
+ *   channels [D/2, D): interleaved-pair RoPE, y[D/2+r] = x[D/2+r] cos[n,r] + x[D/2+(r^1)] sin[n,r];
+ *   inflation = max(|k_out|^2, 1e-12) / max(|k_n|^2, 1e-12).
+ *   q, k, v            [B,N,H,D] fp32 IN (device)
+ *   q_norm_w, k_norm_w [H*D] fp32 IN
+ *   proj_q, proj_kv    [B,N,4,4] fp32 IN (row i, column j)
+ *   rope_cos, rope_sin [N,D/2] fp32 IN: expanded interleaved-pair tables (sin[n,2i] = -sin,
+ *                      sin[n,2i+1] = +sin of the pair's angle)
+ *   q_out, k_out, v_out [B,H,D,N] fp32 OUT (channel-major); inflation [B,H,N] fp32 OUT
+ *   workspace          at least cam_prep_workspace_bytes(B, N), 256-byte aligned (inverse RMS)
+ * Supported: D in {64, 128}, N a multiple of 4 (GDN_ERR_UNSUPPORTED otherwise).
+ * GDN_ERR_INVALID for null pointers, non-positive sizes, norm_eps <= 0.
+ */
+GDN_API size_t cam_prep_workspace_bytes(int B, int N);
+GDN_API int cam_prep(const float* q, const float* k, const float* v, const float* q_norm_w,
+                     const float* k_norm_w, const float* proj_q, const float* proj_kv,
+                     const float* rope_cos, const float* rope_sin, float k_scale, float norm_eps,
+                     float* q_out, float* k_out, float* v_out, float* inflation, int B, int N,
+                     int H, int D, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cam_scan -- camera-branch numerator-only frame scan ([SANA fused_cam_gdn.py page],
+ * _cam_scan_kernel and cam_scan_func).  Per (b, h), state St [D_k rows, D_v columns]:
+ *   forward: for each frame f: St *= decay[f]; St += K_f diag(beta_f) (V_f - K_f^T St)^T with
+ *            every token of the frame predicting from the same decayed St; the frame's
+ *            outputs are out[:, n] = St^T q_n (after the update).
+ *   reverse: frame f reads the state built from the frames after it (zero for the last);
+ *            absorbing frame f+1 first multiplies the state by decay[f+1].
+ *   q, k, v     [B,H,D,N] fp32 IN (channel-major, N = F*S); beta [B,H,F,S], decay [B,H,F] fp32 IN
+ *   init_state  [B*H,D,D] fp32 IN or NULL: state at the end of a prefix (decayed by decay[0]
+ *               at the first frame); forward only
+ *   final_state [B*H,D,D] fp32 OUT or NULL: St after the last frame; forward only
+ *   out         [B,H,D,N] fp32 OUT
+ *   workspace   at least cam_scan_workspace_bytes(B, H, D, F), 256-byte aligned
+ * Products use fp16 operands with fp32 accumulation (the page's scan uses TF32 dots) and the
+ * state is kept in fp32; operands must lie within fp16 range (the prep's outputs do).
+ * Supported: D in {64, 128}, S a multiple of 64, F <= 65535 (GDN_ERR_UNSUPPORTED otherwise);
+ * GDN_ERR_UNSUPPORTED also for reverse != 0 with init_state or final_state (the page raises
+ * NotImplementedError there).  GDN_ERR_INVALID for null pointers or non-positive sizes.
+ */
+GDN_API size_t cam_scan_workspace_bytes(int B, int H, int D, int F);
+GDN_API int cam_scan(const float* q, const float* k, const float* v, const float* beta,
+                     const float* decay, int reverse, const float* init_state, float* final_state,
+                     float* out, int B, int H, int D, int F, int S, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -155,3 +155,39 @@ def test_bigdn_merged_validation_codes():
     # reverse-direction inputs need the larger workspace
     assert call(ws=FAKE, ws_n=n0, qb=FAKE) == L.ERR_WORKSPACE
     assert call(ws=FAKE, ws_n=n0, bb=FAKE) == L.ERR_WORKSPACE
+
+
+def test_cam_validation_codes():
+    L, lib = _lib()
+
+    def prep(**kw):
+        a = dict(q=FAKE, N=128, D=128, ws=None, ws_n=0, eps=1e-5)
+        a.update(kw)
+        return lib.cam_prep(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1,
+                            a["eps"], FAKE, FAKE, FAKE, FAKE, 1, a["N"], 2, a["D"], a["ws"],
+                            a["ws_n"], None)
+
+    assert prep(q=None) == L.ERR_INVALID
+    assert prep(D=60) == L.ERR_INVALID      # D/2 not a multiple of 4
+    assert prep(D=96) == L.ERR_UNSUPPORTED
+    assert prep(N=6) == L.ERR_UNSUPPORTED   # N a multiple of 4
+    assert prep(eps=0.0) == L.ERR_INVALID
+    assert prep() == L.ERR_WORKSPACE
+    assert lib.cam_prep_workspace_bytes(2, 100) == 2 * 1024
+
+    def scan(**kw):
+        a = dict(q=FAKE, rev=0, init=None, fin=None, D=128, F=3, S=64, ws=None, ws_n=0)
+        a.update(kw)
+        return lib.cam_scan(a["q"], FAKE, FAKE, FAKE, FAKE, a["rev"], a["init"], a["fin"], FAKE,
+                            1, 2, a["D"], a["F"], a["S"], a["ws"], a["ws_n"], None)
+
+    assert scan(q=None) == L.ERR_INVALID
+    assert scan(F=0) == L.ERR_INVALID
+    assert scan(rev=1, fin=FAKE) == L.ERR_UNSUPPORTED   # state in / out: forward only
+    assert scan(rev=1, init=FAKE) == L.ERR_UNSUPPORTED
+    assert scan(S=100) == L.ERR_UNSUPPORTED
+    assert scan(D=32) == L.ERR_UNSUPPORTED
+    assert scan() == L.ERR_WORKSPACE
+    n = lib.cam_scan_workspace_bytes(1, 2, 128, 3)
+    assert n == 2 * 3 * 128 * 128 * (2 + 4 + 2)
+    assert scan(ws=FAKE, ws_n=n - 1) == L.ERR_WORKSPACE

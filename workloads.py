@@ -159,6 +159,9 @@ WORKLOADS = {
     # decay 0 at every fourth frame) and the merge epilogue with a SiLU gate
     "bigdn_video_merged_f16x1024": dict(kind="bigdn_merged", B=1, F=16, S=1024, H=16, D=128,
                                         seed=0),
+    # the camera branch of the same video block (fp32): camera prep, then the forward and
+    # the reverse numerator-only frame scans
+    "cam_video_f16x1024": dict(kind="cam", B=1, F=16, S=1024, H=16, D=128, seed=0),
     "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
                                     dtype="bf16", seed=0, g_shift=3.0, per_key=True,
                                     save=True),
@@ -188,4 +191,6 @@ def make(name):
         inp["decay_bwd"][:, :, ::4] = 0.0
         inp["gate"] = torch.randn(B, N, H, D, generator=gen).to(torch.bfloat16)
         return inp
+    if kind == "cam":
+        return cam_inputs(**w)
     raise KeyError(name)
