@@ -77,6 +77,19 @@ def alg_bytes_bigdn(B, F, S, H, D):
             + 2 * H * D * 4 + B * N * H * D * 2 + B * H * N * 2)
 
 
+def alg_bytes_cam(B, F, S, H, D):
+    """Minimum HBM bytes of the camera branch step (fp32): the prep reads q, k, v, the camera
+    matrices, the half-width RoPE tables and norm weights once and writes q_t, k_t, v_t and
+    the inflation; each scan direction reads q_t, k_t, v_t, beta and decay once and writes
+    its output."""
+    N = F * S
+    C = H * D
+    prep = 3 * B * N * C * 4 + 2 * B * N * 16 * 4 + 2 * N * (D // 2) * 4 + 2 * C * 4 \
+        + 3 * B * N * C * 4 + B * H * N * 4
+    scan = 3 * B * N * C * 4 + B * H * N * 4 + B * H * F * 4 + B * N * C * 4
+    return prep + 2 * scan
+
+
 def kernel_source_hash():
     """Hash of every kernel source: a counter summary is valid only for the code it measured."""
     h = hashlib.sha256()
@@ -127,6 +140,23 @@ def cpu_baseline(kind, inp, max_chains=64):
             decay_bwd=inp["decay_bwd"], gate=inp["gate"], merge_eps=1e-6),
             "whole merged block: prep + both directions + merge, %d heads x %d tokens"
             % (H, N), B * N * H)
+    if kind == "cam":
+        B, N, H, D = inp["q"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        fs = min(F, 8)
+        n = fs * S
+        sub = {k: oracle._f64(inp[k][:, :n]) for k in ("q", "k", "v", "proj_q", "proj_kv")}
+
+        def run():
+            qt, kt, vt, _ = oracle.cam_prep(sub["q"], sub["k"], sub["v"], inp["q_norm_w"],
+                                            inp["k_norm_w"], sub["proj_q"], sub["proj_kv"],
+                                            inp["rope_cos"][:n], inp["rope_sin"][:n],
+                                            inp["k_scale"], inp["eps"])
+            for rev in (False, True):
+                oracle.cam_scan(qt, kt, vt, inp["beta"][:, :, :fs], inp["decay"][:, :, :fs],
+                                reverse=rev)
+        return _cpu_time(run, "camera prep + both scan directions on the first %d of %d frames, "
+                         "all %d heads (%d tokens)" % (fs, F, H, n), B * n * H)
     if kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -277,6 +307,25 @@ def main():
                                         s["k_norm_w"], s["rope_cos"], s["rope_sin"],
                                         s["k_scale"], s["eps"], decay_bwd=s["decay_bwd"],
                                         gate=s["gate"], merge_eps=1e-6)
+    elif kind == "cam":
+        B, N, H, D = inp["q"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        dt = torch.float32
+        th = B * N * H
+        alg = alg_bytes_cam(B, F, S, H, D)
+        kernel = "cam_prep + cam_scan forward + cam_scan reverse (8 kernels, whole step)"
+        config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
+                  "state": "fp32", "products": "fp16 operands, fp32 accumulation",
+                  "step": "camera prep, then the forward and the reverse frame scans"}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            qt, kt, vt, infl = gdn.cam_prep(s["q"], s["k"], s["v"], s["q_norm_w"],
+                                            s["k_norm_w"], s["proj_q"], s["proj_kv"],
+                                            s["rope_cos"], s["rope_sin"], s["k_scale"], s["eps"])
+            fwd = gdn.cam_scan(qt, kt, vt, s["beta"], s["decay"])
+            rev = gdn.cam_scan(qt, kt, vt, s["beta"], s["decay"], reverse=True)
+            return fwd, rev, infl
     elif kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

@@ -30,156 +30,189 @@ namespace gdn {
 namespace {
 
 // ---- inverse RMS ------------------------------------------------------------------------
-// One workgroup per token: 1 / sqrt(mean of x^2 over the H*D channels + eps), q and k.
+// One wave per token (eight tokens per workgroup): 1 / sqrt(mean of x^2 over the H*D channels
+// + eps) of q and k; a lane reads 16-byte pieces, so a wave's load covers 1 KB of the row.
+constexpr int kRmsTokens = 8;
 __global__ __launch_bounds__(256) void cam_rms_kernel(const CamPrepParams p) {
-  __shared__ float red[8];
-  const long bn = blockIdx.x;
-  const int C = p.H * p.D;
-  const float* qr = p.q + bn * C;
-  const float* kr = p.k + bn * C;
-  float sq = 0.f, sk = 0.f;
-  for (int i = threadIdx.x; i < C / 4; i += 256) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(qr)[i];
-    const f32x4 b = reinterpret_cast<const f32x4*>(kr)[i];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int C4 = p.H * p.D / 4;
+  const long total = (long)p.B * p.N;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sq += a[j] * a[j];
-      sk += b[j] * b[j];
+  for (int r = 0; r < kRmsTokens / 4; ++r) {
+    const long bn = (long)blockIdx.x * kRmsTokens + 4 * r + wave;
+    if (bn >= total) break;
+    const f32x4* qr = reinterpret_cast<const f32x4*>(p.q + bn * 4 * C4);
+    const f32x4* kr = reinterpret_cast<const f32x4*>(p.k + bn * 4 * C4);
+    float sq = 0.f, sk = 0.f;
+#pragma unroll 8
+    for (int i = lane; i < C4; i += 64) {
+      const f32x4 a = qr[i], b = kr[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sq += a[j] * a[j];
+        sk += b[j] * b[j];
+      }
     }
-  }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    sq += __shfl_xor(sq, off, 64);
-    sk += __shfl_xor(sk, off, 64);
-  }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    red[wave] = sq;
-    red[4 + wave] = sk;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    p.q_inv_rms[bn] = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)C + p.eps);
-    p.k_inv_rms[bn] = rsqrtf((red[4] + red[5] + red[6] + red[7]) / (float)C + p.eps);
+    for (int off = 32; off > 0; off >>= 1) {
+      sq += __shfl_xor(sq, off, 64);
+      sk += __shfl_xor(sk, off, 64);
+    }
+    if (lane == 0) {
+      p.q_inv_rms[bn] = rsqrtf(sq / (float)(4 * C4) + p.eps);
+      p.k_inv_rms[bn] = rsqrtf(sk / (float)(4 * C4) + p.eps);
+    }
   }
 }
 
 // ---- prep -------------------------------------------------------------------------------
-// One workgroup per (b, h, 64-token tile).  A thread takes (4-token quad, 4-channel group)
-// items with a fixed group g (so its norm weights and table half are fixed); a wave's loads
-// are whole 512-byte head rows of a token.  Each tensor in turn is transformed, written to an
-// LDS tile [D][64] (row stride 68 floats) and stored as 256-byte runs of its [B, H, D, N] rows.
+// One workgroup of 4D threads per (b, h, 64-token tile).  The first 2D threads (whole waves)
+// take the camera-matrix half of the channels, the others the RoPE half, so neither branch
+// diverges inside a wave.  A thread owns one (4-token quad, 4-channel group) item of each of
+// q, k, v: all its input loads (12 pieces of 16 bytes, plus its RoPE table pieces) are issued
+// at once; the tile's camera matrices and inverse RMS are staged in LDS.  Results go to LDS
+// tiles [D][64] (row stride 68 floats), q and k first, then v, and leave as 256-byte runs of
+// the [B, H, D, N] rows.  Tokens past N (a ragged last tile) load token N - 1 and are not
+// stored.
 template <int D>
-__global__ __launch_bounds__(256) void cam_prep_kernel(const CamPrepParams p) {
-  constexpr int G = D / 4, kItems = 16 * G / 256, kRow = 68;
-  __shared__ __attribute__((aligned(16))) float tile[D * kRow];
+__global__ __launch_bounds__(4 * D) void cam_prep_kernel(const CamPrepParams p) {
+  constexpr int kThreads = 4 * D, G2 = D / 8, kRow = 68;  // G2 groups per half
+  __shared__ __attribute__((aligned(16))) float tile[2][D * kRow];
+  __shared__ __attribute__((aligned(16))) float pm[2][64 * 16];  // proj_q, proj_kv per token
+  __shared__ __attribute__((aligned(16))) float inv[2][64];
+  __shared__ float red[2][2][64];  // [half][pre, post][token]
   const int nt = (p.N + 63) / 64;
   int x = blockIdx.x;
   const int tb = x % nt;
   x /= nt;
   const int h = x % p.H, b = x / p.H;
   const int n0 = tb * 64;
-  const int tid = threadIdx.x, g = tid % G;
-  const bool ucpe = g < G / 2;
+  const int tid = threadIdx.x;
+  const int half = tid / (2 * D);         // 0: camera matrix, 1: RoPE (wave-uniform)
+  const int gl = tid % G2, qd = (tid % (2 * D)) / G2;
+  const int g = half * G2 + gl;           // channel group: channels 4g .. 4g + 3
   const long C = (long)p.H * D;
-  const long out_bh = ((long)b * p.H + h) * D * p.N;
+  auto tok = [&](int t) { return n0 + t < p.N ? n0 + t : p.N - 1; };
+  // stage the tile's camera matrices (16-byte pieces) and inverse RMS
+  for (int i = tid; i < 2 * 64 * 4; i += kThreads) {
+    const int which = i / 256, t = (i % 256) / 4, r = i % 4;
+    const float* src = (which ? p.proj_kv : p.proj_q) + ((long)b * p.N + tok(t)) * 16 + 4 * r;
+    *reinterpret_cast<f32x4*>(&pm[which][t * 16 + 4 * r]) = *reinterpret_cast<const f32x4*>(src);
+  }
+  if (tid < 128) inv[tid / 64][tid % 64] = (tid < 64 ? p.q_inv_rms : p.k_inv_rms)[(long)b * p.N + tok(tid % 64)];
+  // this thread's raw inputs and RoPE table pieces
+  f32x4 xr[3][4], cs[4], sn[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const long row = ((long)b * p.N + tok(4 * qd + j)) * C + h * D + 4 * g;
+    xr[0][j] = *reinterpret_cast<const f32x4*>(p.q + row);
+    xr[1][j] = *reinterpret_cast<const f32x4*>(p.k + row);
+    xr[2][j] = *reinterpret_cast<const f32x4*>(p.v + row);
+    if (half) {
+      const long tr = (long)tok(4 * qd + j) * (D / 2) + 4 * gl;
+      cs[j] = *reinterpret_cast<const f32x4*>(p.rope_cos + tr);
+      sn[j] = *reinterpret_cast<const f32x4*>(p.rope_sin + tr);
+    }
+  }
   const f32x4 wq = *reinterpret_cast<const f32x4*>(p.q_norm_w + h * D + 4 * g);
   const f32x4 wk = *reinterpret_cast<const f32x4*>(p.k_norm_w + h * D + 4 * g);
-  for (int which = 0; which < 3; ++which) {
-    const float* src = which == 0 ? p.q : which == 1 ? p.k : p.v;
-    const float* proj = which == 0 ? p.proj_q : p.proj_kv;
-    const f32x4 w = which == 0 ? wq : wk;
-    const float* invp = which == 0 ? p.q_inv_rms : p.k_inv_rms;
+  __syncthreads();
+  const long out_bh = ((long)b * p.H + h) * D * p.N;
+  auto transform = [&](int which, int slot) {
+    float pre[4], post[4];
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int qd = tid / G + (256 / G) * i;
-      const int n = n0 + 4 * qd;  // first token of the quad (N is a multiple of 4)
-      const bool live = n < p.N;
-      f32x4 y[4];
-      float pre[4], post[4];
-      f32x4 inv = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (live && which < 2) inv = *reinterpret_cast<const f32x4*>(invp + (long)b * p.N + n);
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * qd + j;
+      f32x4 xn = xr[which][j];
+      if (which < 2) {
+        const f32x4 w = which ? wk : wq;
+        const float iv = inv[which][t];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 xn = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (live) xn = *reinterpret_cast<const f32x4*>(src + ((long)b * p.N + n + j) * C + h * D + 4 * g);
-        if (which < 2) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float t = xn[c] * inv[j] * w[c];
-            xn[c] = t > 0.f ? t : 0.f;
-            if (which == 1) xn[c] *= p.k_scale;
-          }
-        }
-        f32x4 o;
-        if (ucpe) {
-          const f32x4* pm = reinterpret_cast<const f32x4*>(proj + ((long)b * p.N + n + j) * 16);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const f32x4 row = live ? pm[r] : f32x4{0.f, 0.f, 0.f, 0.f};
-            o[r] = row[0] * xn[0] + row[1] * xn[1] + row[2] * xn[2] + row[3] * xn[3];
-          }
-        } else {
-          f32x4 cs = f32x4{1.f, 1.f, 1.f, 1.f}, sn = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (live) {
-            const long tr = (long)(n + j) * (D / 2) + 4 * g - D / 2;
-            cs = *reinterpret_cast<const f32x4*>(p.rope_cos + tr);
-            sn = *reinterpret_cast<const f32x4*>(p.rope_sin + tr);
-          }
-          o[0] = xn[0] * cs[0] + xn[1] * sn[0];
-          o[1] = xn[1] * cs[1] + xn[0] * sn[1];
-          o[2] = xn[2] * cs[2] + xn[3] * sn[2];
-          o[3] = xn[3] * cs[3] + xn[2] * sn[3];
-        }
-        y[j] = o;
-        pre[j] = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
-        post[j] = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-      }
-      // channel-major tile: row 4g + c holds the quad's four tokens
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<f32x4*>(&tile[(4 * g + c) * kRow + 4 * qd]) = f32x4{y[0][c], y[1][c], y[2][c], y[3][c]};
-      if (which == 1) {
-        // sums over the G consecutive threads of the quad
-#pragma unroll
-        for (int off = 1; off < G; off <<= 1)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pre[j] += __shfl_xor(pre[j], off, 64);
-            post[j] += __shfl_xor(post[j], off, 64);
-          }
-        if (g == 0 && live) {
-          f32x4 r;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) r[j] = fmaxf(post[j], 1e-12f) / fmaxf(pre[j], 1e-12f);
-          *reinterpret_cast<f32x4*>(p.inflation + ((long)b * p.H + h) * p.N + n) = r;
+        for (int c = 0; c < 4; ++c) {
+          const float u = xn[c] * iv * w[c];
+          xn[c] = (u > 0.f ? u : 0.f) * (which ? p.k_scale : 1.f);
         }
       }
+      f32x4 o;
+      if (half == 0) {
+        const float* P = &pm[which ? 1 : 0][t * 16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 row = *reinterpret_cast<const f32x4*>(P + 4 * r);
+          o[r] = row[0] * xn[0] + row[1] * xn[1] + row[2] * xn[2] + row[3] * xn[3];
+        }
+      } else {
+        o[0] = xn[0] * cs[j][0] + xn[1] * sn[j][0];
+        o[1] = xn[1] * cs[j][1] + xn[0] * sn[j][1];
+        o[2] = xn[2] * cs[j][2] + xn[3] * sn[j][2];
+        o[3] = xn[3] * cs[j][3] + xn[2] * sn[j][3];
+      }
+      pre[j] = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+      post[j] = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+      xr[which][j] = o;
     }
-    __syncthreads();
-    float* dst = which == 0 ? p.q_out : which == 1 ? p.k_out : p.v_out;
 #pragma unroll
-    for (int r = 0; r < D * 16 / 256; ++r) {
-      const int c = tid + 256 * r, d = c / 16, m = c % 16;
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<f32x4*>(&tile[slot][(4 * g + c) * kRow + 4 * qd]) =
+          f32x4{xr[which][0][c], xr[which][1][c], xr[which][2][c], xr[which][3][c]};
+    if (which == 1) {  // |k|^2 before and after, summed over the G2 threads of the half-quad
+#pragma unroll
+      for (int off = 1; off < G2; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pre[j] += __shfl_xor(pre[j], off, 64);
+          post[j] += __shfl_xor(post[j], off, 64);
+        }
+      if (gl == 0)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          red[half][0][4 * qd + j] = pre[j];
+          red[half][1][4 * qd + j] = post[j];
+        }
+    }
+  };
+  auto store = [&](int slot, float* dst) {
+#pragma unroll
+    for (int r = 0; r < D * 16 / kThreads; ++r) {
+      const int c = tid + kThreads * r, d = c / 16, m = c % 16;
       if (n0 + 4 * m < p.N)
         *reinterpret_cast<f32x4*>(dst + out_bh + (long)d * p.N + n0 + 4 * m) =
-            *reinterpret_cast<const f32x4*>(&tile[d * kRow + 4 * m]);
+            *reinterpret_cast<const f32x4*>(&tile[slot][d * kRow + 4 * m]);
     }
-    __syncthreads();
+  };
+  transform(0, 0);
+  transform(1, 1);
+  __syncthreads();
+  store(0, p.q_out);
+  store(1, p.k_out);
+  if (tid < 16 && n0 + 4 * tid < p.N) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * tid + j;
+      r[j] = fmaxf(red[0][1][t] + red[1][1][t], 1e-12f) / fmaxf(red[0][0][t] + red[1][0][t], 1e-12f);
+    }
+    *reinterpret_cast<f32x4*>(p.inflation + ((long)b * p.H + h) * p.N + n0 + 4 * tid) = r;
   }
+  __syncthreads();
+  transform(2, 0);
+  __syncthreads();
+  store(0, p.v_out);
 }
 
 // ---- frame statistics -------------------------------------------------------------------
 // One workgroup of eight waves per (b, h, frame): waves 0-3 accumulate the four D/2 x D/2
 // quadrants of G = K diag(beta) K^T, waves 4-7 those of U = K diag(beta) V^T, over the
-// frame's tokens 64 at a time.  beta >= 0 splits as sqrt(beta) on both operands, so the LDS
-// tiles hold sqrt(beta) K and sqrt(beta) V as fp16 [D][64] (row stride 72 halves: the 16
-// rows of an operand read fall in distinct banks).  The tiles are double-buffered and an
-// item's slab rows and betas are loaded a block ahead into registers.
-template <int D>
+// frame's tokens kT at a time (128 when S allows, so that a CU has 160 KB of loads in
+// flight).  beta >= 0 splits as sqrt(beta) on both operands, so the LDS tiles hold
+// sqrt(beta) K and sqrt(beta) V as fp16 [D][kT] (row stride kT + 8 halves: the 16 rows of an
+// operand read fall in distinct banks).  The tiles are double-buffered and an item's slab
+// rows and betas are loaded a block ahead into registers.
+template <int D, int kT>
 __global__ __launch_bounds__(512) void cam_stats_kernel(const CamScanParams p) {
-  constexpr int kT = 64, kRow = kT + 8, kQ = D / 2, kA = kQ / 16;
-  constexpr int kItems = 2 * D * (kT / 8) / 512;  // (tensor, channel, 8-token octet) items
+  constexpr int kRow = kT + 8, kQ = D / 2, kA = kQ / 16;
+  constexpr int kO = kT / 8;                      // 8-token octets per slab row
+  constexpr int kItems = 2 * D * kO / 512;        // (tensor, channel, octet) items
   __shared__ __attribute__((aligned(16))) f16 tl[2][2][D * kRow];
   const int F = p.F, S = p.S;
   const long N = (long)F * S;
@@ -188,7 +221,7 @@ __global__ __launch_bounds__(512) void cam_stats_kernel(const CamScanParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
   const int m = wave >> 2, qi = (wave >> 1) & 1, qj = wave & 1;
-  const int oct = tid % 8;  // fixed: 512 is a multiple of 8
+  const int oct = tid % kO;  // fixed: 512 is a multiple of kO
   const float* kb = p.k + (long)bh * D * N + (long)f * S;
   const float* vb = p.v + (long)bh * D * N + (long)f * S;
   const float* bt = p.beta + ((long)bh * F + f) * S;
@@ -201,7 +234,7 @@ __global__ __launch_bounds__(512) void cam_stats_kernel(const CamScanParams p) {
   auto load_items = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-      const int it = tid + 512 * i, ten = it / (D * 8), d = (it % (D * 8)) / 8;
+      const int it = tid + 512 * i, ten = it / (D * kO), d = (it % (D * kO)) / kO;
       const float* row = (ten ? vb : kb) + (long)d * N + t0 + 8 * oct;
       xs[i][0] = reinterpret_cast<const f32x4*>(row)[0];
       xs[i][1] = reinterpret_cast<const f32x4*>(row)[1];
@@ -218,7 +251,7 @@ __global__ __launch_bounds__(512) void cam_stats_kernel(const CamScanParams p) {
     }
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-      const int it = tid + 512 * i, ten = it / (D * 8), d = (it % (D * 8)) / 8;
+      const int it = tid + 512 * i, ten = it / (D * kO), d = (it % (D * kO)) / kO;
       f16x8 r;
 #pragma unroll
       for (int j = 0; j < 8; ++j) r[j] = (f16)(xs[i][j >> 2][j & 3] * sb[j]);
@@ -346,10 +379,12 @@ __global__ __launch_bounds__(256) void cam_out_kernel(const CamScanParams p, int
 }  // namespace
 
 hipError_t launch_cam_prep(const CamPrepParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(cam_rms_kernel, dim3(p.B * p.N), dim3(256), 0, stream, p);
+  const long ntok = (long)p.B * p.N;
+  hipLaunchKernelGGL(cam_rms_kernel, dim3((ntok + kRmsTokens - 1) / kRmsTokens), dim3(256), 0,
+                     stream, p);
   const dim3 grid(p.B * p.H * ((p.N + 63) / 64));
   if (p.D == 128)
-    hipLaunchKernelGGL(cam_prep_kernel<128>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(cam_prep_kernel<128>, grid, dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL(cam_prep_kernel<64>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -378,10 +413,12 @@ hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream) {
   int grp = 4;
   while (nblk % grp) grp >>= 1;
   const dim3 og(p.B * p.H * p.F * (nblk / grp));
-  if (p.D == 128)
-    hipLaunchKernelGGL(cam_stats_kernel<128>, dim3(p.B * p.H * p.F), dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL(cam_stats_kernel<64>, dim3(p.B * p.H * p.F), dim3(512), 0, stream, p);
+  const dim3 sg(p.B * p.H * p.F);
+  const bool t128 = p.S % 128 == 0;
+  if (p.D == 128 && t128) hipLaunchKernelGGL((cam_stats_kernel<128, 128>), sg, dim3(512), 0, stream, p);
+  else if (p.D == 128) hipLaunchKernelGGL((cam_stats_kernel<128, 64>), sg, dim3(512), 0, stream, p);
+  else if (t128) hipLaunchKernelGGL((cam_stats_kernel<64, 128>), sg, dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL((cam_stats_kernel<64, 64>), sg, dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_frame_scan(sp, stream);
