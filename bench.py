@@ -80,14 +80,14 @@ def alg_bytes_bigdn(B, F, S, H, D):
 def alg_bytes_cam(B, F, S, H, D):
     """Minimum HBM bytes of the camera branch step (fp32): the prep reads q, k, v, the camera
     matrices, the half-width RoPE tables and norm weights once and writes q_t, k_t, v_t and
-    the inflation; each scan direction reads q_t, k_t, v_t, beta and decay once and writes
-    its output."""
+    the inflation; the two scan directions together read q_t, k_t, v_t, beta and decay once
+    and write their two outputs."""
     N = F * S
     C = H * D
     prep = 3 * B * N * C * 4 + 2 * B * N * 16 * 4 + 2 * N * (D // 2) * 4 + 2 * C * 4 \
         + 3 * B * N * C * 4 + B * H * N * 4
-    scan = 3 * B * N * C * 4 + B * H * N * 4 + B * H * F * 4 + B * N * C * 4
-    return prep + 2 * scan
+    scans = 3 * B * N * C * 4 + B * H * N * 4 + B * H * F * 4 + 2 * B * N * C * 4
+    return prep + scans
 
 
 def kernel_source_hash():
@@ -313,18 +313,18 @@ def main():
         dt = torch.float32
         th = B * N * H
         alg = alg_bytes_cam(B, F, S, H, D)
-        kernel = "cam_prep + cam_scan forward + cam_scan reverse (8 kernels, whole step)"
+        kernel = "cam_prep + cam_scan_bidi (5 kernels, whole step)"
         config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
                   "state": "fp32", "products": "fp16 operands, fp32 accumulation",
-                  "step": "camera prep, then the forward and the reverse frame scans"}
+                  "step": "camera prep, then the forward and the reverse frame scans (one "
+                          "bidirectional call)"}
 
         def step(i):
             s = sets[i % len(sets)]
             qt, kt, vt, infl = gdn.cam_prep(s["q"], s["k"], s["v"], s["q_norm_w"],
                                             s["k_norm_w"], s["proj_q"], s["proj_kv"],
                                             s["rope_cos"], s["rope_sin"], s["k_scale"], s["eps"])
-            fwd = gdn.cam_scan(qt, kt, vt, s["beta"], s["decay"])
-            rev = gdn.cam_scan(qt, kt, vt, s["beta"], s["decay"], reverse=True)
+            fwd, rev = gdn.cam_scan_bidi(qt, kt, vt, s["beta"], s["decay"])
             return fwd, rev, infl
     elif kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape

@@ -18,6 +18,7 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
+           "cam_scan_bidi",
            "gdn_abi_version", "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
@@ -342,3 +343,31 @@ def cam_scan(q, k, v, beta, decay, *, reverse=False, init_state=None, save_final
                       _stream(dev))
     _lib.check(rc, "cam_scan")
     return (out, fin) if save_final_state else out
+
+
+def cam_scan_bidi(q, k, v, beta, decay, *, decay_bwd=None, init_state=None,
+                  save_final_state=False):
+    """Both camera-scan directions in one call (shared frame statistics).  Returns (out_fwd,
+    out_rev) [B,H,D,N] fp32, plus the forward final state with save_final_state."""
+    B, H, D, N = q.shape
+    dev = q.device
+    F, S = beta.shape[2], beta.shape[3]
+    if F * S != N:
+        raise ValueError("q must be [B,H,D,N] with N = F*S")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, (B, H, D, N), torch.float32, dev)
+    _need(beta, "beta", (B, H, F, S), torch.float32, dev)
+    _need(decay, "decay", (B, H, F), torch.float32, dev)
+    _need(decay_bwd, "decay_bwd", (B, H, F), torch.float32, dev)
+    _need(init_state, "init_state", (B * H, D, D), torch.float32, dev)
+    of = torch.empty(B, H, D, N, dtype=torch.float32, device=dev)
+    orv = torch.empty(B, H, D, N, dtype=torch.float32, device=dev)
+    fin = torch.empty(B * H, D, D, dtype=torch.float32, device=dev) if save_final_state else None
+    lib = _lib.load()
+    ws_n = lib.cam_scan_bidi_workspace_bytes(B, H, D, F)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.cam_scan_bidi(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), _ptr(decay_bwd),
+                           _ptr(init_state), _ptr(fin), _ptr(of), _ptr(orv), B, H, D, F, S,
+                           _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "cam_scan_bidi")
+    return (of, orv, fin) if save_final_state else (of, orv)

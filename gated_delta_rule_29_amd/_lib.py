@@ -42,6 +42,8 @@ SIGNATURES = {
     "cam_prep": (I, [P, P, P, P, P, P, P, P, P, F, F, P, P, P, P, I, I, I, I, P, SZ, P]),
     "cam_scan_workspace_bytes": (SZ, [I, I, I, I]),
     "cam_scan": (I, [P, P, P, P, P, I, P, P, P, I, I, I, I, I, P, SZ, P]),
+    "cam_scan_bidi_workspace_bytes": (SZ, [I, I, I, I]),
+    "cam_scan_bidi": (I, [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, SZ, P]),
 }
 
 _lib = None

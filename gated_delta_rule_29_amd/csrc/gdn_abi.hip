@@ -453,16 +453,27 @@ size_t cam_scan_workspace_bytes(int B, int H, int D, int F) {
   return al256(mats * 2) + al256(mats * 4) + al256(mats * 2);
 }
 
-int cam_scan(const float* q, const float* k, const float* v, const float* beta,
-             const float* decay, int reverse, const float* init_state, float* final_state,
-             float* out, int B, int H, int D, int F, int S, void* workspace,
-             size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !beta || !decay || !out)
-    return fail(GDN_ERR_INVALID, "q, k, v, beta, decay and out must be non-null");
+size_t cam_scan_bidi_workspace_bytes(int B, int H, int D, int F) {
+  if (B <= 0 || H <= 0 || D <= 0 || F <= 0) return 0;
+  const size_t mats = (size_t)B * H * F * D * D;
+  return al256(mats * 2) + al256(mats * 4) + al256(2 * mats * 2);
+}
+
+}  // extern "C"
+
+namespace {
+
+// mode: 0 forward, 1 reverse, 2 both (out = forward, out_rev = reverse)
+int cam_scan_impl(const float* q, const float* k, const float* v, const float* beta,
+                  const float* decay, const float* decay_bwd, int mode, const float* init_state,
+                  float* final_state, float* out, float* out_rev, int B, int H, int D, int F,
+                  int S, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !beta || !decay || !out || (mode == 2 && !out_rev))
+    return fail(GDN_ERR_INVALID, "q, k, v, beta, decay and the outputs must be non-null");
   if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S <= 0)
     return fail(GDN_ERR_INVALID, "B, H, D, F, S must be positive (got %d, %d, %d, %d, %d)", B, H,
                 D, F, S);
-  if (reverse && (init_state || final_state))
+  if (mode == 1 && (init_state || final_state))
     return fail(GDN_ERR_UNSUPPORTED,
                 "state in / out is defined for the forward scan only (reverse=1 with a state)");
   if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
@@ -471,15 +482,17 @@ int cam_scan(const float* q, const float* k, const float* v, const float* beta,
   if ((int64_t)F * S > INT32_MAX || (int64_t)B * H * F * (S / 64) > INT32_MAX)
     return fail(GDN_ERR_INVALID, "F*S exceeds the grid limit");
   const size_t mats = (size_t)B * H * F * D * D;
-  const size_t need = cam_scan_workspace_bytes(B, H, D, F);
+  const size_t need = mode == 2 ? cam_scan_bidi_workspace_bytes(B, H, D, F)
+                                : cam_scan_workspace_bytes(B, H, D, F);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
   gdn::CamScanParams p{};
-  p.q = q; p.k = k; p.v = v; p.beta = beta; p.decay = decay; p.reverse = reverse ? 1 : 0;
-  p.init_state = init_state; p.final_state = final_state; p.out = out;
+  p.q = q; p.k = k; p.v = v; p.beta = beta; p.decay = decay; p.decay_bwd = decay_bwd;
+  p.reverse = mode; p.init_state = init_state; p.final_state = final_state;
+  p.out = out; p.out_rev = out_rev;
   p.B = B; p.H = H; p.D = D; p.F = F; p.S = S;
   p.G = reinterpret_cast<_Float16*>(ws);
   p.U = reinterpret_cast<float*>(ws + al256(mats * 2));
@@ -487,6 +500,26 @@ int cam_scan(const float* q, const float* k, const float* v, const float* beta,
   hipError_t e = gdn::launch_cam_scan(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cam_scan launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int cam_scan(const float* q, const float* k, const float* v, const float* beta,
+             const float* decay, int reverse, const float* init_state, float* final_state,
+             float* out, int B, int H, int D, int F, int S, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  return cam_scan_impl(q, k, v, beta, decay, nullptr, reverse ? 1 : 0, init_state, final_state,
+                       out, nullptr, B, H, D, F, S, workspace, workspace_bytes, stream);
+}
+
+int cam_scan_bidi(const float* q, const float* k, const float* v, const float* beta,
+                  const float* decay, const float* decay_bwd, const float* init_state,
+                  float* final_state, float* out_fwd, float* out_rev, int B, int H, int D, int F,
+                  int S, void* workspace, size_t workspace_bytes, void* stream) {
+  return cam_scan_impl(q, k, v, beta, decay, decay_bwd, 2, init_state, final_state, out_fwd,
+                       out_rev, B, H, D, F, S, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

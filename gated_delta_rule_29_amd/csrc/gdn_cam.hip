@@ -18,7 +18,9 @@
 // frames after f (flip-and-shift).  Kernels: stats (G_f, U_f per (b, h, f) with matrix cores:
 // the channel-major slabs are already in operand order, 8 consecutive tokens of one channel
 // per lane), the frame scan of gdn_bigdn.hip (one direction, no z; state in / out), out
-// (S_f^T Q_f per 64-token block; Q is transposed through LDS).  Products use fp16 operands
+// (S_f^T Q_f per 64-token block; Q is transposed through LDS).  The bidirectional form
+// computes the statistics once, scans both directions concurrently and forms both outputs
+// from one read of Q.  Products use fp16 operands
 // with fp32 accumulation (the page's scan uses TF32 dots: the same 10-bit mantissa); the
 // scanned state is fp32.
 #include "gdn_device.h"
@@ -315,7 +317,10 @@ __global__ __launch_bounds__(512) void cam_stats_kernel(const CamScanParams p) {
 // registers for the whole group; the A operand (tokens x keys) comes from the block's Q slab,
 // converted to fp16 into LDS [D][64] and read transposed.  The accumulator of lane (li, lq)
 // holds four consecutive tokens of value column li (16-byte stores).
-template <int D>
+//
+// kDirs = 2 (both directions): the two directions' states are both held as B operands and
+// one Q tile serves both outputs.
+template <int D, int kDirs>
 __global__ __launch_bounds__(256) void cam_out_kernel(const CamScanParams p, int grp) {
   constexpr int kRow = 72, kCT = D / 64;
   __shared__ __attribute__((aligned(16))) f16 qt[D * kRow];
@@ -329,15 +334,18 @@ __global__ __launch_bounds__(256) void cam_out_kernel(const CamScanParams p, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const long bhf = (long)bh * F + f;
-  f16x8 sa[kCT][D / 32];
+  f16x8 sa[kDirs][kCT][D / 32];
+  const long dir_m = (long)p.B * p.H * F * D * D;
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct)
+  for (int r = 0; r < kDirs; ++r)
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k)
-      sa[ct][k] = *reinterpret_cast<const f16x8*>(
-          p.SdT + bhf * D * D + (long)((D / 4) * wave + 16 * ct + li) * D + 32 * k + 8 * lq);
+    for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k)
+        sa[r][ct][k] = *reinterpret_cast<const f16x8*>(
+            p.SdT + r * dir_m + bhf * D * D + (long)((D / 4) * wave + 16 * ct + li) * D + 32 * k + 8 * lq);
   const float* qb = p.q + (long)bh * D * N;
-  float* ob = p.out + (long)bh * D * N;
+  float* ob[2] = {p.out + (long)bh * D * N, (kDirs == 2 ? p.out_rev : p.out) + (long)bh * D * N};
   const int trj = li >> 2, trm = li & 3;  // transpose-read piece: key row offset, token quad
   for (int blk = gi * grp; blk < (gi + 1) * grp; ++blk) {
     const long n0 = (long)f * S + blk * 64;
@@ -359,19 +367,25 @@ __global__ __launch_bounds__(256) void cam_out_kernel(const CamScanParams p, int
     __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      f32x4 acc[kCT];
+      f32x4 acc[kDirs][kCT];
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < kDirs; ++r)
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) acc[r][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < D / 32; ++k) {
         const f16x8 aq = tr_pair(&qt[(32 * k + 8 * lq + trj) * kRow + 16 * tt + 4 * trm],
                                  &qt[(32 * k + 8 * lq + 4 + trj) * kRow + 16 * tt + 4 * trm]);
 #pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) acc[ct] = mma16(aq, sa[ct][k], acc[ct]);
+        for (int r = 0; r < kDirs; ++r)
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct) acc[r][ct] = mma16(aq, sa[r][ct][k], acc[r][ct]);
       }
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct)
-        *reinterpret_cast<f32x4*>(ob + (long)((D / 4) * wave + 16 * ct + li) * N + n0 + 16 * tt + 4 * lq) = acc[ct];
+      for (int r = 0; r < kDirs; ++r)
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct)
+          *reinterpret_cast<f32x4*>(ob[r] + (long)((D / 4) * wave + 16 * ct + li) * N + n0 + 16 * tt + 4 * lq) = acc[r][ct];
     }
   }
 }
@@ -391,9 +405,10 @@ hipError_t launch_cam_prep(const CamPrepParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream) {
+  const bool both = p.reverse == 2;
   BigdnParams sp{};
   sp.decay = p.decay;
-  sp.decay_bwd = p.decay;
+  sp.decay_bwd = both && p.decay_bwd ? p.decay_bwd : p.decay;
   sp.B = p.B;
   sp.H = p.H;
   sp.F = p.F;
@@ -403,9 +418,9 @@ hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream) {
   sp.G = sp.G_b = p.G;
   sp.U = sp.U_b = p.U;
   sp.SdT = p.SdT;
-  sp.scan_dirs = p.reverse ? 2 : 1;
+  sp.scan_dirs = both ? 3 : p.reverse ? 2 : 1;
   sp.scan_z = 0;
-  sp.dir_slots = 1;
+  sp.dir_slots = both ? 2 : 1;
   sp.s_init = p.init_state;
   sp.s_final = p.final_state;
   // 64-token blocks per output workgroup: the largest divisor of a frame's blocks up to 4
@@ -423,10 +438,10 @@ hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = launch_frame_scan(sp, stream);
   if (e != hipSuccess) return e;
-  if (p.D == 128)
-    hipLaunchKernelGGL(cam_out_kernel<128>, og, dim3(256), 0, stream, p, grp);
-  else
-    hipLaunchKernelGGL(cam_out_kernel<64>, og, dim3(256), 0, stream, p, grp);
+  if (p.D == 128 && both) hipLaunchKernelGGL((cam_out_kernel<128, 2>), og, dim3(256), 0, stream, p, grp);
+  else if (p.D == 128) hipLaunchKernelGGL((cam_out_kernel<128, 1>), og, dim3(256), 0, stream, p, grp);
+  else if (both) hipLaunchKernelGGL((cam_out_kernel<64, 2>), og, dim3(256), 0, stream, p, grp);
+  else hipLaunchKernelGGL((cam_out_kernel<64, 1>), og, dim3(256), 0, stream, p, grp);
   return hipGetLastError();
 }
 

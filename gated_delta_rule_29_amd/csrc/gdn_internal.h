@@ -139,15 +139,17 @@ struct CamScanParams {
   const float* v;
   const float* beta;   // [B, H, F, S]
   const float* decay;  // [B, H, F]
-  int reverse;
+  int reverse;              // one direction: 0 forward, 1 reverse; 2: both (bidirectional)
+  const float* decay_bwd;   // [B, H, F] decay of the reverse direction (both), or nullptr
   const float* init_state;  // [B*H, D, D] or nullptr (forward only)
   float* final_state;       // [B*H, D, D] or nullptr (forward only)
-  float* out;               // [B, H, D, N] fp32
+  float* out;               // [B, H, D, N] fp32 (the direction run; forward when both)
+  float* out_rev;           // [B, H, D, N] fp32 (reverse, when both)
   int B, H, D, F, S;
   // workspace views
   _Float16* G;    // [B, H, F, D, D]
   float* U;       // [B, H, F, D, D]
-  _Float16* SdT;  // [B, H, F, D, D]
+  _Float16* SdT;  // [dirs, B, H, F, D, D]
 };
 hipError_t launch_cam_prep(const CamPrepParams& p, hipStream_t stream);
 hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream);

@@ -298,6 +298,24 @@ GDN_API int cam_scan(const float* q, const float* k, const float* v, const float
                      float* out, int B, int H, int D, int F, int S, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * cam_scan_bidi -- both directions of cam_scan over the same q, k, v and beta in one call:
+ * out_fwd is cam_scan(reverse=0) (with init_state / final_state as there) and out_rev is
+ * cam_scan(reverse=1), the reverse direction using decay_bwd [B,H,F] when it is non-NULL
+ * (chunk-causal resets: a zero at frame f+1 cuts frames > f off from frame f) and decay
+ * otherwise.  The frame statistics are computed once, the two scans run concurrently and
+ * one read of q serves both outputs.
+ *   out_fwd, out_rev  [B,H,D,N] fp32 OUT
+ *   workspace         at least cam_scan_bidi_workspace_bytes(B, H, D, F), 256-byte aligned
+ * Errors as cam_scan (GDN_ERR_INVALID also for a null out_rev).
+ */
+GDN_API size_t cam_scan_bidi_workspace_bytes(int B, int H, int D, int F);
+GDN_API int cam_scan_bidi(const float* q, const float* k, const float* v, const float* beta,
+                          const float* decay, const float* decay_bwd, const float* init_state,
+                          float* final_state, float* out_fwd, float* out_rev, int B, int H,
+                          int D, int F, int S, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

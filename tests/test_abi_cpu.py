@@ -191,3 +191,20 @@ def test_cam_validation_codes():
     n = lib.cam_scan_workspace_bytes(1, 2, 128, 3)
     assert n == 2 * 3 * 128 * 128 * (2 + 4 + 2)
     assert scan(ws=FAKE, ws_n=n - 1) == L.ERR_WORKSPACE
+
+
+def test_cam_bidi_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(orv=FAKE, init=None, fin=None, ws=None, ws_n=0)
+        a.update(kw)
+        return lib.cam_scan_bidi(FAKE, FAKE, FAKE, FAKE, FAKE, None, a["init"], a["fin"], FAKE,
+                                 a["orv"], 1, 2, 128, 3, 64, a["ws"], a["ws_n"], None)
+
+    assert call(orv=None) == L.ERR_INVALID
+    assert call() == L.ERR_WORKSPACE
+    n1 = lib.cam_scan_workspace_bytes(1, 2, 128, 3)
+    n2 = lib.cam_scan_bidi_workspace_bytes(1, 2, 128, 3)
+    assert n2 == n1 + 2 * 3 * 128 * 128 * 2
+    assert call(ws=FAKE, ws_n=n1) == L.ERR_WORKSPACE

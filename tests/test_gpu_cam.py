@@ -122,3 +122,31 @@ def test_cam_video_workload():
         assert_close("fwd h%d" % h, fwd[:, sl], oracle.cam_scan(*args), FP16_OPERAND_TOL)
         assert_close("rev h%d" % h, rev[:, sl], oracle.cam_scan(*args, reverse=True),
                      FP16_OPERAND_TOL)
+
+
+@pytest.mark.parametrize("B,F,S,H,D", [(1, 6, 128, 2, 128), (2, 3, 64, 3, 64)])
+def test_cam_scan_bidi(B, F, S, H, D):
+    """Both directions in one call: against the oracle (the reverse with its own decay, zero
+    at one frame: chunk-causal), and bit for bit equal to the two single-direction calls."""
+    import gated_delta_rule_29_amd as g
+
+    w = workloads.cam_scan_inputs(B, F, S, H, D, seed=3 * F + D)
+    db = w["decay"].clone()
+    db[:, :, F // 2] = 0.0
+    h0 = 0.3 * torch.randn(B * H, D, D, generator=torch.Generator().manual_seed(F))
+    say("cam scan bidi B%d F%d S%d H%d D%d" % (B, F, S, H, D))
+    d = _dev(w)
+    of, orv, fin = g.cam_scan_bidi(d["q"], d["k"], d["v"], d["beta"], d["decay"],
+                                   decay_bwd=db.to(DEV), init_state=h0.to(DEV),
+                                   save_final_state=True)
+    sf, sfin = g.cam_scan(d["q"], d["k"], d["v"], d["beta"], d["decay"], init_state=h0.to(DEV),
+                          save_final_state=True)
+    sr = g.cam_scan(d["q"], d["k"], d["v"], d["beta"], db.to(DEV), reverse=True)
+    torch.cuda.synchronize()
+    rf, rfin = oracle.cam_scan(w["q"], w["k"], w["v"], w["beta"], w["decay"], init_state=h0,
+                               want_final=True)
+    rr = oracle.cam_scan(w["q"], w["k"], w["v"], w["beta"], db, reverse=True)
+    assert_close("fwd", of, rf, FP16_OPERAND_TOL)
+    assert_close("final", fin, rfin, FP16_OPERAND_TOL)
+    assert_close("rev", orv, rr, FP16_OPERAND_TOL)
+    assert torch.equal(of, sf) and torch.equal(orv, sr) and torch.equal(fin, sfin)
