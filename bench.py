@@ -143,7 +143,7 @@ def cpu_baseline(kind, inp, max_chains=64):
     if kind == "cam":
         B, N, H, D = inp["q"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
-        fs = min(F, 8)
+        fs = min(F, 4)
         n = fs * S
         sub = {k: oracle._f64(inp[k][:, :n]) for k in ("q", "k", "v", "proj_q", "proj_kv")}
 
