@@ -11,8 +11,9 @@ Contents
     map from initial to final state), the packed-varlen tables and driver, the BiGDN
     front end (full-channel RMSNorm, ReLU, k-scale, interleaved-pair RoPE) and the
     frame-level BiGDN scan in both directions, the camera-branch prep (UCPE 4x4 blocks and
-    half-width RoPE) and its numerator-only frame scan with state in and out.  This is the
-    reference every GPU result is compared with.
+    half-width RoPE) and its numerator-only frame scan with state in and out, and the
+    state-gradient pass of the chunked backward (dhu).  This is the reference every GPU
+    result is compared with.
   * ``forms.py``: independent numpy cross-check forms (global O(T^2) solve, chunked WY
     form, BiGDN product form with flip-and-shift reverse) used only to pin the oracle.
 
@@ -67,6 +68,7 @@ def _load():
         lib.oracle_cam_prep.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, Dd, Dd, P, P, P,
                                         P]
         lib.oracle_cam_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        lib.oracle_gdn_dhu.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, Dd, P, P, P]
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
@@ -299,3 +301,22 @@ def cam_scan(q, k, v, beta, decay, reverse=False, init_state=None, want_final=Fa
     if rc != 0:
         raise RuntimeError("oracle_cam_scan failed")
     return (out, fin) if want_final else out
+
+
+def gdn_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, chunk=CHUNK):
+    """State-gradient pass of the chunked backward (dhu): q, k, w [B,T,H,K]; do, dv [B,T,H,V];
+    g [B,T,H] per-token log gates (the chunk-local cumsum is taken here); dht [B,H,K,V].
+    Returns dict with dh [B,H,NT,K,V] (gradient of the state entering each chunk), dv2
+    [B,T,H,V] (gradient of v_new) and dh0 [B,H,K,V]."""
+    q, k, w, do, dv, g, dht = map(_f64, (q, k, w, do, dv, g, dht))
+    B, T, H, K = q.shape
+    V = do.shape[-1]
+    NT = (T + chunk - 1) // chunk
+    dh = np.empty((B, H, NT, K, V))
+    dv2 = np.empty((B, T, H, V))
+    dh0 = np.empty((B, H, K, V))
+    rc = _load().oracle_gdn_dhu(B, T, H, K, V, chunk, _p(q), _p(k), _p(w), _p(g), _p(do),
+                                _p(dv), _p(dht), float(scale), _p(dh), _p(dv2), _p(dh0))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_dhu failed")
+    return {"dh": dh, "dv2": dv2, "dh0": dh0}
