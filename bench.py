@@ -90,6 +90,14 @@ def alg_bytes_cam(B, F, S, H, D):
     return prep + scans
 
 
+def alg_bytes_dhu(B, T, H, K, V, elt):
+    """Minimum HBM bytes of one state-gradient pass: read q, k, w, do, dv (input dtype), the
+    gates and dht once; write dv2 (input dtype), the per-chunk state gradients and dh0 (fp32)."""
+    NT = (T + 63) // 64
+    return (3 * B * T * H * K * elt + 2 * B * T * H * V * elt + B * T * H * 4 + B * H * K * V * 4
+            + B * T * H * V * elt + B * H * NT * K * V * 4 + B * H * K * V * 4)
+
+
 def kernel_source_hash():
     """Hash of every kernel source: a counter summary is valid only for the code it measured."""
     h = hashlib.sha256()
@@ -140,6 +148,17 @@ def cpu_baseline(kind, inp, max_chains=64):
             decay_bwd=inp["decay_bwd"], gate=inp["gate"], merge_eps=1e-6),
             "whole merged block: prep + both directions + merge, %d heads x %d tokens"
             % (H, N), B * N * H)
+    if kind == "dhu":
+        B, T, H, K = inp["q"].shape
+        hh = min(H, 8)
+        sub = {k: (oracle._f64(v[:1, :, :hh]) if k not in ("dht", "scale") else v)
+               for k, v in inp.items()}
+        return _cpu_time(lambda: oracle.gdn_dhu(sub["q"], sub["k"], sub["w"], sub["do"],
+                                                sub["dv"], g=sub["g"],
+                                                dht=oracle._f64(inp["dht"][:1, :hh]),
+                                                scale=inp["scale"]),
+                         "1 of %d batch rows x %d of %d heads (%d chains x %d tokens)"
+                         % (B, hh, H, hh, T), hh * T)
     if kind == "cam":
         B, N, H, D = inp["q"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -307,6 +326,21 @@ def main():
                                         s["k_norm_w"], s["rope_cos"], s["rope_sin"],
                                         s["k_scale"], s["eps"], decay_bwd=s["decay_bwd"],
                                         gate=s["gate"], merge_eps=1e-6)
+    elif kind == "dhu":
+        B, T, H, K = inp["q"].shape
+        V = inp["do"].shape[-1]
+        dt = inp["q"].dtype
+        th = B * T * H
+        alg = alg_bytes_dhu(B, T, H, K, V, 2 if dt == torch.bfloat16 else 4)
+        kernel = "gdn_bwd_dhu call: dhu_kernel"
+        config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
+                  "chunk": 64, "arithmetic": "fp32",
+                  "outputs": "dv2, dh per chunk [B,H,NT,K,V] fp32, dh0"}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.gdn_bwd_dhu(s["q"], s["k"], s["w"], s["do"], s["dv"], g=s["g"],
+                                   dht=s["dht"], scale=s["scale"])
     elif kind == "cam":
         B, N, H, D = inp["q"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

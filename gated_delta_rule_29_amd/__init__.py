@@ -18,7 +18,7 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi",
+           "cam_scan_bidi", "gdn_bwd_dhu",
            "gdn_abi_version", "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
@@ -371,3 +371,31 @@ def cam_scan_bidi(q, k, v, beta, decay, *, decay_bwd=None, init_state=None,
                            _ptr(ws), ws_n, _stream(dev))
     _lib.check(rc, "cam_scan_bidi")
     return (of, orv, fin) if save_final_state else (of, orv)
+
+
+def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, want_dh=True, want_dh0=True):
+    """State-gradient pass of the chunked backward.  q, k, w [B,T,H,K], do, dv [B,T,H,V] (fp32
+    or bf16, one dtype); g [B,T,H] fp32 log gates; dht [B,H,K,V] fp32.  Returns dict with dv2
+    [B,T,H,V] (input dtype), dh [B,H,NT,K,V] fp32 (gradient of the state entering each
+    64-token chunk) and dh0 [B,H,K,V] fp32."""
+    B, T, H, K = q.shape
+    V = do.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("q must be float32 or bfloat16")
+    for t, name in ((q, "q"), (k, "k"), (w, "w")):
+        _need(t, name, (B, T, H, K), dt, dev)
+    _need(do, "do", (B, T, H, V), dt, dev)
+    _need(dv, "dv", (B, T, H, V), dt, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(dht, "dht", (B, H, K, V), torch.float32, dev)
+    NT = (T + CHUNK - 1) // CHUNK
+    dv2 = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    dh = torch.empty(B, H, NT, K, V, dtype=torch.float32, device=dev) if want_dh else None
+    dh0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if want_dh0 else None
+    rc = _lib.load().gdn_bwd_dhu(_ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(dv), _ptr(g), _ptr(dht),
+                                 float(scale), _ptr(dh), _ptr(dv2), _ptr(dh0), B, T, H, K, V,
+                                 _DT[dt], _stream(dev))
+    _lib.check(rc, "gdn_bwd_dhu")
+    return {"dv2": dv2, "dh": dh, "dh0": dh0}

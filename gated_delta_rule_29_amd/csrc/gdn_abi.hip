@@ -522,4 +522,29 @@ int cam_scan_bidi(const float* q, const float* k, const float* v, const float* b
                        out_rev, B, H, D, F, S, workspace, workspace_bytes, stream);
 }
 
+
+// ---- backward: state-gradient pass --------------------------------------------------------
+
+int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_, const void* dv,
+                const float* g, const float* dht, float scale, float* dh_chunks, void* dv2,
+                float* dh0, int B, int T, int H, int K, int V, int dtype, void* stream) {
+  if (!q || !k || !w || !do_ || !dv || !dv2)
+    return fail(GDN_ERR_INVALID, "q, k, w, do, dv and dv2 must be non-null");
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID, "B, T, H, K, V must be positive (got %d, %d, %d, %d, %d)", B, T,
+                H, K, V);
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID, "dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16, got %d", dtype);
+  if (K != 128) return fail(GDN_ERR_UNSUPPORTED, "K must be 128, got %d", K);
+  if (V % 32) return fail(GDN_ERR_UNSUPPORTED, "V must be a multiple of 32, got %d", V);
+  if ((int64_t)B * H * (V / 32) > INT32_MAX) return fail(GDN_ERR_INVALID, "B*H*V/32 exceeds the grid limit");
+  gdn::DhuParams p{};
+  p.q = q; p.k = k; p.w = w; p.do_ = do_; p.dv = dv; p.g = g; p.dht = dht; p.scale = scale;
+  p.dh_chunks = dh_chunks; p.dv2 = dv2; p.dh0 = dh0;
+  p.B = B; p.T = T; p.H = H; p.V = V;
+  hipError_t e = gdn::launch_dhu(p, dtype == GDN_DTYPE_F32 ? 0 : 1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_bwd_dhu launch");
+  return ok();
+}
+
 }  // extern "C"

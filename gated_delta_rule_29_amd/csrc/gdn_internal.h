@@ -151,6 +151,23 @@ struct CamScanParams {
   float* U;       // [B, H, F, D, D]
   _Float16* SdT;  // [dirs, B, H, F, D, D]
 };
+// state-gradient pass of the chunked backward (gdn_bwd.hip)
+struct DhuParams {
+  const void* q;    // [B, T, H, K] (fp32 or bf16, as every input here)
+  const void* k;
+  const void* w;    // [B, T, H, K] the WY w of the forward
+  const void* do_;  // [B, T, H, V]
+  const void* dv;   // [B, T, H, V] the intra-chunk gradient of v_new
+  const float* g;   // [B, T, H] per-token log gates, or nullptr
+  const float* dht; // [B, H, K, V] or nullptr
+  float scale;
+  float* dh_chunks; // [B, H, NT, K, V] or nullptr
+  void* dv2;        // [B, T, H, V] (input dtype)
+  float* dh0;       // [B, H, K, V] or nullptr
+  int B, T, H, V;
+};
+hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream);  // K = 128
+
 hipError_t launch_cam_prep(const CamPrepParams& p, hipStream_t stream);
 hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream);
 // the frame scan of gdn_bigdn.hip, for one direction without z

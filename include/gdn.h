@@ -316,6 +316,32 @@ GDN_API int cam_scan_bidi(const float* q, const float* k, const float* v, const 
                           int D, int F, int S, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * gdn_bwd_dhu -- state-gradient pass of the chunked backward ([hyper-parallel "Diff Coverage"
+ * page], the dhu fragments): the adjoint of the chunk state pass of gdn_fwd, over 64-token
+ * chunks in reverse.  With dh the gradient of the state leaving chunk n (dht, or 0, after
+ * the last chunk), gamma the chunk-local inclusive cumsum of g and gamma_L its value at the
+ * chunk's last token:
+ *     dv2_t = dv_t + e^{gamma_L - gamma_t} (dh^T k_t)
+ *     dh    = e^{gamma_L} dh + scale sum_t e^{gamma_t} q_t do_t^T - sum_t w_t dv2_t^T
+ *     dh_chunks[n] = dh   (the gradient of h[n], the state entering chunk n, as gdn_fwd saves it)
+ * and dh0 = dh after chunk 0.
+ *   q, k, w   [B,T,H,K] IN; w is the forward's WY w (v_new = u - w h)
+ *   do_, dv   [B,T,H,V] IN: the output gradient, and the intra-chunk gradient of v_new (P^T do)
+ *   g         [B,T,H] fp32 IN per-token log gates, or NULL (no decay)
+ *   dht       [B,H,K,V] fp32 IN or NULL (zero)
+ *   dh_chunks [B,H,NT,K,V] fp32 OUT or NULL (NT = ceil(T/64)); dv2 [B,T,H,V] OUT (dtype);
+ *   dh0       [B,H,K,V] fp32 OUT or NULL
+ *   dtype     GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, w, do_, dv and dv2; the arithmetic is
+ *             fp32 either way
+ * Supported: K = 128, V a multiple of 32 (GDN_ERR_UNSUPPORTED otherwise).  GDN_ERR_INVALID for
+ * null required pointers, non-positive sizes or an unknown dtype.
+ */
+GDN_API int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_,
+                        const void* dv, const float* g, const float* dht, float scale,
+                        float* dh_chunks, void* dv2, float* dh0, int B, int T, int H, int K,
+                        int V, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -208,3 +208,19 @@ def test_cam_bidi_validation_codes():
     n2 = lib.cam_scan_bidi_workspace_bytes(1, 2, 128, 3)
     assert n2 == n1 + 2 * 3 * 128 * 128 * 2
     assert call(ws=FAKE, ws_n=n1) == L.ERR_WORKSPACE
+
+
+def test_dhu_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, K=128, V=64, dt=0, T=100)
+        a.update(kw)
+        return lib.gdn_bwd_dhu(a["q"], FAKE, FAKE, FAKE, FAKE, None, None, 1.0, None, FAKE, None,
+                               1, a["T"], 2, a["K"], a["V"], a["dt"], None)
+
+    assert call(q=None) == L.ERR_INVALID
+    assert call(T=0) == L.ERR_INVALID
+    assert call(dt=5) == L.ERR_INVALID
+    assert call(K=64) == L.ERR_UNSUPPORTED
+    assert call(V=48) == L.ERR_UNSUPPORTED
