@@ -56,8 +56,19 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
   __shared__ __attribute__((aligned(16))) float sdh[K * kSV];
   __shared__ float gam[kC];
   static_assert(kItK * 256 == kC * kPK && kItV * 256 == kC * kPV, "tile pieces");
+  // Workgroups are dealt to the eight XCDs round-robin by index; when B*H is a multiple of
+  // eight, the value blocks of one chain get indices on one XCD, so its q, k, w rows come
+  // from that XCD's L2 after the first read.
   const int nvb = p.V / 32;
-  const int vb = blockIdx.x % nvb, bh = blockIdx.x / nvb;
+  int vb, bh;
+  if (p.B * p.H % 8 == 0) {
+    const int x8 = blockIdx.x / 8;
+    bh = blockIdx.x % 8 + 8 * (x8 / nvb);
+    vb = x8 % nvb;
+  } else {
+    vb = blockIdx.x % nvb;
+    bh = blockIdx.x / nvb;
+  }
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
@@ -79,35 +90,56 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
       for (int e = 0; e < 4; ++e)
         dh[a][ct][e] = p.dht ? p.dht[((long)bh * K + 32 * wave + 16 * a + 4 * lq + e) * p.V + v0 + 16 * ct + li] : 0.f;
 
-  // the next chunk's inputs, loaded a chunk ahead (tokens past T read as zero)
+  // The next chunk's inputs, loaded a chunk ahead.  Every load is unconditional, from the
+  // token clamped to T - 1, and rows past T are zeroed where they are used: a load under a
+  // branch makes the compiler wait for all outstanding memory right after it, which would
+  // also wait for the prefetch itself.
   uint4 rk[kItK], rq[kItK], rw[kItK], rdo[kItV];
-  float rdv[2][4], rg = 0.f;
+  TIn rdv[2][4];
+  float rg = 0.f;
+  auto tok = [&](int t) { return t < T ? t : T - 1; };
   auto load = [&](int n) {
     const int t0 = n * kC;
 #pragma unroll
     for (int i = 0; i < kItK; ++i) {
       const int pc = tid + 256 * i, t = pc / kPK, j = pc % kPK;
-      const bool live = t0 + t < T;
-      const long o = ((long)b * T + t0 + t) * HK + (long)h * K + j * E;
-      rk[i] = live ? *reinterpret_cast<const uint4*>(k + o) : uint4{0, 0, 0, 0};
-      rq[i] = live ? *reinterpret_cast<const uint4*>(q + o) : uint4{0, 0, 0, 0};
-      rw[i] = live ? *reinterpret_cast<const uint4*>(w + o) : uint4{0, 0, 0, 0};
+      const long o = ((long)b * T + tok(t0 + t)) * HK + (long)h * K + j * E;
+      rk[i] = *reinterpret_cast<const uint4*>(k + o);
+      rq[i] = *reinterpret_cast<const uint4*>(q + o);
+      rw[i] = *reinterpret_cast<const uint4*>(w + o);
     }
 #pragma unroll
     for (int i = 0; i < kItV; ++i) {
       const int pc = tid + 256 * i, t = pc / kPV, j = pc % kPV;
-      const long o = ((long)b * T + t0 + t) * HV + (long)h * p.V + v0 + j * E;
-      rdo[i] = t0 + t < T ? *reinterpret_cast<const uint4*>(dO + o) : uint4{0, 0, 0, 0};
+      const long o = ((long)b * T + tok(t0 + t)) * HV + (long)h * p.V + v0 + j * E;
+      rdo[i] = *reinterpret_cast<const uint4*>(dO + o);
     }
     // dv in the accumulator layout of the K dh product: tokens 16w + 4lq + e, column 16ct + li
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + 16 * wave + 4 * lq + e;
-        rdv[ct][e] = t < T ? (float)dV[((long)b * T + t) * HV + (long)h * p.V + v0 + 16 * ct + li] : 0.f;
+      for (int e = 0; e < 4; ++e)
+        rdv[ct][e] = dV[((long)b * T + tok(t0 + 16 * wave + 4 * lq + e)) * HV + (long)h * p.V + v0 + 16 * ct + li];
+    if (p.g && tid < kC) rg = p.g[((long)b * T + tok(t0 + tid)) * p.H + h];
+  };
+
+  // dv2 of chunk m from its LDS tile: wave w stores the tokens 16w .. 16w + 15 it writes
+  auto store_dv2 = [&](int m) {
+    TIn* dst = static_cast<TIn*>(p.dv2) + (long)h * p.V + v0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int pc = lane + 64 * i, r = pc / 8, c4 = pc % 8, t = 16 * wave + r;
+      if (m * kC + t < T) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sdv[t * kSV + 4 * c4]);
+        TIn* o = dst + ((long)b * T + m * kC + t) * HV + 4 * c4;
+        if constexpr (sizeof(TIn) == 4) {
+          *reinterpret_cast<f32x4*>(o) = x;
+        } else {
+          typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<bf16x4_t*>(o) = bf16x4_t{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+        }
       }
-    if (tid < kC) rg = (p.g && t0 + tid < T) ? p.g[((long)b * T + t0 + tid) * p.H + h] : 0.f;
+    }
   };
 
   load(NT - 1);
@@ -115,7 +147,7 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
     const int t0 = n * kC;
     // chunk-local inclusive cumsum of the gate (wave 0), padded tokens add 0
     if (wave == 0) {
-      float x = rg;
+      float x = t0 + lane < T ? rg : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -140,7 +172,13 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
       to_f32<TIn>(rk[i], xk);
       to_f32<TIn>(rq[i], xq);
       to_f32<TIn>(rw[i], xw);
-      const float fq = p.scale * __expf(gam[t]);
+      const float live = t0 + t < T ? 1.f : 0.f;
+      const float fq = live * p.scale * __expf(gam[t]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        xk[e] *= live;
+        xw[e] *= live;
+      }
 #pragma unroll
       for (int e = 0; e < E; e += 4) {
         *reinterpret_cast<f32x4*>(&sk[t * kSK + j * E + e]) = f32x4{xk[e], xk[e + 1], xk[e + 2], xk[e + 3]};
@@ -154,6 +192,9 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
       const int pc = tid + 256 * i, t = pc / kPV, j = pc % kPV;
       float x[E];
       to_f32<TIn>(rdo[i], x);
+      const float live = t0 + t < T ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] *= live;
 #pragma unroll
       for (int e = 0; e < E; e += 4)
         *reinterpret_cast<f32x4*>(&sdo[t * kSV + j * E + e]) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
@@ -162,27 +203,47 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dvc[ct][e] = rdv[ct][e];
+      for (int e = 0; e < 4; ++e) dvc[ct][e] = t0 + 16 * wave + 4 * lq + e < T ? (float)rdv[ct][e] : 0.f;
     __syncthreads();
     if (n > 0) load(n - 1);  // registers are free again
-    // dv2 = dv + e^{gamma_L - gamma} (K dh): wave w takes tokens 16w .. 16w + 15
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 8
-    for (int ks = 0; ks < K / 4; ++ks) {
-      const float a = sk[(16 * wave + li) * kSK + 4 * ks + lq];
+    // The previous chunk's results leave now, from LDS, so that their stores are in flight
+    // during this chunk's products rather than in front of the next wait for loads (on this
+    // GPU the wait counts stores too): dh (in sdh since the top of this step) and dv2.
+    if (n + 1 < NT) {
+      store_dv2(n + 1);
+      if (p.dh_chunks) {
+        float* dst = p.dh_chunks + ((long)bh * NT + n + 1) * K * p.V + v0;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) acc[ct] = mma4(a, sdh[(4 * ks + lq) * kSV + 16 * ct + li], acc[ct]);
+        for (int i = 0; i < K * 8 / 256; ++i) {
+          const int pc = tid + 256 * i, r = pc / 8, c4 = pc % 8;
+          *reinterpret_cast<f32x4*>(dst + (long)r * p.V + 4 * c4) = *reinterpret_cast<const f32x4*>(&sdh[r * kSV + 4 * c4]);
+        }
+      }
     }
+    // dv2 = dv + e^{gamma_L - gamma} (K dh): wave w takes tokens 16w .. 16w + 15
+    // (two accumulator sets over even and odd steps, so consecutive products are independent)
+    f32x4 acc[2], acc2[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc[ct] = acc2[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int ks = 0; ks < K / 4; ks += 2) {
+      const float a0 = sk[(16 * wave + li) * kSK + 4 * ks + lq];
+      const float a1 = sk[(16 * wave + li) * kSK + 4 * ks + 4 + lq];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        acc[ct] = mma4(a0, sdh[(4 * ks + lq) * kSV + 16 * ct + li], acc[ct]);
+        acc2[ct] = mma4(a1, sdh[(4 * ks + 4 + lq) * kSV + 16 * ct + li], acc2[ct]);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc[ct] += acc2[ct];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * wave + 4 * lq + e;
       const float f = __expf(gl - gam[t]);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const float x = dvc[ct][e] + f * acc[ct][e];
-        sdv[t * kSV + 16 * ct + li] = x;
-        if (t0 + t < T)
-          static_cast<TIn*>(p.dv2)[((long)b * T + t0 + t) * HV + (long)h * p.V + v0 + 16 * ct + li] = (TIn)x;
+        sdv[t * kSV + 16 * ct + li] = dvc[ct][e] + f * acc[ct][e];
       }
     }
     __syncthreads();
@@ -194,6 +255,12 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) dh[a][ct][e] *= el;
+    // the W^T dv2 products go to a second accumulator set (independent of the Q^T do ones)
+    f32x4 dw[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) dw[a][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int ks = 0; ks < kC / 4; ++ks) {
       const int t = 4 * ks + lq;
@@ -211,21 +278,28 @@ __global__ __launch_bounds__(256) void dhu_kernel(const DhuParams p) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          dh[a][ct] = mma4(aq[a], bo[ct], dh[a][ct]);
-          dh[a][ct] = mma4(aw[a], bv[ct], dh[a][ct]);
-        }
-    }
-    if (p.dh_chunks) {
-      float* dst = p.dh_chunks + ((long)bh * NT + n) * K * p.V + v0;
+        for (int ct = 0; ct < 2; ++ct) dh[a][ct] = mma4(aq[a], bo[ct], dh[a][ct]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[(long)(32 * wave + 16 * a + 4 * lq + e) * p.V + 16 * ct + li] = dh[a][ct][e];
+        for (int ct = 0; ct < 2; ++ct) dw[a][ct] = mma4(aw[a], bv[ct], dw[a][ct]);
     }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) dh[a][ct] += dw[a][ct];
     __syncthreads();  // the tiles are rewritten by the next chunk
+  }
+  // the last chunk's results: dv2 from LDS, dh from the accumulators
+  store_dv2(0);
+  if (p.dh_chunks) {
+    float* dst = p.dh_chunks + (long)bh * NT * K * p.V + v0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(long)(32 * wave + 16 * a + 4 * lq + e) * p.V + 16 * ct + li] = dh[a][ct][e];
   }
   if (p.dh0) {
 #pragma unroll
