@@ -16,6 +16,7 @@
 // in their natural [token][channel] layout with row strides chosen so every operand read of
 // a wave falls in distinct banks.
 #include "gdn_device.h"
+#include "gdn_frame.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -254,6 +255,201 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
     }
 }
 
+// The bf16 form: the same pass with fp16 matrix-core operands (16x16x32).  bf16 inputs are
+// exact in fp16 (within its range); dh and dv2 are rounded to fp16 as operands, with fp32
+// accumulation and an fp32 dh, at the precision of the bf16 forward.  Tiles are fp16:
+// K [token][channel] read by rows (K dh contracts over channels), Q, W, do and dv2
+// [token][column] read transposed (ds_read_b64_tr_b16) where the products contract over
+// tokens; dh goes to LDS twice, fp32 for the output and fp16 transposed as an operand.
+template <int K>
+__global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
+  constexpr int E = 8, kPK = K / E, kItK = kC * kPK / kThreads, kPV = 32 / E, kNV = kC * kPV;
+  constexpr int kRK = K + 8, kRQ = K + 16, kR32 = 36, kRT = K + 8;  // fp16 row strides
+  __shared__ __attribute__((aligned(16))) f16 sk[kC * kRK];
+  __shared__ __attribute__((aligned(16))) f16 sq[kC * kRQ];
+  __shared__ __attribute__((aligned(16))) f16 sw[kC * kRQ];
+  __shared__ __attribute__((aligned(16))) f16 sdo[kC * kR32];
+  __shared__ __attribute__((aligned(16))) f16 sdv[kC * kR32];
+  __shared__ __attribute__((aligned(16))) f16 dht16[32 * kRT];  // dh^T, [column][row]
+  __shared__ __attribute__((aligned(16))) float sdv32[kC * kSV];
+  __shared__ __attribute__((aligned(16))) float sdh[K * kSV];
+  __shared__ float gam[kC];
+  static_assert(kItK * kThreads == kC * kPK && kNV <= kThreads, "tile pieces");
+  const int nvb = p.V / 32;
+  int vb, bh;
+  if (p.B * p.H % 8 == 0) {
+    const int x8 = blockIdx.x / 8;
+    bh = blockIdx.x % 8 + 8 * (x8 / nvb);
+    vb = x8 % nvb;
+  } else {
+    vb = blockIdx.x % nvb;
+    bh = blockIdx.x / nvb;
+  }
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave & 3, wc = wave >> 2;
+  const int li = lane & 15, lq = lane >> 4, trj = li >> 2, trm = li & 3;
+  const int T = p.T, NT = (T + kC - 1) / kC;
+  const bf16* q = static_cast<const bf16*>(p.q);
+  const bf16* k = static_cast<const bf16*>(p.k);
+  const bf16* w = static_cast<const bf16*>(p.w);
+  const bf16* dO = static_cast<const bf16*>(p.do_);
+  const bf16* dV = static_cast<const bf16*>(p.dv);
+  const long HK = (long)p.H * K, HV = (long)p.H * p.V;
+  const int v0 = 32 * vb, col = 16 * wc + li;
+  auto row = [&](int a, int e) { return 32 * wr + 16 * a + 4 * lq + e; };
+  f32x4 dh[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dh[a][e] = p.dht ? p.dht[((long)bh * K + row(a, e)) * p.V + v0 + col] : 0.f;
+  // next chunk's inputs (unconditional loads from clamped tokens; see dhu_kernel)
+  uint4 rk[kItK], rq[kItK], rw[kItK], rdo;
+  bf16 rdv[4];
+  float rg = 0.f;
+  auto tok = [&](int t) { return t < T ? t : T - 1; };
+  auto load = [&](int n) {
+    const int t0 = n * kC;
+#pragma unroll
+    for (int i = 0; i < kItK; ++i) {
+      const int pc = tid + kThreads * i, t = pc / kPK, j = pc % kPK;
+      const long o = ((long)b * T + tok(t0 + t)) * HK + (long)h * K + j * E;
+      rk[i] = *reinterpret_cast<const uint4*>(k + o);
+      rq[i] = *reinterpret_cast<const uint4*>(q + o);
+      rw[i] = *reinterpret_cast<const uint4*>(w + o);
+    }
+    {
+      const int pc = tid < kNV ? tid : 0, t = pc / kPV, j = pc % kPV;
+      rdo = *reinterpret_cast<const uint4*>(dO + ((long)b * T + tok(t0 + t)) * HV + (long)h * p.V + v0 + j * E);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      rdv[e] = dV[((long)b * T + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
+    if (p.g && tid < kC) rg = p.g[((long)b * T + tok(t0 + tid)) * p.H + h];
+  };
+  auto store_dv2 = [&](int m) {
+    const int r = lane >> 2, c4 = lane & 3, t = 16 * wr + r;
+    if (m * kC + t < T) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&sdv32[t * kSV + 16 * wc + 4 * c4]);
+      typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<bf16x4_t*>(static_cast<bf16*>(p.dv2) + ((long)b * T + m * kC + t) * HV +
+                                   (long)h * p.V + v0 + 16 * wc + 4 * c4) =
+          bf16x4_t{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    }
+  };
+  // 8 bf16 scaled into 8 fp16
+  auto cvt = [](const uint4& raw, float f) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
+    f16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (f16)(f * (float)v[j]);
+    return r;
+  };
+
+  load(NT - 1);
+  for (int n = NT - 1; n >= 0; --n) {
+    const int t0 = n * kC;
+    if (wave == 0) {
+      float x = t0 + lane < T ? rg : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      gam[lane] = x;
+    }
+    // dh to LDS: fp32 for the output, fp16 transposed as the B operand of K dh
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      f16x4 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sdh[row(a, e) * kSV + col] = dh[a][e];
+        hv[e] = (f16)dh[a][e];
+      }
+      *reinterpret_cast<f16x4*>(&dht16[col * kRT + row(a, 0)]) = hv;
+    }
+    __syncthreads();
+    const float gl = gam[kC - 1];
+#pragma unroll
+    for (int i = 0; i < kItK; ++i) {
+      const int pc = tid + kThreads * i, t = pc / kPK, j = pc % kPK;
+      const float live = t0 + t < T ? 1.f : 0.f;
+      *reinterpret_cast<f16x8*>(&sk[t * kRK + j * E]) = cvt(rk[i], live);
+      *reinterpret_cast<f16x8*>(&sq[t * kRQ + j * E]) = cvt(rq[i], live * p.scale * __expf(gam[t]));
+      *reinterpret_cast<f16x8*>(&sw[t * kRQ + j * E]) = cvt(rw[i], -live);
+    }
+    if (tid < kNV) {
+      const int t = tid / kPV, j = tid % kPV;
+      // two 8-byte halves: the 72-byte rows keep only 8-byte alignment
+      const f16x8 x = cvt(rdo, t0 + t < T ? 1.f : 0.f);
+      *reinterpret_cast<f16x4*>(&sdo[t * kR32 + j * E]) = f16x4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f16x4*>(&sdo[t * kR32 + j * E + 4]) = f16x4{x[4], x[5], x[6], x[7]};
+    }
+    float dvc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dvc[e] = t0 + 16 * wr + 4 * lq + e < T ? (float)rdv[e] : 0.f;
+    __syncthreads();
+    if (n > 0) load(n - 1);
+    if (n + 1 < NT) {
+      store_dv2(n + 1);
+      if (p.dh_chunks) {
+        float* dst = p.dh_chunks + ((long)bh * NT + n + 1) * K * p.V + v0;
+#pragma unroll
+        for (int i = 0; i < K * 8 / kThreads; ++i) {
+          const int pc = tid + kThreads * i, r = pc / 8, c4 = pc % 8;
+          *reinterpret_cast<f32x4*>(dst + (long)r * p.V + 4 * c4) = *reinterpret_cast<const f32x4*>(&sdh[r * kSV + 4 * c4]);
+        }
+      }
+    }
+    // dv2 = dv + e^{gamma_L - gamma} (K dh): tokens 16wr .. 16wr + 15, column half wc
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < K / 32; ++kk)
+      acc = mma16(lds8(&sk[(16 * wr + li) * kRK + 32 * kk + 8 * lq]),
+                  lds8(&dht16[col * kRT + 32 * kk + 8 * lq]), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * wr + 4 * lq + e;
+      const float x = dvc[e] + __expf(gl - gam[t]) * acc[e];
+      sdv32[t * kSV + col] = x;
+      sdv[t * kR32 + col] = (f16)x;
+    }
+    __syncthreads();
+    // dh <- e^{gamma_L} dh + (scale e^gamma Q)^T do + (-W)^T dv2: rows 32wr .. 32wr + 31
+    const float el = __expf(gl);
+    f32x4 dw[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[a][e] *= el;
+#pragma unroll
+    for (int kk = 0; kk < kC / 32; ++kk) {
+      const int r0 = 32 * kk + 8 * lq + trj;
+      const f16x8 bo = tr_pair(&sdo[r0 * kR32 + 16 * wc + 4 * trm], &sdo[(r0 + 4) * kR32 + 16 * wc + 4 * trm]);
+      const f16x8 bv = tr_pair(&sdv[r0 * kR32 + 16 * wc + 4 * trm], &sdv[(r0 + 4) * kR32 + 16 * wc + 4 * trm]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int c0 = 32 * wr + 16 * a + 4 * trm;
+        dh[a] = mma16(tr_pair(&sq[r0 * kRQ + c0], &sq[(r0 + 4) * kRQ + c0]), bo, dh[a]);
+        dw[a] = mma16(tr_pair(&sw[r0 * kRQ + c0], &sw[(r0 + 4) * kRQ + c0]), bv, dw[a]);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a) dh[a] += dw[a];
+    __syncthreads();
+  }
+  store_dv2(0);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (p.dh_chunks) p.dh_chunks[((long)bh * NT * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
+      if (p.dh0) p.dh0[((long)bh * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream) {
@@ -261,7 +457,7 @@ hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream) {
   if (dtype == 0)
     hipLaunchKernelGGL((dhu_kernel<128, float>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((dhu_kernel<128, bf16>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(dhu16_kernel<128>, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -166,7 +166,7 @@ struct DhuParams {
   float* dh0;       // [B, H, K, V] or nullptr
   int B, T, H, V;
 };
-hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream);  // K = 128
+hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream);  // K = 128; dtype 0 fp32, 1 bf16
 
 hipError_t launch_cam_prep(const CamPrepParams& p, hipStream_t stream);
 hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream);

@@ -332,8 +332,9 @@ GDN_API int cam_scan_bidi(const float* q, const float* k, const float* v, const 
  *   dht       [B,H,K,V] fp32 IN or NULL (zero)
  *   dh_chunks [B,H,NT,K,V] fp32 OUT or NULL (NT = ceil(T/64)); dv2 [B,T,H,V] OUT (dtype);
  *   dh0       [B,H,K,V] fp32 OUT or NULL
- *   dtype     GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, w, do_, dv and dv2; the arithmetic is
- *             fp32 either way
+ *   dtype     GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, w, do_, dv and dv2.  fp32: fp32
+ *             arithmetic.  bf16: fp16 matrix-core operands (dh and dv2 rounded to fp16 where
+ *             they enter a product) with fp32 accumulation and an fp32 dh
  * Supported: K = 128, V a multiple of 32 (GDN_ERR_UNSUPPORTED otherwise).  GDN_ERR_INVALID for
  * null required pointers, non-positive sizes or an unknown dtype.
  */

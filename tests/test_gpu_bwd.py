@@ -1,13 +1,14 @@
 """GPU parity of the state-gradient pass (gdn_bwd_dhu) against the fp64 oracle, through the C
-ABI.  The arithmetic is fp32 for both input dtypes (bf16 inputs are exact in fp32), so every
-output is held to 1e-4 * RMS; dv2 stored in bf16 under the storage rule."""
+ABI.  fp32 inputs: fp32 arithmetic, 1e-4 * RMS.  bf16 inputs: fp16 matrix-core operands (dh
+and dv2 rounded to fp16 where they enter a product) with fp32 accumulation, held to the
+fp16-operand rule; dv2 stored in bf16 under the storage rule."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from tests.gpu_util import assert_close, say
+from tests.gpu_util import FP16_OPERAND_TOL, assert_close, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -35,8 +36,9 @@ def test_dhu(B, T, H, V, dtype, gated, final):
     torch.cuda.synchronize()
     ref = oracle.gdn_dhu(w["q"], w["k"], w["w"], w["do"], w["dv"], g=gg, dht=dht,
                          scale=w["scale"])
+    tol = 1e-4 if dtype == "f32" else FP16_OPERAND_TOL
     for name in ("dv2", "dh", "dh0"):
-        assert_close(name, r[name], ref[name], 1e-4)
+        assert_close(name, r[name], ref[name], tol)
 
 
 def test_dhu_workload_sampled():
@@ -54,6 +56,7 @@ def test_dhu_workload_sampled():
         sl = lambda x: x[b:b + 1, :, h:h + 1]
         ref = oracle.gdn_dhu(sl(w["q"]), sl(w["k"]), sl(w["w"]), sl(w["do"]), sl(w["dv"]),
                              g=sl(w["g"]), dht=w["dht"][b:b + 1, h:h + 1], scale=w["scale"])
-        assert_close("dv2 %d,%d" % (b, h), r["dv2"][b:b + 1, :, h:h + 1], ref["dv2"], 1e-4)
-        assert_close("dh %d,%d" % (b, h), r["dh"][b:b + 1, h:h + 1], ref["dh"], 1e-4)
-        assert_close("dh0 %d,%d" % (b, h), r["dh0"][b:b + 1, h:h + 1], ref["dh0"], 1e-4)
+        tol = FP16_OPERAND_TOL
+        assert_close("dv2 %d,%d" % (b, h), r["dv2"][b:b + 1, :, h:h + 1], ref["dv2"], tol)
+        assert_close("dh %d,%d" % (b, h), r["dh"][b:b + 1, h:h + 1], ref["dh"], tol)
+        assert_close("dh0 %d,%d" % (b, h), r["dh0"][b:b + 1, h:h + 1], ref["dh0"], tol)
