@@ -332,7 +332,7 @@ def main():
         dt = inp["q"].dtype
         th = B * T * H
         alg = alg_bytes_dhu(B, T, H, K, V, 2 if dt == torch.bfloat16 else 4)
-        kernel = "gdn_bwd_dhu call: dhu16_kernel" if dt == torch.bfloat16 else "gdn_bwd_dhu call: dhu_kernel"
+        kernel = "gdn_bwd_dhu call: " + ("dhu16_kernel" if dt == torch.bfloat16 else "dhu_kernel")
         config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
                   "chunk": 64, "arithmetic": "fp32",
                   "outputs": "dv2, dh per chunk [B,H,NT,K,V] fp32, dh0"}
