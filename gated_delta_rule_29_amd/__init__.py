@@ -18,7 +18,7 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi", "gdn_bwd_dhu",
+           "cam_scan_bidi", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
            "gdn_abi_version", "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
@@ -398,4 +398,41 @@ def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, want_dh=True, w
                                  float(scale), _ptr(dh), _ptr(dv2), _ptr(dh0), B, T, H, K, V,
                                  _DT[dt], _stream(dev))
     _lib.check(rc, "gdn_bwd_dhu")
+    return {"dv2": dv2, "dh": dh, "dh0": dh0}
+
+
+def gdn_bwd_dhu_varlen(q, k, w, do, dv, cu_seqlens, g=None, dht=None, scale=1.0, *,
+                       want_dh=True, want_dh0=True):
+    """gdn_bwd_dhu over packed sequences: q, k, w [1,T,H,K], do, dv [1,T,H,V]; cu_seqlens [N+1]
+    int32 (any device; copied to both sides); g [1,T,H]; dht [N,H,K,V].  Returns dict with dv2,
+    dh [1,H,NT_total,K,V] and dh0 [N,H,K,V]."""
+    _, T, H, K = q.shape
+    V = do.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("q must be float32 or bfloat16")
+    for t, name in ((q, "q"), (k, "k"), (w, "w")):
+        _need(t, name, (1, T, H, K), dt, dev)
+    _need(do, "do", (1, T, H, V), dt, dev)
+    _need(dv, "dv", (1, T, H, V), dt, dev)
+    cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    N = cu_host.numel() - 1
+    cu_dev = cu_host.to(dev)
+    _need(g, "g", (1, T, H), torch.float32, dev)
+    _need(dht, "dht", (N, H, K, V), torch.float32, dev)
+    lib = _lib.load()
+    nt = lib.gdn_varlen_num_chunks(ctypes.c_void_p(cu_host.data_ptr()), N)
+    if nt < 0:
+        raise ValueError("malformed cu_seqlens")
+    dv2 = torch.empty(1, T, H, V, dtype=dt, device=dev)
+    dh = torch.empty(1, H, nt, K, V, dtype=torch.float32, device=dev) if want_dh else None
+    dh0 = torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if want_dh0 else None
+    ws_n = lib.gdn_bwd_dhu_varlen_workspace_bytes(N, max(nt, 1))
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.gdn_bwd_dhu_varlen(_ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(dv), _ptr(g), _ptr(dht),
+                                float(scale), _ptr(cu_dev), ctypes.c_void_p(cu_host.data_ptr()), N,
+                                _ptr(dh), _ptr(dv2), _ptr(dh0), T, H, K, V, _DT[dt], _ptr(ws), ws_n,
+                                _stream(dev))
+    _lib.check(rc, "gdn_bwd_dhu_varlen")
     return {"dv2": dv2, "dh": dh, "dh0": dh0}

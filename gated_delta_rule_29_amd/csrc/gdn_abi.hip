@@ -547,4 +547,54 @@ int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_, co
   return ok();
 }
 
+size_t gdn_bwd_dhu_varlen_workspace_bytes(int N, int NT_total) {
+  if (N <= 0 || NT_total <= 0) return 0;
+  return al256((size_t)(N + 1) * 4) + al256((size_t)NT_total * 2 * 4);
+}
+
+int gdn_bwd_dhu_varlen(const void* q, const void* k, const void* w, const void* do_,
+                       const void* dv, const float* g, const float* dht, float scale,
+                       const int* cu_seqlens, const int* cu_seqlens_host, int N, float* dh_chunks,
+                       void* dv2, float* dh0, int T_total, int H, int K, int V, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !w || !do_ || !dv || !dv2)
+    return fail(GDN_ERR_INVALID, "q, k, w, do, dv and dv2 must be non-null");
+  if (!cu_seqlens || !cu_seqlens_host)
+    return fail(GDN_ERR_INVALID, "cu_seqlens (device) and cu_seqlens_host must be non-null");
+  if (N < 1 || T_total < 1 || H <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID, "N, T_total, H, K, V must be positive (got %d, %d, %d, %d, %d)", N,
+                T_total, H, K, V);
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID, "dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16, got %d", dtype);
+  if (cu_seqlens_host[0] != 0) return fail(GDN_ERR_INVALID, "cu_seqlens[0] must be 0 (got %d)", cu_seqlens_host[0]);
+  for (int i = 0; i < N; ++i)
+    if (cu_seqlens_host[i + 1] <= cu_seqlens_host[i])
+      return fail(GDN_ERR_INVALID, "cu_seqlens must be strictly increasing (sequence %d is empty or negative)", i);
+  if (cu_seqlens_host[N] != T_total)
+    return fail(GDN_ERR_INVALID, "cu_seqlens[N] = %d differs from T_total = %d", cu_seqlens_host[N], T_total);
+  if (K != 128) return fail(GDN_ERR_UNSUPPORTED, "K must be 128, got %d", K);
+  if (V % 32) return fail(GDN_ERR_UNSUPPORTED, "V must be a multiple of 32, got %d", V);
+  const int nt = gdn_varlen_num_chunks(cu_seqlens_host, N);
+  if (nt < 0) return fail(GDN_ERR_INVALID, "too many chunks");
+  if ((int64_t)N * H * (V / 32) > INT32_MAX) return fail(GDN_ERR_INVALID, "N*H*V/32 exceeds the grid limit");
+  const size_t need = gdn_bwd_dhu_varlen_workspace_bytes(N, nt);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* coffs = static_cast<int*>(workspace);
+  int* cidx = reinterpret_cast<int*>(static_cast<char*>(workspace) + al256((size_t)(N + 1) * 4));
+  hipError_t e = gdn::launch_varlen_tables(cu_seqlens, N, coffs, cidx, st);
+  if (e != hipSuccess) return hip_fail(e, "varlen table launch");
+  gdn::DhuParams p{};
+  p.q = q; p.k = k; p.w = w; p.do_ = do_; p.dv = dv; p.g = g; p.dht = dht; p.scale = scale;
+  p.dh_chunks = dh_chunks; p.dv2 = dv2; p.dh0 = dh0;
+  p.B = N; p.T = T_total; p.H = H; p.V = V;
+  p.cu = cu_seqlens; p.coffs = coffs; p.nt_total = nt;
+  e = gdn::launch_dhu(p, dtype == GDN_DTYPE_F32 ? 0 : 1, st);
+  if (e != hipSuccess) return hip_fail(e, "gdn_bwd_dhu_varlen launch");
+  return ok();
+}
+
 }  // extern "C"

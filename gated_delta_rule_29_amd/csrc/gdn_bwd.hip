@@ -72,11 +72,25 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
     vb = blockIdx.x % nvb;
     bh = blockIdx.x / nvb;
   }
-  const int b = bh / p.H, h = bh % p.H;
+  const int h = bh % p.H;
+  // the chain's first token, length and first dh_chunks slot (dense, or a packed sequence)
+  long tb;
+  int T;
+  long dhc0;
+  if (p.cu) {
+    const int sq = bh / p.H, c0 = p.coffs[sq];
+    tb = p.cu[sq];
+    T = p.cu[sq + 1] - p.cu[sq];
+    dhc0 = (long)h * p.nt_total + c0;
+  } else {
+    tb = (long)(bh / p.H) * p.T;
+    T = p.T;
+    dhc0 = (long)bh * ((p.T + kC - 1) / kC);
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave & 3, wc = wave >> 2;  // row group and 16-column half of this wave
   const int li = lane & 15, lq = lane >> 4;
-  const int T = p.T, NT = (T + kC - 1) / kC;
+  const int NT = (T + kC - 1) / kC;
   const TIn* q = static_cast<const TIn*>(p.q);
   const TIn* k = static_cast<const TIn*>(p.k);
   const TIn* w = static_cast<const TIn*>(p.w);
@@ -106,27 +120,27 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
 #pragma unroll
     for (int i = 0; i < kItK; ++i) {
       const int pc = tid + kThreads * i, t = pc / kPK, j = pc % kPK;
-      const long o = ((long)b * T + tok(t0 + t)) * HK + (long)h * K + j * E;
+      const long o = (tb + tok(t0 + t)) * HK + (long)h * K + j * E;
       rk[i] = *reinterpret_cast<const uint4*>(k + o);
       rq[i] = *reinterpret_cast<const uint4*>(q + o);
       rw[i] = *reinterpret_cast<const uint4*>(w + o);
     }
     {
       const int pc = tid < kNV ? tid : 0, t = pc / kPV, j = pc % kPV;
-      rdo = *reinterpret_cast<const uint4*>(dO + ((long)b * T + tok(t0 + t)) * HV + (long)h * p.V + v0 + j * E);
+      rdo = *reinterpret_cast<const uint4*>(dO + (tb + tok(t0 + t)) * HV + (long)h * p.V + v0 + j * E);
     }
     // dv in the accumulator layout of the K dh product: tokens 16wr + 4lq + e, column col
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      rdv[e] = dV[((long)b * T + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
-    if (p.g && tid < kC) rg = p.g[((long)b * T + tok(t0 + tid)) * p.H + h];
+      rdv[e] = dV[(tb + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
+    if (p.g && tid < kC) rg = p.g[(tb + tok(t0 + tid)) * p.H + h];
   };
   // dv2 of chunk m from its LDS tile: wave (wr, wc) stores the 16 x 16 block it writes
   auto store_dv2 = [&](int m) {
     const int r = lane >> 2, c4 = lane & 3, t = 16 * wr + r;
     if (m * kC + t < T) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(&sdv[t * kSV + 16 * wc + 4 * c4]);
-      TIn* o = static_cast<TIn*>(p.dv2) + ((long)b * T + m * kC + t) * HV + (long)h * p.V + v0 + 16 * wc + 4 * c4;
+      TIn* o = static_cast<TIn*>(p.dv2) + (tb + m * kC + t) * HV + (long)h * p.V + v0 + 16 * wc + 4 * c4;
       if constexpr (sizeof(TIn) == 4) {
         *reinterpret_cast<f32x4*>(o) = x;
       } else {
@@ -200,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
     if (n + 1 < NT) {
       store_dv2(n + 1);
       if (p.dh_chunks) {
-        float* dst = p.dh_chunks + ((long)bh * NT + n + 1) * K * p.V + v0;
+        float* dst = p.dh_chunks + (dhc0 + n + 1) * K * p.V + v0;
 #pragma unroll
         for (int i = 0; i < K * 8 / kThreads; ++i) {
           const int pc = tid + kThreads * i, r = pc / 8, c4 = pc % 8;
@@ -250,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (p.dh_chunks) p.dh_chunks[((long)bh * NT * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
+      if (p.dh_chunks) p.dh_chunks[(dhc0 * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
       if (p.dh0) p.dh0[((long)bh * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
     }
 }
@@ -285,11 +299,25 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
     vb = blockIdx.x % nvb;
     bh = blockIdx.x / nvb;
   }
-  const int b = bh / p.H, h = bh % p.H;
+  const int h = bh % p.H;
+  // the chain's first token, length and first dh_chunks slot (dense, or a packed sequence)
+  long tb;
+  int T;
+  long dhc0;
+  if (p.cu) {
+    const int sq = bh / p.H, c0 = p.coffs[sq];
+    tb = p.cu[sq];
+    T = p.cu[sq + 1] - p.cu[sq];
+    dhc0 = (long)h * p.nt_total + c0;
+  } else {
+    tb = (long)(bh / p.H) * p.T;
+    T = p.T;
+    dhc0 = (long)bh * ((p.T + kC - 1) / kC);
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave & 3, wc = wave >> 2;
   const int li = lane & 15, lq = lane >> 4, trj = li >> 2, trm = li & 3;
-  const int T = p.T, NT = (T + kC - 1) / kC;
+  const int NT = (T + kC - 1) / kC;
   const bf16* q = static_cast<const bf16*>(p.q);
   const bf16* k = static_cast<const bf16*>(p.k);
   const bf16* w = static_cast<const bf16*>(p.w);
@@ -314,26 +342,26 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
 #pragma unroll
     for (int i = 0; i < kItK; ++i) {
       const int pc = tid + kThreads * i, t = pc / kPK, j = pc % kPK;
-      const long o = ((long)b * T + tok(t0 + t)) * HK + (long)h * K + j * E;
+      const long o = (tb + tok(t0 + t)) * HK + (long)h * K + j * E;
       rk[i] = *reinterpret_cast<const uint4*>(k + o);
       rq[i] = *reinterpret_cast<const uint4*>(q + o);
       rw[i] = *reinterpret_cast<const uint4*>(w + o);
     }
     {
       const int pc = tid < kNV ? tid : 0, t = pc / kPV, j = pc % kPV;
-      rdo = *reinterpret_cast<const uint4*>(dO + ((long)b * T + tok(t0 + t)) * HV + (long)h * p.V + v0 + j * E);
+      rdo = *reinterpret_cast<const uint4*>(dO + (tb + tok(t0 + t)) * HV + (long)h * p.V + v0 + j * E);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      rdv[e] = dV[((long)b * T + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
-    if (p.g && tid < kC) rg = p.g[((long)b * T + tok(t0 + tid)) * p.H + h];
+      rdv[e] = dV[(tb + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
+    if (p.g && tid < kC) rg = p.g[(tb + tok(t0 + tid)) * p.H + h];
   };
   auto store_dv2 = [&](int m) {
     const int r = lane >> 2, c4 = lane & 3, t = 16 * wr + r;
     if (m * kC + t < T) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(&sdv32[t * kSV + 16 * wc + 4 * c4]);
       typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<bf16x4_t*>(static_cast<bf16*>(p.dv2) + ((long)b * T + m * kC + t) * HV +
+      *reinterpret_cast<bf16x4_t*>(static_cast<bf16*>(p.dv2) + (tb + m * kC + t) * HV +
                                    (long)h * p.V + v0 + 16 * wc + 4 * c4) =
           bf16x4_t{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
     }
@@ -395,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
     if (n + 1 < NT) {
       store_dv2(n + 1);
       if (p.dh_chunks) {
-        float* dst = p.dh_chunks + ((long)bh * NT + n + 1) * K * p.V + v0;
+        float* dst = p.dh_chunks + (dhc0 + n + 1) * K * p.V + v0;
 #pragma unroll
         for (int i = 0; i < K * 8 / kThreads; ++i) {
           const int pc = tid + kThreads * i, r = pc / 8, c4 = pc % 8;
@@ -445,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (p.dh_chunks) p.dh_chunks[((long)bh * NT * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
+      if (p.dh_chunks) p.dh_chunks[(dhc0 * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
       if (p.dh0) p.dh0[((long)bh * K + row(a, e)) * p.V + v0 + col] = dh[a][e];
     }
 }

@@ -165,6 +165,11 @@ struct DhuParams {
   void* dv2;        // [B, T, H, V] (input dtype)
   float* dh0;       // [B, H, K, V] or nullptr
   int B, T, H, V;
+  // packed sequences (B = number of sequences, T = total tokens): cu [B + 1] token offsets and
+  // coffs [B + 1] chunk offsets on the device; dh_chunks is then [1, H, nt_total, K, V]
+  const int* cu;
+  const int* coffs;
+  int nt_total;
 };
 hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream);  // K = 128; dtype 0 fp32, 1 bf16
 

@@ -343,6 +343,25 @@ GDN_API int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void*
                         float* dh_chunks, void* dv2, float* dh0, int B, int T, int H, int K,
                         int V, int dtype, void* stream);
 
+/*
+ * gdn_bwd_dhu_varlen -- gdn_bwd_dhu over packed sequences (the layout of gdn_fwd_varlen):
+ * every (sequence, head) is its own chain, with chunks restarting at each sequence start.
+ *   q, k, w [1,T_total,H,K]; do_, dv, dv2 [1,T_total,H,V]; g [1,T_total,H] or NULL
+ *   cu_seqlens [N+1] int32 on the device and cu_seqlens_host, the same offsets on the host
+ *   dht, dh0 [N,H,K,V] fp32 (nullable); dh_chunks [1,H,NT_total,K,V] fp32 (nullable), chunk
+ *   c = chunk_offsets[i] + n of sequence i as in gdn_fwd_varlen (NT_total = gdn_varlen_num_chunks)
+ *   workspace  at least gdn_bwd_dhu_varlen_workspace_bytes(N, NT_total), 256-byte aligned
+ *              (the chunk tables, built on the device)
+ * Errors as gdn_bwd_dhu and gdn_fwd_varlen (malformed cu_seqlens: GDN_ERR_INVALID).
+ */
+GDN_API size_t gdn_bwd_dhu_varlen_workspace_bytes(int N, int NT_total);
+GDN_API int gdn_bwd_dhu_varlen(const void* q, const void* k, const void* w, const void* do_,
+                               const void* dv, const float* g, const float* dht, float scale,
+                               const int* cu_seqlens, const int* cu_seqlens_host, int N,
+                               float* dh_chunks, void* dv2, float* dh0, int T_total, int H,
+                               int K, int V, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -228,3 +228,20 @@ def test_dhu_validation_codes():
     assert call(dt=5) == L.ERR_INVALID
     assert call(K=64) == L.ERR_UNSUPPORTED
     assert call(V=48) == L.ERR_UNSUPPORTED
+
+
+def test_dhu_varlen_validation_codes():
+    L, lib = _lib()
+    IntArr = ctypes.c_int * 4
+
+    def call(cu, T=10, K=128, ws=None, ws_n=0):
+        return lib.gdn_bwd_dhu_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE,
+                                      IntArr(*cu), 3, None, FAKE, None, T, 2, K, 64, 0, ws, ws_n,
+                                      None)
+
+    assert call([1, 3, 6, 10]) == L.ERR_INVALID      # does not start at 0
+    assert call([0, 3, 3, 10]) == L.ERR_INVALID      # empty sequence
+    assert call([0, 3, 6, 9]) == L.ERR_INVALID       # last offset differs from T_total
+    assert call([0, 3, 6, 10], K=64) == L.ERR_UNSUPPORTED
+    assert call([0, 3, 6, 10]) == L.ERR_WORKSPACE
+    assert lib.gdn_bwd_dhu_varlen_workspace_bytes(3, 3) == 256 + 256
