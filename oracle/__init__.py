@@ -68,7 +68,7 @@ def _load():
         lib.oracle_cam_prep.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, Dd, Dd, P, P, P,
                                         P]
         lib.oracle_cam_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
-        lib.oracle_gdn_dhu.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, Dd, P, P, P]
+        lib.oracle_gdn_dhu.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, Dd, P, P, P]
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
@@ -303,20 +303,21 @@ def cam_scan(q, k, v, beta, decay, reverse=False, init_state=None, want_final=Fa
     return (out, fin) if want_final else out
 
 
-def gdn_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, chunk=CHUNK):
+def gdn_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, chunk=CHUNK, gk=None):
     """State-gradient pass of the chunked backward (dhu): q, k, w [B,T,H,K]; do, dv [B,T,H,V];
-    g [B,T,H] per-token log gates (the chunk-local cumsum is taken here); dht [B,H,K,V].
-    Returns dict with dh [B,H,NT,K,V] (gradient of the state entering each chunk), dv2
-    [B,T,H,V] (gradient of v_new) and dh0 [B,H,K,V]."""
-    q, k, w, do, dv, g, dht = map(_f64, (q, k, w, do, dv, g, dht))
+    g [B,T,H] per-token and gk [B,T,H,K] per-key log gates (the chunk-local cumsum is taken
+    here); dht [B,H,K,V].  Returns dict with dh [B,H,NT,K,V] (gradient of the state entering
+    each chunk), dv2 [B,T,H,V] (gradient of v_new) and dh0 [B,H,K,V]."""
+    q, k, w, do, dv, g, gk, dht = map(_f64, (q, k, w, do, dv, g, gk, dht))
     B, T, H, K = q.shape
     V = do.shape[-1]
     NT = (T + chunk - 1) // chunk
     dh = np.empty((B, H, NT, K, V))
     dv2 = np.empty((B, T, H, V))
     dh0 = np.empty((B, H, K, V))
-    rc = _load().oracle_gdn_dhu(B, T, H, K, V, chunk, _p(q), _p(k), _p(w), _p(g), _p(do),
-                                _p(dv), _p(dht), float(scale), _p(dh), _p(dv2), _p(dh0))
+    rc = _load().oracle_gdn_dhu(B, T, H, K, V, chunk, _p(q), _p(k), _p(w), _p(g), _p(gk),
+                                _p(do), _p(dv), _p(dht), float(scale), _p(dh), _p(dv2),
+                                _p(dh0))
     if rc != 0:
         raise RuntimeError("oracle_gdn_dhu failed")
     return {"dh": dh, "dv2": dv2, "dh0": dh0}

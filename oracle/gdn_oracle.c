@@ -618,26 +618,28 @@ int oracle_cam_scan(int B, int H, int D, int F, int S_, int reverse, const doubl
 /*
  * State-gradient pass of the chunked backward (the dhu fragments on the hyper-parallel
  * "Diff Coverage" page): the adjoint of the chunk state pass
- *     v_new = u - w h,   o = scale (e^gamma q)^T h + P v_new,   h_next = e^{gamma_L} h + K~^T v_new
- * run over chunks in reverse.  Per chain, with dh = dht (or 0) on entry and for each chunk n
- * from last to first (gamma the chunk-local inclusive cumsum of g, gamma_L at its last token):
- *     dv2_t = dv_t + e^{gamma_L - gamma_t} (dh^T k_t)        (the gradient of v_new_t)
- *     dh    = e^{gamma_L} dh + scale sum_t e^{gamma_t} q_t do_t^T - sum_t w_t dv2_t^T
+ *     v_new = u - w h,   o = scale (e^gamma q)^T h + P v_new,   h_next = diag(e^{gamma_L}) h + K~^T v_new
+ * run over chunks in reverse.  gamma_{t,d} is the chunk-local inclusive cumsum of
+ * g_t + gk_{t,d} (either may be absent), gamma_L,d its value at the chunk's last token.  Per
+ * chain, with dh = dht (or 0) on entry and for each chunk n from last to first:
+ *     dv2_t = dv_t + sum_d k_{t,d} e^{gamma_L,d - gamma_{t,d}} dh[d, :]   (the gradient of v_new_t)
+ *     dh    = diag(e^{gamma_L}) dh + scale sum_t (e^{gamma_t} * q_t) do_t^T - sum_t w_t dv2_t^T
  *     dh_chunks[n] = dh    (the gradient of the state entering chunk n)
  * and dh0 = dh at the end.  q, k, w [B,T,H,K]; do_, dv, dv2 [B,T,H,V]; g [B,T,H] or NULL;
- * dht, dh0 [B,H,K,V] (dht may be NULL); dh_chunks [B,H,NT,K,V] (may be NULL).
+ * gk [B,T,H,K] or NULL; dht, dh0 [B,H,K,V] (dht may be NULL); dh_chunks [B,H,NT,K,V] (may be
+ * NULL).
  */
 int oracle_gdn_dhu(int B, int T, int H, int K, int V, int C, const double* q, const double* k,
-                   const double* w, const double* g, const double* do_, const double* dv,
-                   const double* dht, double scale, double* dh_chunks, double* dv2,
-                   double* dh0) {
+                   const double* w, const double* g, const double* gk, const double* do_,
+                   const double* dv, const double* dht, double scale, double* dh_chunks,
+                   double* dv2, double* dh0) {
   if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || C <= 0) return -1;
   const int NT = (T + C - 1) / C;
   int fail = 0;
 #pragma omp parallel
   {
     double* dh = (double*)malloc(sizeof(double) * (size_t)K * V);
-    double* gam = (double*)malloc(sizeof(double) * (size_t)C);
+    double* gam = (double*)malloc(sizeof(double) * (size_t)C * K);
     if (!dh || !gam) {
 #pragma omp atomic write
       fail = 1;
@@ -651,29 +653,33 @@ int oracle_gdn_dhu(int B, int T, int H, int K, int V, int C, const double* q, co
           memset(dh, 0, sizeof(double) * (size_t)K * V);
         for (int n = NT - 1; n >= 0; --n) {
           const int t0 = n * C, L = (T - t0 < C) ? T - t0 : C;
-          double acc = 0.0;
-          for (int i = 0; i < L; ++i) {
-            acc += g ? g[((long)b * T + t0 + i) * H + h] : 0.0;
-            gam[i] = acc;
+          for (int d = 0; d < K; ++d) {
+            double acc = 0.0;
+            for (int i = 0; i < L; ++i) {
+              const long tk = ((long)b * T + t0 + i) * H + h;
+              acc += (g ? g[tk] : 0.0) + (gk ? gk[tk * K + d] : 0.0);
+              gam[(size_t)i * K + d] = acc;
+            }
           }
-          const double gl = gam[L - 1];
+          const double* gl = gam + (size_t)(L - 1) * K;
           /* dv2 from the gradient of the state leaving the chunk */
           for (int i = 0; i < L; ++i) {
             const long tk = ((long)b * T + t0 + i) * H + h;
-            const double f = exp(gl - gam[i]);
             for (int c = 0; c < V; ++c) {
               double s = 0.0;
-              for (int r = 0; r < K; ++r) s += k[tk * K + r] * dh[(size_t)r * V + c];
-              dv2[tk * V + c] = dv[tk * V + c] + f * s;
+              for (int r = 0; r < K; ++r)
+                s += k[tk * K + r] * exp(gl[r] - gam[(size_t)i * K + r]) * dh[(size_t)r * V + c];
+              dv2[tk * V + c] = dv[tk * V + c] + s;
             }
           }
-          const double el = exp(gl);
-          for (long e = 0; e < (long)K * V; ++e) dh[e] *= el;
+          for (int r = 0; r < K; ++r) {
+            const double el = exp(gl[r]);
+            for (int c = 0; c < V; ++c) dh[(size_t)r * V + c] *= el;
+          }
           for (int i = 0; i < L; ++i) {
             const long tk = ((long)b * T + t0 + i) * H + h;
-            const double eg = scale * exp(gam[i]);
             for (int r = 0; r < K; ++r) {
-              const double qr = eg * q[tk * K + r], wr = w[tk * K + r];
+              const double qr = scale * exp(gam[(size_t)i * K + r]) * q[tk * K + r], wr = w[tk * K + r];
               for (int c = 0; c < V; ++c)
                 dh[(size_t)r * V + c] += qr * do_[tk * V + c] - wr * dv2[tk * V + c];
             }

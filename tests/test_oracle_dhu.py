@@ -20,7 +20,7 @@ pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
 C = 4
 
 
-def _setup(T=11, H=2, K=4, V=3, seed=0, gated=True):
+def _setup(T=11, H=2, K=4, V=3, seed=0, gated=True, per_key=False):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((1, T, H, K))
     k = rng.standard_normal((1, T, H, K))
@@ -31,7 +31,9 @@ def _setup(T=11, H=2, K=4, V=3, seed=0, gated=True):
     h0 = rng.standard_normal((1, H, K, V))
     do = rng.standard_normal((1, T, H, V))
     dht = rng.standard_normal((1, H, K, V))
-    return dict(q=q, k=k, v=v, beta=beta, g=g, h0=h0, do=do, dht=dht, scale=0.7)
+    gk = (np.log(1.0 / (1.0 + np.exp(-(rng.standard_normal((1, T, H, K)) + 2.0))))
+          if per_key else None)
+    return dict(q=q, k=k, v=v, beta=beta, g=g, gk=gk, h0=h0, do=do, dht=dht, scale=0.7)
 
 
 def _loss(s, v=None, h0=None, t0=0):
@@ -40,7 +42,8 @@ def _loss(s, v=None, h0=None, t0=0):
     h0 = s["h0"] if h0 is None else h0
     sl = slice(t0, None)
     g = None if s["g"] is None else s["g"][:, sl]
-    r = oracle.gdn(s["q"][:, sl], s["k"][:, sl], v[:, sl], s["beta"][:, sl], g=g,
+    gk = None if s["gk"] is None else s["gk"][:, sl]
+    r = oracle.gdn(s["q"][:, sl], s["k"][:, sl], v[:, sl], s["beta"][:, sl], g=g, gk=gk,
                    scale=s["scale"], h0=h0)
     return float(np.sum(r["o"] * s["do"][:, sl]) + np.sum(r["ht"] * s["dht"]))
 
@@ -57,13 +60,16 @@ def _wy_inputs(s):
             L = min(C, T - t0)
             sl = slice(t0, t0 + L)
             gg = np.zeros(L) if s["g"] is None else s["g"][0, sl, h]
-            gam = np.cumsum(gg)
+            lam = gg[:, None] + (0.0 if s["gk"] is None else s["gk"][0, sl, h])  # [L, K]
+            gam = np.cumsum(lam * np.ones((L, K)), axis=0)
             kk, qq, bt = k[0, sl, h], q[0, sl, h], beta[0, sl, h]
-            D = np.exp(gam[:, None] - gam[None, :])
-            A = np.tril(bt[:, None] * (kk @ kk.T) * D, -1)
+            # sum_d x_{r,d} y_{s,d} e^{gamma_{r,d} - gamma_{s,d}}
+            gram = lambda x, y: np.einsum("rd,sd,rsd->rs", x, y,
+                                          np.exp(gam[:, None, :] - gam[None, :, :]))
+            A = np.tril(bt[:, None] * gram(kk, kk), -1)
             Tm = np.linalg.inv(np.eye(L) + A)
-            w[0, sl, h] = Tm @ (bt[:, None] * kk * np.exp(gam)[:, None])
-            P = s["scale"] * np.tril((qq @ kk.T) * D)
+            w[0, sl, h] = Tm @ (bt[:, None] * kk * np.exp(gam))
+            P = s["scale"] * np.tril(gram(qq, kk))
             dv[0, sl, h] = P.T @ do[0, sl, h]
             tms[(h, t0)] = Tm
     return w, dv, tms
@@ -80,18 +86,20 @@ def _central(f, x, eps=1e-3):
     return gr
 
 
-@pytest.mark.parametrize("gated", [True, False])
-def test_dhu_dh0_and_chunk_states_are_gradients(gated):
-    s = _setup(gated=gated)
+@pytest.mark.parametrize("gated,per_key", [(True, False), (False, False), (True, True),
+                                           (False, True)])
+def test_dhu_dh0_and_chunk_states_are_gradients(gated, per_key):
+    s = _setup(gated=gated, per_key=per_key)
     w, dv, _ = _wy_inputs(s)
     r = oracle.gdn_dhu(s["q"], s["k"], w, s["do"], dv, g=s["g"], dht=s["dht"], scale=s["scale"],
-                       chunk=C)
+                       chunk=C, gk=s["gk"])
     np.testing.assert_allclose(r["dh0"], _central(lambda h: _loss(s, h0=h), s["h0"]),
                                rtol=1e-7, atol=1e-8)
     T = s["q"].shape[1]
     for n in range(1, (T + C - 1) // C):
         pre = oracle.gdn(s["q"][:, :n * C], s["k"][:, :n * C], s["v"][:, :n * C],
                          s["beta"][:, :n * C], g=None if s["g"] is None else s["g"][:, :n * C],
+                         gk=None if s["gk"] is None else s["gk"][:, :n * C],
                          scale=s["scale"], h0=s["h0"])
         hn = pre["ht"]
         fd = _central(lambda h: _loss(s, h0=h, t0=n * C), hn)
@@ -99,11 +107,12 @@ def test_dhu_dh0_and_chunk_states_are_gradients(gated):
     np.testing.assert_array_equal(r["dh"][:, :, 0], r["dh0"])
 
 
-def test_dhu_dv2_is_the_gradient_of_v_new():
-    s = _setup(seed=1)
+@pytest.mark.parametrize("per_key", [False, True])
+def test_dhu_dv2_is_the_gradient_of_v_new(per_key):
+    s = _setup(seed=1, per_key=per_key)
     w, dv, tms = _wy_inputs(s)
     r = oracle.gdn_dhu(s["q"], s["k"], w, s["do"], dv, g=s["g"], dht=s["dht"], scale=s["scale"],
-                       chunk=C)
+                       chunk=C, gk=s["gk"])
     dl_dv = _central(lambda x: _loss(s, v=x), s["v"])
     _, T, H, _ = s["q"].shape
     for (h, t0), Tm in tms.items():
