@@ -138,6 +138,7 @@ def cpu_baseline(kind, inp, max_chains=64):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload (whole
     independent chains, so the sample does the same per-token work), timed on this host."""
     import oracle
+    import torch
 
     oracle.build()
     if kind == "bigdn_merged":
@@ -151,14 +152,15 @@ def cpu_baseline(kind, inp, max_chains=64):
     if kind == "dhu":
         B, T, H, K = inp["q"].shape
         hh = min(H, 8)
-        sub = {k: (oracle._f64(v[:1, :, :hh]) if k not in ("dht", "scale") else v)
-               for k, v in inp.items()}
+        ts = T if inp["gk"] is None else min(T, 4096)  # per-key: a bounded prefix of each chain
+        sub = {k: (oracle._f64(v[:1, :ts, :hh]) if isinstance(v, torch.Tensor) and k != "dht"
+                   else v) for k, v in inp.items()}
         return _cpu_time(lambda: oracle.gdn_dhu(sub["q"], sub["k"], sub["w"], sub["do"],
                                                 sub["dv"], g=sub["g"],
                                                 dht=oracle._f64(inp["dht"][:1, :hh]),
-                                                scale=inp["scale"]),
-                         "1 of %d batch rows x %d of %d heads (%d chains x %d tokens)"
-                         % (B, hh, H, hh, T), hh * T)
+                                                scale=inp["scale"], gk=sub["gk"]),
+                         "1 of %d batch rows x %d of %d heads (%d chains x %d of %d tokens)"
+                         % (B, hh, H, hh, ts, T), hh * ts)
     if kind == "cam":
         B, N, H, D = inp["q"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -332,15 +334,17 @@ def main():
         dt = inp["q"].dtype
         th = B * T * H
         alg = alg_bytes_dhu(B, T, H, K, V, 2 if dt == torch.bfloat16 else 4)
+        if inp["gk"] is not None:
+            alg += B * T * H * K * 4
         kernel = "gdn_bwd_dhu call: " + ("dhu16_kernel" if dt == torch.bfloat16 else "dhu_kernel")
         config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
-                  "chunk": 64, "arithmetic": "fp32",
+                  "chunk": 64, "per_key_gate": inp["gk"] is not None,
                   "outputs": "dv2, dh per chunk [B,H,NT,K,V] fp32, dh0"}
 
         def step(i):
             s = sets[i % len(sets)]
             return gdn.gdn_bwd_dhu(s["q"], s["k"], s["w"], s["do"], s["dv"], g=s["g"],
-                                   dht=s["dht"], scale=s["scale"])
+                                   dht=s["dht"], scale=s["scale"], gk=s["gk"])
     elif kind == "cam":
         B, N, H, D = inp["q"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

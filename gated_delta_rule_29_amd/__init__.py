@@ -373,9 +373,11 @@ def cam_scan_bidi(q, k, v, beta, decay, *, decay_bwd=None, init_state=None,
     return (of, orv, fin) if save_final_state else (of, orv)
 
 
-def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, want_dh=True, want_dh0=True):
+def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, gk=None, want_dh=True,
+                want_dh0=True):
     """State-gradient pass of the chunked backward.  q, k, w [B,T,H,K], do, dv [B,T,H,V] (fp32
-    or bf16, one dtype); g [B,T,H] fp32 log gates; dht [B,H,K,V] fp32.  Returns dict with dv2
+    or bf16, one dtype); g [B,T,H] and gk [B,T,H,K] fp32 log gates (gk with bf16 only); dht
+    [B,H,K,V] fp32.  Returns dict with dv2
     [B,T,H,V] (input dtype), dh [B,H,NT,K,V] fp32 (gradient of the state entering each
     64-token chunk) and dh0 [B,H,K,V] fp32."""
     B, T, H, K = q.shape
@@ -389,19 +391,20 @@ def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, want_dh=True, w
     _need(do, "do", (B, T, H, V), dt, dev)
     _need(dv, "dv", (B, T, H, V), dt, dev)
     _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(gk, "gk", (B, T, H, K), torch.float32, dev)
     _need(dht, "dht", (B, H, K, V), torch.float32, dev)
     NT = (T + CHUNK - 1) // CHUNK
     dv2 = torch.empty(B, T, H, V, dtype=dt, device=dev)
     dh = torch.empty(B, H, NT, K, V, dtype=torch.float32, device=dev) if want_dh else None
     dh0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if want_dh0 else None
-    rc = _lib.load().gdn_bwd_dhu(_ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(dv), _ptr(g), _ptr(dht),
-                                 float(scale), _ptr(dh), _ptr(dv2), _ptr(dh0), B, T, H, K, V,
+    rc = _lib.load().gdn_bwd_dhu(_ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(dv), _ptr(g), _ptr(gk),
+                                 _ptr(dht), float(scale), _ptr(dh), _ptr(dv2), _ptr(dh0), B, T, H, K, V,
                                  _DT[dt], _stream(dev))
     _lib.check(rc, "gdn_bwd_dhu")
     return {"dv2": dv2, "dh": dh, "dh0": dh0}
 
 
-def gdn_bwd_dhu_varlen(q, k, w, do, dv, cu_seqlens, g=None, dht=None, scale=1.0, *,
+def gdn_bwd_dhu_varlen(q, k, w, do, dv, cu_seqlens, g=None, dht=None, scale=1.0, *, gk=None,
                        want_dh=True, want_dh0=True):
     """gdn_bwd_dhu over packed sequences: q, k, w [1,T,H,K], do, dv [1,T,H,V]; cu_seqlens [N+1]
     int32 (any device; copied to both sides); g [1,T,H]; dht [N,H,K,V].  Returns dict with dv2,
@@ -420,6 +423,7 @@ def gdn_bwd_dhu_varlen(q, k, w, do, dv, cu_seqlens, g=None, dht=None, scale=1.0,
     N = cu_host.numel() - 1
     cu_dev = cu_host.to(dev)
     _need(g, "g", (1, T, H), torch.float32, dev)
+    _need(gk, "gk", (1, T, H, K), torch.float32, dev)
     _need(dht, "dht", (N, H, K, V), torch.float32, dev)
     lib = _lib.load()
     nt = lib.gdn_varlen_num_chunks(ctypes.c_void_p(cu_host.data_ptr()), N)
@@ -430,8 +434,8 @@ def gdn_bwd_dhu_varlen(q, k, w, do, dv, cu_seqlens, g=None, dht=None, scale=1.0,
     dh0 = torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if want_dh0 else None
     ws_n = lib.gdn_bwd_dhu_varlen_workspace_bytes(N, max(nt, 1))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
-    rc = lib.gdn_bwd_dhu_varlen(_ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(dv), _ptr(g), _ptr(dht),
-                                float(scale), _ptr(cu_dev), ctypes.c_void_p(cu_host.data_ptr()), N,
+    rc = lib.gdn_bwd_dhu_varlen(_ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(dv), _ptr(g), _ptr(gk),
+                                _ptr(dht), float(scale), _ptr(cu_dev), ctypes.c_void_p(cu_host.data_ptr()), N,
                                 _ptr(dh), _ptr(dv2), _ptr(dh0), T, H, K, V, _DT[dt], _ptr(ws), ws_n,
                                 _stream(dev))
     _lib.check(rc, "gdn_bwd_dhu_varlen")

@@ -526,7 +526,7 @@ int cam_scan_bidi(const float* q, const float* k, const float* v, const float* b
 // ---- backward: state-gradient pass --------------------------------------------------------
 
 int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_, const void* dv,
-                const float* g, const float* dht, float scale, float* dh_chunks, void* dv2,
+                const float* g, const float* gk, const float* dht, float scale, float* dh_chunks, void* dv2,
                 float* dh0, int B, int T, int H, int K, int V, int dtype, void* stream) {
   if (!q || !k || !w || !do_ || !dv || !dv2)
     return fail(GDN_ERR_INVALID, "q, k, w, do, dv and dv2 must be non-null");
@@ -537,9 +537,11 @@ int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_, co
     return fail(GDN_ERR_INVALID, "dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16, got %d", dtype);
   if (K != 128) return fail(GDN_ERR_UNSUPPORTED, "K must be 128, got %d", K);
   if (V % 32) return fail(GDN_ERR_UNSUPPORTED, "V must be a multiple of 32, got %d", V);
+  if (gk && dtype == GDN_DTYPE_F32)
+    return fail(GDN_ERR_UNSUPPORTED, "per-key gates need bf16 inputs");
   if ((int64_t)B * H * (V / 32) > INT32_MAX) return fail(GDN_ERR_INVALID, "B*H*V/32 exceeds the grid limit");
   gdn::DhuParams p{};
-  p.q = q; p.k = k; p.w = w; p.do_ = do_; p.dv = dv; p.g = g; p.dht = dht; p.scale = scale;
+  p.q = q; p.k = k; p.w = w; p.do_ = do_; p.dv = dv; p.g = g; p.gk = gk; p.dht = dht; p.scale = scale;
   p.dh_chunks = dh_chunks; p.dv2 = dv2; p.dh0 = dh0;
   p.B = B; p.T = T; p.H = H; p.V = V;
   hipError_t e = gdn::launch_dhu(p, dtype == GDN_DTYPE_F32 ? 0 : 1, static_cast<hipStream_t>(stream));
@@ -553,8 +555,8 @@ size_t gdn_bwd_dhu_varlen_workspace_bytes(int N, int NT_total) {
 }
 
 int gdn_bwd_dhu_varlen(const void* q, const void* k, const void* w, const void* do_,
-                       const void* dv, const float* g, const float* dht, float scale,
-                       const int* cu_seqlens, const int* cu_seqlens_host, int N, float* dh_chunks,
+                       const void* dv, const float* g, const float* gk, const float* dht,
+                       float scale, const int* cu_seqlens, const int* cu_seqlens_host, int N, float* dh_chunks,
                        void* dv2, float* dh0, int T_total, int H, int K, int V, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !w || !do_ || !dv || !dv2)
@@ -574,6 +576,8 @@ int gdn_bwd_dhu_varlen(const void* q, const void* k, const void* w, const void* 
     return fail(GDN_ERR_INVALID, "cu_seqlens[N] = %d differs from T_total = %d", cu_seqlens_host[N], T_total);
   if (K != 128) return fail(GDN_ERR_UNSUPPORTED, "K must be 128, got %d", K);
   if (V % 32) return fail(GDN_ERR_UNSUPPORTED, "V must be a multiple of 32, got %d", V);
+  if (gk && dtype == GDN_DTYPE_F32)
+    return fail(GDN_ERR_UNSUPPORTED, "per-key gates need bf16 inputs");
   const int nt = gdn_varlen_num_chunks(cu_seqlens_host, N);
   if (nt < 0) return fail(GDN_ERR_INVALID, "too many chunks");
   if ((int64_t)N * H * (V / 32) > INT32_MAX) return fail(GDN_ERR_INVALID, "N*H*V/32 exceeds the grid limit");
@@ -588,7 +592,7 @@ int gdn_bwd_dhu_varlen(const void* q, const void* k, const void* w, const void* 
   hipError_t e = gdn::launch_varlen_tables(cu_seqlens, N, coffs, cidx, st);
   if (e != hipSuccess) return hip_fail(e, "varlen table launch");
   gdn::DhuParams p{};
-  p.q = q; p.k = k; p.w = w; p.do_ = do_; p.dv = dv; p.g = g; p.dht = dht; p.scale = scale;
+  p.q = q; p.k = k; p.w = w; p.do_ = do_; p.dv = dv; p.g = g; p.gk = gk; p.dht = dht; p.scale = scale;
   p.dh_chunks = dh_chunks; p.dv2 = dv2; p.dh0 = dh0;
   p.B = N; p.T = T_total; p.H = H; p.V = V;
   p.cu = cu_seqlens; p.coffs = coffs; p.nt_total = nt;

@@ -275,7 +275,12 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
 // K [token][channel] read by rows (K dh contracts over channels), Q, W, do and dv2
 // [token][column] read transposed (ds_read_b64_tr_b16) where the products contract over
 // tokens; dh goes to LDS twice, fp32 for the output and fp16 transposed as an operand.
-template <int K>
+//
+// kGK (per-key gates): gamma_{t,d} = cumsum of g_t + gk_{t,d}.  Each thread takes one key and
+// a quarter of the chunk's tokens, sums its quarter in registers, and the quarters are joined
+// through LDS into a [token][key] tile of the per-key part; the decay factors then go into the
+// staged K (e^{gamma_L,d - gamma_{t,d}}) and Q (e^{gamma_{t,d}}) and into dh's rows.
+template <int K, bool kGK>
 __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
   constexpr int E = 8, kPK = K / E, kItK = kC * kPK / kThreads, kPV = 32 / E, kNV = kC * kPV;
   constexpr int kRK = K + 8, kRQ = K + 16, kR32 = 36, kRT = K + 8;  // fp16 row strides
@@ -288,7 +293,11 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
   __shared__ __attribute__((aligned(16))) float sdv32[kC * kSV];
   __shared__ __attribute__((aligned(16))) float sdh[K * kSV];
   __shared__ float gam[kC];
+  constexpr int kRG = K + 4;
+  __shared__ __attribute__((aligned(16))) float sg[kGK ? kC * kRG : 4];  // per-key cumsum part
+  __shared__ float gq[kGK ? 4 * K : 4];                                 // quarter totals
   static_assert(kItK * kThreads == kC * kPK && kNV <= kThreads, "tile pieces");
+  static_assert(!kGK || kThreads == 4 * K, "one thread per (key, quarter of the chunk)");
   const int nvb = p.V / 32;
   int vb, bh;
   if (p.B * p.H % 8 == 0) {
@@ -335,7 +344,8 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
   // next chunk's inputs (unconditional loads from clamped tokens; see dhu_kernel)
   uint4 rk[kItK], rq[kItK], rw[kItK], rdo;
   bf16 rdv[4];
-  float rg = 0.f;
+  float rg = 0.f, rgk[kGK ? 16 : 1];
+  const int gkd = tid % K, gkq = tid / K;  // this thread's key and token quarter (kGK)
   auto tok = [&](int t) { return t < T ? t : T - 1; };
   auto load = [&](int n) {
     const int t0 = n * kC;
@@ -355,6 +365,10 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
     for (int e = 0; e < 4; ++e)
       rdv[e] = dV[(tb + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
     if (p.g && tid < kC) rg = p.g[(tb + tok(t0 + tid)) * p.H + h];
+    if constexpr (kGK) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rgk[i] = p.gk[(tb + tok(t0 + 16 * gkq + i)) * HK + (long)h * K + gkd];
+    }
   };
   auto store_dv2 = [&](int m) {
     const int r = lane >> 2, c4 = lane & 3, t = 16 * wr + r;
@@ -387,6 +401,16 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
       }
       gam[lane] = x;
     }
+    float cg[kGK ? 16 : 1];
+    if constexpr (kGK) {  // this quarter's running sums of gk (tokens past T add 0)
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x += t0 + 16 * gkq + i < T ? rgk[i] : 0.f;
+        cg[i] = x;
+      }
+      gq[gkq * K + gkd] = x;
+    }
     // dh to LDS: fp32 for the output, fp16 transposed as the B operand of K dh
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -400,12 +424,33 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
     }
     __syncthreads();
     const float gl = gam[kC - 1];
+    if constexpr (kGK) {
+      float off = 0.f;
+      for (int r = 0; r < gkq; ++r) off += gq[r * K + gkd];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sg[(16 * gkq + i) * kRG + gkd] = cg[i] + off;
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < kItK; ++i) {
       const int pc = tid + kThreads * i, t = pc / kPK, j = pc % kPK;
       const float live = t0 + t < T ? 1.f : 0.f;
-      *reinterpret_cast<f16x8*>(&sk[t * kRK + j * E]) = cvt(rk[i], live);
-      *reinterpret_cast<f16x8*>(&sq[t * kRQ + j * E]) = cvt(rq[i], live * p.scale * __expf(gam[t]));
+      if constexpr (kGK) {
+        // K~ = k e^{gamma_L,d - gamma_{t,d}}, Q~ = scale q e^{gamma_{t,d}} (scalar and per-key parts)
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, rk[i]), qv = __builtin_bit_cast(bf16x8, rq[i]);
+        f16x8 ko, qo;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float gt = gam[t] + sg[t * kRG + j * E + e], gL = gl + sg[(kC - 1) * kRG + j * E + e];
+          ko[e] = (f16)(live * __expf(gL - gt) * (float)kv[e]);
+          qo[e] = (f16)(live * p.scale * __expf(gt) * (float)qv[e]);
+        }
+        *reinterpret_cast<f16x8*>(&sk[t * kRK + j * E]) = ko;
+        *reinterpret_cast<f16x8*>(&sq[t * kRQ + j * E]) = qo;
+      } else {
+        *reinterpret_cast<f16x8*>(&sk[t * kRK + j * E]) = cvt(rk[i], live);
+        *reinterpret_cast<f16x8*>(&sq[t * kRQ + j * E]) = cvt(rq[i], live * p.scale * __expf(gam[t]));
+      }
       *reinterpret_cast<f16x8*>(&sw[t * kRQ + j * E]) = cvt(rw[i], -live);
     }
     if (tid < kNV) {
@@ -440,7 +485,8 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * wr + 4 * lq + e;
-      const float x = dvc[e] + __expf(gl - gam[t]) * acc[e];
+      // (with per-key gates the factor is already inside the staged K)
+      const float x = dvc[e] + (kGK ? 1.f : __expf(gl - gam[t])) * acc[e];
       sdv32[t * kSV + col] = x;
       sdv[t * kR32 + col] = (f16)x;
     }
@@ -451,7 +497,8 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dh[a][e] *= el;
+      for (int e = 0; e < 4; ++e)
+        dh[a][e] *= kGK ? __expf(gl + sg[(kC - 1) * kRG + row(a, e)]) : el;
 #pragma unroll
     for (int kk = 0; kk < kC / 32; ++kk) {
       const int r0 = 32 * kk + 8 * lq + trj;
@@ -484,8 +531,10 @@ hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream) {
   const dim3 grid(p.B * p.H * (p.V / 32));
   if (dtype == 0)
     hipLaunchKernelGGL((dhu_kernel<128, float>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.gk)
+    hipLaunchKernelGGL((dhu16_kernel<128, true>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(dhu16_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dhu16_kernel<128, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

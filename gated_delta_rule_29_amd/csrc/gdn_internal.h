@@ -159,6 +159,7 @@ struct DhuParams {
   const void* do_;  // [B, T, H, V]
   const void* dv;   // [B, T, H, V] the intra-chunk gradient of v_new
   const float* g;   // [B, T, H] per-token log gates, or nullptr
+  const float* gk;  // [B, T, H, K] per-key log gates, or nullptr (bf16 inputs only)
   const float* dht; // [B, H, K, V] or nullptr
   float scale;
   float* dh_chunks; // [B, H, NT, K, V] or nullptr

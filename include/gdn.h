@@ -329,24 +329,29 @@ GDN_API int cam_scan_bidi(const float* q, const float* k, const float* v, const 
  *   q, k, w   [B,T,H,K] IN; w is the forward's WY w (v_new = u - w h)
  *   do_, dv   [B,T,H,V] IN: the output gradient, and the intra-chunk gradient of v_new (P^T do)
  *   g         [B,T,H] fp32 IN per-token log gates, or NULL (no decay)
+ *   gk        [B,T,H,K] fp32 IN per-key log gates, or NULL; bf16 inputs only (the chunk-local
+ *             cumsum is of g_t + gk_{t,d}: dv2 takes e^{gamma_L,d - gamma_{t,d}} inside the sum
+ *             over keys, dh's row d decays by e^{gamma_L,d}, q_t is scaled per key)
  *   dht       [B,H,K,V] fp32 IN or NULL (zero)
  *   dh_chunks [B,H,NT,K,V] fp32 OUT or NULL (NT = ceil(T/64)); dv2 [B,T,H,V] OUT (dtype);
  *   dh0       [B,H,K,V] fp32 OUT or NULL
  *   dtype     GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, w, do_, dv and dv2.  fp32: fp32
  *             arithmetic.  bf16: fp16 matrix-core operands (dh and dv2 rounded to fp16 where
  *             they enter a product) with fp32 accumulation and an fp32 dh
- * Supported: K = 128, V a multiple of 32 (GDN_ERR_UNSUPPORTED otherwise).  GDN_ERR_INVALID for
- * null required pointers, non-positive sizes or an unknown dtype.
+ * Supported: K = 128, V a multiple of 32, gk only with bf16 (GDN_ERR_UNSUPPORTED otherwise).
+ * GDN_ERR_INVALID for null required pointers, non-positive sizes or an unknown dtype.
  */
 GDN_API int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_,
-                        const void* dv, const float* g, const float* dht, float scale,
+                        const void* dv, const float* g, const float* gk, const float* dht,
+                        float scale,
                         float* dh_chunks, void* dv2, float* dh0, int B, int T, int H, int K,
                         int V, int dtype, void* stream);
 
 /*
  * gdn_bwd_dhu_varlen -- gdn_bwd_dhu over packed sequences (the layout of gdn_fwd_varlen):
  * every (sequence, head) is its own chain, with chunks restarting at each sequence start.
- *   q, k, w [1,T_total,H,K]; do_, dv, dv2 [1,T_total,H,V]; g [1,T_total,H] or NULL
+ *   q, k, w [1,T_total,H,K]; do_, dv, dv2 [1,T_total,H,V]; g [1,T_total,H] or NULL;
+ *   gk [1,T_total,H,K] or NULL
  *   cu_seqlens [N+1] int32 on the device and cu_seqlens_host, the same offsets on the host
  *   dht, dh0 [N,H,K,V] fp32 (nullable); dh_chunks [1,H,NT_total,K,V] fp32 (nullable), chunk
  *   c = chunk_offsets[i] + n of sequence i as in gdn_fwd_varlen (NT_total = gdn_varlen_num_chunks)
@@ -356,8 +361,8 @@ GDN_API int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void*
  */
 GDN_API size_t gdn_bwd_dhu_varlen_workspace_bytes(int N, int NT_total);
 GDN_API int gdn_bwd_dhu_varlen(const void* q, const void* k, const void* w, const void* do_,
-                               const void* dv, const float* g, const float* dht, float scale,
-                               const int* cu_seqlens, const int* cu_seqlens_host, int N,
+                               const void* dv, const float* g, const float* gk,
+                               const float* dht, float scale, const int* cu_seqlens, const int* cu_seqlens_host, int N,
                                float* dh_chunks, void* dv2, float* dh0, int T_total, int H,
                                int K, int V, int dtype, void* workspace, size_t workspace_bytes,
                                void* stream);

@@ -218,16 +218,17 @@ def test_dhu_validation_codes():
     L, lib = _lib()
 
     def call(**kw):
-        a = dict(q=FAKE, K=128, V=64, dt=0, T=100)
+        a = dict(q=FAKE, K=128, V=64, dt=0, T=100, gk=None)
         a.update(kw)
-        return lib.gdn_bwd_dhu(a["q"], FAKE, FAKE, FAKE, FAKE, None, None, 1.0, None, FAKE, None,
-                               1, a["T"], 2, a["K"], a["V"], a["dt"], None)
+        return lib.gdn_bwd_dhu(a["q"], FAKE, FAKE, FAKE, FAKE, None, a["gk"], None, 1.0, None, FAKE,
+                               None, 1, a["T"], 2, a["K"], a["V"], a["dt"], None)
 
     assert call(q=None) == L.ERR_INVALID
     assert call(T=0) == L.ERR_INVALID
     assert call(dt=5) == L.ERR_INVALID
     assert call(K=64) == L.ERR_UNSUPPORTED
     assert call(V=48) == L.ERR_UNSUPPORTED
+    assert call(gk=FAKE) == L.ERR_UNSUPPORTED   # per-key gates need bf16 inputs
 
 
 def test_dhu_varlen_validation_codes():
@@ -235,7 +236,7 @@ def test_dhu_varlen_validation_codes():
     IntArr = ctypes.c_int * 4
 
     def call(cu, T=10, K=128, ws=None, ws_n=0):
-        return lib.gdn_bwd_dhu_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE,
+        return lib.gdn_bwd_dhu_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1.0, FAKE,
                                       IntArr(*cu), 3, None, FAKE, None, T, 2, K, 64, 0, ws, ws_n,
                                       None)
 

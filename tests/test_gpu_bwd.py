@@ -18,24 +18,29 @@ def _dev(w):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
 
 
-@pytest.mark.parametrize("B,T,H,V,dtype,gated,final", [(1, 200, 2, 64, "f32", True, True),
-                                                        (2, 128, 3, 32, "bf16", False, False),
-                                                        (1, 64, 1, 128, "f32", True, False),
-                                                        (1, 1, 2, 32, "bf16", True, True),
-                                                        (1, 333, 2, 96, "bf16", True, True)])
-def test_dhu(B, T, H, V, dtype, gated, final):
+@pytest.mark.parametrize("B,T,H,V,dtype,gated,final,per_key",
+                         [(1, 200, 2, 64, "f32", True, True, False),
+                          (2, 128, 3, 32, "bf16", False, False, False),
+                          (1, 64, 1, 128, "f32", True, False, False),
+                          (1, 1, 2, 32, "bf16", True, True, False),
+                          (1, 333, 2, 96, "bf16", True, True, False),
+                          (1, 200, 2, 64, "bf16", True, True, True),
+                          (2, 130, 3, 32, "bf16", False, False, True)])
+def test_dhu(B, T, H, V, dtype, gated, final, per_key):
     import gated_delta_rule_29_amd as g
 
-    w = workloads.dhu_inputs(B, T, H, 128, V, dtype=dtype, seed=T + V)
+    w = workloads.dhu_inputs(B, T, H, 128, V, dtype=dtype, seed=T + V, per_key=per_key)
     gg = w["g"] if gated else None
     dht = w["dht"] if final else None
-    say("dhu B%d T%d H%d V%d %s gated%d final%d" % (B, T, H, V, dtype, gated, final))
+    say("dhu B%d T%d H%d V%d %s gated%d final%d per_key%d" % (B, T, H, V, dtype, gated, final,
+                                                              per_key))
     d = _dev(w)
     r = g.gdn_bwd_dhu(d["q"], d["k"], d["w"], d["do"], d["dv"], g=None if gg is None else d["g"],
-                      dht=None if dht is None else d["dht"], scale=w["scale"])
+                      dht=None if dht is None else d["dht"], scale=w["scale"],
+                      gk=d["gk"] if per_key else None)
     torch.cuda.synchronize()
     ref = oracle.gdn_dhu(w["q"], w["k"], w["w"], w["do"], w["dv"], g=gg, dht=dht,
-                         scale=w["scale"])
+                         scale=w["scale"], gk=w["gk"])
     tol = 1e-4 if dtype == "f32" else FP16_OPERAND_TOL
     for name in ("dv2", "dh", "dh0"):
         assert_close(name, r[name], ref[name], tol)
@@ -62,8 +67,8 @@ def test_dhu_workload_sampled():
         assert_close("dh0 %d,%d" % (b, h), r["dh0"][b:b + 1, h:h + 1], ref["dh0"], tol)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_dhu_varlen(dtype):
+@pytest.mark.parametrize("dtype,per_key", [("f32", False), ("bf16", False), ("bf16", True)])
+def test_dhu_varlen(dtype, per_key):
     """Packed sequences (1, 70, 128, 200 and 5 tokens): every sequence against the oracle run
     on it alone, and bit for bit equal to the dense pass run on each sequence separately."""
     import gated_delta_rule_29_amd as g
@@ -71,12 +76,15 @@ def test_dhu_varlen(dtype):
     lens = [1, 70, 128, 200, 5]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T, H, V = int(cu[-1]), 2, 64
-    w = workloads.dhu_inputs(1, T, H, 128, V, dtype=dtype, seed=11)
+    w = workloads.dhu_inputs(1, T, H, 128, V, dtype=dtype, seed=11, per_key=per_key)
+    gk = d_gk = None
     dht = torch.randn(len(lens), H, 128, V, generator=torch.Generator().manual_seed(3))
     say("dhu varlen %s lengths %s" % (dtype, lens))
     d = _dev(w)
+    if per_key:
+        gk, d_gk = w["gk"], d["gk"]
     r = g.gdn_bwd_dhu_varlen(d["q"], d["k"], d["w"], d["do"], d["dv"], torch.from_numpy(cu),
-                             g=d["g"], dht=dht.to(DEV), scale=w["scale"])
+                             g=d["g"], dht=dht.to(DEV), scale=w["scale"], gk=d_gk)
     torch.cuda.synchronize()
     tol = 1e-4 if dtype == "f32" else FP16_OPERAND_TOL
     c0 = 0
@@ -84,16 +92,40 @@ def test_dhu_varlen(dtype):
         sl = slice(int(cu[i]), int(cu[i + 1]))
         nt = (L + 63) // 64
         ref = oracle.gdn_dhu(w["q"][:, sl], w["k"][:, sl], w["w"][:, sl], w["do"][:, sl],
-                             w["dv"][:, sl], g=w["g"][:, sl], dht=dht[i:i + 1], scale=w["scale"])
+                             w["dv"][:, sl], g=w["g"][:, sl], dht=dht[i:i + 1], scale=w["scale"],
+                             gk=None if gk is None else gk[:, sl])
         assert_close("dv2 s%d" % i, r["dv2"][:, sl], ref["dv2"], tol)
         assert_close("dh s%d" % i, r["dh"][:, :, c0:c0 + nt], ref["dh"], tol)
         assert_close("dh0 s%d" % i, r["dh0"][i:i + 1], ref["dh0"], tol)
         one = g.gdn_bwd_dhu(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
                             d["w"][:, sl].contiguous(), d["do"][:, sl].contiguous(),
                             d["dv"][:, sl].contiguous(), g=d["g"][:, sl].contiguous(),
-                            dht=dht[i:i + 1].to(DEV), scale=w["scale"])
+                            dht=dht[i:i + 1].to(DEV), scale=w["scale"],
+                            gk=None if d_gk is None else d_gk[:, sl].contiguous())
         torch.cuda.synchronize()
         assert torch.equal(one["dv2"], r["dv2"][:, sl])
         assert torch.equal(one["dh"], r["dh"][:, :, c0:c0 + nt])
         assert torch.equal(one["dh0"], r["dh0"][i:i + 1])
         c0 += nt
+
+
+def test_dhu_perkey_workload_sampled():
+    """The long-context per-key shape (B2 H32 T32768 V128, bf16, per-key gates) in the launch
+    configuration the benchmark times; chains (0, 0) and (1, 31) against the oracle."""
+    import gated_delta_rule_29_amd as g
+
+    w = workloads.make("dhu_perkey_b2h32t32768")
+    say("dhu per-key workload")
+    d = _dev(w)
+    r = g.gdn_bwd_dhu(d["q"], d["k"], d["w"], d["do"], d["dv"], g=d["g"], dht=d["dht"],
+                      scale=w["scale"], gk=d["gk"])
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 31)):
+        sl = lambda x: x[b:b + 1, :, h:h + 1]
+        ref = oracle.gdn_dhu(sl(w["q"]), sl(w["k"]), sl(w["w"]), sl(w["do"]), sl(w["dv"]),
+                             g=sl(w["g"]), dht=w["dht"][b:b + 1, h:h + 1], scale=w["scale"],
+                             gk=sl(w["gk"]))
+        tol = FP16_OPERAND_TOL
+        assert_close("dv2 %d,%d" % (b, h), r["dv2"][b:b + 1, :, h:h + 1], ref["dv2"], tol)
+        assert_close("dh %d,%d" % (b, h), r["dh"][b:b + 1, h:h + 1], ref["dh"], tol)
+        assert_close("dh0 %d,%d" % (b, h), r["dh0"][b:b + 1, h:h + 1], ref["dh0"], tol)

@@ -102,10 +102,11 @@ def bigdn_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
             "k_scale": 1.0 / math.sqrt(D) / math.sqrt(S), "eps": 1e-5}
 
 
-def dhu_inputs(B, T, H, K, V, dtype="bf16", seed=0, g_shift=3.0):
+def dhu_inputs(B, T, H, K, V, dtype="bf16", seed=0, g_shift=3.0, per_key=False):
     """Inputs of the state-gradient pass: q, k L2-normalised per (token, head) and w with the
     magnitude of the WY w (a unit vector times a sigmoid), do, dv ~ N(0,1) in the given dtype;
-    g = log sigmoid(N(0,1) + g_shift) [B,T,H]; dht ~ N(0,1) [B,H,K,V] fp32; scale K^-1/2."""
+    g = log sigmoid(N(0,1) + g_shift) [B,T,H]; dht ~ N(0,1) [B,H,K,V] fp32; scale K^-1/2;
+    with per_key, gk = log sigmoid(N(0,1) + 3) [B,T,H,K] (drawn last)."""
     gen = _gen(seed)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     q = _l2n(torch.randn(B, T, H, K, generator=gen))
@@ -116,8 +117,10 @@ def dhu_inputs(B, T, H, K, V, dtype="bf16", seed=0, g_shift=3.0):
     dv = torch.randn(B, T, H, V, generator=gen)
     g = torch.nn.functional.logsigmoid(torch.randn(B, T, H, generator=gen) + g_shift)
     dht = torch.randn(B, H, K, V, generator=gen)
+    gk = (torch.nn.functional.logsigmoid(torch.randn(B, T, H, K, generator=gen) + 3.0)
+          if per_key else None)
     return {"q": q.to(dt), "k": k.to(dt), "w": w.to(dt), "do": do.to(dt), "dv": dv.to(dt),
-            "g": g, "dht": dht, "scale": K ** -0.5}
+            "g": g, "gk": gk, "dht": dht, "scale": K ** -0.5}
 
 
 def cam_inputs(B, F, S, H, D, seed=0, decay_shift=3.0, translate=0.3):
@@ -180,6 +183,9 @@ WORKLOADS = {
     # state-gradient pass of the backward (dhu) at the dense bf16 shape
     "dhu_bf16_b4h16t4096": dict(kind="dhu", B=4, T=4096, H=16, K=128, V=128, dtype="bf16",
                                 seed=0),
+    # the same pass at the long-context per-key shape
+    "dhu_perkey_b2h32t32768": dict(kind="dhu", B=2, T=32768, H=32, K=128, V=128, dtype="bf16",
+                                   seed=0, per_key=True),
     # the camera branch of the same video block (fp32): camera prep, then the forward and
     # the reverse numerator-only frame scans
     "cam_video_f16x1024": dict(kind="cam", B=1, F=16, S=1024, H=16, D=128, seed=0),
