@@ -31,6 +31,13 @@ namespace gdn {
 
 namespace {
 
+// Workgroup ids are dealt to the eight XCDs round-robin.  When the grid is a multiple of eight,
+// XCD x takes the contiguous range [x n/8, (x+1) n/8) of logical indices in order, so logical
+// neighbours (which share table or state reads) run close in time on one XCD's L2.
+__device__ __forceinline__ int xcd_logical(int bid, int n) {
+  return n % 8 ? bid : (bid % 8) * (n / 8) + bid / 8;
+}
+
 // ---- inverse RMS ------------------------------------------------------------------------
 // One wave per token (eight tokens per workgroup): 1 / sqrt(mean of x^2 over the H*D channels
 // + eps) of q and k; a lane reads 16-byte pieces, so a wave's load covers 1 KB of the row.
@@ -83,11 +90,13 @@ __global__ __launch_bounds__(4 * D) void cam_prep_kernel(const CamPrepParams p) 
   __shared__ __attribute__((aligned(16))) float pm[2][64 * 16];  // proj_q, proj_kv per token
   __shared__ __attribute__((aligned(16))) float inv[2][64];
   __shared__ float red[2][2][64];  // [half][pre, post][token]
+  // logical order: head fastest, so the heads of one token tile (which read the same camera
+  // matrices and RoPE rows) follow one another on one XCD
   const int nt = (p.N + 63) / 64;
-  int x = blockIdx.x;
-  const int tb = x % nt;
-  x /= nt;
-  const int h = x % p.H, b = x / p.H;
+  int x = xcd_logical(blockIdx.x, gridDim.x);
+  const int h = x % p.H;
+  x /= p.H;
+  const int tb = x % nt, b = x / nt;
   const int n0 = tb * 64;
   const int tid = threadIdx.x;
   const int half = tid / (2 * D);         // 0: camera matrix, 1: RoPE (wave-uniform)
@@ -327,7 +336,8 @@ __global__ __launch_bounds__(256) void cam_out_kernel(const CamScanParams p, int
   const int F = p.F, S = p.S;
   const long N = (long)F * S;
   const int ngrp = (S / 64) / grp;
-  int x = blockIdx.x;
+  // the token groups of one (b, h, frame), which read the same states, on one XCD in turn
+  int x = xcd_logical(blockIdx.x, gridDim.x);
   const int gi = x % ngrp;
   x /= ngrp;
   const int f = x % F, bh = x / F;
