@@ -12,6 +12,16 @@
  * chunk_gated_delta_rule_fwd_h on the hyper-parallel "Diff Coverage" page), and the masked
  * intra-chunk output.  The result equals the token recurrence up to rounding.
  *
+ * Entry points, in the order declared below:
+ *  - the forward, dense (gdn_fwd) and packed (gdn_fwd_varlen, gdn_varlen_num_chunks);
+ *  - the BiGDN video block of the SANA pages: its front end (gdn_prep), the frame-level scan
+ *    in both directions (bigdn_fwd) and the block output with reverse-direction overrides and
+ *    the merge (bigdn_fwd_merged);
+ *  - a fragment's state summary and the joining of fragments (gdn_state_summary,
+ *    gdn_state_apply), the single-GPU part of context parallelism;
+ *  - the camera branch of the video block (cam_prep, cam_scan, cam_scan_bidi);
+ *  - the backward's state-gradient pass (gdn_bwd_dhu, gdn_bwd_dhu_varlen).
+ *
  * Conventions shared by every entry point.
  *  - All tensor pointers are DEVICE pointers unless the name ends in _host.  The caller owns
  *    all memory, including any workspace; the library keeps no device allocation between
@@ -26,8 +36,8 @@
  *  - Every argument is validated on the host before anything is launched; on an error
  *    nothing is written.  The return value is a status code below, and gdn_last_error()
  *    returns a message for the calling thread's most recent failure.
- *  - Results are deterministic: the forward path uses no atomics, so two identical calls
- *    give bitwise-identical outputs.
+ *  - Results are deterministic: no entry point uses atomics, so two identical calls give
+ *    bitwise-identical outputs.
  */
 #ifndef GDN_H_
 #define GDN_H_
