@@ -129,3 +129,16 @@ def test_dhu_perkey_workload_sampled():
         assert_close("dv2 %d,%d" % (b, h), r["dv2"][b:b + 1, :, h:h + 1], ref["dv2"], tol)
         assert_close("dh %d,%d" % (b, h), r["dh"][b:b + 1, h:h + 1], ref["dh"], tol)
         assert_close("dh0 %d,%d" % (b, h), r["dh0"][b:b + 1, h:h + 1], ref["dh0"], tol)
+
+
+def test_dhu_deterministic():
+    """Two identical calls give bitwise-identical outputs (no atomics anywhere)."""
+    import gated_delta_rule_29_amd as g
+
+    w = _dev(workloads.dhu_inputs(2, 300, 3, 128, 64, seed=5, per_key=True))
+    args = (w["q"], w["k"], w["w"], w["do"], w["dv"])
+    ra = g.gdn_bwd_dhu(*args, g=w["g"], dht=w["dht"], scale=w["scale"], gk=w["gk"])
+    rb = g.gdn_bwd_dhu(*args, g=w["g"], dht=w["dht"], scale=w["scale"], gk=w["gk"])
+    torch.cuda.synchronize()
+    for key in ("dv2", "dh", "dh0"):
+        assert torch.equal(ra[key], rb[key])
