@@ -595,13 +595,17 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
   __shared__ __attribute__((aligned(16))) f16 qr[kHW][64 * kSP];  // Q_rot rows, padded
   __shared__ float zsum[kHW][D];
   __shared__ float den_part[kHW][64];
-  const int ngrp = (p.S / 64) / grp;
-  int x = blockIdx.x;
+  // Logical order: head group fastest, then token group, frame and batch; when the grid is a
+  // multiple of eight, XCD x takes the contiguous range [x n/8, (x+1) n/8) of it, so the head
+  // groups of one token block (same RoPE rows) and the token groups of one (head, frame)
+  // (same states) run close in time on one XCD's L2.
+  const int ngrp = (p.S / 64) / grp, nhg = p.H / kHeads, nwg = gridDim.x;
+  int x = nwg % 8 ? (int)blockIdx.x : (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+  const int h0 = (x % nhg) * kHeads;
+  x /= nhg;
   const int g = x % ngrp;
   x /= ngrp;
-  const int f = x % p.F;
-  x /= p.F;
-  const int h0 = (x % (p.H / kHeads)) * kHeads, b = x / (p.H / kHeads);
+  const int f = x % p.F, b = x / p.F;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const int C = p.H * D, o = tid % kOct;
