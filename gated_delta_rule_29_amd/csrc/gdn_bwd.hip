@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       rdv[e] = dV[(tb + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
-    if (p.g && tid < kC) rg = p.g[(tb + tok(t0 + tid)) * p.H + h];
+    if (p.g && tid < kC) rg = floor_gate(p.g[(tb + tok(t0 + tid)) * p.H + h]);
   };
   // dv2 of chunk m from its LDS tile: wave (wr, wc) stores the 16 x 16 block it writes
   auto store_dv2 = [&](int m) {
@@ -364,10 +364,16 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       rdv[e] = dV[(tb + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
-    if (p.g && tid < kC) rg = p.g[(tb + tok(t0 + tid)) * p.H + h];
+    if (p.g && tid < kC) rg = floor_gate(p.g[(tb + tok(t0 + tid)) * p.H + h]);
     if constexpr (kGK) {
+      // gk' = max(g + gk, floor) - g, so that the two cumulative sums add up to the floored
+      // per-key decay of the forward pass
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rgk[i] = p.gk[(tb + tok(t0 + 16 * gkq + i)) * HK + (long)h * K + gkd];
+      for (int i = 0; i < 16; ++i) {
+        const long ti = tb + tok(t0 + 16 * gkq + i);
+        const float gt = p.g ? floor_gate(p.g[ti * p.H + h]) : 0.f;
+        rgk[i] = floor_key_gate(gt + p.gk[ti * HK + (long)h * K + gkd]) - gt;
+      }
     }
   };
   auto store_dv2 = [&](int m) {

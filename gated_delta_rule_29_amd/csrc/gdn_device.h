@@ -97,6 +97,19 @@ __device__ __forceinline__ typename Vec8<T>::type pack8(const f32x4& a, const f3
   return r;
 }
 
+// Gate floors.  A per-token log decay of -inf (a hard reset of the state, alpha = 0) would
+// turn the differences of cumulative decays into inf - inf.  Every kernel therefore reads a
+// scalar gate as max(g, kGateFloor): e^-40 = 4.2e-18 leaves at most that fraction of the state
+// it erases, below fp32 resolution.  With a per-key gate the combined per-key log decay
+// g + gk of one token is floored at kKeyGateFloor instead: the per-key intra-chunk products
+// factor e^{gamma_r - gamma_s} around a reference token inside each 16-token block, and the
+// factors stay inside the fp32 / bf16 exponent range (|x| <= e^88) only while 8 tokens of
+// decay span at most 80; a floored token keeps at most e^-10 = 4.5e-5 of what it erases.
+constexpr float kGateFloor = -40.f;
+constexpr float kKeyGateFloor = -10.f;
+__device__ __forceinline__ float floor_gate(float g) { return fmaxf(g, kGateFloor); }
+__device__ __forceinline__ float floor_key_gate(float lam) { return fmaxf(lam, kKeyGateFloor); }
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
 #pragma unroll

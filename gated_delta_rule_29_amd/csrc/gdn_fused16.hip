@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       const int t = c * kC + lane;
       const bool ok = c < nchunks && t < len;
       const long gi = (tok0 + t) * p.H + h;
-      gv = ok && p.g ? p.g[gi] : 0.f;
+      gv = ok && p.g ? floor_gate(p.g[gi]) : 0.f;
       bv = ok ? p.beta[gi] : 0.f;
     };
     // gate slot of chunk c from its g, beta (rows past the end carry g = 0, beta = 0)
@@ -580,15 +580,23 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         for (int t = 0; t < 2; ++t) qfr[G][t][Gk] = lds_at<bf16x8>(qb[t], 1024 * G + 2048 * Gk);
   };
   __syncthreads();
+  // Step -1 (the other roles' first step): the first half of chunk 0's K rows.  It is peeled
+  // off the loop so that the loop body has one path: a loop whose body merges two paths makes
+  // the compiler copy every loop-carried register (state and prefetched K rows) at the end of
+  // each step.
+  {
+    const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+    const int ob[2] = {tix(pair_row(0, 0, li), 8 * lq), tix(pair_row(0, 1, li), 8 * lq)};
+    read_k(0, ob, 0, kG / 2);  // chunk 0's slot (stale and unused when there are no chunks)
+  }
+  __syncthreads();
 
-  for (int n = -1; n < nchunks; ++n) {
+  for (int n = 0; n < nchunks; ++n) {
     const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
     const int trj = (lane >> 2) & 3, trc = lane & 3;
     const int ob[2] = {tix(pair_row(0, 0, li), 8 * lq), tix(pair_row(0, 1, li), 8 * lq)};
     const int ot[2] = {tix(8 * lq + trj, 8 * trc), tix(8 * lq + 4 + trj, 8 * trc)};
-    if (n < 0) {
-      if (nchunks > 0) read_k(0, ob, 0, kG / 2);
-    } else {
+    {
       const typename SM::QK& Q = s.qk[n % 3];
       const u16* vt = s.v[n & 1];
       const typename SM::TP& T = s.tp[n & 1];

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(const FwdParams p)
   if (tid < kC) {
     const bool ok = tid < rows;
     const long gi = (cp.tok0 + t0 + tid) * p.H + h;
-    s.g[tid] = ok && p.g ? p.g[gi] : 0.f;
+    s.g[tid] = ok && p.g ? floor_gate(p.g[gi]) : 0.f;
     s.beta[tid] = ok ? p.beta[gi] : 0.f;
   }
   constexpr int kTPK = kThreads / K, kGT = kC / kTPK;
@@ -358,7 +358,7 @@ __device__ __forceinline__ void scan_load(ScanStage<TI, K, PK>& st, const FwdPar
   const float* fs = reinterpret_cast<const float*>(slot + SL::kEg);
   if (tid < 128) st.vec = PK ? 0.f : fs[tid];  // e^gamma, then e^{gl - gamma}
   else if (tid < 192) st.vec = t < rows ? p.beta[gi] : 0.f;
-  else st.vec = (t < rows && p.g) ? p.g[gi] : 0.f;
+  else st.vec = (t < rows && p.g) ? floor_gate(p.g[gi]) : 0.f;
   st.egl = PK ? 0.f : fs[2 * kC];
   if constexpr (PK) {
     const int d = tid / St::kTPK, part = tid % St::kTPK;

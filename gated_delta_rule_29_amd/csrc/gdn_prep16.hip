@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void prep16_kernel(const FwdParams p) {
   if (tid < kC) {
     const bool ok = tid < rows;
     const long gi = (tok + tid) * p.H + h;
-    s.g[tid] = ok && p.g ? p.g[gi] : 0.f;
+    s.g[tid] = ok && p.g ? floor_gate(p.g[gi]) : 0.f;
     s.beta[tid] = ok ? p.beta[gi] : 0.f;
   }
   constexpr int kTPK = kThreads / K, kGT = kC / kTPK;
@@ -233,24 +233,46 @@ __global__ __launch_bounds__(kThreads) void prep16_kernel(const FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-key gate.  The scaled operands are formed in registers from global loads: thread
-// (octet o, part) holds keys 8o .. 8o+7 for kTP consecutive tokens, so the per-key cumulative
-// decay is a running sum over its tokens plus a prefix over the parts (lanes of one wave),
-// and every scaled operand leaves as 16-byte pieces: to LDS for the Gram and Q K^T products
-// and straight to the slot for the scan.  The operand tiles share LDS with the solve's work
-// arrays, which keeps the kernel at 2 workgroups per CU.
+// Per-key gate.  Thread (octet o, part) loads keys 8o .. 8o+7 of q, k and gk for kTP
+// consecutive tokens, so the per-key cumulative decay is a running sum over its tokens plus a
+// prefix over the parts (lanes of one wave).
+//
+// The decay of a Gram / Q K^T entry sits inside the key sum, sum_d x_{r,d} k_{s,d}
+// e^{gamma_{r,d} - gamma_{s,d}} (s <= r), so it is factored around a reference token m as
+// (x_r e^{gamma_r - gamma_m}) . (k_s e^{gamma_m - gamma_s}).  Each 16x16 tile takes its own
+// reference, chosen so that the factors stay in range for any decay:
+//  - off-diagonal tile (I, J < I): m = 16I, the first row of block I.  Both factors are then
+//    at most 1 (gamma only decreases), so the tiles take fp16 operands; a factor that
+//    underflows belongs to a product that is smaller still.
+//  - diagonal tile (I, I): m = 16I + 8.  The factors span e^{+-8 lambda_max}; with the per-key
+//    log decay floored at kKeyGateFloor (-10) they stay within e^{+-80}, inside the bf16
+//    exponent range.  The Gram tile takes bf16 operands; the Q K^T tile (the intra-chunk part
+//    of the output) needs more than bf16's 8-bit significand, so both of its operands are
+//    split into a bf16 value and a bf16 remainder and three products are summed.
+// The operand tiles of the four phases (off-diagonal K rows, off-diagonal Q rows, diagonal
+// tiles of blocks 0-1, of blocks 2-3) share one LDS region with the solve's work arrays,
+// which keeps the kernel at 2 workgroups per CU.
+//
+// The scan's operands go straight to the slot in fp16: Q e^{gamma}, K e^{gamma} and
+// K e^{gamma_last - gamma}, all at most |x| (the per-key reference of the scan is 1).
 // ---------------------------------------------------------------------------------------
 template <int K>
 struct __attribute__((aligned(16))) PrepPkSmem {
   typedef f16 TO;
   static constexpr int kTP = kC + 8;
+  static constexpr int kBlk = 16 * K;  // elements of one 16-row operand block
   union {
-    struct {
-      u16 q[kC * K];   // fp16 Q e^{gamma - gamma_mid}        (pix layout)
-      u16 k[kC * K];   // fp16 K e^{gamma - gamma_mid}        (pix layout)
-      u16 kb[kC * K];  // fp16 K e^{gamma_mid - gamma}: Gram columns (pix layout)
+    struct {                   // off-diagonal tiles (fp16)
+      u16 row[kC * K];         // K (then Q) times e^{gamma - gamma_{16b}}, b the row's block (pix)
+      u16 col[6 * kBlk];       // K times e^{gamma_{16I} - gamma} on the rows of block J < I,
+                               // pair (I, J) at block I (I - 1) / 2 + J (tix_s32<16>)
     };
-    struct {           // solve work arrays, used once the products are done
+    struct {                   // diagonal tiles of two blocks (bf16, tix_s32<32>)
+      u16 dqh[2 * kBlk], dql[2 * kBlk];  // Q e^{gamma - gamma_mid}: value and remainder
+      u16 dk[2 * kBlk];                  // K e^{gamma - gamma_mid}
+      u16 dch[2 * kBlk], dcl[2 * kBlk];  // K e^{gamma_mid - gamma}: value and remainder
+    };
+    struct {                   // solve work arrays, used once the products are done
       float x[32][36];
       TO tm[kC][kTP];
     };
@@ -316,19 +338,20 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
     kv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, t * qk_row + 16 * o, 0, 0));
     gk0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * gk_row + 32 * o, 0, 0));
     gk1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * gk_row + 32 * o + 16, 0, 0));
-    gt[i] = (p.g && (uint32_t)t < rows) ? p.g[(tok + t) * p.H + h] : 0.f;
+    gt[i] = (p.g && (uint32_t)t < rows) ? floor_gate(p.g[(tok + t) * p.H + h]) : 0.f;
   }
   if (tid < kC) s.beta[tid] = (uint32_t)tid < rows ? p.beta[(tok + tid) * p.H + h] : 0.f;
 
-  // ---- per-key cumulative decay gamma[t][8o + j]: running sum over this thread's tokens,
-  // then the exclusive prefix over the parts before it (Hillis-Steele over the part lanes)
+  // ---- per-key cumulative decay gamma[t][8o + j] of lambda = max(g + gk, kKeyGateFloor):
+  // running sum over this thread's tokens, then the exclusive prefix over the parts before it
+  // (Hillis-Steele over the part lanes).  Rows past the end carry lambda = 0.
   float gam[kTP][8], tot[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < kTP; ++i) {
-      run += gt[i] + (j < 4 ? gk0[i][j] : gk1[i][j - 4]);
+      run += floor_key_gate(gt[i] + (j < 4 ? gk0[i][j] : gk1[i][j - 4]));
       gam[i][j] = run;
     }
     tot[j] = run;
@@ -344,64 +367,90 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
       incl[j] += part >= sh ? u : 0.f;
     }
   }
-  float gm[8], gl[8];
   const int row0 = lane & ~(kParts - 1);  // lane of part 0 of this octet
+  float gl[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float ex = incl[j] - tot[j];
 #pragma unroll
     for (int i = 0; i < kTP; ++i) gam[i][j] += ex;
-    gm[j] = __shfl(incl[j], row0 + (kC / 2) / kTP - 1, 64);  // gamma at token 31
-    gl[j] = __shfl(incl[j], row0 + kParts - 1, 64);          // gamma at token 63
+    gl[j] = __shfl(incl[j], row0 + kParts - 1, 64);  // gamma at token 63
   }
+  // gamma at the first and the middle token of each 16-token block (element 0 of a part,
+  // since kTP divides 8)
+  float gs[4][8], gmid[4][8];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      gs[I][j] = __shfl(gam[0][j], row0 + (16 * I) / kTP, 64);
+      gmid[I][j] = __shfl(gam[0][j], row0 + (16 * I + 8) / kTP, 64);
+    }
   if (part == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      vec[SL::kEmid + 8 * o + j] = __expf(gm[j]);
+      vec[SL::kEmid + 8 * o + j] = 1.f;  // the scan's operands carry e^{gamma} themselves
       vec[SL::kEglk + 8 * o + j] = __expf(gl[j]);
     }
   }
+  const int blk = (part * kTP) / 16;  // this thread's 16-token block
 
-  // ---- scaled operands: Q, K times e^{gamma - gamma_mid} (LDS and slot), K times
-  // e^{gamma_mid - gamma} (LDS: Gram columns), K times e^{gamma_last - gamma} (slot)
-  float lm[8];
+  // bf16 raw -> fp32
+  auto unpack = [](const u32x4& w, f32x4& lo4, f32x4& hi4) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) lm[j] = __expf(gl[j] - gm[j]);
+    for (int j = 0; j < 4; ++j) {
+      const unsigned x0 = w[j >> 1], x1 = w[2 + (j >> 1)];
+      lo4[j] = (j & 1) ? __uint_as_float(x0 & 0xffff0000u) : __uint_as_float(x0 << 16);
+      hi4[j] = (j & 1) ? __uint_as_float(x1 & 0xffff0000u) : __uint_as_float(x1 << 16);
+    }
+  };
+  // x (8 keys) times e^{e[j]} into 8 16-bit values of type T
+  auto scaled = [](const f32x4& x0, const f32x4& x1, const float* e, auto tag) {
+    typedef decltype(tag) T;
+    f32x4 y0, y1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y0[j] = x0[j] * __expf(e[j]);
+      y1[j] = x1[j] * __expf(e[4 + j]);
+    }
+    return __builtin_bit_cast(u32x4, pack8<T>(y0, y1));
+  };
+  // bf16 value and bf16 remainder of x (8 keys) times e^{e[j]}
+  auto split = [](const f32x4& x0, const f32x4& x1, const float* e, u32x4& hi, u32x4& lo) {
+    f32x4 y0, y1, r0, r1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y0[j] = x0[j] * __expf(e[j]);
+      y1[j] = x1[j] * __expf(e[4 + j]);
+    }
+    const bf16x8 h = pack8<bf16>(y0, y1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r0[j] = y0[j] - (float)h[j];
+      r1[j] = y1[j] - (float)h[4 + j];
+    }
+    hi = __builtin_bit_cast(u32x4, h);
+    lo = __builtin_bit_cast(u32x4, pack8<bf16>(r0, r1));
+  };
+
+  // ---- the scan's operands, straight to the slot: Q e^{gamma}, K e^{gamma} and
+  // K e^{gamma_last - gamma} (fp16)
+  f32x4 qf0[kTP], qf1[kTP], kf0[kTP], kf1[kTP];
 #pragma unroll
   for (int i = 0; i < kTP; ++i) {
     const int t = part * kTP + i;
-    f32x4 up0, up1, dn0, dn1, kf0, kf1, qf0, qf1;
+    unpack(qv[i], qf0[i], qf1[i]);
+    unpack(kv[i], kf0[i], kf1[i]);
+    float e[8], el[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      up0[j] = __expf(gam[i][j] - gm[j]);
-      up1[j] = __expf(gam[i][4 + j] - gm[4 + j]);
-      dn0[j] = __expf(gm[j] - gam[i][j]);
-      dn1[j] = __expf(gm[4 + j] - gam[i][4 + j]);
-      const unsigned kw0 = kv[i][j >> 1], kw1 = kv[i][2 + (j >> 1)];
-      const unsigned qw0 = qv[i][j >> 1], qw1 = qv[i][2 + (j >> 1)];
-      kf0[j] = (j & 1) ? __uint_as_float(kw0 & 0xffff0000u) : __uint_as_float(kw0 << 16);
-      kf1[j] = (j & 1) ? __uint_as_float(kw1 & 0xffff0000u) : __uint_as_float(kw1 << 16);
-      qf0[j] = (j & 1) ? __uint_as_float(qw0 & 0xffff0000u) : __uint_as_float(qw0 << 16);
-      qf1[j] = (j & 1) ? __uint_as_float(qw1 & 0xffff0000u) : __uint_as_float(qw1 << 16);
+    for (int j = 0; j < 8; ++j) {
+      e[j] = gam[i][j];
+      el[j] = gl[j] - gam[i][j];
     }
-    f32x4 lh0, lh1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lh0[j] = lm[j] * dn0[j];
-      lh1[j] = lm[4 + j] * dn1[j];
-    }
-    const u32x4 qu = __builtin_bit_cast(u32x4, pack8<f16>(qf0 * up0, qf1 * up1));
-    const u32x4 ku = __builtin_bit_cast(u32x4, pack8<f16>(kf0 * up0, kf1 * up1));
-    const u32x4 kb = __builtin_bit_cast(u32x4, pack8<f16>(kf0 * dn0, kf1 * dn1));
-    const u32x4 kh = __builtin_bit_cast(u32x4, pack8<f16>(kf0 * lh0, kf1 * lh1));
-    const int ix = pix(t, 8 * o);
-    *reinterpret_cast<u32x4*>(&s.q[ix]) = qu;
-    *reinterpret_cast<u32x4*>(&s.k[ix]) = ku;
-    *reinterpret_cast<u32x4*>(&s.kb[ix]) = kb;
     const int sx = 2 * tix_s32<kC>(t, 8 * o);
-    *reinterpret_cast<u32x4*>(slot + SL::kQ + sx) = qu;
-    *reinterpret_cast<u32x4*>(slot + SL::kK + sx) = ku;
-    *reinterpret_cast<u32x4*>(slot + SL::kKh + sx) = kh;
+    *reinterpret_cast<u32x4*>(slot + SL::kQ + sx) = scaled(qf0[i], qf1[i], e, f16{});
+    *reinterpret_cast<u32x4*>(slot + SL::kK + sx) = scaled(kf0[i], kf1[i], e, f16{});
+    *reinterpret_cast<u32x4*>(slot + SL::kKh + sx) = scaled(kf0[i], kf1[i], el, f16{});
   }
   // strict upper 16x16 tiles of A and P stay zero
   for (int e = tid; e < 6 * 256; e += kThreads) {
@@ -411,38 +460,130 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
     s.a[16 * I + r][16 * J + c] = 0.f;
     s.p[16 * I + r][16 * J + c] = (f16)0.f;
   }
-  __syncthreads();
-  if (tid < kC) vec[SL::kBeta + tid] = s.beta[tid];
 
-  // ---- Gram (-> A, rows scaled by beta) and Q K^T (-> P), lower 16x16 tiles: 20 jobs,
-  // 5 per wave
-  const f16* qt = reinterpret_cast<const f16*>(s.q);
-  const f16* kt = reinterpret_cast<const f16*>(s.k);
-  const f16* kbt = reinterpret_cast<const f16*>(s.kb);
-#pragma unroll
-  for (int ji = 0; ji < 5; ++ji) {
-    const int job = wave + 4 * ji;
-    const bool is_qk = job >= 10;
-    int I, J;
-    tri_tile(is_qk ? job - 10 : job, I, J);
-    const f16* at = is_qk ? qt : kt;
-    f16x8 av[kG], bv[kG];
+  // One 16x16 product tile: rows 16 RI + li of tile `at`, rows 16 RJ + li of tile `bt` (both
+  // R-row column-split tiles), contraction over the K keys.
+  auto tile = [&](auto ra_c, const u16* at, int RI, auto rb_c, const u16* bt, int RJ, auto elt,
+                  f32x4 acc) {
+    constexpr int RA = decltype(ra_c)::value, RB = decltype(rb_c)::value;
+    typedef decltype(elt) T;
+    typedef typename Vec8<T>::type T8;
+    const T* a = reinterpret_cast<const T*>(at);
+    const T* b = reinterpret_cast<const T*>(bt);
+    T8 av[kG], bv[kG];
 #pragma unroll
     for (int kk = 0; kk < kG; ++kk) {
-      av[kk] = lds8(at + pix(16 * I + li, 32 * kk + 8 * lq));
-      bv[kk] = lds8(kbt + pix(16 * J + li, 32 * kk + 8 * lq));
+      av[kk] = *reinterpret_cast<const T8*>(a + tix_s32<RA>(16 * RI + li, 32 * kk + 8 * lq));
+      bv[kk] = *reinterpret_cast<const T8*>(b + tix_s32<RB>(16 * RJ + li, 32 * kk + 8 * lq));
     }
-    const int sc = 16 * J + li;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < kG; ++kk) acc = mma16(av[kk], bv[kk], acc);
+    return acc;
+  };
+  // stores of a tile's accumulator: lane holds column 16 J + li, rows 16 I + 4 lq + e
+  auto store_a = [&](int I, int J, const f32x4& acc) {
+    const int sc = 16 * J + li;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * I + 4 * lq + e;
-      if (is_qk) s.p[r][sc] = (f16)(sc <= r ? acc[e] : 0.f);
-      else s.a[r][sc] = sc < r ? s.beta[r] * acc[e] : 0.f;
+      s.a[r][sc] = sc < r ? s.beta[r] * acc[e] : 0.f;
+    }
+  };
+  auto store_p = [&](int I, int J, const f32x4& acc) {
+    const int sc = 16 * J + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + 4 * lq + e;
+      s.p[r][sc] = (f16)(sc <= r ? acc[e] : 0.f);
+    }
+  };
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  constexpr auto R16 = std::integral_constant<int, 16>{};
+  constexpr auto R32 = std::integral_constant<int, 32>{};
+  constexpr auto R64 = std::integral_constant<int, kC>{};
+
+  // ---- off-diagonal tiles, reference = first row of the row block (fp16 operands).
+  // Column operands: this thread's tokens (block blk) for every row block I > blk.
+#pragma unroll
+  for (int i = 0; i < kTP; ++i) {
+    const int t = part * kTP + i;
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+      if (I <= blk) continue;
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = gs[I][j] - gam[i][j];
+      const int c = I * (I - 1) / 2 + blk;
+      *reinterpret_cast<u32x4*>(&s.col[c * SM::kBlk + tix_s32<16>(t - 16 * blk, 8 * o)]) =
+          scaled(kf0[i], kf1[i], e, f16{});
     }
   }
+  // phase 1a: K rows; Gram tiles (I, J < I)
+  auto rows_off = [&](const f32x4* x0, const f32x4* x1) {
+#pragma unroll
+    for (int i = 0; i < kTP; ++i) {
+      const int t = part * kTP + i;
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = gam[i][j] - gs[blk][j];
+      *reinterpret_cast<u32x4*>(&s.row[pix(t, 8 * o)]) = scaled(x0[i], x1[i], e, f16{});
+    }
+  };
+  rows_off(kf0, kf1);
+  __syncthreads();
+  // six tiles (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); waves 0, 1 take two, waves 2, 3 one
+  for (int jb = wave; jb < 6; jb += 4) {
+    const int I = jb < 1 ? 1 : (jb < 3 ? 2 : 3), J = jb - I * (I - 1) / 2;
+    const f32x4 acc = tile(R64, s.row, I, R16, s.col + (I * (I - 1) / 2 + J) * SM::kBlk, 0, f16{}, zero);
+    store_a(I, J, acc);
+  }
+  __syncthreads();
+  // phase 1b: Q rows; Q K^T tiles (I, J < I)
+  rows_off(qf0, qf1);
+  __syncthreads();
+  for (int jb = wave; jb < 6; jb += 4) {
+    const int I = jb < 1 ? 1 : (jb < 3 ? 2 : 3), J = jb - I * (I - 1) / 2;
+    const f32x4 acc = tile(R64, s.row, I, R16, s.col + (I * (I - 1) / 2 + J) * SM::kBlk, 0, f16{}, zero);
+    store_p(I, J, acc);
+  }
+  // ---- diagonal tiles, reference = middle row of the block (bf16 operands), two blocks per
+  // phase: waves 0, 1 the Gram tiles, waves 2, 3 the Q K^T tiles (split operands)
+#pragma unroll
+  for (int ph = 0; ph < 2; ++ph) {
+    __syncthreads();  // the previous phase's operand reads are done
+    if ((blk >> 1) == ph) {
+#pragma unroll
+      for (int i = 0; i < kTP; ++i) {
+        const int t = part * kTP + i, rr = t - 32 * ph;
+        float eu[8], ed[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          eu[j] = gam[i][j] - gmid[blk][j];
+          ed[j] = -eu[j];
+        }
+        const int ix = tix_s32<32>(rr, 8 * o);
+        u32x4 hi, lo;
+        split(qf0[i], qf1[i], eu, hi, lo);
+        *reinterpret_cast<u32x4*>(&s.dqh[ix]) = hi;
+        *reinterpret_cast<u32x4*>(&s.dql[ix]) = lo;
+        *reinterpret_cast<u32x4*>(&s.dk[ix]) = scaled(kf0[i], kf1[i], eu, bf16{});
+        split(kf0[i], kf1[i], ed, hi, lo);
+        *reinterpret_cast<u32x4*>(&s.dch[ix]) = hi;
+        *reinterpret_cast<u32x4*>(&s.dcl[ix]) = lo;
+      }
+    }
+    __syncthreads();
+    const int u = wave & 1, I = 2 * ph + u;
+    if (wave < 2) {
+      store_a(I, I, tile(R32, s.dk, u, R32, s.dch, u, bf16{}, zero));
+    } else {
+      f32x4 acc = tile(R32, s.dqh, u, R32, s.dch, u, bf16{}, zero);
+      acc = tile(R32, s.dqh, u, R32, s.dcl, u, bf16{}, acc);
+      acc = tile(R32, s.dql, u, R32, s.dch, u, bf16{}, acc);
+      store_p(I, I, acc);
+    }
+  }
+  if (tid < kC) vec[SL::kBeta + tid] = s.beta[tid];
   __syncthreads();  // the operand tiles are dead from here: x and tm reuse their space
   // strict upper 16x16 tiles of Tm stay zero
   for (int e = tid; e < 6 * 256; e += kThreads) {

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void transition_kernel(const TI* __restrict__ 
     }
     if (tid < 2 * kC && (tid % kC) < n) {
       const long row = ((long)b * T + t0 + tid % kC) * H + h;
-      sp = tid < kC ? beta[row] : (g ? g[row] : 0.f);
+      sp = tid < kC ? beta[row] : (g ? floor_gate(g[row]) : 0.f);
     }
   };
   load_chunk(0);
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void transition_kernel(const TI* __restrict__ 
         const int e = tid + 256 * i, t = e / (K / 4), d = (e % (K / 4)) * 4;
         if (t < n)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) as[t][d + j] = __expf(gp[i][j] + gs[t]);
+          for (int j = 0; j < 4; ++j) as[t][d + j] = __expf(floor_key_gate(gp[i][j] + gs[t]));
       }
     }
     __syncthreads();

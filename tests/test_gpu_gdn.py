@@ -160,10 +160,58 @@ def test_per_key_gate_only():
     _run_and_check(inp, label="gk only")
 
 
+@pytest.mark.parametrize("K,V,T,gk_shift,saves", [
+    (128, 128, 200, 0.0, True), (128, 128, 200, -2.0, False), (64, 128, 131, -2.0, True),
+    (64, 64, 77, 0.0, False), (128, 64, 256, -2.0, True)])
+def test_per_key_strong_decay(K, V, T, gk_shift, saves):
+    """Per-key gates that forget fast: gk = logsigmoid(N(0,1) + shift) with shift 0 (alpha
+    about 0.5 per token) and -2 (about 0.12), so that a key's decay over half a chunk reaches
+    e^-30 to e^-70, with and without saved h / v_new."""
+    inp = workloads.gdn_inputs(2, T, 3, K, V, dtype="bf16", seed=T + K + 7, g_shift=3.0,
+                               per_key=True, gk_shift=gk_shift)
+    h0 = torch.randn(2, 3, K, V, generator=torch.Generator().manual_seed(4)) * 0.3
+    _run_and_check(inp, scale=0.8, h0=h0, want_h=saves, want_vnew=saves,
+                   label="per-key strong decay K%d V%d T%d shift %g" % (K, V, T, gk_shift))
+
+
+@pytest.mark.parametrize("K,saves", [(128, True), (128, False), (64, True)])
+def test_per_key_reset(K, saves):
+    """Per-key resets inside chunks: gk = -30 for every key at token 100, -inf for half the
+    keys at token 150 and a run of -12 over tokens 200..215 (the kernels floor a token's
+    per-key log decay at -10, which keeps at most e^-10 of the state it erases)."""
+    T = 260
+    inp = workloads.gdn_inputs(1, T, 2, K, 128, dtype="bf16", seed=21 + K, per_key=True,
+                               gk_shift=1.0)
+    inp["gk"][0, 100] = -30.0
+    inp["gk"][0, 150, :, : K // 2] = float("-inf")
+    inp["gk"][0, 200:216] = -12.0
+    _run_and_check(inp, want_h=saves, want_vnew=saves, label="per-key reset K%d" % K)
+
+
+@pytest.mark.parametrize("path", ["single", "two_kernel"])
+def test_hard_reset_scalar_gate(path):
+    """g = -inf (alpha = 0) at tokens 5, 64, 130 and 131: the state is erased there, so the
+    output at such a token is scale * beta (q . k) v (the reset pin), and every output matches
+    the oracle.  Both the single-kernel path and the two-kernel path (saves requested)."""
+    g = _gpu()
+    T, scale = 200, 0.5
+    inp = workloads.gdn_inputs(1, T, 2, 128, 128, dtype="bf16", seed=33, g_shift=2.0)
+    for t in (5, 64, 130, 131):
+        inp["g"][0, t] = float("-inf")
+    saves = path == "two_kernel"
+    out = _run_and_check(inp, scale=scale, want_h=saves, want_vnew=saves,
+                         label="hard reset %s" % path)
+    q, k, v = (inp[n][0].double() for n in ("q", "k", "v"))
+    for t in (5, 64, 130, 131):
+        want = scale * inp["beta"][0, t].double()[:, None] * (q[t] * k[t]).sum(-1)[:, None] * v[t]
+        assert_close("o[%d]" % t, out["o"][0, t], want.numpy(), TOL[torch.bfloat16])
+
+
 def test_long_perkey_workload_sampled():
     """B=2 H=32 T=32768 K=V=128 bf16 with per-key gate, saving h [B,H,T/64,K,V] and v_new
-    (the long-context workload), run whole on the GPU; four (b, h) chains are compared with
-    the oracle element by element (o, ht, every saved h and v_new of those chains)."""
+    (the long-context workload), run whole on the GPU: every output of all 64 chains is
+    finite, and sixteen (b, h) chains (both batch rows, heads spread over 0..31) are compared
+    with the oracle element by element (o, ht, every saved h and v_new of those chains)."""
     g = _gpu()
     inp = workloads.make("long_perkey_b2h32t32768")
     say("long per-key workload generated")
@@ -171,7 +219,9 @@ def test_long_perkey_workload_sampled():
     out = g.gdn_fwd(d["q"], d["k"], d["v"], d["beta"], g=d["g"], gk=d["gk"], want_h=True,
                     want_v_new=True)
     torch.cuda.synchronize()
-    picks = [(0, 0), (0, 17), (1, 5), (1, 31)]
+    for name in ("o", "ht", "h", "v_new"):
+        assert bool(torch.isfinite(out[name]).all()), "%s has non-finite values" % name
+    picks = [(b, h) for b in range(2) for h in range(b, 32, 4)]
     sub = {}
     for name in ("q", "k", "v", "beta", "g", "gk"):
         sub[name] = torch.stack([inp[name][b, :, h] for b, h in picks], dim=1).unsqueeze(0)

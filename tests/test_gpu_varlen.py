@@ -80,3 +80,19 @@ def test_varlen_workload_full():
     """8 sequences with lengths uniform in [512, 8192], H=16, K=V=128, bf16: every element."""
     inp = workloads.make("varlen_bf16_8seq")
     _run(inp, want_h=False, label="varlen_bf16_8seq")
+
+
+@pytest.mark.parametrize("want_h", [True, False])
+def test_packed_per_key_strong_decay(want_h):
+    """Packed sequences with a fast-forgetting per-key gate (gk = logsigmoid(N(0,1) - 2)) and a
+    per-key reset (gk = -30) inside a chunk, with and without saves."""
+    lengths = [70, 1, 200, 64, 33]
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths), 0)
+    T = int(cu[-1])
+    inp = workloads.gdn_inputs(1, T, 2, 128, 128, dtype="bf16", seed=41, g_shift=3.0,
+                               per_key=True, gk_shift=-2.0)
+    inp["gk"][0, 150] = -30.0
+    inp["cu_seqlens"] = cu
+    h0 = torch.randn(len(lengths), 2, 128, 128, generator=torch.Generator().manual_seed(5)) * 0.3
+    _run(inp, h0=h0, want_h=want_h, label="packed per-key strong decay saves %s" % want_h)
