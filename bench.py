@@ -289,10 +289,12 @@ def main():
         config = {"workload": args.workload, "T_total": T, "N": N, "H": H, "K": K, "V": V,
                   "lengths": (cu[1:] - cu[:-1]).tolist(), "chunk": 64, "state": "fp32"}
 
+        cu_host = cu.to(torch.int32).contiguous()  # the host copy, made once
+
         def step(i):
             s = sets[i % len(sets)]
             return gdn.gdn_fwd_varlen(s["q"], s["k"], s["v"], s["beta"], s["cu_seqlens"],
-                                      g=s["g"], want_tables=False)
+                                      g=s["g"], want_tables=False, cu_seqlens_host=cu_host)
     elif kind == "summary":
         B, T, H, K = inp["q"].shape
         V = inp["v"].shape[-1]

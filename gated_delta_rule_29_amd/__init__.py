@@ -41,6 +41,31 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _fwd_flags(gk, want_h, want_v_new):
+    return ((_lib.FWD_PER_KEY if gk is not None else 0)
+            | (_lib.FWD_SAVES if (want_h or want_v_new) else 0))
+
+
+def _cu_pair(cu_seqlens, cu_seqlens_host, dev):
+    """(device, host) int32 copies of the packed offsets.  A host copy given by the caller is
+    used as is, so a device cu_seqlens plus its host copy costs no transfer; otherwise the
+    missing side is copied (device to host waits for the device)."""
+    if cu_seqlens_host is not None:
+        cu_host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+        if cu_host.device.type != "cpu":
+            raise ValueError("cu_seqlens_host must be a host tensor")
+    else:
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device == dev and \
+            cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous():
+        cu_dev = cu_seqlens
+    else:
+        cu_dev = torch.as_tensor(cu_seqlens, dtype=torch.int32).to(dev).contiguous()
+    if cu_dev.numel() != cu_host.numel():
+        raise ValueError("cu_seqlens and cu_seqlens_host differ in length")
+    return cu_dev, cu_host
+
+
 def _need(t, name, shape, dtype, device):
     if t is None:
         return
@@ -80,7 +105,7 @@ def gdn_fwd(q, k, v, beta, g=None, gk=None, scale=1.0, h0=None, *, want_ht=True,
     hch = torch.empty(B, H, NT, K, V, dtype=dt, device=dev) if want_h else None
     vn = torch.empty(B, T, H, V, dtype=dt, device=dev) if want_v_new else None
     lib = _lib.load()
-    ws_n = lib.gdn_fwd_workspace_bytes(B, T, H, K, V, _DT[dt], int(gk is not None))
+    ws_n = lib.gdn_fwd_workspace_bytes(B, T, H, K, V, _DT[dt], _fwd_flags(gk, want_h, want_v_new))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     rc = lib.gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta), float(scale),
                      _ptr(h0), _ptr(o), _ptr(ht), _ptr(hch), _ptr(vn), B, T, H, K, V, _DT[dt],
@@ -113,7 +138,7 @@ def gdn_state_summary(k, v, beta, g=None, gk=None, *, want_transition=True):
     st = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
     tr = torch.empty(B, H, K, K, dtype=torch.float32, device=dev) if want_transition else None
     lib = _lib.load()
-    ws_n = lib.gdn_state_summary_workspace_bytes(B, T, H, K, V, _DT[dt], int(gk is not None))
+    ws_n = lib.gdn_state_summary_workspace_bytes(B, T, H, K, V, _DT[dt], _fwd_flags(gk, False, False))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     rc = lib.gdn_state_summary(_ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta), _ptr(st),
                                _ptr(tr), B, T, H, K, V, _DT[dt], _ptr(ws), ws_n, _stream(dev))
@@ -144,10 +169,13 @@ def gdn_varlen_num_chunks(cu_seqlens_host) -> int:
 
 
 def gdn_fwd_varlen(q, k, v, beta, cu_seqlens, g=None, gk=None, scale=1.0, h0=None, *,
-                   want_ht=True, want_h=False, want_v_new=False, want_tables=True):
-    """Packed forward (batch 1).  cu_seqlens [N+1] int32 (a device copy is made if it is a
-    host tensor).  Returns o, and ht [N,H,K,V], h [1,H,NT_total,K,V], v_new,
-    chunk_offsets [N+1] and chunk_indices [NT_total,2] (int32) when requested."""
+                   want_ht=True, want_h=False, want_v_new=False, want_tables=True,
+                   cu_seqlens_host=None):
+    """Packed forward (batch 1).  cu_seqlens [N+1] int32 on the device (a device copy is made
+    if it is a host tensor); cu_seqlens_host: its host copy, which the library validates and
+    sizes the call from (made from cu_seqlens, with a device wait, when not given).  Returns
+    o, and ht [N,H,K,V], h [1,H,NT_total,K,V], v_new, chunk_offsets [N+1] and
+    chunk_indices [NT_total,2] (int32) when requested."""
     if q.dtype not in _DT:
         raise ValueError("q must be float32 or bfloat16, got %s" % q.dtype)
     one, T, H, K = q.shape
@@ -155,8 +183,7 @@ def gdn_fwd_varlen(q, k, v, beta, cu_seqlens, g=None, gk=None, scale=1.0, h0=Non
         raise ValueError("packed input must have batch 1, got %d" % one)
     V = v.shape[-1]
     dev, dt = q.device, q.dtype
-    cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
-    cu_dev = cu_seqlens.detach().to(dev, torch.int32).contiguous()
+    cu_dev, cu_host = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
     N = cu_host.numel() - 1
     _need(q, "q", (1, T, H, K), dt, dev)
     _need(k, "k", (1, T, H, K), dt, dev)
@@ -175,7 +202,8 @@ def gdn_fwd_varlen(q, k, v, beta, cu_seqlens, g=None, gk=None, scale=1.0, h0=Non
     vn = torch.empty(1, T, H, V, dtype=dt, device=dev) if want_v_new else None
     offs = torch.empty(N + 1, dtype=torch.int32, device=dev) if want_tables else None
     idx = torch.empty(NT, 2, dtype=torch.int32, device=dev) if want_tables else None
-    ws_n = lib.gdn_fwd_varlen_workspace_bytes(T, N, H, K, V, _DT[dt], int(gk is not None))
+    ws_n = lib.gdn_fwd_varlen_workspace_bytes(T, N, NT, H, K, V, _DT[dt],
+                                              _fwd_flags(gk, want_h, want_v_new))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     rc = lib.gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
                             float(scale), _ptr(cu_dev), _ptr(cu_host), N, _ptr(h0), _ptr(o),

@@ -13,9 +13,11 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 DTYPE_F32, DTYPE_BF16 = 0, 1
+FWD_PER_KEY, FWD_SAVES = 1, 2
 
 P = ctypes.c_void_p
 I = ctypes.c_int
+U = ctypes.c_uint
 F = ctypes.c_float
 SZ = ctypes.c_size_t
 
@@ -23,14 +25,14 @@ SZ = ctypes.c_size_t
 SIGNATURES = {
     "gdn_abi_version": (I, []),
     "gdn_last_error": (ctypes.c_char_p, []),
-    "gdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I, I, I]),
+    "gdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I, I, U]),
     "gdn_fwd": (I, [P, P, P, P, P, P, F, P, P, P, P, P, I, I, I, I, I, I, P, SZ, P]),
     "gdn_varlen_num_chunks": (I, [P, I]),
-    "gdn_fwd_varlen_workspace_bytes": (SZ, [I, I, I, I, I, I, I]),
+    "gdn_fwd_varlen_workspace_bytes": (SZ, [I, I, I, I, I, I, I, U]),
     "gdn_fwd_varlen": (I, [P, P, P, P, P, P, F, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, P,
                            SZ, P]),
     "gdn_prep": (I, [P, P, P, P, P, F, F, P, P, P, P, P, P, P, I, I, I, I, P]),
-    "gdn_state_summary_workspace_bytes": (SZ, [I, I, I, I, I, I, I]),
+    "gdn_state_summary_workspace_bytes": (SZ, [I, I, I, I, I, I, U]),
     "gdn_state_summary": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, P, SZ, P]),
     "gdn_state_apply": (I, [P, P, P, P, I, I, I, P]),
     "bigdn_fwd_workspace_bytes": (SZ, [I, I, I, I, I]),

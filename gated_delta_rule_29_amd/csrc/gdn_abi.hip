@@ -65,6 +65,25 @@ int check_row_span(int64_t tokens, int H, int K, int V, int dtype) {
   return GDN_OK;
 }
 
+// Flags implied by a forward call's arguments (what its workspace must be sized for).
+unsigned fwd_flags(const float* gk, const void* h_chunks, const void* v_new) {
+  return (gk ? GDN_FWD_PER_KEY : 0u) | ((h_chunks || v_new) ? GDN_FWD_SAVES : 0u);
+}
+
+// bf16 with a scalar gate and nothing saved per chunk runs the single fused kernel, which
+// keeps every per-chunk term on chip (its only scratch is the rank table of a packed batch).
+bool fused_path(int dtype, unsigned flags) {
+  return dtype == GDN_DTYPE_BF16 && !(flags & (GDN_FWD_PER_KEY | GDN_FWD_SAVES));
+}
+
+int check_workspace(const void* ws, size_t bytes, size_t need) {
+  if (need == 0) return GDN_OK;
+  if (!ws || bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws ? bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,10 +92,11 @@ int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 const char* gdn_last_error(void) { return g_err; }
 
-size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype, int per_key) {
-  if (B <= 0 || T <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key != 0)) return 0;
+size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype, unsigned flags) {
+  const bool per_key = flags & GDN_FWD_PER_KEY;
+  if (B <= 0 || T <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key)) return 0;
   return gdn::fwd_workspace_bytes((long)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK), 0, dtype, K,
-                                  per_key != 0);
+                                  per_key, fused_path(dtype, flags));
 }
 
 int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* gk,
@@ -92,11 +112,9 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   if (wgs > INT32_MAX || nslots > INT32_MAX)
     return fail(GDN_ERR_INVALID, "B*H*(V/32) = %lld or B*H*chunks = %lld exceeds the grid limit",
                 (long long)wgs, (long long)nslots);
-  const size_t need = gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, gk != nullptr);
-  if (!workspace || workspace_bytes < need)
-    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256)
-    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  const size_t need = gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, fwd_flags(gk, h_chunks, v_new));
+  rc = check_workspace(workspace, workspace_bytes, need);
+  if (rc) return rc;
   gdn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.g = g; p.gk = gk; p.beta = beta; p.h0 = h0;
   p.o = o; p.ht = ht; p.h_chunks = h_chunks; p.v_new = v_new; p.cu = nullptr;
@@ -124,7 +142,7 @@ SummaryWs summary_ws(int B, int T, int H, int K, int V, int dtype, bool per_key)
   const size_t es = dtype == GDN_DTYPE_BF16 ? 2 : 4, tok = (size_t)B * T * H;
   size_t off = 0;
   w.fwd = off;
-  off = al256s(off + gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, per_key));
+  off = al256s(off + gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, per_key ? GDN_FWD_PER_KEY : 0u));
   w.o = off;
   off = al256s(off + tok * (size_t)V * es);
   w.total = off;
@@ -135,9 +153,10 @@ SummaryWs summary_ws(int B, int T, int H, int K, int V, int dtype, bool per_key)
 
 extern "C" {
 
-size_t gdn_state_summary_workspace_bytes(int B, int T, int H, int K, int V, int dtype, int per_key) {
-  if (B <= 0 || T <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key != 0)) return 0;
-  return summary_ws(B, T, H, K, V, dtype, per_key != 0).total;
+size_t gdn_state_summary_workspace_bytes(int B, int T, int H, int K, int V, int dtype, unsigned flags) {
+  const bool per_key = flags & GDN_FWD_PER_KEY;
+  if (B <= 0 || T <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key)) return 0;
+  return summary_ws(B, T, H, K, V, dtype, per_key).total;
 }
 
 int gdn_state_summary(const void* k, const void* v, const float* g, const float* gk,
@@ -201,20 +220,26 @@ int gdn_varlen_num_chunks(const int* cu, int N) {
   return total > INT32_MAX ? -1 : (int)total;
 }
 
-size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype,
-                                      int per_key) {
-  if (T_total <= 0 || N <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key != 0)) return 0;
+size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int NT_total, int H, int K, int V,
+                                      int dtype, unsigned flags) {
+  const bool per_key = flags & GDN_FWD_PER_KEY;
+  if (T_total <= 0 || N <= 0 || H <= 0 || !kv_supported(dtype, K, V, per_key)) return 0;
   // chunks <= T_total / 64 + N (each sequence adds at most one partial chunk)
-  const long nt_max = (long)T_total / GDN_CHUNK + N;
-  return gdn::fwd_workspace_bytes((long)H * nt_max, N, dtype, K, per_key != 0);
+  const long nt = NT_total > 0 ? (long)NT_total : (long)T_total / GDN_CHUNK + N;
+  return gdn::fwd_workspace_bytes((long)H * nt, N, dtype, K, per_key, fused_path(dtype, flags));
 }
 
-int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
-                   const float* gk, const float* beta, float scale, const int* cu_seqlens,
-                   const int* cu_seqlens_host, int N, const float* h0, void* o, float* ht,
-                   void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
-                   int T_total, int H, int K, int V, int dtype, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_fwd_varlen with its scratch given: validation, then the launches.
+int fwd_varlen_impl(const void* q, const void* k, const void* v, const float* g,
+                    const float* gk, const float* beta, float scale, const int* cu_seqlens,
+                    const int* cu_seqlens_host, int N, const float* h0, void* o, float* ht,
+                    void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
+                    int T_total, int H, int K, int V, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   int rc = check_fwd_common(q, k, v, beta, o, gk, H, K, V, dtype);
   if (rc) return rc;
   if (!cu_seqlens || !cu_seqlens_host)
@@ -233,11 +258,10 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
   const int64_t wgs = (int64_t)N * H * (V / 32);
   if (wgs > INT32_MAX || (int64_t)H * nt > INT32_MAX)
     return fail(GDN_ERR_INVALID, "N*H*(V/32) or H*chunks exceeds the grid limit");
-  const size_t need = gdn::fwd_workspace_bytes((long)H * nt, N, dtype, K, gk != nullptr);
-  if (!workspace || workspace_bytes < need)
-    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256)
-    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  const unsigned flags = fwd_flags(gk, h_chunks, v_new);
+  const size_t need = gdn_fwd_varlen_workspace_bytes(T_total, N, nt, H, K, V, dtype, flags);
+  rc = check_workspace(workspace, workspace_bytes, need);
+  if (rc) return rc;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (chunk_offsets || chunk_indices) {
     hipError_t e = gdn::launch_varlen_tables(cu_seqlens, N, chunk_offsets, chunk_indices, s);
@@ -248,10 +272,29 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
   p.o = o; p.ht = ht; p.h_chunks = h_chunks; p.v_new = v_new; p.cu = cu_seqlens;
   p.scale = scale; p.B = 1; p.T = T_total; p.H = H; p.V = V; p.nvb = V / 64;
   p.nseq = N; p.nt_total = nt; p.ws = workspace;
-  p.coffs = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)H * nt * gdn::fwd_slot_bytes(dtype, K, gk != nullptr));
+  p.coffs = fused_path(dtype, flags)
+                ? nullptr
+                : reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                         (size_t)H * nt * gdn::fwd_slot_bytes(dtype, K, gk != nullptr));
   hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, true, s);
   if (e != hipSuccess) return hip_fail(e, "gdn_fwd_varlen launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                   const float* gk, const float* beta, float scale, const int* cu_seqlens,
+                   const int* cu_seqlens_host, int N, const float* h0, void* o, float* ht,
+                   void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
+                   int T_total, int H, int K, int V, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return fwd_varlen_impl(q, k, v, g, gk, beta, scale, cu_seqlens,
+                         cu_seqlens_host, N, h0, o, ht, h_chunks, v_new, chunk_offsets,
+                         chunk_indices, T_total, H, K, V, dtype, workspace, workspace_bytes,
+                         stream);
 }
 
 }  // extern "C"

@@ -772,7 +772,10 @@ size_t fwd_slot_bytes(int dtype, int K, bool pk) {
   return pk ? chunk::Slot16<64, true>::kBytes : chunk::Slot16<64, false>::kBytes;
 }
 
-size_t fwd_workspace_bytes(long nslots, int nseq, int dtype, int K, bool pk) {
+size_t fwd_workspace_bytes(long nslots, int nseq, int dtype, int K, bool pk, bool fused) {
+  // the single fused kernel keeps every per-chunk term on chip; a packed batch needs its
+  // sequence rank table (nseq ints)
+  if (fused) return nseq > 0 ? (((size_t)nseq * sizeof(int) + 255) & ~(size_t)255) : 0;
   size_t b = (size_t)nslots * fwd_slot_bytes(dtype, K, pk);
   if (nseq > 0) b += ((size_t)(nseq + 1) * sizeof(int) + 255) & ~(size_t)255;
   return b;

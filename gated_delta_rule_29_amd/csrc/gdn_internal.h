@@ -29,8 +29,9 @@ struct FwdParams {
 };
 
 // Workspace of a forward call with `nslots` chunk slots (B*H*NT dense, H*NT_total packed)
-// and, for packed batches, nseq + 1 chunk offsets.
-size_t fwd_workspace_bytes(long nslots, int nseq, int dtype, int K, bool per_key);
+// and, for packed batches, nseq + 1 chunk offsets; `fused`: the single-kernel path, whose
+// only scratch is the rank table of a packed batch (nseq ints).
+size_t fwd_workspace_bytes(long nslots, int nseq, int dtype, int K, bool per_key, bool fused);
 size_t fwd_slot_bytes(int dtype, int K, bool per_key);
 
 hipError_t launch_gdn_fwd(const FwdParams& p, int dtype, int K, bool varlen, hipStream_t stream);

@@ -54,7 +54,7 @@ extern "C" {
 #define GDN_API
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 #define GDN_CHUNK 64
 
 /* Status codes (the pages' wrappers raise ValueError / NotImplementedError / RuntimeError
@@ -67,6 +67,10 @@ extern "C" {
 
 #define GDN_DTYPE_F32 0
 #define GDN_DTYPE_BF16 1
+
+/* Flags of the forward workspace queries: what the call they size will ask for. */
+#define GDN_FWD_PER_KEY 1u /* gk is given                                */
+#define GDN_FWD_SAVES 2u   /* h_chunks or v_new is requested             */
 
 /* ABI version (GDN_ABI_VERSION) of the loaded library. */
 GDN_API int gdn_abi_version(void);
@@ -97,18 +101,20 @@ GDN_API const char* gdn_last_error(void);
  *                                      v_new = u - w h of the state pass; NULL = not written
  *   workspace, workspace_bytes          caller-owned device scratch, 256-byte aligned, of at
  *                                      least gdn_fwd_workspace_bytes(B, T, H, K, V, dtype,
- *                                      gk != NULL) bytes.  The call fills it with per-chunk
- *                                      terms (WY inverse, masked Q K^T, decays) and reads them
- *                                      back; it is free again once the call's work on
- *                                      `stream` has completed.  Too small or NULL:
- *                                      GDN_ERR_WORKSPACE.
+ *                                      flags) bytes, flags = GDN_FWD_PER_KEY if gk is given |
+ *                                      GDN_FWD_SAVES if h_chunks or v_new is.  The call fills
+ *                                      it with per-chunk terms (WY inverse, masked Q K^T,
+ *                                      decays) and reads them back; it is free again once the
+ *                                      call's work on `stream` has completed.  Smaller than
+ *                                      that, or NULL when that is not 0: GDN_ERR_WORKSPACE.
+ *                                      A bf16 call with neither flag needs none (0 bytes).
  * Supported: K in {64, 128}, V in {64, 128} for bf16; K = 64 and V in {64, 128} for fp32
  * (gk is bf16 only).  B, T, H >= 1 and B*H*(V/32) <= 2^31 - 1 (else GDN_ERR_INVALID); bf16
  * also needs T*H*max(K, V)*2 < 2^32, the byte span of one head's rows (else
  * GDN_ERR_UNSUPPORTED).  The size query returns 0 for arguments it cannot size.
  */
 GDN_API size_t gdn_fwd_workspace_bytes(int B, int T, int H, int K, int V, int dtype,
-                                       int per_key);
+                                       unsigned flags);
 GDN_API int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* gk,
             const float* beta, float scale, const float* h0, void* o, float* ht, void* h_chunks,
             void* v_new, int B, int T, int H, int K, int V, int dtype, void* workspace,
@@ -125,9 +131,11 @@ GDN_API int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
  */
 GDN_API int gdn_varlen_num_chunks(const int* cu_seqlens_host, int N);
 
-/* Workspace bound for any packing of T_total tokens into N sequences (per_key: gk given). */
-GDN_API size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int H, int K, int V, int dtype,
-                                              int per_key);
+/* Workspace of a packed call with N sequences, T_total tokens and NT_total chunks
+ * (gdn_varlen_num_chunks); NT_total <= 0 gives a bound for any packing (T_total / 64 + N
+ * chunks).  flags as for gdn_fwd_workspace_bytes. */
+GDN_API size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int NT_total, int H, int K,
+                                              int V, int dtype, unsigned flags);
 
 /*
  *   cu_seqlens       [N+1] int32 device   offsets, cu[0] = 0, strictly increasing,
@@ -182,12 +190,13 @@ GDN_API int gdn_prep(const void* qkv, const float* q_norm_w, const float* k_norm
  *   from the forward kernels; the transition from an fp32 kernel that keeps a power-of-two
  *   exponent per column (it decays like the product of all the fragment's decays, so values
  *   below fp32 range become zero, as they would in any fp32 result).
- *   workspace  at least gdn_state_summary_workspace_bytes(B, T, H, K, V, dtype, gk != NULL)
+ *   workspace  at least gdn_state_summary_workspace_bytes(B, T, H, K, V, dtype, flags)
+ *              (flags = GDN_FWD_PER_KEY if gk is given)
  *              bytes, 256-byte aligned, caller-owned
  * Supported and errors: as gdn_fwd.
  */
 GDN_API size_t gdn_state_summary_workspace_bytes(int B, int T, int H, int K, int V, int dtype,
-                                                 int per_key);
+                                                 unsigned flags);
 GDN_API int gdn_state_summary(const void* k, const void* v, const float* g, const float* gk,
                               const float* beta, float* state_ext, float* transition, int B,
                               int T, int H, int K, int V, int dtype, void* workspace,

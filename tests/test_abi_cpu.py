@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, "binding lacks %s" % n
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -62,6 +62,30 @@ def test_fwd_validation_codes():
     assert _fwd(lib, V=96) == L.ERR_UNSUPPORTED
     assert _fwd(lib, dtype=0, K=128) == L.ERR_UNSUPPORTED
     assert _fwd(lib, B=1 << 20, H=1 << 12) == L.ERR_INVALID  # grid too large
+
+
+def test_fwd_workspace_sizes_follow_the_flags():
+    """The single fused kernel (bf16, no per-key gate, nothing saved) needs no workspace for
+    a dense call and only its rank table (4 bytes per sequence, 256-byte rounded) for a packed
+    one; per-key gates, saves and fp32 need per-chunk slots."""
+    L, lib = _lib()
+    PK, SV = L.FWD_PER_KEY, L.FWD_SAVES
+    assert lib.gdn_fwd_workspace_bytes(2, 300, 4, 128, 128, 1, 0) == 0
+    n_pk = lib.gdn_fwd_workspace_bytes(2, 300, 4, 128, 128, 1, PK)
+    n_sv = lib.gdn_fwd_workspace_bytes(2, 300, 4, 128, 128, 1, SV)
+    assert n_pk > n_sv > 0 and n_pk == lib.gdn_fwd_workspace_bytes(2, 300, 4, 128, 128, 1, PK | SV)
+    assert n_sv % (2 * 4 * 5) == 0  # one slot per chunk: B * H * ceil(300 / 64)
+    assert lib.gdn_fwd_workspace_bytes(1, 64, 2, 64, 64, 0, 0) > 0  # fp32: two-kernel path
+    assert lib.gdn_fwd_workspace_bytes(1, 64, 2, 128, 128, 0, 0) == 0  # fp32 K=128 unsupported
+    # packed: exact with NT_total, a bound without it
+    assert lib.gdn_fwd_varlen_workspace_bytes(1000, 3, 17, 4, 128, 128, 1, 0) == 256
+    assert lib.gdn_fwd_varlen_workspace_bytes(1000, 100, 100, 4, 128, 128, 1, 0) == 512
+    exact = lib.gdn_fwd_varlen_workspace_bytes(1000, 3, 17, 4, 128, 128, 1, SV)
+    bound = lib.gdn_fwd_varlen_workspace_bytes(1000, 3, 0, 4, 128, 128, 1, SV)
+    assert 0 < exact < bound
+    # a dense bf16 call on the fused path accepts a NULL workspace; the others do not
+    assert _fwd(lib, ht=FAKE, hch=FAKE) == L.ERR_WORKSPACE
+    assert _fwd(lib, gk=FAKE) == L.ERR_WORKSPACE
 
 
 def test_varlen_num_chunks():
