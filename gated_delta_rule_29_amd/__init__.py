@@ -170,12 +170,14 @@ def gdn_varlen_num_chunks(cu_seqlens_host) -> int:
 
 def gdn_fwd_varlen(q, k, v, beta, cu_seqlens, g=None, gk=None, scale=1.0, h0=None, *,
                    want_ht=True, want_h=False, want_v_new=False, want_tables=True,
-                   cu_seqlens_host=None):
+                   cu_seqlens_host=None, no_alloc=False):
     """Packed forward (batch 1).  cu_seqlens [N+1] int32 on the device (a device copy is made
     if it is a host tensor); cu_seqlens_host: its host copy, which the library validates and
     sizes the call from (made from cu_seqlens, with a device wait, when not given).  Returns
     o, and ht [N,H,K,V], h [1,H,NT_total,K,V], v_new, chunk_offsets [N+1] and
-    chunk_indices [NT_total,2] (int32) when requested."""
+    chunk_indices [NT_total,2] (int32) when requested.  no_alloc: call
+    gdn_fwd_varlen_noalloc, whose scratch is the library's static device array (for callers
+    that cannot allocate; the call allocates nothing but its outputs here)."""
     if q.dtype not in _DT:
         raise ValueError("q must be float32 or bfloat16, got %s" % q.dtype)
     one, T, H, K = q.shape
@@ -202,14 +204,21 @@ def gdn_fwd_varlen(q, k, v, beta, cu_seqlens, g=None, gk=None, scale=1.0, h0=Non
     vn = torch.empty(1, T, H, V, dtype=dt, device=dev) if want_v_new else None
     offs = torch.empty(N + 1, dtype=torch.int32, device=dev) if want_tables else None
     idx = torch.empty(NT, 2, dtype=torch.int32, device=dev) if want_tables else None
-    ws_n = lib.gdn_fwd_varlen_workspace_bytes(T, N, NT, H, K, V, _DT[dt],
-                                              _fwd_flags(gk, want_h, want_v_new))
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
-    rc = lib.gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
-                            float(scale), _ptr(cu_dev), _ptr(cu_host), N, _ptr(h0), _ptr(o),
-                            _ptr(ht), _ptr(hch), _ptr(vn), _ptr(offs), _ptr(idx), T, H, K, V,
-                            _DT[dt], _ptr(ws), ws_n, _stream(dev))
-    _lib.check(rc, "gdn_fwd_varlen")
+    if no_alloc:
+        rc = lib.gdn_fwd_varlen_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
+                                        float(scale), _ptr(cu_dev), _ptr(cu_host), N, _ptr(h0),
+                                        _ptr(o), _ptr(ht), _ptr(hch), _ptr(vn), _ptr(offs),
+                                        _ptr(idx), T, H, K, V, _DT[dt], _stream(dev))
+        _lib.check(rc, "gdn_fwd_varlen_noalloc")
+    else:
+        ws_n = lib.gdn_fwd_varlen_workspace_bytes(T, N, NT, H, K, V, _DT[dt],
+                                                  _fwd_flags(gk, want_h, want_v_new))
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+        rc = lib.gdn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
+                                float(scale), _ptr(cu_dev), _ptr(cu_host), N, _ptr(h0), _ptr(o),
+                                _ptr(ht), _ptr(hch), _ptr(vn), _ptr(offs), _ptr(idx), T, H, K,
+                                V, _DT[dt], _ptr(ws), ws_n, _stream(dev))
+        _lib.check(rc, "gdn_fwd_varlen")
     out = {"o": o}
     if want_ht:
         out["ht"] = ht

@@ -31,6 +31,8 @@ SIGNATURES = {
     "gdn_fwd_varlen_workspace_bytes": (SZ, [I, I, I, I, I, I, I, U]),
     "gdn_fwd_varlen": (I, [P, P, P, P, P, P, F, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, P,
                            SZ, P]),
+    "gdn_fwd_varlen_noalloc": (I, [P, P, P, P, P, P, F, P, P, I, P, P, P, P, P, P, P, I, I, I, I,
+                                   I, P]),
     "gdn_prep": (I, [P, P, P, P, P, F, F, P, P, P, P, P, P, P, I, I, I, I, P]),
     "gdn_state_summary_workspace_bytes": (SZ, [I, I, I, I, I, I, U]),
     "gdn_state_summary": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, P, SZ, P]),

@@ -10,6 +10,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
 
@@ -233,8 +235,36 @@ size_t gdn_fwd_varlen_workspace_bytes(int T_total, int N, int NT_total, int H, i
 
 namespace {
 
-// gdn_fwd_varlen with its scratch given: validation, then the launches.
-int fwd_varlen_impl(const void* q, const void* k, const void* v, const float* g,
+// Scratch of gdn_fwd_varlen_noalloc: a static device array, one copy per GPU, held until the
+// process ends.  In host code `scratch` only names the symbol; its device address on the
+// current GPU comes from hipGetSymbolAddress, looked up once per device on the first call
+// there (with that device current) and kept in g_scratch_ptr.
+__device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256)
+      return fail(GDN_ERR_HIP, "static scratch has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+// gdn_fwd_varlen with its scratch given (noalloc: the static array instead): validation,
+// then the launches.
+int fwd_varlen_impl(bool noalloc, const void* q, const void* k, const void* v, const float* g,
                     const float* gk, const float* beta, float scale, const int* cu_seqlens,
                     const int* cu_seqlens_host, int N, const float* h0, void* o, float* ht,
                     void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
@@ -260,6 +290,15 @@ int fwd_varlen_impl(const void* q, const void* k, const void* v, const float* g,
     return fail(GDN_ERR_INVALID, "N*H*(V/32) or H*chunks exceeds the grid limit");
   const unsigned flags = fwd_flags(gk, h_chunks, v_new);
   const size_t need = gdn_fwd_varlen_workspace_bytes(T_total, N, nt, H, K, V, dtype, flags);
+  if (noalloc) {
+    if (need > GDN_NOALLOC_SCRATCH_BYTES)
+      return fail(GDN_ERR_WORKSPACE,
+                  "gdn_fwd_varlen_noalloc needs %zu bytes of scratch; the static scratch holds %zu "
+                  "(GDN_NOALLOC_SCRATCH_BYTES)", need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    rc = scratch_of_current_device(&workspace);
+    if (rc) return rc;
+    workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+  }
   rc = check_workspace(workspace, workspace_bytes, need);
   if (rc) return rc;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -291,10 +330,21 @@ int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
                    void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
                    int T_total, int H, int K, int V, int dtype, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  return fwd_varlen_impl(q, k, v, g, gk, beta, scale, cu_seqlens,
+  return fwd_varlen_impl(false, q, k, v, g, gk, beta, scale, cu_seqlens,
                          cu_seqlens_host, N, h0, o, ht, h_chunks, v_new, chunk_offsets,
                          chunk_indices, T_total, H, K, V, dtype, workspace, workspace_bytes,
                          stream);
+}
+
+int gdn_fwd_varlen_noalloc(const void* q, const void* k, const void* v, const float* g,
+                           const float* gk, const float* beta, float scale, const int* cu_seqlens,
+                           const int* cu_seqlens_host, int N, const float* h0, void* o,
+                           float* ht, void* h_chunks, void* v_new, int* chunk_offsets,
+                           int* chunk_indices, int T_total, int H, int K, int V, int dtype,
+                           void* stream) {
+  return fwd_varlen_impl(true, q, k, v, g, gk, beta, scale, cu_seqlens, cu_seqlens_host, N, h0,
+                         o, ht, h_chunks, v_new, chunk_offsets, chunk_indices, T_total, H, K, V,
+                         dtype, nullptr, 0, stream);
 }
 
 }  // extern "C"

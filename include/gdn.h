@@ -13,7 +13,8 @@
  * intra-chunk output.  The result equals the token recurrence up to rounding.
  *
  * Entry points, in the order declared below:
- *  - the forward, dense (gdn_fwd) and packed (gdn_fwd_varlen, gdn_varlen_num_chunks);
+ *  - the forward, dense (gdn_fwd) and packed (gdn_fwd_varlen, gdn_varlen_num_chunks), and the
+ *    packed forward for callers that cannot allocate (gdn_fwd_varlen_noalloc);
  *  - the BiGDN video block of the SANA pages: its front end (gdn_prep), the frame-level scan
  *    in both directions (bigdn_fwd) and the block output with reverse-direction overrides and
  *    the merge (bigdn_fwd_merged);
@@ -25,7 +26,8 @@
  * Conventions shared by every entry point.
  *  - All tensor pointers are DEVICE pointers unless the name ends in _host.  The caller owns
  *    all memory, including any workspace; the library keeps no device allocation between
- *    calls and has no other global mutable state.
+ *    calls and has no other global mutable state, except the static scratch array of
+ *    gdn_fwd_varlen_noalloc (one per GPU, held until the process ends).
  *  - Tensors are dense and row-major in the shapes given (no strides).
  *  - dtype: GDN_DTYPE_F32 (fp32 inputs, fp32 MFMA, fp32 state) or GDN_DTYPE_BF16 (bf16 q/k/v
  *    and bf16 outputs, bf16 MFMA operands, fp32 accumulation and fp32 state).  Gates (g, gk,
@@ -155,6 +157,31 @@ GDN_API int gdn_fwd_varlen(const void* q, const void* k, const void* v, const fl
                    void* h_chunks, void* v_new, int* chunk_offsets, int* chunk_indices,
                    int T_total, int H, int K, int V, int dtype, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_fwd_varlen_noalloc -- gdn_fwd_varlen for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * arguments are those of gdn_fwd_varlen without the workspace: the call's scratch (the
+ * sequence rank table of the single-kernel path; the per-chunk slots and chunk offsets of the
+ * two-kernel path) lives in a static device array of GDN_NOALLOC_SCRATCH_BYTES per GPU, which
+ * the library holds until the process ends.  The call itself allocates nothing.
+ *   - A call whose scratch (gdn_fwd_varlen_workspace_bytes with its own NT_total and flags)
+ *     exceeds GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_WORKSPACE and launches nothing.
+ *     bf16 calls without gk or saves need 4 bytes per sequence; the others about 66 KB
+ *     (74 KB with gk) per chunk and head.
+ *   - Every call on one GPU shares that GPU's array.  Calls that overlap on one GPU (on
+ *     different streams, or from different threads without ordering) race on it; calls
+ *     ordered on one stream do not.  No call relies on the array's previous contents.
+ *   - The first call on a device looks up the array's device address (once per device).
+ * Results are bitwise those of gdn_fwd_varlen.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+GDN_API int gdn_fwd_varlen_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                   const float* gk, const float* beta, float scale,
+                                   const int* cu_seqlens, const int* cu_seqlens_host, int N,
+                                   const float* h0, void* o, float* ht, void* h_chunks,
+                                   void* v_new, int* chunk_offsets, int* chunk_indices,
+                                   int T_total, int H, int K, int V, int dtype, void* stream);
 
 /*
  * gdn_prep -- BiGDN front end (SANA fused_gdn.py page: _fused_qk_inv_rms_kernel,

@@ -270,3 +270,21 @@ def test_dhu_varlen_validation_codes():
     assert call([0, 3, 6, 10], K=64) == L.ERR_UNSUPPORTED
     assert call([0, 3, 6, 10]) == L.ERR_WORKSPACE
     assert lib.gdn_bwd_dhu_varlen_workspace_bytes(3, 3) == 256 + 256
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_launch():
+    """gdn_fwd_varlen_noalloc refuses a call whose scratch would exceed the static array,
+    during validation (no HIP call is made, so this runs without a GPU)."""
+    L, lib = _lib()
+    cu = np.array([0, 2560, 5120, 7680, 10240], np.int32)  # 4 x 40 chunks
+    rc = lib.gdn_fwd_varlen_noalloc(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1.0, FAKE,
+                                    cu.ctypes.data_as(ctypes.c_void_p), 4, None, FAKE, None, None,
+                                    None, None, None, 10240, 4, 128, 128, 1, None)
+    assert rc == L.ERR_WORKSPACE
+    assert "static scratch" in L.last_error()
+    # malformed offsets are still INVALID
+    bad = np.array([0, 5, 5], np.int32)
+    rc = lib.gdn_fwd_varlen_noalloc(FAKE, FAKE, FAKE, None, None, FAKE, 1.0, FAKE,
+                                    bad.ctypes.data_as(ctypes.c_void_p), 2, None, FAKE, None, None,
+                                    None, None, None, 5, 4, 128, 128, 1, None)
+    assert rc == L.ERR_INVALID
