@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       rdv[e] = dV[(tb + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
-    if (p.g && tid < kC) rg = floor_gate(p.g[(tb + tok(t0 + tid)) * p.H + h]);
+    if (p.g && tid < kC) rg = p.g[(tb + tok(t0 + tid)) * p.H + h];
   };
   // dv2 of chunk m from its LDS tile: wave (wr, wc) stores the 16 x 16 block it writes
   auto store_dv2 = [&](int m) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void dhu_kernel(const DhuParams p) {
     const int t0 = n * kC;
     // chunk-local inclusive cumsum of the gate (wave 0), padded tokens add 0
     if (wave == 0) {
-      float x = t0 + lane < T ? rg : 0.f;
+      float x = t0 + lane < T ? floor_gate(rg) : 0.f;  // floored at use: rg is a prefetch
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
   // next chunk's inputs (unconditional loads from clamped tokens; see dhu_kernel)
   uint4 rk[kItK], rq[kItK], rw[kItK], rdo;
   bf16 rdv[4];
-  float rg = 0.f, rgk[kGK ? 16 : 1];
+  float rg = 0.f, rgk[kGK ? 16 : 1], rgt[kGK ? 16 : 1];
   const int gkd = tid % K, gkq = tid / K;  // this thread's key and token quarter (kGK)
   auto tok = [&](int t) { return t < T ? t : T - 1; };
   auto load = [&](int n) {
@@ -364,15 +364,13 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       rdv[e] = dV[(tb + tok(t0 + 16 * wr + 4 * lq + e)) * HV + (long)h * p.V + v0 + col];
-    if (p.g && tid < kC) rg = floor_gate(p.g[(tb + tok(t0 + tid)) * p.H + h]);
+    if (p.g && tid < kC) rg = p.g[(tb + tok(t0 + tid)) * p.H + h];
     if constexpr (kGK) {
-      // gk' = max(g + gk, floor) - g, so that the two cumulative sums add up to the floored
-      // per-key decay of the forward pass
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const long ti = tb + tok(t0 + 16 * gkq + i);
-        const float gt = p.g ? floor_gate(p.g[ti * p.H + h]) : 0.f;
-        rgk[i] = floor_key_gate(gt + p.gk[ti * HK + (long)h * K + gkd]) - gt;
+        rgt[i] = p.g ? p.g[ti * p.H + h] : 0.f;
+        rgk[i] = p.gk[ti * HK + (long)h * K + gkd];
       }
     }
   };
@@ -399,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
   for (int n = NT - 1; n >= 0; --n) {
     const int t0 = n * kC;
     if (wave == 0) {
-      float x = t0 + lane < T ? rg : 0.f;
+      float x = t0 + lane < T ? floor_gate(rg) : 0.f;  // floored at use: rg is a prefetch
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -412,7 +410,10 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
       float x = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x += t0 + 16 * gkq + i < T ? rgk[i] : 0.f;
+        // gk' = max(g + gk, floor) - g (floors applied here, not at the prefetch loads), so
+        // that the two cumulative sums add up to the floored per-key decay of the forward
+        const float gt = floor_gate(rgt[i]);
+        x += t0 + 16 * gkq + i < T ? floor_key_gate(gt + rgk[i]) - gt : 0.f;
         cg[i] = x;
       }
       gq[gkq * K + gkd] = x;

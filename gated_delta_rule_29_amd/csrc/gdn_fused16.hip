@@ -254,14 +254,15 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       const int t = c * kC + lane;
       const bool ok = c < nchunks && t < len;
       const long gi = (tok0 + t) * p.H + h;
-      gv = ok && p.g ? floor_gate(p.g[gi]) : 0.f;
+      gv = ok && p.g ? p.g[gi] : 0.f;
       bv = ok ? p.beta[gi] : 0.f;
     };
     // gate slot of chunk c from its g, beta (rows past the end carry g = 0, beta = 0)
     auto gates = [&](int c, float gv, float bv) {
       if (c >= nchunks) return;
       float* G = s.gate[c % 3];
-      const float gam = wave_incl_scan(gv, lane);
+      // floored here, where it is used, not at the load (which is a prefetch)
+      const float gam = wave_incl_scan(floor_gate(gv), lane);
       const float gl = __shfl(gam, 63, 64), gref = __shfl(gam, 31, 64), g0 = __shfl(gam, 0, 64);
       G[kEg + lane] = __expf(gam);
       G[kEl + lane] = __expf(gl - gam);

@@ -358,7 +358,7 @@ __device__ __forceinline__ void scan_load(ScanStage<TI, K, PK>& st, const FwdPar
   const float* fs = reinterpret_cast<const float*>(slot + SL::kEg);
   if (tid < 128) st.vec = PK ? 0.f : fs[tid];  // e^gamma, then e^{gl - gamma}
   else if (tid < 192) st.vec = t < rows ? p.beta[gi] : 0.f;
-  else st.vec = (t < rows && p.g) ? floor_gate(p.g[gi]) : 0.f;
+  else st.vec = (t < rows && p.g) ? p.g[gi] : 0.f;  // a prefetch: floored where it lands
   st.egl = PK ? 0.f : fs[2 * kC];
   if constexpr (PK) {
     const int d = tid / St::kTPK, part = tid % St::kTPK;
@@ -424,7 +424,7 @@ __device__ __forceinline__ void scan_store(const ScanStage<TI, K, PK>& st, ScanB
   if (tid < 64) b.eg[t] = st.vec;
   else if (tid < 128) b.el[t] = st.vec;
   else if (tid < 192) b.beta[t] = st.vec;
-  else b.g[t] = st.vec;
+  else b.g[t] = floor_gate(st.vec);
   if (tid == 0) b.egl = st.egl;
 }
 

@@ -125,14 +125,14 @@ __global__ __launch_bounds__(256) void transition_kernel(const TI* __restrict__ 
     }
     if (tid < 2 * kC && (tid % kC) < n) {
       const long row = ((long)b * T + t0 + tid % kC) * H + h;
-      sp = tid < kC ? beta[row] : (g ? floor_gate(g[row]) : 0.f);
+      sp = tid < kC ? beta[row] : (g ? g[row] : 0.f);
     }
   };
   load_chunk(0);
   for (int t0 = 0; t0 < T; t0 += kC) {
     const int n = min(kC, T - t0);
     __syncthreads();  // the previous chunk's LDS reads are done
-    if (tid < 2 * kC && (tid % kC) < n) (tid < kC ? bs : gs)[tid % kC] = sp;
+    if (tid < 2 * kC && (tid % kC) < n) (tid < kC ? bs : gs)[tid % kC] = tid < kC ? sp : floor_gate(sp);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kKP; ++i) {
