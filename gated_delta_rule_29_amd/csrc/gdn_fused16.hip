@@ -93,16 +93,6 @@ struct __attribute__((aligned(16))) FusedSmem {
   unsigned pbar;        // prep-wave pair barrier counter
 };
 
-__device__ __forceinline__ u32x2 tr16(const u16* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lds_addr(p)));
-}
-
-// A operand of 8 16-bit values from two transpose reads (elements 0..3, then 4..7).
-__device__ __forceinline__ bf16x8 tr16_pair(const u16* p0, const u16* p1) {
-  const u32x4 w = __builtin_shufflevector(tr16(p0), tr16(p1), 0, 1, 2, 3);
-  return __builtin_bit_cast(bf16x8, w);
-}
-
 // LDS base addresses the optimiser cannot relate to one another: each tile read is then
 // issued as its own base plus an instruction immediate (the compiler would otherwise derive
 // many addresses from one register with a separate add each).
@@ -169,6 +159,101 @@ __device__ __forceinline__ void solve_bar(unsigned* ctr, unsigned& target) {
   asm volatile("" : : : "memory");
 }
 
+// Stores of 16x16 accumulator rows into a [64][64] fp16 tile: element
+// tix(16I + li, 16J + 4lq) = tix(li, 16(J & 1) + 4lq) + 2048 (J >> 1) + 512 I (the octet
+// permutation sees only li), so two per-lane bases (J even, J odd) plus instruction immediates
+// address every tile.
+typedef __attribute__((address_space(3))) u16 lds_u16w;
+__device__ __forceinline__ lds_u16w* lds_wbase(u16* p) {
+  lds_u16w* b = (lds_u16w*)(uintptr_t)lds_addr(p);
+  asm volatile("" : "+v"(b));
+  return b;
+}
+__device__ __forceinline__ void put_f16x4(lds_u16w* b, int off, const f16x4& v) {
+  *(__attribute__((address_space(3))) f16x4*)(b + off) = v;
+}
+
+// Lower 16x16 tiles (I, J) of the Gram K K^T (ISQ false: A, strictly lower, rows scaled by
+// beta) or of Q K^T (ISQ true: P, with the output scale), those selected by MASK (bit
+// I(I+1)/2 + J), decay-weighted and stored as fp16 rows of dst.  The products take the rows of
+// their second factor as the A operand, so a lane's accumulator of tile (I, J) holds columns
+// s = 16J + 4lq + e of row r = 16I + li.  decay(r, s) = e^{gamma_r - gamma_s} comes from the
+// per-token factors of the gate slot (FAST) or, when the chunk decays too fast for them, from
+// gamma itself.
+template <int K, bool ISQ, unsigned MASK, bool FAST>
+__device__ __forceinline__ void prod_tiles(const bf16* qt, const bf16* kt, const float* G,
+                                           u16* dst, float scale) {
+  constexpr int kG = K / 32;
+  const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+  constexpr auto tile_on = [](int I, int J) { return ((MASK >> (I * (I + 1) / 2 + J)) & 1u) != 0; };
+  constexpr auto row_on = [](int I) {
+    for (int J = 0; J <= I; ++J)
+      if (((MASK >> (I * (I + 1) / 2 + J)) & 1u) != 0) return true;
+    return false;
+  };
+  constexpr auto col_on = [](int J) {
+    for (int I = J; I < 4; ++I)
+      if (((MASK >> (I * (I + 1) / 2 + J)) & 1u) != 0) return true;
+    return false;
+  };
+  bf16x8 af[4][kG], bf[4][kG];
+#pragma unroll
+  for (int kk = 0; kk < kG; ++kk)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      if (col_on(I) || (!ISQ && row_on(I))) bf[I][kk] = lds8(kt + tix(16 * I + li, 32 * kk + 8 * lq));
+      if (ISQ && row_on(I)) af[I][kk] = lds8(qt + tix(16 * I + li, 32 * kk + 8 * lq));
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < kG; ++kk) {
+#pragma unroll
+    for (int I = 0, t = 0; I < 4; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J, ++t)
+        if (tile_on(I, J)) acc[t] = mma16(bf[J][kk], ISQ ? af[I][kk] : bf[I][kk], acc[t]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lds_u16w* sb[2] = {lds_wbase(dst + tix(li, 4 * lq)), lds_wbase(dst + tix(li, 16 + 4 * lq))};
+  f32x4 cv[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
+    if (col_on(J)) cv[J] = *reinterpret_cast<const f32x4*>(&G[(FAST ? kFc : kGam) + 16 * J + 4 * lq]);
+#pragma unroll
+  for (int I = 0, t = 0; I < 4; ++I) {
+    if (!row_on(I)) {
+      t += I + 1;
+      continue;
+    }
+    const int r = 16 * I + li;
+    // P carries the output scale: one factor per row here instead of one per output element
+    // in the scan
+    float rv, be_r;
+    if constexpr (FAST) {
+      rv = G[(ISQ ? kFrq : kFrk) + r] * (ISQ ? scale : 1.f);
+      be_r = 1.f;
+    } else {
+      rv = G[kGam + r];
+      be_r = ISQ ? scale : G[kBeta + r];
+    }
+#pragma unroll
+    for (int J = 0; J <= I; ++J, ++t) {
+      if (!tile_on(I, J)) continue;
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = FAST ? rv * cv[J][e] : be_r * __expf(rv - cv[J][e]);
+        val[e] = d * acc[t][e];
+        if (J == I) val[e] = (4 * lq + e <= li) ? val[e] : 0.f;
+      }
+      put_f16x4(sb[J & 1], 2048 * (J >> 1) + 512 * I, cvt_f16x4(val));
+    }
+  }
+}
+
 template <int K, bool VARLEN>
 __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   typedef FusedSmem<K> SM;
@@ -177,8 +262,6 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 15, lq = lane >> 4;
-  const int trj = (lane >> 2) & 3, trc = lane & 3;
 
   // Workgroup -> (chain, value block); the value blocks of a chain stay on one XCD.
   // Consecutive workgroup ids go round-robin to the 8 XCDs, and each XCD starts its
@@ -334,7 +417,6 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         const bf16* qt = reinterpret_cast<const bf16*>(Q.q);
         const bf16* kt = reinterpret_cast<const bf16*>(Q.k);
         f16* tmt = reinterpret_cast<f16*>(T.tm);
-        f16* ptt = reinterpret_cast<f16*>(T.p);
         f16* aft = reinterpret_cast<f16*>(s.af);
         const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(G[kFast])) != 0;
         f16x4 tc0;  // C-form (accumulator layout) of this wave's first diagonal block of Tm
@@ -440,60 +522,12 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
               *reinterpret_cast<f16x4*>(&tmt[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u] * bc);
             }
             tc0 = cvt_f16x4(xc[0] * G[kBeta + 32 * pq + li]);
+          } else if (pq == 2) {
+            // ---- off-diagonal Gram tiles -> A rows (fp16)
+            prod_tiles<K, false, 0x1dau, kFastDecay>(qt, kt, G, s.af, p.scale);
           } else {
-            // ---- pq 2: off-diagonal Gram tiles -> A rows (fp16); pq 3: Q K^T tiles -> P rows
-            auto tiles = [&](auto isq_c) {
-              constexpr bool isq = decltype(isq_c)::value;
-              // lower tiles (I, J), bit I (I + 1) / 2 + J; the Gram leaves out the diagonal
-              constexpr int mask = isq ? 0x3ff : (0x3ff & ~(0x001 | 0x004 | 0x020 | 0x200));
-              f16* dst = isq ? ptt : aft;
-              bf16x8 af[4][kG], bf[4][kG];
-#pragma unroll
-              for (int kk = 0; kk < kG; ++kk)
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                  bf[I][kk] = lds8(kt + tix(16 * I + li, 32 * kk + 8 * lq));
-                  if constexpr (isq) af[I][kk] = lds8(qt + tix(16 * I + li, 32 * kk + 8 * lq));
-                  else af[I][kk] = bf[I][kk];
-                }
-              __builtin_amdgcn_sched_barrier(0);
-              f32x4 acc[10];
-#pragma unroll
-              for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int kk = 0; kk < kG; ++kk) {
-#pragma unroll
-                for (int I = 0, t = 0; I < 4; ++I)
-#pragma unroll
-                  for (int J = 0; J <= I; ++J, ++t)
-                    if ((mask >> t) & 1) acc[t] = mma16(bf[J][kk], af[I][kk], acc[t]);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-              f32x4 cv[4];
-#pragma unroll
-              for (int J = 0; J < 4; ++J) cv[J] = cols4(16 * J + 4 * lq);
-#pragma unroll
-              for (int I = 0, t = 0; I < 4; ++I) {
-                const int r = 16 * I + li;
-                // P carries the output scale: one factor per row here instead of one per
-                // output element in the scan
-                const float rv = rowv(r, isq) * ((isq && kFastDecay) ? p.scale : 1.f);
-                const float be_r = isq ? (kFastDecay ? 1.f : p.scale) : (kFastDecay ? 1.f : G[kBeta + r]);
-#pragma unroll
-                for (int J = 0; J <= I; ++J, ++t) {
-                  if (!((mask >> t) & 1)) continue;
-                  f32x4 val;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) {
-                    val[e] = dec(rv, cv[J][e], be_r) * acc[t][e];
-                    if (J == I) val[e] = (4 * lq + e <= li) ? val[e] : 0.f;
-                  }
-                  *reinterpret_cast<f16x4*>(&dst[tix(r, 16 * J + 4 * lq)]) = cvt_f16x4(val);
-                }
-              }
-            };
-            if (pq == 3) tiles(std::true_type{});
-            else tiles(std::false_type{});
+            // ---- Q K^T tiles -> P rows (fp16)
+            prod_tiles<K, true, 0x3ffu, kFastDecay>(qt, kt, G, T.p, p.scale);
           }
         };
         if (fast) body(std::true_type{});
@@ -545,6 +579,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   // =============================== scan waves ===============================
   // hs[G][t] holds keys 32G + 8lq + 4t + e (e = 0..3) of value column v0 + 16 wave + li.
   f32x4 hs[kG][2];
+  const int li = lane & 15, lq = lane >> 4;
 #pragma unroll
   for (int G = 0; G < kG; ++G)
 #pragma unroll
@@ -602,8 +637,6 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       const u16* vt = s.v[n & 1];
       const typename SM::TP& T = s.tp[n & 1];
       const float* vec = s.gate[n % 3];
-      const f16* tmt = reinterpret_cast<const f16*>(T.tm);
-      const f16* ptt = reinterpret_cast<const f16*>(T.p);
       const long tok = tok0 + (long)n * kC;
       const uint32_t rows = (uint32_t)min(kC, len - n * kC);
 
