@@ -402,6 +402,10 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = total_ms / args.steps
+    srt = sorted(launch_ms)
+
+    def pct(q):  # nearest-rank percentile of the per-launch times
+        return srt[min(len(srt) - 1, max(0, int(round(q * (len(srt) - 1)))))]
     value = th / (ms_per_step / 1e3)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     achieved = alg / avg_launch_s / 1e9
@@ -426,6 +430,9 @@ def main():
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic (seeded workloads.py recipe: %s)" % args.workload,
         "config": dict(config, input_copies_rotated=len(sets)),
+        "launch_ms": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9), "mean":
+                      avg_launch_s * 1e3, "n": len(launch_ms),
+                      "clock": "HIP events around each call on its stream"},
         "roofline": dict(roof, traffic=traffic, kernel=kernel,
                          **{("alg_flops_per_launch" if kind == "summary" else
                              "alg_bytes_per_launch"): alg},
@@ -434,6 +441,16 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(kind, inp)
+        if args.workload == "tiny_f32":
+            # the small fp32 workload is also timed on one host thread (whole workload)
+            import oracle
+
+            n0 = oracle.max_threads()
+            oracle.set_threads(1)
+            one = cpu_baseline(kind, inp)
+            oracle.set_threads(n0)
+            out["cpu_baseline"]["single_thread"] = {"value": one["value"], "cores": 1,
+                                                    "sample": one["sample"]}
     print(json.dumps(out), flush=True)
 
 

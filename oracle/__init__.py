@@ -29,8 +29,10 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "gdn_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+# GDN_ORACLE_SRC names another copy of gdn_oracle.c to build and load (it is built next to
+# that copy); tests/test_oracle_mutations.py uses it to plant mistakes in a scratch copy.
+_SRC = os.environ.get("GDN_ORACLE_SRC") or os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(_SRC)), "_build", "liboracle.so")
 _lib = None
 
 CHUNK = 64

@@ -1,0 +1,81 @@
+"""The oracle's pins must catch plausible mistakes (CPU).
+
+Each case plants one mistake in a scratch copy of oracle/gdn_oracle.c (a dropped term, a wrong
+sign or index, a transposed operand, a decay at the wrong place), builds that copy, and runs
+the pin tests against it in a fresh process (GDN_ORACLE_SRC selects the copy).  The pins pass
+on the real oracle (the rest of the suite), so a failing run here is the planted mistake being
+caught.  A mistake that no pin caught would show as a passing run, and the case fails.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "gdn_oracle.c")
+
+PINS_GDN = "tests/test_oracle_pins.py"
+PINS_CAM = "tests/test_oracle_cam.py"
+PINS_DHU = "tests/test_oracle_dhu.py"
+
+# (name, pin file, text in gdn_oracle.c, replacement)
+MUTATIONS = [
+    ("missing beta", PINS_GDN, "d[c] = bt * (vt[c] - d[c]);", "d[c] = (vt[c] - d[c]);"),
+    ("per-key gate sign", PINS_GDN, "if (gk) lam += gk[(long)t * sqk + r];",
+     "if (gk) lam -= gk[(long)t * sqk + r];"),
+    ("transposed read-out", PINS_GDN, "ot[c] += S[(size_t)r * V + c] * qt[r];",
+     "ot[c] += S[(size_t)(c % K) * V + (r % V)] * qt[r];"),
+    ("saved state after the decay", PINS_GDN,
+     "    if (hch && (t % C) == 0)  /* state entering chunk t/C, before this token's decay */\n"
+     "      memcpy(hch + (size_t)(t / C) * K * V, S, sizeof(double) * (size_t)K * V);", ""),
+    ("k_scale on q", PINS_GDN, "qx = qx > 0.0 ? qx : 0.0;", "qx = (qx > 0.0 ? qx : 0.0) * k_scale;"),
+    ("reverse decay index", PINS_GDN, "const double dcy = decay[(long)bh * F + fa];",
+     "const double dcy = decay[(long)bh * F + f];"),
+    ("transition: decay on columns", PINS_GDN,
+     "      for (int c = 0; c < K; ++c) M[(size_t)r * K + c] *= a[r];",
+     "      for (int c = 0; c < K; ++c) M[(size_t)r * K + c] *= a[c];"),
+    ("transition: transposed rank-one update", PINS_GDN,
+     "      for (int c = 0; c < K; ++c) M[(size_t)r * K + c] -= bt * kt[r] * w[c];",
+     "      for (int c = 0; c < K; ++c) M[(size_t)r * K + c] -= bt * kt[c] * w[r];"),
+    ("camera: transposed 4x4 matrix", PINS_CAM,
+     "for (int j = 0; j < 4; ++j) acc += P[which][i * 4 + j] * xn[4 * g + j];",
+     "for (int j = 0; j < 4; ++j) acc += P[which][j * 4 + i] * xn[4 * g + j];"),
+    ("camera: RoPE without the pair swap", PINS_CAM,
+     "y[Dh + r] = xn[Dh + r] * cosv[n * Dh + r] + xn[Dh + (r ^ 1)] * sinv[n * Dh + r];",
+     "y[Dh + r] = xn[Dh + r] * cosv[n * Dh + r] + xn[Dh + r] * sinv[n * Dh + r];"),
+    ("dhu: no decay on dv2's state term", PINS_DHU,
+     "s += k[tk * K + r] * exp(gl[r] - gam[(size_t)i * K + r]) * dh[(size_t)r * V + c];",
+     "s += k[tk * K + r] * dh[(size_t)r * V + c];"),
+    ("dhu: sign of the w term", PINS_DHU,
+     "dh[(size_t)r * V + c] += qr * do_[tk * V + c] - wr * dv2[tk * V + c];",
+     "dh[(size_t)r * V + c] += qr * do_[tk * V + c] + wr * dv2[tk * V + c];"),
+]
+
+
+def _run_pins(src_path, pins):
+    env = dict(os.environ, GDN_ORACLE_SRC=src_path, OMP_NUM_THREADS="4")
+    cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+           "-m", "not gpu", os.path.join(ROOT, pins)]
+    return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("name,pins,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_fails_a_pin(tmp_path, name, pins, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation anchor of %r is not unique in gdn_oracle.c" % name
+    dst = tmp_path / "gdn_oracle.c"
+    dst.write_text(text.replace(old, new))
+    res = _run_pins(str(dst), pins)
+    assert res.returncode != 0, "no pin in %s caught the planted mistake %r:\n%s" % (
+        pins, name, res.stdout[-2000:])
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same procedure on an unchanged copy passes every pin file."""
+    dst = tmp_path / "gdn_oracle.c"
+    shutil.copy(SRC, dst)
+    for pins in (PINS_GDN, PINS_CAM, PINS_DHU):
+        res = _run_pins(str(dst), pins)
+        assert res.returncode == 0, res.stdout[-2000:]
