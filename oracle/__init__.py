@@ -71,6 +71,7 @@ def _load():
                                         P]
         lib.oracle_cam_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
         lib.oracle_gdn_dhu.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, Dd, P, P, P]
+        lib.oracle_cam_scan_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
@@ -303,6 +304,25 @@ def cam_scan(q, k, v, beta, decay, reverse=False, init_state=None, want_final=Fa
     if rc != 0:
         raise RuntimeError("oracle_cam_scan failed")
     return (out, fin) if want_final else out
+
+
+def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False):
+    """Backward of the camera-branch scan (no initial state), SANA fused_cam_gdn.py page,
+    _cam_scan_bwd_kernel: gradients of sum(out * dout) for out = cam_scan(q, k, v, beta,
+    decay, reverse).  Returns dict dq, dk, dv [B,H,D,N], dbeta [B,H,F,S], ddecay [B,H,F]."""
+    q, k, v, beta, decay, dout = map(_f64, (q, k, v, beta, decay, dout))
+    B, H, D, N = q.shape
+    F, S = beta.shape[2], beta.shape[3]
+    out = {n: np.empty((B, H, D, N)) for n in ("dq", "dk", "dv")}
+    out["dbeta"] = np.empty((B, H, F, S))
+    out["ddecay"] = np.empty((B, H, F))
+    rc = _load().oracle_cam_scan_bwd(B, H, D, F, S, int(bool(reverse)), _p(q), _p(k), _p(v),
+                                     _p(beta), _p(decay), _p(dout), _p(out["dq"]),
+                                     _p(out["dk"]), _p(out["dv"]), _p(out["dbeta"]),
+                                     _p(out["ddecay"]))
+    if rc != 0:
+        raise RuntimeError("oracle_cam_scan_bwd failed")
+    return out
 
 
 def gdn_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, chunk=CHUNK, gk=None):

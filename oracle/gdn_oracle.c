@@ -616,6 +616,149 @@ int oracle_cam_scan(int B, int H, int D, int F, int S_, int reverse, const doubl
 }
 
 /*
+ * Backward of the camera-branch scan (SANA fused_cam_gdn.py page, "Backward Triton kernel":
+ * _cam_scan_bwd_kernel): the gradients of L = sum(out * dout) with respect to q, k, v, beta
+ * and decay, for the scan of oracle_cam_scan without an initial state (one direction).
+ * The forward steps are replayed, keeping the state after each step's decay (Sp) and after
+ * its update (St); then, step by step in reverse order, with dSt the gradient of the state
+ * after the step's update:
+ *   output of frame f (out_s = St^T q_s):   dq_s = St dout_s,   dSt += q_s dout_s^T
+ *   absorption of frame fa (St = Sp + sum_s k_s d_s^T, d_s = beta_s (v_s - Sp^T k_s)):
+ *       dd_s = dSt^T k_s,  dv_s = beta_s dd_s,  dbeta_s = dd_s . (v_s - Sp^T k_s),
+ *       dk_s = dSt d_s + Sp (-beta_s dd_s),  dSp = dSt + sum_s k_s (-beta_s dd_s)^T
+ *   decay (Sp = g St_prev):  ddecay[fa] = sum(dSp * St_prev),  dSt_prev = g dSp.
+ * Tokens of a frame that is never absorbed (frame 0 of the reverse scan) get zero k, v, beta
+ * gradients, and a decay that is never applied (or that multiplies the zero initial state)
+ * gets ddecay = 0.
+ */
+int oracle_cam_scan_bwd(int B, int H, int D, int F, int S_, int reverse, const double* q,
+                        const double* k, const double* v, const double* beta,
+                        const double* decay, const double* dout, double* dq, double* dk,
+                        double* dv, double* dbeta, double* ddecay) {
+  if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S_ <= 0) return -1;
+  const long N = (long)F * S_;
+  const size_t DD = (size_t)D * D;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* Sp = (double*)malloc(sizeof(double) * DD * F);  /* per step: after the decay */
+    double* St = (double*)malloc(sizeof(double) * DD * F);  /* per step: after the update */
+    double* dS = (double*)malloc(sizeof(double) * DD);
+    double* dP = (double*)malloc(sizeof(double) * DD);
+    double* vec = (double*)malloc(sizeof(double) * 4 * (size_t)D);
+    if (!Sp || !St || !dS || !dP || !vec) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int bh = 0; bh < B * H; ++bh) {
+        const long base = (long)bh * D * N;
+        double* r_ = vec;           /* v_s - Sp^T k_s */
+        double* dd = vec + D;       /* dd_s */
+        double* d_ = vec + 2 * D;   /* d_s */
+        /* ---- forward replay ---- */
+        for (int it = 0; it < F; ++it) {
+          double* sp = Sp + (size_t)it * DD;
+          double* st = St + (size_t)it * DD;
+          if (it == 0) memset(st, 0, sizeof(double) * DD);
+          else memcpy(st, St + (size_t)(it - 1) * DD, sizeof(double) * DD);
+          memcpy(sp, st, sizeof(double) * DD);
+          const int f = reverse ? F - 1 - it : it;
+          if (reverse && it == 0) continue;  /* the reverse scan absorbs nothing first */
+          const int fa = reverse ? f + 1 : f;
+          const double g = decay[(long)bh * F + fa];
+          for (size_t e = 0; e < DD; ++e) sp[e] = g * sp[e];
+          memcpy(st, sp, sizeof(double) * DD);
+          for (int s = 0; s < S_; ++s) {
+            const long t = (long)fa * S_ + s;
+            for (int c = 0; c < D; ++c) {
+              double pred = 0.0;
+              for (int r = 0; r < D; ++r) pred += k[base + (long)r * N + t] * sp[(size_t)r * D + c];
+              d_[c] = beta[(long)bh * N + t] * (v[base + (long)c * N + t] - pred);
+            }
+            for (int r = 0; r < D; ++r)
+              for (int c = 0; c < D; ++c) st[(size_t)r * D + c] += k[base + (long)r * N + t] * d_[c];
+          }
+        }
+        /* ---- reverse pass ---- */
+        for (long e = 0; e < (long)D * N; ++e) {
+          dk[base + e] = 0.0;
+          dv[base + e] = 0.0;
+        }
+        for (long t = 0; t < N; ++t) dbeta[(long)bh * N + t] = 0.0;
+        for (int f = 0; f < F; ++f) ddecay[(long)bh * F + f] = 0.0;
+        memset(dS, 0, sizeof(double) * DD);
+        for (int it = F - 1; it >= 0; --it) {
+          const double* sp = Sp + (size_t)it * DD;
+          const double* st = St + (size_t)it * DD;
+          const int f = reverse ? F - 1 - it : it;
+          /* output of frame f */
+          for (int s = 0; s < S_; ++s) {
+            const long t = (long)f * S_ + s;
+            for (int r = 0; r < D; ++r) {
+              double acc = 0.0;
+              for (int c = 0; c < D; ++c) acc += st[(size_t)r * D + c] * dout[base + (long)c * N + t];
+              dq[base + (long)r * N + t] = acc;
+            }
+            for (int r = 0; r < D; ++r)
+              for (int c = 0; c < D; ++c)
+                dS[(size_t)r * D + c] += q[base + (long)r * N + t] * dout[base + (long)c * N + t];
+          }
+          if (reverse && it == 0) continue;
+          const int fa = reverse ? f + 1 : f;
+          const double g = decay[(long)bh * F + fa];
+          memcpy(dP, dS, sizeof(double) * DD);
+          for (int s = 0; s < S_; ++s) {
+            const long t = (long)fa * S_ + s;
+            const double bt = beta[(long)bh * N + t];
+            for (int c = 0; c < D; ++c) {
+              double pred = 0.0, g_ = 0.0;
+              for (int r = 0; r < D; ++r) {
+                pred += k[base + (long)r * N + t] * sp[(size_t)r * D + c];
+                g_ += dS[(size_t)r * D + c] * k[base + (long)r * N + t];
+              }
+              r_[c] = v[base + (long)c * N + t] - pred;
+              d_[c] = bt * r_[c];
+              dd[c] = g_;
+            }
+            double db = 0.0;
+            for (int c = 0; c < D; ++c) {
+              dv[base + (long)c * N + t] = bt * dd[c];
+              db += dd[c] * r_[c];
+            }
+            dbeta[(long)bh * N + t] = db;
+            for (int r = 0; r < D; ++r) {
+              double acc = 0.0;
+              for (int c = 0; c < D; ++c)
+                acc += dS[(size_t)r * D + c] * d_[c] - sp[(size_t)r * D + c] * bt * dd[c];
+              dk[base + (long)r * N + t] = acc;
+            }
+            for (int r = 0; r < D; ++r)
+              for (int c = 0; c < D; ++c)
+                dP[(size_t)r * D + c] -= k[base + (long)r * N + t] * bt * dd[c];
+          }
+          /* decay: Sp = g * (state before the step); that state is St of the previous step
+             (zero before the first) */
+          double dg = 0.0;
+          if (it > 0) {
+            const double* prev = St + (size_t)(it - 1) * DD;
+            for (size_t e = 0; e < DD; ++e) dg += dP[e] * prev[e];
+          }
+          ddecay[(long)bh * F + fa] = dg;
+          for (size_t e = 0; e < DD; ++e) dS[e] = g * dP[e];
+        }
+      }
+    }
+    free(Sp);
+    free(St);
+    free(dS);
+    free(dP);
+    free(vec);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
  * State-gradient pass of the chunked backward (the dhu fragments on the hyper-parallel
  * "Diff Coverage" page): the adjoint of the chunk state pass
  *     v_new = u - w h,   o = scale (e^gamma q)^T h + P v_new,   h_next = diag(e^{gamma_L}) h + K~^T v_new

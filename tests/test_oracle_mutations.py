@@ -19,6 +19,7 @@ SRC = os.path.join(ROOT, "oracle", "gdn_oracle.c")
 PINS_GDN = "tests/test_oracle_pins.py"
 PINS_CAM = "tests/test_oracle_cam.py"
 PINS_DHU = "tests/test_oracle_dhu.py"
+PINS_CBWD = "tests/test_oracle_cam_bwd.py"
 
 # (name, pin file, text in gdn_oracle.c, replacement)
 MUTATIONS = [
@@ -51,6 +52,14 @@ MUTATIONS = [
     ("dhu: sign of the w term", PINS_DHU,
      "dh[(size_t)r * V + c] += qr * do_[tk * V + c] - wr * dv2[tk * V + c];",
      "dh[(size_t)r * V + c] += qr * do_[tk * V + c] + wr * dv2[tk * V + c];"),
+    ("camera backward: dv without beta", PINS_CBWD,
+     "dv[base + (long)c * N + t] = bt * dd[c];", "dv[base + (long)c * N + t] = dd[c];"),
+    ("camera backward: dk without the prediction term", PINS_CBWD,
+     "acc += dS[(size_t)r * D + c] * d_[c] - sp[(size_t)r * D + c] * bt * dd[c];",
+     "acc += dS[(size_t)r * D + c] * d_[c];"),
+    ("camera backward: decay gradient against the decayed state", PINS_CBWD,
+     "            const double* prev = St + (size_t)(it - 1) * DD;",
+     "            const double* prev = Sp + (size_t)it * DD;"),
 ]
 
 
@@ -76,6 +85,6 @@ def test_unmutated_copy_passes(tmp_path):
     """Control: the same procedure on an unchanged copy passes every pin file."""
     dst = tmp_path / "gdn_oracle.c"
     shutil.copy(SRC, dst)
-    for pins in (PINS_GDN, PINS_CAM, PINS_DHU):
+    for pins in (PINS_GDN, PINS_CAM, PINS_DHU, PINS_CBWD):
         res = _run_pins(str(dst), pins)
         assert res.returncode == 0, res.stdout[-2000:]
