@@ -18,7 +18,7 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
+           "cam_scan_bidi", "cam_scan_bwd", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
            "gdn_abi_version", "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
@@ -408,6 +408,33 @@ def cam_scan_bidi(q, k, v, beta, decay, *, decay_bwd=None, init_state=None,
                            _ptr(ws), ws_n, _stream(dev))
     _lib.check(rc, "cam_scan_bidi")
     return (of, orv, fin) if save_final_state else (of, orv)
+
+
+def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False):
+    """Backward of cam_scan (one direction, no state in / out): gradients of sum(out * dout).
+    q, k, v, dout [B,H,D,N] fp32; beta [B,H,F,S]; decay [B,H,F].  Returns a dict with dq,
+    dk, dv [B,H,D,N], dbeta [B,H,F,S] and ddecay [B,H,F] (fp32)."""
+    B, H, D, N = q.shape
+    F, S = beta.shape[2], beta.shape[3]
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, name, (B, H, D, N), torch.float32, dev)
+    _need(beta, "beta", (B, H, F, S), torch.float32, dev)
+    _need(decay, "decay", (B, H, F), torch.float32, dev)
+    if F * S != N:
+        raise ValueError("beta is [B,H,F,S] with F*S = %d, but N = %d" % (F * S, N))
+    out = {n: torch.empty(B, H, D, N, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
+    out["dbeta"] = torch.empty(B, H, F, S, dtype=torch.float32, device=dev)
+    out["ddecay"] = torch.empty(B, H, F, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    ws_n = lib.cam_scan_bwd_workspace_bytes(B, H, D, F)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.cam_scan_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), _ptr(dout),
+                          int(bool(reverse)), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                          _ptr(out["dbeta"]), _ptr(out["ddecay"]), B, H, D, F, S, _ptr(ws), ws_n,
+                          _stream(dev))
+    _lib.check(rc, "cam_scan_bwd")
+    return out
 
 
 def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, gk=None, want_dh=True,

@@ -616,6 +616,57 @@ int cam_scan_bidi(const float* q, const float* k, const float* v, const float* b
 }
 
 
+// ---- backward of the camera-branch scan ----------------------------------------------------
+
+size_t cam_scan_bwd_workspace_bytes(int B, int H, int D, int F) {
+  if (B <= 0 || H <= 0 || (D != 64 && D != 128) || F <= 0) return 0;
+  const size_t mats = (size_t)B * H * F * D * D;
+  return 8 * al256(mats * 4) + al256((size_t)B * H * F * (D / 32) * 4);
+}
+
+int cam_scan_bwd(const float* q, const float* k, const float* v, const float* beta,
+                 const float* decay, const float* dout, int reverse, float* dq, float* dk,
+                 float* dv, float* dbeta, float* ddecay, int B, int H, int D, int F, int S,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !beta || !decay || !dout || !dq || !dk || !dv || !dbeta || !ddecay)
+    return fail(GDN_ERR_INVALID, "every input and gradient pointer must be non-null");
+  if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S <= 0)
+    return fail(GDN_ERR_INVALID, "B, H, D, F, S must be positive (got %d, %d, %d, %d, %d)", B, H,
+                D, F, S);
+  if (reverse != 0 && reverse != 1) return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, got %d", reverse);
+  if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
+  if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
+  if ((int64_t)F * S > INT32_MAX || (int64_t)B * H * F * 3 > INT32_MAX ||
+      (int64_t)B * H * F * (S / 64) > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "F*S or B*H*F exceeds the grid limit");
+  const size_t need = cam_scan_bwd_workspace_bytes(B, H, D, F);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  const size_t mats = (size_t)B * H * F * D * D;
+  char* ws = static_cast<char*>(workspace);
+  gdn::CamBwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.beta = beta; p.decay = decay; p.dout = dout; p.reverse = reverse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.ddecay = ddecay;
+  p.B = B; p.H = H; p.D = D; p.F = F; p.S = S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* r = ws + off; off += al256(bytes); return r; };
+  p.G = reinterpret_cast<float*>(take(mats * 4));
+  p.U = reinterpret_cast<float*>(take(mats * 4));
+  p.W = reinterpret_cast<float*>(take(mats * 4));
+  p.Spf = reinterpret_cast<float*>(take(mats * 4));
+  p.Sp = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
+  p.SpT = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
+  p.Ab = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
+  p.AbT = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
+  p.ddecay_part = reinterpret_cast<float*>(take((size_t)B * H * F * (D / 32) * 4));
+  p.lo = mats;
+  hipError_t e = gdn::launch_cam_scan_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cam_scan_bwd launch");
+  return ok();
+}
+
 // ---- backward: state-gradient pass --------------------------------------------------------
 
 int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_, const void* dv,

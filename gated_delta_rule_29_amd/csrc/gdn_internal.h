@@ -175,6 +175,37 @@ struct DhuParams {
 };
 hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream);  // K = 128; dtype 0 fp32, 1 bf16
 
+// backward of the camera-branch scan (gdn_cambwd.hip)
+struct CamBwdParams {
+  const float* q;     // [B, H, D, N] fp32
+  const float* k;
+  const float* v;
+  const float* beta;  // [B, H, F, S]
+  const float* decay; // [B, H, F]
+  const float* dout;  // [B, H, D, N]
+  int reverse;
+  float* dq;          // [B, H, D, N]
+  float* dk;
+  float* dv;
+  float* dbeta;       // [B, H, F, S]
+  float* ddecay;      // [B, H, F]
+  int B, H, D, F, S;
+  // workspace views, per (b, h, frame or step) D x D
+  float* G;           // frame statistics K diag(beta) K^T, K diag(beta) V^T, Q dout^T (fp32)
+  float* U;
+  float* W;
+  float* Spf;         // state after each step (fp32)
+  // bf16 operand pairs: element e of a matrix is hi[e] + lo[e] with hi[e] = bf16(x) and
+  // lo[e] = bf16(x - hi[e]); the lo half of each array starts `lo` elements after the hi half
+  __bf16* Sp;         // state after each step, row-major and transposed
+  __bf16* SpT;
+  __bf16* Ab;         // gradient of the state after each step's update, both orientations
+  __bf16* AbT;
+  size_t lo;          // B * H * F * D * D
+  float* ddecay_part; // [B, H, F, D/32] partial sums of the decay gradient
+};
+hipError_t launch_cam_scan_bwd(const CamBwdParams& p, hipStream_t stream);
+
 hipError_t launch_cam_prep(const CamPrepParams& p, hipStream_t stream);
 hipError_t launch_cam_scan(const CamScanParams& p, hipStream_t stream);
 // the frame scan of gdn_bigdn.hip, for one direction without z

@@ -20,7 +20,8 @@
  *    the merge (bigdn_fwd_merged);
  *  - a fragment's state summary and the joining of fragments (gdn_state_summary,
  *    gdn_state_apply), the single-GPU part of context parallelism;
- *  - the camera branch of the video block (cam_prep, cam_scan, cam_scan_bidi);
+ *  - the camera branch of the video block (cam_prep, cam_scan, cam_scan_bidi) and the
+ *    backward of its scan (cam_scan_bwd);
  *  - the backward's state-gradient pass (gdn_bwd_dhu, gdn_bwd_dhu_varlen).
  *
  * Conventions shared by every entry point.
@@ -361,6 +362,32 @@ GDN_API int cam_scan_bidi(const float* q, const float* k, const float* v, const 
                           float* final_state, float* out_fwd, float* out_rev, int B, int H,
                           int D, int F, int S, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * cam_scan_bwd -- backward of cam_scan (one direction, no initial or final state): the
+ * gradients of L = sum(out * dout) for out = cam_scan(q, k, v, beta, decay, reverse)
+ * (SANA fused_cam_gdn.py page, "Backward Triton kernel": _cam_scan_bwd_kernel, and its
+ * per-iteration derivation).  The forward states are recomputed here, so the call needs only
+ * the forward's inputs.
+ *   q, k, v, dout [B,H,D,N] fp32 channel-major, N = F*S; beta [B,H,F,S]; decay [B,H,F]
+ *   dq, dk, dv    [B,H,D,N] fp32 OUT;  dbeta [B,H,F,S] fp32 OUT;  ddecay [B,H,F] fp32 OUT
+ *   Tokens never absorbed (frame 0 of the reverse scan) get zero dk, dv, dbeta; a decay that
+ *   is never applied, or that multiplies the zero initial state, gets ddecay = 0.
+ *   Precision: every product splits each fp32 operand x into bf16 hi = bf16(x) and
+ *   lo = bf16(x - hi) and sums hi*hi + hi*lo + lo*hi with fp32 accumulation (about 16
+ *   mantissa bits per operand; the page's backward takes plain bf16 operands, whose
+ *   rounding alone moves the gradients by up to 4e-2 of their RMS); the recomputed forward
+ *   states and their gradients are scanned in fp32.
+ *   workspace  at least cam_scan_bwd_workspace_bytes(B, H, D, F) bytes, 256-byte aligned
+ *   (per (b, h, frame) three D x D fp32 statistics, the fp32 state, and hi/lo bf16 pairs of
+ *   the state and its gradient in both orientations).
+ * Supported: D in {64, 128}, S a multiple of 64.
+ */
+GDN_API size_t cam_scan_bwd_workspace_bytes(int B, int H, int D, int F);
+GDN_API int cam_scan_bwd(const float* q, const float* k, const float* v, const float* beta,
+                         const float* decay, const float* dout, int reverse, float* dq,
+                         float* dk, float* dv, float* dbeta, float* ddecay, int B, int H, int D,
+                         int F, int S, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdn_bwd_dhu -- state-gradient pass of the chunked backward ([hyper-parallel "Diff Coverage"

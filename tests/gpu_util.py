@@ -18,6 +18,11 @@ pages' own scan uses TF32 dots, whose mantissa is as wide): c = 1e-2 there.  Eac
 term carries two operand roundings of relative size u = 2^-11, so an output's error is about
 2u * RMS in standard deviation; 1e-2 is 5.5 of those standard deviations, doubled.
 
+The camera-branch scan backward splits each fp32 operand into a bf16 pair x = hi + lo and
+sums three products (hi*hi + hi*lo + lo*hi), so an operand carries a relative rounding of
+about u = 2^-17 (plus the dropped lo*lo term, 2^-18): by the same count as above, 2u * RMS in
+standard deviation, 5.5 of those doubled is 1.7e-4, rounded up to c = 2e-4.
+
 Integer tables are compared bit for bit.
 """
 import sys
@@ -27,6 +32,7 @@ import torch
 
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 FP16_OPERAND_TOL = 1e-2
+SPLIT_OPERAND_TOL = 2e-4
 
 
 def _np(x):

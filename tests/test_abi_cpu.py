@@ -288,3 +288,25 @@ def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_launch():
                                     bad.ctypes.data_as(ctypes.c_void_p), 2, None, FAKE, None, None,
                                     None, None, None, 5, 4, 128, 128, 1, None)
     assert rc == L.ERR_INVALID
+
+
+def test_cam_scan_bwd_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, dout=FAKE, rev=0, B=1, H=2, D=128, F=3, S=64, ws=None, wsn=0)
+        a.update(kw)
+        return lib.cam_scan_bwd(a["q"], FAKE, FAKE, FAKE, FAKE, a["dout"], a["rev"], FAKE, FAKE,
+                                FAKE, FAKE, FAKE, a["B"], a["H"], a["D"], a["F"], a["S"],
+                                a["ws"], a["wsn"], None)
+
+    assert call(q=None) == L.ERR_INVALID
+    assert call(dout=None) == L.ERR_INVALID
+    assert call(F=0) == L.ERR_INVALID
+    assert call(rev=2) == L.ERR_INVALID
+    assert call(D=32) == L.ERR_UNSUPPORTED
+    assert call(S=100) == L.ERR_UNSUPPORTED
+    assert call() == L.ERR_WORKSPACE
+    n = lib.cam_scan_bwd_workspace_bytes(1, 2, 128, 3)
+    assert n >= 1 * 2 * 3 * 128 * 128 * (4 * 4 + 4 * 2)
+    assert lib.cam_scan_bwd_workspace_bytes(1, 2, 96, 3) == 0

@@ -168,6 +168,15 @@ def cam_scan_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
     return {"q": q, "k": k, "v": v, "beta": beta, "decay": decay}
 
 
+def cam_scan_bwd_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
+    """Inputs of the camera-scan backward: cam_scan_inputs, then the upstream gradient
+    dout ~ N(0, 1) [B,H,D,N] fp32, drawn last."""
+    inp = cam_scan_inputs(B, F, S, H, D, seed=seed, decay_shift=decay_shift)
+    gen = _gen(seed + 7919)
+    inp["dout"] = torch.randn(B, H, D, F * S, generator=gen)
+    return inp
+
+
 # The workloads, named by what they are.
 WORKLOADS = {
     "tiny_f32": dict(kind="gdn", B=1, T=256, H=2, K=64, V=64, dtype="f32", seed=0, g_shift=2.0),
