@@ -90,6 +90,13 @@ def alg_bytes_cam(B, F, S, H, D):
     return prep + scans
 
 
+def alg_bytes_cam_bwd(B, F, S, H, D):
+    """Minimum HBM bytes of one camera-scan backward call (fp32): read q, k, v, dout, beta and
+    decay once; write dq, dk, dv, dbeta and ddecay."""
+    N = F * S
+    return 7 * B * H * D * N * 4 + 2 * B * H * N * 4 + 2 * B * H * F * 4
+
+
 def alg_bytes_dhu(B, T, H, K, V, elt):
     """Minimum HBM bytes of one state-gradient pass: read q, k, w, do, dv (input dtype), the
     gates and dht once; write dv2 (input dtype), the per-chunk state gradients and dh0 (fp32)."""
@@ -178,6 +185,19 @@ def cpu_baseline(kind, inp, max_chains=64):
                                 reverse=rev)
         return _cpu_time(run, "camera prep + both scan directions on the first %d of %d frames, "
                          "all %d heads (%d tokens)" % (fs, F, H, n), B * n * H)
+    if kind == "cam_bwd":
+        B, H, D, N = inp["q"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        fs = min(F, 4)
+        n = fs * S
+        sub = {k: inp[k][..., :n] for k in ("q", "k", "v", "dout")}
+        sub["beta"], sub["decay"] = inp["beta"][:, :, :fs], inp["decay"][:, :, :fs]
+
+        def run():
+            for rev in (False, True):
+                oracle.cam_scan_bwd(**sub, reverse=rev)
+        return _cpu_time(run, "both scan directions' backward on the first %d of %d frames, "
+                         "all %d heads (%d tokens)" % (fs, F, H, n), 2 * B * n * H)
     if kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -366,6 +386,22 @@ def main():
                                             s["rope_cos"], s["rope_sin"], s["k_scale"], s["eps"])
             fwd, rev = gdn.cam_scan_bidi(qt, kt, vt, s["beta"], s["decay"])
             return fwd, rev, infl
+    elif kind == "cam_bwd":
+        B, H, D, N = inp["q"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        dt = torch.float32
+        th = 2 * B * N * H  # tokens*heads of both directions
+        alg = 2 * alg_bytes_cam_bwd(B, F, S, H, D)
+        kernel = "cam_scan_bwd x 2 directions (3 kernels each, whole step)"
+        config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
+                  "state": "fp32", "products": "split bf16 (hi/lo) operands, fp32 accumulation",
+                  "step": "gradients of the forward and of the reverse frame scan (two calls; "
+                          "summing the two directions' gradients is the caller's)"}
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return [gdn.cam_scan_bwd(s["q"], s["k"], s["v"], s["beta"], s["decay"], s["dout"],
+                                     reverse=rev) for rev in (False, True)]
     elif kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

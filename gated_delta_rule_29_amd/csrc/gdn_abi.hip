@@ -134,7 +134,7 @@ namespace {
 // gdn_state_summary workspace: the forward pass's own workspace and its discarded per-token
 // outputs.  Every view 256-byte aligned.
 struct SummaryWs {
-  size_t fwd, o, total;
+  size_t fwd, o, wy, total;
 };
 
 size_t al256s(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -147,6 +147,8 @@ SummaryWs summary_ws(int B, int T, int H, int K, int V, int dtype, bool per_key)
   off = al256s(off + gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, per_key ? GDN_FWD_PER_KEY : 0u));
   w.o = off;
   off = al256s(off + tok * (size_t)V * es);
+  w.wy = off;
+  off = al256s(off + gdn::transition_ws_bytes(B, T, H, K, dtype, per_key));
   w.total = off;
   return w;
 }
@@ -190,7 +192,7 @@ int gdn_state_summary(const void* k, const void* v, const float* g, const float*
   hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, false, st);
   if (e != hipSuccess) return hip_fail(e, "gdn_state_summary launch");
   if (transition) {
-    e = gdn::launch_transition(k, g, gk, beta, transition, B, T, H, K, dtype, st);
+    e = gdn::launch_transition(k, g, gk, beta, transition, B, T, H, K, dtype, ws + w.wy, st);
     if (e != hipSuccess) return hip_fail(e, "gdn_state_summary launch");
   }
   return ok();

@@ -42,9 +42,12 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);  // bytes a m
 hipError_t launch_identity(float* m, long BH, int K, hipStream_t stream);
 hipError_t launch_apply(const float* c, const float* M, const float* h_in, float* h_out, int BH,
                         int K, int V, hipStream_t stream);
-// M [B,H,K,K] fp32 from k (dtype 0 fp32, 1 bf16), g, gk (each may be null), beta; K in {64, 128}
+// M [B,H,K,K] fp32 from k (dtype 0 fp32, 1 bf16), g, gk (each may be null), beta; K in {64, 128}.
+// wy: transition_ws_bytes(B, T, H, K, dtype, gk != null) bytes of workspace (256-byte aligned).
 hipError_t launch_transition(const void* k, const float* g, const float* gk, const float* beta,
-                             float* M, int B, int T, int H, int K, int dtype, hipStream_t stream);
+                             float* M, int B, int T, int H, int K, int dtype, void* wy,
+                             hipStream_t stream);
+size_t transition_ws_bytes(int B, int T, int H, int K, int dtype, bool per_key);
 constexpr int kApplyMaxK = 256;
 
 }  // namespace gdn

@@ -198,6 +198,9 @@ WORKLOADS = {
     # the camera branch of the same video block (fp32): camera prep, then the forward and
     # the reverse numerator-only frame scans
     "cam_video_f16x1024": dict(kind="cam", B=1, F=16, S=1024, H=16, D=128, seed=0),
+    # backward of the camera branch's two frame scans at the same shape (fp32 tensors with the
+    # magnitudes of prepped ones, upstream gradient N(0, 1))
+    "cam_bwd_video_f16x1024": dict(kind="cam_bwd", B=1, F=16, S=1024, H=16, D=128, seed=0),
     "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
                                     dtype="bf16", seed=0, g_shift=3.0, per_key=True,
                                     save=True),
@@ -231,4 +234,6 @@ def make(name):
         return cam_inputs(**w)
     if kind == "dhu":
         return dhu_inputs(**w)
+    if kind == "cam_bwd":
+        return cam_scan_bwd_inputs(**w)
     raise KeyError(name)
