@@ -72,10 +72,11 @@ def _load():
         lib.oracle_cam_scan.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
         lib.oracle_gdn_dhu.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, Dd, P, P, P]
         lib.oracle_cam_scan_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_gdn_bwd_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, Dd, P, P]
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
-                     "oracle_gdn_transition"):
+                     "oracle_gdn_transition", "oracle_gdn_bwd_prep"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -343,3 +344,30 @@ def gdn_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, chunk=CHUNK, gk=None):
     if rc != 0:
         raise RuntimeError("oracle_gdn_dhu failed")
     return {"dh": dh, "dv2": dv2, "dh0": dh0}
+
+
+def gdn_bwd_prep(q, k, beta, do, g=None, gk=None, scale=1.0, chunk=CHUNK):
+    """Inputs of the state-gradient pass formed from the forward's inputs ([hyper-parallel
+    "Diff Coverage" page], the chunk state pass and its dhu backward): per chunk, the WY factor
+    w = (I + A)^-1 diag(beta) (e^gamma * K) and dv = P^T do, P the decayed causal Q K^T times
+    scale.  q, k [B,T,H,K]; beta, g [B,T,H]; gk [B,T,H,K]; do [B,T,H,V].  Returns w, dv."""
+    q, k, beta, do, g, gk = map(_f64, (q, k, beta, do, g, gk))
+    B, T, H, K = q.shape
+    V = do.shape[-1]
+    w = np.empty((B, T, H, K))
+    dv = np.empty((B, T, H, V))
+    rc = _load().oracle_gdn_bwd_prep(B, T, H, K, V, chunk, _p(q), _p(k), _p(beta), _p(g), _p(gk),
+                                     _p(do), float(scale), _p(w), _p(dv))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_bwd_prep failed")
+    return w, dv
+
+
+def apply_grad_summary(grad_ext, trans, grad_in=None):
+    """Gradient of the state entering a fragment from the gradient of the state leaving it
+    (the reverse summary of the context-parallel backward): grad_ext + M^T grad_in, with M the
+    fragment's transition (h_out = M h_in + state_ext).  [B,H,K,V] and [B,H,K,K] arrays."""
+    grad_ext = _f64(grad_ext)
+    if grad_in is None:
+        return grad_ext.copy()
+    return grad_ext + np.matmul(np.swapaxes(_f64(trans), -1, -2), _f64(grad_in))

@@ -838,3 +838,74 @@ int oracle_gdn_dhu(int B, int T, int H, int K, int V, int C, const double* q, co
   }
   return fail ? -1 : 0;
 }
+
+/*
+ * Inputs of the state-gradient pass formed from the forward's inputs, per chunk of C tokens
+ * ([hyper-parallel "Diff Coverage" page]: the WY factor w that the chunk state pass takes in
+ * v_new = u - w h, and the intra-chunk part of the gradient of v_new).  With gamma the
+ * chunk-local inclusive cumsum of lambda_{t,d} = g_t + gk_{t,d}:
+ *     A_{r,s} = beta_r sum_d k_{r,d} k_{s,d} e^{gamma_{r,d} - gamma_{s,d}}    (s < r, else 0)
+ *     w       = (I + A)^-1 diag(beta) (e^{gamma} * K)     (forward substitution, row by row)
+ *     P_{r,s} = scale sum_d q_{r,d} k_{s,d} e^{gamma_{r,d} - gamma_{s,d}}    (s <= r, else 0)
+ *     dv      = P^T do.
+ * q, k, w [B,T,H,K]; do_, dv [B,T,H,V]; beta, g [B,T,H] (g may be NULL); gk [B,T,H,K] or NULL.
+ */
+int oracle_gdn_bwd_prep(int B, int T, int H, int K, int V, int C, const double* q,
+                        const double* k, const double* beta, const double* g, const double* gk,
+                        const double* do_, double scale, double* w, double* dv) {
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || C <= 0) return -1;
+  const int NT = (T + C - 1) / C;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* gam = (double*)malloc(sizeof(double) * (size_t)C * K);
+    if (!gam) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1) collapse(2)
+      for (int bh = 0; bh < B * H; ++bh)
+        for (int n = 0; n < NT; ++n) {
+          const int b = bh / H, h = bh % H;
+          const int t0 = n * C, L = (T - t0 < C) ? T - t0 : C;
+#define TOK(i) (((long)b * T + t0 + (i)) * H + h)
+          for (int d = 0; d < K; ++d) {
+            double acc = 0.0;
+            for (int i = 0; i < L; ++i) {
+              acc += (g ? g[TOK(i)] : 0.0) + (gk ? gk[TOK(i) * K + d] : 0.0);
+              gam[(size_t)i * K + d] = acc;
+            }
+          }
+          /* w row r = beta_r e^{gamma_r} k_r - sum_{s<r} A_{r,s} w_s, rows in order */
+          for (int r = 0; r < L; ++r) {
+            const double br = beta[TOK(r)];
+            for (int d = 0; d < K; ++d)
+              w[TOK(r) * K + d] = br * exp(gam[(size_t)r * K + d]) * k[TOK(r) * K + d];
+            for (int s = 0; s < r; ++s) {
+              double a = 0.0;
+              for (int d = 0; d < K; ++d)
+                a += k[TOK(r) * K + d] * k[TOK(s) * K + d] *
+                     exp(gam[(size_t)r * K + d] - gam[(size_t)s * K + d]);
+              a *= br;
+              for (int d = 0; d < K; ++d) w[TOK(r) * K + d] -= a * w[TOK(s) * K + d];
+            }
+          }
+          /* dv_s = sum_{r >= s} P_{r,s} do_r */
+          for (int s = 0; s < L; ++s)
+            for (int c = 0; c < V; ++c) dv[TOK(s) * V + c] = 0.0;
+          for (int r = 0; r < L; ++r)
+            for (int s = 0; s <= r; ++s) {
+              double p = 0.0;
+              for (int d = 0; d < K; ++d)
+                p += q[TOK(r) * K + d] * k[TOK(s) * K + d] *
+                     exp(gam[(size_t)r * K + d] - gam[(size_t)s * K + d]);
+              p *= scale;
+              for (int c = 0; c < V; ++c) dv[TOK(s) * V + c] += p * do_[TOK(r) * V + c];
+            }
+#undef TOK
+        }
+    }
+    free(gam);
+  }
+  return fail ? -1 : 0;
+}

@@ -130,3 +130,41 @@ def test_dhu_without_final_gradient():
                        scale=s["scale"], chunk=C)
     for key in ("dh", "dv2", "dh0"):
         np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("gated,per_key", [(True, False), (False, False), (True, True)])
+def test_bwd_prep_forms_the_inputs_whose_pass_gives_the_gradient(gated, per_key):
+    """oracle.gdn_bwd_prep (w and P^T do from the forward's inputs) feeds oracle.gdn_dhu, and
+    the result must be dL/dh0 by central differences of the token-level forward."""
+    s = _setup(T=13, seed=3, gated=gated, per_key=per_key)
+    w, dv = oracle.gdn_bwd_prep(s["q"], s["k"], s["beta"], s["do"], g=s["g"], gk=s["gk"],
+                                scale=s["scale"], chunk=C)
+    r = oracle.gdn_dhu(s["q"], s["k"], w, s["do"], dv, g=s["g"], dht=s["dht"], scale=s["scale"],
+                       chunk=C, gk=s["gk"])
+    np.testing.assert_allclose(r["dh0"], _central(lambda h: _loss(s, h0=h), s["h0"]),
+                               rtol=1e-7, atol=1e-8)
+    # and the same w, dv as the definitions written out above (einsum form)
+    w2, dv2, _ = _wy_inputs(s)
+    np.testing.assert_allclose(w, w2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_reverse_summaries_join_to_the_whole_gradient(per_key):
+    """Context-parallel backward: fragments cut at any token (each with its own chunk grid)
+    give grad_state_ext = dh0 of the pass from a zero final gradient; walking the fragments
+    from the right with grad_in <- grad_ext + M^T grad_in (M the fragment's forward transition)
+    must give dL/dh0 of the whole run."""
+    s = _setup(T=23, seed=4, per_key=per_key)
+    cuts = [0, 6, 15, 23]
+    sl = lambda x, a, b: None if x is None else x[:, a:b]
+    g_in = s["dht"]
+    for a, b in reversed(list(zip(cuts[:-1], cuts[1:]))):
+        q, k, beta, do = (sl(s[n], a, b) for n in ("q", "k", "beta", "do"))
+        g, gk = sl(s["g"], a, b), sl(s["gk"], a, b)
+        w, dv = oracle.gdn_bwd_prep(q, k, beta, do, g=g, gk=gk, scale=s["scale"], chunk=C)
+        ext = oracle.gdn_dhu(q, k, w, do, dv, g=g, scale=s["scale"], chunk=C, gk=gk)["dh0"]
+        M = oracle.transition(k, beta, g=g, gk=gk)
+        g_in = oracle.apply_grad_summary(ext, M, g_in)
+    np.testing.assert_allclose(g_in, _central(lambda h: _loss(s, h0=h), s["h0"]),
+                               rtol=1e-7, atol=1e-8)

@@ -52,6 +52,12 @@ MUTATIONS = [
     ("dhu: sign of the w term", PINS_DHU,
      "dh[(size_t)r * V + c] += qr * do_[tk * V + c] - wr * dv2[tk * V + c];",
      "dh[(size_t)r * V + c] += qr * do_[tk * V + c] + wr * dv2[tk * V + c];"),
+    ("backward inputs: w without beta", PINS_DHU,
+     "w[TOK(r) * K + d] = br * exp(gam[(size_t)r * K + d]) * k[TOK(r) * K + d];",
+     "w[TOK(r) * K + d] = exp(gam[(size_t)r * K + d]) * k[TOK(r) * K + d];"),
+    ("backward inputs: P without its diagonal", PINS_DHU,
+     "            for (int s = 0; s <= r; ++s) {\n              double p = 0.0;",
+     "            for (int s = 0; s < r; ++s) {\n              double p = 0.0;"),
     ("camera backward: dv without beta", PINS_CBWD,
      "dv[base + (long)c * N + t] = bt * dd[c];", "dv[base + (long)c * N + t] = dd[c];"),
     ("camera backward: dk without the prediction term", PINS_CBWD,
