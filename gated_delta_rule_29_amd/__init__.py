@@ -18,8 +18,9 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi", "cam_scan_bwd", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
-           "gdn_abi_version", "gdn_last_error", "CHUNK"]
+           "cam_scan_bidi", "cam_scan_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
+           "gdn_state_grad_summary", "gdn_state_grad_apply", "gdn_abi_version",
+           "gdn_last_error", "CHUNK"]
 
 CHUNK = 64
 _DT = {torch.float32: _lib.DTYPE_F32, torch.bfloat16: _lib.DTYPE_BF16}
@@ -161,6 +162,24 @@ def gdn_state_apply(state_ext, transition, h_in=None):
                                      BH, K, V, _stream(dev))
     _lib.check(rc, "gdn_state_apply")
     return h_out
+
+
+def gdn_state_grad_apply(grad_state_ext, transition, grad_in=None):
+    """grad_out = transition^T @ grad_in + grad_state_ext per (b, h) (fp32 [.., K, V]); the
+    gradient of the state entering a fragment from that of the state leaving it."""
+    *lead, K, V = grad_state_ext.shape
+    BH = 1
+    for d in lead:
+        BH *= d
+    dev = grad_state_ext.device
+    _need(grad_state_ext, "grad_state_ext", tuple(lead) + (K, V), torch.float32, dev)
+    _need(transition, "transition", tuple(lead) + (K, K), torch.float32, dev)
+    _need(grad_in, "grad_in", tuple(lead) + (K, V), torch.float32, dev)
+    out = torch.empty_like(grad_state_ext)
+    rc = _lib.load().gdn_state_grad_apply(_ptr(grad_state_ext), _ptr(transition), _ptr(grad_in),
+                                          _ptr(out), BH, K, V, _stream(dev))
+    _lib.check(rc, "gdn_state_grad_apply")
+    return out
 
 
 def gdn_varlen_num_chunks(cu_seqlens_host) -> int:
@@ -466,6 +485,57 @@ def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, gk=None, want_d
                                  _DT[dt], _stream(dev))
     _lib.check(rc, "gdn_bwd_dhu")
     return {"dv2": dv2, "dh": dh, "dh0": dh0}
+
+
+def gdn_bwd_prep(q, k, beta, do, g=None, scale=1.0, *, gk=None):
+    """w [B,T,H,K] and dv = P^T do [B,T,H,V] per 64-token chunk (the inputs of gdn_bwd_dhu)
+    from q, k [B,T,H,K], beta, g [B,T,H] fp32 and do [B,T,H,V] (q's dtype).  Scalar gates
+    only (gk is refused by the library)."""
+    B, T, H, K = q.shape
+    V = do.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("q must be float32 or bfloat16")
+    _need(q, "q", (B, T, H, K), dt, dev)
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(do, "do", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(gk, "gk", (B, T, H, K), torch.float32, dev)
+    w = torch.empty(B, T, H, K, dtype=dt, device=dev)
+    dv = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    rc = _lib.load().gdn_bwd_prep(_ptr(q), _ptr(k), _ptr(beta), _ptr(g), _ptr(gk), _ptr(do),
+                                  float(scale), _ptr(w), _ptr(dv), B, T, H, K, V, _DT[dt],
+                                  _stream(dev))
+    _lib.check(rc, "gdn_bwd_prep")
+    return w, dv
+
+
+def gdn_state_grad_summary(q, k, w, do, dv, g=None, scale=1.0, *, gk=None):
+    """Reverse (gradient) summary of a fragment: the gradient of its entering state from its
+    own outputs alone, [B,H,K,V] fp32 (inputs as gdn_bwd_dhu)."""
+    B, T, H, K = q.shape
+    V = do.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("q must be float32 or bfloat16")
+    for t, name in ((q, "q"), (k, "k"), (w, "w")):
+        _need(t, name, (B, T, H, K), dt, dev)
+    _need(do, "do", (B, T, H, V), dt, dev)
+    _need(dv, "dv", (B, T, H, V), dt, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(gk, "gk", (B, T, H, K), torch.float32, dev)
+    lib = _lib.load()
+    ws_n = lib.gdn_state_grad_summary_workspace_bytes(B, T, H, V, _DT[dt])
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    out = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
+    rc = lib.gdn_state_grad_summary(_ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(dv), _ptr(g),
+                                    _ptr(gk), float(scale), _ptr(out), B, T, H, K, V, _DT[dt],
+                                    _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "gdn_state_grad_summary")
+    return out
 
 
 def gdn_bwd_dhu_varlen(q, k, w, do, dv, cu_seqlens, g=None, dht=None, scale=1.0, *, gk=None,

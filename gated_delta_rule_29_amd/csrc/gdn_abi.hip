@@ -695,6 +695,69 @@ int gdn_bwd_dhu(const void* q, const void* k, const void* w, const void* do_, co
   return ok();
 }
 
+int gdn_bwd_prep(const void* q, const void* k, const float* beta, const float* g, const float* gk,
+                 const void* do_, float scale, void* w, void* dv, int B, int T, int H, int K, int V,
+                 int dtype, void* stream) {
+  if (!q || !k || !beta || !do_ || !w || !dv)
+    return fail(GDN_ERR_INVALID, "q, k, beta, do, w and dv must be non-null");
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID, "B, T, H, K, V must be positive (got %d, %d, %d, %d, %d)", B, T,
+                H, K, V);
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID, "dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16, got %d", dtype);
+  if ((K != 64 && K != 128) || (V != 64 && V != 128))
+    return fail(GDN_ERR_UNSUPPORTED, "K and V must be 64 or 128 (got %d, %d)", K, V);
+  if (gk) return fail(GDN_ERR_UNSUPPORTED, "gdn_bwd_prep takes scalar gates only (gk must be NULL)");
+  if ((int64_t)B * H * ((T + GDN_CHUNK - 1) / GDN_CHUNK) > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "B*H*chunks exceeds the grid limit");
+  gdn::BwdPrepParams p{};
+  p.q = q; p.k = k; p.beta = beta; p.g = g; p.do_ = do_; p.scale = scale; p.w = w; p.dv = dv;
+  p.B = B; p.T = T; p.H = H;
+  hipError_t e = gdn::launch_bwd_prep(p, K, V, dtype == GDN_DTYPE_F32 ? 0 : 1,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_bwd_prep launch");
+  return ok();
+}
+
+size_t gdn_state_grad_summary_workspace_bytes(int B, int T, int H, int V, int dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || V <= 0 || (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16))
+    return 0;
+  return al256((size_t)B * T * H * V * (dtype == GDN_DTYPE_BF16 ? 2 : 4));
+}
+
+int gdn_state_grad_summary(const void* q, const void* k, const void* w, const void* do_,
+                           const void* dv, const float* g, const float* gk, float scale,
+                           float* grad_state_ext, int B, int T, int H, int K, int V, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!grad_state_ext) return fail(GDN_ERR_INVALID, "grad_state_ext must be non-null");
+  if (T <= 0) return fail(GDN_ERR_INVALID, "a state summary needs a nonempty fragment (T = %d)", T);
+  if (B <= 0 || H <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID, "B, H, K, V must be positive (got %d, %d, %d, %d)", B, H, K, V);
+  const size_t need = gdn_state_grad_summary_workspace_bytes(B, T, H, V, dtype);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  return gdn_bwd_dhu(q, k, w, do_, dv, g, gk, nullptr, scale, nullptr, workspace, grad_state_ext,
+                     B, T, H, K, V, dtype, stream);
+}
+
+int gdn_state_grad_apply(const float* grad_state_ext, const float* transition, const float* grad_in,
+                         float* grad_out, int BH, int K, int V, void* stream) {
+  if (!grad_state_ext || !grad_out || (grad_in && !transition))
+    return fail(GDN_ERR_INVALID, "grad_state_ext and grad_out must be non-null, and transition too when grad_in is");
+  if (BH <= 0 || K <= 0 || V <= 0) return fail(GDN_ERR_INVALID, "BH, K, V must be positive (got %d, %d, %d)", BH, K, V);
+  if (K > gdn::kApplyMaxK) return fail(GDN_ERR_UNSUPPORTED, "K must be <= %d, got %d", gdn::kApplyMaxK, K);
+  if (BH > 65535) return fail(GDN_ERR_INVALID, "BH must be <= 65535, got %d", BH);
+  const uintptr_t bytes = (uintptr_t)BH * K * V * 4;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(grad_out), b0 = reinterpret_cast<uintptr_t>(grad_in);
+  if (grad_in && a0 < b0 + bytes && b0 < a0 + bytes) return fail(GDN_ERR_INVALID, "grad_out must not overlap grad_in");
+  hipError_t e = gdn::launch_grad_apply(grad_state_ext, transition, grad_in, grad_out, BH, K, V,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_state_grad_apply launch");
+  return ok();
+}
+
 size_t gdn_bwd_dhu_varlen_workspace_bytes(int N, int NT_total) {
   if (N <= 0 || NT_total <= 0) return 0;
   return al256((size_t)(N + 1) * 4) + al256((size_t)NT_total * 2 * 4);

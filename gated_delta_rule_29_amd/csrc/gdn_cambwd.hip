@@ -41,30 +41,14 @@ namespace {
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// x = hi + lo as a bf16 pair: hi = bf16(x), lo = bf16(x - hi)
-#define SPLIT1(x, H, L)              \
-  do {                               \
-    const float x_ = (x);            \
-    H = (bf16)x_;                    \
-    L = (bf16)(x_ - (float)(bf16)H); \
-  } while (0)
-
 // 8 fp32 at p (32-byte aligned), times s[j], as a hi/lo bf16 pair
 __device__ __forceinline__ void ld_split8(const float* p, const float* s, bf16x8& h, bf16x8& l) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    SPLIT1(s ? a[j] * s[j] : a[j], h[j], l[j]);
-    SPLIT1(s ? b[j] * s[4 + j] : b[j], h[4 + j], l[4 + j]);
+    GDN_SPLIT(s ? a[j] * s[j] : a[j], h[j], l[j]);
+    GDN_SPLIT(s ? b[j] * s[4 + j] : b[j], h[4 + j], l[4 + j]);
   }
-}
-
-// c + (ah + al)(bh + bl) without the al bl term
-__device__ __forceinline__ f32x4 mma3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
-                                      const bf16x8& bl, f32x4 c) {
-  c = mma16(al, bh, c);
-  c = mma16(ah, bl, c);
-  return mma16(ah, bh, c);
 }
 
 // ---- stats: G_f, U_f, W_f ----------------------------------------------------------------
@@ -163,7 +147,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
         for (int e = 0; e < 4; ++e) {
           const float x = st[16 * c + li][i0 + e];
           if (f32) f32[(size_t)(i0 + e) * D + j] = x;
-          SPLIT1(x, ch[e], cl[e]);
+          GDN_SPLIT(x, ch[e], cl[e]);
           m[(size_t)(i0 + e) * D + j] = ch[e];
           m[p.lo + (size_t)(i0 + e) * D + j] = cl[e];
         }
@@ -287,8 +271,8 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
 #pragma unroll 4
     for (int c = 2 * cg; c < D; c += 8) {
       bf16x2 h, l;
-      SPLIT1(x[base + (long)c * N + t0 + t], h[0], l[0]);
-      SPLIT1(x[base + (long)(c + 1) * N + t0 + t], h[1], l[1]);
+      GDN_SPLIT(x[base + (long)c * N + t0 + t], h[0], l[0]);
+      GDN_SPLIT(x[base + (long)(c + 1) * N + t0 + t], h[1], l[1]);
       *reinterpret_cast<bf16x2*>(&H[t * kT + c]) = h;
       *reinterpret_cast<bf16x2*>(&L[t * kT + c]) = l;
     }
@@ -297,7 +281,7 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
   auto put = [&](int T, int t, int i0, const float (&x)[4]) {
     bf16x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) SPLIT1(x[e], h[e], l[e]);
+    for (int e = 0; e < 4; ++e) GDN_SPLIT(x[e], h[e], l[e]);
     *reinterpret_cast<bf16x4*>(&tl[T][0][t * kT + i0]) = h;
     *reinterpret_cast<bf16x4*>(&tl[T][1][t * kT + i0]) = l;
   };

@@ -14,6 +14,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace gdn {
@@ -109,6 +111,41 @@ constexpr float kGateFloor = -40.f;
 constexpr float kKeyGateFloor = -10.f;
 __device__ __forceinline__ float floor_gate(float g) { return fmaxf(g, kGateFloor); }
 __device__ __forceinline__ float floor_key_gate(float lam) { return fmaxf(lam, kKeyGateFloor); }
+
+// Split bf16 operands.  x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) keeps about 16
+// mantissa bits and fp32's exponent range; a product of two split operands is summed as
+// hi*hi + hi*lo + lo*hi (the lo*lo term is below 2^-16 of the result).
+#define GDN_SPLIT(x, H, L)           \
+  do {                               \
+    const float x_ = (x);            \
+    H = (bf16)x_;                    \
+    L = (bf16)(x_ - (float)(bf16)H); \
+  } while (0)
+
+// c + (ah + al)(bh + bl) without the al bl term
+__device__ __forceinline__ f32x4 mma3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                      const bf16x8& bl, f32x4 c) {
+  c = mma16(al, bh, c);
+  c = mma16(ah, bl, c);
+  return mma16(ah, bh, c);
+}
+
+// 8 consecutive inputs as fp32
+template <typename TI>
+__device__ __forceinline__ void load8f(const TI* p, float (&x)[8]) {
+  if constexpr (std::is_same<TI, float>::value) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  } else {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
+  }
+}
 
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x, int lane) {

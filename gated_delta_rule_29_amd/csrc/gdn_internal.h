@@ -177,6 +177,23 @@ struct DhuParams {
   int nt_total;
 };
 hipError_t launch_dhu(const DhuParams& p, int dtype, hipStream_t stream);  // K = 128; dtype 0 fp32, 1 bf16
+// Inputs of the state-gradient pass (gdn_bwdprep.hip): w [B,T,H,K] and dv = P^T do [B,T,H,V]
+// from q, k [B,T,H,K], beta, g [B,T,H] (g may be null) and do [B,T,H,V]; scalar gate only.
+struct BwdPrepParams {
+  const void* q;
+  const void* k;
+  const float* beta;
+  const float* g;
+  const void* do_;
+  float scale;
+  void* w;
+  void* dv;
+  int B, T, H;
+};
+hipError_t launch_bwd_prep(const BwdPrepParams& p, int K, int V, int dtype, hipStream_t stream);
+// grad_out = grad_ext + M^T grad_in (grad_in may be null: zero)
+hipError_t launch_grad_apply(const float* grad_ext, const float* M, const float* grad_in,
+                             float* grad_out, int BH, int K, int V, hipStream_t stream);
 
 // backward of the camera-branch scan (gdn_cambwd.hip)
 struct CamBwdParams {

@@ -40,7 +40,9 @@ __global__ __launch_bounds__(256) void identity_kernel(float* m, long BH, int K)
 // h_out = M h_in + c per (b, h): one workgroup per (bh, 16 output rows); the 16 rows of M
 // are staged in LDS, each thread forms outputs (row, column) with column-contiguous loads of
 // h_in.  fp32 throughout.
+// With TR the map is h_out = M^T h_in + c (the gradient form): the staged rows are columns of M.
 constexpr int kApplyRows = 16;
+template <bool TR>
 __global__ __launch_bounds__(256) void apply_kernel(const float* c, const float* M, const float* h_in,
                                                     float* h_out, int K, int V) {
   __shared__ float ms[kApplyRows][kApplyMaxK];
@@ -48,8 +50,13 @@ __global__ __launch_bounds__(256) void apply_kernel(const float* c, const float*
   const int r0 = blockIdx.x * kApplyRows;
   const int rows = min(kApplyRows, K - r0);
   if (h_in) {
-    for (int e = threadIdx.x; e < rows * K; e += 256)
-      ms[e / K][e % K] = M[(bh * K + r0 + e / K) * K + e % K];
+    if (TR) {
+      for (int e = threadIdx.x; e < rows * K; e += 256)
+        ms[e % rows][e / rows] = M[(bh * K + e / rows) * K + r0 + e % rows];
+    } else {
+      for (int e = threadIdx.x; e < rows * K; e += 256)
+        ms[e / K][e % K] = M[(bh * K + r0 + e / K) * K + e % K];
+    }
     __syncthreads();
   }
   const float* hb = h_in ? h_in + bh * K * V : nullptr;
@@ -231,44 +238,11 @@ __global__ __launch_bounds__(256) void transition_kernel(const TI* __restrict__ 
 // Mt = prod_n (I - K_n^T W_n) over the 64-token chunks n in order, W_n = Tm diag(beta) K_n and
 // Tm = (I + strict_lower(diag(beta) K_n K_n^T))^-1 (the WY form of an ungated chunk: its
 // deltas are U - W S for the state S entering it).  trans_wy_kernel forms every chunk's W_n in
-// parallel; trans_chain_kernel walks a chain's chunks for 32 columns of Mt.  Products split
-// each fp32 operand into a bf16 pair x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) and sum
-// hi*hi + hi*lo + lo*hi: about 16 mantissa bits with fp32's exponent range (bf16 keys are
-// exact, lo = 0).  With unit keys and beta in [0, 1] every factor has spectral norm <= 1.
-
-// x = hi + lo as a bf16 pair
-#define GDN_SPLIT(x, H, L)           \
-  do {                               \
-    const float x_ = (x);            \
-    H = (bf16)x_;                    \
-    L = (bf16)(x_ - (float)(bf16)H); \
-  } while (0)
+// parallel; trans_chain_kernel walks a chain's chunks for 32 columns of Mt.  Products take
+// split bf16 operands (GDN_SPLIT; bf16 keys are exact, lo = 0).  With unit keys and beta in
+// [0, 1] every factor has spectral norm <= 1.
 
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// 8 consecutive inputs as fp32
-template <typename TI>
-__device__ __forceinline__ void load8f(const TI* p, float (&x)[8]) {
-  if constexpr (std::is_same<TI, float>::value) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j] = a[j];
-      x[4 + j] = b[j];
-    }
-  } else {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
-  }
-}
-
-__device__ __forceinline__ f32x4 mma3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
-                                      const bf16x8& bl, f32x4 c) {
-  c = mma16(al, bh, c);
-  c = mma16(ah, bl, c);
-  return mma16(ah, bh, c);
-}
 
 // Workgroup ids are dealt to the eight XCDs round-robin; with a grid that is a multiple of
 // eight, logical neighbours (the column blocks of one chain) land on one XCD's L2.
@@ -613,8 +587,6 @@ __global__ __launch_bounds__(256) void trans_chain_kernel(const float* __restric
         out[(size_t)(16 * (RT * w + rt) + 4 * lq + e) * K + 32 * cb + 16 * c + li] = m[rt][c][e] * sc;
 }
 
-#undef GDN_SPLIT
-
 }  // namespace
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
@@ -680,8 +652,15 @@ size_t transition_ws_bytes(int B, int T, int H, int K, int dtype, bool per_key) 
 
 hipError_t launch_apply(const float* c, const float* M, const float* h_in, float* h_out, int BH,
                         int K, int V, hipStream_t stream) {
-  hipLaunchKernelGGL(apply_kernel, dim3((K + kApplyRows - 1) / kApplyRows, BH), dim3(256), 0, stream,
-                     c, M, h_in, h_out, K, V);
+  hipLaunchKernelGGL(apply_kernel<false>, dim3((K + kApplyRows - 1) / kApplyRows, BH), dim3(256), 0,
+                     stream, c, M, h_in, h_out, K, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_apply(const float* grad_ext, const float* M, const float* grad_in,
+                             float* grad_out, int BH, int K, int V, hipStream_t stream) {
+  hipLaunchKernelGGL(apply_kernel<true>, dim3((K + kApplyRows - 1) / kApplyRows, BH), dim3(256), 0,
+                     stream, grad_ext, M, grad_in, grad_out, K, V);
   return hipGetLastError();
 }
 

@@ -19,10 +19,12 @@
  *    in both directions (bigdn_fwd) and the block output with reverse-direction overrides and
  *    the merge (bigdn_fwd_merged);
  *  - a fragment's state summary and the joining of fragments (gdn_state_summary,
- *    gdn_state_apply), the single-GPU part of context parallelism;
+ *    gdn_state_apply), and their gradient counterparts (gdn_state_grad_summary,
+ *    gdn_state_grad_apply): the single-GPU part of context parallelism;
  *  - the camera branch of the video block (cam_prep, cam_scan, cam_scan_bidi) and the
  *    backward of its scan (cam_scan_bwd);
- *  - the backward's state-gradient pass (gdn_bwd_dhu, gdn_bwd_dhu_varlen).
+ *  - the backward's inputs (gdn_bwd_prep) and state-gradient pass (gdn_bwd_dhu,
+ *    gdn_bwd_dhu_varlen).
  *
  * Conventions shared by every entry point.
  *  - All tensor pointers are DEVICE pointers unless the name ends in _host.  The caller owns
@@ -57,7 +59,7 @@ extern "C" {
 #define GDN_API
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 #define GDN_CHUNK 64
 
 /* Status codes (the pages' wrappers raise ValueError / NotImplementedError / RuntimeError
@@ -215,9 +217,13 @@ GDN_API int gdn_prep(const void* qkv, const float* q_norm_w, const float* k_norm
  *                                                                    [B,H,K,K] fp32 OUT
  *   k [B,T,H,K], v [B,T,H,V] (dtype), g [B,T,H] or NULL, gk [B,T,H,K] or NULL, beta [B,T,H]
  *   as in gdn_fwd (q is not needed).  transition may be NULL (not formed).  state_ext comes
- *   from the forward kernels; the transition from an fp32 kernel that keeps a power-of-two
- *   exponent per column (it decays like the product of all the fragment's decays, so values
- *   below fp32 range become zero, as they would in any fp32 result).
+ *   from the forward kernels.  The transition decays like the product of all the fragment's
+ *   decays, so values below fp32 range become zero, as they would in any fp32 result.  With a
+ *   scalar (or no) gate it is e^{sum_t g_t} times the ordered product of the ungated chunk
+ *   maps I - K^T W (W = Tm diag(beta) K, the chunk's WY factor), formed on matrix cores with
+ *   split bf16 operands (each fp32 value as hi + lo, about 16 mantissa bits, fp32's exponent
+ *   range); with a per-key gate it is the token recurrence in fp32 with a power-of-two
+ *   exponent per column.
  *   workspace  at least gdn_state_summary_workspace_bytes(B, T, H, K, V, dtype, flags)
  *              (flags = GDN_FWD_PER_KEY if gk is given)
  *              bytes, 256-byte aligned, caller-owned
@@ -240,6 +246,36 @@ GDN_API int gdn_state_summary(const void* k, const void* v, const float* g, cons
  */
 GDN_API int gdn_state_apply(const float* state_ext, const float* transition, const float* h_in,
                             float* h_out, int BH, int K, int V, void* stream);
+
+/*
+ * gdn_state_grad_summary -- the reverse (gradient) summary of one fragment, for the
+ * context-parallel backward (the KDA state-gradient summary of the hyper-parallel "Diff
+ * Coverage" page): the gradient of the loss with respect to the state entering the fragment,
+ * counting only the fragment's own outputs (a zero gradient for the state leaving it),
+ *     grad_state_ext = dh0 of gdn_bwd_dhu with dht = 0           [B,H,K,V] fp32 OUT.
+ * The gradient for a nonzero gradient of the leaving state follows from gdn_state_grad_apply
+ * with the fragment's forward transition.  Inputs, dtype, gates, Supported and errors as
+ * gdn_bwd_dhu (q, k, w, do_, dv of the fragment alone, with its own 64-token chunk grid).
+ *   workspace  at least gdn_state_grad_summary_workspace_bytes(B, T, H, V, dtype) bytes,
+ *              256-byte aligned (the pass's per-token dv2, which is not returned)
+ */
+GDN_API size_t gdn_state_grad_summary_workspace_bytes(int B, int T, int H, int V, int dtype);
+GDN_API int gdn_state_grad_summary(const void* q, const void* k, const void* w, const void* do_,
+                                   const void* dv, const float* g, const float* gk, float scale,
+                                   float* grad_state_ext, int B, int T, int H, int K, int V,
+                                   int dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * gdn_state_grad_apply -- joins a fragment's gradient to the gradient after it: per (b, h),
+ *     grad_out = transition^T grad_in + grad_state_ext     ([K,K]^T x [K,V] + [K,V], fp32)
+ * where transition is the fragment's forward transition (gdn_state_summary) and grad_in the
+ * gradient of the state leaving the fragment (NULL = zero).  grad_out is the gradient of the
+ * state entering it.  Layouts, Supported and errors as gdn_state_apply.
+ */
+GDN_API int gdn_state_grad_apply(const float* grad_state_ext, const float* transition,
+                                 const float* grad_in, float* grad_out, int BH, int K, int V,
+                                 void* stream);
 
 /*
  * bigdn_fwd -- frame-level bidirectional GDN block forward (SANA fused_gdn.py page,
@@ -388,6 +424,23 @@ GDN_API int cam_scan_bwd(const float* q, const float* k, const float* v, const f
                          const float* decay, const float* dout, int reverse, float* dq,
                          float* dk, float* dv, float* dbeta, float* ddecay, int B, int H, int D,
                          int F, int S, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_bwd_prep -- the inputs of the state-gradient pass, from the forward's inputs
+ * ([hyper-parallel "Diff Coverage" page]: the chunk state pass v_new = u - w h and its dhu
+ * backward).  Per 64-token chunk, gamma the chunk-local inclusive cumsum of g:
+ *     A_{r,s} = beta_r e^{gamma_r - gamma_s} (k_r . k_s)   (s < r)
+ *     w       = (I + A)^-1 diag(beta e^gamma) K                      [B,T,H,K] OUT (dtype)
+ *     P_{r,s} = scale e^{gamma_r - gamma_s} (q_r . k_s)    (s <= r)
+ *     dv      = P^T do                                               [B,T,H,V] OUT (dtype)
+ *   q, k [B,T,H,K], do_ [B,T,H,V] (dtype); beta, g [B,T,H] fp32 (g NULL: no decay); gk must
+ *   be NULL.  Products take split bf16 operands with fp32 accumulation, so the results are
+ *   near fp32 before they are stored in dtype.
+ * Supported: K, V in {64, 128}; scalar gates (GDN_ERR_UNSUPPORTED for gk).
+ */
+GDN_API int gdn_bwd_prep(const void* q, const void* k, const float* beta, const float* g,
+                         const float* gk, const void* do_, float scale, void* w, void* dv, int B,
+                         int T, int H, int K, int V, int dtype, void* stream);
 
 /*
  * gdn_bwd_dhu -- state-gradient pass of the chunked backward ([hyper-parallel "Diff Coverage"

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, "binding lacks %s" % n
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first

@@ -53,6 +53,18 @@ def gdn_inputs(B, T, H, K, V, dtype="bf16", seed=0, g_shift=3.0, per_key=False,
     return {"q": q, "k": k, "v": v, "beta": beta, "g": g, "gk": gk}
 
 
+def bwd_inputs(B, T, H, K, V, dtype="bf16", seed=0, g_shift=3.0):
+    """Inputs of the backward chain (gdn_bwd_prep, then gdn_bwd_dhu): gdn_inputs, then from
+    seed + 7919 the output gradient do ~ N(0, 1) [B,T,H,V] in dtype and the final-state
+    gradient dht ~ N(0, 1) [B,H,K,V] fp32; scale K^-1/2."""
+    inp = gdn_inputs(B, T, H, K, V, dtype=dtype, seed=seed, g_shift=g_shift)
+    gen = _gen(seed + 7919)
+    inp["do"] = torch.randn(B, T, H, V, generator=gen).to(DTYPES[dtype])
+    inp["dht"] = torch.randn(B, H, K, V, generator=gen)
+    inp["scale"] = K ** -0.5
+    return inp
+
+
 def varlen_lengths(n_seqs, lo, hi, seed):
     """Sequence lengths uniform in [lo, hi] (inclusive), drawn first from the seed."""
     gen = _gen(seed)
