@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-FP32_VALU_PEAK_TFLOPS = 157.3  # published fp32 vector peak (packed fp32 FMA, 256 CUs, 2.4 GHz)
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # published dense bf16 matrix-core peak
 METRIC = "tokens·heads/sec for chunked gated delta-rule fwd; % MFMA (or HBM) peak"
 KERNEL_SOURCE_DIR = "gated_delta_rule_29_amd/csrc"
 # The kernels one forward call launches; the roofline covers the whole call (every kernel on
@@ -48,8 +48,23 @@ def kernels_of(dt, per_key, save):
     if per_key:
         return KERNELS_BF16_PK
     return KERNELS_BF16 if save else KERNELS_FUSED
-COUNTER_FILE = "profiles/fused16_kernel_b4h16t4096_hbm_counters.md"
+COUNTER_FILE = "profiles/all_workloads_counters.md"
 
+# The .hip files that define and launch each workload's kernels; their hash (with every local
+# header they include) stamps the counter summary, which is used only while it matches.
+SOURCES = {
+    KERNELS_FUSED: ["gdn_fwd.hip", "gdn_fused16.hip"],
+    KERNELS_FUSED_PACKED: ["gdn_fwd.hip", "gdn_fused16.hip"],
+    KERNELS_BF16: ["gdn_fwd.hip", "gdn_prep16.hip", "gdn_scan16.hip"],
+    KERNELS_BF16_PK: ["gdn_fwd.hip", "gdn_prep16.hip", "gdn_scan16.hip"],
+    KERNELS_F32: ["gdn_fwd.hip"],
+    "bigdn": ["gdn_bigdn.hip"],
+    "bigdn_merged": ["gdn_bigdn.hip"],
+    "cam": ["gdn_cam.hip", "gdn_bigdn.hip"],
+    "cam_bwd": ["gdn_cambwd.hip"],
+    "summary": ["gdn_fwd.hip", "gdn_fused16.hip", "gdn_summary.hip"],
+    "dhu": ["gdn_bwd.hip"],
+}
 
 def alg_bytes_per_launch(B, T, H, K, V, elt=2, per_key=False, save=False, n_states=None,
                          n_chunks=None):
@@ -105,30 +120,38 @@ def alg_bytes_dhu(B, T, H, K, V, elt):
             + B * T * H * V * elt + B * H * NT * K * V * 4 + B * H * K * V * 4)
 
 
-def kernel_source_hash():
-    """Hash of every kernel source: a counter summary is valid only for the code it measured."""
-    h = hashlib.sha256()
+def kernel_source_hash(files):
+    """Hash of the given kernel sources and of every local header they include (transitively):
+    a counter summary is valid only for the code it measured."""
     d = os.path.join(ROOT, KERNEL_SOURCE_DIR)
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+    seen, todo = set(), list(files)
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        with open(os.path.join(d, name)) as f:
+            todo += re.findall(r'^#include "([^"]+)"', f.read(), flags=re.M)
+    h = hashlib.sha256()
+    for name in sorted(seen):
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source (else None)."""
+def measured_traffic(workload, files):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on the
+    current sources of the workload's kernels (else None).  Lines of the form
+    `traffic <workload> <bytes per call> <source hash>`."""
     path = os.path.join(ROOT, COUNTER_FILE)
     if not os.path.exists(path):
         return None
-    text = open(path).read()
-    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+    m = re.search(r"^traffic %s ([0-9.eE+]+) ([0-9a-f]+)$" % re.escape(workload), open(path).read(),
+                  flags=re.M)
+    if not m or m.group(2) != kernel_source_hash(files):
         return None
-    return float(m_b.group(1))
+    return float(m.group(1))
 
 
 def _cpu_time(fn, sample, th):
@@ -320,10 +343,12 @@ def main():
         V = inp["v"].shape[-1]
         dt = inp["q"].dtype
         th = B * T * H
-        # the transition's token recurrence: decay (K^2), k^T M (2K^2) and the rank-one
-        # update (2K^2) flops per token and chain
-        alg = 5 * K * K * th
-        kernel = "gdn_state_summary call: fused16_kernel (zero-start state) + transition_kernel"
+        # the transition's chunked products per token and chain: X = W M and M -= K^T X,
+        # 2 K^2 flops each (the split-operand form takes 3 matrix-core products per product, 2
+        # with bf16 keys; counted once here)
+        alg = 4 * K * K * th
+        kernel = ("gdn_state_summary call: fused16_kernel (zero-start state) + trans_wy_kernel + "
+                  "trans_chain_kernel")
         config = {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
                   "state": "fp32", "outputs": "state_ext [B,H,K,V] + transition [B,H,K,K]"}
 
@@ -445,13 +470,14 @@ def main():
     value = th / (ms_per_step / 1e3)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     achieved = alg / avg_launch_s / 1e9
-    if kind == "summary":  # flop-bound: alg counts flops, reported in TFLOP/s
-        roof = {"bound": "alu", "achieved": achieved / 1e3, "peak": FP32_VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / 1e3 / FP32_VALU_PEAK_TFLOPS}
+    if kind == "summary":  # matrix-core work: alg counts flops, reported in TFLOP/s
+        roof = {"bound": "mfma", "achieved": achieved / 1e3, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / 1e3 / BF16_MFMA_PEAK_TFLOPS}
     else:
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
-    traffic = measured_traffic(alg) if args.workload == "gdn_bf16_b4h16t4096" else None
+    files = SOURCES.get(kernel if kind in ("gdn", "varlen") else kind)
+    traffic = measured_traffic(args.workload, files) if files else None
     out = {
         "metric": METRIC,
         "value": value,
