@@ -73,10 +73,11 @@ def _load():
         lib.oracle_gdn_dhu.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, Dd, P, P, P]
         lib.oracle_cam_scan_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_gdn_bwd_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, Dd, P, P]
+        lib.oracle_bigdn_dir_bwd.argtypes = [I, I, I, I, I, I] + [P] * 16
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
-                     "oracle_gdn_transition", "oracle_gdn_bwd_prep"):
+                     "oracle_gdn_transition", "oracle_gdn_bwd_prep", "oracle_bigdn_dir_bwd"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -229,6 +230,27 @@ def bigdn_dir(q_rot, k_rot, q_pos, k_pos, v, beta, decay, reverse):
     if rc != 0:
         raise RuntimeError("oracle_bigdn_dir failed")
     return num, den
+
+
+def bigdn_dir_bwd(q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden, reverse):
+    """Backward of one BiGDN direction (SANA fused_gdn.py page, "Backward / autograd
+    Functions"): gradients of sum(num * dnum) + sum(den * dden) for (num, den) =
+    bigdn_dir(...).  Returns dict dq_rot, dk_rot, dq_pos, dk_pos, dv [B,H,N,D], dbeta
+    [B,H,F,S], ddecay [B,H,F]."""
+    q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden = map(
+        _f64, (q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden))
+    B, H, N, D = q_rot.shape
+    F, S = beta.shape[2], beta.shape[3]
+    out = {n: np.empty((B, H, N, D)) for n in ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv")}
+    out["dbeta"] = np.empty((B, H, F, S))
+    out["ddecay"] = np.empty((B, H, F))
+    rc = _load().oracle_bigdn_dir_bwd(
+        B, F, S, H, D, int(bool(reverse)), *(_p(x) for x in (q_rot, k_rot, q_pos, k_pos, v, beta,
+                                                              decay, dnum, dden)),
+        *(_p(out[n]) for n in ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv", "dbeta", "ddecay")))
+    if rc != 0:
+        raise RuntimeError("oracle_bigdn_dir_bwd failed")
+    return out
 
 
 def bigdn(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, eps=1e-5):

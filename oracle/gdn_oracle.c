@@ -909,3 +909,184 @@ int oracle_gdn_bwd_prep(int B, int T, int H, int K, int V, int C, const double* 
   }
   return fail ? -1 : 0;
 }
+
+/*
+ * Backward of one BiGDN direction (SANA fused_gdn.py page, "Backward / autograd Functions":
+ * the reverse replay of the frame recurrence behind FusedBiGDNFunction.backward): gradients of
+ * L = sum(num * dnum) + sum(den * dden) for (num, den) = oracle_bigdn_dir(..., reverse).
+ * With A and a the gradients of S and z after a step's update (num_s = S^T q_rot_s and
+ * den_s = q_pos_s . z of the step's output frame), per step in reverse:
+ *   A += sum_s q_rot_s dnum_s^T,  a += sum_s dden_s q_pos_s;
+ *   dq_rot_s = S dnum_s,  dq_pos_s = dden_s z                       (output frame's tokens)
+ * and, when the step absorbs frame fa with decay g from the states S_prev, z_prev
+ * (S_pre = g S_prev, z_pre = g z_prev), for its tokens s:
+ *   r_s = v_s - S_pre^T k_rot_s,  dd_s = A^T k_rot_s:
+ *     dv_s = beta_s dd_s,  dk_rot_s = A (beta_s r_s) - beta_s S_pre dd_s
+ *   e_s = 1 - k_pos_s . z_pre,    ee_s = a . k_pos_s:
+ *     dk_pos_s = a (beta_s e_s) - beta_s ee_s z_pre
+ *   dbeta_s = dd_s . r_s + ee_s e_s
+ *   dS_pre = A - sum_s beta_s k_rot_s dd_s^T,  dz_pre = a - sum_s beta_s ee_s k_pos_s
+ *   ddecay[fa] = <dS_pre, S_prev> + <dz_pre, z_prev>;  A = g dS_pre,  a = g dz_pre.
+ * Frames that are never absorbed (frame 0 of the reverse direction) get zero k, v and beta
+ * gradients and ddecay 0.  Layouts as oracle_bigdn_dir; dnum [B,N,H,D], dden [B,H,N];
+ * outputs dq_rot, dk_rot, dq_pos, dk_pos, dv [B,H,N,D], dbeta [B,H,F,S], ddecay [B,H,F].
+ */
+int oracle_bigdn_dir_bwd(int B, int F, int S_, int H, int D, int reverse, const double* q_rot,
+                         const double* k_rot, const double* q_pos, const double* k_pos,
+                         const double* v, const double* beta, const double* decay,
+                         const double* dnum, const double* dden, double* dq_rot,
+                         double* dk_rot, double* dq_pos, double* dk_pos, double* dv,
+                         double* dbeta, double* ddecay) {
+  if (B <= 0 || F <= 0 || S_ <= 0 || H <= 0 || D <= 0) return -1;
+  const long N = (long)F * S_;
+  const size_t DD = (size_t)D * D;
+  int fail = 0;
+#pragma omp parallel
+  {
+    /* states after every step (S, z), the running gradients, scratch vectors */
+    double* Ss = (double*)malloc(sizeof(double) * DD * F);
+    double* zs = (double*)malloc(sizeof(double) * (size_t)D * F);
+    double* A = (double*)malloc(sizeof(double) * DD);
+    double* dSp = (double*)malloc(sizeof(double) * DD);
+    double* a = (double*)malloc(sizeof(double) * D);
+    double* dzp = (double*)malloc(sizeof(double) * D);
+    double* Sp = (double*)malloc(sizeof(double) * DD);
+    double* zp = (double*)malloc(sizeof(double) * D);
+    double* vec = (double*)malloc(sizeof(double) * 3 * D);
+    if (!Ss || !zs || !A || !dSp || !a || !dzp || !Sp || !zp || !vec) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        const long base = (long)bh * N * D;
+        /* forward replay, keeping the state after every step */
+        double* St = Sp; /* reused below; the replay's running state */
+        memset(St, 0, sizeof(double) * DD);
+        memset(zp, 0, sizeof(double) * D);
+        for (int it = 0; it < F; ++it) {
+          const int f = reverse ? F - 1 - it : it;
+          if (!reverse || it > 0) {
+            const int fa = reverse ? f + 1 : f;
+            const double g = decay[(long)bh * F + fa];
+            for (size_t e = 0; e < DD; ++e) St[e] *= g;
+            for (int r = 0; r < D; ++r) zp[r] *= g;
+            const long t0 = (long)fa * S_;
+            absorb_frame(S_, D, k_rot + base + t0 * D, k_pos + base + t0 * D, v + base + t0 * D,
+                         beta + (long)bh * N + t0, St, zp, dSp, dzp, vec);
+          }
+          memcpy(Ss + (size_t)it * DD, St, sizeof(double) * DD);
+          memcpy(zs + (size_t)it * D, zp, sizeof(double) * D);
+        }
+        /* reverse pass */
+        memset(A, 0, sizeof(double) * DD);
+        memset(a, 0, sizeof(double) * D);
+        for (int it = F - 1; it >= 0; --it) {
+          const int f = reverse ? F - 1 - it : it;
+          const double* Sa = Ss + (size_t)it * DD;
+          const double* za = zs + (size_t)it * D;
+          for (int s = 0; s < S_; ++s) {
+            const long t = (long)f * S_ + s;
+            const double* qr = q_rot + base + t * D;
+            const double* qp = q_pos + base + t * D;
+            const double* dn = dnum + (((long)b * N + t) * H + h) * D;
+            const double dd = dden[(long)bh * N + t];
+            for (int r = 0; r < D; ++r) {
+              double acc = 0.0;
+              for (int c = 0; c < D; ++c) {
+                A[(size_t)r * D + c] += qr[r] * dn[c];
+                acc += Sa[(size_t)r * D + c] * dn[c];
+              }
+              dq_rot[base + t * D + r] = acc;
+              a[r] += dd * qp[r];
+              dq_pos[base + t * D + r] = dd * za[r];
+            }
+          }
+          if (reverse && it == 0) break; /* frame 0 of the reverse direction is not absorbed */
+          const int fa = reverse ? f + 1 : f;
+          const double g = decay[(long)bh * F + fa];
+          /* S_prev, z_prev: the state after the previous step (zero before the first) */
+          if (it > 0) {
+            for (size_t e = 0; e < DD; ++e) Sp[e] = g * Ss[(size_t)(it - 1) * DD + e];
+            for (int r = 0; r < D; ++r) zp[r] = g * zs[(size_t)(it - 1) * D + r];
+          } else {
+            memset(Sp, 0, sizeof(double) * DD);
+            memset(zp, 0, sizeof(double) * D);
+          }
+          memcpy(dSp, A, sizeof(double) * DD);
+          memcpy(dzp, a, sizeof(double) * D);
+          for (int s = 0; s < S_; ++s) {
+            const long t = (long)fa * S_ + s;
+            const double* kr = k_rot + base + t * D;
+            const double* kp = k_pos + base + t * D;
+            const double* vv = v + base + t * D;
+            const double bt = beta[(long)bh * N + t];
+            double* r_ = vec;
+            double* dd_ = vec + D;
+            double db = 0.0;
+            for (int c = 0; c < D; ++c) {
+              double pr = 0.0, q = 0.0;
+              for (int r = 0; r < D; ++r) {
+                pr += Sp[(size_t)r * D + c] * kr[r];
+                q += A[(size_t)r * D + c] * kr[r];
+              }
+              r_[c] = vv[c] - pr;
+              dd_[c] = q;
+              dv[base + t * D + c] = bt * q;
+              db += q * r_[c];
+            }
+            for (int r = 0; r < D; ++r) {
+              double acc = 0.0;
+              for (int c = 0; c < D; ++c)
+                acc += A[(size_t)r * D + c] * bt * r_[c] - Sp[(size_t)r * D + c] * bt * dd_[c];
+              dk_rot[base + t * D + r] = acc;
+              for (int c = 0; c < D; ++c) dSp[(size_t)r * D + c] -= bt * kr[r] * dd_[c];
+            }
+            double zh = 0.0, ee = 0.0;
+            for (int r = 0; r < D; ++r) {
+              zh += kp[r] * zp[r];
+              ee += a[r] * kp[r];
+            }
+            const double e1 = 1.0 - zh;
+            for (int r = 0; r < D; ++r) {
+              dk_pos[base + t * D + r] = a[r] * bt * e1 - bt * ee * zp[r];
+              dzp[r] -= bt * ee * kp[r];
+            }
+            dbeta[(long)bh * N + t] = db + ee * e1;
+          }
+          double gd = 0.0;
+          if (it > 0) {
+            for (size_t e = 0; e < DD; ++e) gd += dSp[e] * Ss[(size_t)(it - 1) * DD + e];
+            for (int r = 0; r < D; ++r) gd += dzp[r] * zs[(size_t)(it - 1) * D + r];
+          }
+          ddecay[(long)bh * F + fa] = gd;
+          for (size_t e = 0; e < DD; ++e) A[e] = g * dSp[e];
+          for (int r = 0; r < D; ++r) a[r] = g * dzp[r];
+        }
+        if (reverse) {
+          /* frame 0 is never absorbed */
+          for (long t = 0; t < S_; ++t) {
+            for (int r = 0; r < D; ++r) {
+              dk_rot[base + t * D + r] = 0.0;
+              dk_pos[base + t * D + r] = 0.0;
+              dv[base + t * D + r] = 0.0;
+            }
+            dbeta[(long)bh * N + t] = 0.0;
+          }
+          ddecay[(long)bh * F] = 0.0;
+        }
+      }
+    }
+    free(Ss);
+    free(zs);
+    free(A);
+    free(dSp);
+    free(a);
+    free(dzp);
+    free(Sp);
+    free(zp);
+    free(vec);
+  }
+  return fail ? -1 : 0;
+}

@@ -20,6 +20,7 @@ PINS_GDN = "tests/test_oracle_pins.py"
 PINS_CAM = "tests/test_oracle_cam.py"
 PINS_DHU = "tests/test_oracle_dhu.py"
 PINS_CBWD = "tests/test_oracle_cam_bwd.py"
+PINS_BBWD = "tests/test_oracle_bigdn_bwd.py"
 
 # (name, pin file, text in gdn_oracle.c, replacement)
 MUTATIONS = [
@@ -58,6 +59,11 @@ MUTATIONS = [
     ("backward inputs: P without its diagonal", PINS_DHU,
      "            for (int s = 0; s <= r; ++s) {\n              double p = 0.0;",
      "            for (int s = 0; s < r; ++s) {\n              double p = 0.0;"),
+    ("BiGDN backward: dk_pos without the prediction term", PINS_BBWD,
+     "dk_pos[base + t * D + r] = a[r] * bt * e1 - bt * ee * zp[r];",
+     "dk_pos[base + t * D + r] = a[r] * bt * e1;"),
+    ("BiGDN backward: dbeta without the z stream", PINS_BBWD,
+     "dbeta[(long)bh * N + t] = db + ee * e1;", "dbeta[(long)bh * N + t] = db;"),
     ("camera backward: dv without beta", PINS_CBWD,
      "dv[base + (long)c * N + t] = bt * dd[c];", "dv[base + (long)c * N + t] = dd[c];"),
     ("camera backward: dk without the prediction term", PINS_CBWD,
