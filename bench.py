@@ -62,6 +62,7 @@ SOURCES = {
     "bigdn_merged": ["gdn_bigdn.hip"],
     "cam": ["gdn_cam.hip", "gdn_bigdn.hip"],
     "cam_bwd": ["gdn_cambwd.hip"],
+    "bigdn_bwd": ["gdn_bigdnbwd.hip", "gdn_cambwd.hip"],
     "summary": ["gdn_fwd.hip", "gdn_fused16.hip", "gdn_summary.hip"],
     "dhu": ["gdn_bwd.hip"],
 }
@@ -110,6 +111,14 @@ def alg_bytes_cam_bwd(B, F, S, H, D):
     decay once; write dq, dk, dv, dbeta and ddecay."""
     N = F * S
     return 7 * B * H * D * N * 4 + 2 * B * H * N * 4 + 2 * B * H * F * 4
+
+
+def alg_bytes_bigdn_bwd(B, F, S, H, D):
+    """Minimum HBM bytes of one BiGDN direction backward call: read the five prepped bf16
+    tensors, dnum (fp32), beta, decay and dden once; write the five fp32 gradients, dbeta and
+    ddecay."""
+    N = F * S
+    return (5 * 2 + 4 + 5 * 4) * B * H * N * D + 3 * B * H * N * 4 + 2 * B * H * F * 4
 
 
 def alg_bytes_dhu(B, T, H, K, V, elt):
@@ -221,6 +230,22 @@ def cpu_baseline(kind, inp, max_chains=64):
                 oracle.cam_scan_bwd(**sub, reverse=rev)
         return _cpu_time(run, "both scan directions' backward on the first %d of %d frames, "
                          "all %d heads (%d tokens)" % (fs, F, H, n), 2 * B * n * H)
+    if kind == "bigdn_bwd":
+        B, H, N, D = inp["q_rot"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        fs = min(F, 4)
+        n = fs * S
+        names = ("q_rot", "k_rot", "q_pos", "k_pos", "v")
+        sub = {k: inp[k][:, :, :n] for k in names}
+        sub.update(beta=inp["beta"][:, :, :fs], decay=inp["decay"][:, :, :fs],
+                   dnum=inp["dnum"][:, :n], dden=inp["dden"][:, :, :n])
+
+        def run():
+            for rev in (False, True):
+                oracle.bigdn_dir_bwd(*(sub[k] for k in names + ("beta", "decay", "dnum", "dden")),
+                                     reverse=rev)
+        return _cpu_time(run, "both directions' backward on the first %d of %d frames, all %d "
+                         "heads (%d tokens)" % (fs, F, H, n), 2 * B * n * H)
     if kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -427,6 +452,22 @@ def main():
             s = sets[i % len(sets)]
             return [gdn.cam_scan_bwd(s["q"], s["k"], s["v"], s["beta"], s["decay"], s["dout"],
                                      reverse=rev) for rev in (False, True)]
+    elif kind == "bigdn_bwd":
+        B, H, N, D = inp["q_rot"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        dt = torch.bfloat16
+        th = 2 * B * N * H  # tokens*heads of both directions
+        alg = 2 * alg_bytes_bigdn_bwd(B, F, S, H, D)
+        kernel = "bigdn_dir_bwd x 2 directions (5 kernels each, whole step)"
+        config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
+                  "state": "fp32", "products": "split bf16 (hi/lo) operands, fp32 accumulation",
+                  "step": "gradients of the forward and of the reverse direction (two calls; "
+                          "summing the two directions' gradients is the caller's)"}
+        names = ("q_rot", "k_rot", "q_pos", "k_pos", "v", "beta", "decay", "dnum", "dden")
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return [gdn.bigdn_dir_bwd(*(s[k] for k in names), reverse=rev) for rev in (False, True)]
     elif kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

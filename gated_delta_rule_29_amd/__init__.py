@@ -18,7 +18,7 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi", "cam_scan_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
+           "cam_scan_bidi", "cam_scan_bwd", "bigdn_dir_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
            "gdn_state_grad_summary", "gdn_state_grad_apply", "gdn_abi_version",
            "gdn_last_error", "CHUNK"]
 
@@ -485,6 +485,38 @@ def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, gk=None, want_d
                                  _DT[dt], _stream(dev))
     _lib.check(rc, "gdn_bwd_dhu")
     return {"dv2": dv2, "dh": dh, "dh0": dh0}
+
+
+def bigdn_dir_bwd(q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden, reverse=False):
+    """Backward of one BiGDN direction on the prepped tensors (q_rot .. v [B,H,N,D] bf16, as
+    gdn_prep returns them); beta [B,H,F,S], decay [B,H,F]; dnum [B,N,H,D], dden [B,H,N] fp32.
+    Returns a dict with dq_rot, dk_rot, dq_pos, dk_pos, dv [B,H,N,D], dbeta [B,H,F,S] and
+    ddecay [B,H,F] (fp32)."""
+    B, H, N, D = q_rot.shape
+    F, S = beta.shape[2], beta.shape[3]
+    dev = q_rot.device
+    for t, name in ((q_rot, "q_rot"), (k_rot, "k_rot"), (q_pos, "q_pos"), (k_pos, "k_pos"),
+                    (v, "v")):
+        _need(t, name, (B, H, N, D), torch.bfloat16, dev)
+    _need(beta, "beta", (B, H, F, S), torch.float32, dev)
+    _need(decay, "decay", (B, H, F), torch.float32, dev)
+    _need(dnum, "dnum", (B, N, H, D), torch.float32, dev)
+    _need(dden, "dden", (B, H, N), torch.float32, dev)
+    if F * S != N:
+        raise ValueError("beta is [B,H,F,S] with F*S = %d, but N = %d" % (F * S, N))
+    names = ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv")
+    out = {n: torch.empty(B, H, N, D, dtype=torch.float32, device=dev) for n in names}
+    out["dbeta"] = torch.empty(B, H, F, S, dtype=torch.float32, device=dev)
+    out["ddecay"] = torch.empty(B, H, F, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    ws_n = lib.bigdn_dir_bwd_workspace_bytes(B, H, D, F)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.bigdn_dir_bwd(*(_ptr(x) for x in (q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum,
+                                               dden)), int(bool(reverse)),
+                           *(_ptr(out[n]) for n in names + ("dbeta", "ddecay")),
+                           B, H, D, F, S, _ptr(ws), ws_n, _stream(dev))
+    _lib.check(rc, "bigdn_dir_bwd")
+    return out
 
 
 def gdn_bwd_prep(q, k, beta, do, g=None, scale=1.0, *, gk=None):

@@ -50,6 +50,8 @@ SIGNATURES = {
     "cam_scan_bidi": (I, [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, SZ, P]),
     "cam_scan_bwd_workspace_bytes": (SZ, [I, I, I, I]),
     "cam_scan_bwd": (I, [P, P, P, P, P, P, I, P, P, P, P, P, I, I, I, I, I, P, SZ, P]),
+    "bigdn_dir_bwd_workspace_bytes": (SZ, [I, I, I, I]),
+    "bigdn_dir_bwd": (I, [P] * 9 + [I] + [P] * 7 + [I, I, I, I, I, P, SZ, P]),
     "gdn_bwd_prep": (I, [P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]),
     "gdn_state_grad_summary_workspace_bytes": (SZ, [I, I, I, I, I]),
     "gdn_state_grad_summary": (I, [P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, P, SZ, P]),

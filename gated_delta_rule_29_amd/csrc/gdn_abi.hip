@@ -13,6 +13,7 @@
 #include <mutex>
 
 #include "../../include/gdn.h"
+#include "gdn_bwd_params.h"
 #include "gdn_internal.h"
 
 namespace {
@@ -666,6 +667,70 @@ int cam_scan_bwd(const float* q, const float* k, const float* v, const float* be
   p.lo = mats;
   hipError_t e = gdn::launch_cam_scan_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cam_scan_bwd launch");
+  return ok();
+}
+
+// ---- backward of one BiGDN direction ----------------------------------------------------------
+
+size_t bigdn_dir_bwd_workspace_bytes(int B, int H, int D, int F) {
+  if (B <= 0 || H <= 0 || (D != 64 && D != 128) || F <= 0) return 0;
+  const size_t mats = (size_t)B * H * F * D * D, vecs = (size_t)B * H * F * D;
+  return 9 * al256(mats * 4) + al256((size_t)B * H * F * (D / 32) * 4) + 4 * al256(vecs * 4) +
+         al256((size_t)B * H * F * 4);
+}
+
+int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_pos, const void* k_pos,
+                  const void* v, const float* beta, const float* decay, const float* dnum,
+                  const float* dden, int reverse, float* dq_rot, float* dk_rot, float* dq_pos,
+                  float* dk_pos, float* dv, float* dbeta, float* ddecay, int B, int H, int D, int F,
+                  int S, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_rot || !k_rot || !q_pos || !k_pos || !v || !beta || !decay || !dnum || !dden || !dq_rot ||
+      !dk_rot || !dq_pos || !dk_pos || !dv || !dbeta || !ddecay)
+    return fail(GDN_ERR_INVALID, "every input and gradient pointer must be non-null");
+  if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S <= 0)
+    return fail(GDN_ERR_INVALID, "B, H, D, F, S must be positive (got %d, %d, %d, %d, %d)", B, H,
+                D, F, S);
+  if (reverse != 0 && reverse != 1) return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, got %d", reverse);
+  if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
+  if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
+  if ((int64_t)F * S > INT32_MAX || (int64_t)B * H * F * 4 > INT32_MAX ||
+      (int64_t)B * H * F * (S / 64) > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "F*S or B*H*F exceeds the grid limit");
+  const size_t need = bigdn_dir_bwd_workspace_bytes(B, H, D, F);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  const size_t mats = (size_t)B * H * F * D * D, vecs = (size_t)B * H * F * D;
+  char* ws = static_cast<char*>(workspace);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* r = ws + off; off += al256(bytes); return r; };
+  gdn::BigdnBwdParams p{};
+  gdn::CamBwdParams& c = p.cam;
+  c.beta = beta; c.decay = decay; c.reverse = reverse; c.dbeta = dbeta; c.ddecay = ddecay;
+  c.B = B; c.H = H; c.D = D; c.F = F; c.S = S;
+  c.G = reinterpret_cast<float*>(take(mats * 4));
+  c.U = reinterpret_cast<float*>(take(mats * 4));
+  c.W = reinterpret_cast<float*>(take(mats * 4));
+  c.Spf = reinterpret_cast<float*>(take(mats * 4));
+  c.Sp = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
+  c.SpT = reinterpret_cast<__bf16*>(take(mats * 4));
+  c.Ab = reinterpret_cast<__bf16*>(take(mats * 4));
+  c.AbT = reinterpret_cast<__bf16*>(take(mats * 4));
+  c.ddecay_part = reinterpret_cast<float*>(take((size_t)B * H * F * (D / 32) * 4));
+  c.lo = mats;
+  p.Gpos = reinterpret_cast<float*>(take(mats * 4));
+  p.upos = reinterpret_cast<float*>(take(vecs * 4));
+  p.wz = reinterpret_cast<float*>(take(vecs * 4));
+  p.zs = reinterpret_cast<float*>(take(vecs * 4));
+  p.as = reinterpret_cast<float*>(take(vecs * 4));
+  p.ddz = reinterpret_cast<float*>(take((size_t)B * H * F * 4));
+  p.q_rot = static_cast<const __bf16*>(q_rot); p.k_rot = static_cast<const __bf16*>(k_rot);
+  p.q_pos = static_cast<const __bf16*>(q_pos); p.k_pos = static_cast<const __bf16*>(k_pos);
+  p.v = static_cast<const __bf16*>(v); p.dnum = dnum; p.dden = dden;
+  p.dq_rot = dq_rot; p.dk_rot = dk_rot; p.dq_pos = dq_pos; p.dk_pos = dk_pos; p.dv = dv;
+  hipError_t e = gdn::launch_bigdn_dir_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bigdn_dir_bwd launch");
   return ok();
 }
 

@@ -1,0 +1,469 @@
+// gdn_bigdnbwd.hip -- backward of one BiGDN direction for gfx950 (SANA fused_gdn.py page,
+// "Backward / autograd Functions": the reverse replay of the frame recurrence behind
+// FusedBiGDNFunction.backward; the forward is one direction of bigdn_fwd).
+//
+// A direction carries the state S (D x D; keys k_rot, values v, read out by q_rot into num)
+// and the normaliser z (D; keys k_pos, value 1, read out by q_pos into den).  S follows the
+// camera-branch recurrence exactly, so its backward reuses the camera backward's state /
+// gradient scan (gdn_cambwd.hip) on statistics formed here from the token-major prepped
+// tensors; z is the same recurrence with a scalar value, scanned as vectors.  With A and a
+// the gradients of S and z after a step's update, for the tokens s of the frame that a step
+// absorbs (S_pre = g S_prev, z_pre = g z_prev):
+//   dk_rot_s = A (beta_s r_s) - beta_s S_pre (A^T k_rot_s),  r_s = v_s - S_pre^T k_rot_s
+//   dv_s = beta_s A^T k_rot_s
+//   dk_pos_s = a (beta_s e_s) - beta_s (a . k_pos_s) z_pre,   e_s = 1 - k_pos_s . z_pre
+//   dbeta_s = (A^T k_rot_s) . r_s + (a . k_pos_s) e_s
+// and for the tokens of the frame the step outputs: dq_rot = S dnum, dq_pos = dden z.
+//
+// Kernels:
+//   stats  per (b, h, frame, matrix): G, U, W (the S stream) and G_pos (the z stream) as
+//          D x D fp32, plus the vectors u_pos = K_pos^T beta and w_z = Q_pos^T dden; the token
+//          slabs are transposed into LDS 32 tokens at a time (the contraction runs over tokens)
+//   S scan the camera backward's scan (states and their gradients as hi/lo pairs)
+//   z scan per (b, h): z after every step and a, by matrix-vector products with G_pos
+//   S tok  per (b, h, step, 64 tokens): as the camera backward's token kernel, with token-
+//          major tiles (no transpose) and token-major outputs
+//   z tok  per (b, h, step, 64 tokens): dq_pos, dk_pos and the z part of dbeta
+// Products take split bf16 operands (GDN_SPLIT); the z stream is fp32 arithmetic.
+#include "gdn_bwd_params.h"
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// ---- statistics ---------------------------------------------------------------------------
+// blockIdx.x = (bh * F + f) * 4 + which: 0 G (X = beta k_rot, Y = k_rot), 1 U (X = beta k_rot,
+// Y = v), 2 W (X = q_rot, Y = dnum), 3 G_pos (X = beta k_pos, Y = k_pos).  Out[i][j] =
+// sum_s X[s][i] Y[s][j].  Wave w owns rows 16 RT w .., all columns.
+template <int D>
+__global__ __launch_bounds__(256) void bbwd_stats_kernel(const BigdnBwdParams p) {
+  constexpr int RT = D / 64, CT = D / 16;
+  constexpr int kX = 40;  // bf16 row stride of the [channel][32 tokens] tiles
+  __shared__ __attribute__((aligned(16))) bf16 xt[2][D * kX];
+  __shared__ __attribute__((aligned(16))) bf16 yt[2][D * kX];
+  const CamBwdParams& c = p.cam;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
+  const int which = blockIdx.x % 4;
+  const long bf = blockIdx.x / 4;
+  const int f = (int)(bf % c.F);
+  const long bh = bf / c.F;
+  const int b = (int)(bh / c.H), h = (int)(bh % c.H);
+  const long N = (long)c.F * c.S;
+  const long t0f = (long)f * c.S;  // first token of the frame
+  const __bf16* X = which == 2 ? p.q_rot : (which == 3 ? p.k_pos : p.k_rot);
+  const __bf16* Y = which == 0 ? p.k_rot : (which == 1 ? p.v : p.k_pos);
+  const bool xbeta = which != 2;
+  const float* bt = c.beta + bh * N + t0f;
+  f32x4 acc[RT][CT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc) acc[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int t = tid % 32, cg = tid / 32;  // this thread's token and first channel group
+  for (int s0 = 0; s0 < c.S; s0 += 32) {
+    const long tok = t0f + s0 + t;
+    const float sc = xbeta ? bt[s0 + t] : 1.f;
+#pragma unroll
+    for (int g8 = cg; g8 < D / 8; g8 += 8) {
+      const bf16x8 xr = *reinterpret_cast<const bf16x8*>(X + (bh * N + tok) * D + 8 * g8);
+      float y[8];
+      if (which == 2) {
+        const float* src = p.dnum + (((long)b * N + tok) * c.H + h) * D + 8 * g8;
+        const f32x4 y0 = *reinterpret_cast<const f32x4*>(src), y1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[j] = y0[j];
+          y[4 + j] = y1[j];
+        }
+      } else {
+        const bf16x8 yr = *reinterpret_cast<const bf16x8*>(Y + (bh * N + tok) * D + 8 * g8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = (float)yr[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int o = (8 * g8 + j) * kX + t;
+        bf16 a0, a1, b0, b1;
+        GDN_SPLIT((float)xr[j] * sc, a0, a1);
+        GDN_SPLIT(y[j], b0, b1);
+        xt[0][o] = a0;
+        xt[1][o] = a1;
+        yt[0][o] = b0;
+        yt[1][o] = b1;
+      }
+    }
+    __syncthreads();
+    bf16x8 ah[RT], al[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int o = (16 * (RT * w + r) + li) * kX + 8 * lq;
+      ah[r] = lds8(&xt[0][o]);
+      al[r] = lds8(&xt[1][o]);
+    }
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc) {
+      const int o = (16 * cc + li) * kX + 8 * lq;
+      const bf16x8 bh_ = lds8(&yt[0][o]), bl = lds8(&yt[1][o]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r][cc] = mma3(ah[r], al[r], bh_, bl, acc[r][cc]);
+    }
+    __syncthreads();
+  }
+  float* out = (which == 0 ? c.G : (which == 1 ? c.U : (which == 2 ? c.W : p.Gpos))) + bf * D * D;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(16 * (RT * w + r) + 4 * lq + e) * D + 16 * cc + li] = acc[r][cc][e];
+  // the z stream's vectors: w_z = Q_pos^T dden (with W), u_pos = K_pos^T beta (with G_pos)
+  if (which >= 2 && tid < D) {
+    float s = 0.f;
+    for (int sI = 0; sI < c.S; ++sI) {
+      const long tok = t0f + sI;
+      const float wt = which == 2 ? p.dden[bh * N + tok] : bt[sI];
+      s += wt * (float)(which == 2 ? p.q_pos : p.k_pos)[(bh * N + tok) * D + tid];
+    }
+    (which == 2 ? p.wz : p.upos)[bf * D + tid] = s;
+  }
+}
+
+// ---- z scan --------------------------------------------------------------------------------
+// One workgroup per (b, h).  y = G_pos x with P = 256 / D threads per row (adjacent lanes).
+template <int D>
+__global__ __launch_bounds__(256) void bbwd_zscan_kernel(const BigdnBwdParams p) {
+  constexpr int P = 256 / D;
+  __shared__ float zv[D], xv[D], red[4];
+  const CamBwdParams& c = p.cam;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const long bh = blockIdx.x;
+  const int F = c.F;
+  const int row = tid / P, part = tid % P;
+  // y[row] = sum_j M[row][j] x[j] (this thread: columns j = part, part + P, ...)
+  auto matvec = [&](const float* M, const float* x) {
+    float s = 0.f;
+    for (int j = part; j < D; j += P) s += M[(size_t)row * D + j] * x[j];
+    s += __shfl_xor(s, 1, 64);
+    if (P == 4) s += __shfl_xor(s, 2, 64);
+    return s;
+  };
+  if (tid < D) zv[tid] = 0.f;
+  __syncthreads();
+  for (int it = 0; it < F; ++it) {
+    const int f = c.reverse ? F - 1 - it : it;
+    if (!(c.reverse && it == 0)) {
+      const int fa = c.reverse ? f + 1 : f;
+      const float g = c.decay[bh * F + fa];
+      if (tid < D) xv[tid] = g * zv[tid];  // z_pre
+      __syncthreads();
+      const float y = matvec(p.Gpos + (bh * F + fa) * D * D, xv);
+      __syncthreads();
+      if (part == 0) zv[row] = xv[row] - y + p.upos[(bh * F + fa) * D + row];
+      __syncthreads();
+    }
+    if (tid < D) p.zs[(bh * F + it) * D + tid] = zv[tid];
+  }
+  // gradients of z after each step's update, in reverse (zv holds a)
+  __syncthreads();
+  if (tid < D) zv[tid] = 0.f;
+  __syncthreads();
+  for (int it = F - 1; it >= 0; --it) {
+    const int f = c.reverse ? F - 1 - it : it;
+    if (tid < D) {
+      zv[tid] += p.wz[(bh * F + f) * D + tid];
+      p.as[(bh * F + it) * D + tid] = zv[tid];
+    }
+    __syncthreads();
+    if (c.reverse && it == 0) break;
+    const int fa = c.reverse ? f + 1 : f;
+    const float g = c.decay[bh * F + fa];
+    const float y = matvec(p.Gpos + (bh * F + fa) * D * D, zv);  // G_pos is symmetric
+    float part_dd = 0.f;
+    __syncthreads();  // every thread has read zv
+    if (part == 0) {
+      const float dzp = zv[row] - y;
+      if (it > 0) part_dd = dzp * p.zs[(bh * F + it - 1) * D + row];
+      zv[row] = g * dzp;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part_dd += __shfl_xor(part_dd, off, 64);
+    if (lane == 0) red[w] = part_dd;
+    __syncthreads();
+    if (tid == 0) p.ddz[bh * F + fa] = (red[0] + red[1]) + (red[2] + red[3]);
+  }
+}
+
+// ---- S stream token gradients ---------------------------------------------------------------
+// As cbwd_tok_kernel (gdn_cambwd.hip) with token-major operands: blockIdx.x = (bh * F + it) *
+// (S / 64) + token block; two LDS tiles, each a hi/lo pair of bf16 [token][D]; wave w forms
+// output rows (channels) 16 RW w .. 16 RW (w + 1) - 1 for the 64 tokens.
+template <int D>
+__global__ __launch_bounds__(256) void bbwd_tok_kernel(const BigdnBwdParams p) {
+  constexpr int RW = D / 64;
+  constexpr int kT = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 tl[2][2][64 * kT];
+  __shared__ float red[4][64];
+  const CamBwdParams& c = p.cam;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
+  const int nblk = c.S / 64;
+  const int blk = blockIdx.x % nblk;
+  const long sb = blockIdx.x / nblk;
+  const int F = c.F;
+  const int it = (int)(sb % F);
+  const long bh = sb / F;
+  const int b = (int)(bh / c.H), h = (int)(bh % c.H);
+  const long N = (long)F * c.S;
+  const size_t DD = (size_t)D * D;
+  const int s0 = 64 * blk;
+  const int f = c.reverse ? F - 1 - it : it;
+  const bool absorb = !(c.reverse && it == 0);
+  const int fa = c.reverse ? f + 1 : f;  // used only when absorb
+
+  if (blk == 0 && tid == 0) {
+    if (absorb) {
+      float s = p.ddz[bh * F + fa];
+      for (int cb = 0; cb < D / 32; ++cb) s += c.ddecay_part[((size_t)bh * F + fa) * (D / 32) + cb];
+      c.ddecay[bh * F + fa] = it > 0 ? s : 0.f;
+    } else {
+      c.ddecay[bh * F] = 0.f;
+    }
+  }
+  // 64 token rows from t0 (token-major, row stride rs elements) into tile T as a split pair
+  auto stage16 = [&](const __bf16* x, long t0, int T) {
+    for (int e = tid; e < 64 * D / 8; e += 256) {
+      const int t = e / (D / 8), d = 8 * (e % (D / 8));
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + (bh * N + t0 + t) * D + d);
+      *reinterpret_cast<bf16x8*>(&tl[T][0][t * kT + d]) = v;
+      *reinterpret_cast<bf16x8*>(&tl[T][1][t * kT + d]) = bf16x8{};
+    }
+  };
+  auto stage_dnum = [&](long t0, int T) {
+    for (int e = tid; e < 64 * D / 8; e += 256) {
+      const int t = e / (D / 8), d = 8 * (e % (D / 8));
+      const float* src = p.dnum + (((long)b * N + t0 + t) * c.H + h) * D + d;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src), x1 = *reinterpret_cast<const f32x4*>(src + 4);
+      bf16x8 xh, xl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        GDN_SPLIT(x0[j], xh[j], xl[j]);
+        GDN_SPLIT(x1[j], xh[4 + j], xl[4 + j]);
+      }
+      *reinterpret_cast<bf16x8*>(&tl[T][0][t * kT + d]) = xh;
+      *reinterpret_cast<bf16x8*>(&tl[T][1][t * kT + d]) = xl;
+    }
+  };
+  auto put = [&](int T, int t, int i0, const float (&x)[4]) {
+    bf16x4 xh, xl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) GDN_SPLIT(x[e], xh[e], xl[e]);
+    *reinterpret_cast<bf16x4*>(&tl[T][0][t * kT + i0]) = xh;
+    *reinterpret_cast<bf16x4*>(&tl[T][1][t * kT + i0]) = xl;
+  };
+  auto prod = [&](const bf16* M, int T, f32x4 (&C)[RW][4]) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) C[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      bf16x8 bh_[4], bl[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        bh_[cc] = lds8(&tl[T][0][(16 * cc + li) * kT + 32 * kk + 8 * lq]);
+        bl[cc] = lds8(&tl[T][1][(16 * cc + li) * kT + 32 * kk + 8 * lq]);
+      }
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const size_t ro = (size_t)(16 * (RW * w + r) + li) * D + 32 * kk + 8 * lq;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(M + ro);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(M + c.lo + ro);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) C[r][cc] = mma3(ah, al, bh_[cc], bl[cc], C[r][cc]);
+      }
+    }
+  };
+  auto ch0 = [&](int r) { return 16 * (RW * w + r) + 4 * lq; };  // first of a lane's 4 channels
+  auto store4 = [&](float* out, long t, int r, const f32x4& x) {
+    *reinterpret_cast<f32x4*>(out + (bh * N + t) * D + ch0(r)) = x;
+  };
+
+  // ---- dq_rot = S dnum for the output frame's tokens
+  stage_dnum((long)f * c.S + s0, 0);
+  __syncthreads();
+  {
+    f32x4 C[RW][4];
+    prod(c.Sp + ((size_t)bh * F + it) * DD, 0, C);
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) store4(p.dq_rot, (long)f * c.S + s0 + 16 * cc + li, r, C[r][cc]);
+  }
+  if (!absorb) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const long t = s0 + 16 * cc + li;
+        store4(p.dk_rot, t, r, f32x4{0.f, 0.f, 0.f, 0.f});
+        store4(p.dv, t, r, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    if (tid < 64) c.dbeta[bh * N + s0 + tid] = 0.f;
+    return;
+  }
+  const long ta = (long)fa * c.S + s0;
+  const float g = c.decay[bh * F + fa];
+  float bcol[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) bcol[cc] = c.beta[bh * N + ta + 16 * cc + li];
+  __syncthreads();
+  stage16(p.k_rot, ta, 0);
+  __syncthreads();
+  f32x4 P[RW][4], Dd[RW][4];
+  if (it > 0) {
+    prod(c.SpT + ((size_t)bh * F + it - 1) * DD, 0, P);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) P[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  prod(c.AbT + ((size_t)bh * F + it) * DD, 0, Dd);
+  float db[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const long t = ta + 16 * cc + li;
+      const bf16x4 vv = *reinterpret_cast<const bf16x4*>(p.v + (bh * N + t) * D + ch0(r));
+      f32x4 dvv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float rr = (float)vv[e] - g * P[r][cc][e];
+        const float dd = Dd[r][cc][e];
+        dvv[e] = bcol[cc] * dd;
+        db[cc] += dd * rr;
+        P[r][cc][e] = bcol[cc] * rr;
+        Dd[r][cc][e] = -bcol[cc] * dd;
+      }
+      store4(p.dv, t, r, dvv);
+    }
+  __syncthreads();  // every wave is done with the k tile
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const float xr[4] = {P[r][cc][0], P[r][cc][1], P[r][cc][2], P[r][cc][3]};
+      const float xd[4] = {Dd[r][cc][0], Dd[r][cc][1], Dd[r][cc][2], Dd[r][cc][3]};
+      put(1, 16 * cc + li, ch0(r), xr);
+      put(0, 16 * cc + li, ch0(r), xd);
+    }
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    db[cc] += __shfl_xor(db[cc], 16, 64);
+    db[cc] += __shfl_xor(db[cc], 32, 64);
+    if (lq == 0) red[w][16 * cc + li] = db[cc];
+  }
+  __syncthreads();
+  if (tid < 64) c.dbeta[bh * N + ta + tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+  f32x4 K1[RW][4];
+  prod(c.Ab + ((size_t)bh * F + it) * DD, 1, K1);
+  if (it > 0) {
+    f32x4 K2[RW][4];
+    prod(c.Sp + ((size_t)bh * F + it - 1) * DD, 0, K2);
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) K1[r][cc] = K1[r][cc] + g * K2[r][cc];
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) store4(p.dk_rot, ta + 16 * cc + li, r, K1[r][cc]);
+}
+
+// ---- z stream token gradients ----------------------------------------------------------------
+// blockIdx.x as bbwd_tok_kernel; wave w takes 16 tokens, a lane D / 64 channels.  Runs after
+// bbwd_tok_kernel, whose dbeta it adds to.
+template <int D>
+__global__ __launch_bounds__(256) void bbwd_ztok_kernel(const BigdnBwdParams p) {
+  constexpr int CL = D / 64;  // channels per lane
+  const CamBwdParams& c = p.cam;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nblk = c.S / 64;
+  const int blk = blockIdx.x % nblk;
+  const long sb = blockIdx.x / nblk;
+  const int F = c.F;
+  const int it = (int)(sb % F);
+  const long bh = sb / F;
+  const long N = (long)F * c.S;
+  const int f = c.reverse ? F - 1 - it : it;
+  const bool absorb = !(c.reverse && it == 0);
+  const int fa = c.reverse ? f + 1 : f;
+  const int s0 = 64 * blk + 16 * w;
+  float za[CL], av[CL], zp[CL];
+#pragma unroll
+  for (int j = 0; j < CL; ++j) {
+    const int ch = lane + 64 * j;
+    za[j] = p.zs[(bh * F + it) * D + ch];
+    av[j] = p.as[(bh * F + it) * D + ch];
+    zp[j] = absorb && it > 0 ? c.decay[bh * F + fa] * p.zs[(bh * F + it - 1) * D + ch] : 0.f;
+  }
+  for (int i = 0; i < 16; ++i) {
+    const long t = (long)f * c.S + s0 + i;  // output frame
+    const float dd = p.dden[bh * N + t];
+#pragma unroll
+    for (int j = 0; j < CL; ++j) p.dq_pos[(bh * N + t) * D + lane + 64 * j] = dd * za[j];
+  }
+  if (!absorb) {
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < CL; ++j) p.dk_pos[(bh * N + s0 + i) * D + lane + 64 * j] = 0.f;
+    return;
+  }
+  for (int i = 0; i < 16; ++i) {
+    const long t = (long)fa * c.S + s0 + i;  // absorbed frame
+    const float bt = c.beta[bh * N + t];
+    float kp[CL], zh = 0.f, ee = 0.f;
+#pragma unroll
+    for (int j = 0; j < CL; ++j) {
+      kp[j] = (float)p.k_pos[(bh * N + t) * D + lane + 64 * j];
+      zh += kp[j] * zp[j];
+      ee += kp[j] * av[j];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      zh += __shfl_xor(zh, off, 64);
+      ee += __shfl_xor(ee, off, 64);
+    }
+    const float e1 = 1.f - zh;
+#pragma unroll
+    for (int j = 0; j < CL; ++j)
+      p.dk_pos[(bh * N + t) * D + lane + 64 * j] = av[j] * bt * e1 - bt * ee * zp[j];
+    if (lane == 0) c.dbeta[bh * N + t] += ee * e1;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const BigdnBwdParams& p, hipStream_t stream) {
+  const CamBwdParams& c = p.cam;
+  const long bh = (long)c.B * c.H;
+  hipLaunchKernelGGL((bbwd_stats_kernel<D>), dim3(bh * c.F * 4), dim3(256), 0, stream, p);
+  hipError_t e = launch_cam_bwd_scan(c, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bbwd_zscan_kernel<D>), dim3(bh), dim3(256), 0, stream, p);
+  const dim3 tg(bh * c.F * (c.S / 64));
+  hipLaunchKernelGGL((bbwd_tok_kernel<D>), tg, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bbwd_ztok_kernel<D>), tg, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bigdn_dir_bwd(const BigdnBwdParams& p, hipStream_t stream) {
+  return p.cam.D == 128 ? launch_d<128>(p, stream) : launch_d<64>(p, stream);
+}
+
+}  // namespace gdn

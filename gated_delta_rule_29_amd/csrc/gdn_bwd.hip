@@ -345,7 +345,9 @@ __global__ __launch_bounds__(kThreads) void dhu16_kernel(const DhuParams p) {
   uint4 rk[kItK], rq[kItK], rw[kItK], rdo;
   bf16 rdv[4];
   float rg = 0.f, rgk[kGK ? 16 : 1], rgt[kGK ? 16 : 1];
-  const int gkd = tid % K, gkq = tid / K;  // this thread's key and token quarter (kGK)
+  // this thread's key and token quarter (kGK); the quarter is the same for a whole wave
+  // (K = 128 threads per quarter), so its gate reads are wave-uniform
+  const int gkd = tid % K, gkq = __builtin_amdgcn_readfirstlane(tid / K);
   auto tok = [&](int t) { return t < T ? t : T - 1; };
   auto load = [&](int n) {
     const int t0 = n * kC;

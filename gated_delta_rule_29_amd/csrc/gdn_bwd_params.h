@@ -1,0 +1,45 @@
+// gdn_bwd_params.h -- host/device parameter blocks of the frame-scan backward kernels that
+// are not shared with the forward (the forward's translation units do not include this file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// The state / gradient scan of the camera-scan backward alone (gdn_cambwd.hip): the forward
+// states and the state gradients from the frame statistics G, U, W in p's workspace views.
+// The BiGDN direction backward reuses it for its S stream.
+hipError_t launch_cam_bwd_scan(const CamBwdParams& p, hipStream_t stream);
+
+// Backward of one BiGDN direction (gdn_bigdnbwd.hip).  Prepped tensors token-major bf16
+// [B,H,N,D]; dnum [B,N,H,D] and dden [B,H,N] fp32; gradients fp32 (dq_rot .. dv [B,H,N,D],
+// dbeta [B,H,F,S], ddecay [B,H,F]).  cam holds the S stream's workspace views (G = K_rot
+// diag(beta) K_rot^T, U = K_rot diag(beta) V^T, W = Q_rot dnum^T, the saved states and
+// their gradients); the z stream adds its own.
+struct BigdnBwdParams {
+  CamBwdParams cam;       // S stream: q, k, v, dout unused here (token-major copies below)
+  const __bf16* q_rot;
+  const __bf16* k_rot;
+  const __bf16* q_pos;
+  const __bf16* k_pos;
+  const __bf16* v;
+  const float* dnum;      // [B,N,H,D]
+  const float* dden;      // [B,H,N]
+  float* dq_rot;
+  float* dk_rot;
+  float* dq_pos;
+  float* dk_pos;
+  float* dv;
+  // z stream workspace, per (b, h, frame or step)
+  float* Gpos;            // K_pos diag(beta) K_pos^T, D x D
+  float* upos;            // K_pos^T beta, D
+  float* wz;              // Q_pos^T dden, D
+  float* zs;              // z after every step, D
+  float* as;              // gradient of z after every step's update, D
+  float* ddz;             // the z stream's part of ddecay, per absorbed frame
+};
+hipError_t launch_bigdn_dir_bwd(const BigdnBwdParams& p, hipStream_t stream);
+
+}  // namespace gdn

@@ -32,6 +32,7 @@
 // lo = bf16(x - hi)) and sums hi*hi + hi*lo + lo*hi in fp32, about 16 mantissa bits per
 // operand.  The page's backward takes plain bf16 operands; their rounding alone moves the
 // gradients by up to 4e-2 of their RMS on the small test shapes.
+#include "gdn_bwd_params.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -429,6 +430,15 @@ hipError_t launch_d(const CamBwdParams& p, hipStream_t stream) {
 
 hipError_t launch_cam_scan_bwd(const CamBwdParams& p, hipStream_t stream) {
   return p.D == 128 ? launch_d<128>(p, stream) : launch_d<64>(p, stream);
+}
+
+hipError_t launch_cam_bwd_scan(const CamBwdParams& p, hipStream_t stream) {
+  const long bh = (long)p.B * p.H;
+  if (p.D == 128)
+    hipLaunchKernelGGL((cbwd_scan_kernel<128>), dim3(bh * 4), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((cbwd_scan_kernel<64>), dim3(bh * 2), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace gdn

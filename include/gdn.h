@@ -22,7 +22,7 @@
  *    gdn_state_apply), and their gradient counterparts (gdn_state_grad_summary,
  *    gdn_state_grad_apply): the single-GPU part of context parallelism;
  *  - the camera branch of the video block (cam_prep, cam_scan, cam_scan_bidi) and the
- *    backward of its scan (cam_scan_bwd);
+ *    backward of its scan (cam_scan_bwd); the backward of a BiGDN direction (bigdn_dir_bwd);
  *  - the backward's inputs (gdn_bwd_prep) and state-gradient pass (gdn_bwd_dhu,
  *    gdn_bwd_dhu_varlen).
  *
@@ -424,6 +424,38 @@ GDN_API int cam_scan_bwd(const float* q, const float* k, const float* v, const f
                          const float* decay, const float* dout, int reverse, float* dq,
                          float* dk, float* dv, float* dbeta, float* ddecay, int B, int H, int D,
                          int F, int S, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bigdn_dir_bwd -- backward of one BiGDN direction (SANA fused_gdn.py page, "Backward /
+ * autograd Functions": the reverse replay of the frame recurrence behind
+ * FusedBiGDNFunction.backward): gradients of L = sum(num * dnum) + sum(den * dden) for the
+ * num, den of one direction of bigdn_fwd on the prepped tensors (reverse = 0 forward, 1
+ * reverse; the block's outputs sum both directions, so the caller runs both and adds).
+ * With S, z the states and A, a their gradients after a step's update (S_pre = g S_prev,
+ * z_pre = g z_prev for the frame the step absorbs), per token:
+ *   output frame:   dq_rot = S dnum,  dq_pos = dden z
+ *   absorbed frame: dv = beta A^T k_rot,  dk_rot = A (beta r) - beta S_pre (A^T k_rot),
+ *                   r = v - S_pre^T k_rot;  dk_pos = a (beta e) - beta (a . k_pos) z_pre,
+ *                   e = 1 - k_pos . z_pre;  dbeta = (A^T k_rot) . r + (a . k_pos) e
+ *   ddecay[f] = <dS_pre, S_prev> + <dz_pre, z_prev> for the frame f absorbed with decay[f].
+ * Frames a direction never absorbs (frame 0 of the reverse one) get zero k, v, beta
+ * gradients; the decay applied to the zero initial state gets 0.
+ *   q_rot, k_rot, q_pos, k_pos, v   [B,H,N,D] bf16 IN (as gdn_prep writes them), N = F * S
+ *   beta [B,H,F,S], decay [B,H,F] fp32 IN; dnum [B,N,H,D], dden [B,H,N] fp32 IN
+ *   dq_rot, dk_rot, dq_pos, dk_pos, dv [B,H,N,D], dbeta [B,H,F,S], ddecay [B,H,F] fp32 OUT
+ *   Products take split bf16 operands (as cam_scan_bwd); the z stream is fp32 arithmetic.
+ *   workspace  at least bigdn_dir_bwd_workspace_bytes(B, H, D, F) bytes, 256-byte aligned
+ *   (per (b, h, frame) the D x D statistics and saved states of the S stream, G_pos and the
+ *   z stream's vectors).
+ * Supported: D in {64, 128}, S a multiple of 64.
+ */
+GDN_API size_t bigdn_dir_bwd_workspace_bytes(int B, int H, int D, int F);
+GDN_API int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_pos,
+                          const void* k_pos, const void* v, const float* beta,
+                          const float* decay, const float* dnum, const float* dden, int reverse,
+                          float* dq_rot, float* dk_rot, float* dq_pos, float* dk_pos, float* dv,
+                          float* dbeta, float* ddecay, int B, int H, int D, int F, int S,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdn_bwd_prep -- the inputs of the state-gradient pass, from the forward's inputs

@@ -189,6 +189,29 @@ def cam_scan_bwd_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
     return inp
 
 
+def bigdn_bwd_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
+    """Inputs of the BiGDN direction backward, with the magnitudes of prepped tensors, all
+    [B,H,N,D] bf16: q_rot, v ~ N(0, 1); q_pos = |N(0, 1)|; k_rot ~ N(0, k_scale^2) and
+    k_pos = |N(0, 1)| k_scale (k_scale = D^-1/2 S^-1/2); beta [B,H,F,S] = sigmoid(N(0, 1));
+    decay [B,H,F] = sigmoid(N(0, 1) + decay_shift); then, from seed + 7919, dnum [B,N,H,D] and
+    dden [B,H,N] ~ N(0, 1) fp32."""
+    gen = _gen(seed)
+    N = F * S
+    ks = 1.0 / math.sqrt(D) / math.sqrt(S)
+    bf = torch.bfloat16
+    inp = {"q_rot": torch.randn(B, H, N, D, generator=gen).to(bf),
+           "k_rot": (ks * torch.randn(B, H, N, D, generator=gen)).to(bf),
+           "q_pos": torch.randn(B, H, N, D, generator=gen).abs().to(bf),
+           "k_pos": (ks * torch.randn(B, H, N, D, generator=gen).abs()).to(bf),
+           "v": torch.randn(B, H, N, D, generator=gen).to(bf),
+           "beta": torch.sigmoid(torch.randn(B, H, F, S, generator=gen)),
+           "decay": torch.sigmoid(torch.randn(B, H, F, generator=gen) + decay_shift)}
+    gen = _gen(seed + 7919)
+    inp["dnum"] = torch.randn(B, N, H, D, generator=gen)
+    inp["dden"] = torch.randn(B, H, N, generator=gen)
+    return inp
+
+
 # The workloads, named by what they are.
 WORKLOADS = {
     "tiny_f32": dict(kind="gdn", B=1, T=256, H=2, K=64, V=64, dtype="f32", seed=0, g_shift=2.0),
@@ -213,6 +236,9 @@ WORKLOADS = {
     # backward of the camera branch's two frame scans at the same shape (fp32 tensors with the
     # magnitudes of prepped ones, upstream gradient N(0, 1))
     "cam_bwd_video_f16x1024": dict(kind="cam_bwd", B=1, F=16, S=1024, H=16, D=128, seed=0),
+    # backward of the BiGDN block's two frame-scan directions at the same shape (prepped bf16
+    # tensors, fp32 upstream gradients)
+    "bigdn_bwd_video_f16x1024": dict(kind="bigdn_bwd", B=1, F=16, S=1024, H=16, D=128, seed=0),
     "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
                                     dtype="bf16", seed=0, g_shift=3.0, per_key=True,
                                     save=True),
@@ -248,4 +274,6 @@ def make(name):
         return dhu_inputs(**w)
     if kind == "cam_bwd":
         return cam_scan_bwd_inputs(**w)
+    if kind == "bigdn_bwd":
+        return bigdn_bwd_inputs(**w)
     raise KeyError(name)
