@@ -17,8 +17,9 @@
 //
 // Kernels:
 //   stats  per (b, h, frame, matrix): G, U, W (the S stream) and G_pos (the z stream) as
-//          D x D fp32, plus the vectors u_pos = K_pos^T beta and w_z = Q_pos^T dden; the token
-//          slabs are transposed into LDS 32 tokens at a time (the contraction runs over tokens)
+//          D x D fp32, plus the vectors u_pos = K_pos^T beta and w_z = Q_pos^T dden; token rows
+//          staged in LDS 32 at a time, operands taken with transpose reads (the contraction
+//          runs over tokens)
 //   S scan the camera backward's scan (states and their gradients as hi/lo pairs)
 //   z scan per (b, h): z after every step and a, by matrix-vector products with G_pos
 //   S tok  per (b, h, step, 64 tokens): as the camera backward's token kernel, with token-
@@ -27,23 +28,40 @@
 // Products take split bf16 operands (GDN_SPLIT); the z stream is fp32 arithmetic.
 #include "gdn_bwd_params.h"
 #include "gdn_device.h"
+#include "gdn_dma.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+using namespace dma;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transpose read of 8 bytes per lane (ds_read_b64_tr_b16); the result is used only as a whole
+// vector (bit casts), as element-wise casts of it have been miscompiled.
+__device__ __forceinline__ u32x2 tr16(const u16* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lds_addr(p)));
+}
 
 // ---- statistics ---------------------------------------------------------------------------
 // blockIdx.x = (bh * F + f) * 4 + which: 0 G (X = beta k_rot, Y = k_rot), 1 U (X = beta k_rot,
 // Y = v), 2 W (X = q_rot, Y = dnum), 3 G_pos (X = beta k_pos, Y = k_pos).  Out[i][j] =
-// sum_s X[s][i] Y[s][j].  Wave w owns rows 16 RT w .., all columns.
+// sum_s X[s][i] Y[s][j].  Wave w owns rows 16 RT w .., all columns.  Per 32-token step the
+// token rows go to LDS as split pairs [token][D] (16-byte copies of the token-major rows),
+// and the operands, whose contraction runs over tokens, come out with transpose reads
+// (ds_read_b64_tr_b16): in each 16-lane group, result lane n takes element j from the 8 bytes
+// that lane 4j + n/4 addresses, halfword n % 4; so lane L addresses token 8 lq + L/4 (+4 for
+// the second half), channels 16 tile + 4 (L % 4) .. + 3, and lane n receives channel
+// 16 tile + n of those tokens.  The next step's rows are loaded while the products run.
 template <int D>
 __global__ __launch_bounds__(256) void bbwd_stats_kernel(const BigdnBwdParams p) {
   constexpr int RT = D / 64, CT = D / 16;
-  constexpr int kX = 40;  // bf16 row stride of the [channel][32 tokens] tiles
-  __shared__ __attribute__((aligned(16))) bf16 xt[2][D * kX];
-  __shared__ __attribute__((aligned(16))) bf16 yt[2][D * kX];
+  constexpr int kR = D + 8;              // bf16 row stride of the [32 tokens][D] tiles
+  constexpr int NI = 32 * D / 8 / 256;   // 8-channel items per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 xt[2][32 * kR];
+  __shared__ __attribute__((aligned(16))) bf16 yt[2][32 * kR];
   const CamBwdParams& c = p.cam;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
   const int which = blockIdx.x % 4;
@@ -62,51 +80,76 @@ __global__ __launch_bounds__(256) void bbwd_stats_kernel(const BigdnBwdParams p)
   for (int r = 0; r < RT; ++r)
 #pragma unroll
     for (int cc = 0; cc < CT; ++cc) acc[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int t = tid % 32, cg = tid / 32;  // this thread's token and first channel group
-  for (int s0 = 0; s0 < c.S; s0 += 32) {
-    const long tok = t0f + s0 + t;
-    const float sc = xbeta ? bt[s0 + t] : 1.f;
+  // item i of this thread: token (tid + 256 i) / (D / 8), channels 8 ((tid + 256 i) % (D / 8)) ..
+  bf16x8 xr[NI], qr[NI];
+  f32x4 yr[NI][2];
+  float br[NI], dr[NI];
+  // the z stream's vector (which 2: w_z = Q_pos^T dden; which 3: u_pos = K_pos^T beta), summed
+  // over this thread's tokens for its 8 channels
+  float vacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int s0) {
 #pragma unroll
-    for (int g8 = cg; g8 < D / 8; g8 += 8) {
-      const bf16x8 xr = *reinterpret_cast<const bf16x8*>(X + (bh * N + tok) * D + 8 * g8);
-      float y[8];
+    for (int i = 0; i < NI; ++i) {
+      const int e = tid + 256 * i, t = e / (D / 8), d = 8 * (e % (D / 8));
+      const long tok = t0f + s0 + t;
+      xr[i] = *reinterpret_cast<const bf16x8*>(X + (bh * N + tok) * D + d);
+      br[i] = xbeta ? bt[s0 + t] : 1.f;
       if (which == 2) {
-        const float* src = p.dnum + (((long)b * N + tok) * c.H + h) * D + 8 * g8;
-        const f32x4 y0 = *reinterpret_cast<const f32x4*>(src), y1 = *reinterpret_cast<const f32x4*>(src + 4);
+        qr[i] = *reinterpret_cast<const bf16x8*>(p.q_pos + (bh * N + tok) * D + d);
+        dr[i] = p.dden[bh * N + tok];
+      }
+      if (which == 2) {
+        const float* src = p.dnum + (((long)b * N + tok) * c.H + h) * D + d;
+        yr[i][0] = *reinterpret_cast<const f32x4*>(src);
+        yr[i][1] = *reinterpret_cast<const f32x4*>(src + 4);
+      } else {
+        const bf16x8 y = *reinterpret_cast<const bf16x8*>(Y + (bh * N + tok) * D + d);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          y[j] = y0[j];
-          y[4 + j] = y1[j];
+          yr[i][0][j] = (float)y[j];
+          yr[i][1][j] = (float)y[4 + j];
         }
-      } else {
-        const bf16x8 yr = *reinterpret_cast<const bf16x8*>(Y + (bh * N + tok) * D + 8 * g8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = (float)yr[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int o = (8 * g8 + j) * kX + t;
-        bf16 a0, a1, b0, b1;
-        GDN_SPLIT((float)xr[j] * sc, a0, a1);
-        GDN_SPLIT(y[j], b0, b1);
-        xt[0][o] = a0;
-        xt[1][o] = a1;
-        yt[0][o] = b0;
-        yt[1][o] = b1;
       }
     }
+  };
+  // two transpose reads of tile T (channels 16 tile ..): the B / A operand of 8 tokens
+  const int L = lane & 15;
+  auto tr8 = [&](const bf16* T, int tile) {
+    const int o = (8 * lq + L / 4) * kR + 16 * tile + 4 * (L % 4);
+    const u32x4 v = __builtin_shufflevector(tr16(reinterpret_cast<const u16*>(T + o)),
+                                            tr16(reinterpret_cast<const u16*>(T + o + 4 * kR)),
+                                            0, 1, 2, 3);
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  load(0);
+  for (int s0 = 0; s0 < c.S; s0 += 32) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int e = tid + 256 * i, t = e / (D / 8), d = 8 * (e % (D / 8));
+      bf16x8 xh, xl, yh, yl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        GDN_SPLIT((float)xr[i][j] * br[i], xh[j], xl[j]);
+        GDN_SPLIT(yr[i][j / 4][j % 4], yh[j], yl[j]);
+        if (which == 2) vacc[j] = fmaf(dr[i], (float)qr[i][j], vacc[j]);
+        if (which == 3) vacc[j] = fmaf(br[i], (float)xr[i][j], vacc[j]);
+      }
+      *reinterpret_cast<bf16x8*>(&xt[0][t * kR + d]) = xh;
+      *reinterpret_cast<bf16x8*>(&xt[1][t * kR + d]) = xl;
+      *reinterpret_cast<bf16x8*>(&yt[0][t * kR + d]) = yh;
+      *reinterpret_cast<bf16x8*>(&yt[1][t * kR + d]) = yl;
+    }
     __syncthreads();
+    if (s0 + 32 < c.S) load(s0 + 32);
     bf16x8 ah[RT], al[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int o = (16 * (RT * w + r) + li) * kX + 8 * lq;
-      ah[r] = lds8(&xt[0][o]);
-      al[r] = lds8(&xt[1][o]);
+      ah[r] = tr8(xt[0], RT * w + r);
+      al[r] = tr8(xt[1], RT * w + r);
     }
 #pragma unroll
     for (int cc = 0; cc < CT; ++cc) {
-      const int o = (16 * cc + li) * kX + 8 * lq;
-      const bf16x8 bh_ = lds8(&yt[0][o]), bl = lds8(&yt[1][o]);
+      const bf16x8 bh_ = tr8(yt[0], cc), bl = tr8(yt[1], cc);
 #pragma unroll
       for (int r = 0; r < RT; ++r) acc[r][cc] = mma3(ah[r], al[r], bh_, bl, acc[r][cc]);
     }
@@ -119,56 +162,79 @@ __global__ __launch_bounds__(256) void bbwd_stats_kernel(const BigdnBwdParams p)
     for (int cc = 0; cc < CT; ++cc)
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[(16 * (RT * w + r) + 4 * lq + e) * D + 16 * cc + li] = acc[r][cc][e];
-  // the z stream's vectors: w_z = Q_pos^T dden (with W), u_pos = K_pos^T beta (with G_pos)
-  if (which >= 2 && tid < D) {
-    float s = 0.f;
-    for (int sI = 0; sI < c.S; ++sI) {
-      const long tok = t0f + sI;
-      const float wt = which == 2 ? p.dden[bh * N + tok] : bt[sI];
-      s += wt * (float)(which == 2 ? p.q_pos : p.k_pos)[(bh * N + tok) * D + tid];
+  // the z stream's vectors: the threads of one channel group (tid % (D / 8) equal; the item
+  // offset 256 i keeps the group) add their sums through LDS
+  if (which >= 2) {
+    constexpr int TG = 256 / (D / 8);  // threads per channel group
+    float* red = reinterpret_cast<float*>(&xt[0][0]);  // [TG][D], after the last barrier
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[(tid / (D / 8)) * D + 8 * (tid % (D / 8)) + j] = vacc[j];
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.f;
+      for (int q = 0; q < TG; ++q) sum += red[q * D + tid];
+      (which == 2 ? p.wz : p.upos)[bf * D + tid] = sum;
     }
-    (which == 2 ? p.wz : p.upos)[bf * D + tid] = s;
   }
 }
 
 // ---- z scan --------------------------------------------------------------------------------
-// One workgroup per (b, h).  y = G_pos x with P = 256 / D threads per row (adjacent lanes).
+// One workgroup of 1024 threads per (b, h).  y = G_pos x: G_pos is symmetric, so
+// y[i] = sum_j G_pos[j][i] x[j]; thread (part, i) takes the rows j = part + P m (m < D / P),
+// reading element i of each (consecutive lanes, consecutive elements), and the P partial sums
+// meet in LDS.  The next step's elements are loaded into registers while a step runs.
 template <int D>
-__global__ __launch_bounds__(256) void bbwd_zscan_kernel(const BigdnBwdParams p) {
-  constexpr int P = 256 / D;
-  __shared__ float zv[D], xv[D], red[4];
+__global__ __launch_bounds__(1024) void bbwd_zscan_kernel(const BigdnBwdParams p) {
+  constexpr int P = 1024 / D, M = D / P;
+  __shared__ float zv[D], xv[D], red[16], ps[P][D];
   const CamBwdParams& c = p.cam;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const long bh = blockIdx.x;
   const int F = c.F;
-  const int row = tid / P, part = tid % P;
-  // y[row] = sum_j M[row][j] x[j] (this thread: columns j = part, part + P, ...)
-  auto matvec = [&](const float* M, const float* x) {
-    float s = 0.f;
-    for (int j = part; j < D; j += P) s += M[(size_t)row * D + j] * x[j];
-    s += __shfl_xor(s, 1, 64);
-    if (P == 4) s += __shfl_xor(s, 2, 64);
-    return s;
+  const int row = tid % D, part = tid / D;
+  float gc[M], gn[M];
+  auto fetch = [&](int fa, float (&o)[M]) {
+    const float* G = p.Gpos + (bh * F + fa) * D * D;
+#pragma unroll
+    for (int m = 0; m < M; ++m) o[m] = G[(size_t)(part + P * m) * D + row];
   };
+  // y[row] in the threads with part == 0
+  auto matvec = [&](const float* x) {
+    float sum = 0.f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) sum = fmaf(gc[m], x[part + P * m], sum);
+    ps[part][row] = sum;
+    __syncthreads();
+    float y = 0.f;
+    if (part == 0)
+#pragma unroll
+      for (int q = 0; q < P; ++q) y += ps[q][row];
+    return y;
+  };
+  auto fa_of = [&](int it) { return c.reverse ? F - it : it; };  // frame absorbed at step it
   if (tid < D) zv[tid] = 0.f;
+  const int first = c.reverse ? 1 : 0;  // the first step that absorbs a frame
+  if (first < F) fetch(fa_of(first), gc);
   __syncthreads();
   for (int it = 0; it < F; ++it) {
-    const int f = c.reverse ? F - 1 - it : it;
     if (!(c.reverse && it == 0)) {
-      const int fa = c.reverse ? f + 1 : f;
+      const int fa = fa_of(it);
+      if (it + 1 < F) fetch(fa_of(it + 1), gn);
       const float g = c.decay[bh * F + fa];
       if (tid < D) xv[tid] = g * zv[tid];  // z_pre
       __syncthreads();
-      const float y = matvec(p.Gpos + (bh * F + fa) * D * D, xv);
-      __syncthreads();
+      const float y = matvec(xv);
       if (part == 0) zv[row] = xv[row] - y + p.upos[(bh * F + fa) * D + row];
       __syncthreads();
+#pragma unroll
+      for (int m = 0; m < M; ++m) gc[m] = gn[m];
     }
     if (tid < D) p.zs[(bh * F + it) * D + tid] = zv[tid];
   }
   // gradients of z after each step's update, in reverse (zv holds a)
   __syncthreads();
   if (tid < D) zv[tid] = 0.f;
+  if (!(c.reverse && F - 1 == 0)) fetch(fa_of(F - 1), gc);
   __syncthreads();
   for (int it = F - 1; it >= 0; --it) {
     const int f = c.reverse ? F - 1 - it : it;
@@ -178,11 +244,12 @@ __global__ __launch_bounds__(256) void bbwd_zscan_kernel(const BigdnBwdParams p)
     }
     __syncthreads();
     if (c.reverse && it == 0) break;
-    const int fa = c.reverse ? f + 1 : f;
+    const int fa = fa_of(it);
+    if (it - 1 >= 0 && !(c.reverse && it - 1 == 0)) fetch(fa_of(it - 1), gn);
     const float g = c.decay[bh * F + fa];
-    const float y = matvec(p.Gpos + (bh * F + fa) * D * D, zv);  // G_pos is symmetric
+    const float y = matvec(zv);  // G_pos is symmetric
     float part_dd = 0.f;
-    __syncthreads();  // every thread has read zv
+    __syncthreads();  // every thread has read zv and ps
     if (part == 0) {
       const float dzp = zv[row] - y;
       if (it > 0) part_dd = dzp * p.zs[(bh * F + it - 1) * D + row];
@@ -192,7 +259,13 @@ __global__ __launch_bounds__(256) void bbwd_zscan_kernel(const BigdnBwdParams p)
     for (int off = 32; off > 0; off >>= 1) part_dd += __shfl_xor(part_dd, off, 64);
     if (lane == 0) red[w] = part_dd;
     __syncthreads();
-    if (tid == 0) p.ddz[bh * F + fa] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (tid == 0) {
+      float sum = 0.f;
+      for (int q = 0; q < 16; ++q) sum += red[q];
+      p.ddz[bh * F + fa] = sum;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) gc[m] = gn[m];
   }
 }
 
@@ -453,7 +526,7 @@ hipError_t launch_d(const BigdnBwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((bbwd_stats_kernel<D>), dim3(bh * c.F * 4), dim3(256), 0, stream, p);
   hipError_t e = launch_cam_bwd_scan(c, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bbwd_zscan_kernel<D>), dim3(bh), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bbwd_zscan_kernel<D>), dim3(bh), dim3(1024), 0, stream, p);
   const dim3 tg(bh * c.F * (c.S / 64));
   hipLaunchKernelGGL((bbwd_tok_kernel<D>), tg, dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bbwd_ztok_kernel<D>), tg, dim3(256), 0, stream, p);

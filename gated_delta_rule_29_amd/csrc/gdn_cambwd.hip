@@ -19,8 +19,8 @@
 //
 // Kernels:
 //   stats  per (b, h, frame, matrix): G, U, W (D x D fp32) with 16x16x32 bf16 matrix products;
-//          a channel-major slab row is already in operand order (8 consecutive tokens of one
-//          channel per lane), so the operands are loaded straight from memory.
+//          a channel-major slab row is already in operand order (consecutive tokens of one
+//          channel), so the slabs go to LDS 32 tokens at a time without a transpose.
 //   scan   per (b, h, 32 state columns): the forward states and then A, in fp32 (16x16x4
 //          fp32 matrix products, the state in LDS); every step's state and A leave as hi/lo
 //          bf16 pairs in both orientations for the token kernel, the states also in fp32 for
@@ -42,23 +42,19 @@ namespace {
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// 8 fp32 at p (32-byte aligned), times s[j], as a hi/lo bf16 pair
-__device__ __forceinline__ void ld_split8(const float* p, const float* s, bf16x8& h, bf16x8& l) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    GDN_SPLIT(s ? a[j] * s[j] : a[j], h[j], l[j]);
-    GDN_SPLIT(s ? b[j] * s[4 + j] : b[j], h[4 + j], l[4 + j]);
-  }
-}
-
 // ---- stats: G_f, U_f, W_f ----------------------------------------------------------------
 // blockIdx.x = (bh * F + f) * 3 + which; four waves, wave w owns rows 16 RT w .. of the D x D
-// result, all columns.
+// result, all columns.  Per 32-token step the two slabs go to LDS as split pairs [channel][32
+// tokens] (a slab row is already token-contiguous), shared by the four waves; the next
+// step's rows are loaded into registers while the current step's products run.
 template <int D>
 __global__ __launch_bounds__(256) void cbwd_stats_kernel(const CamBwdParams p) {
   constexpr int RT = D / 64, CT = D / 16;  // row tiles per wave, column tiles
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
+  constexpr int kX = 40;                   // bf16 row stride of the [channel][32] tiles
+  constexpr int NI = D * 4 / 256;          // (channel, token octet) items per thread per slab
+  __shared__ __attribute__((aligned(16))) bf16 xt[2][D * kX];
+  __shared__ __attribute__((aligned(16))) bf16 yt[2][D * kX];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
   const int which = blockIdx.x % 3;
   const long bf = blockIdx.x / 3;
   const int f = (int)(bf % p.F);
@@ -73,20 +69,60 @@ __global__ __launch_bounds__(256) void cbwd_stats_kernel(const CamBwdParams p) {
   for (int r = 0; r < RT; ++r)
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // item i of this thread: channel (tid + 256 i) / 4, tokens 8 ((tid + 256 i) % 4) ..
+  f32x4 xr[NI][2], yr[NI][2], br[2];
+  const int oc = tid % 4;  // token octet (the same for every item)
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int ch = (tid + 256 * i) / 4;
+      const float* xs = X + base + (long)ch * N + t0 + 8 * oc;
+      const float* ys = Y + base + (long)ch * N + t0 + 8 * oc;
+      xr[i][0] = *reinterpret_cast<const f32x4*>(xs);
+      xr[i][1] = *reinterpret_cast<const f32x4*>(xs + 4);
+      yr[i][0] = *reinterpret_cast<const f32x4*>(ys);
+      yr[i][1] = *reinterpret_cast<const f32x4*>(ys + 4);
+    }
+    if (which != 2) {
+      br[0] = *reinterpret_cast<const f32x4*>(bt + t0 + 8 * oc);
+      br[1] = *reinterpret_cast<const f32x4*>(bt + t0 + 8 * oc + 4);
+    } else {
+      br[0] = br[1] = f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+  };
+  load(0);
   for (int t0 = 0; t0 < p.S; t0 += 32) {
-    const int tt = t0 + 8 * lq;
-    float sc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sc[j] = which == 2 ? 1.f : bt[tt + j];
-    bf16x8 ah[RT], al[RT], bh[CT], bl[CT];
+    for (int i = 0; i < NI; ++i) {
+      const int ch = (tid + 256 * i) / 4, o = ch * kX + 8 * oc;
+      bf16x8 xh, xl, yh, yl;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) ld_split8(X + base + (long)(16 * (RT * w + r) + li) * N + tt, sc, ah[r], al[r]);
+      for (int j = 0; j < 8; ++j) {
+        GDN_SPLIT(xr[i][j / 4][j % 4] * br[j / 4][j % 4], xh[j], xl[j]);
+        GDN_SPLIT(yr[i][j / 4][j % 4], yh[j], yl[j]);
+      }
+      *reinterpret_cast<bf16x8*>(&xt[0][o]) = xh;
+      *reinterpret_cast<bf16x8*>(&xt[1][o]) = xl;
+      *reinterpret_cast<bf16x8*>(&yt[0][o]) = yh;
+      *reinterpret_cast<bf16x8*>(&yt[1][o]) = yl;
+    }
+    __syncthreads();
+    if (t0 + 32 < p.S) load(t0 + 32);
+    bf16x8 ah[RT], al[RT];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) ld_split8(Y + base + (long)(16 * c + li) * N + tt, nullptr, bh[c], bl[c]);
+    for (int r = 0; r < RT; ++r) {
+      const int o = (16 * (RT * w + r) + li) * kX + 8 * lq;
+      ah[r] = lds8(&xt[0][o]);
+      al[r] = lds8(&xt[1][o]);
+    }
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int c = 0; c < CT; ++c) {
+      const int o = (16 * c + li) * kX + 8 * lq;
+      const bf16x8 bh_ = lds8(&yt[0][o]), bl = lds8(&yt[1][o]);
 #pragma unroll
-      for (int c = 0; c < CT; ++c) acc[r][c] = mma3(ah[r], al[r], bh[c], bl[c], acc[r][c]);
+      for (int r = 0; r < RT; ++r) acc[r][c] = mma3(ah[r], al[r], bh_, bl, acc[r][c]);
+    }
+    __syncthreads();
   }
   float* out = (which == 0 ? p.G : (which == 1 ? p.U : p.W)) + bf * D * D;
 #pragma unroll
@@ -113,24 +149,44 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
   const size_t DD = (size_t)D * D;
   for (int e = threadIdx.x; e < 32 * kS; e += 256) (&st[0][0])[e] = 0.f;
   __syncthreads();
-  // T = M st (rows of this wave, the block's 32 columns): tile (r, c) holds rows
-  // 16 (RT w + r) + 4 lq + e, column 16 c + li
-  auto prod = [&](const float* M, f32x4 (&T)[RT][2]) {
+  // T = M st (rows of this wave, the block's 32 columns) with M's A operands already in
+  // registers: tile (r, c) holds rows 16 (RT w + r) + 4 lq + e, column 16 c + li
+  constexpr int KK = D / 32;
+  struct Ops {
+    f32x8 a[RT][KK];     // rows 16 (RT w + r) + li of G, columns 32 kk + 8 lq ..
+    float x[RT][2][4];   // U (forward) or W (backward) at this lane's elements
+    float y[RT][2][4];   // the state before the step (backward)
+    float g;
+  };
+  auto fetch_g = [&](const float* M, Ops& o) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) o.a[r][kk] = lds8(M + (16 * (RT * w + r) + li) * D + 32 * kk + 8 * lq);
+  };
+  auto fetch_el = [&](const float* M, float (&x)[RT][2][4]) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[r][c][e] = M ? M[(size_t)(16 * (RT * w + r) + 4 * lq + e) * D + c0 + 16 * c + li] : 0.f;
+  };
+  auto prod = [&](const Ops& o, f32x4 (&T)[RT][2]) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int c = 0; c < 2; ++c) T[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      f32x8 a[RT], b[2];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) a[r] = lds8(M + (16 * (RT * w + r) + li) * D + 32 * kk + 8 * lq);
+    for (int kk = 0; kk < KK; ++kk) {
+      f32x8 b[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) b[c] = lds8(&st[16 * c + li][32 * kk + 8 * lq]);
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) T[r][c] = mma16(a[r], b[c], T[r][c]);
+        for (int c = 0; c < 2; ++c) T[r][c] = mma16(o.a[r][kk], b[c], T[r][c]);
     }
   };
   // this lane's elements: row i = 16 (RT w + r) + 4 lq + e, column j = 16 c + li of the block
@@ -157,16 +213,21 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
       }
   };
 
-  // ---- forward states
+  // ---- forward states; the operands of step it + 1 are loaded while step it runs
+  auto fetch_fwd = [&](int it, Ops& o) {
+    if (it >= F || (p.reverse && it == 0)) return;
+    const int fa = p.reverse ? F - it : it;
+    o.g = p.decay[bh * F + fa];
+    fetch_g(p.G + ((size_t)bh * F + fa) * DD, o);
+    fetch_el(p.U + ((size_t)bh * F + fa) * DD, o.x);
+  };
+  Ops cur, nxt;
+  fetch_fwd(0, cur);
   for (int it = 0; it < F; ++it) {
-    const int f = p.reverse ? F - 1 - it : it;
+    fetch_fwd(it + 1, nxt);
     if (!(p.reverse && it == 0)) {
-      const int fa = p.reverse ? f + 1 : f;
-      const float g = p.decay[bh * F + fa];
-      const float* G = p.G + ((size_t)bh * F + fa) * DD;
-      const float* U = p.U + ((size_t)bh * F + fa) * DD;
       f32x4 T[RT][2];
-      prod(G, T);
+      prod(cur, T);
       __syncthreads();  // every wave has read st
 #pragma unroll
       for (int r = 0; r < RT; ++r)
@@ -175,19 +236,31 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 16 * (RT * w + r) + 4 * lq + e, jl = 16 * c + li;
-            st[jl][i] = g * (st[jl][i] - T[r][c][e]) + U[(size_t)i * D + c0 + jl];
+            st[jl][i] = cur.g * (st[jl][i] - T[r][c][e]) + cur.x[r][c][e];
           }
       __syncthreads();
     }
     save(it, false);
+    cur = nxt;
   }
-  // ---- state gradients, steps in reverse
+  // ---- state gradients, steps in reverse (operands of step it - 1 loaded during step it)
+  auto fetch_bwd = [&](int it, Ops& o) {
+    if (it < 0) return;
+    const int f = p.reverse ? F - 1 - it : it;
+    fetch_el(p.W + ((size_t)bh * F + f) * DD, o.x);
+    if (p.reverse && it == 0) return;
+    const int fa = p.reverse ? f + 1 : f;
+    o.g = p.decay[bh * F + fa];
+    fetch_g(p.G + ((size_t)bh * F + fa) * DD, o);
+    fetch_el(it > 0 ? p.Spf + ((size_t)bh * F + it - 1) * DD : nullptr, o.y);
+  };
   __syncthreads();
   for (int e = threadIdx.x; e < 32 * kS; e += 256) (&st[0][0])[e] = 0.f;
   __syncthreads();
+  fetch_bwd(F - 1, cur);
   for (int it = F - 1; it >= 0; --it) {
     const int f = p.reverse ? F - 1 - it : it;
-    const float* W = p.W + ((size_t)bh * F + f) * DD;
+    fetch_bwd(it - 1, nxt);
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -195,19 +268,16 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * (RT * w + r) + 4 * lq + e, jl = 16 * c + li;
-          st[jl][i] += W[(size_t)i * D + c0 + jl];
+          st[jl][i] += cur.x[r][c][e];
         }
     __syncthreads();
     save(it, true);
     if (p.reverse && it == 0) break;
     const int fa = p.reverse ? f + 1 : f;
-    const float g = p.decay[bh * F + fa];
-    const float* G = p.G + ((size_t)bh * F + fa) * DD;
     f32x4 T[RT][2];
-    prod(G, T);
+    prod(cur, T);
     __syncthreads();
     // dP = A - G A; its sum against the state before the step (zero before the first step)
-    const float* prev = it > 0 ? p.Spf + ((size_t)bh * F + it - 1) * DD : nullptr;
     float part = 0.f;
 #pragma unroll
     for (int r = 0; r < RT; ++r)
@@ -217,8 +287,8 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * (RT * w + r) + 4 * lq + e, jl = 16 * c + li;
           const float dp = st[jl][i] - T[r][c][e];
-          if (prev) part += dp * prev[(size_t)i * D + c0 + jl];
-          st[jl][i] = g * dp;
+          part += dp * cur.y[r][c][e];
+          st[jl][i] = cur.g * dp;
         }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
@@ -226,6 +296,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
     __syncthreads();
     if (threadIdx.x == 0)
       p.ddecay_part[((size_t)bh * F + fa) * (D / 32) + blockIdx.x % (D / 32)] = (red[0] + red[1]) + (red[2] + red[3]);
+    cur = nxt;
   }
 }
 
