@@ -64,8 +64,9 @@ __global__ __launch_bounds__(256) void bbwd_stats_kernel(const BigdnBwdParams p)
   __shared__ __attribute__((aligned(16))) bf16 yt[2][32 * kR];
   const CamBwdParams& c = p.cam;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
-  const int which = blockIdx.x % 4;
-  const long bf = blockIdx.x / 4;
+  const int bid = xcd_logical(blockIdx.x, gridDim.x);
+  const int which = bid % 4;
+  const long bf = bid / 4;
   const int f = (int)(bf % c.F);
   const long bh = bf / c.F;
   const int b = (int)(bh / c.H), h = (int)(bh % c.H);
@@ -282,8 +283,9 @@ __global__ __launch_bounds__(256) void bbwd_tok_kernel(const BigdnBwdParams p) {
   const CamBwdParams& c = p.cam;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
   const int nblk = c.S / 64;
-  const int blk = blockIdx.x % nblk;
-  const long sb = blockIdx.x / nblk;
+  const int bid = xcd_logical(blockIdx.x, gridDim.x);
+  const int blk = bid % nblk;
+  const long sb = bid / nblk;
   const int F = c.F;
   const int it = (int)(sb % F);
   const long bh = sb / F;
@@ -466,8 +468,9 @@ __global__ __launch_bounds__(256) void bbwd_ztok_kernel(const BigdnBwdParams p) 
   const CamBwdParams& c = p.cam;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nblk = c.S / 64;
-  const int blk = blockIdx.x % nblk;
-  const long sb = blockIdx.x / nblk;
+  const int bid = xcd_logical(blockIdx.x, gridDim.x);
+  const int blk = bid % nblk;
+  const long sb = bid / nblk;
   const int F = c.F;
   const int it = (int)(sb % F);
   const long bh = sb / F;

@@ -8,6 +8,13 @@
 
 namespace gdn {
 
+// Workgroup ids are dealt to the eight XCDs round-robin.  When the grid is a multiple of eight,
+// XCD x takes the contiguous range [x n/8, (x+1) n/8) of logical indices in order, so logical
+// neighbours (which read the same slabs or matrices) run close in time on one XCD's L2.
+__device__ __forceinline__ int xcd_logical(int bid, int n) {
+  return n % 8 ? bid : (bid % 8) * (n / 8) + bid / 8;
+}
+
 // The state / gradient scan of the camera-scan backward alone (gdn_cambwd.hip): the forward
 // states and the state gradients from the frame statistics G, U, W in p's workspace views.
 // The BiGDN direction backward reuses it for its S stream.

@@ -55,8 +55,9 @@ __global__ __launch_bounds__(256) void cbwd_stats_kernel(const CamBwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 xt[2][D * kX];
   __shared__ __attribute__((aligned(16))) bf16 yt[2][D * kX];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
-  const int which = blockIdx.x % 3;
-  const long bf = blockIdx.x / 3;
+  const int bid = xcd_logical(blockIdx.x, gridDim.x);
+  const int which = bid % 3;
+  const long bf = bid / 3;
   const int f = (int)(bf % p.F);
   const long bh = bf / p.F;
   const long N = (long)p.F * p.S;
@@ -143,8 +144,9 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
   __shared__ float st[32][kS];
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
-  const long bh = blockIdx.x / (D / 32);
-  const int c0 = 32 * (blockIdx.x % (D / 32));
+  const int bid = xcd_logical(blockIdx.x, gridDim.x);
+  const long bh = bid / (D / 32);
+  const int c0 = 32 * (bid % (D / 32));
   const int F = p.F;
   const size_t DD = (size_t)D * D;
   for (int e = threadIdx.x; e < 32 * kS; e += 256) (&st[0][0])[e] = 0.f;
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
     if (lane == 0) red[w] = part;
     __syncthreads();
     if (threadIdx.x == 0)
-      p.ddecay_part[((size_t)bh * F + fa) * (D / 32) + blockIdx.x % (D / 32)] = (red[0] + red[1]) + (red[2] + red[3]);
+      p.ddecay_part[((size_t)bh * F + fa) * (D / 32) + bid % (D / 32)] = (red[0] + red[1]) + (red[2] + red[3]);
     cur = nxt;
   }
 }
@@ -312,8 +314,9 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
   __shared__ float red[4][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
   const int nblk = p.S / 64;
-  const int blk = blockIdx.x % nblk;
-  const long sb = blockIdx.x / nblk;
+  const int bid = xcd_logical(blockIdx.x, gridDim.x);
+  const int blk = bid % nblk;
+  const long sb = bid / nblk;
   const int F = p.F;
   const int it = (int)(sb % F);
   const long bh = sb / F;
