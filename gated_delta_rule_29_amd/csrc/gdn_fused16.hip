@@ -138,9 +138,8 @@ __device__ __forceinline__ f32x4 mma16x16x16(const f16x4& a, const f16x4& b, con
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// The lane index, opaque to the optimiser: addresses derived from it inside a loop are
-// recomputed each iteration (a few integer operations) instead of being hoisted out and kept
-// in registers for the whole loop.
+// The lane index, opaque to the optimiser: addresses derived from it are recomputed where
+// they are used instead of being kept in registers from an earlier computation.
 __device__ __forceinline__ int opaque_lane() {
   int l = __lane_id();
   asm volatile("" : "+v"(l));
@@ -184,7 +183,7 @@ template <int K, bool ISQ, unsigned MASK, bool FAST>
 __device__ __forceinline__ void prod_tiles(const bf16* qt, const bf16* kt, const float* G,
                                            u16* dst, float scale) {
   constexpr int kG = K / 32;
-  const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+  const int lane = __lane_id(), li = lane & 15, lq = lane >> 4;
   constexpr auto tile_on = [](int I, int J) { return ((MASK >> (I * (I + 1) / 2 + J)) & 1u) != 0; };
   constexpr auto row_on = [](int I) {
     for (int J = 0; J <= I; ++J)
@@ -396,183 +395,194 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
     //     (pq 0: column 0; pq 1: columns 1, 2)
     //   pq 2 (wave 6): off-diagonal Gram tiles -> A (fp16 rows)
     //   pq 3 (wave 7): Q K^T tiles -> P
-    const int pq = wave == 2 ? 0 : wave == 3 ? 1 : wave == 6 ? 2 : 3;
-    unsigned pbt = 0;
-    if (pq == 0 && lane == 0) s.pbar = 0u;
-    // upper 16x16 tiles (0,1) and (2,3) of Tm and P stay zero in both slots
-    for (int e = 64 * pq + lane; e < 2 * 2 * 2 * 256; e += 256) {
-      const int slot = e >> 10, which = (e >> 9) & 1, t = (e >> 8) & 1, rr = (e >> 4) & 15, cc = e & 15;
-      u16* tile = which ? s.tp[slot].p : s.tp[slot].tm;
-      tile[tix(32 * t + rr, 32 * t + 16 + cc)] = 0;
-    }
-    __syncthreads();
-
-    for (int n = -1; n < nchunks; ++n) {
-      const int m = n + 1;  // chunk prepared in this step
-      if (m < nchunks) {
-        const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
-        typename SM::TP& T = s.tp[m & 1];
-        const typename SM::QK& Q = s.qk[m % 3];
-        const float* G = s.gate[m % 3];
-        const bf16* qt = reinterpret_cast<const bf16*>(Q.q);
-        const bf16* kt = reinterpret_cast<const bf16*>(Q.k);
-        f16* tmt = reinterpret_cast<f16*>(T.tm);
-        f16* aft = reinterpret_cast<f16*>(s.af);
-        const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(G[kFast])) != 0;
-        f16x4 tc0;  // C-form (accumulator layout) of this wave's first diagonal block of Tm
-
-        // The products below take the rows of their second factor as the A operand, so a
-        // lane's accumulator of tile (I, J) holds columns s = 16J + 4lq + e of row
-        // r = 16I + li ("row form", the A-operand layout of the product); the Gram tile is
-        // symmetric, so the same accumulator also gives the C form r = 16I + 4lq + e,
-        // s = 16I + li of a diagonal block.  decay(r, s) = e^{gamma_r - gamma_s} (times
-        // beta_r unless the Q K^T tile is meant), from per-token factors or, when the chunk
-        // decays too fast for them, from gamma itself.
-        auto body = [&](auto fast_c) {
-          constexpr bool kFastDecay = decltype(fast_c)::value;
-          auto rowv = [&](int r, bool qk) -> float {
-            return kFastDecay ? G[(qk ? kFrq : kFrk) + r] : G[kGam + r];
-          };
-          auto colv = [&](int c) -> float { return kFastDecay ? G[kFc + c] : G[kGam + c]; };
-          auto rows4 = [&](int r0, bool qk) -> f32x4 {
-            return *reinterpret_cast<const f32x4*>(&G[(kFastDecay ? (qk ? kFrq : kFrk) : kGam) + r0]);
-          };
-          auto cols4 = [&](int c0) -> f32x4 {
-            return *reinterpret_cast<const f32x4*>(&G[(kFastDecay ? kFc : kGam) + c0]);
-          };
-          auto dec = [&](float rv, float cv, float beta_r) -> float {
-            if constexpr (kFastDecay) return rv * cv;
-            else return beta_r * __expf(rv - cv);
-          };
-
-          if (pq < 2) {
-            // ---- diagonal blocks b = 2pq, 2pq + 1: Gram tile, then (I + L)^-1 as
-            // (I - L)(I + L^2)(I + L^4)(I + L^8) (L strictly lower, L^16 = 0) on fp16 operands
-            bf16x8 kf[2][kG];
-#pragma unroll
-            for (int kk = 0; kk < kG; ++kk)
-#pragma unroll
-              for (int u = 0; u < 2; ++u) kf[u][kk] = lds8(kt + tix(16 * (2 * pq + u) + li, 32 * kk + 8 * lq));
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 g[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int kk = 0; kk < kG; ++kk)
-#pragma unroll
-              for (int u = 0; u < 2; ++u) g[u] = mma16(kf[u][kk], kf[u][kk], g[u]);
-            f16x4 la[2], lc[2];
-            f32x4 x0a[2], x0c[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int b0 = 16 * (2 * pq + u);
-              const float r_li = rowv(b0 + li, false), c_li = colv(b0 + li);
-              const float be_li = kFastDecay ? 1.f : G[kBeta + b0 + li];
-              const f32x4 r_q = rows4(b0 + 4 * lq, false), c_q = cols4(b0 + 4 * lq);
-              f32x4 be_q = {1.f, 1.f, 1.f, 1.f};
-              if constexpr (!kFastDecay) be_q = *reinterpret_cast<const f32x4*>(&G[kBeta + b0 + 4 * lq]);
-              f32x4 va, vc;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int c = 4 * lq + e;
-                va[e] = (c < li) ? dec(r_li, c_q[e], be_li) * g[u][e] : 0.f;   // L[li][c]
-                vc[e] = (li < c) ? dec(r_q[e], c_li, be_q[e]) * g[u][e] : 0.f;  // L[c][li]
-                x0a[u][e] = (c == li ? 1.f : 0.f) - va[e];
-                x0c[u][e] = (c == li ? 1.f : 0.f) - vc[e];
-              }
-              la[u] = cvt_f16x4(va);
-              lc[u] = cvt_f16x4(vc);
-            }
-            f16x4 p2a[2], p2c[2], p4a[2], p4c[2], p8c[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              p2c[u] = cvt_f16x4(mma16x16x16(la[u], lc[u], f32x4{0.f, 0.f, 0.f, 0.f}));
-              p2a[u] = cvt_f16x4(mma16x16x16(lc[u], la[u], f32x4{0.f, 0.f, 0.f, 0.f}));
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              p4c[u] = cvt_f16x4(mma16x16x16(p2a[u], p2c[u], f32x4{0.f, 0.f, 0.f, 0.f}));
-              p4a[u] = cvt_f16x4(mma16x16x16(p2c[u], p2a[u], f32x4{0.f, 0.f, 0.f, 0.f}));
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) p8c[u] = cvt_f16x4(mma16x16x16(p4a[u], p4c[u], f32x4{0.f, 0.f, 0.f, 0.f}));
-            // X_{k+1} = X_k + X_k L^(2^k) in both forms (the row form of X is the C form of X^T).
-            // The scan forms v_new = (Tm diag(beta)) (V - diag(e^gamma) K h), so the Tm it reads
-            // carries beta on its columns; the unscaled T_bb, the left factor of the block-column
-            // chains below, goes into the diagonal block of the A tile, which A leaves unused.
-            f32x4 xa[2], xc[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const f16x4 x0a16 = cvt_f16x4(x0a[u]);
-              xc[u] = mma16x16x16(x0a16, p2c[u], x0c[u]);
-              xa[u] = mma16x16x16(p2c[u], x0a16, x0a[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const f16x4 x1a16 = cvt_f16x4(xa[u]);
-              xc[u] = mma16x16x16(x1a16, p4c[u], xc[u]);
-              xa[u] = mma16x16x16(p4c[u], x1a16, xa[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const f16x4 x2a16 = cvt_f16x4(xa[u]);
-              xc[u] = mma16x16x16(x2a16, p8c[u], xc[u]);
-              xa[u] = mma16x16x16(p8c[u], x2a16, xa[u]);
-              const int b0 = 16 * (2 * pq + u);
-              const f32x4 bc = *reinterpret_cast<const f32x4*>(&G[kBeta + b0 + 4 * lq]);
-              *reinterpret_cast<f16x4*>(&aft[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u]);
-              *reinterpret_cast<f16x4*>(&tmt[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u] * bc);
-            }
-            tc0 = cvt_f16x4(xc[0] * G[kBeta + 32 * pq + li]);
-          } else if (pq == 2) {
-            // ---- off-diagonal Gram tiles -> A rows (fp16)
-            prod_tiles<K, false, 0x1dau, kFastDecay>(qt, kt, G, s.af, p.scale);
-          } else {
-            // ---- Q K^T tiles -> P rows (fp16)
-            prod_tiles<K, true, 0x3ffu, kFastDecay>(qt, kt, G, T.p, p.scale);
-          }
-        };
-        if (fast) body(std::true_type{});
-        else body(std::false_type{});
-
-        if (pq < 3) solve_bar(&s.pbar, pbt);  // A rows (pq 2) and T_bb (pq 0, 1) are in LDS
-        // Off-diagonal 16x16 blocks, one block column per chain of products (fp16 operands,
-        // fp32 accumulation):  T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, with A_ik and T_ii as
-        // row-form A operands from LDS and T_kj in C form (the B-operand layout) in registers.
-        // Scaling column block j by beta commutes with the chain, so seeding it with the
-        // scaled T_jj yields the scaled T_ij.
-        // pq 0 takes column 0, pq 1 columns 1 and 2.
-        if (pq < 2) {
-          auto chain = [&](int j, f16x4 tjj) {
-            f16x4 bt[4];
-            bt[j] = tjj;
-#pragma unroll
-            for (int i = 1; i < 4; ++i) {
-              if (i <= j) continue;
-              f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int k = 0; k < i; ++k)
-                if (k >= j)
-                  sacc = mma16x16x16(*reinterpret_cast<const f16x4*>(&aft[tix(16 * i + li, 16 * k + 4 * lq)]), bt[k], sacc);
-              const f16x4 tii = *reinterpret_cast<const f16x4*>(&aft[tix(16 * i + li, 16 * i + 4 * lq)]);
-              const f32x4 t = mma16x16x16(tii, cvt_f16x4(sacc), f32x4{0.f, 0.f, 0.f, 0.f});
-              bt[i] = cvt_f16x4(-t);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) tmt[tix(16 * i + 4 * lq + e, 16 * j + li)] = bt[i][e];
-            }
-          };
-          if (pq == 0) {
-            chain(0, tc0);
-          } else {
-            // T_11 in C form from the stored rows of block 1
-            f16x4 t11;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t11[e] = tmt[tix(16 + 4 * lq + e, 16 + li)];
-            chain(1, t11);
-            chain(2, tc0);
-          }
-        }
+    // Each role runs its own loop (the lambda is instantiated per role), so that the
+    // lane-derived LDS addresses of a role stay in registers across the steps.
+    auto prep_role = [&](auto pq_c) {
+      constexpr int pq = decltype(pq_c)::value;
+      unsigned pbt = 0;
+      if (pq == 0 && lane == 0) s.pbar = 0u;
+      // upper 16x16 tiles (0,1) and (2,3) of Tm and P stay zero in both slots
+      for (int e = 64 * pq + lane; e < 2 * 2 * 2 * 256; e += 256) {
+        const int slot = e >> 10, which = (e >> 9) & 1, t = (e >> 8) & 1, rr = (e >> 4) & 15, cc = e & 15;
+        u16* tile = which ? s.tp[slot].p : s.tp[slot].tm;
+        tile[tix(32 * t + rr, 32 * t + 16 + cc)] = 0;
       }
       __syncthreads();
-    }
+
+      for (int n = -1; n < nchunks; ++n) {
+        const int m = n + 1;  // chunk prepared in this step
+        if (m < nchunks) {
+          const int lane = __lane_id(), li = lane & 15, lq = lane >> 4;
+          typename SM::TP& T = s.tp[m & 1];
+          const typename SM::QK& Q = s.qk[m % 3];
+          const float* G = s.gate[m % 3];
+          const bf16* qt = reinterpret_cast<const bf16*>(Q.q);
+          const bf16* kt = reinterpret_cast<const bf16*>(Q.k);
+          f16* tmt = reinterpret_cast<f16*>(T.tm);
+          f16* aft = reinterpret_cast<f16*>(s.af);
+          const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(G[kFast])) != 0;
+          f16x4 tc0;  // C-form (accumulator layout) of this wave's first diagonal block of Tm
+
+          // The products below take the rows of their second factor as the A operand, so a
+          // lane's accumulator of tile (I, J) holds columns s = 16J + 4lq + e of row
+          // r = 16I + li ("row form", the A-operand layout of the product); the Gram tile is
+          // symmetric, so the same accumulator also gives the C form r = 16I + 4lq + e,
+          // s = 16I + li of a diagonal block.  decay(r, s) = e^{gamma_r - gamma_s} (times
+          // beta_r unless the Q K^T tile is meant), from per-token factors or, when the chunk
+          // decays too fast for them, from gamma itself.
+          auto body = [&](auto fast_c) {
+            constexpr bool kFastDecay = decltype(fast_c)::value;
+            auto rowv = [&](int r, bool qk) -> float {
+              return kFastDecay ? G[(qk ? kFrq : kFrk) + r] : G[kGam + r];
+            };
+            auto colv = [&](int c) -> float { return kFastDecay ? G[kFc + c] : G[kGam + c]; };
+            auto rows4 = [&](int r0, bool qk) -> f32x4 {
+              return *reinterpret_cast<const f32x4*>(&G[(kFastDecay ? (qk ? kFrq : kFrk) : kGam) + r0]);
+            };
+            auto cols4 = [&](int c0) -> f32x4 {
+              return *reinterpret_cast<const f32x4*>(&G[(kFastDecay ? kFc : kGam) + c0]);
+            };
+            auto dec = [&](float rv, float cv, float beta_r) -> float {
+              if constexpr (kFastDecay) return rv * cv;
+              else return beta_r * __expf(rv - cv);
+            };
+
+            if (pq < 2) {
+              // ---- diagonal blocks b = 2pq, 2pq + 1: Gram tile, then (I + L)^-1 as
+              // (I - L)(I + L^2)(I + L^4)(I + L^8) (L strictly lower, L^16 = 0) on fp16 operands
+              bf16x8 kf[2][kG];
+#pragma unroll
+              for (int kk = 0; kk < kG; ++kk)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) kf[u][kk] = lds8(kt + tix(16 * (2 * pq + u) + li, 32 * kk + 8 * lq));
+              __builtin_amdgcn_sched_barrier(0);
+              f32x4 g[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+              for (int kk = 0; kk < kG; ++kk)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) g[u] = mma16(kf[u][kk], kf[u][kk], g[u]);
+              f16x4 la[2], lc[2];
+              f32x4 x0a[2], x0c[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int b0 = 16 * (2 * pq + u);
+                const float r_li = rowv(b0 + li, false), c_li = colv(b0 + li);
+                const float be_li = kFastDecay ? 1.f : G[kBeta + b0 + li];
+                const f32x4 r_q = rows4(b0 + 4 * lq, false), c_q = cols4(b0 + 4 * lq);
+                f32x4 be_q = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (!kFastDecay) be_q = *reinterpret_cast<const f32x4*>(&G[kBeta + b0 + 4 * lq]);
+                f32x4 va, vc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int c = 4 * lq + e;
+                  va[e] = (c < li) ? dec(r_li, c_q[e], be_li) * g[u][e] : 0.f;   // L[li][c]
+                  vc[e] = (li < c) ? dec(r_q[e], c_li, be_q[e]) * g[u][e] : 0.f;  // L[c][li]
+                  x0a[u][e] = (c == li ? 1.f : 0.f) - va[e];
+                  x0c[u][e] = (c == li ? 1.f : 0.f) - vc[e];
+                }
+                la[u] = cvt_f16x4(va);
+                lc[u] = cvt_f16x4(vc);
+              }
+              f16x4 p2a[2], p2c[2], p4a[2], p4c[2], p8c[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                p2c[u] = cvt_f16x4(mma16x16x16(la[u], lc[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+                p2a[u] = cvt_f16x4(mma16x16x16(lc[u], la[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+              }
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                p4c[u] = cvt_f16x4(mma16x16x16(p2a[u], p2c[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+                p4a[u] = cvt_f16x4(mma16x16x16(p2c[u], p2a[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+              }
+#pragma unroll
+              for (int u = 0; u < 2; ++u) p8c[u] = cvt_f16x4(mma16x16x16(p4a[u], p4c[u], f32x4{0.f, 0.f, 0.f, 0.f}));
+              // X_{k+1} = X_k + X_k L^(2^k) in both forms (the row form of X is the C form of X^T).
+              // The scan forms v_new = (Tm diag(beta)) (V - diag(e^gamma) K h), so the Tm it reads
+              // carries beta on its columns; the unscaled T_bb, the left factor of the block-column
+              // chains below, goes into the diagonal block of the A tile, which A leaves unused.
+              f32x4 xa[2], xc[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const f16x4 x0a16 = cvt_f16x4(x0a[u]);
+                xc[u] = mma16x16x16(x0a16, p2c[u], x0c[u]);
+                xa[u] = mma16x16x16(p2c[u], x0a16, x0a[u]);
+              }
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const f16x4 x1a16 = cvt_f16x4(xa[u]);
+                xc[u] = mma16x16x16(x1a16, p4c[u], xc[u]);
+                xa[u] = mma16x16x16(p4c[u], x1a16, xa[u]);
+              }
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const f16x4 x2a16 = cvt_f16x4(xa[u]);
+                xc[u] = mma16x16x16(x2a16, p8c[u], xc[u]);
+                xa[u] = mma16x16x16(p8c[u], x2a16, xa[u]);
+                const int b0 = 16 * (2 * pq + u);
+                const f32x4 bc = *reinterpret_cast<const f32x4*>(&G[kBeta + b0 + 4 * lq]);
+                *reinterpret_cast<f16x4*>(&aft[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u]);
+                *reinterpret_cast<f16x4*>(&tmt[tix(b0 + li, b0 + 4 * lq)]) = cvt_f16x4(xa[u] * bc);
+              }
+              tc0 = cvt_f16x4(xc[0] * G[kBeta + 32 * pq + li]);
+              // the C form of the scaled T_11 for the other solve wave's block-column chain,
+              // parked in the (unused) upper tile (0, 1) of the A tile
+              if (pq == 0) *reinterpret_cast<f16x4*>(&aft[tix(li, 16 + 4 * lq)]) = cvt_f16x4(xc[1] * G[kBeta + 16 + li]);
+            } else if (pq == 2) {
+              // ---- off-diagonal Gram tiles -> A rows (fp16)
+              prod_tiles<K, false, 0x1dau, kFastDecay>(qt, kt, G, s.af, p.scale);
+            } else {
+              // ---- Q K^T tiles -> P rows (fp16)
+              prod_tiles<K, true, 0x3ffu, kFastDecay>(qt, kt, G, T.p, p.scale);
+            }
+          };
+          if (fast) body(std::true_type{});
+          else body(std::false_type{});
+
+          if (pq < 3) solve_bar(&s.pbar, pbt);  // A rows (pq 2) and T_bb (pq 0, 1) are in LDS
+          // Off-diagonal 16x16 blocks, one block column per chain of products (fp16 operands,
+          // fp32 accumulation):  T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, with A_ik and T_ii as
+          // row-form A operands from LDS and T_kj in C form (the B-operand layout) in registers.
+          // Scaling column block j by beta commutes with the chain, so seeding it with the
+          // scaled T_jj yields the scaled T_ij.
+          // pq 0 takes column 0, pq 1 columns 1 and 2.
+          if (pq < 2) {
+            auto chain = [&](int j, f16x4 tjj) {
+              f16x4 bt[4];
+              bt[j] = tjj;
+#pragma unroll
+              for (int i = 1; i < 4; ++i) {
+                if (i <= j) continue;
+                f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < i; ++k)
+                  if (k >= j)
+                    sacc = mma16x16x16(*reinterpret_cast<const f16x4*>(&aft[tix(16 * i + li, 16 * k + 4 * lq)]), bt[k], sacc);
+                const f16x4 tii = *reinterpret_cast<const f16x4*>(&aft[tix(16 * i + li, 16 * i + 4 * lq)]);
+                const f16x4 s16 = cvt_f16x4(sacc);
+                const f32x4 t = mma16x16x16(tii, s16, f32x4{0.f, 0.f, 0.f, 0.f});
+                bt[i] = cvt_f16x4(-t);
+                // the row form of T_ij for the store: (T_ii S)^T = S^T T_ii^T
+                const f32x4 tr = mma16x16x16(s16, tii, f32x4{0.f, 0.f, 0.f, 0.f});
+                *reinterpret_cast<f16x4*>(&tmt[tix(16 * i + li, 16 * j + 4 * lq)]) = cvt_f16x4(-tr);
+              }
+            };
+            if (pq == 0) {
+              chain(0, tc0);
+            } else {
+              // T_11 in C form, parked by the other solve wave
+              const f16x4 t11 = *reinterpret_cast<const f16x4*>(&aft[tix(li, 16 + 4 * lq)]);
+              chain(1, t11);
+              chain(2, tc0);
+            }
+          }
+        }
+        __syncthreads();
+      }
+    };
+    if (wave == 2) prep_role(std::integral_constant<int, 0>{});
+    else if (wave == 3) prep_role(std::integral_constant<int, 1>{});
+    else if (wave == 6) prep_role(std::integral_constant<int, 2>{});
+    else prep_role(std::integral_constant<int, 3>{});
     return;
   }
 
@@ -621,14 +631,14 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   // the compiler copy every loop-carried register (state and prefetched K rows) at the end of
   // each step.
   {
-    const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+    const int lane = __lane_id(), li = lane & 15, lq = lane >> 4;
     const int ob[2] = {tix(pair_row(0, 0, li), 8 * lq), tix(pair_row(0, 1, li), 8 * lq)};
     read_k(0, ob, 0, kG / 2);  // chunk 0's slot (stale and unused when there are no chunks)
   }
   __syncthreads();
 
   for (int n = 0; n < nchunks; ++n) {
-    const int lane = opaque_lane(), li = lane & 15, lq = lane >> 4;
+    const int lane = __lane_id(), li = lane & 15, lq = lane >> 4;
     const int trj = (lane >> 2) & 3, trc = lane & 3;
     const int ob[2] = {tix(pair_row(0, 0, li), 8 * lq), tix(pair_row(0, 1, li), 8 * lq)};
     const int ot[2] = {tix(8 * lq + trj, 8 * trc), tix(8 * lq + 4 + trj, 8 * trc)};
