@@ -64,6 +64,10 @@ MUTATIONS = [
      "dk_pos[base + t * D + r] = a[r] * bt * e1;"),
     ("BiGDN backward: dbeta without the z stream", PINS_BBWD,
      "dbeta[(long)bh * N + t] = db + ee * e1;", "dbeta[(long)bh * N + t] = db;"),
+    ("BiGDN backward: decay gradient without the z stream's term", PINS_BBWD,
+     "for (int r = 0; r < D; ++r) gd += dzp[r] * zs[(size_t)(it - 1) * D + r];", ";"),
+    ("BiGDN backward: z gradient carried back without the decay", PINS_BBWD,
+     "for (int r = 0; r < D; ++r) a[r] = g * dzp[r];", "for (int r = 0; r < D; ++r) a[r] = dzp[r];"),
     ("camera backward: dv without beta", PINS_CBWD,
      "dv[base + (long)c * N + t] = bt * dd[c];", "dv[base + (long)c * N + t] = dd[c];"),
     ("camera backward: dk without the prediction term", PINS_CBWD,
