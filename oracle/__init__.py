@@ -74,10 +74,13 @@ def _load():
         lib.oracle_cam_scan_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_gdn_bwd_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, Dd, P, P]
         lib.oracle_bigdn_dir_bwd.argtypes = [I, I, I, I, I, I] + [P] * 16
+        lib.oracle_prep_bwd.argtypes = [I, I, I, I, P, P, P, P, P, Dd, Dd, I] + [P] * 8
+        lib.oracle_bigdn_merge_bwd.argtypes = [I, I, I, I, P, P, P, P, Dd, P, P, P]
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
-                     "oracle_gdn_transition", "oracle_gdn_bwd_prep", "oracle_bigdn_dir_bwd"):
+                     "oracle_gdn_transition", "oracle_gdn_bwd_prep", "oracle_bigdn_dir_bwd",
+                     "oracle_prep_bwd", "oracle_bigdn_merge_bwd"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -284,11 +287,57 @@ def bigdn_merged(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_sca
     nr, dr = bigdn_dir(*tr, beta if beta_bwd is None else beta_bwd,
                        decay if decay_bwd is None else decay_bwd, reverse=True)
     num, den = nf + nr, df + dr
+    return bigdn_merge(num, den, gate, merge_eps), num, den
+
+
+def bigdn_merge(num, den, gate=None, merge_eps=1e-6):
+    """The merge of the BiGDN block (SANA fused_gdn.py page, fused_bidi_merge): out =
+    num / (den + merge_eps) * SiLU(gate) (no gate: factor 1).  num, gate [B,N,H,D]; den
+    [B,H,N]."""
+    num, den = _f64(num), _f64(den)
     out = num / (np.transpose(den, (0, 2, 1))[..., None] + merge_eps)
     if gate is not None:
         g = _f64(gate)
         out = out * (g / (1.0 + np.exp(-g)))
-    return out, num, den
+    return out
+
+
+def bigdn_merge_bwd(num, den, dout, gate=None, merge_eps=1e-6):
+    """Backward of bigdn_merge (SANA fused_gdn.py page: the dnum / dden of
+    FusedBiGDNFunction.backward, with fused_bidi_merge's gate): returns dict dnum [B,N,H,D],
+    dden [B,H,N] and dgate [B,N,H,D] (None without a gate)."""
+    num, den, dout, gate = map(_f64, (num, den, dout, gate))
+    B, N, H, D = num.shape
+    out = {"dnum": np.empty((B, N, H, D)), "dden": np.empty((B, H, N)),
+           "dgate": None if gate is None else np.empty((B, N, H, D))}
+    rc = _load().oracle_bigdn_merge_bwd(B, N, H, D, _p(num), _p(den), _p(gate), _p(dout),
+                                        float(merge_eps), _p(out["dnum"]), _p(out["dden"]),
+                                        _p(out["dgate"]))
+    if rc != 0:
+        raise RuntimeError("oracle_bigdn_merge_bwd failed")
+    return out
+
+
+def prep_bwd(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, grads, eps=1e-5):
+    """Backward of prep (SANA fused_gdn.py page, "Backward / autograd Functions": the RoPE,
+    ReLU and k-scale backward of _fused_gdn_bwd_kernel and the full-channel RMSNorm backward
+    of FusedBiGDNFunction.backward).  grads: dict of dq_rot, dk_rot, dq_pos, dk_pos, dv, each
+    [B,H,N,D] or [ndir,B,H,N,D] (the directions are summed).  Returns dict dqkv [B,N,3,H,D],
+    dq_norm_w, dk_norm_w [H*D]."""
+    qkv, qw, kw, cs, sn = map(_f64, (qkv, q_norm_w, k_norm_w, rope_cos, rope_sin))
+    B, N, _, H, D = qkv.shape
+    names = ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv")
+    g = {n: _f64(grads[n]) for n in names}
+    g = {n: (x[None] if x.ndim == 4 else x) for n, x in g.items()}
+    ndir = g["dq_rot"].shape[0]
+    out = {"dqkv": np.empty((B, N, 3, H, D)), "dq_norm_w": np.empty(H * D),
+           "dk_norm_w": np.empty(H * D)}
+    rc = _load().oracle_prep_bwd(B, N, H, D, _p(qkv), _p(qw), _p(kw), _p(cs), _p(sn),
+                                 float(k_scale), float(eps), ndir, *(_p(g[n]) for n in names),
+                                 _p(out["dqkv"]), _p(out["dq_norm_w"]), _p(out["dk_norm_w"]))
+    if rc != 0:
+        raise RuntimeError("oracle_prep_bwd failed")
+    return out
 
 
 def cam_prep(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale,

@@ -1090,3 +1090,106 @@ int oracle_bigdn_dir_bwd(int B, int F, int S_, int H, int D, int reverse, const 
   }
   return fail ? -1 : 0;
 }
+
+/*
+ * Backward of the BiGDN front end (oracle_prep), following the backward of the SANA
+ * fused_gdn.py page ("Backward / autograd Functions": the RoPE inverse, ReLU and k-scale
+ * backward inside _fused_gdn_bwd_kernel, and the full-channel RMSNorm backward of
+ * FusedBiGDNFunction.backward).  Inputs are the gradients of the prepped tensors from ndir
+ * scan directions, each [ndir, B, H, N, D] (the directions' contributions are summed);
+ * outputs dqkv [B, N, 3, H, D] and the norm weights' gradients dqw, dkw [H*D].
+ * Per token, with C = H*D, r the inverse RMS and x_hat = x r w:
+ *   g_pos[d] = dpos[d] + drot[d] cos[d] + drot[d^1] sin[d^1]      (x_rot = x_pos cos + x_pos[d^1] sin)
+ *   g[c]     = g_pos * (k_scale for k) * [x_hat > 0]               (the gradient of x_hat)
+ *   dx[c]    = r w[c] g[c] - r^3 / C * x[c] * sum_c' w[c'] g[c'] x[c']
+ *   dw[c]   += g[c] x[c] r
+ * The token loop is serial so that the weight gradients are summed in token order.
+ */
+int oracle_prep_bwd(int B, int N, int H, int D, const double* qkv, const double* qw,
+                    const double* kw, const double* cosv, const double* sinv, double k_scale,
+                    double eps, int ndir, const double* dq_rot, const double* dk_rot,
+                    const double* dq_pos, const double* dk_pos, const double* dv,
+                    double* dqkv, double* dqw, double* dkw) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0 || (D % 2) != 0 || ndir < 1) return -1;
+  const long C = (long)H * D;
+  const long dirs = (long)B * H * N * D;  /* elements of one direction's gradient */
+  double* g = (double*)malloc(sizeof(double) * 2 * C);
+  if (!g) return -1;
+  for (long c = 0; c < C; ++c) dqw[c] = dkw[c] = 0.0;
+  for (long bn = 0; bn < (long)B * N; ++bn) {
+    const long b = bn / N, n = bn % N;
+    const double* row = qkv + bn * 3 * C;
+    double* out = dqkv + bn * 3 * C;
+    for (int which = 0; which < 2; ++which) {
+      const double* x = row + which * C;
+      const double* w = which ? kw : qw;
+      const double* drot = which ? dk_rot : dq_rot;
+      const double* dpos = which ? dk_pos : dq_pos;
+      double ss = 0.0;
+      for (long c = 0; c < C; ++c) ss += x[c] * x[c];
+      const double r = 1.0 / sqrt(ss / (double)C + eps);
+      double s = 0.0;
+      for (int h = 0; h < H; ++h) {
+        for (int dd = 0; dd < D; ++dd) {
+          const int pd = dd ^ 1;
+          const long c = (long)h * D + dd;
+          double gp = 0.0;
+          for (int dir = 0; dir < ndir; ++dir) {
+            const long o = dir * dirs + (((long)b * H + h) * N + n) * D;
+            gp += dpos[o + dd] + drot[o + dd] * cosv[n * D + dd] + drot[o + pd] * sinv[n * D + pd];
+          }
+          const double xhat = x[c] * r * w[c];
+          g[which * C + c] = xhat > 0.0 ? gp * (which ? k_scale : 1.0) : 0.0;
+          s += w[c] * g[which * C + c] * x[c];
+        }
+      }
+      double* dw = which ? dkw : dqw;
+      for (long c = 0; c < C; ++c) {
+        out[which * C + c] = r * w[c] * g[which * C + c] - r * r * r / (double)C * x[c] * s;
+        dw[c] += g[which * C + c] * x[c] * r;
+      }
+    }
+    for (int h = 0; h < H; ++h)
+      for (int dd = 0; dd < D; ++dd) {
+        double a = 0.0;
+        for (int dir = 0; dir < ndir; ++dir) a += dv[dir * dirs + (((long)b * H + h) * N + n) * D + dd];
+        out[2 * C + (long)h * D + dd] = a;
+      }
+  }
+  free(g);
+  return 0;
+}
+
+/*
+ * Backward of the BiGDN merge (SANA fused_gdn.py page: the dnum / dden of
+ * FusedBiGDNFunction.backward, with the SiLU gate of fused_bidi_merge):
+ *   out = num / (den + eps) * silu(gate)     (silu = 1 without a gate)
+ *   dnum  = dout silu(gate) / (den + eps)
+ *   dden  = -sum_d dout silu(gate) num / (den + eps)^2
+ *   dgate = dout num / (den + eps) * silu'(gate),  silu'(x) = s(x) (1 + x (1 - s(x)))
+ * num, dout, gate, dnum, dgate [B, N, H, D]; den, dden [B, H, N].
+ */
+int oracle_bigdn_merge_bwd(int B, int N, int H, int D, const double* num, const double* den,
+                           const double* gate, const double* dout, double eps, double* dnum,
+                           double* dden, double* dgate) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0) return -1;
+  for (long b = 0; b < B; ++b)
+    for (long n = 0; n < N; ++n)
+      for (long h = 0; h < H; ++h) {
+        const double inv = 1.0 / (den[(b * H + h) * N + n] + eps);
+        const long o = ((b * N + n) * H + h) * D;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) {
+          double sl = 1.0;
+          if (gate) {
+            const double x = gate[o + d], sg = 1.0 / (1.0 + exp(-x));
+            sl = x * sg;
+            if (dgate) dgate[o + d] = dout[o + d] * num[o + d] * inv * sg * (1.0 + x * (1.0 - sg));
+          }
+          dnum[o + d] = dout[o + d] * sl * inv;
+          acc += dout[o + d] * sl * num[o + d];
+        }
+        dden[(b * H + h) * N + n] = -acc * inv * inv;
+      }
+  return 0;
+}

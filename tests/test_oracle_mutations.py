@@ -21,6 +21,7 @@ PINS_CAM = "tests/test_oracle_cam.py"
 PINS_DHU = "tests/test_oracle_dhu.py"
 PINS_CBWD = "tests/test_oracle_cam_bwd.py"
 PINS_BBWD = "tests/test_oracle_bigdn_bwd.py"
+PINS_PREPBWD = "tests/test_oracle_prep_bwd.py"
 
 # (name, pin file, text in gdn_oracle.c, replacement)
 MUTATIONS = [
@@ -68,6 +69,16 @@ MUTATIONS = [
      "for (int r = 0; r < D; ++r) gd += dzp[r] * zs[(size_t)(it - 1) * D + r];", ";"),
     ("BiGDN backward: z gradient carried back without the decay", PINS_BBWD,
      "for (int r = 0; r < D; ++r) a[r] = g * dzp[r];", "for (int r = 0; r < D; ++r) a[r] = dzp[r];"),
+    ("front-end backward: RoPE inverse with the token's own sine", PINS_PREPBWD,
+     "drot[o + pd] * sinv[n * D + pd];", "drot[o + pd] * sinv[n * D + dd];"),
+    ("front-end backward: RMSNorm without its correction term", PINS_PREPBWD,
+     "out[which * C + c] = r * w[c] * g[which * C + c] - r * r * r / (double)C * x[c] * s;",
+     "out[which * C + c] = r * w[c] * g[which * C + c];"),
+    ("front-end backward: k without its scale", PINS_PREPBWD,
+     "g[which * C + c] = xhat > 0.0 ? gp * (which ? k_scale : 1.0) : 0.0;",
+     "g[which * C + c] = xhat > 0.0 ? gp : 0.0;"),
+    ("merge backward: dden with one factor of 1 / (den + eps)", PINS_PREPBWD,
+     "dden[(b * H + h) * N + n] = -acc * inv * inv;", "dden[(b * H + h) * N + n] = -acc * inv;"),
     ("camera backward: dv without beta", PINS_CBWD,
      "dv[base + (long)c * N + t] = bt * dd[c];", "dv[base + (long)c * N + t] = dd[c];"),
     ("camera backward: dk without the prediction term", PINS_CBWD,
