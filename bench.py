@@ -63,6 +63,7 @@ SOURCES = {
     "cam": ["gdn_cam.hip", "gdn_bigdn.hip"],
     "cam_bwd": ["gdn_cambwd.hip"],
     "bigdn_bwd": ["gdn_bigdnbwd.hip", "gdn_cambwd.hip"],
+    "bigdn_block_bwd": ["gdn_bigdn.hip", "gdn_bigdnbwd.hip", "gdn_cambwd.hip", "gdn_prepbwd.hip"],
     "summary": ["gdn_fwd.hip", "gdn_fused16.hip", "gdn_summary.hip"],
     "dhu": ["gdn_bwd.hip"],
 }
@@ -119,6 +120,17 @@ def alg_bytes_bigdn_bwd(B, F, S, H, D):
     ddecay."""
     N = F * S
     return (5 * 2 + 4 + 5 * 4) * B * H * N * D + 3 * B * H * N * 4 + 2 * B * H * F * 4
+
+
+def alg_bytes_bigdn_block_bwd(B, F, S, H, D):
+    """Minimum HBM bytes of the whole BiGDN block's backward: read qkv, num, den and the gate
+    (bf16), dout (fp32), beta, decay, the RoPE tables and norm weights once; write dqkv,
+    dgate (fp32), dbeta, ddecay and the two norm weights' gradients."""
+    N = F * S
+    C = H * D
+    return (B * N * 3 * C * 2 + 2 * B * N * C * 2 + B * H * N * 2 + B * N * C * 4
+            + B * H * N * 4 + B * H * F * 4 + 2 * N * D * 4 + 2 * C * 4
+            + B * N * 3 * C * 4 + B * N * C * 4 + B * H * N * 4 + B * H * F * 4 + 2 * C * 4)
 
 
 def alg_bytes_dhu(B, T, H, K, V, elt):
@@ -246,6 +258,32 @@ def cpu_baseline(kind, inp, max_chains=64):
                                      reverse=rev)
         return _cpu_time(run, "both directions' backward on the first %d of %d frames, all %d "
                          "heads (%d tokens)" % (fs, F, H, n), 2 * B * n * H)
+    if kind == "bigdn_block_bwd":
+        import numpy as np
+
+        B, N, _, H, D = inp["qkv"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        fs = min(F, 4)
+        n = fs * S
+        sub = {k: oracle._f64(inp[k][:, :n]) for k in ("qkv", "gate", "dout")}
+        sub.update(beta=oracle._f64(inp["beta"][:, :, :fs]), decay=oracle._f64(inp["decay"][:, :, :fs]),
+                   rope_cos=oracle._f64(inp["rope_cos"][:n]), rope_sin=oracle._f64(inp["rope_sin"][:n]))
+        pw = (oracle._f64(inp["q_norm_w"]), oracle._f64(inp["k_norm_w"]))
+        ks, eps = inp["k_scale"], inp["eps"]
+        _, num, den = oracle.bigdn_merged(sub["qkv"], sub["beta"], sub["decay"], *pw,
+                                          sub["rope_cos"], sub["rope_sin"], ks, eps,
+                                          gate=sub["gate"])  # the saved forward sums (not timed)
+        names = ("q_rot", "k_rot", "q_pos", "k_pos", "v")
+
+        def run():
+            p = oracle.prep(sub["qkv"], *pw, sub["rope_cos"], sub["rope_sin"], ks, eps)
+            m = oracle.bigdn_merge_bwd(num, den, sub["dout"], sub["gate"])
+            d = [oracle.bigdn_dir_bwd(*(p[k] for k in names), sub["beta"], sub["decay"],
+                                      m["dnum"], m["dden"], reverse=rev) for rev in (False, True)]
+            oracle.prep_bwd(sub["qkv"], *pw, sub["rope_cos"], sub["rope_sin"], ks,
+                            {"d" + k: np.stack([x["d" + k] for x in d]) for k in names}, eps)
+        return _cpu_time(run, "the block's backward on the first %d of %d frames, all %d heads "
+                         "(%d tokens)" % (fs, F, H, n), B * n * H)
     if kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -468,6 +506,30 @@ def main():
         def step(i):
             s = sets[i % len(sets)]
             return [gdn.bigdn_dir_bwd(*(s[k] for k in names), reverse=rev) for rev in (False, True)]
+    elif kind == "bigdn_block_bwd":
+        B, N, _, H, D = inp["qkv"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        dt = torch.bfloat16
+        th = B * N * H
+        alg = alg_bytes_bigdn_block_bwd(B, F, S, H, D)
+        kernel = ("bigdn_bwd: gdn_prep, bigdn_merge_bwd, bigdn_dir_bwd x 2 directions, "
+                  "gdn_prep_bwd (15 kernels, whole step)")
+        config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
+                  "state": "fp32", "products": "split bf16 (hi/lo) operands, fp32 accumulation",
+                  "step": "from the gated output's gradient to qkv, the norm weights, beta, "
+                          "decay and the gate (num, den from one forward before timing)"}
+        pre = ("q_norm_w", "k_norm_w", "rope_cos", "rope_sin")
+        for s in sets:  # the forward's saved sums, as a training step would hold them
+            _, s["num"], s["den"] = gdn.bigdn_fwd_merged(
+                s["qkv"], s["beta"], s["decay"], *(s[k] for k in pre), s["k_scale"], s["eps"],
+                gate=s["gate"], merge_eps=1e-6, want_num_den=True)
+        torch.cuda.synchronize()
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.bigdn_bwd(s["qkv"], s["beta"], s["decay"], *(s[k] for k in pre),
+                                 s["k_scale"], s["num"], s["den"], s["dout"], s["gate"], 1e-6,
+                                 s["eps"])
     elif kind == "bigdn":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

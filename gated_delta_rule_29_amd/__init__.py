@@ -18,7 +18,8 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi", "cam_scan_bwd", "bigdn_dir_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
+           "cam_scan_bidi", "cam_scan_bwd", "bigdn_dir_bwd", "bigdn_merge_bwd", "gdn_prep_bwd",
+           "bigdn_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
            "gdn_state_grad_summary", "gdn_state_grad_apply", "gdn_abi_version",
            "gdn_last_error", "CHUNK"]
 
@@ -487,11 +488,14 @@ def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, gk=None, want_d
     return {"dv2": dv2, "dh": dh, "dh0": dh0}
 
 
-def bigdn_dir_bwd(q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden, reverse=False):
+def bigdn_dir_bwd(q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden, reverse=False, *,
+                  accumulate=False, out=None):
     """Backward of one BiGDN direction on the prepped tensors (q_rot .. v [B,H,N,D] bf16, as
     gdn_prep returns them); beta [B,H,F,S], decay [B,H,F]; dnum [B,N,H,D], dden [B,H,N] fp32.
     Returns a dict with dq_rot, dk_rot, dq_pos, dk_pos, dv [B,H,N,D], dbeta [B,H,F,S] and
-    ddecay [B,H,F] (fp32)."""
+    ddecay [B,H,F] (fp32).  out: a dict of those tensors to write into (contiguous; e.g. one
+    direction's slice of [2,B,H,N,D] tensors for gdn_prep_bwd); accumulate: add dbeta and
+    ddecay to out's contents instead of writing them."""
     B, H, N, D = q_rot.shape
     F, S = beta.shape[2], beta.shape[3]
     dev = q_rot.device
@@ -505,18 +509,115 @@ def bigdn_dir_bwd(q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden, revers
     if F * S != N:
         raise ValueError("beta is [B,H,F,S] with F*S = %d, but N = %d" % (F * S, N))
     names = ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv")
-    out = {n: torch.empty(B, H, N, D, dtype=torch.float32, device=dev) for n in names}
-    out["dbeta"] = torch.empty(B, H, F, S, dtype=torch.float32, device=dev)
-    out["ddecay"] = torch.empty(B, H, F, dtype=torch.float32, device=dev)
+    shapes = dict({n: (B, H, N, D) for n in names}, dbeta=(B, H, F, S), ddecay=(B, H, F))
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out (the dbeta and ddecay to add to)")
+        out = {n: torch.empty(*shp, dtype=torch.float32, device=dev) for n, shp in shapes.items()}
+    else:
+        for n, shp in shapes.items():
+            _need(out.get(n), n, shp, torch.float32, dev)
+            if n not in out or not out[n].is_contiguous():
+                raise ValueError("out[%r] must be a contiguous tensor" % n)
     lib = _lib.load()
     ws_n = lib.bigdn_dir_bwd_workspace_bytes(B, H, D, F)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    flag = int(bool(reverse)) | (_lib.BWD_ACCUMULATE if accumulate else 0)
     rc = lib.bigdn_dir_bwd(*(_ptr(x) for x in (q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum,
-                                               dden)), int(bool(reverse)),
+                                               dden)), flag,
                            *(_ptr(out[n]) for n in names + ("dbeta", "ddecay")),
                            B, H, D, F, S, _ptr(ws), ws_n, _stream(dev))
     _lib.check(rc, "bigdn_dir_bwd")
     return out
+
+
+def bigdn_merge_bwd(num, den, dout, gate=None, merge_eps=1e-6):
+    """Backward of the block merge out = num / (den + merge_eps) * SiLU(gate): num [B,N,H,D],
+    den [B,H,N], gate [B,N,H,D] (bf16, or None), dout [B,N,H,D] fp32.  Returns a dict with
+    dnum [B,N,H,D], dden [B,H,N] and dgate [B,N,H,D] (None without a gate), fp32."""
+    B, N, H, D = num.shape
+    dev = num.device
+    _need(num, "num", (B, N, H, D), torch.bfloat16, dev)
+    _need(den, "den", (B, H, N), torch.bfloat16, dev)
+    _need(gate, "gate", (B, N, H, D), torch.bfloat16, dev)
+    _need(dout, "dout", (B, N, H, D), torch.float32, dev)
+    out = {"dnum": torch.empty(B, N, H, D, dtype=torch.float32, device=dev),
+           "dden": torch.empty(B, H, N, dtype=torch.float32, device=dev),
+           "dgate": None if gate is None else torch.empty(B, N, H, D, dtype=torch.float32,
+                                                          device=dev)}
+    rc = _lib.load().bigdn_merge_bwd(_ptr(num), _ptr(den), _ptr(gate), _ptr(dout),
+                                     float(merge_eps), _ptr(out["dnum"]), _ptr(out["dden"]),
+                                     _ptr(out["dgate"]), B, N, H, D, _stream(dev))
+    _lib.check(rc, "bigdn_merge_bwd")
+    return out
+
+
+def gdn_prep_bwd(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, grads, norm_eps=1e-5):
+    """Backward of gdn_prep: grads is a dict of dq_rot, dk_rot, dq_pos, dk_pos, dv, each
+    [ndir,B,H,N,D] (or [B,H,N,D]) fp32, the scan directions' gradients of the prepped
+    tensors (summed).  Returns a dict with dqkv [B,N,3,H,D], dq_norm_w, dk_norm_w [H*D]
+    (fp32)."""
+    B, N, three, H, D = qkv.shape
+    dev = qkv.device
+    _need(qkv, "qkv", (B, N, 3, H, D), torch.bfloat16, dev)
+    _need(q_norm_w, "q_norm_w", (H * D,), torch.float32, dev)
+    _need(k_norm_w, "k_norm_w", (H * D,), torch.float32, dev)
+    _need(rope_cos, "rope_cos", (N, D), torch.float32, dev)
+    _need(rope_sin, "rope_sin", (N, D), torch.float32, dev)
+    names = ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv")
+    ndir = 1 if grads["dq_rot"].dim() == 4 else grads["dq_rot"].shape[0]
+    shape = (B, H, N, D) if grads["dq_rot"].dim() == 4 else (ndir, B, H, N, D)
+    for n in names:
+        _need(grads[n], n, shape, torch.float32, dev)
+    out = {"dqkv": torch.empty(B, N, 3, H, D, dtype=torch.float32, device=dev),
+           "dq_norm_w": torch.empty(H * D, dtype=torch.float32, device=dev),
+           "dk_norm_w": torch.empty(H * D, dtype=torch.float32, device=dev)}
+    lib = _lib.load()
+    ws_n = lib.gdn_prep_bwd_workspace_bytes(B, N, H, D)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.gdn_prep_bwd(_ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(rope_cos),
+                          _ptr(rope_sin), float(k_scale), float(norm_eps), ndir,
+                          *(_ptr(grads[n]) for n in names), _ptr(out["dqkv"]),
+                          _ptr(out["dq_norm_w"]), _ptr(out["dk_norm_w"]), B, N, H, D, _ptr(ws),
+                          ws_n, _stream(dev))
+    _lib.check(rc, "gdn_prep_bwd")
+    return out
+
+
+def bigdn_bwd(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, num, den, dout,
+              gate=None, merge_eps=1e-6, norm_eps=1e-5, *, beta_bwd=None, decay_bwd=None):
+    """Backward of the BiGDN block out = (num_f + num_r) / (den_f + den_r + merge_eps) *
+    SiLU(gate) from the upstream gradient dout [B,N,H,D] fp32, given the block's inputs (as
+    passed to bigdn_fwd_merged) and its num, den sums (bf16, as it returns them).  The library
+    calls, in order: gdn_prep (the prepped tensors again), bigdn_merge_bwd, bigdn_dir_bwd for
+    the forward and the reverse direction (beta_bwd / decay_bwd: the reverse direction's
+    overrides), gdn_prep_bwd over both directions.  Returns a dict with dqkv [B,N,3,H,D],
+    dq_norm_w, dk_norm_w [H*D], dbeta [B,H,F,S], ddecay [B,H,F] (the reverse direction's are
+    added in unless overridden, then dbeta_bwd / ddecay_bwd), dgate (or None)."""
+    B, N, three, H, D = qkv.shape
+    F, S = beta.shape[2], beta.shape[3]
+    dev = qkv.device
+    p = gdn_prep(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, norm_eps,
+                 outputs=("q_rot", "k_rot", "q_pos", "k_pos", "v"))
+    t = (p["q_rot"], p["k_rot"], p["q_pos"], p["k_pos"], p["v"])
+    m = bigdn_merge_bwd(num, den, dout, gate, merge_eps)
+    names = ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv")
+    grads = {n: torch.empty(2, B, H, N, D, dtype=torch.float32, device=dev) for n in names}
+    par = {"dbeta": torch.empty(B, H, F, S, dtype=torch.float32, device=dev),
+           "ddecay": torch.empty(B, H, F, dtype=torch.float32, device=dev)}
+    bigdn_dir_bwd(*t, beta, decay, m["dnum"], m["dden"], reverse=False,
+                  out=dict({n: grads[n][0] for n in names}, **par))
+    sep = beta_bwd is not None or decay_bwd is not None
+    par_r = ({"dbeta": torch.empty_like(par["dbeta"]), "ddecay": torch.empty_like(par["ddecay"])}
+             if sep else par)
+    bigdn_dir_bwd(*t, beta if beta_bwd is None else beta_bwd,
+                  decay if decay_bwd is None else decay_bwd, m["dnum"], m["dden"], reverse=True,
+                  accumulate=not sep, out=dict({n: grads[n][1] for n in names}, **par_r))
+    g = gdn_prep_bwd(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, grads, norm_eps)
+    res = dict(g, dbeta=par["dbeta"], ddecay=par["ddecay"], dgate=m["dgate"])
+    if sep:
+        res["dbeta_bwd"], res["ddecay_bwd"] = par_r["dbeta"], par_r["ddecay"]
+    return res
 
 
 def gdn_bwd_prep(q, k, beta, do, g=None, scale=1.0, *, gk=None):

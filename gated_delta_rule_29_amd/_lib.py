@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FWD_PER_KEY, FWD_SAVES = 1, 2
+BWD_ACCUMULATE = 2
 
 P = ctypes.c_void_p
 I = ctypes.c_int
@@ -52,6 +53,9 @@ SIGNATURES = {
     "cam_scan_bwd": (I, [P, P, P, P, P, P, I, P, P, P, P, P, I, I, I, I, I, P, SZ, P]),
     "bigdn_dir_bwd_workspace_bytes": (SZ, [I, I, I, I]),
     "bigdn_dir_bwd": (I, [P] * 9 + [I] + [P] * 7 + [I, I, I, I, I, P, SZ, P]),
+    "bigdn_merge_bwd": (I, [P, P, P, P, F, P, P, P, I, I, I, I, P]),
+    "gdn_prep_bwd_workspace_bytes": (SZ, [I, I, I, I]),
+    "gdn_prep_bwd": (I, [P, P, P, P, P, F, F, I] + [P] * 8 + [I, I, I, I, P, SZ, P]),
     "gdn_bwd_prep": (I, [P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]),
     "gdn_state_grad_summary_workspace_bytes": (SZ, [I, I, I, I, I]),
     "gdn_state_grad_summary": (I, [P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, P, SZ, P]),

@@ -690,7 +690,10 @@ int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_pos, const
   if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S <= 0)
     return fail(GDN_ERR_INVALID, "B, H, D, F, S must be positive (got %d, %d, %d, %d, %d)", B, H,
                 D, F, S);
-  if (reverse != 0 && reverse != 1) return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, got %d", reverse);
+  if (reverse & ~(1 | GDN_BWD_ACCUMULATE))
+    return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, optionally with GDN_BWD_ACCUMULATE, got %d", reverse);
+  const int acc = (reverse & GDN_BWD_ACCUMULATE) ? 1 : 0;
+  reverse &= 1;
   if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
   if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
   if ((int64_t)F * S > INT32_MAX || (int64_t)B * H * F * 4 > INT32_MAX ||
@@ -729,8 +732,73 @@ int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_pos, const
   p.q_pos = static_cast<const __bf16*>(q_pos); p.k_pos = static_cast<const __bf16*>(k_pos);
   p.v = static_cast<const __bf16*>(v); p.dnum = dnum; p.dden = dden;
   p.dq_rot = dq_rot; p.dk_rot = dk_rot; p.dq_pos = dq_pos; p.dk_pos = dk_pos; p.dv = dv;
+  p.acc = acc;
   hipError_t e = gdn::launch_bigdn_dir_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "bigdn_dir_bwd launch");
+  return ok();
+}
+
+// ---- backward of the BiGDN front end and of the merge -------------------------------------
+
+namespace {
+constexpr long kPrepBwdGroups = 1024;  // token groups of gdn_prep_bwd (one workgroup each)
+long prep_bwd_groups(int B, int N) {
+  const long bn = (long)B * N;
+  return bn < kPrepBwdGroups ? bn : kPrepBwdGroups;
+}
+}  // namespace
+
+size_t gdn_prep_bwd_workspace_bytes(int B, int N, int H, int D) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0) return 0;
+  return al256((size_t)prep_bwd_groups(B, N) * 2 * H * D * 4);
+}
+
+int gdn_prep_bwd(const void* qkv, const float* q_norm_w, const float* k_norm_w,
+                 const float* rope_cos, const float* rope_sin, float k_scale, float norm_eps,
+                 int ndir, const float* dq_rot, const float* dk_rot, const float* dq_pos,
+                 const float* dk_pos, const float* dv, float* dqkv, float* dq_norm_w,
+                 float* dk_norm_w, int B, int N, int H, int D, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!qkv || !q_norm_w || !k_norm_w || !rope_cos || !rope_sin || !dq_rot || !dk_rot || !dq_pos ||
+      !dk_pos || !dv || !dqkv || !dq_norm_w || !dk_norm_w)
+    return fail(GDN_ERR_INVALID, "every input and gradient pointer must be non-null");
+  int rc = check_bigdn_dims(B, N, H, D);
+  if (rc) return rc;
+  if (ndir != 1 && ndir != 2) return fail(GDN_ERR_INVALID, "ndir must be 1 or 2, got %d", ndir);
+  if (!(norm_eps > 0.f)) return fail(GDN_ERR_INVALID, "norm_eps must be positive");
+  const size_t need = gdn_prep_bwd_workspace_bytes(B, N, H, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  gdn::PrepBwdParams p{};
+  p.qkv = static_cast<const __bf16*>(qkv); p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w;
+  p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.k_scale = k_scale; p.eps = norm_eps;
+  p.ndir = ndir; p.dq_rot = dq_rot; p.dk_rot = dk_rot; p.dq_pos = dq_pos; p.dk_pos = dk_pos;
+  p.dv = dv; p.dqkv = dqkv; p.dq_norm_w = dq_norm_w; p.dk_norm_w = dk_norm_w;
+  p.part = static_cast<float*>(workspace); p.nwg = (int)prep_bwd_groups(B, N);
+  p.B = B; p.N = N; p.H = H; p.D = D;
+  hipError_t e = gdn::launch_prep_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_prep_bwd launch");
+  return ok();
+}
+
+int bigdn_merge_bwd(const void* num, const void* den, const void* gate, const float* dout,
+                    float merge_eps, float* dnum, float* dden, float* dgate, int B, int N, int H,
+                    int D, void* stream) {
+  if (!num || !den || !dout || !dnum || !dden)
+    return fail(GDN_ERR_INVALID, "num, den, dout, dnum and dden must be non-null");
+  if (!gate != !dgate) return fail(GDN_ERR_INVALID, "gate and dgate must be given together");
+  int rc = check_bigdn_dims(B, N, H, D);
+  if (rc) return rc;
+  if (!(merge_eps >= 0.f)) return fail(GDN_ERR_INVALID, "merge_eps must be >= 0");
+  if ((int64_t)B * N * H > (int64_t)INT32_MAX * 4) return fail(GDN_ERR_INVALID, "B*N*H exceeds the grid limit");
+  gdn::MergeBwdParams p{};
+  p.num = static_cast<const __bf16*>(num); p.den = static_cast<const __bf16*>(den);
+  p.gate = static_cast<const __bf16*>(gate); p.dout = dout; p.eps = merge_eps;
+  p.dnum = dnum; p.dden = dden; p.dgate = dgate; p.B = B; p.N = N; p.H = H; p.D = D;
+  hipError_t e = gdn::launch_merge_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bigdn_merge_bwd launch");
   return ok();
 }
 

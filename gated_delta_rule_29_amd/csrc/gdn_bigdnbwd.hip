@@ -297,12 +297,13 @@ __global__ __launch_bounds__(256) void bbwd_tok_kernel(const BigdnBwdParams p) {
   const bool absorb = !(c.reverse && it == 0);
   const int fa = c.reverse ? f + 1 : f;  // used only when absorb
 
+  // p.acc: this direction's dbeta and ddecay are added to the arrays' contents
   if (blk == 0 && tid == 0) {
     if (absorb) {
       float s = p.ddz[bh * F + fa];
       for (int cb = 0; cb < D / 32; ++cb) s += c.ddecay_part[((size_t)bh * F + fa) * (D / 32) + cb];
-      c.ddecay[bh * F + fa] = it > 0 ? s : 0.f;
-    } else {
+      c.ddecay[bh * F + fa] = (p.acc ? c.ddecay[bh * F + fa] : 0.f) + (it > 0 ? s : 0.f);
+    } else if (!p.acc) {
       c.ddecay[bh * F] = 0.f;
     }
   }
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(256) void bbwd_tok_kernel(const BigdnBwdParams p) {
         store4(p.dk_rot, t, r, f32x4{0.f, 0.f, 0.f, 0.f});
         store4(p.dv, t, r, f32x4{0.f, 0.f, 0.f, 0.f});
       }
-    if (tid < 64) c.dbeta[bh * N + s0 + tid] = 0.f;
+    if (tid < 64 && !p.acc) c.dbeta[bh * N + s0 + tid] = 0.f;
     return;
   }
   const long ta = (long)fa * c.S + s0;
@@ -442,7 +443,9 @@ __global__ __launch_bounds__(256) void bbwd_tok_kernel(const BigdnBwdParams p) {
     if (lq == 0) red[w][16 * cc + li] = db[cc];
   }
   __syncthreads();
-  if (tid < 64) c.dbeta[bh * N + ta + tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+  if (tid < 64)
+    c.dbeta[bh * N + ta + tid] = (p.acc ? c.dbeta[bh * N + ta + tid] : 0.f) +
+                                 ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
   f32x4 K1[RW][4];
   prod(c.Ab + ((size_t)bh * F + it) * DD, 1, K1);
   if (it > 0) {

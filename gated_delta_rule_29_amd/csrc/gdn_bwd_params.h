@@ -46,7 +46,47 @@ struct BigdnBwdParams {
   float* zs;              // z after every step, D
   float* as;              // gradient of z after every step's update, D
   float* ddz;             // the z stream's part of ddecay, per absorbed frame
+  int acc;                // dbeta and ddecay are added to the arrays' contents
 };
 hipError_t launch_bigdn_dir_bwd(const BigdnBwdParams& p, hipStream_t stream);
+
+// Backward of the BiGDN front end (gdn_prepbwd.hip): the scan directions' gradients of the
+// prepped tensors, summed, taken back through RoPE, ReLU, k-scale and the full-channel
+// RMSNorm to qkv and the norm weights.
+struct PrepBwdParams {
+  const __bf16* qkv;      // [B,N,3,H,D]
+  const float* q_norm_w;  // [H*D]
+  const float* k_norm_w;
+  const float* rope_cos;  // [N,D]
+  const float* rope_sin;
+  float k_scale, eps;
+  int ndir;               // 1 or 2 directions in each gradient tensor
+  const float* dq_rot;    // [ndir,B,H,N,D]
+  const float* dk_rot;
+  const float* dq_pos;
+  const float* dk_pos;
+  const float* dv;
+  float* dqkv;            // [B,N,3,H,D]
+  float* dq_norm_w;       // [H*D]
+  float* dk_norm_w;
+  float* part;            // workspace: the norm weights' partial gradients [nwg][2][H*D]
+  int nwg;                // token groups (one workgroup each)
+  int B, N, H, D;
+};
+hipError_t launch_prep_bwd(const PrepBwdParams& p, hipStream_t stream);
+
+// Backward of the merge out = num / (den + eps) * SiLU(gate) (gdn_prepbwd.hip).
+struct MergeBwdParams {
+  const __bf16* num;      // [B,N,H,D] (the sums over both directions, as bigdn_fwd stores them)
+  const __bf16* den;      // [B,H,N]
+  const __bf16* gate;     // [B,N,H,D] or nullptr
+  const float* dout;      // [B,N,H,D]
+  float eps;
+  float* dnum;            // [B,N,H,D]
+  float* dden;            // [B,H,N]
+  float* dgate;           // [B,N,H,D], given with gate
+  int B, N, H, D;
+};
+hipError_t launch_merge_bwd(const MergeBwdParams& p, hipStream_t stream);
 
 }  // namespace gdn

@@ -22,7 +22,8 @@
  *    gdn_state_apply), and their gradient counterparts (gdn_state_grad_summary,
  *    gdn_state_grad_apply): the single-GPU part of context parallelism;
  *  - the camera branch of the video block (cam_prep, cam_scan, cam_scan_bidi) and the
- *    backward of its scan (cam_scan_bwd); the backward of a BiGDN direction (bigdn_dir_bwd);
+ *    backward of its scan (cam_scan_bwd); the backward of a BiGDN direction (bigdn_dir_bwd),
+ *    of the block's merge (bigdn_merge_bwd) and of its front end (gdn_prep_bwd);
  *  - the backward's inputs (gdn_bwd_prep) and state-gradient pass (gdn_bwd_dhu,
  *    gdn_bwd_dhu_varlen).
  *
@@ -59,8 +60,9 @@ extern "C" {
 #define GDN_API
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 #define GDN_CHUNK 64
+#define GDN_BWD_ACCUMULATE 2  /* bigdn_dir_bwd: add dbeta, ddecay into the outputs */
 
 /* Status codes (the pages' wrappers raise ValueError / NotImplementedError / RuntimeError
  * for these classes, SANA fused_gdn.py page, fused_gdn_func argument checks). */
@@ -431,6 +433,9 @@ GDN_API int cam_scan_bwd(const float* q, const float* k, const float* v, const f
  * FusedBiGDNFunction.backward): gradients of L = sum(num * dnum) + sum(den * dden) for the
  * num, den of one direction of bigdn_fwd on the prepped tensors (reverse = 0 forward, 1
  * reverse; the block's outputs sum both directions, so the caller runs both and adds).
+ * reverse | GDN_BWD_ACCUMULATE adds this direction's dbeta and ddecay to the arrays' contents
+ * instead of writing them (the two directions share beta and decay unless the reverse one is
+ * overridden); the token gradients are always written (gdn_prep_bwd sums directions).
  * With S, z the states and A, a their gradients after a step's update (S_pre = g S_prev,
  * z_pre = g z_prev for the frame the step absorbs), per token:
  *   output frame:   dq_rot = S dnum,  dq_pos = dden z
@@ -456,6 +461,52 @@ GDN_API int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_po
                           float* dq_rot, float* dk_rot, float* dq_pos, float* dk_pos, float* dv,
                           float* dbeta, float* ddecay, int B, int H, int D, int F, int S,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bigdn_merge_bwd -- backward of the BiGDN block's merge (SANA fused_gdn.py page: the dnum and
+ * dden that FusedBiGDNFunction.backward forms from the upstream gradient, with the SiLU gate of
+ * fused_bidi_merge):
+ *   out   = num / (den + merge_eps) * silu(gate)       (silu = 1 when gate is NULL)
+ *   dnum  = dout silu(gate) / (den + merge_eps)
+ *   dden  = -sum_d dout silu(gate) num / (den + merge_eps)^2
+ *   dgate = dout num / (den + merge_eps) * s (1 + gate (1 - s)),  s = sigmoid(gate)
+ *   num [B,N,H,D], den [B,H,N] bf16 IN (the sums over both directions, as bigdn_fwd /
+ *   bigdn_fwd_merged store them); gate [B,N,H,D] bf16 IN or NULL; dout [B,N,H,D] fp32 IN;
+ *   dnum [B,N,H,D], dden [B,H,N] fp32 OUT (the inputs of bigdn_dir_bwd for either direction);
+ *   dgate [B,N,H,D] fp32 OUT, given exactly when gate is.
+ * Supported: D in {64, 128}, H*D <= 4096.  GDN_ERR_INVALID when merge_eps < 0 or when only one
+ * of gate and dgate is given.
+ */
+GDN_API int bigdn_merge_bwd(const void* num, const void* den, const void* gate, const float* dout,
+                            float merge_eps, float* dnum, float* dden, float* dgate, int B, int N,
+                            int H, int D, void* stream);
+
+/*
+ * gdn_prep_bwd -- backward of gdn_prep (SANA fused_gdn.py page, "Backward / autograd
+ * Functions": the RoPE inverse, ReLU and k-scale backward of _fused_gdn_bwd_kernel and the
+ * full-channel RMSNorm backward of FusedBiGDNFunction.backward).  The gradients of the
+ * prepped tensors from ndir scan directions (each tensor [ndir,B,H,N,D], the directions
+ * summed; bigdn_dir_bwd writes one direction's slice) are taken back to qkv and the norm
+ * weights.  Per token, C = H*D, r the inverse RMS, x_hat = x r w:
+ *   g_pos[d] = dpos[d] + drot[d] cos[n,d] + drot[d^1] sin[n,d^1]
+ *   g        = g_pos (times k_scale for k) where x_hat > 0, else 0
+ *   dx[c]    = r w[c] g[c] - r^3 / C x[c] sum_c' w[c'] g[c'] x[c'],   dv passes through
+ *   dw[c]    = sum over all tokens of g[c] x[c] r
+ *   qkv [B,N,3,H,D] bf16, q_norm_w, k_norm_w [H*D], rope_cos, rope_sin [N,D] fp32 IN (as given
+ *   to gdn_prep); dq_rot, dk_rot, dq_pos, dk_pos, dv [ndir,B,H,N,D] fp32 IN, ndir in {1, 2};
+ *   dqkv [B,N,3,H,D], dq_norm_w, dk_norm_w [H*D] fp32 OUT.
+ *   workspace  at least gdn_prep_bwd_workspace_bytes(B, N, H, D) bytes, 256-byte aligned (the
+ *   weight gradients' per-workgroup partial sums, added in a fixed order).
+ * Supported: D in {64, 128}, H*D <= 4096.  GDN_ERR_INVALID for ndir outside {1, 2} or
+ * norm_eps <= 0.
+ */
+GDN_API size_t gdn_prep_bwd_workspace_bytes(int B, int N, int H, int D);
+GDN_API int gdn_prep_bwd(const void* qkv, const float* q_norm_w, const float* k_norm_w,
+                         const float* rope_cos, const float* rope_sin, float k_scale,
+                         float norm_eps, int ndir, const float* dq_rot, const float* dk_rot,
+                         const float* dq_pos, const float* dk_pos, const float* dv, float* dqkv,
+                         float* dq_norm_w, float* dk_norm_w, int B, int N, int H, int D,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdn_bwd_prep -- the inputs of the state-gradient pass, from the forward's inputs

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, "binding lacks %s" % n
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -310,3 +310,63 @@ def test_cam_scan_bwd_validation_codes():
     n = lib.cam_scan_bwd_workspace_bytes(1, 2, 128, 3)
     assert n >= 1 * 2 * 3 * 128 * 128 * (4 * 4 + 4 * 2)
     assert lib.cam_scan_bwd_workspace_bytes(1, 2, 96, 3) == 0
+
+
+def test_bigdn_dir_bwd_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, dnum=FAKE, rev=0, B=1, H=2, D=128, F=3, S=64, ws=None, wsn=0)
+        a.update(kw)
+        return lib.bigdn_dir_bwd(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["dnum"], FAKE,
+                                 a["rev"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"],
+                                 a["H"], a["D"], a["F"], a["S"], a["ws"], a["wsn"], None)
+
+    assert call(q=None) == L.ERR_INVALID
+    assert call(dnum=None) == L.ERR_INVALID
+    assert call(rev=4) == L.ERR_INVALID
+    assert call(rev=-1) == L.ERR_INVALID
+    assert call(D=32) == L.ERR_UNSUPPORTED
+    assert call(S=100) == L.ERR_UNSUPPORTED
+    for rev in (0, 1, L.BWD_ACCUMULATE, 1 | L.BWD_ACCUMULATE):  # valid flags: only the workspace is missing
+        assert call(rev=rev) == L.ERR_WORKSPACE
+
+
+def test_bigdn_merge_bwd_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(num=FAKE, gate=None, dgate=None, eps=1e-6, B=1, N=64, H=2, D=128)
+        a.update(kw)
+        return lib.bigdn_merge_bwd(a["num"], FAKE, a["gate"], FAKE, a["eps"], FAKE, FAKE, a["dgate"],
+                                   a["B"], a["N"], a["H"], a["D"], None)
+
+    assert call(num=None) == L.ERR_INVALID
+    assert call(gate=FAKE) == L.ERR_INVALID   # gate without dgate
+    assert call(dgate=FAKE) == L.ERR_INVALID  # dgate without gate
+    assert call(eps=-1.0) == L.ERR_INVALID
+    assert call(N=0) == L.ERR_INVALID
+    assert call(D=96) == L.ERR_UNSUPPORTED
+    assert call(H=64) == L.ERR_UNSUPPORTED    # H*D > 4096
+
+
+def test_prep_bwd_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(qkv=FAKE, ndir=2, eps=1e-5, B=1, N=64, H=2, D=128, ws=None, wsn=0)
+        a.update(kw)
+        return lib.gdn_prep_bwd(a["qkv"], FAKE, FAKE, FAKE, FAKE, 0.5, a["eps"], a["ndir"], FAKE,
+                                FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["N"], a["H"],
+                                a["D"], a["ws"], a["wsn"], None)
+
+    assert call(qkv=None) == L.ERR_INVALID
+    assert call(ndir=0) == L.ERR_INVALID
+    assert call(ndir=3) == L.ERR_INVALID
+    assert call(eps=0.0) == L.ERR_INVALID
+    assert call(D=96) == L.ERR_UNSUPPORTED
+    assert call() == L.ERR_WORKSPACE
+    n = lib.gdn_prep_bwd_workspace_bytes(1, 64, 2, 128)
+    assert n >= 64 * 2 * 256 * 4                    # one partial pair per token group
+    assert lib.gdn_prep_bwd_workspace_bytes(1, 1 << 20, 16, 128) >= 1024 * 2 * 2048 * 4
+    assert call(ws=ctypes.c_void_p(0x1000 + 16), wsn=n) == L.ERR_INVALID  # misaligned

@@ -22,4 +22,5 @@ def test_more_than_one_gpu_is_refused():
 @pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
 def test_workload_recipes_are_known_kinds(name):
     assert workloads.WORKLOADS[name]["kind"] in ("gdn", "varlen", "bigdn", "bigdn_merged",
-                                                 "summary", "cam", "dhu", "cam_bwd", "bigdn_bwd")
+                                                 "summary", "cam", "dhu", "cam_bwd", "bigdn_bwd",
+                                                 "bigdn_block_bwd")

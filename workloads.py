@@ -114,6 +114,41 @@ def bigdn_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
             "k_scale": 1.0 / math.sqrt(D) / math.sqrt(S), "eps": 1e-5}
 
 
+def prep_bwd_inputs(B, F, S, H, D, ndir=2, seed=0):
+    """Inputs of the front-end backward: bigdn_inputs, then (from seed + 7919) the scan
+    directions' gradients of the prepped tensors, dq_rot, dk_rot, dq_pos, dk_pos, dv
+    [ndir,B,H,N,D] fp32 ~ N(0, 1)."""
+    inp = bigdn_inputs(B, F, S, H, D, seed=seed)
+    gen = _gen(seed + 7919)
+    N = F * S
+    inp["grads"] = {n: torch.randn(ndir, B, H, N, D, generator=gen)
+                    for n in ("dq_rot", "dk_rot", "dq_pos", "dk_pos", "dv")}
+    return inp
+
+
+def merge_bwd_inputs(B, N, H, D, gated=True, seed=0):
+    """Inputs of the merge backward: num [B,N,H,D] bf16 ~ N(0, 1), den [B,H,N] bf16 ~ U(0.5, 2)
+    (the normaliser sums are positive), gate [B,N,H,D] bf16 ~ N(0, 1) (or None), dout
+    [B,N,H,D] fp32 ~ N(0, 1)."""
+    gen = _gen(seed)
+    inp = {"num": torch.randn(B, N, H, D, generator=gen).to(torch.bfloat16),
+           "den": (0.5 + 1.5 * torch.rand(B, H, N, generator=gen)).to(torch.bfloat16),
+           "gate": torch.randn(B, N, H, D, generator=gen).to(torch.bfloat16) if gated else None}
+    inp["dout"] = torch.randn(B, N, H, D, generator=gen)
+    return inp
+
+
+def bigdn_block_bwd_inputs(B, F, S, H, D, seed=0):
+    """Inputs of the whole block's backward: bigdn_inputs, a gate [B,N,H,D] bf16 ~ N(0, 1) and
+    (from seed + 7919) the upstream gradient dout [B,N,H,D] fp32 ~ N(0, 1)."""
+    inp = bigdn_inputs(B, F, S, H, D, seed=seed)
+    gen = _gen(seed + 7919)
+    N = F * S
+    inp["gate"] = torch.randn(B, N, H, D, generator=gen).to(torch.bfloat16)
+    inp["dout"] = torch.randn(B, N, H, D, generator=gen)
+    return inp
+
+
 def dhu_inputs(B, T, H, K, V, dtype="bf16", seed=0, g_shift=3.0, per_key=False):
     """Inputs of the state-gradient pass: q, k L2-normalised per (token, head) and w with the
     magnitude of the WY w (a unit vector times a sigmoid), do, dv ~ N(0,1) in the given dtype;
@@ -239,6 +274,10 @@ WORKLOADS = {
     # backward of the BiGDN block's two frame-scan directions at the same shape (prepped bf16
     # tensors, fp32 upstream gradients)
     "bigdn_bwd_video_f16x1024": dict(kind="bigdn_bwd", B=1, F=16, S=1024, H=16, D=128, seed=0),
+    # backward of the whole BiGDN block at the same shape, from the upstream gradient of its
+    # gated output to qkv, the norm weights, beta, decay and the gate
+    "bigdn_block_bwd_video_f16x1024": dict(kind="bigdn_block_bwd", B=1, F=16, S=1024, H=16, D=128,
+                                           seed=0),
     "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
                                     dtype="bf16", seed=0, g_shift=3.0, per_key=True,
                                     save=True),
@@ -276,4 +315,6 @@ def make(name):
         return cam_scan_bwd_inputs(**w)
     if kind == "bigdn_bwd":
         return bigdn_bwd_inputs(**w)
+    if kind == "bigdn_block_bwd":
+        return bigdn_block_bwd_inputs(**w)
     raise KeyError(name)
