@@ -132,8 +132,9 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
 
 namespace {
 
-// gdn_state_summary workspace: the forward pass's own workspace and its discarded per-token
-// outputs.  Every view 256-byte aligned.
+// gdn_state_summary workspace: the forward pass's own workspace and, except on the fused bf16
+// path (which forms the state alone), its discarded per-token outputs.  Every view 256-byte
+// aligned.
 struct SummaryWs {
   size_t fwd, o, wy, total;
 };
@@ -147,7 +148,7 @@ SummaryWs summary_ws(int B, int T, int H, int K, int V, int dtype, bool per_key)
   w.fwd = off;
   off = al256s(off + gdn_fwd_workspace_bytes(B, T, H, K, V, dtype, per_key ? GDN_FWD_PER_KEY : 0u));
   w.o = off;
-  off = al256s(off + tok * (size_t)V * es);
+  if (!fused_path(dtype, per_key ? GDN_FWD_PER_KEY : 0u)) off = al256s(off + tok * (size_t)V * es);
   w.wy = off;
   off = al256s(off + gdn::transition_ws_bytes(B, T, H, K, dtype, per_key));
   w.total = off;
@@ -184,10 +185,11 @@ int gdn_state_summary(const void* k, const void* v, const float* g, const float*
     return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  // state_ext: the fragment from a zero initial state (the per-token outputs are discarded)
+  // state_ext: the fragment from a zero initial state (the per-token outputs are discarded; the
+  // fused bf16 path does not form them at all)
   gdn::FwdParams p{};
   p.q = k; p.k = k; p.v = v; p.g = g; p.gk = gk; p.beta = beta; p.h0 = nullptr;
-  p.o = ws + w.o; p.ht = state_ext; p.h_chunks = nullptr; p.v_new = nullptr; p.cu = nullptr;
+  p.o = fused_path(dtype, gk ? GDN_FWD_PER_KEY : 0u) ? nullptr : ws + w.o; p.ht = state_ext; p.h_chunks = nullptr; p.v_new = nullptr; p.cu = nullptr;
   p.scale = 1.f; p.B = B; p.T = T; p.H = H; p.V = V; p.nvb = V / 64;
   p.nseq = 0; p.nt_total = 0; p.ws = ws + w.fwd; p.coffs = nullptr;
   hipError_t e = gdn::launch_gdn_fwd(p, dtype, K, false, st);

@@ -253,7 +253,9 @@ __device__ __forceinline__ void prod_tiles(const bf16* qt, const bf16* kt, const
   }
 }
 
-template <int K, bool VARLEN>
+// OUT false: the state pass alone (o is not formed): no q transfers, no Q K^T role, and the
+// scan waves skip Q h, P v_new and the output stores (the fragment state summary's use).
+template <int K, bool VARLEN, bool OUT>
 __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
   typedef FusedSmem<K> SM;
   constexpr int kG = K / 32;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
     const bf16* vg = static_cast<const bf16*>(p.v);
     auto rows_of = [&](int c) { return (uint32_t)min(kC, len - c * kC); };
     auto issue_qk = [&](int c) {  // q (wave 4) or k (wave 5) of chunk c into ring slot c % 3
-      if (c >= nchunks) return;
+      if (c >= nchunks || (!OUT && tw == 0)) return;
       const long tok = tok0 + (long)c * kC;
       const i32x4 r = make_rsrc((tw ? kg : qg) + (tok * p.H + h) * K, rows_of(c) * qk_row);
       u16* dst = tw ? s.qk[c % 3].k : s.qk[c % 3].q;
@@ -530,7 +532,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
             } else if (pq == 2) {
               // ---- off-diagonal Gram tiles -> A rows (fp16)
               prod_tiles<K, false, 0x1dau, kFastDecay>(qt, kt, G, s.af, p.scale);
-            } else {
+            } else if constexpr (OUT) {
               // ---- Q K^T tiles -> P rows (fp16)
               prod_tiles<K, true, 0x3ffu, kFastDecay>(qt, kt, G, T.p, p.scale);
             }
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
               eg[P][t] = lds_at<f32x4>(gq, 2 * (kEg + r0 - 8 * lq));
             }
         }
-        if (G == kG - 1) read_q(n, ob);
+        if (OUT && G == kG - 1) read_q(n, ob);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -717,10 +719,11 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       f16x8 by[2];
 #pragma unroll
       for (int Gk = 0; Gk < kG; ++Gk) {
+        if constexpr (OUT)
 #pragma unroll
-        for (int G = 0; G < 2; ++G)
+          for (int G = 0; G < 2; ++G)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) oacc[G][t] = mma16(bh[Gk], qfr[G][t][Gk], oacc[G][t]);
+            for (int t = 0; t < 2; ++t) oacc[G][t] = mma16(bh[Gk], qfr[G][t][Gk], oacc[G][t]);
         if (Gk == 0) {
 #pragma unroll
           for (int P = 0; P < 2; ++P)
@@ -756,15 +759,16 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       f16x8 pfr[2][2][2];
       lds_u16* pb[2] = {lds_base(T.p + ob[0]), lds_base(T.p + ob[1])};
       float ego[2][2];
+      if constexpr (OUT)
 #pragma unroll
-      for (int G = 0; G < 2; ++G)
+        for (int G = 0; G < 2; ++G)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = pair_row(G, t, li);
+          for (int t = 0; t < 2; ++t) {
+            const int r = pair_row(G, t, li);
 #pragma unroll
-          for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds_at<f16x8>(pb[t], 1024 * G + 2048 * P);
-          ego[G][t] = lds_at<float>(gp, 2 * (kEg + r - pair_row(0, 0, li))) * p.scale;
-        }
+            for (int P = 0; P <= G; ++P) pfr[G][t][P] = lds_at<f16x8>(pb[t], 1024 * G + 2048 * P);
+            ego[G][t] = lds_at<float>(gp, 2 * (kEg + r - pair_row(0, 0, li))) * p.scale;
+          }
       f32x4 vn[2][2];
 #pragma unroll
       for (int G = 0; G < 2; ++G)
@@ -816,17 +820,19 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       // stale ring slot and go unused: reading unconditionally keeps the registers in place
       // instead of copying the old values on the path that skips the read)
       read_k(n + 1, ob, 0, kG / 2);
-      const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
+      if constexpr (OUT) {
+        const __amdgpu_buffer_rsrc_t ro = store_rsrc(og + (tok * p.H + h) * p.V + v0, rows * v_row);
 #pragma unroll
-      for (int G = 0; G < 2; ++G)
+        for (int G = 0; G < 2; ++G)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f32x4 acc = oacc[G][t] * ego[G][t];
+          for (int t = 0; t < 2; ++t) {
+            f32x4 acc = oacc[G][t] * ego[G][t];
 #pragma unroll
-          for (int P = 0; P <= G; ++P) acc = mma16(bv[P], pfr[G][t][P], acc);
-          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(acc[0], acc[1], acc[2], acc[3]), ro,
-                                                pair_row(G, t, li) * v_row + (16 * wave + 4 * lq) * 2, 0, 0);
-        }
+            for (int P = 0; P <= G; ++P) acc = mma16(bv[P], pfr[G][t][P], acc);
+            __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(acc[0], acc[1], acc[2], acc[3]), ro,
+                                                  pair_row(G, t, li) * v_row + (16 * wave + 4 * lq) * 2, 0, 0);
+          }
+      }
     }
     __syncthreads();
   }
@@ -867,7 +873,7 @@ __global__ __launch_bounds__(1024) void rank_kernel(const int* cu, int N, int* o
   }
 }
 
-template <int K, bool VL>
+template <int K, bool VL, bool OUT>
 hipError_t launch_k(const FwdParams& p0, int nchains, hipStream_t stream) {
   FwdParams p = p0;
   p.nvb = p.V / kBV;
@@ -878,15 +884,19 @@ hipError_t launch_k(const FwdParams& p0, int nchains, hipStream_t stream) {
     hipLaunchKernelGGL(rank_kernel, dim3(1), dim3(1024), 0, stream, p.cu, p.nseq, order);
     p.order = order;
   }
-  hipLaunchKernelGGL((fused16_kernel<K, VL>), dim3(nchains * p.nvb), dim3(kThr), 0, stream, p);
+  hipLaunchKernelGGL((fused16_kernel<K, VL, OUT>), dim3(nchains * p.nvb), dim3(kThr), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// o == nullptr (dense batches): the state pass alone
 hipError_t launch_fused16(const FwdParams& p, int K, bool varlen, int nchains, hipStream_t stream) {
-  if (K == 128) return varlen ? launch_k<128, true>(p, nchains, stream) : launch_k<128, false>(p, nchains, stream);
-  return varlen ? launch_k<64, true>(p, nchains, stream) : launch_k<64, false>(p, nchains, stream);
+  if (!p.o && !varlen)
+    return K == 128 ? launch_k<128, false, false>(p, nchains, stream) : launch_k<64, false, false>(p, nchains, stream);
+  if (K == 128)
+    return varlen ? launch_k<128, true, true>(p, nchains, stream) : launch_k<128, false, true>(p, nchains, stream);
+  return varlen ? launch_k<64, true, true>(p, nchains, stream) : launch_k<64, false, true>(p, nchains, stream);
 }
 
 }  // namespace gdn
