@@ -11,9 +11,10 @@ Contents
     map from initial to final state), the packed-varlen tables and driver, the BiGDN
     front end (full-channel RMSNorm, ReLU, k-scale, interleaved-pair RoPE) and the
     frame-level BiGDN scan in both directions, the camera-branch prep (UCPE 4x4 blocks and
-    half-width RoPE) and its numerator-only frame scan with state in and out, and the
-    state-gradient pass of the chunked backward (dhu).  This is the reference every GPU
-    result is compared with.
+    half-width RoPE) and its numerator-only frame scan with state in and out, the
+    state-gradient pass of the chunked backward (dhu), and the backward of the BiGDN block
+    (frame scan per direction, merge, front end) and of the camera branch (scan, prep).
+    This is the reference every GPU result is compared with.
   * ``forms.py``: independent numpy cross-check forms (global O(T^2) solve, chunked WY
     form, BiGDN product form with flip-and-shift reverse) used only to pin the oracle.
 
@@ -76,11 +77,12 @@ def _load():
         lib.oracle_bigdn_dir_bwd.argtypes = [I, I, I, I, I, I] + [P] * 16
         lib.oracle_prep_bwd.argtypes = [I, I, I, I, P, P, P, P, P, Dd, Dd, I] + [P] * 8
         lib.oracle_bigdn_merge_bwd.argtypes = [I, I, I, I, P, P, P, P, Dd, P, P, P]
+        lib.oracle_cam_prep_bwd.argtypes = [I, I, I, I] + [P] * 8 + [Dd, Dd] + [P] * 9
         lib.oracle_set_threads.argtypes = [I]
         for name in ("oracle_gdn", "oracle_gdn_varlen", "oracle_varlen_tables", "oracle_prep",
                      "oracle_bigdn_dir", "oracle_bigdn", "oracle_max_threads",
                      "oracle_gdn_transition", "oracle_gdn_bwd_prep", "oracle_bigdn_dir_bwd",
-                     "oracle_prep_bwd", "oracle_bigdn_merge_bwd"):
+                     "oracle_prep_bwd", "oracle_bigdn_merge_bwd", "oracle_cam_prep_bwd"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -356,6 +358,27 @@ def cam_prep(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k
     if rc != 0:
         raise RuntimeError("oracle_cam_prep failed")
     return outs[0], outs[1], outs[2], infl
+
+
+def cam_prep_bwd(q, k, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, dq_t,
+                 dk_t, dv_t, dinfl=None, eps=1e-5):
+    """Backward of cam_prep (SANA fused_cam_gdn.py page, _cam_prep_bwd_kernel and
+    _cam_prep_bwd_dispatch): from the gradients of q_t, k_t, v_t [B,H,D,N] and of the
+    inflation [B,H,N] (or None), the gradients of q, k, v [B,N,H,D] and of the norm weights
+    [H*D].  Returns dict dq, dk, dv, dq_norm_w, dk_norm_w."""
+    q, k, qw, kw, pq, pkv, cs, sn, dq_t, dk_t, dv_t, dinfl = map(
+        _f64, (q, k, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, dq_t, dk_t, dv_t,
+               dinfl))
+    B, N, H, D = q.shape
+    out = {n: np.empty((B, N, H, D)) for n in ("dq", "dk", "dv")}
+    out["dq_norm_w"], out["dk_norm_w"] = np.empty(H * D), np.empty(H * D)
+    rc = _load().oracle_cam_prep_bwd(B, N, H, D, _p(q), _p(k), _p(qw), _p(kw), _p(pq), _p(pkv),
+                                     _p(cs), _p(sn), float(k_scale), float(eps), _p(dq_t),
+                                     _p(dk_t), _p(dv_t), _p(dinfl), _p(out["dq"]), _p(out["dk"]),
+                                     _p(out["dv"]), _p(out["dq_norm_w"]), _p(out["dk_norm_w"]))
+    if rc != 0:
+        raise RuntimeError("oracle_cam_prep_bwd failed")
+    return out
 
 
 def cam_scan(q, k, v, beta, decay, reverse=False, init_state=None, want_final=False):

@@ -1193,3 +1193,114 @@ int oracle_bigdn_merge_bwd(int B, int N, int H, int D, const double* num, const 
       }
   return 0;
 }
+
+/*
+ * Backward of the camera-branch prep (oracle_cam_prep), following the SANA fused_cam_gdn.py
+ * page (_cam_prep_bwd_kernel, _cam_prep_bwd_dispatch): gradients of q, k, v [B,N,H,D] and of
+ * the norm weights [H*D] from the gradients of the outputs q_t, k_t, v_t [B,H,D,N] and of the
+ * inflation [B,H,N] (dinfl may be NULL: no inflation gradient).  Per token (serial, so the
+ * weight gradients are summed in token order) and head, with xn the post-ReLU (k: times
+ * k_scale) vector, y = T xn the output (UCPE 4x4 blocks on channels [0, D/2), RoPE on
+ * [D/2, D)), pre = |xn_k|^2, post = |y_k|^2, inflation = max(post, 1e-12) / max(pre, 1e-12):
+ *   d_post = dinfl [post > 1e-12] / max(pre, 1e-12)
+ *   d_pre  = -dinfl max(post, 1e-12) / max(pre, 1e-12)^2 [pre > 1e-12]
+ *   dxn    = T^T dy   (dy_k = dk_t + 2 y_k d_post);   dxn_k += 2 xn_k d_pre
+ *   T^T:  dxn[4g+j] = sum_i P[i][j] dy[4g+i];  dxn[D/2+r] = dy[D/2+r] cos[r] + dy[D/2+(r^1)] sin[r^1]
+ *   g = dxn (times k_scale for k) where x_hat > 0;  dv = dxn_v
+ * then the full-channel RMSNorm backward of oracle_prep_bwd.
+ */
+int oracle_cam_prep_bwd(int B, int N, int H, int D, const double* q, const double* k,
+                        const double* qw, const double* kw, const double* pq, const double* pkv,
+                        const double* cosv, const double* sinv, double k_scale, double eps,
+                        const double* dq_t, const double* dk_t, const double* dv_t,
+                        const double* dinfl, double* dq, double* dk, double* dv, double* dqw,
+                        double* dkw) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0 || (D % 8) != 0 || D > 512) return -1;
+  const long C = (long)H * D;
+  const int Dh = D / 2;
+  double* g = (double*)malloc(sizeof(double) * 2 * C);
+  if (!g) return -1;
+  for (long c = 0; c < C; ++c) dqw[c] = dkw[c] = 0.0;
+  for (long bn = 0; bn < (long)B * N; ++bn) {
+    const long b = bn / N, n = bn % N;
+    const double* xr[2] = {q + bn * C, k + bn * C};
+    double inv[2];
+    for (int which = 0; which < 2; ++which) {
+      double ss = 0.0;
+      for (long c = 0; c < C; ++c) ss += xr[which][c] * xr[which][c];
+      inv[which] = 1.0 / sqrt(ss / (double)C + eps);
+    }
+    const double* P[3] = {pq + bn * 16, pkv + bn * 16, pkv + bn * 16};
+    const double* dyt[3] = {dq_t, dk_t, dv_t};
+    for (int h = 0; h < H; ++h) {
+      double xn[2][512], y[512], dy[512], dx[512];
+      for (int which = 0; which < 2; ++which)
+        for (int d = 0; d < D; ++d) {
+          const double w = (which ? kw : qw)[(long)h * D + d];
+          const double t = xr[which][(long)h * D + d] * inv[which] * w;
+          xn[which][d] = (t > 0.0 ? t : 0.0) * (which ? k_scale : 1.0);
+        }
+      /* the k output and the inflation's two squared norms */
+      double pre = 0.0, post = 0.0;
+      for (int gi = 0; gi < Dh / 4; ++gi)
+        for (int i = 0; i < 4; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < 4; ++j) acc += P[1][i * 4 + j] * xn[1][4 * gi + j];
+          y[4 * gi + i] = acc;
+        }
+      for (int r = 0; r < Dh; ++r)
+        y[Dh + r] = xn[1][Dh + r] * cosv[n * Dh + r] + xn[1][Dh + (r ^ 1)] * sinv[n * Dh + r];
+      for (int d = 0; d < D; ++d) {
+        pre += xn[1][d] * xn[1][d];
+        post += y[d] * y[d];
+      }
+      double d_post = 0.0, d_pre = 0.0;
+      if (dinfl) {
+        const double di = dinfl[((long)b * H + h) * N + n];
+        const double prec = pre > 1e-12 ? pre : 1e-12, postc = post > 1e-12 ? post : 1e-12;
+        d_post = post > 1e-12 ? di / prec : 0.0;
+        d_pre = pre > 1e-12 ? -di * postc / (prec * prec) : 0.0;
+      }
+      for (int which = 0; which < 3; ++which) {
+        for (int d = 0; d < D; ++d) {
+          dy[d] = dyt[which][(((long)b * H + h) * D + d) * N + n];
+          if (which == 1) dy[d] += 2.0 * y[d] * d_post;
+        }
+        for (int gi = 0; gi < Dh / 4; ++gi)
+          for (int j = 0; j < 4; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < 4; ++i) acc += P[which][i * 4 + j] * dy[4 * gi + i];
+            dx[4 * gi + j] = acc;
+          }
+        for (int r = 0; r < Dh; ++r)
+          dx[Dh + r] = dy[Dh + r] * cosv[n * Dh + r] + dy[Dh + (r ^ 1)] * sinv[n * Dh + (r ^ 1)];
+        for (int d = 0; d < D; ++d) {
+          const long c = (long)h * D + d;
+          if (which == 2) {
+            dv[bn * C + c] = dx[d];
+          } else {
+            double gv = dx[d];
+            if (which == 1) gv = (gv + 2.0 * xn[1][d] * d_pre) * k_scale;
+            const double w = (which ? kw : qw)[c];
+            g[which * C + c] = xr[which][c] * inv[which] * w > 0.0 ? gv : 0.0;
+          }
+        }
+      }
+    }
+    for (int which = 0; which < 2; ++which) {
+      const double* x = xr[which];
+      const double* w = which ? kw : qw;
+      double s = 0.0;
+      for (long c = 0; c < C; ++c) s += w[c] * g[which * C + c] * x[c];
+      const double r = inv[which];
+      double* out = which ? dk : dq;
+      double* dw = which ? dkw : dqw;
+      for (long c = 0; c < C; ++c) {
+        out[bn * C + c] = r * w[c] * g[which * C + c] - r * r * r / (double)C * x[c] * s;
+        dw[c] += g[which * C + c] * x[c] * r;
+      }
+    }
+  }
+  free(g);
+  return 0;
+}

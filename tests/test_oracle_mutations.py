@@ -22,6 +22,7 @@ PINS_DHU = "tests/test_oracle_dhu.py"
 PINS_CBWD = "tests/test_oracle_cam_bwd.py"
 PINS_BBWD = "tests/test_oracle_bigdn_bwd.py"
 PINS_PREPBWD = "tests/test_oracle_prep_bwd.py"
+PINS_CPBWD = "tests/test_oracle_cam_prep_bwd.py"
 
 # (name, pin file, text in gdn_oracle.c, replacement)
 MUTATIONS = [
@@ -79,6 +80,16 @@ MUTATIONS = [
      "g[which * C + c] = xhat > 0.0 ? gp : 0.0;"),
     ("merge backward: dden with one factor of 1 / (den + eps)", PINS_PREPBWD,
      "dden[(b * H + h) * N + n] = -acc * inv * inv;", "dden[(b * H + h) * N + n] = -acc * inv;"),
+    ("camera prep backward: RoPE transpose with the token's own sine", PINS_CPBWD,
+     "dy[Dh + (r ^ 1)] * sinv[n * Dh + (r ^ 1)];", "dy[Dh + (r ^ 1)] * sinv[n * Dh + r];"),
+    ("camera prep backward: 4x4 block not transposed", PINS_CPBWD,
+     "for (int i = 0; i < 4; ++i) acc += P[which][i * 4 + j] * dy[4 * gi + i];",
+     "for (int i = 0; i < 4; ++i) acc += P[which][j * 4 + i] * dy[4 * gi + i];"),
+    ("camera prep backward: inflation without its pre-norm term", PINS_CPBWD,
+     "if (which == 1) gv = (gv + 2.0 * xn[1][d] * d_pre) * k_scale;",
+     "if (which == 1) gv = gv * k_scale;"),
+    ("camera prep backward: inflation's output term with one factor of y", PINS_CPBWD,
+     "if (which == 1) dy[d] += 2.0 * y[d] * d_post;", "if (which == 1) dy[d] += 2.0 * d_post;"),
     ("camera backward: dv without beta", PINS_CBWD,
      "dv[base + (long)c * N + t] = bt * dd[c];", "dv[base + (long)c * N + t] = dd[c];"),
     ("camera backward: dk without the prediction term", PINS_CBWD,
