@@ -1202,8 +1202,9 @@ int oracle_bigdn_merge_bwd(int B, int N, int H, int D, const double* num, const 
  * weight gradients are summed in token order) and head, with xn the post-ReLU (k: times
  * k_scale) vector, y = T xn the output (UCPE 4x4 blocks on channels [0, D/2), RoPE on
  * [D/2, D)), pre = |xn_k|^2, post = |y_k|^2, inflation = max(post, 1e-12) / max(pre, 1e-12):
- *   d_post = dinfl [post > 1e-12] / max(pre, 1e-12)
- *   d_pre  = -dinfl max(post, 1e-12) / max(pre, 1e-12)^2 [pre > 1e-12]
+ *   d_post = dinfl [post >= 1e-12] / max(pre, 1e-12)
+ *   d_pre  = -dinfl max(post, 1e-12) / max(pre, 1e-12)^2 [pre >= 1e-12]
+ * (the indicators of the two clamps include equality, as the page's dispatch states them)
  *   dxn    = T^T dy   (dy_k = dk_t + 2 y_k d_post);   dxn_k += 2 xn_k d_pre
  *   T^T:  dxn[4g+j] = sum_i P[i][j] dy[4g+i];  dxn[D/2+r] = dy[D/2+r] cos[r] + dy[D/2+(r^1)] sin[r^1]
  *   g = dxn (times k_scale for k) where x_hat > 0;  dv = dxn_v
@@ -1258,8 +1259,8 @@ int oracle_cam_prep_bwd(int B, int N, int H, int D, const double* q, const doubl
       if (dinfl) {
         const double di = dinfl[((long)b * H + h) * N + n];
         const double prec = pre > 1e-12 ? pre : 1e-12, postc = post > 1e-12 ? post : 1e-12;
-        d_post = post > 1e-12 ? di / prec : 0.0;
-        d_pre = pre > 1e-12 ? -di * postc / (prec * prec) : 0.0;
+        d_post = post >= 1e-12 ? di / prec : 0.0;
+        d_pre = pre >= 1e-12 ? -di * postc / (prec * prec) : 0.0;
       }
       for (int which = 0; which < 3; ++which) {
         for (int d = 0; d < D; ++d) {
