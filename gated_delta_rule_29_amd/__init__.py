@@ -18,7 +18,7 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi", "cam_scan_bwd", "bigdn_dir_bwd", "bigdn_merge_bwd", "gdn_prep_bwd",
+           "cam_scan_bidi", "cam_scan_bwd", "cam_prep_bwd", "bigdn_dir_bwd", "bigdn_merge_bwd", "gdn_prep_bwd",
            "bigdn_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
            "gdn_state_grad_summary", "gdn_state_grad_apply", "gdn_abi_version",
            "gdn_last_error", "CHUNK"]
@@ -374,6 +374,43 @@ def cam_prep(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k
                       B, N, H, D, _ptr(ws), ws_n, _stream(dev))
     _lib.check(rc, "cam_prep")
     return outs[0], outs[1], outs[2], infl
+
+
+def cam_prep_bwd(q, k, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, dq_t,
+                 dk_t, dv_t, dinfl=None, norm_eps=1e-5):
+    """Backward of cam_prep.  q, k and the prep's parameters as given to cam_prep; dq_t, dk_t,
+    dv_t the gradients of its outputs, [B,H,D,N] or [ndir,B,H,D,N] fp32 (the directions are
+    summed); dinfl [B,H,N] fp32 or None.  Returns a dict with dq, dk, dv [B,N,H,D] and
+    dq_norm_w, dk_norm_w [H*D] (fp32)."""
+    B, N, H, D = q.shape
+    dev = q.device
+    _need(q, "q", (B, N, H, D), torch.float32, dev)
+    _need(k, "k", (B, N, H, D), torch.float32, dev)
+    _need(q_norm_w, "q_norm_w", (H * D,), torch.float32, dev)
+    _need(k_norm_w, "k_norm_w", (H * D,), torch.float32, dev)
+    _need(proj_q, "proj_q", (B, N, 4, 4), torch.float32, dev)
+    _need(proj_kv, "proj_kv", (B, N, 4, 4), torch.float32, dev)
+    _need(rope_cos, "rope_cos", (N, D // 2), torch.float32, dev)
+    _need(rope_sin, "rope_sin", (N, D // 2), torch.float32, dev)
+    ndir = 1 if dq_t.dim() == 4 else dq_t.shape[0]
+    shape = (B, H, D, N) if dq_t.dim() == 4 else (ndir, B, H, D, N)
+    for t, name in ((dq_t, "dq_t"), (dk_t, "dk_t"), (dv_t, "dv_t")):
+        _need(t, name, shape, torch.float32, dev)
+    _need(dinfl, "dinfl", (B, H, N), torch.float32, dev)
+    out = {n: torch.empty(B, N, H, D, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
+    out["dq_norm_w"] = torch.empty(H * D, dtype=torch.float32, device=dev)
+    out["dk_norm_w"] = torch.empty(H * D, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    ws_n = lib.cam_prep_bwd_workspace_bytes(B, N, H, D)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rc = lib.cam_prep_bwd(_ptr(q), _ptr(k), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(proj_q),
+                          _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin), float(k_scale),
+                          float(norm_eps), ndir, _ptr(dq_t), _ptr(dk_t), _ptr(dv_t), _ptr(dinfl),
+                          _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                          _ptr(out["dq_norm_w"]), _ptr(out["dk_norm_w"]), B, N, H, D, _ptr(ws),
+                          ws_n, _stream(dev))
+    _lib.check(rc, "cam_prep_bwd")
+    return out
 
 
 def cam_scan(q, k, v, beta, decay, *, reverse=False, init_state=None, save_final_state=False):

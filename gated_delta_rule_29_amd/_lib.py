@@ -56,6 +56,8 @@ SIGNATURES = {
     "bigdn_merge_bwd": (I, [P, P, P, P, F, P, P, P, I, I, I, I, P]),
     "gdn_prep_bwd_workspace_bytes": (SZ, [I, I, I, I]),
     "gdn_prep_bwd": (I, [P, P, P, P, P, F, F, I] + [P] * 8 + [I, I, I, I, P, SZ, P]),
+    "cam_prep_bwd_workspace_bytes": (SZ, [I, I, I, I]),
+    "cam_prep_bwd": (I, [P] * 8 + [F, F, I] + [P] * 9 + [I, I, I, I, P, SZ, P]),
     "gdn_bwd_prep": (I, [P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]),
     "gdn_state_grad_summary_workspace_bytes": (SZ, [I, I, I, I, I]),
     "gdn_state_grad_summary": (I, [P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, P, SZ, P]),

@@ -785,6 +785,49 @@ int gdn_prep_bwd(const void* qkv, const float* q_norm_w, const float* k_norm_w,
   return ok();
 }
 
+size_t cam_prep_bwd_workspace_bytes(int B, int N, int H, int D) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0) return 0;
+  return al256((size_t)B * N * 4) + al256((size_t)prep_bwd_groups(B, N) * 2 * H * D * 4);
+}
+
+int cam_prep_bwd(const float* q, const float* k, const float* q_norm_w, const float* k_norm_w,
+                 const float* proj_q, const float* proj_kv, const float* rope_cos,
+                 const float* rope_sin, float k_scale, float norm_eps, int ndir, const float* dq_t,
+                 const float* dk_t, const float* dv_t, const float* dinfl, float* dq, float* dk,
+                 float* dv, float* dq_norm_w, float* dk_norm_w, int B, int N, int H, int D,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !q_norm_w || !k_norm_w || !proj_q || !proj_kv || !rope_cos || !rope_sin ||
+      !dq_t || !dk_t || !dv_t || !dq || !dk || !dv || !dq_norm_w || !dk_norm_w)
+    return fail(GDN_ERR_INVALID, "every input and gradient pointer except dinfl must be non-null");
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0)
+    return fail(GDN_ERR_INVALID, "B, N, H, D must be positive (got %d, %d, %d, %d)", B, N, H, D);
+  if (D % 8) return fail(GDN_ERR_INVALID, "D must be even with D/2 a multiple of 4, got %d", D);
+  if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
+  if (N % 4) return fail(GDN_ERR_UNSUPPORTED, "N must be a multiple of 4, got %d", N);
+  if ((int64_t)H * D > 4096) return fail(GDN_ERR_UNSUPPORTED, "H*D must be <= 4096, got %d", H * D);
+  if ((int64_t)B * N > INT32_MAX || (int64_t)B * H * ((N + 63) / 64) > INT32_MAX)
+    return fail(GDN_ERR_INVALID, "B*N exceeds the grid limit");
+  if (ndir != 1 && ndir != 2) return fail(GDN_ERR_INVALID, "ndir must be 1 or 2, got %d", ndir);
+  if (!(norm_eps > 0.f)) return fail(GDN_ERR_INVALID, "norm_eps must be positive");
+  const size_t need = cam_prep_bwd_workspace_bytes(B, N, H, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GDN_ERR_INVALID, "workspace must be 256-byte aligned");
+  gdn::CamPrepBwdParams p{};
+  p.q = q; p.k = k; p.q_norm_w = q_norm_w; p.k_norm_w = k_norm_w; p.proj_q = proj_q;
+  p.proj_kv = proj_kv; p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.k_scale = k_scale;
+  p.eps = norm_eps; p.ndir = ndir; p.dq_t = dq_t; p.dk_t = dk_t; p.dv_t = dv_t; p.dinfl = dinfl;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dq_norm_w = dq_norm_w; p.dk_norm_w = dk_norm_w;
+  p.k_inv_rms = static_cast<float*>(workspace);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + al256((size_t)B * N * 4));
+  p.nwg = (int)prep_bwd_groups(B, N);
+  p.B = B; p.N = N; p.H = H; p.D = D;
+  hipError_t e = gdn::launch_cam_prep_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cam_prep_bwd launch");
+  return ok();
+}
+
 int bigdn_merge_bwd(const void* num, const void* den, const void* gate, const float* dout,
                     float merge_eps, float* dnum, float* dden, float* dgate, int B, int N, int H,
                     int D, void* stream) {

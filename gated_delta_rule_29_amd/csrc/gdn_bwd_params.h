@@ -89,4 +89,32 @@ struct MergeBwdParams {
 };
 hipError_t launch_merge_bwd(const MergeBwdParams& p, hipStream_t stream);
 
+// Backward of the camera-branch prep (gdn_prepbwd.hip).
+struct CamPrepBwdParams {
+  const float* q;          // [B,N,H,D] fp32, the raw inputs of the prep
+  const float* k;
+  const float* q_norm_w;   // [H*D]
+  const float* k_norm_w;
+  const float* proj_q;     // [B,N,4,4]
+  const float* proj_kv;
+  const float* rope_cos;   // [N,D/2]
+  const float* rope_sin;
+  float k_scale, eps;
+  int ndir;                // 1 or 2 directions in each upstream gradient tensor
+  const float* dq_t;       // [ndir,B,H,D,N] gradients of the prep's outputs
+  const float* dk_t;
+  const float* dv_t;
+  const float* dinfl;      // [B,H,N] gradient of the inflation, or nullptr
+  float* k_inv_rms;        // [B,N] workspace (written first when dinfl is given)
+  float* dq;               // [B,N,H,D]: the gradient before the RMSNorm first, then dq in place
+  float* dk;
+  float* dv;
+  float* dq_norm_w;        // [H*D]
+  float* dk_norm_w;
+  float* part;             // workspace: the norm weights' partial gradients [nwg][2][H*D]
+  int nwg;                 // token groups of the RMSNorm backward (one workgroup each)
+  int B, N, H, D;
+};
+hipError_t launch_cam_prep_bwd(const CamPrepBwdParams& p, hipStream_t stream);
+
 }  // namespace gdn

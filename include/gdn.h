@@ -22,7 +22,7 @@
  *    gdn_state_apply), and their gradient counterparts (gdn_state_grad_summary,
  *    gdn_state_grad_apply): the single-GPU part of context parallelism;
  *  - the camera branch of the video block (cam_prep, cam_scan, cam_scan_bidi) and the
- *    backward of its scan (cam_scan_bwd); the backward of a BiGDN direction (bigdn_dir_bwd),
+ *    backward of its scan (cam_scan_bwd) and of its prep (cam_prep_bwd); the backward of a BiGDN direction (bigdn_dir_bwd),
  *    of the block's merge (bigdn_merge_bwd) and of its front end (gdn_prep_bwd);
  *  - the backward's inputs (gdn_bwd_prep) and state-gradient pass (gdn_bwd_dhu,
  *    gdn_bwd_dhu_varlen).
@@ -60,7 +60,7 @@ extern "C" {
 #define GDN_API
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 #define GDN_CHUNK 64
 #define GDN_BWD_ACCUMULATE 2  /* bigdn_dir_bwd: add dbeta, ddecay into the outputs */
 
@@ -505,6 +505,40 @@ GDN_API int gdn_prep_bwd(const void* qkv, const float* q_norm_w, const float* k_
                          const float* rope_cos, const float* rope_sin, float k_scale,
                          float norm_eps, int ndir, const float* dq_rot, const float* dk_rot,
                          const float* dq_pos, const float* dk_pos, const float* dv, float* dqkv,
+                         float* dq_norm_w, float* dk_norm_w, int B, int N, int H, int D,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cam_prep_bwd -- backward of cam_prep (SANA fused_cam_gdn.py page: _cam_prep_bwd_kernel and
+ * _cam_prep_bwd_dispatch): the gradients of q, k, v and of the two norm weights from those of
+ * cam_prep's outputs q_t, k_t, v_t (each [ndir,B,H,D,N], the directions summed, so the two
+ * directions' cam_scan_bwd results go in unchanged) and, optionally, of the inflation.  With
+ * x_n = relu(x r w) (times k_scale for k; v is not normed), y = T x_n the output (T the token's
+ * 4x4 camera matrix on each group of four of channels [0, D/2), RoPE on [D/2, D)), pre =
+ * |x_n,k|^2, post = |y_k|^2 per (b, h, n):
+ *   d_post = dinfl [post >= 1e-12] / max(pre, 1e-12)
+ *   d_pre  = -dinfl max(post, 1e-12) / max(pre, 1e-12)^2 [pre >= 1e-12]
+ *   dx_n   = T^T (dy + 2 y d_post) (+ 2 x_n d_pre for k);  dv = T^T dy_v
+ *   T^T:  dx_n[4g + j] = sum_i P[i][j] dy[4g + i],
+ *         dx_n[D/2 + r] = dy[D/2 + r] cos[n,r] + dy[D/2 + (r^1)] sin[n,r^1]
+ *   g      = dx_n (times k_scale for k) where x w > 0, else 0
+ *   dx[c]  = r w[c] g[c] - r^3 / C x[c] sum_c' w[c'] g[c'] x[c'],  C = H*D
+ *   dw[c]  = sum over all tokens of g[c] x[c] r
+ *   q, k [B,N,H,D], q_norm_w, k_norm_w [H*D], proj_q, proj_kv [B,N,4,4], rope_cos, rope_sin
+ *   [N,D/2] fp32 IN (as given to cam_prep); dq_t, dk_t, dv_t [ndir,B,H,D,N] fp32 IN, ndir in
+ *   {1, 2}; dinfl [B,H,N] fp32 IN or NULL (no inflation gradient);
+ *   dq, dk, dv [B,N,H,D], dq_norm_w, dk_norm_w [H*D] fp32 OUT.  Tensors 16-byte aligned.
+ *   workspace  at least cam_prep_bwd_workspace_bytes(B, N, H, D) bytes, 256-byte aligned (k's
+ *   inverse RMS and the weight gradients' per-workgroup partial sums, added in a fixed order).
+ * Supported: D in {64, 128}, H*D <= 4096, N a multiple of 4.  GDN_ERR_INVALID for ndir outside
+ * {1, 2} or norm_eps <= 0.
+ */
+GDN_API size_t cam_prep_bwd_workspace_bytes(int B, int N, int H, int D);
+GDN_API int cam_prep_bwd(const float* q, const float* k, const float* q_norm_w,
+                         const float* k_norm_w, const float* proj_q, const float* proj_kv,
+                         const float* rope_cos, const float* rope_sin, float k_scale,
+                         float norm_eps, int ndir, const float* dq_t, const float* dk_t,
+                         const float* dv_t, const float* dinfl, float* dq, float* dk, float* dv,
                          float* dq_norm_w, float* dk_norm_w, int B, int N, int H, int D,
                          void* workspace, size_t workspace_bytes, void* stream);
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, "binding lacks %s" % n
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -369,4 +369,29 @@ def test_prep_bwd_validation_codes():
     n = lib.gdn_prep_bwd_workspace_bytes(1, 64, 2, 128)
     assert n >= 64 * 2 * 256 * 4                    # one partial pair per token group
     assert lib.gdn_prep_bwd_workspace_bytes(1, 1 << 20, 16, 128) >= 1024 * 2 * 2048 * 4
+    assert call(ws=ctypes.c_void_p(0x1000 + 16), wsn=n) == L.ERR_INVALID  # misaligned
+
+
+def test_cam_prep_bwd_validation_codes():
+    L, lib = _lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, dinfl=None, ndir=2, eps=1e-5, B=1, N=64, H=2, D=128, ws=None, wsn=0)
+        a.update(kw)
+        return lib.cam_prep_bwd(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.5, a["eps"],
+                                a["ndir"], FAKE, FAKE, FAKE, a["dinfl"], FAKE, FAKE, FAKE, FAKE,
+                                FAKE, a["B"], a["N"], a["H"], a["D"], a["ws"], a["wsn"], None)
+
+    assert call(q=None) == L.ERR_INVALID
+    assert call(ndir=0) == L.ERR_INVALID
+    assert call(ndir=3) == L.ERR_INVALID
+    assert call(eps=0.0) == L.ERR_INVALID
+    assert call(D=36) == L.ERR_INVALID            # D/2 not a multiple of 4
+    assert call(D=96) == L.ERR_UNSUPPORTED
+    assert call(N=66) == L.ERR_UNSUPPORTED        # N not a multiple of 4
+    assert call(H=64) == L.ERR_UNSUPPORTED        # H*D > 4096
+    assert call() == L.ERR_WORKSPACE
+    assert call(dinfl=FAKE) == L.ERR_WORKSPACE    # dinfl is optional
+    n = lib.cam_prep_bwd_workspace_bytes(1, 64, 2, 128)
+    assert n >= 64 * 4 + 64 * 2 * 256 * 4         # k inverse RMS + one partial pair per group
     assert call(ws=ctypes.c_void_p(0x1000 + 16), wsn=n) == L.ERR_INVALID  # misaligned

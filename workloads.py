@@ -200,6 +200,19 @@ def cam_inputs(B, F, S, H, D, seed=0, decay_shift=3.0, translate=0.3):
             "eps": 1e-5}
 
 
+def cam_prep_bwd_inputs(B, F, S, H, D, ndir=2, infl=True, seed=0):
+    """Inputs of the camera prep backward: cam_inputs, then (from seed + 7919) the gradients
+    of the prep's outputs dq_t, dk_t, dv_t [ndir,B,H,D,N] fp32 ~ N(0, 1) and of the inflation,
+    dinfl [B,H,N] ~ N(0, 1) (None without infl)."""
+    inp = cam_inputs(B, F, S, H, D, seed=seed)
+    gen = _gen(seed + 7919)
+    N = F * S
+    for n in ("dq_t", "dk_t", "dv_t"):
+        inp[n] = torch.randn(ndir, B, H, D, N, generator=gen)
+    inp["dinfl"] = torch.randn(B, H, N, generator=gen) if infl else None
+    return inp
+
+
 def cam_scan_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
     """Camera-scan inputs in the channel-major layout [B,H,D,N] fp32, with the magnitudes of
     prepped tensors: q, v ~ N(0, 1), k ~ N(0, k_scale^2) (k_scale = D^-1/2 * S^-1/2); beta
