@@ -18,8 +18,8 @@ from . import _lib
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_prep", "bigdn_fwd", "gdn_varlen_num_chunks",
            "gdn_state_summary", "gdn_state_apply", "bigdn_fwd_merged", "cam_prep", "cam_scan",
-           "cam_scan_bidi", "cam_scan_bwd", "cam_prep_bwd", "bigdn_dir_bwd", "bigdn_merge_bwd", "gdn_prep_bwd",
-           "bigdn_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
+           "cam_scan_bidi", "cam_scan_bwd", "cam_prep_bwd", "cam_bwd", "bigdn_dir_bwd",
+           "bigdn_merge_bwd", "gdn_prep_bwd", "bigdn_bwd", "gdn_bwd_prep", "gdn_bwd_dhu", "gdn_bwd_dhu_varlen",
            "gdn_state_grad_summary", "gdn_state_grad_apply", "gdn_abi_version",
            "gdn_last_error", "CHUNK"]
 
@@ -467,10 +467,13 @@ def cam_scan_bidi(q, k, v, beta, decay, *, decay_bwd=None, init_state=None,
     return (of, orv, fin) if save_final_state else (of, orv)
 
 
-def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False):
+def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False, *, accumulate=False, out=None):
     """Backward of cam_scan (one direction, no state in / out): gradients of sum(out * dout).
     q, k, v, dout [B,H,D,N] fp32; beta [B,H,F,S]; decay [B,H,F].  Returns a dict with dq,
-    dk, dv [B,H,D,N], dbeta [B,H,F,S] and ddecay [B,H,F] (fp32)."""
+    dk, dv [B,H,D,N], dbeta [B,H,F,S] and ddecay [B,H,F] (fp32).  out: a dict of those
+    tensors to write into (contiguous; e.g. one direction's slice of [2,B,H,D,N] tensors for
+    cam_prep_bwd); accumulate: add dbeta and ddecay to out's contents instead of writing
+    them."""
     B, H, D, N = q.shape
     F, S = beta.shape[2], beta.shape[3]
     dev = q.device
@@ -480,18 +483,65 @@ def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False):
     _need(decay, "decay", (B, H, F), torch.float32, dev)
     if F * S != N:
         raise ValueError("beta is [B,H,F,S] with F*S = %d, but N = %d" % (F * S, N))
-    out = {n: torch.empty(B, H, D, N, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
-    out["dbeta"] = torch.empty(B, H, F, S, dtype=torch.float32, device=dev)
-    out["ddecay"] = torch.empty(B, H, F, dtype=torch.float32, device=dev)
+    shapes = dict({n: (B, H, D, N) for n in ("dq", "dk", "dv")}, dbeta=(B, H, F, S),
+                  ddecay=(B, H, F))
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out (the dbeta and ddecay to add to)")
+        out = {n: torch.empty(*shp, dtype=torch.float32, device=dev) for n, shp in shapes.items()}
+    else:
+        for n, shp in shapes.items():
+            if n not in out or not isinstance(out[n], torch.Tensor):
+                raise ValueError("out[%r] must be a tensor" % n)
+            _need(out[n], n, shp, torch.float32, dev)
     lib = _lib.load()
     ws_n = lib.cam_scan_bwd_workspace_bytes(B, H, D, F)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    flag = int(bool(reverse)) | (_lib.BWD_ACCUMULATE if accumulate else 0)
     rc = lib.cam_scan_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), _ptr(dout),
-                          int(bool(reverse)), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                          flag, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                           _ptr(out["dbeta"]), _ptr(out["ddecay"]), B, H, D, F, S, _ptr(ws), ws_n,
                           _stream(dev))
     _lib.check(rc, "cam_scan_bwd")
     return out
+
+
+def cam_bwd(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, beta,
+            decay, dout_fwd, dout_rev, dinfl=None, norm_eps=1e-5, *, decay_bwd=None):
+    """Backward of the camera branch: cam_prep, then cam_scan_bidi's two outputs, from their
+    gradients dout_fwd, dout_rev [B,H,D,N] fp32 and (optionally) the inflation's, dinfl
+    [B,H,N].  Inputs as given to cam_prep and cam_scan_bidi (decay_bwd: the reverse
+    direction's decay).  The library calls, in order: cam_prep (the prepped tensors again),
+    cam_scan_bwd for the forward and the reverse direction into one [2,B,H,D,N] set of
+    gradients (the reverse call's dbeta added into the forward one's, and its ddecay too
+    unless decay_bwd is given), cam_prep_bwd over both directions.  Returns a dict with dq, dk, dv [B,N,H,D],
+    dq_norm_w, dk_norm_w [H*D], dbeta [B,H,F,S] (both directions), ddecay [B,H,F] (both
+    directions, or the forward one's with ddecay_bwd the reverse one's when decay_bwd is
+    given)."""
+    B, N, H, D = q.shape
+    F, S = beta.shape[2], beta.shape[3]
+    dev = q.device
+    qt, kt, vt, _ = cam_prep(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin,
+                             k_scale, norm_eps)
+    grads = {n: torch.empty(2, B, H, D, N, dtype=torch.float32, device=dev)
+             for n in ("dq", "dk", "dv")}
+    par = {"dbeta": torch.empty(B, H, F, S, dtype=torch.float32, device=dev),
+           "ddecay": torch.empty(B, H, F, dtype=torch.float32, device=dev)}
+    cam_scan_bwd(qt, kt, vt, beta, decay, dout_fwd, reverse=False,
+                 out=dict({n: grads[n][0] for n in grads}, **par))
+    # beta is shared by the two directions, so the reverse call always adds its dbeta; its
+    # ddecay goes to a zeroed array of its own when the reverse direction has its own decay
+    sep = decay_bwd is not None
+    ddecay_r = torch.zeros_like(par["ddecay"]) if sep else par["ddecay"]
+    cam_scan_bwd(qt, kt, vt, beta, decay if decay_bwd is None else decay_bwd, dout_rev,
+                 reverse=True, accumulate=True,
+                 out=dict({n: grads[n][1] for n in grads}, dbeta=par["dbeta"], ddecay=ddecay_r))
+    g = cam_prep_bwd(q, k, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale,
+                     grads["dq"], grads["dk"], grads["dv"], dinfl, norm_eps)
+    res = dict(g, dbeta=par["dbeta"], ddecay=par["ddecay"])
+    if sep:
+        res["ddecay_bwd"] = ddecay_r
+    return res
 
 
 def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, gk=None, want_dh=True,

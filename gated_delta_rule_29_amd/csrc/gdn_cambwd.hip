@@ -328,12 +328,13 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
   const int fa = p.reverse ? f + 1 : f;  // used only when absorb
   const long base = bh * D * N;
 
+  // p.acc: this direction's dbeta and ddecay are added to the arrays' contents
   if (blk == 0 && tid == 0) {
     if (absorb) {
       float s = 0.f;
       for (int cb = 0; cb < D / 32; ++cb) s += p.ddecay_part[((size_t)bh * F + fa) * (D / 32) + cb];
-      p.ddecay[bh * F + fa] = it > 0 ? s : 0.f;
-    } else {
+      p.ddecay[bh * F + fa] = (p.acc ? p.ddecay[bh * F + fa] : 0.f) + (it > 0 ? s : 0.f);
+    } else if (!p.acc) {
       p.ddecay[bh * F] = 0.f;  // frame 0 of the reverse scan is never absorbed
     }
   }
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
           p.dk[o] = 0.f;
           p.dv[o] = 0.f;
         }
-    if (tid < 64) p.dbeta[bh * N + s0 + tid] = 0.f;
+    if (tid < 64 && !p.acc) p.dbeta[bh * N + s0 + tid] = 0.f;
     return;
   }
   const long ta = (long)fa * p.S + s0;  // first token of this block in the absorbed frame
@@ -470,7 +471,9 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
     if (lq == 0) red[w][16 * c + li] = db[c];
   }
   __syncthreads();
-  if (tid < 64) p.dbeta[bh * N + ta + tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+  if (tid < 64)
+    p.dbeta[bh * N + ta + tid] = (p.acc ? p.dbeta[bh * N + ta + tid] : 0.f) +
+                                 ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
 
   // ---- dk = A (beta r) + g S_prev (-beta dd)
   f32x4 K1[RW][4];

@@ -204,6 +204,7 @@ struct CamBwdParams {
   const float* decay; // [B, H, F]
   const float* dout;  // [B, H, D, N]
   int reverse;
+  int acc;            // add dbeta and ddecay to the arrays' contents
   float* dq;          // [B, H, D, N]
   float* dk;
   float* dv;

@@ -406,7 +406,9 @@ GDN_API int cam_scan_bidi(const float* q, const float* k, const float* v, const 
  * gradients of L = sum(out * dout) for out = cam_scan(q, k, v, beta, decay, reverse)
  * (SANA fused_cam_gdn.py page, "Backward Triton kernel": _cam_scan_bwd_kernel, and its
  * per-iteration derivation).  The forward states are recomputed here, so the call needs only
- * the forward's inputs.
+ * the forward's inputs.  reverse | GDN_BWD_ACCUMULATE adds this direction's dbeta and ddecay
+ * to the arrays' contents instead of writing them (both directions of cam_scan_bidi share beta
+ * and, unless decay_bwd is given, decay); dq, dk, dv are always written.
  *   q, k, v, dout [B,H,D,N] fp32 channel-major, N = F*S; beta [B,H,F,S]; decay [B,H,F]
  *   dq, dk, dv    [B,H,D,N] fp32 OUT;  dbeta [B,H,F,S] fp32 OUT;  ddecay [B,H,F] fp32 OUT
  *   Tokens never absorbed (frame 0 of the reverse scan) get zero dk, dv, dbeta; a decay that

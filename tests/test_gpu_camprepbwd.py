@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_util import TOL, assert_close, say
+from tests.gpu_util import SPLIT_OPERAND_TOL, TOL, assert_close, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -74,3 +74,49 @@ def test_cam_prep_bwd_video_shape_and_determinism():
     b = _gpu(inp, 2)
     for name in a:
         assert torch.equal(a[name], b[name]), name
+
+
+def _branch(inp, dout_f, dout_r, decay_bwd=None):
+    import gated_delta_rule_29_amd as g
+
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    db = None if decay_bwd is None else decay_bwd.to(DEV)
+    out = g.cam_bwd(d["q"], d["k"], d["v"], *(d[k] for k in PARAMS), d["k_scale"], d["beta"],
+                    d["decay"], dout_f.to(DEV), dout_r.to(DEV), d["dinfl"], d["eps"],
+                    decay_bwd=db)
+    qt, kt, vt, _ = g.cam_prep(d["q"], d["k"], d["v"], *(d[k] for k in PARAMS), d["k_scale"],
+                               d["eps"])
+    torch.cuda.synchronize()
+    return out, (qt.cpu(), kt.cpu(), vt.cpu())
+
+
+@pytest.mark.parametrize("D,F,S,sep", [(64, 3, 64, False), (128, 2, 128, False),
+                                       (64, 4, 64, True)])
+def test_cam_branch_bwd(D, F, S, sep):
+    """The camera branch's backward (cam_bwd: cam_prep, both scan directions' backward with
+    the reverse call accumulating dbeta and ddecay, cam_prep_bwd over both directions) against
+    the oracle's pieces composed on the GPU path's fp32 prepped tensors.  The scan backward
+    takes split bf16 operands, so the split-operand rule applies."""
+    say("cam_bwd D%d F%d S%d decay_bwd %s" % (D, F, S, sep))
+    inp = workloads.cam_prep_bwd_inputs(1, F, S, 2, D, ndir=2, seed=D + F + int(sep))
+    dout_f, dout_r = inp["dq_t"][0], inp["dq_t"][1]  # any N(0, 1) [B,H,D,N] pair
+    decay_bwd = None
+    if sep:
+        decay_bwd = inp["decay"].clone() * 0.9
+        decay_bwd[:, :, 1::2] = 0.0
+    out, t = _branch(inp, dout_f, dout_r, decay_bwd)
+    fwd = oracle.cam_scan_bwd(*t, inp["beta"], inp["decay"], dout_f, reverse=False)
+    rev = oracle.cam_scan_bwd(*t, inp["beta"], inp["decay"] if decay_bwd is None else decay_bwd,
+                              dout_r, reverse=True)
+    ref = oracle.cam_prep_bwd(inp["q"], inp["k"], *(inp[k] for k in PARAMS), inp["k_scale"],
+                              fwd["dq"] + rev["dq"], fwd["dk"] + rev["dk"], fwd["dv"] + rev["dv"],
+                              inp["dinfl"], inp["eps"])
+    ref["dbeta"] = fwd["dbeta"] + rev["dbeta"]
+    if sep:
+        ref["ddecay"], ref["ddecay_bwd"] = fwd["ddecay"], rev["ddecay"]
+    else:
+        ref["ddecay"] = fwd["ddecay"] + rev["ddecay"]
+    assert set(out) == set(ref)
+    for name in ref:
+        assert bool(torch.isfinite(out[name]).all()), name
+        assert_close(name, out[name], ref[name], SPLIT_OPERAND_TOL)
