@@ -64,6 +64,7 @@ SOURCES = {
     "cam_bwd": ["gdn_cambwd.hip"],
     "bigdn_bwd": ["gdn_bigdnbwd.hip", "gdn_cambwd.hip"],
     "bigdn_block_bwd": ["gdn_bigdn.hip", "gdn_bigdnbwd.hip", "gdn_cambwd.hip", "gdn_prepbwd.hip"],
+    "cam_branch_bwd": ["gdn_cam.hip", "gdn_cambwd.hip", "gdn_prepbwd.hip"],
     "summary": ["gdn_fwd.hip", "gdn_fused16.hip", "gdn_summary.hip"],
     "dhu": ["gdn_bwd.hip"],
 }
@@ -131,6 +132,18 @@ def alg_bytes_bigdn_block_bwd(B, F, S, H, D):
     return (B * N * 3 * C * 2 + 2 * B * N * C * 2 + B * H * N * 2 + B * N * C * 4
             + B * H * N * 4 + B * H * F * 4 + 2 * N * D * 4 + 2 * C * 4
             + B * N * 3 * C * 4 + B * N * C * 4 + B * H * N * 4 + B * H * F * 4 + 2 * C * 4)
+
+
+def alg_bytes_cam_branch_bwd(B, F, S, H, D):
+    """Minimum HBM bytes of the camera branch's backward (fp32): read q, k, v, the camera
+    matrices, the half-width RoPE tables, norm weights, beta, decay, the two scan outputs'
+    gradients and the inflation's once; write dq, dk, dv, the norm weights' gradients, dbeta
+    and ddecay."""
+    N = F * S
+    C = H * D
+    return (3 * B * N * C * 4 + 2 * B * N * 16 * 4 + 2 * N * (D // 2) * 4 + 2 * C * 4
+            + B * H * N * 4 + B * H * F * 4 + 2 * B * N * C * 4 + B * H * N * 4
+            + 3 * B * N * C * 4 + 2 * C * 4 + B * H * N * 4 + B * H * F * 4)
 
 
 def alg_bytes_dhu(B, T, H, K, V, elt):
@@ -242,6 +255,32 @@ def cpu_baseline(kind, inp, max_chains=64):
                 oracle.cam_scan_bwd(**sub, reverse=rev)
         return _cpu_time(run, "both scan directions' backward on the first %d of %d frames, "
                          "all %d heads (%d tokens)" % (fs, F, H, n), 2 * B * n * H)
+    if kind == "cam_branch_bwd":
+        B, N, H, D = inp["q"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        fs = min(F, 4)
+        n = fs * S
+        sub = {k: oracle._f64(inp[k][:, :n]) for k in ("q", "k", "v", "proj_q", "proj_kv")}
+        sub.update({k: oracle._f64(inp[k][..., :n]) for k in ("dout_fwd", "dout_rev", "dinfl")})
+        sub.update(beta=oracle._f64(inp["beta"][:, :, :fs]),
+                   decay=oracle._f64(inp["decay"][:, :, :fs]),
+                   rope_cos=oracle._f64(inp["rope_cos"][:n]), rope_sin=oracle._f64(inp["rope_sin"][:n]))
+        pw = (oracle._f64(inp["q_norm_w"]), oracle._f64(inp["k_norm_w"]))
+        ks, eps = inp["k_scale"], inp["eps"]
+
+        def run():
+            qt, kt, vt, _ = oracle.cam_prep(sub["q"], sub["k"], sub["v"], *pw, sub["proj_q"],
+                                            sub["proj_kv"], sub["rope_cos"], sub["rope_sin"],
+                                            ks, eps)
+            d = [oracle.cam_scan_bwd(qt, kt, vt, sub["beta"], sub["decay"],
+                                     sub["dout_rev" if rev else "dout_fwd"], reverse=rev)
+                 for rev in (False, True)]
+            oracle.cam_prep_bwd(sub["q"], sub["k"], *pw, sub["proj_q"], sub["proj_kv"],
+                                sub["rope_cos"], sub["rope_sin"], ks,
+                                *(d[0][n] + d[1][n] for n in ("dq", "dk", "dv")), sub["dinfl"],
+                                eps)
+        return _cpu_time(run, "the branch's backward on the first %d of %d frames, all %d "
+                         "heads (%d tokens)" % (fs, F, H, n), B * n * H)
     if kind == "bigdn_bwd":
         B, H, N, D = inp["q_rot"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -490,6 +529,25 @@ def main():
             s = sets[i % len(sets)]
             return [gdn.cam_scan_bwd(s["q"], s["k"], s["v"], s["beta"], s["decay"], s["dout"],
                                      reverse=rev) for rev in (False, True)]
+    elif kind == "cam_branch_bwd":
+        B, N, H, D = inp["q"].shape
+        F, S = inp["beta"].shape[2], inp["beta"].shape[3]
+        dt = torch.float32
+        th = B * N * H
+        alg = alg_bytes_cam_branch_bwd(B, F, S, H, D)
+        kernel = ("cam_bwd: cam_prep, cam_scan_bwd x 2 directions, cam_prep_bwd (12 kernels, "
+                  "whole step)")
+        config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
+                  "state": "fp32", "products": "split bf16 (hi/lo) operands, fp32 accumulation",
+                  "step": "from the gradients of the two scan outputs and of the inflation to q, "
+                          "k, v, the norm weights, beta and decay"}
+        pre = ("q_norm_w", "k_norm_w", "proj_q", "proj_kv", "rope_cos", "rope_sin")
+
+        def step(i):
+            s = sets[i % len(sets)]
+            return gdn.cam_bwd(s["q"], s["k"], s["v"], *(s[k] for k in pre), s["k_scale"],
+                               s["beta"], s["decay"], s["dout_fwd"], s["dout_rev"], s["dinfl"],
+                               s["eps"])
     elif kind == "bigdn_bwd":
         B, H, N, D = inp["q_rot"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

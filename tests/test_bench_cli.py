@@ -23,4 +23,4 @@ def test_more_than_one_gpu_is_refused():
 def test_workload_recipes_are_known_kinds(name):
     assert workloads.WORKLOADS[name]["kind"] in ("gdn", "varlen", "bigdn", "bigdn_merged",
                                                  "summary", "cam", "dhu", "cam_bwd", "bigdn_bwd",
-                                                 "bigdn_block_bwd")
+                                                 "bigdn_block_bwd", "cam_branch_bwd")

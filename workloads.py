@@ -213,6 +213,19 @@ def cam_prep_bwd_inputs(B, F, S, H, D, ndir=2, infl=True, seed=0):
     return inp
 
 
+def cam_branch_bwd_inputs(B, F, S, H, D, seed=0):
+    """Inputs of the camera branch's backward: cam_inputs, then (from seed + 7919) the
+    gradients of the two scan outputs dout_fwd, dout_rev [B,H,D,N] and of the inflation, dinfl
+    [B,H,N], all fp32 ~ N(0, 1)."""
+    inp = cam_inputs(B, F, S, H, D, seed=seed)
+    gen = _gen(seed + 7919)
+    N = F * S
+    inp["dout_fwd"] = torch.randn(B, H, D, N, generator=gen)
+    inp["dout_rev"] = torch.randn(B, H, D, N, generator=gen)
+    inp["dinfl"] = torch.randn(B, H, N, generator=gen)
+    return inp
+
+
 def cam_scan_inputs(B, F, S, H, D, seed=0, decay_shift=3.0):
     """Camera-scan inputs in the channel-major layout [B,H,D,N] fp32, with the magnitudes of
     prepped tensors: q, v ~ N(0, 1), k ~ N(0, k_scale^2) (k_scale = D^-1/2 * S^-1/2); beta
@@ -291,6 +304,10 @@ WORKLOADS = {
     # gated output to qkv, the norm weights, beta, decay and the gate
     "bigdn_block_bwd_video_f16x1024": dict(kind="bigdn_block_bwd", B=1, F=16, S=1024, H=16, D=128,
                                            seed=0),
+    # backward of the camera branch at the same shape: from the gradients of the two scan
+    # outputs and of the inflation to q, k, v, the norm weights, beta and decay
+    "cam_branch_bwd_video_f16x1024": dict(kind="cam_branch_bwd", B=1, F=16, S=1024, H=16,
+                                          D=128, seed=0),
     "long_perkey_b2h32t32768": dict(kind="gdn", B=2, T=32768, H=32, K=128, V=128,
                                     dtype="bf16", seed=0, g_shift=3.0, per_key=True,
                                     save=True),
@@ -330,4 +347,6 @@ def make(name):
         return bigdn_bwd_inputs(**w)
     if kind == "bigdn_block_bwd":
         return bigdn_block_bwd_inputs(**w)
+    if kind == "cam_branch_bwd":
+        return cam_branch_bwd_inputs(**w)
     raise KeyError(name)
