@@ -644,9 +644,9 @@ int cam_scan_bwd(const float* q, const float* k, const float* v, const float* be
   reverse &= 1;
   if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
   if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
-  if ((int64_t)F * S > INT32_MAX || (int64_t)B * H * F * 3 > INT32_MAX ||
+  if ((int64_t)D * F * S > (int64_t(1) << 29) || (int64_t)B * H * F * 3 > INT32_MAX ||
       (int64_t)B * H * F * (S / 64) > INT32_MAX)
-    return fail(GDN_ERR_INVALID, "F*S or B*H*F exceeds the grid limit");
+    return fail(GDN_ERR_INVALID, "D*F*S (a head's slab) or B*H*F exceeds the kernel limits");
   const size_t need = cam_scan_bwd_workspace_bytes(B, H, D, F);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, workspace_bytes);

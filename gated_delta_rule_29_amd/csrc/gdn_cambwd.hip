@@ -25,15 +25,17 @@
 //          fp32 matrix products, the state in LDS); every step's state and A leave as hi/lo
 //          bf16 pairs in both orientations for the token kernel, the states also in fp32 for
 //          the decay gradient, whose partial sums over the block's columns go to the workspace.
-//   token  per (b, h, step, 64 tokens): the five products of the per-token gradients, the
-//          token slabs transposed into LDS tiles that the four waves share; wave w forms
-//          output rows D/4 w .. D/4 (w+1) - 1 for all 64 tokens.
+//   token  per (b, h, step) (or a part of the step's token blocks when there are few steps):
+//          the five products of the per-token gradients; each of the D/16 waves keeps its 16
+//          rows of the step's matrices in registers and forms those output rows for every
+//          64-token block, whose token slabs are transposed into LDS tiles the waves share.
 // Precision: each product splits both fp32 operands into bf16 pairs x = hi + lo (hi = bf16(x),
 // lo = bf16(x - hi)) and sums hi*hi + hi*lo + lo*hi in fp32, about 16 mantissa bits per
 // operand.  The page's backward takes plain bf16 operands; their rounding alone moves the
 // gradients by up to 4e-2 of their RMS on the small test shapes.
 #include "gdn_bwd_params.h"
 #include "gdn_device.h"
+#include "gdn_dma.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -303,33 +305,46 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 }
 
 // ---- token gradients ---------------------------------------------------------------------
-// blockIdx.x = (bh * F + it) * (S / 64) + token block: tokens 64 block .. + 63 of the frames of
-// step it.  Two LDS tiles, each a hi/lo pair of bf16 [token][D], hold the token operands;
-// wave w forms output rows 16 RW w .. 16 RW (w + 1) - 1.
+// One workgroup of D/16 waves per (b, h, step, part of the frame's 64-token blocks); wave w
+// owns output rows 16 w .. 16 w + 15 and keeps its rows of the step's D x D matrices (hi/lo
+// A-operand fragments) in registers for all of its token blocks, so each matrix is read once
+// per workgroup: S in a first pass over the blocks (dq), then S_prev^T, A^T, A and S_prev in a
+// second (dv, dbeta, dk; all five at once would not fit the register file).  A block's
+// channel-major slabs (dout in the first pass; k and v in the second) arrive in LDS as raw fp32
+// rows by direct buffer-to-LDS loads issued one block ahead, under the current block's
+// products; at the block's start they are split into hi/lo bf16 [token][D] tiles.  Two tiles:
+// dout (or k), then beta r and -beta dd.
 template <int D>
-__global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
-  constexpr int RW = D / 64;   // 16-row output tiles per wave
-  constexpr int kT = D + 8;    // LDS row stride of a [token][D] tile (elements)
+__global__ __launch_bounds__(D * 4) void cbwd_tok_kernel(const CamBwdParams p, int nsplit) {
+  constexpr int NW = D / 16, KK = D / 32;  // waves (16 output rows each), contraction steps
+  constexpr int kT = D + 8;                // LDS row stride of a [token][D] tile (elements)
+  constexpr int kR = 64;                   // LDS row stride of a raw [D][64] fp32 slab (floats)
   __shared__ __attribute__((aligned(16))) bf16 tl[2][2][64 * kT];  // [tile][hi, lo]
-  __shared__ float red[4][64];
+  __shared__ __attribute__((aligned(16))) float raw[2][D * kR];    // k (or dout), v
+  __shared__ float red[NW][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
   const int nblk = p.S / 64;
   const int bid = xcd_logical(blockIdx.x, gridDim.x);
-  const int blk = bid % nblk;
-  const long sb = bid / nblk;
+  const int part = bid % nsplit;
+  const long sb = bid / nsplit;
   const int F = p.F;
   const int it = (int)(sb % F);
   const long bh = sb / F;
   const long N = (long)F * p.S;
+  const int Ni = (int)N;
   const size_t DD = (size_t)D * D;
-  const int s0 = 64 * blk;  // first token of this block inside its frame
+  const int b0 = part * nblk / nsplit, b1 = (part + 1) * nblk / nsplit;
   const int f = p.reverse ? F - 1 - it : it;
   const bool absorb = !(p.reverse && it == 0);
   const int fa = p.reverse ? f + 1 : f;  // used only when absorb
   const long base = bh * D * N;
+  // this head's [D][N] slabs; element offsets within a slab fit 32 bits (D N < 2^29)
+  float* const dqh = p.dq + base;
+  float* const dkh = p.dk + base;
+  float* const dvh = p.dv + base;
 
   // p.acc: this direction's dbeta and ddecay are added to the arrays' contents
-  if (blk == 0 && tid == 0) {
+  if (part == 0 && tid == 0) {
     if (absorb) {
       float s = 0.f;
       for (int cb = 0; cb < D / 32; ++cb) s += p.ddecay_part[((size_t)bh * F + fa) * (D / 32) + cb];
@@ -339,38 +354,52 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
     }
   }
 
-  // x[:, t0 .. t0 + 63] (channel-major, [D][N] per head) into tile T as a bf16 [token][D] pair
-  auto stage = [&](const float* x, long t0, int T) {
-    const int t = tid & 63, cg = tid >> 6;
-    bf16* H = tl[T][0];
-    bf16* L = tl[T][1];
-#pragma unroll 4
-    for (int c = 2 * cg; c < D; c += 8) {
-      bf16x2 h, l;
-      GDN_SPLIT(x[base + (long)c * N + t0 + t], h[0], l[0]);
-      GDN_SPLIT(x[base + (long)(c + 1) * N + t0 + t], h[1], l[1]);
-      *reinterpret_cast<bf16x2*>(&H[t * kT + c]) = h;
-      *reinterpret_cast<bf16x2*>(&L[t * kT + c]) = l;
+  // this wave's rows of a matrix pair (row-major hi, then lo p.lo elements later)
+  typedef bf16x8 Frag[KK][2];
+  auto load_a = [&](const bf16* M, Frag& a) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const size_t ro = (size_t)(16 * w + li) * D + 32 * kk + 8 * lq;
+      a[kk][0] = *reinterpret_cast<const bf16x8*>(M + ro);
+      a[kk][1] = *reinterpret_cast<const bf16x8*>(M + p.lo + ro);
     }
   };
-  // four consecutive rows i0 .. i0 + 3 of token t into tile T
-  auto put = [&](int T, int t, int i0, const float (&x)[4]) {
-    bf16x4 h, l;
+  const bool prev = it > 0;  // a state before this step exists (else S_prev = 0)
+  const float g = absorb ? p.decay[bh * F + fa] : 0.f;
+
+  // tokens t0 .. t0 + 63 of every channel row of a [D][N] slab into raw slab R (fp32 [D][64],
+  // rows contiguous): an instruction moves four rows (16 lanes of 16 bytes each), wave w the
+  // rows 4 w + 4 NW i .. + 3
+  auto fetch = [&](const float* x, int t0, int R) {
+    const dma::i32x4 rs = dma::make_rsrc(x + base + t0, (uint32_t)(((D - 1) * N + 64) * 4));
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, as a scalar
 #pragma unroll
-    for (int e = 0; e < 4; ++e) GDN_SPLIT(x[e], h[e], l[e]);
-    *reinterpret_cast<bf16x4*>(&tl[T][0][t * kT + i0]) = h;
-    *reinterpret_cast<bf16x4*>(&tl[T][1][t * kT + i0]) = l;
+    for (int i = 0; i < D / (4 * NW); ++i) {
+      const int c0 = 4 * wu + 4 * NW * i;
+      dma::dma16(rs, (uint32_t)(((c0 + (lane >> 4)) * Ni + 4 * (lane & 15)) * 4), 0,
+                 dma::lds_addr(&raw[R][c0 * kR]));
+    }
   };
-  // C[i][t] = sum_k M[i][k] X[t][k]: M a D x D row-major hi/lo matrix pair in memory (A operand
-  // rows read straight from it), X tile T; C tile (r, c): row 16 (RW w + r) + 4 lq + e, token
-  // 16 c + li
-  auto prod = [&](const bf16* M, int T, f32x4 (&C)[RW][4]) {
+  // raw slab R into tile T as hi/lo bf16 [token][D]
+  auto split = [&](int R, int T) {
+    const int t = tid & 63, cg = tid >> 6;
+#pragma unroll 4
+    for (int c = 2 * cg; c < D; c += 2 * NW) {
+      bf16x2 h, l;
+      GDN_SPLIT(raw[R][c * kR + t], h[0], l[0]);
+      GDN_SPLIT(raw[R][(c + 1) * kR + t], h[1], l[1]);
+      *reinterpret_cast<bf16x2*>(&tl[T][0][t * kT + c]) = h;
+      *reinterpret_cast<bf16x2*>(&tl[T][1][t * kT + c]) = l;
+    }
+  };
+  // C[c] (rows 16 w + 4 lq + e, tokens 16 c + li) = M X^T for the wave's fragments of M and
+  // tile T, one contraction step's operand reads at a time (the scheduling barrier keeps the
+  // compiler from hoisting every step's reads beside the fragments)
+  auto prod = [&](const Frag& a, int T, f32x4 (&C)[4]) {
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int c = 0; c < 4; ++c) C[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) C[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       bf16x8 bh[4], bl[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -378,120 +407,141 @@ __global__ __launch_bounds__(256) void cbwd_tok_kernel(const CamBwdParams p) {
         bl[c] = lds8(&tl[T][1][(16 * c + li) * kT + 32 * kk + 8 * lq]);
       }
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        const size_t ro = (size_t)(16 * (RW * w + r) + li) * D + 32 * kk + 8 * lq;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(M + ro);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(M + p.lo + ro);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) C[r][c] = mma3(ah, al, bh[c], bl[c], C[r][c]);
-      }
+      for (int c = 0; c < 4; ++c) C[c] = mma3(a[kk][0], a[kk][1], bh[c], bl[c], C[c]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto row_of = [&](int r, int e) { return 16 * (RW * w + r) + 4 * lq + e; };
-
-  // ---- dq of the output frame's tokens: dq = S dout
-  stage(p.dout, (long)f * p.S + s0, 0);
-  __syncthreads();
-  {
-    f32x4 C[RW][4];
-    prod(p.Sp + ((size_t)bh * F + it) * DD, 0, C);
+  // four consecutive rows i0 .. i0 + 3 of token t into tile T
+  auto put = [&](int T, int t, int i0, const f32x4& x) {
+    bf16x4 h, l;
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int e = 0; e < 4; ++e) GDN_SPLIT(x[e], h[e], l[e]);
+    *reinterpret_cast<bf16x4*>(&tl[T][0][t * kT + i0]) = h;
+    *reinterpret_cast<bf16x4*>(&tl[T][1][t * kT + i0]) = l;
+  };
+  const int r0 = 16 * w + 4 * lq;  // first output row of this lane
+
+  // ---- pass 1, dq of the output frame's tokens: dq = S dout (S's fragments only)
+  if (b0 < b1) fetch(p.dout, f * p.S + 64 * b0, 0);
+  {
+    Frag aS;
+    load_a(p.Sp + ((size_t)bh * F + it) * DD, aS);
+    for (int blk = b0; blk < b1; ++blk) {
+      const int s0 = 64 * blk;  // first token of this block inside its frame
+      dma::wait_vm0();          // this wave's slab rows have arrived
+      __syncthreads();          // everyone's have, and the previous block is done with tile 0
+      split(0, 0);
+      __syncthreads();
+      if (blk + 1 < b1) fetch(p.dout, f * p.S + s0 + 64, 0);
+      else if (absorb) {        // the second pass's first block
+        fetch(p.k, fa * p.S + 64 * b0, 0);
+        fetch(p.v, fa * p.S + 64 * b0, 1);
+      }
+      f32x4 C[4];
+      prod(aS, 0, C);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p.dq[base + (long)row_of(r, e) * N + (long)f * p.S + s0 + 16 * c + li] = C[r][c][e];
+        for (int e = 0; e < 4; ++e) dqh[(r0 + e) * Ni + f * p.S + s0 + 16 * c + li] = C[c][e];
+    }
   }
   if (!absorb) {
     // frame 0 of the reverse scan: its tokens are never absorbed
-#pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int blk = b0; blk < b1; ++blk) {
+      const int s0 = 64 * blk;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const long o = base + (long)row_of(r, e) * N + s0 + 16 * c + li;
-          p.dk[o] = 0.f;
-          p.dv[o] = 0.f;
+          const int o = (r0 + e) * Ni + s0 + 16 * c + li;
+          dkh[o] = 0.f;
+          dvh[o] = 0.f;
         }
-    if (tid < 64 && !p.acc) p.dbeta[bh * N + s0 + tid] = 0.f;
+      if (tid < 64 && !p.acc) p.dbeta[bh * N + s0 + tid] = 0.f;
+    }
     return;
   }
-  const long ta = (long)fa * p.S + s0;  // first token of this block in the absorbed frame
-  const float g = p.decay[bh * F + fa];
-  float bcol[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) bcol[c] = p.beta[bh * N + ta + 16 * c + li];
-  __syncthreads();  // every wave is done with the dout tile
-  stage(p.k, ta, 0);
-  __syncthreads();
-
-  // ---- P = S_prev^T K (S_pre = g S_prev) and dd = A^T K
-  f32x4 P[RW][4], Dd[RW][4];
-  if (it > 0) {
-    prod(p.SpT + ((size_t)bh * F + it - 1) * DD, 0, P);
-  } else {
-#pragma unroll
-    for (int r = 0; r < RW; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) P[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- pass 2, the absorbed frame's tokens (the other four matrices' fragments)
+  Frag aPT, aDT, aA, aSP;
+  load_a(p.AbT + ((size_t)bh * F + it) * DD, aDT);
+  load_a(p.Ab + ((size_t)bh * F + it) * DD, aA);
+  if (prev) {
+    load_a(p.SpT + ((size_t)bh * F + it - 1) * DD, aPT);
+    load_a(p.Sp + ((size_t)bh * F + it - 1) * DD, aSP);
   }
-  prod(p.AbT + ((size_t)bh * F + it) * DD, 0, Dd);
-  // r = v - g P, dv = beta dd, dbeta = dd . r; the next products take beta r and -beta dd
-  float db[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int blk = b0; blk < b1; ++blk) {
+    const int s0 = 64 * blk;
+    const int ta = fa * p.S + s0;  // first token of this block in the absorbed frame
+    dma::wait_vm0();
+    __syncthreads();  // the k and v rows are in; the previous block is done with both tiles
+    split(0, 1);
+    __syncthreads();
+    if (blk + 1 < b1) fetch(p.k, ta + 64, 0);
+    // P = S_prev^T K (S_pre = g S_prev) and dd = A^T K; r = v - g P, dv = beta dd,
+    // dbeta = dd . r; the next products take beta r and -beta dd
+    float bcol[4];
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
+    for (int c = 0; c < 4; ++c) bcol[c] = p.beta[bh * N + ta + 16 * c + li];
+    f32x4 P[4], Dd[4];
+    if (prev) {
+      prod(aPT, 1, P);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) P[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    prod(aDT, 1, Dd);
+    float db[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const long o = base + (long)row_of(r, e) * N + ta + 16 * c + li;
-        const float rr = p.v[o] - g * P[r][c][e];
-        const float dd = Dd[r][c][e];
-        p.dv[o] = bcol[c] * dd;
+        const float rr = raw[1][(r0 + e) * kR + 16 * c + li] - g * P[c][e];
+        const float dd = Dd[c][e];
+        dvh[(r0 + e) * Ni + ta + 16 * c + li] = bcol[c] * dd;
         db[c] += dd * rr;
-        P[r][c][e] = bcol[c] * rr;
-        Dd[r][c][e] = -bcol[c] * dd;
+        P[c][e] = bcol[c] * rr;
+        Dd[c][e] = -bcol[c] * dd;
       }
-  __syncthreads();  // every wave is done with the k tile
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
+    __syncthreads();  // every wave is done with the k tile and the v rows
+    if (blk + 1 < b1) fetch(p.v, ta + 64, 1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float xr[4] = {P[r][c][0], P[r][c][1], P[r][c][2], P[r][c][3]};
-      const float xd[4] = {Dd[r][c][0], Dd[r][c][1], Dd[r][c][2], Dd[r][c][3]};
-      put(1, 16 * c + li, row_of(r, 0), xr);
-      put(0, 16 * c + li, row_of(r, 0), xd);
+      put(1, 16 * c + li, r0, P[c]);
+      put(0, 16 * c + li, r0, Dd[c]);
     }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    db[c] += __shfl_xor(db[c], 16, 64);
-    db[c] += __shfl_xor(db[c], 32, 64);
-    if (lq == 0) red[w][16 * c + li] = db[c];
-  }
-  __syncthreads();
-  if (tid < 64)
-    p.dbeta[bh * N + ta + tid] = (p.acc ? p.dbeta[bh * N + ta + tid] : 0.f) +
-                                 ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
-
-  // ---- dk = A (beta r) + g S_prev (-beta dd)
-  f32x4 K1[RW][4];
-  prod(p.Ab + ((size_t)bh * F + it) * DD, 1, K1);
-  if (it > 0) {
-    f32x4 K2[RW][4];
-    prod(p.Sp + ((size_t)bh * F + it - 1) * DD, 0, K2);
+    for (int c = 0; c < 4; ++c) {
+      db[c] += __shfl_xor(db[c], 16, 64);
+      db[c] += __shfl_xor(db[c], 32, 64);
+      if (lq == 0) red[w][16 * c + li] = db[c];
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+      for (int i = 0; i < NW; ++i) sum += red[i][tid];
+      p.dbeta[bh * N + ta + tid] = (p.acc ? p.dbeta[bh * N + ta + tid] : 0.f) + sum;
+    }
+    // dk = A (beta r) + g S_prev (-beta dd)
+    f32x4 K1[4];
+    prod(aA, 1, K1);
+    if (prev) {
+      f32x4 K2[4];
+      prod(aSP, 0, K2);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) K1[r][c] = K1[r][c] + g * K2[r][c];
-  }
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
+      for (int c = 0; c < 4; ++c) K1[c] = K1[c] + g * K2[c];
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p.dk[base + (long)row_of(r, e) * N + ta + 16 * c + li] = K1[r][c][e];
+      for (int e = 0; e < 4; ++e) dkh[(r0 + e) * Ni + ta + 16 * c + li] = K1[c][e];
+  }
+}
+
+// Workgroups per (b, h, step) for the token kernel: enough for about one per CU in total.
+inline int tok_split(long bhf, int nblk) {
+  long s = (256 + bhf - 1) / bhf;
+  return (int)(s < 1 ? 1 : s > nblk ? nblk : s);
 }
 
 template <int D>
@@ -499,7 +549,8 @@ hipError_t launch_d(const CamBwdParams& p, hipStream_t stream) {
   const long bh = (long)p.B * p.H;
   hipLaunchKernelGGL((cbwd_stats_kernel<D>), dim3(bh * p.F * 3), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((cbwd_scan_kernel<D>), dim3(bh * (D / 32)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((cbwd_tok_kernel<D>), dim3(bh * p.F * (p.S / 64)), dim3(256), 0, stream, p);
+  const int ns = tok_split(bh * p.F, p.S / 64);
+  hipLaunchKernelGGL((cbwd_tok_kernel<D>), dim3(bh * p.F * ns), dim3(D * 4), 0, stream, p, ns);
   return hipGetLastError();
 }
 
