@@ -271,34 +271,42 @@ __global__ __launch_bounds__(1024) void bbwd_zscan_kernel(const BigdnBwdParams p
 }
 
 // ---- S stream token gradients ---------------------------------------------------------------
-// As cbwd_tok_kernel (gdn_cambwd.hip) with token-major operands: blockIdx.x = (bh * F + it) *
-// (S / 64) + token block; two LDS tiles, each a hi/lo pair of bf16 [token][D]; wave w forms
-// output rows (channels) 16 RW w .. 16 RW (w + 1) - 1 for the 64 tokens.
+// As cbwd_tok_kernel (gdn_cambwd.hip) with token-major operands: one workgroup of D/16 waves per
+// (b, h, step, part of the frame's 64-token blocks); wave w owns output channels 16 w .. 16 w + 15
+// and keeps its rows of the step's D x D matrices as register fragments, S in a first pass
+// (dq_rot), S_prev^T, A^T, A and S_prev in a second (dv, dbeta, dk_rot).  A block's token rows
+// (dnum in the first pass; k_rot and v in the second) arrive in LDS by direct buffer-to-LDS
+// loads issued one block ahead; dnum is then split into a hi/lo tile, k_rot copied into the hi
+// half of a tile (bf16 values are exact, so the products against it take two terms).
 template <int D>
-__global__ __launch_bounds__(256) void bbwd_tok_kernel(const BigdnBwdParams p) {
-  constexpr int RW = D / 64;
-  constexpr int kT = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16 tl[2][2][64 * kT];
-  __shared__ float red[4][64];
+__global__ __launch_bounds__(D * 4) void bbwd_tok_kernel(const BigdnBwdParams p, int nsplit) {
+  constexpr int NW = D / 16, NT = NW * 64, KK = D / 32;
+  constexpr int kT = D + 8;  // LDS row stride of a [token][D] tile (elements)
+  __shared__ __attribute__((aligned(16))) bf16 tl[2][2][64 * kT];  // [tile][hi, lo]
+  // raw token rows: dnum fp32 [64][D] in the first pass; k_rot and v bf16 [64][D] in the second
+  __shared__ __attribute__((aligned(16))) float raw[64 * D];
+  __shared__ float red[NW][64];
+  bf16* const rawk = reinterpret_cast<bf16*>(raw);
+  bf16* const rawv = rawk + 64 * D;
   const CamBwdParams& c = p.cam;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
   const int nblk = c.S / 64;
   const int bid = xcd_logical(blockIdx.x, gridDim.x);
-  const int blk = bid % nblk;
-  const long sb = bid / nblk;
+  const int part = bid % nsplit;
+  const long sb = bid / nsplit;
   const int F = c.F;
   const int it = (int)(sb % F);
   const long bh = sb / F;
   const int b = (int)(bh / c.H), h = (int)(bh % c.H);
   const long N = (long)F * c.S;
   const size_t DD = (size_t)D * D;
-  const int s0 = 64 * blk;
+  const int b0 = part * nblk / nsplit, b1 = (part + 1) * nblk / nsplit;
   const int f = c.reverse ? F - 1 - it : it;
   const bool absorb = !(c.reverse && it == 0);
   const int fa = c.reverse ? f + 1 : f;  // used only when absorb
 
   // p.acc: this direction's dbeta and ddecay are added to the arrays' contents
-  if (blk == 0 && tid == 0) {
+  if (part == 0 && tid == 0) {
     if (absorb) {
       float s = p.ddz[bh * F + fa];
       for (int cb = 0; cb < D / 32; ++cb) s += c.ddecay_part[((size_t)bh * F + fa) * (D / 32) + cb];
@@ -307,163 +315,225 @@ __global__ __launch_bounds__(256) void bbwd_tok_kernel(const BigdnBwdParams p) {
       c.ddecay[bh * F] = 0.f;
     }
   }
-  // 64 token rows from t0 (token-major, row stride rs elements) into tile T as a split pair
-  auto stage16 = [&](const __bf16* x, long t0, int T) {
-    for (int e = tid; e < 64 * D / 8; e += 256) {
-      const int t = e / (D / 8), d = 8 * (e % (D / 8));
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + (bh * N + t0 + t) * D + d);
-      *reinterpret_cast<bf16x8*>(&tl[T][0][t * kT + d]) = v;
-      *reinterpret_cast<bf16x8*>(&tl[T][1][t * kT + d]) = bf16x8{};
+
+  typedef bf16x8 Frag[KK][2];
+  auto load_a = [&](const bf16* M, Frag& a) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const size_t ro = (size_t)(16 * w + li) * D + 32 * kk + 8 * lq;
+      a[kk][0] = *reinterpret_cast<const bf16x8*>(M + ro);
+      a[kk][1] = *reinterpret_cast<const bf16x8*>(M + c.lo + ro);
     }
   };
-  auto stage_dnum = [&](long t0, int T) {
-    for (int e = tid; e < 64 * D / 8; e += 256) {
+  const bool prev = it > 0;
+  const float g = absorb ? c.decay[bh * F + fa] : 0.f;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, as a scalar
+
+  // dnum rows of tokens t0 .. t0 + 63 ([B,N,H,D]: token stride H D) into raw as fp32 [64][D]:
+  // an instruction moves 1 KB (256 / D rows, 16 bytes per lane), wave w instructions w, w + NW ..
+  auto fetch_dnum = [&](long t0) {
+    constexpr int RPI = 256 / D;  // rows per instruction
+    const float* src = p.dnum + (((long)b * N + t0) * c.H + h) * D;
+    const dma::i32x4 rs = dma::make_rsrc(src, (uint32_t)((63 * (long)c.H * D + D) * 4));
+#pragma unroll
+    for (int i = 0; i < D / (4 * NW); ++i) {
+      const int ins = wu + NW * i;
+      const int row = RPI * ins + lane / (D / 4), piece = lane % (D / 4);
+      dma::dma16(rs, (uint32_t)((row * c.H * D + 4 * piece) * 4), 0, dma::lds_addr(raw + 1024 / 4 * ins));
+    }
+  };
+  // k_rot or v rows of tokens t0 .. t0 + 63 ([B,H,N,D] bf16, contiguous) into dst [64][D]
+  auto fetch_rows = [&](const __bf16* x, long t0, bf16* dst) {
+    const dma::i32x4 rs = dma::make_rsrc(x + (bh * N + t0) * D, 64 * D * 2);
+#pragma unroll
+    for (int i = 0; i < D / (8 * NW); ++i) {
+      const int ins = wu + NW * i;
+      dma::dma16(rs, (uint32_t)(1024 * ins + 16 * lane), 0, dma::lds_addr(dst + 512 * ins));
+    }
+  };
+  // raw dnum into tile 0 as a hi/lo pair; raw k_rot into tile 1's hi half
+  auto split_dnum = [&]() {
+#pragma unroll
+    for (int e = tid; e < 64 * D / 8; e += NT) {
       const int t = e / (D / 8), d = 8 * (e % (D / 8));
-      const float* src = p.dnum + (((long)b * N + t0 + t) * c.H + h) * D + d;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src), x1 = *reinterpret_cast<const f32x4*>(src + 4);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(raw + t * D + d);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(raw + t * D + d + 4);
       bf16x8 xh, xl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         GDN_SPLIT(x0[j], xh[j], xl[j]);
         GDN_SPLIT(x1[j], xh[4 + j], xl[4 + j]);
       }
-      *reinterpret_cast<bf16x8*>(&tl[T][0][t * kT + d]) = xh;
-      *reinterpret_cast<bf16x8*>(&tl[T][1][t * kT + d]) = xl;
+      *reinterpret_cast<bf16x8*>(&tl[0][0][t * kT + d]) = xh;
+      *reinterpret_cast<bf16x8*>(&tl[0][1][t * kT + d]) = xl;
     }
   };
-  auto put = [&](int T, int t, int i0, const float (&x)[4]) {
+  auto copy_k = [&]() {
+#pragma unroll
+    for (int e = tid; e < 64 * D / 8; e += NT) {
+      const int t = e / (D / 8), d = 8 * (e % (D / 8));
+      *reinterpret_cast<bf16x8*>(&tl[1][0][t * kT + d]) = *reinterpret_cast<const bf16x8*>(rawk + t * D + d);
+    }
+  };
+  // C[cc] (channels 16 w + 4 lq + e, tokens 16 cc + li) = M X^T for the wave's fragments and
+  // tile T; LO: the tile's lo half is used (else the tile holds exact bf16 values)
+  auto prod = [&](const Frag& a, int T, bool LO, f32x4 (&C)[4]) {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) C[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 bh_[4], bl[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        bh_[cc] = lds8(&tl[T][0][(16 * cc + li) * kT + 32 * kk + 8 * lq]);
+        if (LO) bl[cc] = lds8(&tl[T][1][(16 * cc + li) * kT + 32 * kk + 8 * lq]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        if (LO) {
+          C[cc] = mma3(a[kk][0], a[kk][1], bh_[cc], bl[cc], C[cc]);
+        } else {
+          C[cc] = mma16(a[kk][0], bh_[cc], C[cc]);
+          C[cc] = mma16(a[kk][1], bh_[cc], C[cc]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto put = [&](int T, int t, int i0, const f32x4& x) {
     bf16x4 xh, xl;
 #pragma unroll
     for (int e = 0; e < 4; ++e) GDN_SPLIT(x[e], xh[e], xl[e]);
     *reinterpret_cast<bf16x4*>(&tl[T][0][t * kT + i0]) = xh;
     *reinterpret_cast<bf16x4*>(&tl[T][1][t * kT + i0]) = xl;
   };
-  auto prod = [&](const bf16* M, int T, f32x4 (&C)[RW][4]) {
-#pragma unroll
-    for (int r = 0; r < RW; ++r)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) C[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      bf16x8 bh_[4], bl[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        bh_[cc] = lds8(&tl[T][0][(16 * cc + li) * kT + 32 * kk + 8 * lq]);
-        bl[cc] = lds8(&tl[T][1][(16 * cc + li) * kT + 32 * kk + 8 * lq]);
-      }
-#pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        const size_t ro = (size_t)(16 * (RW * w + r) + li) * D + 32 * kk + 8 * lq;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(M + ro);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(M + c.lo + ro);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) C[r][cc] = mma3(ah, al, bh_[cc], bl[cc], C[r][cc]);
-      }
-    }
-  };
-  auto ch0 = [&](int r) { return 16 * (RW * w + r) + 4 * lq; };  // first of a lane's 4 channels
-  auto store4 = [&](float* out, long t, int r, const f32x4& x) {
-    *reinterpret_cast<f32x4*>(out + (bh * N + t) * D + ch0(r)) = x;
+  const int ch0 = 16 * w + 4 * lq;  // first of a lane's four channels
+  auto store4 = [&](float* out, long t, const f32x4& x) {
+    *reinterpret_cast<f32x4*>(out + (bh * N + t) * D + ch0) = x;
   };
 
-  // ---- dq_rot = S dnum for the output frame's tokens
-  stage_dnum((long)f * c.S + s0, 0);
-  __syncthreads();
+  // ---- pass 1, dq_rot = S dnum for the output frame's tokens
+  fetch_dnum((long)f * c.S + 64 * b0);
   {
-    f32x4 C[RW][4];
-    prod(c.Sp + ((size_t)bh * F + it) * DD, 0, C);
+    Frag aS;
+    load_a(c.Sp + ((size_t)bh * F + it) * DD, aS);
+    for (int blk = b0; blk < b1; ++blk) {
+      const int s0 = 64 * blk;
+      dma::wait_vm0();
+      __syncthreads();  // the rows are in; the previous block is done with tile 0
+      split_dnum();
+      __syncthreads();
+      if (blk + 1 < b1) {
+        fetch_dnum((long)f * c.S + s0 + 64);
+      } else if (absorb) {  // the second pass's first block
+        fetch_rows(p.k_rot, (long)fa * c.S + 64 * b0, rawk);
+        fetch_rows(p.v, (long)fa * c.S + 64 * b0, rawv);
+      }
+      f32x4 C[4];
+      prod(aS, 0, true, C);
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) store4(p.dq_rot, (long)f * c.S + s0 + 16 * cc + li, r, C[r][cc]);
+      for (int cc = 0; cc < 4; ++cc) store4(p.dq_rot, (long)f * c.S + s0 + 16 * cc + li, C[cc]);
+    }
   }
   if (!absorb) {
-#pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int blk = b0; blk < b1; ++blk) {
+      const int s0 = 64 * blk;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         const long t = s0 + 16 * cc + li;
-        store4(p.dk_rot, t, r, f32x4{0.f, 0.f, 0.f, 0.f});
-        store4(p.dv, t, r, f32x4{0.f, 0.f, 0.f, 0.f});
+        store4(p.dk_rot, t, f32x4{0.f, 0.f, 0.f, 0.f});
+        store4(p.dv, t, f32x4{0.f, 0.f, 0.f, 0.f});
       }
-    if (tid < 64 && !p.acc) c.dbeta[bh * N + s0 + tid] = 0.f;
+      if (tid < 64 && !p.acc) c.dbeta[bh * N + s0 + tid] = 0.f;
+    }
     return;
   }
-  const long ta = (long)fa * c.S + s0;
-  const float g = c.decay[bh * F + fa];
-  float bcol[4];
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc) bcol[cc] = c.beta[bh * N + ta + 16 * cc + li];
-  __syncthreads();
-  stage16(p.k_rot, ta, 0);
-  __syncthreads();
-  f32x4 P[RW][4], Dd[RW][4];
-  if (it > 0) {
-    prod(c.SpT + ((size_t)bh * F + it - 1) * DD, 0, P);
-  } else {
-#pragma unroll
-    for (int r = 0; r < RW; ++r)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) P[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- pass 2, the absorbed frame's tokens
+  Frag aPT, aDT, aA, aSP;
+  load_a(c.AbT + ((size_t)bh * F + it) * DD, aDT);
+  load_a(c.Ab + ((size_t)bh * F + it) * DD, aA);
+  if (prev) {
+    load_a(c.SpT + ((size_t)bh * F + it - 1) * DD, aPT);
+    load_a(c.Sp + ((size_t)bh * F + it - 1) * DD, aSP);
   }
-  prod(c.AbT + ((size_t)bh * F + it) * DD, 0, Dd);
-  float db[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int blk = b0; blk < b1; ++blk) {
+    const int s0 = 64 * blk;
+    const long ta = (long)fa * c.S + s0;
+    dma::wait_vm0();
+    __syncthreads();  // k_rot and v rows are in; the previous block is done with both tiles
+    copy_k();
+    __syncthreads();
+    if (blk + 1 < b1) fetch_rows(p.k_rot, ta + 64, rawk);
+    float bcol[4];
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
+    for (int cc = 0; cc < 4; ++cc) bcol[cc] = c.beta[bh * N + ta + 16 * cc + li];
+    f32x4 P[4], Dd[4];
+    if (prev) {
+      prod(aPT, 1, false, P);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) P[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    prod(aDT, 1, false, Dd);
+    float db[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const long t = ta + 16 * cc + li;
-      const bf16x4 vv = *reinterpret_cast<const bf16x4*>(p.v + (bh * N + t) * D + ch0(r));
+      const int t = 16 * cc + li;
+      const bf16x4 vv = *reinterpret_cast<const bf16x4*>(rawv + t * D + ch0);
       f32x4 dvv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float rr = (float)vv[e] - g * P[r][cc][e];
-        const float dd = Dd[r][cc][e];
+        const float rr = (float)vv[e] - g * P[cc][e];
+        const float dd = Dd[cc][e];
         dvv[e] = bcol[cc] * dd;
         db[cc] += dd * rr;
-        P[r][cc][e] = bcol[cc] * rr;
-        Dd[r][cc][e] = -bcol[cc] * dd;
+        P[cc][e] = bcol[cc] * rr;
+        Dd[cc][e] = -bcol[cc] * dd;
       }
-      store4(p.dv, t, r, dvv);
+      store4(p.dv, ta + t, dvv);
     }
-  __syncthreads();  // every wave is done with the k tile
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
+    __syncthreads();  // every wave is done with the k tile and the v rows
+    if (blk + 1 < b1) fetch_rows(p.v, ta + 64, rawv);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const float xr[4] = {P[r][cc][0], P[r][cc][1], P[r][cc][2], P[r][cc][3]};
-      const float xd[4] = {Dd[r][cc][0], Dd[r][cc][1], Dd[r][cc][2], Dd[r][cc][3]};
-      put(1, 16 * cc + li, ch0(r), xr);
-      put(0, 16 * cc + li, ch0(r), xd);
+      put(1, 16 * cc + li, ch0, P[cc]);
+      put(0, 16 * cc + li, ch0, Dd[cc]);
     }
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    db[cc] += __shfl_xor(db[cc], 16, 64);
-    db[cc] += __shfl_xor(db[cc], 32, 64);
-    if (lq == 0) red[w][16 * cc + li] = db[cc];
+    for (int cc = 0; cc < 4; ++cc) {
+      db[cc] += __shfl_xor(db[cc], 16, 64);
+      db[cc] += __shfl_xor(db[cc], 32, 64);
+      if (lq == 0) red[w][16 * cc + li] = db[cc];
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) sum += red[i][tid];
+      c.dbeta[bh * N + ta + tid] = (p.acc ? c.dbeta[bh * N + ta + tid] : 0.f) + sum;
+    }
+    f32x4 K1[4];
+    prod(aA, 1, true, K1);
+    if (prev) {
+      f32x4 K2[4];
+      prod(aSP, 0, true, K2);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) K1[cc] = K1[cc] + g * K2[cc];
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) store4(p.dk_rot, ta + 16 * cc + li, K1[cc]);
   }
-  __syncthreads();
-  if (tid < 64)
-    c.dbeta[bh * N + ta + tid] = (p.acc ? c.dbeta[bh * N + ta + tid] : 0.f) +
-                                 ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
-  f32x4 K1[RW][4];
-  prod(c.Ab + ((size_t)bh * F + it) * DD, 1, K1);
-  if (it > 0) {
-    f32x4 K2[RW][4];
-    prod(c.Sp + ((size_t)bh * F + it - 1) * DD, 0, K2);
-#pragma unroll
-    for (int r = 0; r < RW; ++r)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) K1[r][cc] = K1[r][cc] + g * K2[r][cc];
-  }
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) store4(p.dk_rot, ta + 16 * cc + li, r, K1[r][cc]);
+}
+
+// Workgroups per (b, h, step) for the token kernel: enough for about one per CU in total.
+inline int tok_split(long bhf, int nblk) {
+  long s = (256 + bhf - 1) / bhf;
+  return (int)(s < 1 ? 1 : s > nblk ? nblk : s);
 }
 
 // ---- z stream token gradients ----------------------------------------------------------------
-// blockIdx.x as bbwd_tok_kernel; wave w takes 16 tokens, a lane D / 64 channels.  Runs after
+// blockIdx.x = (bh * F + it) * (S / 64) + token block; wave w takes 16 tokens, a lane D / 64
+// channels.  Runs after
 // bbwd_tok_kernel, whose dbeta it adds to.
 template <int D>
 __global__ __launch_bounds__(256) void bbwd_ztok_kernel(const BigdnBwdParams p) {
@@ -533,8 +603,9 @@ hipError_t launch_d(const BigdnBwdParams& p, hipStream_t stream) {
   hipError_t e = launch_cam_bwd_scan(c, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bbwd_zscan_kernel<D>), dim3(bh), dim3(1024), 0, stream, p);
+  const int ns = tok_split(bh * c.F, c.S / 64);
+  hipLaunchKernelGGL((bbwd_tok_kernel<D>), dim3(bh * c.F * ns), dim3(D * 4), 0, stream, p, ns);
   const dim3 tg(bh * c.F * (c.S / 64));
-  hipLaunchKernelGGL((bbwd_tok_kernel<D>), tg, dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bbwd_ztok_kernel<D>), tg, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
