@@ -156,13 +156,27 @@ __global__ __launch_bounds__(256) void bbwd_stats_kernel(const BigdnBwdParams p)
     }
     __syncthreads();
   }
-  float* out = (which == 0 ? c.G : (which == 1 ? c.U : (which == 2 ? c.W : p.Gpos))) + bf * D * D;
+  if (which == 0) {
+    // G as a hi/lo bf16 pair (the S-stream scan's A operands): hi [D][D], then lo
+    bf16* gh = reinterpret_cast<bf16*>(c.G) + bf * 2 * D * D;
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int cc = 0; cc < CT; ++cc)
+      for (int cc = 0; cc < CT; ++cc)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[(16 * (RT * w + r) + 4 * lq + e) * D + 16 * cc + li] = acc[r][cc][e];
+        for (int e = 0; e < 4; ++e) {
+          const size_t o = (size_t)(16 * (RT * w + r) + 4 * lq + e) * D + 16 * cc + li;
+          GDN_SPLIT(acc[r][cc][e], gh[o], gh[D * D + o]);
+        }
+  } else {
+    float* out = (which == 1 ? c.U : (which == 2 ? c.W : p.Gpos)) + bf * D * D;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[(16 * (RT * w + r) + 4 * lq + e) * D + 16 * cc + li] = acc[r][cc][e];
+  }
   // the z stream's vectors: the threads of one channel group (tid % (D / 8) equal; the item
   // offset 256 i keeps the group) add their sums through LDS
   if (which >= 2) {

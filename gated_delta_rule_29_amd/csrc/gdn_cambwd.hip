@@ -21,8 +21,9 @@
 //   stats  per (b, h, frame, matrix): G, U, W (D x D fp32) with 16x16x32 bf16 matrix products;
 //          a channel-major slab row is already in operand order (consecutive tokens of one
 //          channel), so the slabs go to LDS 32 tokens at a time without a transpose.
-//   scan   per (b, h, 32 state columns): the forward states and then A, in fp32 (16x16x4
-//          fp32 matrix products, the state in LDS); every step's state and A leave as hi/lo
+//   scan   per (b, h, 32 state columns): the forward states and then A, in fp32 with split
+//          bf16 products (the state in LDS as fp32 and as a hi/lo pair, G from the statistics
+//          as a hi/lo pair); every step's state and A leave as hi/lo
 //          bf16 pairs in both orientations for the token kernel, the states also in fp32 for
 //          the decay gradient, whose partial sums over the block's columns go to the workspace.
 //   token  per (b, h, step) (or a part of the step's token blocks when there are few steps):
@@ -127,7 +128,21 @@ __global__ __launch_bounds__(256) void cbwd_stats_kernel(const CamBwdParams p) {
     }
     __syncthreads();
   }
-  float* out = (which == 0 ? p.G : (which == 1 ? p.U : p.W)) + bf * D * D;
+  if (which == 0) {
+    // G as a hi/lo bf16 pair (the scan's A operands): hi [D][D], then lo, in the matrix's slot
+    bf16* gh = reinterpret_cast<bf16*>(p.G) + bf * 2 * D * D;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const size_t o = (size_t)(16 * (RT * w + r) + 4 * lq + e) * D + 16 * c + li;
+          GDN_SPLIT(acc[r][c][e], gh[o], gh[D * D + o]);
+        }
+    return;
+  }
+  float* out = (which == 1 ? p.U : p.W) + bf * D * D;
 #pragma unroll
   for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -143,7 +158,9 @@ template <int D>
 __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
   constexpr int RT = D / 64;  // row tiles per wave (16 rows each)
   constexpr int kS = D + 4;   // row stride of st (floats)
+  constexpr int kB = D + 8;   // row stride of the hi/lo copies (elements)
   __shared__ float st[32][kS];
+  __shared__ __attribute__((aligned(16))) bf16 sth[2][32][kB];  // st as a hi/lo bf16 pair
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
   const int bid = xcd_logical(blockIdx.x, gridDim.x);
@@ -151,22 +168,41 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
   const int c0 = 32 * (bid % (D / 32));
   const int F = p.F;
   const size_t DD = (size_t)D * D;
-  for (int e = threadIdx.x; e < 32 * kS; e += 256) (&st[0][0])[e] = 0.f;
+  auto zero_st = [&]() {
+    for (int e = threadIdx.x; e < 32 * kS; e += 256) (&st[0][0])[e] = 0.f;
+    for (int e = threadIdx.x; e < 2 * 32 * kB; e += 256) (&sth[0][0][0])[e] = bf16{};
+  };
+  zero_st();
   __syncthreads();
-  // T = M st (rows of this wave, the block's 32 columns) with M's A operands already in
-  // registers: tile (r, c) holds rows 16 (RT w + r) + 4 lq + e, column 16 c + li
+  // st[jl][i .. i + 3] (this lane's four rows of column jl) is x; also its hi/lo copy
+  auto set4 = [&](int jl, int i, const f32x4& x) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      st[jl][i + e] = x[e];
+      GDN_SPLIT(x[e], h[e], l[e]);
+    }
+    *reinterpret_cast<bf16x4*>(&sth[0][jl][i]) = h;
+    *reinterpret_cast<bf16x4*>(&sth[1][jl][i]) = l;
+  };
+  // T = M st (rows of this wave, the block's 32 columns) with M's A operands (hi/lo bf16)
+  // already in registers: tile (r, c) holds rows 16 (RT w + r) + 4 lq + e, column 16 c + li
   constexpr int KK = D / 32;
   struct Ops {
-    f32x8 a[RT][KK];     // rows 16 (RT w + r) + li of G, columns 32 kk + 8 lq ..
+    bf16x8 ah[RT][KK], al[RT][KK];  // rows 16 (RT w + r) + li of G, columns 32 kk + 8 lq ..
     float x[RT][2][4];   // U (forward) or W (backward) at this lane's elements
     float y[RT][2][4];   // the state before the step (backward)
     float g;
   };
-  auto fetch_g = [&](const float* M, Ops& o) {
+  auto fetch_g = [&](const bf16* M, Ops& o) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) o.a[r][kk] = lds8(M + (16 * (RT * w + r) + li) * D + 32 * kk + 8 * lq);
+      for (int kk = 0; kk < KK; ++kk) {
+        const size_t ro = (size_t)(16 * (RT * w + r) + li) * D + 32 * kk + 8 * lq;
+        o.ah[r][kk] = *reinterpret_cast<const bf16x8*>(M + ro);
+        o.al[r][kk] = *reinterpret_cast<const bf16x8*>(M + DD + ro);
+      }
   };
   auto fetch_el = [&](const float* M, float (&x)[RT][2][4]) {
 #pragma unroll
@@ -184,13 +220,16 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
       for (int c = 0; c < 2; ++c) T[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      f32x8 b[2];
+      bf16x8 bh[2], bl[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) b[c] = lds8(&st[16 * c + li][32 * kk + 8 * lq]);
+      for (int c = 0; c < 2; ++c) {
+        bh[c] = lds8(&sth[0][16 * c + li][32 * kk + 8 * lq]);
+        bl[c] = lds8(&sth[1][16 * c + li][32 * kk + 8 * lq]);
+      }
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) T[r][c] = mma16(o.a[r][kk], b[c], T[r][c]);
+        for (int c = 0; c < 2; ++c) T[r][c] = mma3(o.ah[r][kk], o.al[r][kk], bh[c], bl[c], T[r][c]);
     }
   };
   // this lane's elements: row i = 16 (RT w + r) + 4 lq + e, column j = 16 c + li of the block
@@ -222,7 +261,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
     if (it >= F || (p.reverse && it == 0)) return;
     const int fa = p.reverse ? F - it : it;
     o.g = p.decay[bh * F + fa];
-    fetch_g(p.G + ((size_t)bh * F + fa) * DD, o);
+    fetch_g(reinterpret_cast<const bf16*>(p.G) + ((size_t)bh * F + fa) * 2 * DD, o);
     fetch_el(p.U + ((size_t)bh * F + fa) * DD, o.x);
   };
   Ops cur, nxt;
@@ -236,12 +275,13 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c) {
+          const int i = 16 * (RT * w + r) + 4 * lq, jl = 16 * c + li;
+          f32x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 16 * (RT * w + r) + 4 * lq + e, jl = 16 * c + li;
-            st[jl][i] = cur.g * (st[jl][i] - T[r][c][e]) + cur.x[r][c][e];
-          }
+          for (int e = 0; e < 4; ++e) x[e] = cur.g * (st[jl][i + e] - T[r][c][e]) + cur.x[r][c][e];
+          set4(jl, i, x);
+        }
       __syncthreads();
     }
     save(it, false);
@@ -255,11 +295,11 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
     if (p.reverse && it == 0) return;
     const int fa = p.reverse ? f + 1 : f;
     o.g = p.decay[bh * F + fa];
-    fetch_g(p.G + ((size_t)bh * F + fa) * DD, o);
+    fetch_g(reinterpret_cast<const bf16*>(p.G) + ((size_t)bh * F + fa) * 2 * DD, o);
     fetch_el(it > 0 ? p.Spf + ((size_t)bh * F + it - 1) * DD : nullptr, o.y);
   };
   __syncthreads();
-  for (int e = threadIdx.x; e < 32 * kS; e += 256) (&st[0][0])[e] = 0.f;
+  zero_st();
   __syncthreads();
   fetch_bwd(F - 1, cur);
   for (int it = F - 1; it >= 0; --it) {
@@ -268,12 +308,13 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c) {
+        const int i = 16 * (RT * w + r) + 4 * lq, jl = 16 * c + li;
+        f32x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * (RT * w + r) + 4 * lq + e, jl = 16 * c + li;
-          st[jl][i] += cur.x[r][c][e];
-        }
+        for (int e = 0; e < 4; ++e) x[e] = st[jl][i + e] + cur.x[r][c][e];
+        set4(jl, i, x);
+      }
     __syncthreads();
     save(it, true);
     if (p.reverse && it == 0) break;
@@ -286,14 +327,17 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c) {
+        const int i = 16 * (RT * w + r) + 4 * lq, jl = 16 * c + li;
+        f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 16 * (RT * w + r) + 4 * lq + e, jl = 16 * c + li;
-          const float dp = st[jl][i] - T[r][c][e];
+          const float dp = st[jl][i + e] - T[r][c][e];
           part += dp * cur.y[r][c][e];
-          st[jl][i] = cur.g * dp;
+          x[e] = cur.g * dp;
         }
+        set4(jl, i, x);
+      }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
     if (lane == 0) red[w] = part;

@@ -212,7 +212,8 @@ struct CamBwdParams {
   float* ddecay;      // [B, H, F]
   int B, H, D, F, S;
   // workspace views, per (b, h, frame or step) D x D
-  float* G;           // frame statistics K diag(beta) K^T, K diag(beta) V^T, Q dout^T (fp32)
+  float* G;           // frame statistics K diag(beta) K^T (stored as a hi/lo bf16 pair in its
+                      // fp32 slot), K diag(beta) V^T, Q dout^T (fp32)
   float* U;
   float* W;
   float* Spf;         // state after each step (fp32)
