@@ -626,7 +626,7 @@ int cam_scan_bidi(const float* q, const float* k, const float* v, const float* b
 size_t cam_scan_bwd_workspace_bytes(int B, int H, int D, int F) {
   if (B <= 0 || H <= 0 || (D != 64 && D != 128) || F <= 0) return 0;
   const size_t mats = (size_t)B * H * F * D * D;
-  return 8 * al256(mats * 4) + al256((size_t)B * H * F * (D / 32) * 4);
+  return 8 * al256(mats * 4) + al256((size_t)B * H * F * (D / gdn::kScanCB) * 4);
 }
 
 int cam_scan_bwd(const float* q, const float* k, const float* v, const float* beta,
@@ -668,7 +668,7 @@ int cam_scan_bwd(const float* q, const float* k, const float* v, const float* be
   p.SpT = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
   p.Ab = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
   p.AbT = reinterpret_cast<__bf16*>(take(mats * 4));  // hi, then lo
-  p.ddecay_part = reinterpret_cast<float*>(take((size_t)B * H * F * (D / 32) * 4));
+  p.ddecay_part = reinterpret_cast<float*>(take((size_t)B * H * F * (D / gdn::kScanCB) * 4));
   p.lo = mats;
   hipError_t e = gdn::launch_cam_scan_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cam_scan_bwd launch");
@@ -680,7 +680,7 @@ int cam_scan_bwd(const float* q, const float* k, const float* v, const float* be
 size_t bigdn_dir_bwd_workspace_bytes(int B, int H, int D, int F) {
   if (B <= 0 || H <= 0 || (D != 64 && D != 128) || F <= 0) return 0;
   const size_t mats = (size_t)B * H * F * D * D, vecs = (size_t)B * H * F * D;
-  return 9 * al256(mats * 4) + al256((size_t)B * H * F * (D / 32) * 4) + 4 * al256(vecs * 4) +
+  return 9 * al256(mats * 4) + al256((size_t)B * H * F * (D / gdn::kScanCB) * 4) + 4 * al256(vecs * 4) +
          al256((size_t)B * H * F * 4);
 }
 
@@ -725,7 +725,7 @@ int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_pos, const
   c.SpT = reinterpret_cast<__bf16*>(take(mats * 4));
   c.Ab = reinterpret_cast<__bf16*>(take(mats * 4));
   c.AbT = reinterpret_cast<__bf16*>(take(mats * 4));
-  c.ddecay_part = reinterpret_cast<float*>(take((size_t)B * H * F * (D / 32) * 4));
+  c.ddecay_part = reinterpret_cast<float*>(take((size_t)B * H * F * (D / gdn::kScanCB) * 4));
   c.lo = mats;
   p.Gpos = reinterpret_cast<float*>(take(mats * 4));
   p.upos = reinterpret_cast<float*>(take(vecs * 4));

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(D * 4) void bbwd_tok_kernel(const BigdnBwdParams p,
   if (part == 0 && tid == 0) {
     if (absorb) {
       float s = p.ddz[bh * F + fa];
-      for (int cb = 0; cb < D / 32; ++cb) s += c.ddecay_part[((size_t)bh * F + fa) * (D / 32) + cb];
+      for (int cb = 0; cb < D / kScanCB; ++cb) s += c.ddecay_part[((size_t)bh * F + fa) * (D / kScanCB) + cb];
       c.ddecay[bh * F + fa] = (p.acc ? c.ddecay[bh * F + fa] : 0.f) + (it > 0 ? s : 0.f);
     } else if (!p.acc) {
       c.ddecay[bh * F] = 0.f;

@@ -89,6 +89,10 @@ struct MergeBwdParams {
 };
 hipError_t launch_merge_bwd(const MergeBwdParams& p, hipStream_t stream);
 
+// State columns per workgroup of the backward frame scan (gdn_cambwd.hip); the decay
+// gradient's partial sums come one per column block, D / kScanCB per (b, h, frame).
+constexpr int kScanCB = 16;
+
 // Backward of the camera-branch prep (gdn_prepbwd.hip).
 struct CamPrepBwdParams {
   const float* q;          // [B,N,H,D] fp32, the raw inputs of the prep

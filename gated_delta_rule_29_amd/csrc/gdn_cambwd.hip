@@ -152,25 +152,27 @@ __global__ __launch_bounds__(256) void cbwd_stats_kernel(const CamBwdParams p) {
 }
 
 // ---- scan: forward states, then the state gradients ---------------------------------------
-// blockIdx.x = bh * (D / 32) + column block.  st[col][row] holds the block's 32 columns of the
-// state (then of A), transposed so that a lane's 8 consecutive rows are one 32-byte read.
+// blockIdx.x = bh * (D / kScanCB) + column block.  st[col][row] holds the block's kScanCB
+// columns of the state (then of A), transposed so that a lane's 8 consecutive rows are one
+// contiguous read.
 template <int D>
 __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
   constexpr int RT = D / 64;  // row tiles per wave (16 rows each)
   constexpr int kS = D + 4;   // row stride of st (floats)
   constexpr int kB = D + 8;   // row stride of the hi/lo copies (elements)
-  __shared__ float st[32][kS];
-  __shared__ __attribute__((aligned(16))) bf16 sth[2][32][kB];  // st as a hi/lo bf16 pair
+  constexpr int CB = kScanCB, NC = CB / 16;  // columns per workgroup, 16-column tiles
+  __shared__ float st[CB][kS];
+  __shared__ __attribute__((aligned(16))) bf16 sth[2][CB][kB];  // st as a hi/lo bf16 pair
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
   const int bid = xcd_logical(blockIdx.x, gridDim.x);
-  const long bh = bid / (D / 32);
-  const int c0 = 32 * (bid % (D / 32));
+  const long bh = bid / (D / CB);
+  const int c0 = CB * (bid % (D / CB));
   const int F = p.F;
   const size_t DD = (size_t)D * D;
   auto zero_st = [&]() {
-    for (int e = threadIdx.x; e < 32 * kS; e += 256) (&st[0][0])[e] = 0.f;
-    for (int e = threadIdx.x; e < 2 * 32 * kB; e += 256) (&sth[0][0][0])[e] = bf16{};
+    for (int e = threadIdx.x; e < CB * kS; e += 256) (&st[0][0])[e] = 0.f;
+    for (int e = threadIdx.x; e < 2 * CB * kB; e += 256) (&sth[0][0][0])[e] = bf16{};
   };
   zero_st();
   __syncthreads();
@@ -190,8 +192,8 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
   constexpr int KK = D / 32;
   struct Ops {
     bf16x8 ah[RT][KK], al[RT][KK];  // rows 16 (RT w + r) + li of G, columns 32 kk + 8 lq ..
-    float x[RT][2][4];   // U (forward) or W (backward) at this lane's elements
-    float y[RT][2][4];   // the state before the step (backward)
+    float x[RT][NC][4];   // U (forward) or W (backward) at this lane's elements
+    float y[RT][NC][4];   // the state before the step (backward)
     float g;
   };
   auto fetch_g = [&](const bf16* M, Ops& o) {
@@ -204,32 +206,32 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
         o.al[r][kk] = *reinterpret_cast<const bf16x8*>(M + DD + ro);
       }
   };
-  auto fetch_el = [&](const float* M, float (&x)[RT][2][4]) {
+  auto fetch_el = [&](const float* M, float (&x)[RT][NC][4]) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           x[r][c][e] = M ? M[(size_t)(16 * (RT * w + r) + 4 * lq + e) * D + c0 + 16 * c + li] : 0.f;
   };
-  auto prod = [&](const Ops& o, f32x4 (&T)[RT][2]) {
+  auto prod = [&](const Ops& o, f32x4 (&T)[RT][NC]) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) T[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NC; ++c) T[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 bh[2], bl[2];
+      bf16x8 bh[NC], bl[NC];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NC; ++c) {
         bh[c] = lds8(&sth[0][16 * c + li][32 * kk + 8 * lq]);
         bl[c] = lds8(&sth[1][16 * c + li][32 * kk + 8 * lq]);
       }
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) T[r][c] = mma3(o.ah[r][kk], o.al[r][kk], bh[c], bl[c], T[r][c]);
+        for (int c = 0; c < NC; ++c) T[r][c] = mma3(o.ah[r][kk], o.al[r][kk], bh[c], bl[c], T[r][c]);
     }
   };
   // this lane's elements: row i = 16 (RT w + r) + 4 lq + e, column j = 16 c + li of the block
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NC; ++c) {
         const int j = c0 + 16 * c + li, i0 = 16 * (RT * w + r) + 4 * lq;
         bf16x4 ch, cl;
 #pragma unroll
@@ -269,13 +271,13 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
   for (int it = 0; it < F; ++it) {
     fetch_fwd(it + 1, nxt);
     if (!(p.reverse && it == 0)) {
-      f32x4 T[RT][2];
+      f32x4 T[RT][NC];
       prod(cur, T);
       __syncthreads();  // every wave has read st
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NC; ++c) {
           const int i = 16 * (RT * w + r) + 4 * lq, jl = 16 * c + li;
           f32x4 x;
 #pragma unroll
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NC; ++c) {
         const int i = 16 * (RT * w + r) + 4 * lq, jl = 16 * c + li;
         f32x4 x;
 #pragma unroll
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
     save(it, true);
     if (p.reverse && it == 0) break;
     const int fa = p.reverse ? f + 1 : f;
-    f32x4 T[RT][2];
+    f32x4 T[RT][NC];
     prod(cur, T);
     __syncthreads();
     // dP = A - G A; its sum against the state before the step (zero before the first step)
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NC; ++c) {
         const int i = 16 * (RT * w + r) + 4 * lq, jl = 16 * c + li;
         f32x4 x;
 #pragma unroll
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
     if (lane == 0) red[w] = part;
     __syncthreads();
     if (threadIdx.x == 0)
-      p.ddecay_part[((size_t)bh * F + fa) * (D / 32) + bid % (D / 32)] = (red[0] + red[1]) + (red[2] + red[3]);
+      p.ddecay_part[((size_t)bh * F + fa) * (D / CB) + bid % (D / CB)] = (red[0] + red[1]) + (red[2] + red[3]);
     cur = nxt;
   }
 }
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(D * 4) void cbwd_tok_kernel(const CamBwdParams p, i
   if (part == 0 && tid == 0) {
     if (absorb) {
       float s = 0.f;
-      for (int cb = 0; cb < D / 32; ++cb) s += p.ddecay_part[((size_t)bh * F + fa) * (D / 32) + cb];
+      for (int cb = 0; cb < D / kScanCB; ++cb) s += p.ddecay_part[((size_t)bh * F + fa) * (D / kScanCB) + cb];
       p.ddecay[bh * F + fa] = (p.acc ? p.ddecay[bh * F + fa] : 0.f) + (it > 0 ? s : 0.f);
     } else if (!p.acc) {
       p.ddecay[bh * F] = 0.f;  // frame 0 of the reverse scan is never absorbed
@@ -592,7 +594,7 @@ template <int D>
 hipError_t launch_d(const CamBwdParams& p, hipStream_t stream) {
   const long bh = (long)p.B * p.H;
   hipLaunchKernelGGL((cbwd_stats_kernel<D>), dim3(bh * p.F * 3), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((cbwd_scan_kernel<D>), dim3(bh * (D / 32)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((cbwd_scan_kernel<D>), dim3(bh * (D / kScanCB)), dim3(256), 0, stream, p);
   const int ns = tok_split(bh * p.F, p.S / 64);
   hipLaunchKernelGGL((cbwd_tok_kernel<D>), dim3(bh * p.F * ns), dim3(D * 4), 0, stream, p, ns);
   return hipGetLastError();
@@ -607,9 +609,9 @@ hipError_t launch_cam_scan_bwd(const CamBwdParams& p, hipStream_t stream) {
 hipError_t launch_cam_bwd_scan(const CamBwdParams& p, hipStream_t stream) {
   const long bh = (long)p.B * p.H;
   if (p.D == 128)
-    hipLaunchKernelGGL((cbwd_scan_kernel<128>), dim3(bh * 4), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((cbwd_scan_kernel<128>), dim3(bh * (128 / kScanCB)), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((cbwd_scan_kernel<64>), dim3(bh * 2), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((cbwd_scan_kernel<64>), dim3(bh * (64 / kScanCB)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
