@@ -522,13 +522,19 @@ def main():
         kernel = "cam_scan_bwd x 2 directions (3 kernels each, whole step)"
         config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
                   "state": "fp32", "products": "split bf16 (hi/lo) operands, fp32 accumulation",
-                  "step": "gradients of the forward and of the reverse frame scan (two calls; "
-                          "summing the two directions' gradients is the caller's)"}
+                  "step": "gradients of the forward and of the reverse frame scan (two calls, "
+                          "the second reusing the first's frame statistics; summing the two "
+                          "directions' gradients is the caller's)"}
+
+        ws = torch.empty(gdn._lib.load().cam_scan_bwd_workspace_bytes(B, H, D, F),
+                         dtype=torch.uint8, device=dev)
 
         def step(i):
             s = sets[i % len(sets)]
+            # the reverse call reuses the forward one's frame statistics (same q, k, v, beta)
             return [gdn.cam_scan_bwd(s["q"], s["k"], s["v"], s["beta"], s["decay"], s["dout"],
-                                     reverse=rev) for rev in (False, True)]
+                                     reverse=rev, workspace=ws, reuse_stats=rev)
+                    for rev in (False, True)]
     elif kind == "cam_branch_bwd":
         B, N, H, D = inp["q"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]
@@ -557,13 +563,19 @@ def main():
         kernel = "bigdn_dir_bwd x 2 directions (5 kernels each, whole step)"
         config = {"workload": args.workload, "B": B, "F": F, "S": S, "N": N, "H": H, "D": D,
                   "state": "fp32", "products": "split bf16 (hi/lo) operands, fp32 accumulation",
-                  "step": "gradients of the forward and of the reverse direction (two calls; "
-                          "summing the two directions' gradients is the caller's)"}
+                  "step": "gradients of the forward and of the reverse direction (two calls, the "
+                          "second reusing the first's frame statistics; summing the two "
+                          "directions' gradients is the caller's)"}
         names = ("q_rot", "k_rot", "q_pos", "k_pos", "v", "beta", "decay", "dnum", "dden")
+
+        ws = torch.empty(gdn._lib.load().bigdn_dir_bwd_workspace_bytes(B, H, D, F),
+                         dtype=torch.uint8, device=dev)
 
         def step(i):
             s = sets[i % len(sets)]
-            return [gdn.bigdn_dir_bwd(*(s[k] for k in names), reverse=rev) for rev in (False, True)]
+            # the reverse call reuses the forward one's frame statistics (same inputs)
+            return [gdn.bigdn_dir_bwd(*(s[k] for k in names), reverse=rev, workspace=ws,
+                                      reuse_stats=rev) for rev in (False, True)]
     elif kind == "bigdn_block_bwd":
         B, N, _, H, D = inp["qkv"].shape
         F, S = inp["beta"].shape[2], inp["beta"].shape[3]

@@ -68,6 +68,19 @@ def _cu_pair(cu_seqlens, cu_seqlens_host, dev):
     return cu_dev, cu_host
 
 
+def _workspace(ws, nbytes, device, required=False):
+    """A caller's workspace (uint8, at least nbytes, on device, contiguous), or a new one."""
+    if ws is None:
+        if required:
+            raise ValueError("reuse_stats needs the workspace of the call that formed them")
+        return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+    if (not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.device != device
+            or not ws.is_contiguous() or ws.numel() < nbytes):
+        raise ValueError("workspace must be a contiguous uint8 tensor of at least %d bytes on %s"
+                         % (nbytes, device))
+    return ws
+
+
 def _need(t, name, shape, dtype, device):
     if t is None:
         return
@@ -467,13 +480,16 @@ def cam_scan_bidi(q, k, v, beta, decay, *, decay_bwd=None, init_state=None,
     return (of, orv, fin) if save_final_state else (of, orv)
 
 
-def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False, *, accumulate=False, out=None):
+def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False, *, accumulate=False, out=None,
+                 workspace=None, reuse_stats=False):
     """Backward of cam_scan (one direction, no state in / out): gradients of sum(out * dout).
     q, k, v, dout [B,H,D,N] fp32; beta [B,H,F,S]; decay [B,H,F].  Returns a dict with dq,
     dk, dv [B,H,D,N], dbeta [B,H,F,S] and ddecay [B,H,F] (fp32).  out: a dict of those
     tensors to write into (contiguous; e.g. one direction's slice of [2,B,H,D,N] tensors for
     cam_prep_bwd); accumulate: add dbeta and ddecay to out's contents instead of writing
-    them."""
+    them.  workspace: a uint8 tensor of cam_scan_bwd_workspace_bytes (else one is allocated);
+    reuse_stats: it holds the frame statistics of a previous call with the same q, k, v, beta
+    (the other direction's), which are then not formed again."""
     B, H, D, N = q.shape
     F, S = beta.shape[2], beta.shape[3]
     dev = q.device
@@ -496,8 +512,9 @@ def cam_scan_bwd(q, k, v, beta, decay, dout, reverse=False, *, accumulate=False,
             _need(out[n], n, shp, torch.float32, dev)
     lib = _lib.load()
     ws_n = lib.cam_scan_bwd_workspace_bytes(B, H, D, F)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
-    flag = int(bool(reverse)) | (_lib.BWD_ACCUMULATE if accumulate else 0)
+    ws = _workspace(workspace, ws_n, dev, reuse_stats)
+    flag = (int(bool(reverse)) | (_lib.BWD_ACCUMULATE if accumulate else 0)
+            | (_lib.BWD_REUSE_STATS if reuse_stats else 0))
     rc = lib.cam_scan_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), _ptr(dout),
                           flag, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                           _ptr(out["dbeta"]), _ptr(out["ddecay"]), B, H, D, F, S, _ptr(ws), ws_n,
@@ -514,7 +531,8 @@ def cam_bwd(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_
     direction's decay).  The library calls, in order: cam_prep (the prepped tensors again),
     cam_scan_bwd for the forward and the reverse direction into one [2,B,H,D,N] set of
     gradients (the reverse call's dbeta added into the forward one's, and its ddecay too
-    unless decay_bwd is given), cam_prep_bwd over both directions.  Returns a dict with dq, dk, dv [B,N,H,D],
+    unless decay_bwd is given; it reuses the forward call's frame statistics), cam_prep_bwd
+    over both directions.  Returns a dict with dq, dk, dv [B,N,H,D],
     dq_norm_w, dk_norm_w [H*D], dbeta [B,H,F,S] (both directions), ddecay [B,H,F] (both
     directions, or the forward one's with ddecay_bwd the reverse one's when decay_bwd is
     given)."""
@@ -527,15 +545,18 @@ def cam_bwd(q, k, v, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_
              for n in ("dq", "dk", "dv")}
     par = {"dbeta": torch.empty(B, H, F, S, dtype=torch.float32, device=dev),
            "ddecay": torch.empty(B, H, F, dtype=torch.float32, device=dev)}
+    ws = torch.empty(_lib.load().cam_scan_bwd_workspace_bytes(B, H, D, F), dtype=torch.uint8,
+                     device=dev)
     cam_scan_bwd(qt, kt, vt, beta, decay, dout_fwd, reverse=False,
-                 out=dict({n: grads[n][0] for n in grads}, **par))
+                 out=dict({n: grads[n][0] for n in grads}, **par), workspace=ws)
     # beta is shared by the two directions, so the reverse call always adds its dbeta; its
     # ddecay goes to a zeroed array of its own when the reverse direction has its own decay
     sep = decay_bwd is not None
     ddecay_r = torch.zeros_like(par["ddecay"]) if sep else par["ddecay"]
     cam_scan_bwd(qt, kt, vt, beta, decay if decay_bwd is None else decay_bwd, dout_rev,
                  reverse=True, accumulate=True,
-                 out=dict({n: grads[n][1] for n in grads}, dbeta=par["dbeta"], ddecay=ddecay_r))
+                 out=dict({n: grads[n][1] for n in grads}, dbeta=par["dbeta"], ddecay=ddecay_r),
+                 workspace=ws, reuse_stats=True)
     g = cam_prep_bwd(q, k, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale,
                      grads["dq"], grads["dk"], grads["dv"], dinfl, norm_eps)
     res = dict(g, dbeta=par["dbeta"], ddecay=par["ddecay"])
@@ -576,13 +597,16 @@ def gdn_bwd_dhu(q, k, w, do, dv, g=None, dht=None, scale=1.0, *, gk=None, want_d
 
 
 def bigdn_dir_bwd(q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden, reverse=False, *,
-                  accumulate=False, out=None):
+                  accumulate=False, out=None, workspace=None, reuse_stats=False):
     """Backward of one BiGDN direction on the prepped tensors (q_rot .. v [B,H,N,D] bf16, as
     gdn_prep returns them); beta [B,H,F,S], decay [B,H,F]; dnum [B,N,H,D], dden [B,H,N] fp32.
     Returns a dict with dq_rot, dk_rot, dq_pos, dk_pos, dv [B,H,N,D], dbeta [B,H,F,S] and
     ddecay [B,H,F] (fp32).  out: a dict of those tensors to write into (contiguous; e.g. one
     direction's slice of [2,B,H,N,D] tensors for gdn_prep_bwd); accumulate: add dbeta and
-    ddecay to out's contents instead of writing them."""
+    ddecay to out's contents instead of writing them.  workspace: a uint8 tensor of
+    bigdn_dir_bwd_workspace_bytes (else one is allocated); reuse_stats: it holds the frame
+    statistics of a previous call with the same tensors, beta, dnum and dden (the other
+    direction's), which are then not formed again."""
     B, H, N, D = q_rot.shape
     F, S = beta.shape[2], beta.shape[3]
     dev = q_rot.device
@@ -608,8 +632,9 @@ def bigdn_dir_bwd(q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum, dden, revers
                 raise ValueError("out[%r] must be a contiguous tensor" % n)
     lib = _lib.load()
     ws_n = lib.bigdn_dir_bwd_workspace_bytes(B, H, D, F)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
-    flag = int(bool(reverse)) | (_lib.BWD_ACCUMULATE if accumulate else 0)
+    ws = _workspace(workspace, ws_n, dev, reuse_stats)
+    flag = (int(bool(reverse)) | (_lib.BWD_ACCUMULATE if accumulate else 0)
+            | (_lib.BWD_REUSE_STATS if reuse_stats else 0))
     rc = lib.bigdn_dir_bwd(*(_ptr(x) for x in (q_rot, k_rot, q_pos, k_pos, v, beta, decay, dnum,
                                                dden)), flag,
                            *(_ptr(out[n]) for n in names + ("dbeta", "ddecay")),
@@ -692,14 +717,18 @@ def bigdn_bwd(qkv, beta, decay, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale,
     grads = {n: torch.empty(2, B, H, N, D, dtype=torch.float32, device=dev) for n in names}
     par = {"dbeta": torch.empty(B, H, F, S, dtype=torch.float32, device=dev),
            "ddecay": torch.empty(B, H, F, dtype=torch.float32, device=dev)}
+    ws = torch.empty(_lib.load().bigdn_dir_bwd_workspace_bytes(B, H, D, F), dtype=torch.uint8,
+                     device=dev)
     bigdn_dir_bwd(*t, beta, decay, m["dnum"], m["dden"], reverse=False,
-                  out=dict({n: grads[n][0] for n in names}, **par))
+                  out=dict({n: grads[n][0] for n in names}, **par), workspace=ws)
     sep = beta_bwd is not None or decay_bwd is not None
     par_r = ({"dbeta": torch.empty_like(par["dbeta"]), "ddecay": torch.empty_like(par["ddecay"])}
              if sep else par)
+    # the frame statistics do not depend on the direction (beta does enter them)
     bigdn_dir_bwd(*t, beta if beta_bwd is None else beta_bwd,
                   decay if decay_bwd is None else decay_bwd, m["dnum"], m["dden"], reverse=True,
-                  accumulate=not sep, out=dict({n: grads[n][1] for n in names}, **par_r))
+                  accumulate=not sep, out=dict({n: grads[n][1] for n in names}, **par_r),
+                  workspace=ws, reuse_stats=beta_bwd is None)
     g = gdn_prep_bwd(qkv, q_norm_w, k_norm_w, rope_cos, rope_sin, k_scale, grads, norm_eps)
     res = dict(g, dbeta=par["dbeta"], ddecay=par["ddecay"], dgate=m["dgate"])
     if sep:

@@ -15,6 +15,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FWD_PER_KEY, FWD_SAVES = 1, 2
 BWD_ACCUMULATE = 2
+BWD_REUSE_STATS = 4
 
 P = ctypes.c_void_p
 I = ctypes.c_int

@@ -638,9 +638,10 @@ int cam_scan_bwd(const float* q, const float* k, const float* v, const float* be
   if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S <= 0)
     return fail(GDN_ERR_INVALID, "B, H, D, F, S must be positive (got %d, %d, %d, %d, %d)", B, H,
                 D, F, S);
-  if (reverse & ~(1 | GDN_BWD_ACCUMULATE))
-    return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, optionally with GDN_BWD_ACCUMULATE, got %d", reverse);
+  if (reverse & ~(1 | GDN_BWD_ACCUMULATE | GDN_BWD_REUSE_STATS))
+    return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, optionally with GDN_BWD_ACCUMULATE and GDN_BWD_REUSE_STATS, got %d", reverse);
   const int acc = (reverse & GDN_BWD_ACCUMULATE) ? 1 : 0;
+  const int reuse = (reverse & GDN_BWD_REUSE_STATS) ? 1 : 0;
   reverse &= 1;
   if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
   if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
@@ -656,7 +657,7 @@ int cam_scan_bwd(const float* q, const float* k, const float* v, const float* be
   char* ws = static_cast<char*>(workspace);
   gdn::CamBwdParams p{};
   p.q = q; p.k = k; p.v = v; p.beta = beta; p.decay = decay; p.dout = dout; p.reverse = reverse;
-  p.acc = acc; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.ddecay = ddecay;
+  p.acc = acc; p.reuse = reuse; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.ddecay = ddecay;
   p.B = B; p.H = H; p.D = D; p.F = F; p.S = S;
   size_t off = 0;
   auto take = [&](size_t bytes) { char* r = ws + off; off += al256(bytes); return r; };
@@ -695,9 +696,10 @@ int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_pos, const
   if (B <= 0 || H <= 0 || D <= 0 || F <= 0 || S <= 0)
     return fail(GDN_ERR_INVALID, "B, H, D, F, S must be positive (got %d, %d, %d, %d, %d)", B, H,
                 D, F, S);
-  if (reverse & ~(1 | GDN_BWD_ACCUMULATE))
-    return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, optionally with GDN_BWD_ACCUMULATE, got %d", reverse);
+  if (reverse & ~(1 | GDN_BWD_ACCUMULATE | GDN_BWD_REUSE_STATS))
+    return fail(GDN_ERR_INVALID, "reverse must be 0 or 1, optionally with GDN_BWD_ACCUMULATE and GDN_BWD_REUSE_STATS, got %d", reverse);
   const int acc = (reverse & GDN_BWD_ACCUMULATE) ? 1 : 0;
+  const int reuse = (reverse & GDN_BWD_REUSE_STATS) ? 1 : 0;
   reverse &= 1;
   if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D must be 64 or 128, got %d", D);
   if (S % 64) return fail(GDN_ERR_UNSUPPORTED, "S (tokens per frame) must be a multiple of 64, got %d", S);
@@ -738,6 +740,7 @@ int bigdn_dir_bwd(const void* q_rot, const void* k_rot, const void* q_pos, const
   p.v = static_cast<const __bf16*>(v); p.dnum = dnum; p.dden = dden;
   p.dq_rot = dq_rot; p.dk_rot = dk_rot; p.dq_pos = dq_pos; p.dk_pos = dk_pos; p.dv = dv;
   p.acc = acc;
+  c.reuse = reuse;
   hipError_t e = gdn::launch_bigdn_dir_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "bigdn_dir_bwd launch");
   return ok();

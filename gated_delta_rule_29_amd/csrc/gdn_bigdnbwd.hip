@@ -613,7 +613,8 @@ template <int D>
 hipError_t launch_d(const BigdnBwdParams& p, hipStream_t stream) {
   const CamBwdParams& c = p.cam;
   const long bh = (long)c.B * c.H;
-  hipLaunchKernelGGL((bbwd_stats_kernel<D>), dim3(bh * c.F * 4), dim3(256), 0, stream, p);
+  if (!c.reuse)  // the per-frame statistics (and the z stream's vectors) of every direction
+    hipLaunchKernelGGL((bbwd_stats_kernel<D>), dim3(bh * c.F * 4), dim3(256), 0, stream, p);
   hipError_t e = launch_cam_bwd_scan(c, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bbwd_zscan_kernel<D>), dim3(bh), dim3(1024), 0, stream, p);

@@ -46,7 +46,8 @@ typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // ---- stats: G_f, U_f, W_f ----------------------------------------------------------------
-// blockIdx.x = (bh * F + f) * 3 + which; four waves, wave w owns rows 16 RT w .. of the D x D
+// blockIdx.x = (bh * F + f) * 3 + which (with p.reuse, G and U are kept and blockIdx.x = bh * F
+// + f forms W alone); four waves, wave w owns rows 16 RT w .. of the D x D
 // result, all columns.  Per 32-token step the two slabs go to LDS as split pairs [channel][32
 // tokens] (a slab row is already token-contiguous), shared by the four waves; the next
 // step's rows are loaded into registers while the current step's products run.
@@ -59,8 +60,9 @@ __global__ __launch_bounds__(256) void cbwd_stats_kernel(const CamBwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 yt[2][D * kX];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lq = lane >> 4;
   const int bid = xcd_logical(blockIdx.x, gridDim.x);
-  const int which = bid % 3;
-  const long bf = bid / 3;
+  const int nw = p.reuse ? 1 : 3;  // matrices formed: G, U, W, or W alone
+  const int which = p.reuse ? 2 : bid % 3;
+  const long bf = bid / nw;
   const int f = (int)(bf % p.F);
   const long bh = bf / p.F;
   const long N = (long)p.F * p.S;
@@ -593,7 +595,7 @@ inline int tok_split(long bhf, int nblk) {
 template <int D>
 hipError_t launch_d(const CamBwdParams& p, hipStream_t stream) {
   const long bh = (long)p.B * p.H;
-  hipLaunchKernelGGL((cbwd_stats_kernel<D>), dim3(bh * p.F * 3), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((cbwd_stats_kernel<D>), dim3(bh * p.F * (p.reuse ? 1 : 3)), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((cbwd_scan_kernel<D>), dim3(bh * (D / kScanCB)), dim3(256), 0, stream, p);
   const int ns = tok_split(bh * p.F, p.S / 64);
   hipLaunchKernelGGL((cbwd_tok_kernel<D>), dim3(bh * p.F * ns), dim3(D * 4), 0, stream, p, ns);

@@ -205,6 +205,7 @@ struct CamBwdParams {
   const float* dout;  // [B, H, D, N]
   int reverse;
   int acc;            // add dbeta and ddecay to the arrays' contents
+  int reuse;          // G and U are in the workspace already (only W is formed)
   float* dq;          // [B, H, D, N]
   float* dk;
   float* dv;

@@ -63,6 +63,7 @@ extern "C" {
 #define GDN_ABI_VERSION 6
 #define GDN_CHUNK 64
 #define GDN_BWD_ACCUMULATE 2  /* bigdn_dir_bwd: add dbeta, ddecay into the outputs */
+#define GDN_BWD_REUSE_STATS 4 /* the workspace holds this call's frame statistics already */
 
 /* Status codes (the pages' wrappers raise ValueError / NotImplementedError / RuntimeError
  * for these classes, SANA fused_gdn.py page, fused_gdn_func argument checks). */
@@ -408,7 +409,11 @@ GDN_API int cam_scan_bidi(const float* q, const float* k, const float* v, const 
  * per-iteration derivation).  The forward states are recomputed here, so the call needs only
  * the forward's inputs.  reverse | GDN_BWD_ACCUMULATE adds this direction's dbeta and ddecay
  * to the arrays' contents instead of writing them (both directions of cam_scan_bidi share beta
- * and, unless decay_bwd is given, decay); dq, dk, dv are always written.
+ * and, unless decay_bwd is given, decay); dq, dk, dv are always written.  The per-frame
+ * statistics K diag(beta) K^T and K diag(beta) V^T do not depend on the direction:
+ * reverse | GDN_BWD_REUSE_STATS takes them from the workspace, where a previous call with the
+ * same q, k, v, beta, B, H, D, F, S (the other direction's) left them, and forms only
+ * Q dout^T (the caller guarantees the match; nothing checks it).
  *   q, k, v, dout [B,H,D,N] fp32 channel-major, N = F*S; beta [B,H,F,S]; decay [B,H,F]
  *   dq, dk, dv    [B,H,D,N] fp32 OUT;  dbeta [B,H,F,S] fp32 OUT;  ddecay [B,H,F] fp32 OUT
  *   Tokens never absorbed (frame 0 of the reverse scan) get zero dk, dv, dbeta; a decay that
@@ -438,6 +443,9 @@ GDN_API int cam_scan_bwd(const float* q, const float* k, const float* v, const f
  * reverse | GDN_BWD_ACCUMULATE adds this direction's dbeta and ddecay to the arrays' contents
  * instead of writing them (the two directions share beta and decay unless the reverse one is
  * overridden); the token gradients are always written (gdn_prep_bwd sums directions).
+ * reverse | GDN_BWD_REUSE_STATS skips the per-frame statistics (they do not depend on the
+ * direction): the workspace must hold those of a previous call with the same prepped tensors,
+ * beta, dnum, dden and sizes (the other direction's; the caller guarantees the match).
  * With S, z the states and A, a their gradients after a step's update (S_pre = g S_prev,
  * z_pre = g z_prev for the frame the step absorbs), per token:
  *   output frame:   dq_rot = S dnum,  dq_pos = dden z

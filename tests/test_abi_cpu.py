@@ -303,12 +303,14 @@ def test_cam_scan_bwd_validation_codes():
     assert call(q=None) == L.ERR_INVALID
     assert call(dout=None) == L.ERR_INVALID
     assert call(F=0) == L.ERR_INVALID
-    assert call(rev=4) == L.ERR_INVALID
+    assert call(rev=8) == L.ERR_INVALID
     assert call(rev=-1) == L.ERR_INVALID
     assert call(D=32) == L.ERR_UNSUPPORTED
     assert call(S=100) == L.ERR_UNSUPPORTED
     assert call() == L.ERR_WORKSPACE
     assert call(rev=1 | L.BWD_ACCUMULATE) == L.ERR_WORKSPACE   # the accumulate flag is valid
+    assert call(rev=1 | L.BWD_REUSE_STATS) == L.ERR_WORKSPACE  # so is the reuse flag
+    assert call(rev=8) == L.ERR_INVALID
     n = lib.cam_scan_bwd_workspace_bytes(1, 2, 128, 3)
     assert n >= 1 * 2 * 3 * 128 * 128 * (4 * 4 + 4 * 2)
     assert lib.cam_scan_bwd_workspace_bytes(1, 2, 96, 3) == 0
@@ -326,11 +328,12 @@ def test_bigdn_dir_bwd_validation_codes():
 
     assert call(q=None) == L.ERR_INVALID
     assert call(dnum=None) == L.ERR_INVALID
-    assert call(rev=4) == L.ERR_INVALID
+    assert call(rev=8) == L.ERR_INVALID
     assert call(rev=-1) == L.ERR_INVALID
     assert call(D=32) == L.ERR_UNSUPPORTED
     assert call(S=100) == L.ERR_UNSUPPORTED
-    for rev in (0, 1, L.BWD_ACCUMULATE, 1 | L.BWD_ACCUMULATE):  # valid flags: only the workspace is missing
+    for rev in (0, 1, L.BWD_ACCUMULATE, 1 | L.BWD_ACCUMULATE, 1 | L.BWD_REUSE_STATS,
+                1 | L.BWD_ACCUMULATE | L.BWD_REUSE_STATS):  # valid flags: only the workspace is missing
         assert call(rev=rev) == L.ERR_WORKSPACE
 
 

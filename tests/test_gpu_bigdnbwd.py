@@ -72,3 +72,22 @@ def test_bigdn_dir_bwd_video_shape_sampled(reverse):
     inp = workloads.bigdn_bwd_inputs(1, 16, 1024, 16, 128, seed=33 + int(reverse))
     say("video-shape bigdn_dir_bwd reverse %s" % reverse)
     _check(inp, reverse, heads=[0, 9, 15])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bigdn_dir_bwd_reused_statistics(D):
+    """The reverse call with the forward call's frame statistics (GDN_BWD_REUSE_STATS) equals
+    a call that forms them itself, bit for bit."""
+    import gated_delta_rule_29_amd as g
+
+    inp = workloads.bigdn_bwd_inputs(1, 3, 64, 2, D, seed=11 + D)
+    d = {k: inp[k].to(DEV) for k in IN}
+    B, H, N, D_ = d["q_rot"].shape
+    ws = torch.empty(g._lib.load().bigdn_dir_bwd_workspace_bytes(B, H, D, 3), dtype=torch.uint8,
+                     device=DEV)
+    g.bigdn_dir_bwd(*(d[k] for k in IN), reverse=False, workspace=ws)
+    reused = g.bigdn_dir_bwd(*(d[k] for k in IN), reverse=True, workspace=ws, reuse_stats=True)
+    fresh = g.bigdn_dir_bwd(*(d[k] for k in IN), reverse=True)
+    torch.cuda.synchronize()
+    for name in OUT:
+        assert torch.equal(reused[name], fresh[name]), name

@@ -78,3 +78,24 @@ def test_cam_scan_bwd_video_shape_sampled(reverse):
     inp = workloads.cam_scan_bwd_inputs(1, 16, 1024, 16, 128, seed=77 + int(reverse))
     say("video-shape cam_scan_bwd reverse %s" % reverse)
     _check(inp, reverse, heads=[0, 7, 15])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_cam_scan_bwd_reused_statistics(D):
+    """The reverse call with the forward call's frame statistics (GDN_BWD_REUSE_STATS) and its
+    own upstream gradient equals a call that forms them itself, bit for bit."""
+    import gated_delta_rule_29_amd as g
+
+    inp = workloads.cam_scan_bwd_inputs(1, 3, 128, 2, D, seed=8 + D)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    dout_rev = torch.randn(d["dout"].shape, generator=torch.Generator().manual_seed(9)).to(DEV)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["decay"])
+    B, H, D_, N = d["q"].shape
+    ws = torch.empty(g._lib.load().cam_scan_bwd_workspace_bytes(B, H, D, 3), dtype=torch.uint8,
+                     device=DEV)
+    g.cam_scan_bwd(*args, d["dout"], reverse=False, workspace=ws)
+    reused = g.cam_scan_bwd(*args, dout_rev, reverse=True, workspace=ws, reuse_stats=True)
+    fresh = g.cam_scan_bwd(*args, dout_rev, reverse=True)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        assert torch.equal(reused[name], fresh[name]), name
