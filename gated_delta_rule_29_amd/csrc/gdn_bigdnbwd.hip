@@ -546,14 +546,17 @@ inline int tok_split(long bhf, int nblk) {
 }
 
 // ---- z stream token gradients ----------------------------------------------------------------
-// blockIdx.x = (bh * F + it) * (S / 64) + token block; wave w takes 16 tokens, a lane D / 64
-// channels.  Runs after
-// bbwd_tok_kernel, whose dbeta it adds to.
+// blockIdx.x = (bh * F + it) * (S / 64) + token block; wave w takes 16 tokens.  A lane owns
+// four consecutive channels, so D / 4 lanes cover a token and a wave works on 256 / D tokens at
+// once (16-byte stores, 8-byte k_pos loads, reductions over the token's lanes only).  Runs
+// after bbwd_tok_kernel, whose dbeta it adds to.
 template <int D>
 __global__ __launch_bounds__(256) void bbwd_ztok_kernel(const BigdnBwdParams p) {
-  constexpr int CL = D / 64;  // channels per lane
+  constexpr int LPT = D / 4, TPW = 64 / LPT;  // lanes per token, tokens per wave at once
+  typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   const CamBwdParams& c = p.cam;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tl = lane / LPT, ch = 4 * (lane % LPT);  // token slot, first channel
   const int nblk = c.S / 64;
   const int bid = xcd_logical(blockIdx.x, gridDim.x);
   const int blk = bid % nblk;
@@ -566,46 +569,42 @@ __global__ __launch_bounds__(256) void bbwd_ztok_kernel(const BigdnBwdParams p) 
   const bool absorb = !(c.reverse && it == 0);
   const int fa = c.reverse ? f + 1 : f;
   const int s0 = 64 * blk + 16 * w;
-  float za[CL], av[CL], zp[CL];
-#pragma unroll
-  for (int j = 0; j < CL; ++j) {
-    const int ch = lane + 64 * j;
-    za[j] = p.zs[(bh * F + it) * D + ch];
-    av[j] = p.as[(bh * F + it) * D + ch];
-    zp[j] = absorb && it > 0 ? c.decay[bh * F + fa] * p.zs[(bh * F + it - 1) * D + ch] : 0.f;
-  }
-  for (int i = 0; i < 16; ++i) {
+  const f32x4 za = *reinterpret_cast<const f32x4*>(p.zs + (bh * F + it) * D + ch);
+  const f32x4 av = *reinterpret_cast<const f32x4*>(p.as + (bh * F + it) * D + ch);
+  f32x4 zp = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (absorb && it > 0)
+    zp = c.decay[bh * F + fa] * *reinterpret_cast<const f32x4*>(p.zs + (bh * F + it - 1) * D + ch);
+#pragma unroll 4
+  for (int i = tl; i < 16; i += TPW) {
     const long t = (long)f * c.S + s0 + i;  // output frame
-    const float dd = p.dden[bh * N + t];
-#pragma unroll
-    for (int j = 0; j < CL; ++j) p.dq_pos[(bh * N + t) * D + lane + 64 * j] = dd * za[j];
+    *reinterpret_cast<f32x4*>(p.dq_pos + (bh * N + t) * D + ch) = p.dden[bh * N + t] * za;
   }
   if (!absorb) {
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int j = 0; j < CL; ++j) p.dk_pos[(bh * N + s0 + i) * D + lane + 64 * j] = 0.f;
+#pragma unroll 4
+    for (int i = tl; i < 16; i += TPW)
+      *reinterpret_cast<f32x4*>(p.dk_pos + (bh * N + s0 + i) * D + ch) = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
-  for (int i = 0; i < 16; ++i) {
+#pragma unroll 4
+  for (int i = tl; i < 16; i += TPW) {
     const long t = (long)fa * c.S + s0 + i;  // absorbed frame
     const float bt = c.beta[bh * N + t];
-    float kp[CL], zh = 0.f, ee = 0.f;
+    const bf16x4_t kv = *reinterpret_cast<const bf16x4_t*>(p.k_pos + (bh * N + t) * D + ch);
+    float zh = 0.f, ee = 0.f;
 #pragma unroll
-    for (int j = 0; j < CL; ++j) {
-      kp[j] = (float)p.k_pos[(bh * N + t) * D + lane + 64 * j];
-      zh += kp[j] * zp[j];
-      ee += kp[j] * av[j];
+    for (int j = 0; j < 4; ++j) {
+      const float kp = (float)kv[j];
+      zh += kp * zp[j];
+      ee += kp * av[j];
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+    for (int off = LPT / 2; off > 0; off >>= 1) {
       zh += __shfl_xor(zh, off, 64);
       ee += __shfl_xor(ee, off, 64);
     }
     const float e1 = 1.f - zh;
-#pragma unroll
-    for (int j = 0; j < CL; ++j)
-      p.dk_pos[(bh * N + t) * D + lane + 64 * j] = av[j] * bt * e1 - bt * ee * zp[j];
-    if (lane == 0) c.dbeta[bh * N + t] += ee * e1;
+    *reinterpret_cast<f32x4*>(p.dk_pos + (bh * N + t) * D + ch) = av * (bt * e1) - (bt * ee) * zp;
+    if (lane % LPT == 0) c.dbeta[bh * N + t] += ee * e1;
   }
 }
 
