@@ -400,3 +400,25 @@ def test_cam_prep_bwd_validation_codes():
     n = lib.cam_prep_bwd_workspace_bytes(1, 64, 2, 128)
     assert n >= 64 * 4 + 64 * 2 * 256 * 4         # k inverse RMS + one partial pair per group
     assert call(ws=ctypes.c_void_p(0x1000 + 16), wsn=n) == L.ERR_INVALID  # misaligned
+
+
+def test_binding_reuse_stats_needs_the_workspace():
+    """Asking for reused frame statistics without the workspace that holds them is refused by
+    the binding before anything is launched (CPU tensors: no launch could run here anyway)."""
+    import torch
+
+    import gated_delta_rule_29_amd as g
+
+    B, H, D, F, S = 1, 2, 64, 2, 64
+    N = F * S
+    x = torch.zeros(B, H, D, N)
+    beta, decay = torch.zeros(B, H, F, S), torch.zeros(B, H, F)
+    with pytest.raises(ValueError, match="reuse_stats"):
+        g.cam_scan_bwd(x, x, x, beta, decay, x, reverse=True, reuse_stats=True)
+    t = torch.zeros(B, H, N, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="reuse_stats"):
+        g.bigdn_dir_bwd(t, t, t, t, t, beta, decay, torch.zeros(B, N, H, D), torch.zeros(B, H, N),
+                        reverse=True, reuse_stats=True)
+    with pytest.raises(ValueError, match="workspace"):
+        g.cam_scan_bwd(x, x, x, beta, decay, x, reverse=True, reuse_stats=True,
+                       workspace=torch.zeros(16, dtype=torch.uint8))
