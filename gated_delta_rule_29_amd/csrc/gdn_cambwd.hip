@@ -21,7 +21,7 @@
 //   stats  per (b, h, frame, matrix): G, U, W (D x D fp32) with 16x16x32 bf16 matrix products;
 //          a channel-major slab row is already in operand order (consecutive tokens of one
 //          channel), so the slabs go to LDS 32 tokens at a time without a transpose.
-//   scan   per (b, h, 32 state columns): the forward states and then A, in fp32 with split
+//   scan   per (b, h, kScanCB state columns): the forward states and then A, in fp32 with split
 //          bf16 products (the state in LDS as fp32 and as a hi/lo pair, G from the statistics
 //          as a hi/lo pair); every step's state and A leave as hi/lo
 //          bf16 pairs in both orientations for the token kernel, the states also in fp32 for
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void cbwd_scan_kernel(const CamBwdParams p) {
     *reinterpret_cast<bf16x4*>(&sth[0][jl][i]) = h;
     *reinterpret_cast<bf16x4*>(&sth[1][jl][i]) = l;
   };
-  // T = M st (rows of this wave, the block's 32 columns) with M's A operands (hi/lo bf16)
+  // T = M st (rows of this wave, the block's CB columns) with M's A operands (hi/lo bf16)
   // already in registers: tile (r, c) holds rows 16 (RT w + r) + 4 lq + e, column 16 c + li
   constexpr int KK = D / 32;
   struct Ops {

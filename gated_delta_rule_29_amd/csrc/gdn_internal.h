@@ -225,7 +225,8 @@ struct CamBwdParams {
   __bf16* Ab;         // gradient of the state after each step's update, both orientations
   __bf16* AbT;
   size_t lo;          // B * H * F * D * D
-  float* ddecay_part; // [B, H, F, D/32] partial sums of the decay gradient
+  float* ddecay_part; // [B, H, F, D/kScanCB] (gdn_bwd_params.h) partial sums of the decay gradient (one per
+                      // column block of the scan)
 };
 hipError_t launch_cam_scan_bwd(const CamBwdParams& p, hipStream_t stream);
 
