@@ -376,16 +376,19 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
     for (int i = 0; i < kTP; ++i) gam[i][j] += ex;
     gl[j] = __shfl(incl[j], row0 + kParts - 1, 64);  // gamma at token 63
   }
-  // gamma at the first and the middle token of each 16-token block (element 0 of a part,
-  // since kTP divides 8)
-  float gs[4][8], gmid[4][8];
+  const int blk = (part * kTP) / 16;  // this thread's 16-token block
+  // gamma at the first token of every 16-token block (element 0 of a part, since kTP
+  // divides 8), and at the first and the middle token of this thread's block.  The latter
+  // two are shuffled with a per-lane source: indexing gs by the per-lane blk would compile
+  // to a compare-and-select chain over all 32 values for every key.
+  float gs[4][8], gsb[8], gmb[8];
 #pragma unroll
-  for (int I = 0; I < 4; ++I)
+  for (int j = 0; j < 8; ++j) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      gs[I][j] = __shfl(gam[0][j], row0 + (16 * I) / kTP, 64);
-      gmid[I][j] = __shfl(gam[0][j], row0 + (16 * I + 8) / kTP, 64);
-    }
+    for (int I = 1; I < 4; ++I) gs[I][j] = __shfl(gam[0][j], row0 + (16 * I) / kTP, 64);
+    gsb[j] = __shfl(gam[0][j], row0 + (16 * blk) / kTP, 64);
+    gmb[j] = __shfl(gam[0][j], row0 + (16 * blk + 8) / kTP, 64);
+  }
   if (part == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -393,7 +396,6 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
       vec[SL::kEglk + 8 * o + j] = __expf(gl[j]);
     }
   }
-  const int blk = (part * kTP) / 16;  // this thread's 16-token block
 
   // bf16 raw -> fp32
   auto unpack = [](const u32x4& w, f32x4& lo4, f32x4& hi4) {
@@ -525,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
       const int t = part * kTP + i;
       float e[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = gam[i][j] - gs[blk][j];
+      for (int j = 0; j < 8; ++j) e[j] = gam[i][j] - gsb[j];
       *reinterpret_cast<u32x4*>(&s.row[pix(t, 8 * o)]) = scaled(x0[i], x1[i], e, f16{});
     }
   };
@@ -558,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
         float eu[8], ed[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          eu[j] = gam[i][j] - gmid[blk][j];
+          eu[j] = gam[i][j] - gmb[j];
           ed[j] = -eu[j];
         }
         const int ix = tix_s32<32>(rr, 8 * o);
