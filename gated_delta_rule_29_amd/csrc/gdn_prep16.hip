@@ -280,6 +280,8 @@ struct __attribute__((aligned(16))) PrepPkSmem {
   float a[kC][kC + 4];
   TO p[kC][kTP];
   float beta[kC];
+  float gx[2][4][K];  // per 16-token block and key: the block's decay sum and the decay of
+                      // its first token
 };
 
 template <int K, bool VARLEN>
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
   typedef Slot16<K, true> SL;
   constexpr int kG = K / 32;
   constexpr int kOct = K / 8;              // 16-byte octets per row
-  constexpr int kParts = kThreads / kOct;  // token parts (lanes of one wave per octet)
+  constexpr int kParts = kThreads / kOct;  // token parts of kTP tokens each
   constexpr int kTP = kC / kParts;         // tokens per thread
   static_assert(kParts <= 64 && kC % kParts == 0 && (kC / 2) % kTP == 0, "thread layout");
   __shared__ SM s;
@@ -321,9 +323,16 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
   char* slot = static_cast<char*>(p.ws) + (cp.slot0 + n) * (long)SL::kBytes;
   float* vec = reinterpret_cast<float*>(slot + SL::kVec);
 
+  // ---- thread layout: wave w holds the 16-token block w, lane = o kPB + pb (octet o of the
+  // keys, part pb of the block's tokens), so every branch on the block is wave-uniform
+  constexpr int kPB = 16 / kTP;  // parts per 16-token block
+  static_assert(kOct * kPB == 64, "one 16-token block per wave");
+  const int blk = wave;
+  const int pb = lane % kPB, o = lane / kPB;
+  const int part = blk * kPB + pb;
+
   // ---- loads: q, k (bf16) and gk (fp32) of this thread's keys and tokens, g and beta per
   // token; rows past the end of the sequence read as zero through the buffer bounds
-  const int o = tid / kParts, part = tid % kParts;
   const uint32_t qk_row = (uint32_t)p.H * K * 2, gk_row = (uint32_t)p.H * K * 4;
   const __amdgpu_buffer_rsrc_t rq = store_rsrc(const_cast<bf16*>(static_cast<const bf16*>(p.q)) + (tok * p.H + h) * K, rows * qk_row);
   const __amdgpu_buffer_rsrc_t rk = store_rsrc(const_cast<bf16*>(static_cast<const bf16*>(p.k)) + (tok * p.H + h) * K, rows * qk_row);
@@ -343,8 +352,9 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
   if (tid < kC) s.beta[tid] = (uint32_t)tid < rows ? p.beta[(tok + tid) * p.H + h] : 0.f;
 
   // ---- per-key cumulative decay gamma[t][8o + j] of lambda = max(g + gk, kKeyGateFloor):
-  // running sum over this thread's tokens, then the exclusive prefix over the parts before it
-  // (Hillis-Steele over the part lanes).  Rows past the end carry lambda = 0.
+  // running sum over this thread's tokens, the inclusive prefix over the block's parts (lane
+  // shuffles), then the sums of the blocks before it (through LDS).  Rows past the end carry
+  // lambda = 0.
   float gam[kTP][8], tot[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -360,36 +370,48 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
 #pragma unroll
   for (int j = 0; j < 8; ++j) incl[j] = tot[j];
 #pragma unroll
-  for (int sh = 1; sh < kParts; sh <<= 1) {
+  for (int sh = 1; sh < kPB; sh <<= 1) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float u = __shfl_up(incl[j], sh, kParts);
-      incl[j] += part >= sh ? u : 0.f;
+      const float u = __shfl_up(incl[j], sh, kPB);
+      incl[j] += pb >= sh ? u : 0.f;
     }
   }
-  const int row0 = lane & ~(kParts - 1);  // lane of part 0 of this octet
-  float gl[8];
+  if (pb == kPB - 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s.gx[0][blk][8 * o + j] = incl[j];
+  }
+  if (pb == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s.gx[1][blk][8 * o + j] = gam[0][j];
+  }
+  __syncthreads();
+  // gs[I]: gamma at the first token of block I (used for the blocks after this one); gl:
+  // gamma at token 63
+  float gs[4][8], gl[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float ex = incl[j] - tot[j];
+    float run = 0.f, off = 0.f;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      off = I == blk ? run : off;
+      gs[I][j] = run + s.gx[1][I][8 * o + j];
+      run += s.gx[0][I][8 * o + j];
+    }
+    gl[j] = run;
+    const float ex = off + incl[j] - tot[j];
 #pragma unroll
     for (int i = 0; i < kTP; ++i) gam[i][j] += ex;
-    gl[j] = __shfl(incl[j], row0 + kParts - 1, 64);  // gamma at token 63
   }
-  const int blk = (part * kTP) / 16;  // this thread's 16-token block
-  // gamma at the first token of every 16-token block (element 0 of a part, since kTP
-  // divides 8), and at the first and the middle token of this thread's block.  The latter
-  // two are shuffled with a per-lane source: indexing gs by the per-lane blk would compile
-  // to a compare-and-select chain over all 32 values for every key.
-  float gs[4][8], gsb[8], gmb[8];
+  // gamma at the first and the middle token of this block (element 0 of a part, since kTP
+  // divides 8)
+  float gsb[8], gmb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int I = 1; I < 4; ++I) gs[I][j] = __shfl(gam[0][j], row0 + (16 * I) / kTP, 64);
-    gsb[j] = __shfl(gam[0][j], row0 + (16 * blk) / kTP, 64);
-    gmb[j] = __shfl(gam[0][j], row0 + (16 * blk + 8) / kTP, 64);
+    gsb[j] = __shfl(gam[0][j], o * kPB, 64);
+    gmb[j] = __shfl(gam[0][j], o * kPB + 8 / kTP, 64);
   }
-  if (part == 0) {
+  if (blk == 0 && pb == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       vec[SL::kEmid + 8 * o + j] = 1.f;  // the scan's operands carry e^{gamma} themselves
@@ -435,24 +457,59 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
     lo = __builtin_bit_cast(u32x4, pack8<bf16>(r0, r1));
   };
 
+  // x (8 keys) times m[j] into 8 16-bit values of type T
+  auto scaledm = [](const f32x4& x0, const f32x4& x1, const float* m, auto tag) {
+    typedef decltype(tag) T;
+    f32x4 y0, y1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y0[j] = x0[j] * m[j];
+      y1[j] = x1[j] * m[4 + j];
+    }
+    return __builtin_bit_cast(u32x4, pack8<T>(y0, y1));
+  };
+
   // ---- the scan's operands, straight to the slot: Q e^{gamma}, K e^{gamma} and
-  // K e^{gamma_last - gamma} (fp16)
+  // K e^{gamma_last - gamma} (fp16); and the column operands of the off-diagonal tiles,
+  // K e^{gamma_16I - gamma} on this block's rows for every row block I after it.  The last
+  // two are e^{gamma_mid - gamma} (at most e^{70} inside the block, by the floor) times a
+  // per-key factor of the block that is at most 1, so one exponential per element serves
+  // all four; a factor that underflows leaves products below fp16's subnormal range.
+  float ckh[8], ccol[4][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ckh[j] = __expf(gl[j] - gmb[j]);
+#pragma unroll
+  for (int I = 1; I < 4; ++I) {
+    if (I <= blk) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ccol[I][j] = __expf(gs[I][j] - gmb[j]);
+  }
   f32x4 qf0[kTP], qf1[kTP], kf0[kTP], kf1[kTP];
 #pragma unroll
   for (int i = 0; i < kTP; ++i) {
     const int t = part * kTP + i;
     unpack(qv[i], qf0[i], qf1[i]);
     unpack(kv[i], kf0[i], kf1[i]);
-    float e[8], el[8];
+    float eg[8], ed[8], m[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      e[j] = gam[i][j];
-      el[j] = gl[j] - gam[i][j];
+      eg[j] = __expf(gam[i][j]);
+      ed[j] = __expf(gmb[j] - gam[i][j]);
+      m[j] = ed[j] * ckh[j];
     }
     const int sx = 2 * tix_s32<kC>(t, 8 * o);
-    *reinterpret_cast<u32x4*>(slot + SL::kQ + sx) = scaled(qf0[i], qf1[i], e, f16{});
-    *reinterpret_cast<u32x4*>(slot + SL::kK + sx) = scaled(kf0[i], kf1[i], e, f16{});
-    *reinterpret_cast<u32x4*>(slot + SL::kKh + sx) = scaled(kf0[i], kf1[i], el, f16{});
+    *reinterpret_cast<u32x4*>(slot + SL::kQ + sx) = scaledm(qf0[i], qf1[i], eg, f16{});
+    *reinterpret_cast<u32x4*>(slot + SL::kK + sx) = scaledm(kf0[i], kf1[i], eg, f16{});
+    *reinterpret_cast<u32x4*>(slot + SL::kKh + sx) = scaledm(kf0[i], kf1[i], m, f16{});
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+      if (I <= blk) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = ed[j] * ccol[I][j];
+      const int c = I * (I - 1) / 2 + blk;
+      *reinterpret_cast<u32x4*>(&s.col[c * SM::kBlk + tix_s32<16>(t - 16 * blk, 8 * o)]) =
+          scaledm(kf0[i], kf1[i], m, f16{});
+    }
   }
   // strict upper 16x16 tiles of A and P stay zero
   for (int e = tid; e < 6 * 256; e += kThreads) {
@@ -504,22 +561,8 @@ __global__ __launch_bounds__(kThreads, 2) void prep16pk_kernel(const FwdParams p
   constexpr auto R32 = std::integral_constant<int, 32>{};
   constexpr auto R64 = std::integral_constant<int, kC>{};
 
-  // ---- off-diagonal tiles, reference = first row of the row block (fp16 operands).
-  // Column operands: this thread's tokens (block blk) for every row block I > blk.
-#pragma unroll
-  for (int i = 0; i < kTP; ++i) {
-    const int t = part * kTP + i;
-#pragma unroll
-    for (int I = 1; I < 4; ++I) {
-      if (I <= blk) continue;
-      float e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = gs[I][j] - gam[i][j];
-      const int c = I * (I - 1) / 2 + blk;
-      *reinterpret_cast<u32x4*>(&s.col[c * SM::kBlk + tix_s32<16>(t - 16 * blk, 8 * o)]) =
-          scaled(kf0[i], kf1[i], e, f16{});
-    }
-  }
+  // ---- off-diagonal tiles, reference = first row of the row block (fp16 operands); the
+  // column operands are in place.
   // phase 1a: K rows; Gram tiles (I, J < I)
   auto rows_off = [&](const f32x4* x0, const f32x4* x1) {
 #pragma unroll
