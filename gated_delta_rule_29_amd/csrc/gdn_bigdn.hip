@@ -728,7 +728,7 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
         if constexpr (kMerge) {
           const float dn = kTwoQ ? den_part[0][16 * tt + li] + den_part[1][16 * tt + li]
                                  : den_part[hh][16 * tt + li];
-          rden = 1.f / (dn + p.merge_eps);
+          rden = __builtin_amdgcn_rcpf(dn + p.merge_eps);  // 1 ulp: far below bf16 output
         }
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct) {
@@ -745,7 +745,9 @@ __global__ __launch_bounds__(256) void out_kernel(const BigdnParams p, int grp) 
               float x = acc[tt][ct][e] * rden;
               if (p.gate) {
                 const float gt = (float)gv[tt][ct][e];
-                x *= gt / (1.f + __expf(-gt));
+                // SiLU; the hardware reciprocal instead of a full-precision division (whose
+                // scaling and fix-up steps doubled this epilogue's VALU work)
+                x *= gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt));
               }
               o4[e] = (bf16)x;
             }
