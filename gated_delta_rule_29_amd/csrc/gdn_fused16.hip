@@ -91,7 +91,12 @@ struct __attribute__((aligned(16))) FusedSmem {
   float gate[3][kGateF];
   u16 af[kC * kC];      // fp16 rows of the off-diagonal blocks of A (tix layout)
   unsigned pbar;        // prep-wave pair barrier counter
+  unsigned sink[64];    // destination of the L2 prefetch loads (never read)
 };
+
+// L2 prefetch distance: while chunk n is scanned, transfer wave 1 touches the lines of chunk
+// n + 2 + kPF, whose q / k transfers are issued kPF steps later.
+constexpr int kPF = 2;
 
 // LDS base addresses the optimiser cannot relate to one another: each tile read is then
 // issued as its own base plus an instruction immediate (the compiler would otherwise derive
@@ -361,6 +366,24 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         G[kFast] = (g0 - gl < 80.f) ? 1.f : 0.f;
       }
     };
+    // L2 prefetch of chunk c (wave 1 only: its loads are all direct-to-LDS, so no register
+    // load of this wave makes the compiler wait for them): one-dword loads into a dummy LDS
+    // area, one per 128-byte line.  The value blocks of a chain split the q and k lines between
+    // them (lane L < 32: q, else k; rows 16 vb + (L & 15), line (L >> 4) & 1 of the row);
+    // each workgroup touches its own v rows.  Rows past the chain read nothing.
+    const uint32_t sink = lds_addr(s.sink);
+    const int nvb = p.nvb;
+    auto touch = [&](int c) {
+      const long tok = tok0 + (long)c * kC;
+      const uint32_t rows = (uint32_t)max(0, min(kC, len - c * kC));
+      const int r = (16 * vb + (lane & 15)) % kC;  // nvb <= 4 value blocks cover rows 0..63
+      const i32x4 rqk = make_rsrc((lane < 32 ? qg : kg) + (tok * p.H + h) * K, rows * qk_row);
+      dma4(rqk, (uint32_t)r * qk_row + 128u * ((lane >> 4) & 1), 0, sink);
+      const i32x4 rv = make_rsrc(vg + (tok * p.H + h) * p.V + v0, rows * v_row);
+      dma4(rv, (uint32_t)lane * v_row, 0, sink);
+      (void)nvb;
+    };
+    bool touched = false;  // wave 1 issued two prefetch loads after its transfers
     float g1 = 0.f, b1 = 0.f, g2 = 0.f, b2 = 0.f;
     issue_qk(0);
     if (tw == 0) {
@@ -377,15 +400,21 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
       issue_qk(n + 2);
       if (tw == 1) {
         issue_v(n + 1);
+        touched = n + 2 + kPF < nchunks;
+        if (touched) touch(n + 2 + kPF);
       } else {
         load_gb(n + 3, g2, b2);
         gates(n + 2, g1, b1);
       }
-      wait_vm0();
+      // this wave's transfers have landed in LDS (loads complete in issue order; only the
+      // two prefetch loads issued after them may still be pending)
+      if (touched) wait_vm<2>();
+      else wait_vm0();
       g1 = g2;
       b1 = b2;
       __syncthreads();
     }
+    wait_vm0();
     return;
   }
 

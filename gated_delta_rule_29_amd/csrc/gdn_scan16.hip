@@ -98,7 +98,12 @@ struct __attribute__((aligned(16))) S16Smem {
   S16Buf<K, PK> buf[2];
   u16 stg[kNW][16 * kSW];           // per-wave staging of v_new, [16 columns][64 rows]
   u16 stgh[kNW][K / 64][16 * kSW];  // per-wave staging of the state, one tile per 64 keys
+  unsigned sink[64];                // destination of the L2 prefetch loads (never read)
 };
+
+// L2 prefetch distance in chunks: the transfer waves touch the lines of chunk n + kPF while
+// chunk n is scanned, and that chunk's own transfers are issued kPF - 1 steps later.
+constexpr int kPF = 2;
 
 // The lane index, opaque to the optimiser: addresses derived from it inside the chunk loop are
 // recomputed each iteration (a few integer operations) instead of being hoisted out of the
@@ -232,12 +237,39 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
         for (int b = 0; b < 4 * kG; ++b) dma(rw, l16, (uint32_t)SL::kKh + 1024u * b, lds_addr(B.kh) + 1024u * b);
       }
     };
+    // L2 prefetch of chunk c: one-dword loads, one per 128-byte line, into a dummy LDS area
+    // (no register is written, so nothing waits for them until the next step's count).  The
+    // value blocks of a chain split the slot's lines between them; each workgroup also
+    // touches its own v rows.  Two loads per wave: wave 0 lines [0, 128) of its share, wave 1
+    // lines [128, 192) and the v rows.  Lines past the share or rows past the chain read
+    // nothing (offsets beyond the buffer resource).
+    constexpr uint32_t kLines = (uint32_t)(SL::kBytes / 128);
+    const uint32_t vb = (uint32_t)(logical % p.nvb);
+    const uint32_t share = (kLines + p.nvb - 1) / p.nvb;
+    const uint32_t sink = lds_addr(s.sink);
+    auto touch = [&](int c) {
+      const long tok = cp.tok0 + (long)c * kC;
+      const i32x4 rw = make_rsrc(wsg + (cp.slot0 + c) * (long)SL::kBytes, (uint32_t)SL::kBytes);
+      const uint32_t l0 = 128u * tw + (uint32_t)lane;
+      auto line_off = [&](uint32_t l) { return l < share ? (vb * share + l) * 128u : 0xffffffffu; };
+      dma4(rw, line_off(l0), 0, sink);
+      // (a select, not a branch: the branch form does not compile)
+      const i32x4 rv = make_rsrc(vg + (tok * p.H + h) * p.V + v0, (uint32_t)(cp.len - c * kC) * v_row);
+      dma4(tw == 0 ? rw : rv, tw == 0 ? line_off(l0 + 64) : (uint32_t)lane * v_row, 0, sink);
+    };
+    bool touched = false;  // two prefetch loads were issued after the last transfers
     if (nchunks > 0) issue(0, s.buf[0]);
     for (int n = 0; n < nchunks; ++n) {
-      wait_vm0();       // this wave's transfers of chunk n have landed in LDS
+      // this wave's transfers of chunk n have landed in LDS (loads complete in issue order;
+      // only the two prefetch loads issued after them may still be pending)
+      if (touched) wait_vm<2>();
+      else wait_vm0();
       __syncthreads();  // ... and every compute wave is done with chunk n-1
       if (n + 1 < nchunks) issue(n + 1, s.buf[(n + 1) & 1]);
+      touched = n + kPF < nchunks;
+      if (touched) touch(n + kPF);
     }
+    wait_vm0();
     return;
   }
 
