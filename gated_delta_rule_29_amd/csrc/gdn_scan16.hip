@@ -99,6 +99,7 @@ struct __attribute__((aligned(16))) S16Smem {
   u16 stg[kNW][16 * kSW];           // per-wave staging of v_new, [16 columns][64 rows]
   u16 stgh[kNW][K / 64][16 * kSW];  // per-wave staging of the state, one tile per 64 keys
   unsigned sink[64];                // destination of the L2 prefetch loads (never read)
+  unsigned hread;                   // staged states read by the transfer waves (one per wave and chunk)
 };
 
 // L2 prefetch distance in chunks: the transfer waves touch the lines of chunk n + kPF while
@@ -184,6 +185,7 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
   const int nchunks = (cp.len + kC - 1) / kC;
   const uint32_t qk_row = (uint32_t)p.H * K * 2, v_row = (uint32_t)p.H * p.V * 2;
 
+  if (tid == 0) s.hread = 0u;  // ordered before every use by the first barrier
   if (wave >= kNW) {
     // ---- transfer waves: chunk n+1's tiles into the other LDS buffer while chunk n is used.
     // One wave sustains only a fraction of a CU's load bandwidth, so the 1 KiB blocks of a
@@ -257,6 +259,40 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
       const i32x4 rv = make_rsrc(vg + (tok * p.H + h) * p.V + v0, (uint32_t)(cp.len - c * kC) * v_row);
       dma4(tw == 0 ? rw : rv, tw == 0 ? line_off(l0 + 64) : (uint32_t)lane * v_row, 0, sink);
     };
+    // The state entering chunk m -> h_chunks: the compute waves stage it (one tile per wave and
+    // 64 keys) during step m; transfer wave tw stores the key half tw of both compute waves'
+    // tiles in step m + 1 (after the loop for the last chunk).  Once its staging reads have
+    // completed it counts them in s.hread, which the compute waves wait for before they stage
+    // the next chunk's state.  The global stores are issued before the chunk's transfers, so
+    // the count-based wait of the next step covers them too.
+    bf16* hcg = static_cast<bf16*>(p.h_chunks);
+    auto flush_h = [&](int m) {
+      const __amdgpu_buffer_rsrc_t rh =
+          store_rsrc(hcg + (cp.slot0 + m) * (long)K * p.V + v0, (uint32_t)(K * p.V - v0) * 2u);
+      // Each store writes 16 rows x 64 bytes (the block's 32 columns): within a 16-lane group,
+      // lane n = 4m + r receives row R0 + r, columns 8m .. 8m+7, from two transpose reads in
+      // which source lane 4j + m points at column 8m + j (+4 for the second), rows R0 .. R0+3
+      // (columns 0-15 in compute wave 0's tile, 16-31 in wave 1's).
+      static_assert(kNW == 2 && kWC == 16, "two 16-column staging tiles per key half");
+      const int n16 = lane & 15, grp = lane >> 4;
+      const int src_m = n16 & 3, src_j = n16 >> 2;
+      const int res_r = n16 & 3, res_m = n16 >> 2;
+#pragma unroll
+      for (int half = 0; half < K / 64; ++half) {
+        if (half % kTW != tw) continue;
+        const u16* tile = s.stgh[src_m >> 1][half] + (8 * (src_m & 1) + src_j) * kSW + 4 * grp;
+        u32x4 d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          d[i] = __builtin_shufflevector(tr16(tile + 16 * i), tr16(tile + 4 * kSW + 16 * i), 0, 1, 2, 3);
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        if (lane == 0) __hip_atomic_fetch_add(&s.hread, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              d[i], rh, (uint32_t)(64 * half + 16 * i + 4 * grp + res_r) * (uint32_t)p.V * 2u + 16u * res_m, 0, 0);
+      }
+    };
     bool touched = false;  // two prefetch loads were issued after the last transfers
     if (nchunks > 0) issue(0, s.buf[0]);
     for (int n = 0; n < nchunks; ++n) {
@@ -265,10 +301,13 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
       if (touched) wait_vm<2>();
       else wait_vm0();
       __syncthreads();  // ... and every compute wave is done with chunk n-1
+      if (hcg && n > 0) flush_h(n - 1);
       if (n + 1 < nchunks) issue(n + 1, s.buf[(n + 1) & 1]);
       touched = n + kPF < nchunks;
       if (touched) touch(n + kPF);
     }
+    __syncthreads();  // the compute waves have staged the last chunk's state
+    if (hcg && nchunks > 0) flush_h(nchunks - 1);
     wait_vm0();
     return;
   }
@@ -320,11 +359,6 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
       for (int P = 0; P < 2; ++P)
 #pragma unroll
         for (int t = 0; t < 2; ++t) kfr[P][t][G] = lds8(kt + tix(pair_row(P, t, li), 32 * G + 8 * lq));
-    if (hcg) {  // staged now, stored at the end of the step (stage 5)
-#pragma unroll
-      for (int half = 0; half < K / 64; ++half)
-        stage_rows(s.stgh[wave][half], [&](int G, int t, int e) { return hs[0][2 * half + G][t][e]; }, lane);
-    }
     f16x8 bk[kG];
     Q8 bq[kG];
 #pragma unroll
@@ -470,6 +504,18 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    // the state entering the chunk -> staging tiles, which the transfer waves store to
+    // h_chunks in the next step; the previous chunk's tiles must have been read first
+    if (hcg) {
+      const unsigned target = (unsigned)(K / 64) * (unsigned)n;
+      while (__hip_atomic_load(&s.hread, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+        __builtin_amdgcn_s_sleep(1);
+      lds_order();
+#pragma unroll
+      for (int half = 0; half < K / 64; ++half)
+        stage_rows(s.stgh[wave][half], [&](int G, int t, int e) { return hs[0][2 * half + G][t][e]; }, lane);
+    }
+
     // ---- stage 4: bv = v_new (fp16) for P v_new; bu = the update's B operand (scalar gate:
     // v_new e^{gl-gamma}); h <- decay h + K^T diag(...) v_new, a token half at a time
     f16x8 bv[2], bu[2];
@@ -511,16 +557,8 @@ __global__ __launch_bounds__(kThr) void scan16_kernel(const FwdParams p) {
       stage_rows(s.stg[wave], [&](int G, int t, int e) { return vn[G][t][e]; }, lane);
       flush_rows(s.stg[wave], rv, v_row, (uint32_t)col * 2u, lane);
     }
-    // the state entering the chunk -> h_chunks (its global stores are kept away from the start
-    // of the step, where they would delay the next chunk's transfers)
-    if (hcg) {
-      const __amdgpu_buffer_rsrc_t rh =
-          store_rsrc(hcg + (cp.slot0 + n) * (long)K * p.V + v0, (uint32_t)(K * p.V - v0) * 2u);
-#pragma unroll
-      for (int half = 0; half < K / 64; ++half)
-        flush_rows(s.stgh[wave][half], rh, (uint32_t)p.V * 2u, (uint32_t)(64 * half * p.V + col) * 2u, lane);
-    }
   }
+  __syncthreads();  // the transfer waves store the last chunk's staged state after this
 
   if (p.ht) {
 #pragma unroll
