@@ -746,6 +746,10 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) oacc[G][t] = f32x4{0.f, 0.f, 0.f, 0.f};
       f16x8 by[2];
+      // K^T (the update's A operand, transpose reads), one contraction round per Q h round:
+      // the round's K^T fragments take the registers its Q rows free
+      bf16x8 ktf[kG][2][2];
+      lds_u16* ktb[2] = {lds_base(Q.k + ot[0]), lds_base(Q.k + ot[1])};
 #pragma unroll
       for (int Gk = 0; Gk < kG; ++Gk) {
         if constexpr (OUT)
@@ -753,6 +757,12 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
           for (int G = 0; G < 2; ++G)
 #pragma unroll
             for (int t = 0; t < 2; ++t) oacc[G][t] = mma16(bh[Gk], qfr[G][t][Gk], oacc[G][t]);
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            ktf[Gk][t][P] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr16_at(ktb[0], 1024 * P + 2048 * Gk + 4 * t),
+                                                                               tr16_at(ktb[1], 1024 * P + 2048 * Gk + 4 * t), 0, 1, 2, 3));
         if (Gk == 0) {
 #pragma unroll
           for (int P = 0; P < 2; ++P)
@@ -765,19 +775,8 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- stage 3: reads of K^T (the update's A operand, transpose reads), the update
-      // gates, P rows and the o gates; v_new = Tm Y (token group P feeds groups G >= P)
-      bf16x8 ktf[kG][2][2];
-      lds_u16* ktb[2] = {lds_base(Q.k + ot[0]), lds_base(Q.k + ot[1])};
-#pragma unroll
-      for (int P = 0; P < 2; ++P)
-#pragma unroll
-        for (int G = 0; G < kG; ++G)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            ktf[G][t][P] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr16_at(ktb[0], 1024 * P + 2048 * G + 4 * t),
-                                                                              tr16_at(ktb[1], 1024 * P + 2048 * G + 4 * t), 0, 1, 2, 3));
-          }
+      // ---- stage 3: reads of the update gates, P rows and the o gates; v_new = Tm Y (token
+      // group P feeds groups G >= P)
       f32x4 l0[2], l1[2];
 #pragma unroll
       for (int P = 0; P < 2; ++P) {
