@@ -813,10 +813,10 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
 
       // ---- stage 4: bv = v_new (fp16) for P v_new; v_new e^{gl - gamma} as two bf16 parts;
       // h <- e^gl h + K^T diag(e^{gl - gamma}) v_new, a round (token half, part) at a time
+      // token half 1's operands are formed while half 0's products run
       f16x8 bv[2];
       bf16x8 buh[2], bul[2];
-#pragma unroll
-      for (int P = 0; P < 2; ++P) {
+      auto operands = [&](int P) {
         bv[P] = pack8<f16>(vn[P][0], vn[P][1]);
         const f32x4 u0 = vn[P][0] * l0[P], u1 = vn[P][1] * l1[P];
         buh[P] = pack8<bf16>(u0, u1);
@@ -825,21 +825,26 @@ __global__ __launch_bounds__(kThr) void fused16_kernel(const FwdParams p) {
           bul[P][j] = (bf16)(u0[j] - (float)buh[P][j]);
           bul[P][4 + j] = (bf16)(u1[j] - (float)buh[P][4 + j]);
         }
-      }
+      };
+      operands(0);
 #pragma unroll
       for (int G = 0; G < kG; ++G)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) hs[G][t] = hs[G][t] * egl;
+        for (int t = 0; t < 2; ++t) hs[G][t] = mma16(ktf[G][t][0], buh[0], hs[G][t] * egl);
+      __builtin_amdgcn_sched_barrier(0);
+      operands(1);
 #pragma unroll
-      for (int P = 0; P < 2; ++P) {
+      for (int G = 0; G < kG; ++G)
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {
+        for (int t = 0; t < 2; ++t) hs[G][t] = mma16(ktf[G][t][0], bul[0], hs[G][t]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int G = 0; G < kG; ++G)
+      for (int part = 0; part < 2; ++part) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) hs[G][t] = mma16(ktf[G][t][P], part ? bul[P] : buh[P], hs[G][t]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int G = 0; G < kG; ++G)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) hs[G][t] = mma16(ktf[G][t][1], part ? bul[1] : buh[1], hs[G][t]);
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       // ---- stage 5: o^T = (Q h)^T diag(scale e^gamma) + (scale P v_new)^T (P carries the
